@@ -1,0 +1,44 @@
+"""CPU oracle for INT8-QK quantized attention: TEST INFRASTRUCTURE ONLY.
+
+This package is the slow, plain definition of what the GPU library
+computes. Only the test suite, the smoke check in ``__graft_entry__`` and
+the CPU-baseline leg of ``bench.py`` may import it. The GPU library never
+imports, links or calls it, and it shares no code with the GPU path: the
+only common module is the seeded input generator, which holds none of the
+method's arithmetic.
+
+Sources (the three pages this work follows):
+
+* [QK-MMAC] "INT8 QK MMAC on the gfx936 DCU: paged access, fragment
+  mapping and GQA" (forum article, second of a series).
+* [LP-NEG] "Dynamic INT8 GEMM and FP8 KV-cache attention on gfx936"
+  (forum article reporting negative low-precision results).
+* [SAGE-MACA] "SageAttention - MetaX MXMACA port (v3.0.0)" README.
+
+Precision: quantization follows the pages in IEEE fp32 (one correctly
+rounded operation per step, round-half-even). Everything after the INT32
+accumulator (score recovery, softmax, P.V) is done in fp64, since the pages
+fix no precision there.
+
+Parity status, function by function (pins live in tests/test_oracle_pins.py):
+
+* quant_rows, quantize_q, write_kv_cache, sage_quantize: pinned (worked
+  rounding ties, arg-max maps to +-127, error bound, zero rows, layout
+  round trip, brute force per block, smoothing mean exactness).
+* paged_qk_int32: pinned (INT32 bound 256*127*127, brute force in int64).
+* paged_decode, paged_decode_split, chunked_prefill, dense_sage_attention:
+  pinned (rows sum to one, equality with a textbook fp64 attention of the
+  dequantized tensors, split = unsplit, smoothing invariance, causal
+  structure).
+"""
+from .quant import (widen, quant_rows, quantize_q, write_kv_cache, sage_quantize,
+                    gather_kv)
+from .attention import (paged_qk_int32, paged_decode, paged_decode_split,
+                        chunked_prefill, dense_sage_attention, attention_fp64,
+                        default_scale)
+
+__all__ = [
+    "widen", "quant_rows", "quantize_q", "write_kv_cache", "sage_quantize", "gather_kv",
+    "paged_qk_int32", "paged_decode", "paged_decode_split", "chunked_prefill",
+    "dense_sage_attention", "attention_fp64", "default_scale",
+]

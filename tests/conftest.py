@@ -1,0 +1,19 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size workload; runs in the GPU session")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests without a GPU fail loudly rather than skip, unless the run
+    # explicitly deselects them with -m "not gpu".
+    pass

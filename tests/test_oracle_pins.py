@@ -1,0 +1,487 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other
+than itself (values the pages print, closed forms, brute force, textbook
+attention through scipy, structural invariants). CPU only."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import softmax as sp_softmax
+
+import oracle
+from oracle import quant as oq
+from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, to_bf16_bits,
+                       to_f16_bits)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _nearest_f32(fr: Fraction) -> np.float32:
+    """Nearest float32 to an exact rational (ties to even), found by exact
+    comparison of the neighbours of a float64 guess."""
+    g = np.float32(float(fr))
+    cands = [np.nextafter(g, np.float32(-np.inf)), g, np.nextafter(g, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+# --------------------------------------------------------------------------
+# quantization
+# --------------------------------------------------------------------------
+
+def test_quant_worked_ties_from_golden():
+    rows = _golden("quant_ties.txt")
+    x = np.array([float(r[0]) for r in rows], np.float32)
+    want = np.array([int(r[1]) for r in rows])
+    assert np.array_equal(oq.widen(to_bf16_bits(x), "bf16"), x)  # exact in bf16
+    q, s = oracle.quant_rows(x[None])
+    assert s[0] == np.float32(1.0)
+    assert np.array_equal(q[0].astype(int), want)
+
+
+def test_quant_scale_is_correctly_rounded_division():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((200, 64)).astype(np.float32) * rng.uniform(1e-3, 1e3, (200, 1)).astype(np.float32)
+    _, s = oracle.quant_rows(x)
+    for i in range(x.shape[0]):
+        amax = Fraction(float(np.max(np.abs(x[i]))))
+        assert s[i] == _nearest_f32(amax / 127)
+
+
+def test_quant_codes_match_exact_rounding_of_fp32_quotient():
+    # code = round-half-even of the fp32 quotient x/s; the quotient itself is
+    # the float32 nearest to the exact rational x/s.
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((40, 32)).astype(np.float32) * 3
+    q, s = oracle.quant_rows(x)
+    for i in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            quo = _nearest_f32(Fraction(float(x[i, j])) / Fraction(float(s[i])))
+            want = max(-127, min(127, round(Fraction(float(quo)))))  # Python round: ties to even
+            assert int(q[i, j]) == want
+
+
+def test_quant_near_ties_against_fp64_quotient():
+    # Inputs built to land within a few ulps of k + 1/2 after division by the
+    # row scale, where a reciprocal-multiply or a wrong rounding mode shows.
+    # Reference route: for fp32 operands the fp64 quotient rounded once to
+    # fp32 equals the correctly rounded fp32 quotient.
+    rng = np.random.default_rng(14)
+    n_rows = 400
+    amax = (rng.uniform(0.5, 2.0, n_rows) * 2.0 ** rng.integers(-20, 20, n_rows)).astype(np.float32)
+    s_ref = (amax.astype(np.float64) / 127.0).astype(np.float32)
+    k = rng.integers(-125, 125, (n_rows, 255))
+    x = ((k + 0.5) * s_ref[:, None].astype(np.float64)).astype(np.float32)
+    for _ in range(3):
+        step = rng.integers(-1, 2, x.shape)
+        x = np.where(step > 0, np.nextafter(x, np.float32(np.inf)),
+                     np.where(step < 0, np.nextafter(x, np.float32(-np.inf)), x)).astype(np.float32)
+    rows = np.concatenate([amax[:, None], x], axis=1)
+    q, s = oracle.quant_rows(rows)
+    assert np.array_equal(s, s_ref)
+    quo = (rows.astype(np.float64) / s_ref[:, None].astype(np.float64)).astype(np.float32)
+    want = np.clip(np.rint(quo), -127, 127)
+    assert np.array_equal(q.astype(np.float64), want)
+
+
+def test_quant_properties():
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((500, 256)) * rng.uniform(0.01, 100, (500, 1))).astype(np.float32)
+    q, s = oracle.quant_rows(x)
+    assert q.min() >= -127 and q.max() <= 127
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(q[np.arange(500), am]) == 127)
+    assert np.all(np.sign(q[np.arange(500), am]) == np.sign(x[np.arange(500), am]))
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None])
+    assert np.all(err <= s[:, None].astype(np.float64) * 0.5 * (1 + 2.0 ** -20))
+
+
+def test_quant_zero_row_and_signed_zero():
+    x = np.zeros((2, 64), np.float32)
+    x[1] = -0.0
+    q, s = oracle.quant_rows(x)
+    assert np.all(q == 0) and np.all(s == 0)
+
+
+def test_quant_tiny_values_fp16_subnormal():
+    x = np.array([[6e-8, -1.2e-7, 3e-8, 0.0]], np.float32)
+    x = oq.widen(to_f16_bits(x), "f16")[None][0]
+    q, s = oracle.quant_rows(x)
+    assert s[0] > 0 and abs(int(q[0, 1])) == 127
+
+
+def test_widen_bf16_and_f16_exact():
+    v = np.array([1.0, -2.5, 3.140625, 65504.0, 1e-3], np.float32)
+    bb = to_bf16_bits(v)
+    assert np.array_equal(oq.widen(bb, "bf16"), np.array([1.0, -2.5, 3.140625, 65536.0, 0.00099945068359375], np.float32))
+    hb = to_f16_bits(v)
+    assert np.array_equal(oq.widen(hb, "f16"), v.astype(np.float16).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# cache layout
+# --------------------------------------------------------------------------
+
+def _small_spec(**kw):
+    base = dict(name="t", seed=21, num_seqs=3, num_q_heads=6, num_kv_heads=2, head_dim=64,
+                context_lens=[17, 1, 40], query_lens=[1, 1, 1], k_bias_std=2.0)
+    base.update(kw)
+    return PagedSpec(**base)
+
+
+@pytest.mark.parametrize("v_int8", [False, True])
+def test_cache_layout_elementwise(v_int8):
+    spec = _small_spec(v_int8=v_int8, pool_blocks=9)
+    inp = paged_inputs(spec)
+    c = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks, v_int8)
+    kq, ks = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    vq, vs = oracle.quant_rows(oq.widen(inp.v, "bf16"))
+    # [QK-MMAC] §3 layout: [block, kv_head, head_dim/16, block_size, 16]
+    for t in range(inp.k.shape[0]):
+        slot = int(inp.slot_mapping[t])
+        b, o = slot // 16, slot % 16
+        for h in range(spec.num_kv_heads):
+            assert c["k_scale"][b, h, o] == ks[t, h]
+            for i in range(spec.head_dim):
+                assert c["k_cache"][b, h, i // 16, o, i % 16] == kq[t, h, i]
+                if v_int8:
+                    assert c["v_cache"][b, h, i, o] == vq[t, h, i]
+                else:
+                    assert c["v_cache"][b, h, i, o] == inp.v[t, h, i]
+            if v_int8:
+                assert c["v_scale"][b, h, o] == vs[t, h]
+
+
+def test_cache_negative_slot_skipped():
+    spec = _small_spec()
+    inp = paged_inputs(spec)
+    slots = inp.slot_mapping.copy()
+    slots[::2] = -1
+    c = oracle.write_kv_cache(inp.k, inp.v, "bf16", slots, spec.num_blocks)
+    for t in range(0, inp.k.shape[0], 2):
+        b, o = inp.slot_mapping[t] // 16, inp.slot_mapping[t] % 16
+        assert np.all(c["k_cache"][b, :, :, o, :] == 0) and np.all(c["k_scale"][b, :, o] == 0)
+
+
+# --------------------------------------------------------------------------
+# INT32 QK
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("row", _golden("int32_bound.txt"))
+def test_int32_bound_from_golden(row):
+    d, bound = int(row[0]), int(row[1])
+    assert bound == d * 127 * 127
+    spec = PagedSpec("b", 1, 1, 2, 1, d, [16], [1])
+    k = to_bf16_bits(np.full((16, 1, d), 0.75, np.float32))
+    v = np.zeros_like(k)
+    slots = np.arange(16)
+    c = oracle.write_kv_cache(k, v, "bf16", slots, 1)
+    q = np.stack([np.full((2, d), 127, np.int8)])
+    q[0, 1] = -127
+    acc = oracle.paged_qk_int32(q, c, np.zeros((1, 1), np.int32), [16], 1)[0]
+    assert np.all(acc[0] == bound) and np.all(acc[1] == -bound)
+    assert bound < 2 ** 24 < 2 ** 31 - 1
+
+
+@pytest.mark.parametrize("ctx", [1, 15, 16, 17, 33])
+def test_qk_brute_force_int64(ctx):
+    spec = PagedSpec("bf", 5 + ctx, 2, 6, 2, 64, [ctx, 33], [1, 1], k_bias_std=2.0, pool_blocks=7)
+    inp = paged_inputs(spec)
+    c = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks)
+    q_i8, _ = oracle.quantize_q(inp.q)
+    kq, _ = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    accs = oracle.paged_qk_int32(q_i8, c, inp.block_tables, inp.context_lens, 2)
+    for s in range(2):
+        base = int(inp.cu_seqlens_kv[s])
+        for h in range(6):
+            for t in range(int(inp.context_lens[s])):
+                want = 0
+                for i in range(64):
+                    want += int(q_i8[s, h, i]) * int(kq[base + t, h // 3, i])
+                assert accs[s][h, t] == want
+
+
+# --------------------------------------------------------------------------
+# decode attention
+# --------------------------------------------------------------------------
+
+def _textbook_decode(inp, spec, v_int8):
+    """softmax(Qdeq Kdeq^T / sqrt d) Vdeq per sequence from the UNPAGED token
+    arrays, with scipy's softmax; no block table involved."""
+    q_i8, q_s = oracle.quantize_q(inp.q)
+    kq, ks = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    if v_int8:
+        vq, vs = oracle.quant_rows(oq.widen(inp.v, "bf16"))
+        vd = vq.astype(np.float64) * vs[..., None]
+    else:
+        vd = oq.widen(inp.v, "bf16").astype(np.float64)
+    G = spec.group
+    out = np.zeros(q_i8.shape, np.float64)
+    for s in range(spec.num_seqs):
+        a, b = int(inp.cu_seqlens_kv[s]), int(inp.cu_seqlens_kv[s + 1])
+        if b == a:
+            continue
+        for h in range(spec.num_q_heads):
+            qd = q_i8[s, h].astype(np.float64) * float(q_s[s, h])
+            kd = kq[a:b, h // G].astype(np.float64) * ks[a:b, h // G, None]
+            p = sp_softmax(kd @ qd / math.sqrt(spec.head_dim))
+            out[s, h] = p @ vd[a:b, h // G]
+    return out
+
+
+def _decode_setup(spec):
+    inp = paged_inputs(spec)
+    c = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks, spec.v_int8)
+    q_i8, q_s = oracle.quantize_q(inp.q)
+    return inp, c, q_i8, q_s
+
+
+@pytest.mark.parametrize("G,d,v_int8", [(1, 64, False), (2, 128, True), (6, 64, False), (6, 256, True), (16, 64, False)])
+def test_decode_equals_textbook_attention_of_dequantized(G, d, v_int8):
+    spec = _small_spec(num_q_heads=2 * G, num_kv_heads=2, head_dim=d, v_int8=v_int8,
+                       context_lens=[17, 1, 100], pool_blocks=20)
+    inp, c, q_i8, q_s = _decode_setup(spec)
+    got = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2)
+    want = _textbook_decode(inp, spec, v_int8)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_softmax_rows_sum_to_one_via_one_hot_v():
+    # V[t] = e_t makes the output row equal the probability row.
+    ctx, d = 40, 64
+    spec = PagedSpec("oh", 31, 1, 6, 1, d, [ctx], [1], k_bias_std=1.0, pool_blocks=5)
+    inp = paged_inputs(spec)
+    v = np.zeros((ctx, 1, d), np.float32)
+    v[np.arange(ctx), 0, np.arange(ctx)] = 1.0
+    c = oracle.write_kv_cache(inp.k, to_bf16_bits(v), "bf16", inp.slot_mapping, spec.num_blocks)
+    q_i8, q_s = oracle.quantize_q(inp.q)
+    out = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 1)[0]
+    np.testing.assert_allclose(out.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(out[:, :ctx] > 0) and np.all(out[:, ctx:] == 0)
+    # the probabilities themselves: scipy softmax of brute-force scores
+    acc = oracle.paged_qk_int32(q_i8, c, inp.block_tables, inp.context_lens, 1)[0]
+    kq, ks = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    sc = acc * q_s[0][:, None].astype(np.float64) * ks[:, 0][None].astype(np.float64) / 8.0
+    np.testing.assert_allclose(out[:, :ctx], sp_softmax(sc, axis=1), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("S", [1, 2, 8, 33])
+def test_split_equals_unsplit(S):
+    spec = _small_spec(num_q_heads=12, num_kv_heads=2, head_dim=64, context_lens=[17, 1, 300],
+                       v_int8=True, pool_blocks=30)
+    inp, c, q_i8, q_s = _decode_setup(spec)
+    a = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2)
+    b = oracle.paged_decode_split(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2, S)
+    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-14)
+
+
+def test_split_segments_cover_context():
+    from oracle.attention import split_segments
+    for ctx in [0, 1, 15, 16, 17, 255, 256, 1000]:
+        for S in [1, 2, 3, 8, 33]:
+            segs = split_segments(ctx, S)
+            assert len(segs) == S
+            covered = [t for a, b in segs for t in range(a, b)]
+            assert covered == list(range(ctx))
+            assert all(a % 16 == 0 for a, b in segs if b > a)
+
+
+def test_decode_empty_context_is_zero():
+    spec = _small_spec(context_lens=[0, 5, 0], pool_blocks=3)
+    inp, c, q_i8, q_s = _decode_setup(spec)
+    out = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0) and np.all(np.isfinite(out))
+
+
+def test_decode_single_token_returns_its_value():
+    spec = _small_spec(context_lens=[1, 1, 1], pool_blocks=3)
+    inp, c, q_i8, q_s = _decode_setup(spec)
+    out = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2)
+    vv = oq.widen(inp.v, "bf16").astype(np.float64)
+    for s in range(3):
+        for h in range(6):
+            np.testing.assert_array_equal(out[s, h], vv[s, h // 3])
+
+
+def test_decode_scale_recovery_is_before_softmax():
+    # doubling every K scale must change probabilities, not just rescale
+    # the scores after softmax ([QK-MMAC] §1).
+    spec = _small_spec(context_lens=[64, 64, 64], pool_blocks=12)
+    inp, c, q_i8, q_s = _decode_setup(spec)
+    a = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2)
+    c2 = dict(c)
+    c2["k_scale"] = c["k_scale"] * np.float32(2)
+    b = oracle.paged_decode(q_i8, q_s, c2, inp.block_tables, inp.context_lens, 2)
+    assert np.max(np.abs(a - b)) > 1e-3
+    b2 = oracle.paged_decode(q_i8, q_s, c, inp.block_tables, inp.context_lens, 2, scale=2 / 8.0)
+    np.testing.assert_allclose(b, b2, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# chunked prefill
+# --------------------------------------------------------------------------
+
+def _prefill_setup(ctxs, qls, G=3, d=64, seed=41):
+    spec = PagedSpec("pf", seed, len(ctxs), 2 * G, 2, d, ctxs, qls, k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    c = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks)
+    q_i8, q_s = oracle.quantize_q(inp.q)
+    return spec, inp, c, q_i8, q_s
+
+
+def test_prefill_equals_textbook_masked_attention():
+    spec, inp, c, q_i8, q_s = _prefill_setup([50, 37], [20, 37])
+    got = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c,
+                                 inp.block_tables, 2)
+    kq, ks = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    vd = oq.widen(inp.v, "bf16").astype(np.float64)
+    G = spec.group
+    for s in range(2):
+        a, b = int(inp.cu_seqlens_kv[s]), int(inp.cu_seqlens_kv[s + 1])
+        qa, qb = int(inp.cu_seqlens_q[s]), int(inp.cu_seqlens_q[s + 1])
+        ctx, tq = b - a, qb - qa
+        for i in range(tq):
+            pos = ctx - tq + i
+            for h in range(spec.num_q_heads):
+                qd = q_i8[qa + i, h].astype(np.float64) * float(q_s[qa + i, h])
+                kd = kq[a:a + pos + 1, h // G].astype(np.float64) * ks[a:a + pos + 1, h // G, None]
+                p = sp_softmax(kd @ qd / 8.0)
+                np.testing.assert_allclose(got[qa + i, h], p @ vd[a:a + pos + 1, h // G],
+                                           rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_last_row_equals_decode_and_first_row_of_fresh_chunk():
+    spec, inp, c, q_i8, q_s = _prefill_setup([70], [70])
+    got = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c,
+                                 inp.block_tables, 2)
+    # last chunk row sees the whole context = a decode step with that query
+    dec = oracle.paged_decode(q_i8[-1:], q_s[-1:], c, inp.block_tables, inp.context_lens, 2)
+    np.testing.assert_allclose(got[-1], dec[0], rtol=1e-12, atol=1e-14)
+    # with no history, the first row sees only key 0: output = V[0] exactly
+    vv = oq.widen(inp.v, "bf16").astype(np.float64)
+    for h in range(6):
+        np.testing.assert_array_equal(got[0, h], vv[0, h // 3])
+
+
+def test_prefill_row_subset_matches_full():
+    spec, inp, c, q_i8, q_s = _prefill_setup([90], [33])
+    full = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    part = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2,
+                                  rows=[0, 7, 32], heads=[1, 4])
+    for r in [0, 7, 32]:
+        for h in [1, 4]:
+            np.testing.assert_array_equal(part[r, h], full[r, h])
+
+
+# --------------------------------------------------------------------------
+# dense SageAttention-style path
+# --------------------------------------------------------------------------
+
+def _dense(B=1, H=2, Hkv=2, N=200, Nk=None, d=64, dtype="f16", seed=51, bias=3.0):
+    spec = DenseSpec("d", seed, B, H, Hkv, N, Nk or N, d, k_bias_std=bias, dtype=dtype)
+    return spec, dense_inputs(spec)
+
+
+def test_sage_mean_is_exact_sum():
+    spec, inp = _dense(N=300)
+    qz = oracle.sage_quantize(inp.q, inp.k, "f16")
+    k = oq.widen(inp.k, "f16")
+    for h in range(2):
+        for ch in range(0, 64, 7):
+            tot = sum(Fraction(float(x)) for x in k[0, :, h, ch])
+            assert qz["k_mean"][0, h, ch] == np.float32(float(tot / 300))
+
+
+def test_sage_per_block_scales_brute_force():
+    spec, inp = _dense(N=200)
+    qz = oracle.sage_quantize(inp.q, inp.k, "f16")
+    q = oq.widen(inp.q, "f16")
+    ks = (oq.widen(inp.k, "f16") - qz["k_mean"][:, None]).astype(np.float32)
+    for h in range(2):
+        for j, (a, b) in enumerate([(0, 128), (128, 200)]):
+            amax = max(abs(float(x)) for x in q[0, a:b, h].ravel())
+            assert qz["q_scale"][0, h, j] == _nearest_f32(Fraction(amax) / 127)
+        for j, (a, b) in enumerate([(0, 64), (64, 128), (128, 192), (192, 200)]):
+            amax = max(abs(float(x)) for x in ks[0, a:b, h].ravel())
+            assert qz["k_scale"][0, h, j] == _nearest_f32(Fraction(amax) / 127)
+            blk = ks[0, a:b, h]
+            codes = qz["k_i8"][0, a:b, h]
+            assert np.max(np.abs(codes)) == 127
+            assert np.all(np.abs(blk - codes * qz["k_scale"][0, h, j]) <= qz["k_scale"][0, h, j] * 0.50001)
+
+
+@pytest.mark.parametrize("causal,Nk", [(False, None), (True, None), (True, 260), (False, 70)])
+def test_dense_equals_textbook_attention_of_dequantized(causal, Nk):
+    spec, inp = _dense(B=2, H=4, Hkv=2, N=150, Nk=Nk)
+    qz = oracle.sage_quantize(inp.q, inp.k, "f16")
+    got = oracle.dense_sage_attention(qz, inp.v, "f16", causal=causal)
+    Nq, Nk_ = spec.seq_q, spec.seq_k
+    v = oq.widen(inp.v, "f16").astype(np.float64)
+    for b in range(2):
+        for h in range(4):
+            kvh = h // 2
+            qd = qz["q_i8"][b, :, h].astype(np.float64) * np.repeat(qz["q_scale"][b, h], 128)[:Nq, None]
+            kd = qz["k_i8"][b, :, kvh].astype(np.float64) * np.repeat(qz["k_scale"][b, kvh], 64)[:Nk_, None]
+            s = qd @ kd.T / 8.0
+            if causal:
+                s = np.where(np.arange(Nk_)[None] <= np.arange(Nq)[:, None] + (Nk_ - Nq), s, -np.inf)
+            p = sp_softmax(s, axis=1)
+            p = np.nan_to_num(p)
+            np.testing.assert_allclose(got[b, :, h], p @ v[b, :, kvh], rtol=1e-12, atol=1e-13)
+
+
+def test_dense_causal_first_row_is_first_value():
+    spec, inp = _dense(N=130)
+    qz = oracle.sage_quantize(inp.q, inp.k, "f16")
+    got = oracle.dense_sage_attention(qz, inp.v, "f16", causal=True)
+    v = oq.widen(inp.v, "f16").astype(np.float64)
+    np.testing.assert_array_equal(got[0, 0], v[0, 0])
+
+
+def test_smoothing_leaves_unquantized_attention_unchanged():
+    # softmax is invariant to adding q.mu to every score of a row
+    spec, inp = _dense(N=100, d=64)
+    q = oq.widen(inp.q, "f16").astype(np.float64)[0, :, 0]
+    k = oq.widen(inp.k, "f16").astype(np.float64)[0, :, 0]
+    v = oq.widen(inp.v, "f16").astype(np.float64)[0, :, 0]
+    mu = k.mean(axis=0)
+    a = sp_softmax(q @ k.T / 8.0, axis=1) @ v
+    b = sp_softmax(q @ (k - mu).T / 8.0, axis=1) @ v
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
+def test_smoothing_reduces_quantization_error():
+    # with a strong channel bias, smoothing K lowers the error against
+    # unquantized attention ([SAGE-MACA] presents smooth_k as outlier removal)
+    spec, inp = _dense(N=256, d=64, bias=6.0)
+    ref = np.zeros((256, 2, 64))
+    q = oq.widen(inp.q, "f16").astype(np.float64)[0]
+    k = oq.widen(inp.k, "f16").astype(np.float64)[0]
+    v = oq.widen(inp.v, "f16").astype(np.float64)[0]
+    for h in range(2):
+        ref[:, h] = sp_softmax(q[:, h] @ k[:, h].T / 8.0, axis=1) @ v[:, h]
+    errs = []
+    for smooth in (False, True):
+        qz = oracle.sage_quantize(inp.q, inp.k, "f16", smooth_k=smooth)
+        o = oracle.dense_sage_attention(qz, inp.v, "f16")[0]
+        errs.append(np.linalg.norm(o - ref) / np.linalg.norm(ref))
+    assert errs[1] < errs[0]
+
+
+def test_attention_fp64_matches_scipy():
+    rng = np.random.default_rng(3)
+    q, k, v = rng.standard_normal((3, 20, 16))
+    got = oracle.attention_fp64(q, k, v, 0.25)
+    np.testing.assert_allclose(got, sp_softmax(q @ k.T * 0.25, axis=1) @ v, rtol=1e-13)

@@ -1,0 +1,251 @@
+"""Seeded synthetic workloads for INT8-QK paged and dense attention.
+
+This module only draws inputs. It holds none of the method's arithmetic:
+no quantization, no scores, no softmax. It is shared by the CPU oracle
+tests and the GPU path (tests, benchmark), so both sides consume the
+same bit patterns.
+
+Every draw comes from ``numpy.random.default_rng`` seeded with a tuple
+``(config_seed, stream, index)``, so one sequence's data can be
+regenerated without drawing the others.
+
+Distributions follow the workloads the pages measure on: Qwen3.5-27B
+attention shapes (24 query heads, 4 KV heads, head_dim 256) and the
+SageAttention dense setting. Real activations are not available, so K
+gets a per-(head, channel) bias to imitate the channel outliers that
+motivate smoothing. "N(0, s)" is read as standard deviation s.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+# ---------------------------------------------------------------------------
+# float32 draws -> 16-bit storage formats (round to nearest even)
+# ---------------------------------------------------------------------------
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the
+    raw 16-bit patterns as uint16. Inputs are finite draws."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE half (numpy's cast is round-to-nearest-even);
+    return the raw 16-bit patterns as uint16."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of 16-bit patterns to float32 (for reporting only)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float32)
+    raise ValueError(dtype)
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng(list(key))
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return to_bf16_bits(x) if dtype == "bf16" else to_f16_bits(x)
+
+
+# ---------------------------------------------------------------------------
+# Paged workloads (decode and chunked prefill)
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class PagedSpec:
+    """Shape of a paged-attention workload."""
+    name: str
+    seed: int
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    context_lens: list            # KV length per sequence (incl. new tokens)
+    query_lens: list              # new query tokens per sequence (1 = decode)
+    k_bias_std: float = 0.0       # std of the per-(kv head, channel) K bias
+    v_int8: bool = False          # V cache stored as INT8 + per-token scale
+    num_splits: int = 1
+    dtype: str = "bf16"
+    pool_blocks: Optional[int] = None   # physical pool; default = blocks needed
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def blocks_per_seq(self) -> list:
+        return [-(-c // BLOCK_SIZE) for c in self.context_lens]
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return max(max(self.blocks_per_seq), 1)
+
+    @property
+    def num_blocks(self) -> int:
+        need = sum(self.blocks_per_seq)
+        return max(self.pool_blocks or need, need, 1)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.query_lens))
+
+
+@dataclass
+class PagedInputs:
+    spec: PagedSpec
+    q: np.ndarray                 # [total_q, Hq, d] uint16 bits
+    k: np.ndarray                 # [total_kv, Hkv, d] uint16 bits (all tokens of all seqs)
+    v: np.ndarray                 # [total_kv, Hkv, d] uint16 bits
+    slot_mapping: np.ndarray      # [total_kv] int64: block * 16 + offset
+    block_tables: np.ndarray      # [num_seqs, max_blocks_per_seq] int32
+    context_lens: np.ndarray      # [num_seqs] int32
+    cu_seqlens_q: np.ndarray      # [num_seqs + 1] int32
+    cu_seqlens_kv: np.ndarray     # [num_seqs + 1] int64 (token offsets into k/v)
+    k_bias: np.ndarray = field(default=None)  # [Hkv, d] float32 (reporting)
+
+
+def paged_inputs(spec: PagedSpec, seqs: Optional[list] = None) -> PagedInputs:
+    """Draw a paged workload. Block tables are slices of one seeded
+    permutation of the physical pool, so logical blocks of one sequence
+    land on scattered physical blocks.
+
+    ``seqs`` restricts the K/V/Q draws to a subset of sequences (others are
+    left as zeros); tables and lengths are always complete. Each sequence
+    uses its own generator stream, so a subset equals the full draw there.
+    """
+    S, Hq, Hkv, d = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    assert len(spec.context_lens) == S and len(spec.query_lens) == S
+    nb = spec.num_blocks
+    perm = _rng(spec.seed, 0).permutation(nb).astype(np.int32)
+    mb = spec.max_blocks_per_seq
+    tables = np.zeros((S, mb), np.int32)
+    pos = 0
+    for s, nbs in enumerate(spec.blocks_per_seq):
+        tables[s, :nbs] = perm[pos:pos + nbs]
+        pos += nbs
+    bias = (_rng(spec.seed, 1).standard_normal((Hkv, d), dtype=np.float32)
+            * np.float32(spec.k_bias_std)).astype(np.float32)
+    ctx = np.asarray(spec.context_lens, np.int64)
+    cu_kv = np.zeros(S + 1, np.int64)
+    cu_kv[1:] = np.cumsum(ctx)
+    cu_q = np.zeros(S + 1, np.int32)
+    cu_q[1:] = np.cumsum(np.asarray(spec.query_lens, np.int64))
+    total_kv = int(cu_kv[-1])
+    k = np.zeros((total_kv, Hkv, d), np.uint16)
+    v = np.zeros((total_kv, Hkv, d), np.uint16)
+    q = np.zeros((int(cu_q[-1]), Hq, d), np.uint16)
+    slots = np.zeros(total_kv, np.int64)
+    for s in range(S):
+        c = int(ctx[s])
+        t = np.arange(c, dtype=np.int64)
+        slots[cu_kv[s]:cu_kv[s + 1]] = tables[s, t // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + t % BLOCK_SIZE
+        if seqs is not None and s not in seqs:
+            continue
+        g = _rng(spec.seed, 2, s)
+        kf = g.standard_normal((c, Hkv, d), dtype=np.float32) + bias[None]
+        k[cu_kv[s]:cu_kv[s + 1]] = _store(kf, spec.dtype)
+        del kf
+        v[cu_kv[s]:cu_kv[s + 1]] = _store(g.standard_normal((c, Hkv, d), dtype=np.float32), spec.dtype)
+        q[cu_q[s]:cu_q[s + 1]] = _store(
+            g.standard_normal((spec.query_lens[s], Hq, d), dtype=np.float32), spec.dtype)
+    return PagedInputs(spec, q, k, v, slots, tables, ctx.astype(np.int32), cu_q, cu_kv, bias)
+
+
+# ---------------------------------------------------------------------------
+# Dense (SageAttention-style) workloads
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class DenseSpec:
+    name: str
+    seed: int
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    seq_q: int
+    seq_k: int
+    head_dim: int
+    k_bias_std: float = 0.0
+    dtype: str = "f16"
+    layout: str = "NHD"
+
+
+@dataclass
+class DenseInputs:
+    spec: DenseSpec
+    q: np.ndarray   # NHD: [B, Nq, Hq, d] uint16 bits
+    k: np.ndarray   # [B, Nk, Hkv, d]
+    v: np.ndarray   # [B, Nk, Hkv, d]
+
+
+def dense_inputs(spec: DenseSpec) -> DenseInputs:
+    """Q, V ~ N(0,1); K ~ N(0,1) + bias[head, channel], bias ~ N(0, k_bias_std).
+    Stored NHD (batch, seq, head, dim)."""
+    B, Hq, Hkv, d = spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    bias = _rng(spec.seed, 1).standard_normal((Hkv, d), dtype=np.float32) * np.float32(spec.k_bias_std)
+    q = np.empty((B, spec.seq_q, Hq, d), np.uint16)
+    k = np.empty((B, spec.seq_k, Hkv, d), np.uint16)
+    v = np.empty((B, spec.seq_k, Hkv, d), np.uint16)
+    for b in range(B):
+        g = _rng(spec.seed, 2, b)
+        q[b] = _store(g.standard_normal((spec.seq_q, Hq, d), dtype=np.float32), spec.dtype)
+        k[b] = _store(g.standard_normal((spec.seq_k, Hkv, d), dtype=np.float32) + bias[None], spec.dtype)
+        v[b] = _store(g.standard_normal((spec.seq_k, Hkv, d), dtype=np.float32), spec.dtype)
+    return DenseInputs(spec, q, k, v)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------
+
+
+def tiny_decode() -> PagedSpec:
+    """Batch 1, one query token, 6 query heads over 1 KV head, head_dim 64,
+    context 256: 16 blocks of 16 tokens in permuted order."""
+    return PagedSpec("tiny_decode", 1, 1, 6, 1, 64, [256], [1])
+
+
+def qwen27b_decode(context: int = 32768) -> PagedSpec:
+    """Qwen3.5-27B full-attention shape: 24 query heads, 4 KV heads (GQA 6:1),
+    head_dim 256, one query token over `context` cached tokens. K has a
+    per-channel bias of std 2. The pool holds exactly the blocks in use."""
+    return PagedSpec("qwen27b_decode", 2, 1, 24, 4, 256, [context], [1], k_bias_std=2.0)
+
+
+def batched_splitk_decode(num_seqs: int = 32, lo: int = 1024, hi: int = 32768,
+                          num_splits: int = 8) -> PagedSpec:
+    """32 sequences with context lengths uniform on [1024, 32768] (integers, so
+    most tails are partial blocks), 24/4 heads, head_dim 256, INT8 K and V,
+    8 split-K segments per sequence."""
+    ctx = _rng(3, 9).integers(lo, hi + 1, size=num_seqs).tolist()
+    return PagedSpec("batched_splitk_decode", 3, num_seqs, 24, 4, 256, ctx, [1] * num_seqs,
+                     k_bias_std=2.0, v_int8=True, num_splits=num_splits)
+
+
+def chunked_prefill(history: int = 16384, chunk: int = 2048) -> PagedSpec:
+    """One sequence: `chunk` new query tokens after `history` cached tokens;
+    the KV length is history + chunk and the chunk attends causally."""
+    return PagedSpec("chunked_prefill", 4, 1, 24, 4, 256, [history + chunk], [chunk], k_bias_std=2.0)
+
+
+def dense_sage(seq: int = 8192, batch: int = 2, heads: int = 32, head_dim: int = 128) -> DenseSpec:
+    """SageAttention-style dense forward: batch 2, 32 heads (1:1), seq 8192,
+    head_dim 128, NHD, fp16 Q/K/V; K has a per-channel bias of std 3."""
+    return DenseSpec("dense_sage", 5, batch, heads, heads, seq, seq, head_dim, k_bias_std=3.0)
