@@ -1,0 +1,283 @@
+/*
+ * qattn.h - C ABI of the INT8-QK quantized attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow:
+ *   [QK-MMAC]   "INT8 QK MMAC on the gfx936 DCU: paged access, fragment
+ *               mapping and GQA" (forum article).
+ *   [SAGE-MACA] "SageAttention - MetaX MXMACA port (v3.0.0)" README.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or synchronizes; buffers must stay valid until
+ *     the work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is queued asynchronously on it, in call order.
+ *   - Host-side argument checks run before any HIP call. A non-zero status
+ *     means nothing was queued; qa_last_error() describes the problem.
+ *   - Device-data preconditions are documented but not checked: block-table
+ *     entries lie in [0, num_blocks), context_lens[s] <= max_blocks_per_seq *
+ *     block_size, cache slots written by one call are distinct, and inputs
+ *     are finite. Violating them gives unspecified results.
+ *   - Supported shapes: head_dim in {64, 128, 256}; block_size 16; in paged
+ *     paths num_q_heads % num_kv_heads == 0 with a group of at most 16 query
+ *     heads per KV head. Other valid shapes return QA_ERR_UNSUPPORTED rather
+ *     than run with a wrong mapping ([QK-MMAC] §7 applicability guards).
+ */
+#ifndef QATTN_H
+#define QATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QA_ABI_VERSION 1
+
+typedef enum {
+  QA_OK = 0,
+  QA_ERR_INVALID_ARG = 1,        /* null pointer, bad shape, stride or dtype */
+  QA_ERR_UNSUPPORTED = 2,        /* valid request outside the supported set  */
+  QA_ERR_WORKSPACE_TOO_SMALL = 3,
+  QA_ERR_HIP = 4                 /* a HIP launch reported an error           */
+} qa_status_t;
+
+typedef enum {
+  QA_DT_BF16 = 0,
+  QA_DT_F16 = 1,
+  QA_DT_F32 = 2,
+  QA_DT_I8 = 3
+} qa_dtype_t;
+
+typedef void* qa_stream_t;       /* hipStream_t */
+
+/* ABI version of the loaded library (QA_ABI_VERSION at build time). */
+int qa_abi_version(void);
+
+/* Message for the last non-zero status returned on the calling thread.
+ * The string is owned by the library and valid until the next call. */
+const char* qa_last_error(void);
+
+/*
+ * Per-row symmetric dynamic INT8 quantization of the query.
+ * [QK-MMAC] §1 (one scale per query token and query head), §4 (scale =
+ * max|x| / 127, code = round(x / scale), done once before attention and
+ * reused by all split-K segments), §2.1 (codes in [-127, 127]).
+ *
+ * Arithmetic per row of head_dim values x (bf16/f16 widened exactly):
+ *   s = fl32(max|x| / 127);  q = clamp(rne(fl32(x / s)), -127, 127)
+ * with IEEE-correctly-rounded fp32 divisions and ties to even. A row whose
+ * max|x| is 0 gets s = 0 and zero codes.
+ *
+ *   q        [num_tokens, num_heads, head_dim] bf16 or f16 (dtype), element
+ *            (t, h, i) at q + t*stride_token + h*stride_head + i (strides in
+ *            elements; the innermost stride is 1)
+ *   q_i8     out [num_tokens, num_heads, head_dim] int8, contiguous
+ *   q_scale  out [num_tokens, num_heads] fp32, contiguous
+ * num_tokens == 0 is a no-op.
+ */
+qa_status_t qa_quantize_q(const void* q, qa_dtype_t dtype, int64_t num_tokens,
+                          int32_t num_heads, int32_t head_dim, int64_t stride_token,
+                          int64_t stride_head, int8_t* q_i8, float* q_scale,
+                          qa_stream_t stream);
+
+/*
+ * Quantize K (and optionally V) per (token, KV head) and write the tokens
+ * into the paged cache. [QK-MMAC] §1 (key scale per key token and KV head),
+ * §3 (K cache layout [block, kv_head, head_dim/16, block_size, 16]).
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim] bf16/f16 (dtype); element
+ *                 (t, h, i) at base + t*stride_token + h*stride_head + i
+ *   slot_mapping  [num_tokens] int64: slot = block * block_size + offset;
+ *                 a negative slot skips the token
+ *   k_cache       [num_blocks, num_kv_heads, head_dim/16, block_size, 16] int8
+ *   k_scale       [num_blocks, num_kv_heads, block_size] fp32
+ *   v_cache       [num_blocks, num_kv_heads, head_dim, block_size]: each
+ *                 channel's tokens of a block are contiguous. v_cache_dtype is
+ *                 the input dtype (V copied bit for bit) or QA_DT_I8 (V
+ *                 quantized like K, codes here and scales in v_scale)
+ *   v_scale       [num_blocks, num_kv_heads, block_size] fp32; NULL unless
+ *                 v_cache_dtype == QA_DT_I8
+ * Only the written slots change. block_size must be 16.
+ */
+qa_status_t qa_write_kv_cache(const void* k, const void* v, qa_dtype_t dtype,
+                              int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int64_t stride_token, int64_t stride_head,
+                              const int64_t* slot_mapping, int64_t num_blocks,
+                              int32_t block_size, int8_t* k_cache, float* k_scale,
+                              void* v_cache, qa_dtype_t v_cache_dtype, float* v_scale,
+                              qa_stream_t stream);
+
+/* Shape and options of a decode call (one query token per sequence). */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;          /* must be 16 */
+  int32_t max_blocks_per_seq;  /* row length of block_tables */
+  int64_t num_blocks;          /* physical blocks in the pool */
+  qa_dtype_t v_cache_dtype;    /* QA_DT_BF16 or QA_DT_I8 */
+  qa_dtype_t out_dtype;        /* QA_DT_F32 or QA_DT_BF16 */
+  float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t num_splits;          /* split-K segments per sequence; 0 = choose */
+} qa_decode_params_t;
+
+/* Number of split-K segments a decode call with these parameters uses. */
+int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p);
+
+/* Workspace bytes a decode call needs (0 when it runs unsplit). */
+size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
+
+/*
+ * Paged decode attention with INT8 Q x INT8 K.
+ * [QK-MMAC] §1: score = acc_int32 * sQ(query head) * sK(key token, KV head)
+ * * softmax_scale, recovered per element before the online softmax; §2.1-2.2:
+ * INT8 matrix instructions with INT32 accumulation; §3: K read through the
+ * block table in its INT8 paged layout; §4: long contexts are cut into
+ * segments (split-K) that reuse one quantized query; §5.1: the query heads
+ * of one KV head share the matrix rows. P.V uses fp16 matrix instructions
+ * with fp32 accumulation (P rounded to fp16; bf16 V widened to fp16; INT8 V
+ * as codes with sV folded into P).
+ *
+ * Split-K: segment j of a sequence with ctx tokens covers tokens
+ * [j*L, min((j+1)*L, ctx)) with L = 16 * ceil(ceil(ctx/16) / S). Each segment
+ * stores (max, sum, unnormalized output) in the workspace and a combine
+ * step merges them. S = 1 writes the output directly.
+ *
+ *   q_i8          [num_seqs, num_q_heads, head_dim] int8 (from qa_quantize_q)
+ *   q_scale       [num_seqs, num_q_heads] fp32
+ *   k_cache, k_scale, v_cache, v_scale   as written by qa_write_kv_cache
+ *                 (v_scale NULL unless v_cache_dtype == QA_DT_I8)
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids
+ *   context_lens  [num_seqs] int32 visible keys per sequence (0 gives zeros)
+ *   workspace     device scratch of >= qa_paged_decode_workspace_size bytes
+ *   out           [num_seqs, num_q_heads, head_dim] fp32 or bf16
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t* q_i8,
+                                      const float* q_scale, const int8_t* k_cache,
+                                      const float* k_scale, const void* v_cache,
+                                      const float* v_scale, const int32_t* block_tables,
+                                      const int32_t* context_lens, void* workspace,
+                                      size_t workspace_bytes, void* out, qa_stream_t stream);
+
+/*
+ * Test hook: runs the decode kernel's own block-table gather and INT8
+ * matrix product and stores the raw INT32 accumulators, so they can be
+ * compared bit for bit. acc_out [num_seqs, num_q_heads, max_blocks_per_seq *
+ * block_size] int32; entries at or beyond context_lens[s] are left untouched.
+ * [QK-MMAC] §7 (validation layer checking the fragment mapping over full
+ * head_dim, paging and scales).
+ */
+qa_status_t qa_debug_paged_qk_int32(const qa_decode_params_t* p, const int8_t* q_i8,
+                                    const int8_t* k_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t* acc_out,
+                                    qa_stream_t stream);
+
+/* Shape and options of a chunked-prefill call. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;          /* must be 16 */
+  int32_t max_blocks_per_seq;
+  int64_t num_blocks;
+  int64_t total_q;             /* rows of q_i8 = cu_seqlens_q[num_seqs] */
+  int32_t max_seqlen_q;        /* >= every cu_seqlens_q[s+1] - cu_seqlens_q[s] */
+  qa_dtype_t v_cache_dtype;    /* QA_DT_BF16 or QA_DT_I8 */
+  qa_dtype_t out_dtype;        /* QA_DT_F32 or QA_DT_BF16 */
+  float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
+} qa_prefill_params_t;
+
+/*
+ * Chunked prefill over a paged history ([QK-MMAC] §5.2: matrix rows are
+ * query tokens, one query head at a time, KV head = query head / G; the
+ * query is quantized before attention, §4). Sequence s has
+ * Tq = cu_seqlens_q[s+1] - cu_seqlens_q[s] new tokens, which are the last Tq
+ * of its context_lens[s] cached tokens (so the chunk must already be written
+ * to the cache). Query i of the chunk sits at position ctx - Tq + i and sees
+ * keys t <= that position.
+ *
+ *   q_i8, q_scale  [total_q, num_q_heads, head_dim] int8, [total_q, num_q_heads] fp32
+ *   cu_seqlens_q   [num_seqs + 1] int32, non-decreasing, starting at 0
+ *   context_lens   [num_seqs] int32 (>= the sequence's Tq)
+ *   out            [total_q, num_q_heads, head_dim] fp32 or bf16
+ */
+qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int8_t* q_i8,
+                                         const float* q_scale, const int32_t* cu_seqlens_q,
+                                         const int32_t* context_lens, const int8_t* k_cache,
+                                         const float* k_scale, const void* v_cache,
+                                         const float* v_scale, const int32_t* block_tables,
+                                         void* out, qa_stream_t stream);
+
+/* Shape and options of a dense SageAttention-style call (NHD layout). */
+typedef struct {
+  int32_t batch;
+  int32_t seq_q;
+  int32_t seq_k;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  qa_dtype_t dtype;            /* Q, K, V: QA_DT_F16 or QA_DT_BF16 */
+  int32_t smooth_k;            /* 1 = subtract the per-channel K mean */
+  int32_t is_causal;
+  float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
+  qa_dtype_t out_dtype;        /* QA_DT_F32, QA_DT_F16 or QA_DT_BF16 */
+} qa_dense_params_t;
+
+/* Query rows per quantization block and key rows per block. */
+#define QA_SAGE_Q_BLOCK 128
+#define QA_SAGE_K_BLOCK 64
+
+/*
+ * SageAttention-style preprocessing ([SAGE-MACA] feature matrix "smooth_k";
+ * quantization-kernel table; "per_block" granularity). With smooth_k the
+ * per-(batch, KV head, channel) mean of K over all seq_k tokens is
+ * accumulated exactly in fp64, divided by seq_k in fp64 and rounded to fp32
+ * (mu); K' = fl32(K - mu). Q is quantized per block of QA_SAGE_Q_BLOCK rows of
+ * one (batch, head), K' per block of QA_SAGE_K_BLOCK rows, each block with one
+ * scale computed over all its rows x head_dim values (same rounding rule as
+ * qa_quantize_q; the last block takes the remaining rows).
+ *
+ *   q [batch, seq_q, num_q_heads, head_dim], k [batch, seq_k, num_kv_heads, head_dim]
+ *   q_i8    out, same shape as q, int8
+ *   q_scale out [batch, num_q_heads, ceil(seq_q / 128)] fp32
+ *   k_i8    out, same shape as k, int8
+ *   k_scale out [batch, num_kv_heads, ceil(seq_k / 64)] fp32
+ *   k_mean  out [batch, num_kv_heads, head_dim] fp32 (zeros without smooth_k)
+ *   workspace  >= qa_dense_sage_quantize_workspace_size bytes (fp64 partial sums)
+ */
+size_t qa_dense_sage_quantize_workspace_size(const qa_dense_params_t* p);
+qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, const void* k,
+                                   int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                                   float* k_scale, float* k_mean, void* workspace,
+                                   size_t workspace_bytes, qa_stream_t stream);
+
+/*
+ * Dense SageAttention-style forward ([SAGE-MACA] attention-kernel compute
+ * pipeline, path "accum_f32"): INT8 Q x INT8 K' to INT32, scaled by the
+ * query-block scale, the key-block scale and softmax_scale; online softmax in
+ * base 2; P.V with fp16 matrix instructions and fp32 accumulation; the
+ * causal mask is applied on the diagonal tiles only and tiles above the
+ * diagonal are skipped. Causal alignment is bottom-right: query i sees keys
+ * j <= i + (seq_k - seq_q). Runs the preprocessing above into the workspace
+ * first (full chain). num_q_heads % num_kv_heads == 0.
+ *
+ *   q, k, v   NHD bf16/f16 (dtype); v [batch, seq_k, num_kv_heads, head_dim]
+ *   out       [batch, seq_q, num_q_heads, head_dim] in out_dtype
+ *   workspace >= qa_dense_sage_workspace_size bytes
+ */
+size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p);
+qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, const void* k,
+                                    const void* v, void* workspace, size_t workspace_bytes,
+                                    void* out, qa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QATTN_H */

@@ -1,0 +1,263 @@
+"""Python binding of libqattn (INT8-QK quantized attention for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/qattn.h. Tensors are torch
+device tensors; the calls queue work on the current torch stream. Output
+tensors are allocated here with torch (plumbing), and the library itself
+never allocates.
+
+If the compiled library is missing this module raises at import: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libqattn.so not found at {LIB_PATH}; build it with "
+        "`python -m quantized_attention_quantize_amd.build` (hipcc, gfx950)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+# ---- C types ---------------------------------------------------------------
+QA_OK, QA_ERR_INVALID_ARG, QA_ERR_UNSUPPORTED, QA_ERR_WORKSPACE_TOO_SMALL, QA_ERR_HIP = range(5)
+QA_DT_BF16, QA_DT_F16, QA_DT_F32, QA_DT_I8 = range(4)
+SAGE_Q_BLOCK, SAGE_K_BLOCK = 128, 64
+
+_c_void_p, _i32, _i64, _f32, _size = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("block_size", _i32), ("max_blocks_per_seq", _i32), ("num_blocks", _i64),
+                ("v_cache_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("softmax_scale", _f32),
+                ("num_splits", _i32)]
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("block_size", _i32), ("max_blocks_per_seq", _i32), ("num_blocks", _i64), ("total_q", _i64),
+                ("max_seqlen_q", _i32), ("v_cache_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("softmax_scale", _f32)]
+
+
+class DenseParams(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("seq_q", _i32), ("seq_k", _i32), ("num_q_heads", _i32),
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", ctypes.c_int), ("smooth_k", _i32),
+                ("is_causal", _i32), ("softmax_scale", _f32), ("out_dtype", ctypes.c_int)]
+
+
+_P = ctypes.POINTER
+_SIGS = {
+    "qa_abi_version": (ctypes.c_int, []),
+    "qa_last_error": (ctypes.c_char_p, []),
+    "qa_quantize_q": (ctypes.c_int, [_c_void_p, ctypes.c_int, _i64, _i32, _i32, _i64, _i64, _c_void_p,
+                                      _c_void_p, _c_void_p]),
+    "qa_write_kv_cache": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i32, _i32, _i64, _i64,
+                                          _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, ctypes.c_int,
+                                          _c_void_p, _c_void_p]),
+    "qa_paged_decode_num_splits": (_i32, [_P(DecodeParams)]),
+    "qa_paged_decode_workspace_size": (_size, [_P(DecodeParams)]),
+    "qa_paged_attention_decode": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_size, _c_void_p,
+                                                                                           _c_void_p]),
+    "qa_debug_paged_qk_int32": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 6),
+    "qa_chunked_prefill_attention": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 11),
+    "qa_dense_sage_quantize_workspace_size": (_size, [_P(DenseParams)]),
+    "qa_dense_sage_quantize": (ctypes.c_int, [_P(DenseParams)] + [_c_void_p] * 8 + [_size, _c_void_p]),
+    "qa_dense_sage_workspace_size": (_size, [_P(DenseParams)]),
+    "qa_dense_sage_attention": (ctypes.c_int, [_P(DenseParams)] + [_c_void_p] * 4 + [_size, _c_void_p,
+                                                                                        _c_void_p]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class QAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"qattn status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != QA_OK:
+        raise QAttnError(status, lib.qa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.dtype) -> int:
+    return {torch.bfloat16: QA_DT_BF16, torch.float16: QA_DT_F16, torch.float32: QA_DT_F32,
+            torch.int8: QA_DT_I8}[t]
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+# ---- entry points ------------------------------------------------------------
+
+def quantize_q(q: torch.Tensor):
+    """q [T, H, d] bf16/f16 (innermost dim contiguous) -> (q_i8 [T, H, d], q_scale [T, H])."""
+    _require_cuda(q)
+    T, H, d = q.shape
+    q_i8 = torch.empty((T, H, d), dtype=torch.int8, device=q.device)
+    q_scale = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if q.stride(2) != 1:
+        raise ValueError("innermost dimension of q must be contiguous")
+    _check(lib.qa_quantize_q(_ptr(q), _dt(q.dtype), T, H, d, q.stride(0), q.stride(1), _ptr(q_i8),
+                             _ptr(q_scale), _stream()))
+    return q_i8, q_scale
+
+
+def alloc_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, v_dtype: torch.dtype,
+                   device="cuda", zero: bool = True):
+    """Cache tensors in the library's layout (see include/qattn.h)."""
+    mk = torch.zeros if zero else torch.empty
+    k_cache = mk((num_blocks, num_kv_heads, head_dim // 16, 16, 16), dtype=torch.int8, device=device)
+    k_scale = mk((num_blocks, num_kv_heads, 16), dtype=torch.float32, device=device)
+    v_cache = mk((num_blocks, num_kv_heads, head_dim, 16), dtype=v_dtype, device=device)
+    v_scale = mk((num_blocks, num_kv_heads, 16), dtype=torch.float32, device=device) \
+        if v_dtype == torch.int8 else None
+    return k_cache, k_scale, v_cache, v_scale
+
+
+def write_kv_cache(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale=None):
+    """Quantize K (and V if v_cache is int8) per (token, KV head) into the paged cache."""
+    _require_cuda(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale)
+    T, H, d = k.shape
+    if k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("k and v must share strides with a contiguous innermost dim")
+    _check(lib.qa_write_kv_cache(_ptr(k), _ptr(v), _dt(k.dtype), T, H, d, k.stride(0), k.stride(1),
+                                 _ptr(slot_mapping), k_cache.shape[0], 16, _ptr(k_cache), _ptr(k_scale),
+                                 _ptr(v_cache), _dt(v_cache.dtype), _ptr(v_scale), _stream()))
+
+
+def decode_params(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
+                  v_int8=False, out_dtype=torch.float32, softmax_scale=0.0, num_splits=0) -> DecodeParams:
+    return DecodeParams(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_blocks_per_seq, num_blocks,
+                        QA_DT_I8 if v_int8 else QA_DT_BF16, _dt(out_dtype), softmax_scale, num_splits)
+
+
+def decode_num_splits(p: DecodeParams) -> int:
+    return lib.qa_paged_decode_num_splits(ctypes.byref(p))
+
+
+def decode_workspace(p: DecodeParams, device="cuda") -> torch.Tensor:
+    n = lib.qa_paged_decode_workspace_size(ctypes.byref(p))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def paged_attention_decode(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
+                           num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
+                           workspace=None, out=None):
+    """Decode attention; returns out [num_seqs, Hq, d]."""
+    _require_cuda(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens)
+    S, Hq, d = q_i8.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    p = decode_params(S, Hq, Hkv, d, block_tables.shape[1], k_cache.shape[0], v_cache.dtype == torch.int8,
+                      out_dtype, softmax_scale, num_splits)
+    if workspace is None:
+        workspace = decode_workspace(p, q_i8.device)
+    if out is None:
+        out = torch.empty((S, Hq, d), dtype=out_dtype, device=q_i8.device)
+    _check(lib.qa_paged_attention_decode(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
+                                         _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(block_tables),
+                                         _ptr(context_lens), _ptr(workspace), workspace.numel(), _ptr(out),
+                                         _stream()))
+    return out
+
+
+def debug_paged_qk_int32(q_i8, k_cache, block_tables, context_lens, num_kv_heads=None, fill=0):
+    """INT32 QK accumulators of the decode kernel: [num_seqs, Hq, max_blocks*16]."""
+    _require_cuda(q_i8, k_cache, block_tables, context_lens)
+    S, Hq, d = q_i8.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    p = decode_params(S, Hq, Hkv, d, block_tables.shape[1], k_cache.shape[0])
+    acc = torch.full((S, Hq, block_tables.shape[1] * 16), fill, dtype=torch.int32, device=q_i8.device)
+    _check(lib.qa_debug_paged_qk_int32(ctypes.byref(p), _ptr(q_i8), _ptr(k_cache), _ptr(block_tables),
+                                       _ptr(context_lens), _ptr(acc), _stream()))
+    return acc
+
+
+def chunked_prefill_attention(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
+                              block_tables, max_seqlen_q, num_kv_heads=None, softmax_scale=0.0,
+                              out_dtype=torch.float32, out=None):
+    """Chunked prefill over the paged cache; returns out [total_q, Hq, d]."""
+    _require_cuda(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale, block_tables)
+    T, Hq, d = q_i8.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    p = PrefillParams(context_lens.shape[0], Hq, Hkv, d, 16, block_tables.shape[1], k_cache.shape[0], T,
+                      int(max_seqlen_q), QA_DT_I8 if v_cache.dtype == torch.int8 else QA_DT_BF16,
+                      _dt(out_dtype), softmax_scale)
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=out_dtype, device=q_i8.device)
+    _check(lib.qa_chunked_prefill_attention(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(cu_seqlens_q),
+                                            _ptr(context_lens), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                                            _ptr(v_scale), _ptr(block_tables), _ptr(out), _stream()))
+    return out
+
+
+def dense_params(q, k, smooth_k=True, is_causal=False, softmax_scale=0.0, out_dtype=None) -> DenseParams:
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    return DenseParams(B, Nq, Nk, Hq, Hkv, d, _dt(q.dtype), int(bool(smooth_k)), int(bool(is_causal)),
+                       softmax_scale, _dt(out_dtype or torch.float32))
+
+
+def dense_sage_quantize(q, k, smooth_k=True):
+    """NHD q, k -> dict(q_i8, q_scale, k_i8, k_scale, k_mean) (SageAttention-style preprocessing)."""
+    _require_cuda(q, k)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    p = dense_params(q, k, smooth_k)
+    dev = q.device
+    res = {
+        "q_i8": torch.empty((B, Nq, Hq, d), dtype=torch.int8, device=dev),
+        "q_scale": torch.empty((B, Hq, -(-Nq // SAGE_Q_BLOCK)), dtype=torch.float32, device=dev),
+        "k_i8": torch.empty((B, Nk, Hkv, d), dtype=torch.int8, device=dev),
+        "k_scale": torch.empty((B, Hkv, -(-Nk // SAGE_K_BLOCK)), dtype=torch.float32, device=dev),
+        "k_mean": torch.empty((B, Hkv, d), dtype=torch.float32, device=dev),
+    }
+    ws = torch.empty(max(lib.qa_dense_sage_quantize_workspace_size(ctypes.byref(p)), 16), dtype=torch.uint8,
+                     device=dev)
+    _check(lib.qa_dense_sage_quantize(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(res["q_i8"]), _ptr(res["q_scale"]),
+                                      _ptr(res["k_i8"]), _ptr(res["k_scale"]), _ptr(res["k_mean"]), _ptr(ws),
+                                      ws.numel(), _stream()))
+    return res
+
+
+def dense_sage_workspace(p: DenseParams, device="cuda") -> torch.Tensor:
+    return torch.empty(max(lib.qa_dense_sage_workspace_size(ctypes.byref(p)), 16), dtype=torch.uint8, device=device)
+
+
+def dense_sage_attention(q, k, v, is_causal=False, smooth_k=True, softmax_scale=0.0, out_dtype=torch.float32,
+                         workspace=None, out=None):
+    """SageAttention-style dense forward on NHD tensors; returns out [B, Nq, Hq, d]."""
+    _require_cuda(q, k, v)
+    p = dense_params(q, k, smooth_k, is_causal, softmax_scale, out_dtype)
+    if workspace is None:
+        workspace = dense_sage_workspace(p, q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _check(lib.qa_dense_sage_attention(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
+                                       workspace.numel(), _ptr(out), _stream()))
+    return out

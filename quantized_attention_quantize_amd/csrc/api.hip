@@ -1,0 +1,333 @@
+// C ABI: argument validation, workspace sizing and dispatch. Nothing here
+// allocates or synchronizes; all checks run before the first HIP call.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/qattn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+qa_status_t fail(qa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+qa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QA_OK;
+  return fail(QA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define QA_REQUIRE(cond, st, ...) \
+  do {                            \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+float log2_scale(float softmax_scale, int32_t d) {
+  const double s = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / std::sqrt((double)d);
+  return (float)(s * 1.4426950408889634);
+}
+
+qa_status_t check_decode(const qa_decode_params_t* p) {
+  QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
+  QA_REQUIRE(p->num_seqs >= 0 && p->num_q_heads > 0 && p->num_kv_heads > 0 && p->head_dim > 0,
+             QA_ERR_INVALID_ARG, "non-positive shape (num_seqs=%d, heads=%d/%d, head_dim=%d)",
+             p->num_seqs, p->num_q_heads, p->num_kv_heads, p->head_dim);
+  QA_REQUIRE(p->num_q_heads % p->num_kv_heads == 0, QA_ERR_INVALID_ARG,
+             "num_q_heads (%d) not a multiple of num_kv_heads (%d)", p->num_q_heads, p->num_kv_heads);
+  QA_REQUIRE(p->max_blocks_per_seq > 0 && p->num_blocks > 0, QA_ERR_INVALID_ARG,
+             "max_blocks_per_seq and num_blocks must be positive");
+  QA_REQUIRE(p->num_splits >= 0, QA_ERR_INVALID_ARG, "num_splits < 0");
+  QA_REQUIRE(p->v_cache_dtype == QA_DT_BF16 || p->v_cache_dtype == QA_DT_I8, QA_ERR_UNSUPPORTED,
+             "v_cache_dtype must be BF16 or I8");
+  QA_REQUIRE(p->out_dtype == QA_DT_F32 || p->out_dtype == QA_DT_BF16, QA_ERR_UNSUPPORTED,
+             "decode out_dtype must be F32 or BF16");
+  QA_REQUIRE(supported_dim(p->head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", p->head_dim);
+  QA_REQUIRE(p->block_size == 16, QA_ERR_UNSUPPORTED, "block_size %d != 16", p->block_size);
+  QA_REQUIRE(p->num_q_heads / p->num_kv_heads <= 16, QA_ERR_UNSUPPORTED,
+             "GQA group %d > 16 query heads per KV head", p->num_q_heads / p->num_kv_heads);
+  QA_REQUIRE(p->num_splits <= 65535, QA_ERR_UNSUPPORTED, "num_splits %d too large", p->num_splits);
+  QA_REQUIRE(p->num_seqs <= 65535 && p->num_kv_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
+  return QA_OK;
+}
+
+int32_t splits_of(const qa_decode_params_t* p) {
+  if (p->num_splits > 0) return p->num_splits;
+  return qa::choose_decode_splits(p->num_seqs, p->num_kv_heads, p->max_blocks_per_seq);
+}
+
+size_t decode_ws(const qa_decode_params_t* p, int32_t S) {
+  if (S <= 1) return 0;
+  const size_t units = (size_t)p->num_seqs * p->num_q_heads * S;
+  const size_t o = units * p->head_dim * sizeof(float);
+  return ((o + 255) & ~(size_t)255) + units * 2 * sizeof(float);
+}
+
+qa_status_t check_dense(const qa_dense_params_t* p) {
+  QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
+  QA_REQUIRE(p->batch >= 0 && p->seq_q >= 0 && p->seq_k >= 0 && p->num_q_heads > 0 &&
+                 p->num_kv_heads > 0 && p->head_dim > 0,
+             QA_ERR_INVALID_ARG, "bad dense shape");
+  QA_REQUIRE(p->num_q_heads % p->num_kv_heads == 0, QA_ERR_INVALID_ARG,
+             "num_q_heads (%d) not a multiple of num_kv_heads (%d)", p->num_q_heads, p->num_kv_heads);
+  QA_REQUIRE(p->dtype == QA_DT_F16 || p->dtype == QA_DT_BF16, QA_ERR_UNSUPPORTED, "dtype must be F16 or BF16");
+  QA_REQUIRE(p->out_dtype == QA_DT_F32 || p->out_dtype == QA_DT_F16 || p->out_dtype == QA_DT_BF16,
+             QA_ERR_UNSUPPORTED, "out_dtype must be F32, F16 or BF16");
+  QA_REQUIRE(supported_dim(p->head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", p->head_dim);
+  QA_REQUIRE(p->batch <= 65535 && p->num_q_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
+  return QA_OK;
+}
+
+// Dense workspace: [partial sums][q_i8][k blocks][v blocks][q_scale][k_scale][k_mean], 256-aligned.
+struct DenseWs {
+  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, total;
+};
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DenseWs dense_layout(const qa_dense_params_t* p, bool with_attention) {
+  DenseWs w{};
+  const size_t B = p->batch, Nq = p->seq_q, Nk = p->seq_k, Hq = p->num_q_heads, Hkv = p->num_kv_heads,
+               D = p->head_dim;
+  const size_t nb16 = (Nk + 15) / 16;
+  size_t off = 0;
+  w.partial = off; off += al(qa::sage_partial_bytes(p->batch, p->seq_k, p->num_kv_heads, p->head_dim));
+  if (with_attention) {
+    w.q_i8 = off; off += al(B * Nq * Hq * D);
+    w.k_blk = off; off += al(B * nb16 * Hkv * D * 16);
+    w.v_blk = off; off += al(B * nb16 * Hkv * D * 16 * 2);
+    w.q_scale = off; off += al(B * Hq * ((Nq + 127) / 128) * sizeof(float));
+    w.k_scale = off; off += al(B * Hkv * ((Nk + 63) / 64) * sizeof(float));
+    w.k_mean = off; off += al(B * Hkv * D * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qa_abi_version(void) { return QA_ABI_VERSION; }
+
+const char* qa_last_error(void) { return g_err.c_str(); }
+
+qa_status_t qa_quantize_q(const void* q, qa_dtype_t dtype, int64_t num_tokens, int32_t num_heads,
+                          int32_t head_dim, int64_t stride_token, int64_t stride_head, int8_t* q_i8,
+                          float* q_scale, qa_stream_t stream) {
+  QA_REQUIRE(num_tokens >= 0 && num_heads > 0 && head_dim > 0, QA_ERR_INVALID_ARG,
+             "bad shape (tokens=%lld, heads=%d, head_dim=%d)", (long long)num_tokens, num_heads, head_dim);
+  QA_REQUIRE(dtype == QA_DT_BF16 || dtype == QA_DT_F16, QA_ERR_UNSUPPORTED, "dtype must be BF16 or F16");
+  QA_REQUIRE(supported_dim(head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  if (num_tokens == 0) return QA_OK;
+  QA_REQUIRE(q && q_i8 && q_scale, QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(aligned16(q) && stride_token % 8 == 0 && stride_head % 8 == 0 && stride_token >= 0 &&
+                 stride_head >= 0,
+             QA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  QA_REQUIRE(num_tokens * num_heads / 4 < (int64_t)INT32_MAX, QA_ERR_UNSUPPORTED, "too many rows");
+  return hip_status(qa::launch_quantize_rows(q, dtype == QA_DT_BF16, num_tokens, num_heads, head_dim,
+                                             stride_token, stride_head, q_i8, q_scale, (hipStream_t)stream),
+                    "qa_quantize_q launch");
+}
+
+qa_status_t qa_write_kv_cache(const void* k, const void* v, qa_dtype_t dtype, int64_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int64_t stride_token,
+                              int64_t stride_head, const int64_t* slot_mapping, int64_t num_blocks,
+                              int32_t block_size, int8_t* k_cache, float* k_scale, void* v_cache,
+                              qa_dtype_t v_cache_dtype, float* v_scale, qa_stream_t stream) {
+  QA_REQUIRE(num_tokens >= 0 && num_kv_heads > 0 && head_dim > 0 && num_blocks > 0, QA_ERR_INVALID_ARG,
+             "bad shape");
+  QA_REQUIRE(dtype == QA_DT_BF16 || dtype == QA_DT_F16, QA_ERR_UNSUPPORTED, "dtype must be BF16 or F16");
+  QA_REQUIRE(v_cache_dtype == dtype || v_cache_dtype == QA_DT_I8, QA_ERR_UNSUPPORTED,
+             "v_cache_dtype must equal dtype or be I8");
+  QA_REQUIRE(supported_dim(head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  QA_REQUIRE(block_size == 16, QA_ERR_UNSUPPORTED, "block_size %d != 16", block_size);
+  if (num_tokens == 0) return QA_OK;
+  QA_REQUIRE(k && v && slot_mapping && k_cache && k_scale && v_cache, QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+  QA_REQUIRE(aligned16(k) && aligned16(v) && stride_token % 8 == 0 && stride_head % 8 == 0 &&
+                 stride_token >= 0 && stride_head >= 0,
+             QA_ERR_INVALID_ARG, "k/v must be 16-byte aligned with strides that are multiples of 8 elements");
+  QA_REQUIRE(aligned16(k_cache), QA_ERR_INVALID_ARG, "k_cache must be 16-byte aligned");
+  QA_REQUIRE(num_tokens * num_kv_heads / 4 < (int64_t)INT32_MAX, QA_ERR_UNSUPPORTED, "too many rows");
+  return hip_status(qa::launch_write_kv_cache(k, v, dtype == QA_DT_BF16, num_tokens, num_kv_heads, head_dim,
+                                              stride_token, stride_head, slot_mapping, k_cache, k_scale,
+                                              v_cache, v_cache_dtype == QA_DT_I8, v_scale,
+                                              (hipStream_t)stream),
+                    "qa_write_kv_cache launch");
+}
+
+int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p) {
+  if (check_decode(p) != QA_OK) return -1;
+  return splits_of(p);
+}
+
+size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p) {
+  if (check_decode(p) != QA_OK) return 0;
+  return decode_ws(p, splits_of(p));
+}
+
+qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t* q_i8, const float* q_scale,
+                                      const int8_t* k_cache, const float* k_scale, const void* v_cache,
+                                      const float* v_scale, const int32_t* block_tables,
+                                      const int32_t* context_lens, void* workspace, size_t workspace_bytes,
+                                      void* out, qa_stream_t stream) {
+  qa_status_t st = check_decode(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0) return QA_OK;
+  QA_REQUIRE(q_i8 && q_scale && k_cache && k_scale && v_cache && block_tables && context_lens && out,
+             QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+  QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&
+                 (v_scale == nullptr || aligned16(v_scale)),
+             QA_ERR_INVALID_ARG, "q_i8, caches and scales must be 16-byte aligned");
+  const int32_t S = splits_of(p);
+  const size_t need = decode_ws(p, S);
+  QA_REQUIRE(workspace_bytes >= need, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+             workspace_bytes, need);
+  QA_REQUIRE(need == 0 || workspace != nullptr, QA_ERR_INVALID_ARG, "workspace is NULL");
+  QA_REQUIRE(need == 0 || aligned16(workspace), QA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  qa::DecodeArgs a{};
+  a.q = q_i8; a.q_scale = q_scale; a.k_cache = k_cache; a.k_scale = k_scale; a.v_cache = v_cache;
+  a.v_scale = v_scale; a.tables = block_tables; a.ctx_lens = context_lens; a.out = out;
+  const size_t units = (size_t)p->num_seqs * p->num_q_heads * S;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = need ? (float*)((char*)workspace + ((units * p->head_dim * sizeof(float) + 255) & ~(size_t)255)) : nullptr;
+  a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
+  a.num_splits = S; a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
+  return hip_status(qa::launch_decode(a, (hipStream_t)stream), "qa_paged_attention_decode launch");
+}
+
+qa_status_t qa_debug_paged_qk_int32(const qa_decode_params_t* p, const int8_t* q_i8, const int8_t* k_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t* acc_out, qa_stream_t stream) {
+  qa_status_t st = check_decode(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0) return QA_OK;
+  QA_REQUIRE(q_i8 && k_cache && block_tables && context_lens && acc_out, QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache), QA_ERR_INVALID_ARG, "q_i8 and k_cache must be 16-byte aligned");
+  qa::DecodeArgs a{};
+  a.q = q_i8; a.k_cache = k_cache; a.tables = block_tables; a.ctx_lens = context_lens; a.acc_out = acc_out;
+  a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
+  a.num_splits = 1; a.scale_log2 = 1.0f; a.v_int8 = false;
+  return hip_status(qa::launch_debug_qk(a, (hipStream_t)stream), "qa_debug_paged_qk_int32 launch");
+}
+
+qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int8_t* q_i8, const float* q_scale,
+                                         const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                         const int8_t* k_cache, const float* k_scale, const void* v_cache,
+                                         const float* v_scale, const int32_t* block_tables, void* out,
+                                         qa_stream_t stream) {
+  QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
+  QA_REQUIRE(p->num_seqs >= 0 && p->num_q_heads > 0 && p->num_kv_heads > 0 && p->head_dim > 0 &&
+                 p->total_q >= 0 && p->max_seqlen_q >= 0,
+             QA_ERR_INVALID_ARG, "bad prefill shape");
+  QA_REQUIRE(p->num_q_heads % p->num_kv_heads == 0, QA_ERR_INVALID_ARG,
+             "num_q_heads (%d) not a multiple of num_kv_heads (%d)", p->num_q_heads, p->num_kv_heads);
+  QA_REQUIRE(p->max_blocks_per_seq > 0 && p->num_blocks > 0, QA_ERR_INVALID_ARG,
+             "max_blocks_per_seq and num_blocks must be positive");
+  QA_REQUIRE(p->v_cache_dtype == QA_DT_BF16 || p->v_cache_dtype == QA_DT_I8, QA_ERR_UNSUPPORTED,
+             "v_cache_dtype must be BF16 or I8");
+  QA_REQUIRE(p->out_dtype == QA_DT_F32 || p->out_dtype == QA_DT_BF16, QA_ERR_UNSUPPORTED,
+             "prefill out_dtype must be F32 or BF16");
+  QA_REQUIRE(supported_dim(p->head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", p->head_dim);
+  QA_REQUIRE(p->block_size == 16, QA_ERR_UNSUPPORTED, "block_size %d != 16", p->block_size);
+  QA_REQUIRE(p->num_seqs <= 65535 && p->num_q_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
+  if (p->num_seqs == 0 || p->total_q == 0) return QA_OK;
+  QA_REQUIRE(q_i8 && q_scale && cu_seqlens_q && context_lens && k_cache && k_scale && v_cache && block_tables && out,
+             QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+  QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), QA_ERR_INVALID_ARG,
+             "q_i8, caches and out must be 16-byte aligned");
+  qa::FlashArgs a{};
+  a.q = q_i8; a.q_scale = q_scale; a.k_blocks = k_cache; a.k_scale = k_scale; a.v_blocks = v_cache;
+  a.v_scale = v_scale; a.tables = block_tables; a.cu_q = cu_seqlens_q; a.ctx_lens = context_lens; a.out = out;
+  a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
+  a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq; a.max_seqlen_q = p->max_seqlen_q;
+  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.dense = false; a.causal = true; a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.v_f16 = false;
+  a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = false;
+  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "qa_chunked_prefill_attention launch");
+}
+
+size_t qa_dense_sage_quantize_workspace_size(const qa_dense_params_t* p) {
+  if (check_dense(p) != QA_OK) return 0;
+  return dense_layout(p, false).total;
+}
+
+qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, const void* k, int8_t* q_i8,
+                                   float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* workspace,
+                                   size_t workspace_bytes, qa_stream_t stream) {
+  qa_status_t st = check_dense(p);
+  if (st != QA_OK) return st;
+  if (p->batch == 0 || (p->seq_q == 0 && p->seq_k == 0)) return QA_OK;
+  QA_REQUIRE(q && k && q_i8 && q_scale && k_i8 && k_scale && k_mean && workspace, QA_ERR_INVALID_ARG,
+             "null pointer");
+  QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(workspace) && ((uintptr_t)q_i8 & 7u) == 0 &&
+                 ((uintptr_t)k_i8 & 7u) == 0,
+             QA_ERR_INVALID_ARG, "q, k, workspace must be 16-byte aligned and codes 8-byte aligned");
+  const DenseWs w = dense_layout(p, false);
+  QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+             workspace_bytes, w.total);
+  qa::SagePrepArgs a{};
+  a.q = q; a.k = k; a.v = nullptr; a.bf16 = p->dtype == QA_DT_BF16;
+  a.B = p->batch; a.Nq = p->seq_q; a.Nk = p->seq_k; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.D = p->head_dim; a.smooth_k = p->smooth_k != 0;
+  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_paged = nullptr; a.k_scale = k_scale;
+  a.k_mean = k_mean; a.partial = (double*)((char*)workspace + w.partial); a.v_paged = nullptr;
+  return hip_status(qa::launch_sage_prep(a, (hipStream_t)stream), "qa_dense_sage_quantize launch");
+}
+
+size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p) {
+  if (check_dense(p) != QA_OK) return 0;
+  return dense_layout(p, true).total;
+}
+
+qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, const void* k, const void* v,
+                                    void* workspace, size_t workspace_bytes, void* out, qa_stream_t stream) {
+  qa_status_t st = check_dense(p);
+  if (st != QA_OK) return st;
+  if (p->batch == 0 || p->seq_q == 0) return QA_OK;
+  QA_REQUIRE(q && k && v && out && workspace, QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(workspace),
+             QA_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
+  const DenseWs w = dense_layout(p, true);
+  QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+             workspace_bytes, w.total);
+  char* ws = (char*)workspace;
+  qa::SagePrepArgs pa{};
+  pa.q = q; pa.k = k; pa.v = v; pa.bf16 = p->dtype == QA_DT_BF16;
+  pa.B = p->batch; pa.Nq = p->seq_q; pa.Nk = p->seq_k; pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads;
+  pa.D = p->head_dim; pa.smooth_k = p->smooth_k != 0;
+  pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
+  pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
+  pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
+  st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
+  if (st != QA_OK) return st;
+  qa::FlashArgs a{};
+  a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
+  a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
+  a.num_seqs = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
+  a.D = p->head_dim; a.max_blocks = 0; a.max_seqlen_q = p->seq_q; a.Nq = p->seq_q; a.Nk = p->seq_k;
+  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.dense = true; a.causal = p->is_causal != 0; a.v_int8 = false; a.v_f16 = p->dtype == QA_DT_F16;
+  a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = p->out_dtype == QA_DT_F16;
+  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "dense attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Host-side interface between the C ABI (api.hip) and the kernel files.
+// Every launcher assumes its arguments were validated by the caller and
+// returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qa {
+
+// quantize.hip ---------------------------------------------------------------
+hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t num_tokens, int32_t num_heads,
+                                int32_t head_dim, int64_t stride_t, int64_t stride_h,
+                                int8_t* q, float* scale, hipStream_t st);
+
+hipError_t launch_write_kv_cache(const void* k, const void* v, bool bf16, int64_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int64_t stride_t,
+                                 int64_t stride_h, const int64_t* slots, int8_t* k_cache,
+                                 float* k_scale, void* v_cache, bool v_int8, float* v_scale,
+                                 hipStream_t st);
+
+struct SagePrepArgs {
+  const void* q;
+  const void* k;
+  const void* v;          // only for the V transpose
+  bool bf16;
+  int32_t B, Nq, Nk, Hq, Hkv, D;
+  bool smooth_k;
+  int8_t* q_i8;           // NHD codes
+  float* q_scale;         // [B, Hq, ceil(Nq/128)]
+  int8_t* k_i8;           // NHD codes (public layout) or nullptr
+  int8_t* k_paged;        // blocked layout [B*Nk16, Hkv, D/16, 16, 16] or nullptr
+  float* k_scale;         // [B, Hkv, ceil(Nk/64)]
+  float* k_mean;          // [B, Hkv, D]
+  double* partial;        // fp64 column sums [B, chunks, Hkv*D]
+  uint16_t* v_paged;      // V transposed into [B*Nk16, Hkv, D, 16] or nullptr
+};
+size_t sage_partial_bytes(int32_t B, int32_t Nk, int32_t Hkv, int32_t D);
+hipError_t launch_sage_prep(const SagePrepArgs& a, hipStream_t st);
+
+// decode.hip -----------------------------------------------------------------
+struct DecodeArgs {
+  const int8_t* q;
+  const float* q_scale;
+  const int8_t* k_cache;
+  const float* k_scale;
+  const void* v_cache;
+  const float* v_scale;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  float* ws_o;            // [S, ...] partial outputs (S > 1)
+  float* ws_ml;           // partial (max, sum)
+  void* out;
+  int32_t* acc_out;       // debug export
+  int32_t num_seqs, Hq, Hkv, G, D, max_blocks, num_splits;
+  float scale_log2;       // softmax_scale * log2(e)
+  bool v_int8, out_bf16;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_debug_qk(const DecodeArgs& a, hipStream_t st);
+int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks);
+
+// flash.hip (chunked prefill and dense) --------------------------------------
+struct FlashArgs {
+  const int8_t* q;         // codes, row (token, head) at (q_row0 + i)*q_row_stride + h*D
+  const float* q_scale;    // per-token [T, Hq] (paged) or per-block [B, Hq, nqb] (dense)
+  const int8_t* k_blocks;  // [blocks, Hkv, D/16, 16, 16]
+  const float* k_scale;    // per-token [blocks, Hkv, 16] (paged) or per-64 [B, Hkv, nkb] (dense)
+  const void* v_blocks;    // [blocks, Hkv, D, 16] bf16 / f16 / int8
+  const float* v_scale;    // per-token (int8 V)
+  const int32_t* tables;   // [num_seqs, max_blocks] (paged) or nullptr (dense: identity)
+  const int32_t* cu_q;     // [num_seqs+1] (paged) or nullptr (dense: b*Nq)
+  const int32_t* ctx_lens; // [num_seqs] (paged) or nullptr (dense: Nk)
+  void* out;               // [rows, Hq, D]
+  int32_t num_seqs, Hq, Hkv, G, D, max_blocks, max_seqlen_q;
+  int32_t Nq, Nk;          // dense only
+  float scale_log2;
+  bool dense, causal, v_int8, v_f16, out_bf16, out_f16;
+};
+hipError_t launch_flash(const FlashArgs& a, hipStream_t st);
+
+}  // namespace qa

@@ -1,0 +1,365 @@
+// Quantization and cache-writing kernels (memory-bound).
+//
+// Row rule ([QK-MMAC] §1, §2.1, §4): s = fl32(max|x| / 127), code =
+// clamp(rne(fl32(x / s)), -127, 127), with correctly rounded fp32 divisions.
+// A zero row gets s = 0 and zero codes.
+#include "common.h"
+#include "internal.h"
+
+namespace qa {
+namespace {
+
+// Load E consecutive 16-bit values (E = 1, 2, 4) from a 2E-byte aligned address.
+template <int E, bool BF16>
+__device__ __forceinline__ void load_halves(const uint16_t* p, float (&v)[E]) {
+  if constexpr (E == 4) {
+    uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = half_to_f32<BF16>(w.x & 0xFFFFu);
+    v[1] = half_to_f32<BF16>(w.x >> 16);
+    v[2] = half_to_f32<BF16>(w.y & 0xFFFFu);
+    v[3] = half_to_f32<BF16>(w.y >> 16);
+  } else if constexpr (E == 2) {
+    uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = half_to_f32<BF16>(w & 0xFFFFu);
+    v[1] = half_to_f32<BF16>(w >> 16);
+  } else {
+    v[0] = half_to_f32<BF16>(*p);
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void store_codes(int8_t* p, uint32_t packed) {
+  if constexpr (E == 4) *reinterpret_cast<uint32_t*>(p) = packed;
+  else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(p) = (uint16_t)packed;
+  else *reinterpret_cast<uint8_t*>(p) = (uint8_t)packed;
+}
+
+// Quantize E values held by one lane against the wave-wide scale of its row.
+template <int E>
+__device__ __forceinline__ uint32_t quant_lane(const float (&v)[E], float amax, float s) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    int c = amax > 0.0f ? quant_code(v[e], s) : 0;
+    packed |= ((uint32_t)c & 0xFFu) << (8 * e);
+  }
+  return packed;
+}
+
+// One wave per (token, head) row; 4 rows per workgroup.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int32_t H, int64_t st, int64_t sh,
+                                                       int8_t* __restrict__ q, float* __restrict__ scale) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t t = row / H;
+  const int h = (int)(row - t * H);
+  float v[E];
+  load_halves<E, BF16>(x + t * st + (int64_t)h * sh + lane * E, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  amax = wave_max(amax);
+  const float s = quant_scale(amax);
+  store_codes<E>(q + row * D + lane * E, quant_lane<E>(v, amax, s));
+  if (lane == 0) scale[row] = s;
+}
+
+// One wave per (token, KV head): K -> INT8 codes in [blk, h, D/16, 16, 16] plus a
+// per-token scale; V copied (or quantized) into [blk, h, D, 16].
+template <int D, bool BF16, bool V_I8>
+__global__ __launch_bounds__(256) void k_write_kv(const uint16_t* __restrict__ k,
+                                                  const uint16_t* __restrict__ v, int64_t rows,
+                                                  int32_t H, int64_t st, int64_t sh,
+                                                  const int64_t* __restrict__ slots,
+                                                  int8_t* __restrict__ kc, float* __restrict__ ks,
+                                                  void* __restrict__ vc, float* __restrict__ vs) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t t = row / H;
+  const int h = (int)(row - t * H);
+  const int64_t slot = slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot >> 4;
+  const int off = (int)(slot & 15);
+  const int64_t bh = blk * H + h;
+  const int64_t src = t * st + (int64_t)h * sh + lane * E;
+
+  float kv[E];
+  load_halves<E, BF16>(k + src, kv);
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(kv[e]));
+  amax = wave_max(amax);
+  const float s = quant_scale(amax);
+  // channels lane*E .. lane*E+E-1 share one 16-channel chunk
+  const int ch = lane * E;
+  store_codes<E>(kc + (bh * (D / 16) + ch / 16) * 256 + off * 16 + (ch % 16), quant_lane<E>(kv, amax, s));
+  if (lane == 0) ks[bh * 16 + off] = s;
+
+  if constexpr (V_I8) {
+    float vv[E];
+    load_halves<E, BF16>(v + src, vv);
+    float vmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) vmax = fmaxf(vmax, fabsf(vv[e]));
+    vmax = wave_max(vmax);
+    const float sv = quant_scale(vmax);
+    int8_t* vd = reinterpret_cast<int8_t*>(vc);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      vd[(bh * D + ch + e) * 16 + off] = (int8_t)(vmax > 0.0f ? quant_code(vv[e], sv) : 0);
+    if (lane == 0) vs[bh * 16 + off] = sv;
+  } else {
+    uint16_t* vd = reinterpret_cast<uint16_t*>(vc);
+#pragma unroll
+    for (int e = 0; e < E; ++e) vd[(bh * D + ch + e) * 16 + off] = v[src + e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SageAttention-style preprocessing
+// ---------------------------------------------------------------------------
+
+constexpr int kSumChunk = 64;  // tokens per partial column sum
+
+// partial[b][chunk][c] = sum over the chunk's tokens of K[b, t, c], c in [0, Hkv*D),
+// accumulated in fp64. Every K value is a multiple of 2^-24 (f16) or of a power
+// of two bounded by its exponent (bf16), and the sums stay far below 2^53 units,
+// so every partial sum is exact and the total does not depend on the order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, int32_t Nk,
+                                                int32_t HD, double* __restrict__ partial) {
+  const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
+  const int b = blockIdx.z, chunk = blockIdx.y;
+  const int c8 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c8 >= HD) return;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, Nk);
+  const uint16_t* base = k + ((int64_t)b * Nk) * HD + c8;
+  for (int t = t0; t < t1; ++t) {
+    uint4 w = *reinterpret_cast<const uint4*>(base + (int64_t)t * HD);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += (double)half_to_f32<BF16>(ws[i] & 0xFFFFu);
+      acc[2 * i + 1] += (double)half_to_f32<BF16>(ws[i] >> 16);
+    }
+  }
+  double* dst = partial + ((int64_t)b * chunks + chunk) * HD + c8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = acc[i];
+}
+
+// mu[b][c] = fl32(fl64(sum / Nk)); zeros when smoothing is off.
+__global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, int32_t B,
+                                              int32_t Nk, int32_t HD, bool smooth,
+                                              float* __restrict__ mean) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * HD) return;
+  if (!smooth || Nk == 0) { mean[i] = 0.0f; return; }
+  const int b = (int)(i / HD), c = (int)(i % HD);
+  const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
+  double s = 0.0;
+  for (int j = 0; j < chunks; ++j) s += partial[((int64_t)b * chunks + j) * HD + c];
+  mean[i] = (float)(s / (double)Nk);
+}
+
+// Per-block quantization of one (b, head, block) of ROWS tokens x D channels:
+// one scale over all ROWS*D values (after subtracting mu when given).
+// Writes NHD codes (codes_nhd) and/or the blocked K layout (codes_blk).
+template <int D, int ROWS, bool BF16>
+__global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict__ x, int32_t N,
+                                                     int32_t H, const float* __restrict__ mean,
+                                                     int8_t* __restrict__ codes_nhd,
+                                                     int8_t* __restrict__ codes_blk,
+                                                     float* __restrict__ scale) {
+  constexpr int G8 = D / 8;                // 8-channel groups per row
+  constexpr int PER = ROWS * G8 / 256;     // groups per thread
+  static_assert(ROWS * G8 % 256 == 0, "block must tile the workgroup");
+  const int nblk = (N + ROWS - 1) / ROWS;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float red[4];
+
+  float val[PER][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int gi = threadIdx.x + 256 * k;
+    const int r = gi / G8, c = (gi % G8) * 8;
+    const int t = blk * ROWS + r;
+    if (t < N) {
+      uint4 w = *reinterpret_cast<const uint4*>(x + (((int64_t)b * N + t) * H + h) * D + c);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        val[k][2 * i] = half_to_f32<BF16>(ws[i] & 0xFFFFu);
+        val[k][2 * i + 1] = half_to_f32<BF16>(ws[i] >> 16);
+      }
+      if (mean != nullptr) {
+        const float* mu = mean + ((int64_t)b * H + h) * D + c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) val[k][i] = val[k][i] - mu[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(val[k][i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) val[k][i] = 0.0f;
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = quant_scale(amax);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int gi = threadIdx.x + 256 * k;
+    const int r = gi / G8, c = (gi % G8) * 8;
+    const int t = blk * ROWS + r;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c0 = amax > 0.0f ? quant_code(val[k][i], s) : 0;
+      int c1 = amax > 0.0f ? quant_code(val[k][4 + i], s) : 0;
+      lo |= ((uint32_t)c0 & 0xFFu) << (8 * i);
+      hi |= ((uint32_t)c1 & 0xFFu) << (8 * i);
+    }
+    if (t >= N) lo = hi = 0;
+    if (codes_nhd != nullptr && t < N)
+      *reinterpret_cast<uint2*>(codes_nhd + (((int64_t)b * N + t) * H + h) * D + c) = make_uint2(lo, hi);
+    if (codes_blk != nullptr) {
+      // blocked layout: block (b * ceil(N/16) + t/16), head h, chunk c/16, slot t%16
+      const int64_t pb = (int64_t)b * ((N + 15) / 16) + t / 16;
+      if (t / 16 < (N + 15) / 16)
+        *reinterpret_cast<uint2*>(codes_blk + ((pb * H + h) * (D / 16) + c / 16) * 256 + (t % 16) * 16 + (c % 16)) =
+            make_uint2(lo, hi);
+    }
+  }
+  if (threadIdx.x == 0) scale[((int64_t)b * H + h) * nblk + blk] = s;
+}
+
+// V [B, N, H, D] (16-bit) -> [B*ceil(N/16), H, D, 16]: each channel's 16 tokens of a
+// block contiguous; padding tokens of the last block are zero.
+template <int D>
+__global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, int32_t N, int32_t H,
+                                                  uint16_t* __restrict__ vb) {
+  __shared__ uint16_t tile[16][D + 2];
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nb16 = (N + 15) / 16;
+  for (int i = threadIdx.x; i < 16 * D; i += 256) {
+    const int r = i / D, c = i % D;
+    const int t = blk * 16 + r;
+    tile[r][c] = t < N ? v[(((int64_t)b * N + t) * H + h) * D + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  uint16_t* dst = vb + (((int64_t)b * nb16 + blk) * H + h) * D * 16;
+  for (int i = threadIdx.x; i < 16 * D; i += 256) {
+    const int c = i / 16, r = i % 16;
+    dst[i] = tile[r][c];
+  }
+}
+
+template <int D>
+hipError_t quantize_rows_d(const void* x, bool bf16, int64_t T, int32_t H, int64_t st, int64_t sh,
+                           int8_t* q, float* scale, hipStream_t s) {
+  const int64_t rows = T * H;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (bf16)
+    k_quantize_rows<D, true><<<grid, 256, 0, s>>>((const uint16_t*)x, rows, H, st, sh, q, scale);
+  else
+    k_quantize_rows<D, false><<<grid, 256, 0, s>>>((const uint16_t*)x, rows, H, st, sh, q, scale);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t write_kv_d(const void* k, const void* v, int64_t T, int32_t H, int64_t st, int64_t sh,
+                      const int64_t* slots, int8_t* kc, float* ks, void* vc, bool v_i8, float* vs,
+                      hipStream_t s) {
+  const int64_t rows = T * H;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (v_i8)
+    k_write_kv<D, BF16, true><<<grid, 256, 0, s>>>((const uint16_t*)k, (const uint16_t*)v, rows, H, st,
+                                                   sh, slots, kc, ks, vc, vs);
+  else
+    k_write_kv<D, BF16, false><<<grid, 256, 0, s>>>((const uint16_t*)k, (const uint16_t*)v, rows, H, st,
+                                                    sh, slots, kc, ks, vc, vs);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
+  const int HD = a.Hkv * D;
+  const int chunks = (a.Nk + kSumChunk - 1) / kSumChunk;
+  if (a.smooth_k && a.Nk > 0) {
+    dim3 g((HD / 8 + 255) / 256, chunks, a.B);
+    k_colsum<BF16><<<g, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, HD, a.partial);
+  }
+  k_mean<<<(unsigned)(((int64_t)a.B * HD + 255) / 256), 256, 0, s>>>(a.partial, a.B, a.Nk, HD,
+                                                                        a.smooth_k, a.k_mean);
+  if (a.Nq > 0) {
+    dim3 gq((a.Nq + 127) / 128, a.Hq, a.B);
+    k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.Nq, a.Hq, nullptr, a.q_i8,
+                                                   nullptr, a.q_scale);
+  }
+  if (a.Nk > 0) {
+    dim3 gk((a.Nk + 63) / 64, a.Hkv, a.B);
+    k_block_quant<D, 64, BF16><<<gk, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, a.Hkv, a.k_mean, a.k_i8,
+                                                  a.k_paged, a.k_scale);
+    if (a.v_paged != nullptr) {
+      dim3 gv((a.Nk + 15) / 16, a.Hkv, a.B);
+      k_v_blocks<D><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, a.Hkv, a.v_paged);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t T, int32_t H, int32_t D, int64_t st,
+                                int64_t sh, int8_t* q, float* scale, hipStream_t s) {
+  switch (D) {
+    case 64: return quantize_rows_d<64>(x, bf16, T, H, st, sh, q, scale, s);
+    case 128: return quantize_rows_d<128>(x, bf16, T, H, st, sh, q, scale, s);
+    default: return quantize_rows_d<256>(x, bf16, T, H, st, sh, q, scale, s);
+  }
+}
+
+hipError_t launch_write_kv_cache(const void* k, const void* v, bool bf16, int64_t T, int32_t H,
+                                 int32_t D, int64_t st, int64_t sh, const int64_t* slots,
+                                 int8_t* kc, float* ks, void* vc, bool v_i8, float* vs,
+                                 hipStream_t s) {
+#define QA_WKV(DD)                                                                   \
+  return bf16 ? write_kv_d<DD, true>(k, v, T, H, st, sh, slots, kc, ks, vc, v_i8, vs, s) \
+              : write_kv_d<DD, false>(k, v, T, H, st, sh, slots, kc, ks, vc, v_i8, vs, s)
+  switch (D) {
+    case 64: QA_WKV(64);
+    case 128: QA_WKV(128);
+    default: QA_WKV(256);
+  }
+#undef QA_WKV
+}
+
+size_t sage_partial_bytes(int32_t B, int32_t Nk, int32_t Hkv, int32_t D) {
+  const size_t chunks = (size_t)((Nk + kSumChunk - 1) / kSumChunk);
+  return (size_t)B * (chunks > 0 ? chunks : 1) * (size_t)Hkv * D * sizeof(double);
+}
+
+hipError_t launch_sage_prep(const SagePrepArgs& a, hipStream_t s) {
+#define QA_PREP(DD) return a.bf16 ? sage_prep_d<DD, true>(a, s) : sage_prep_d<DD, false>(a, s)
+  switch (a.D) {
+    case 64: QA_PREP(64);
+    case 128: QA_PREP(128);
+    default: QA_PREP(256);
+  }
+#undef QA_PREP
+}
+
+}  // namespace qa

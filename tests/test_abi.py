@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments on the host before any
+HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qattn.h")
+
+
+@pytest.fixture(scope="module")
+def qa():
+    lib_path = os.path.join(ROOT, "quantized_attention_quantize_amd", "libqattn.so")
+    if not os.path.exists(lib_path):
+        from quantized_attention_quantize_amd.build import build
+        build()
+    import quantized_attention_quantize_amd as m
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(qa):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(qa.lib, n), f"missing export {n}"
+    assert set(names) == set(qa.EXPORTED)
+
+
+def test_abi_version(qa):
+    assert qa.lib.qa_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+
+
+def test_quantize_q_rejects(qa):
+    L = qa.lib
+    assert L.qa_quantize_q(FAKE, qa.QA_DT_BF16, 4, 2, 96, 192, 96, FAKE, FAKE, None) == qa.QA_ERR_UNSUPPORTED
+    assert b"head_dim 96" in L.qa_last_error()
+    assert L.qa_quantize_q(FAKE, qa.QA_DT_F32, 4, 2, 64, 128, 64, FAKE, FAKE, None) == qa.QA_ERR_UNSUPPORTED
+    assert L.qa_quantize_q(None, qa.QA_DT_BF16, 4, 2, 64, 128, 64, FAKE, FAKE, None) == qa.QA_ERR_INVALID_ARG
+    assert L.qa_quantize_q(FAKE, qa.QA_DT_BF16, -1, 2, 64, 128, 64, FAKE, FAKE, None) == qa.QA_ERR_INVALID_ARG
+    assert L.qa_quantize_q(FAKE, qa.QA_DT_BF16, 4, 2, 64, 129, 64, FAKE, FAKE, None) == qa.QA_ERR_INVALID_ARG
+    # zero tokens is a no-op even with null pointers
+    assert L.qa_quantize_q(None, qa.QA_DT_BF16, 0, 2, 64, 128, 64, None, None, None) == qa.QA_OK
+
+
+def test_write_kv_cache_rejects(qa):
+    L = qa.lib
+    args = [FAKE, FAKE, qa.QA_DT_BF16, 8, 2, 64, 128, 64, FAKE, 4, 16, FAKE, FAKE, FAKE, qa.QA_DT_BF16, None, None]
+    a = list(args); a[10] = 32
+    assert L.qa_write_kv_cache(*a) == qa.QA_ERR_UNSUPPORTED
+    a = list(args); a[14] = qa.QA_DT_I8
+    assert L.qa_write_kv_cache(*a) == qa.QA_ERR_INVALID_ARG   # INT8 V without v_scale
+    a = list(args); a[14] = qa.QA_DT_F16
+    assert L.qa_write_kv_cache(*a) == qa.QA_ERR_UNSUPPORTED
+    a = list(args); a[8] = None
+    assert L.qa_write_kv_cache(*a) == qa.QA_ERR_INVALID_ARG
+
+
+def _dp(qa, **kw):
+    p = qa.decode_params(2, 24, 4, 256, 64, 1000)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_decode_validation(qa):
+    L = qa.lib
+    call = lambda p, ws_bytes=0, ws=FAKE: L.qa_paged_attention_decode(
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws, ws_bytes, FAKE, None)
+    assert call(_dp(qa, head_dim=96)) == qa.QA_ERR_UNSUPPORTED
+    assert call(_dp(qa, block_size=32)) == qa.QA_ERR_UNSUPPORTED
+    assert call(_dp(qa, num_q_heads=68, num_kv_heads=4)) == qa.QA_ERR_UNSUPPORTED      # group 17
+    assert call(_dp(qa, num_q_heads=25)) == qa.QA_ERR_INVALID_ARG                      # not a multiple
+    assert call(_dp(qa, v_cache_dtype=qa.QA_DT_F16)) == qa.QA_ERR_UNSUPPORTED
+    assert call(_dp(qa, v_cache_dtype=qa.QA_DT_I8)) == qa.QA_ERR_INVALID_ARG           # v_scale missing
+    assert call(_dp(qa, out_dtype=qa.QA_DT_F16)) == qa.QA_ERR_UNSUPPORTED
+    p = _dp(qa, num_splits=8)
+    need = L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    assert need == 2 * 24 * 8 * (256 + 2) * 4
+    assert call(p, need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert b"needed" in L.qa_last_error()
+    assert L.qa_paged_decode_workspace_size(ctypes.byref(_dp(qa, num_splits=1))) == 0
+
+
+def test_decode_split_heuristic(qa):
+    f = lambda S, Hkv, mb: qa.lib.qa_paged_decode_num_splits(ctypes.byref(qa.decode_params(S, 6 * Hkv, Hkv, 256, mb, 10)))
+    assert f(1, 4, 2048) == 128          # one long sequence: fill the chip
+    assert f(32, 4, 2048) == 4
+    assert f(1, 1, 16) == 2              # short context: at least 8 blocks per split
+    assert f(1, 1, 4) == 1
+    assert f(200, 4, 2048) == 1
+
+
+def test_prefill_and_dense_validation(qa):
+    L = qa.lib
+    p = qa.PrefillParams(1, 24, 4, 256, 16, 100, 1000, 10, 10, qa.QA_DT_BF16, qa.QA_DT_F32, 0.0)
+    p.head_dim = 80
+    assert L.qa_chunked_prefill_attention(ctypes.byref(p), *([FAKE] * 10), None) == qa.QA_ERR_UNSUPPORTED
+    p.head_dim = 256
+    assert L.qa_chunked_prefill_attention(ctypes.byref(p), FAKE, FAKE, None, *([FAKE] * 7), None) == \
+        qa.QA_ERR_INVALID_ARG
+    d = qa.DenseParams(2, 100, 100, 8, 3, 128, qa.QA_DT_F16, 1, 0, 0.0, qa.QA_DT_F32)
+    assert L.qa_dense_sage_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None) == \
+        qa.QA_ERR_INVALID_ARG                                                   # 8 % 3 != 0
+    d.num_kv_heads = 4
+    need = L.qa_dense_sage_workspace_size(ctypes.byref(d))
+    assert need > 0
+    assert L.qa_dense_sage_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need - 1, FAKE, None) == \
+        qa.QA_ERR_WORKSPACE_TOO_SMALL
+    d.dtype = qa.QA_DT_F32
+    assert L.qa_dense_sage_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need, FAKE, None) == \
+        qa.QA_ERR_UNSUPPORTED
+
+
+def test_last_error_is_thread_local(qa):
+    import threading
+    L = qa.lib
+    L.qa_quantize_q(FAKE, qa.QA_DT_BF16, 4, 2, 96, 192, 96, FAKE, FAKE, None)
+    seen = {}
+
+    def other():
+        L.qa_quantize_q(None, qa.QA_DT_BF16, 4, 2, 64, 128, 64, FAKE, FAKE, None)
+        seen["msg"] = L.qa_last_error()
+    t = threading.Thread(target=other)
+    t.start(); t.join()
+    assert b"null" in seen["msg"]
+    assert b"head_dim 96" in L.qa_last_error()

@@ -1,0 +1,228 @@
+"""GPU parity for the attention outputs against the oracle's fp64 result:
+relative L2 <= 1e-3 and max abs <= 2e-3 (fp32 output). Decode (split and
+unsplit, bf16 and INT8 V), chunked prefill and dense SageAttention-style."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, tiny_decode, qwen27b_decode,
+                       batched_splitk_decode, chunked_prefill, dense_sage)
+from tests.gpu_helpers import say, dev_bits, gpu_cache, oracle_cache, assert_close, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qa():
+    import quantized_attention_quantize_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def _decode_run(qa, inp, splits, out_dtype=torch.float32, seqs=None):
+    spec = inp.spec
+    kc, ks, vc, vs = gpu_cache(qa, inp, spec.v_int8)
+    q8, qs = qa.quantize_q(dev_bits(inp.q, spec.dtype))
+    out = qa.paged_attention_decode(q8, qs, kc, ks, vc, vs, torch.from_numpy(inp.block_tables).cuda(),
+                                    torch.from_numpy(inp.context_lens).cuda(), num_splits=splits,
+                                    out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def _decode_oracle(inp, heads=None, seqs=None):
+    spec = inp.spec
+    c = oracle_cache(inp, spec.v_int8)
+    w8, ws = oracle.quantize_q(inp.q, spec.dtype)
+    lens = inp.context_lens.copy()
+    if seqs is not None:
+        lens = np.where(np.isin(np.arange(len(lens)), seqs), lens, 0)
+    return oracle.paged_decode(w8, ws, c, inp.block_tables, lens, spec.num_kv_heads, heads=heads)
+
+
+DECODE = [
+    # (d, G, Hkv, contexts, v_int8)
+    (64, 6, 1, [256], False),
+    (64, 1, 2, [1, 15, 16, 17], False),
+    (128, 2, 2, [97, 300], True),
+    (128, 8, 1, [1000], False),
+    (256, 6, 4, [17, 1024, 555], False),
+    (256, 6, 4, [1, 2049, 64], True),
+    (256, 16, 1, [700], True),
+    (64, 6, 2, [0, 40], False),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 0])
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: f"d{c[0]}_G{c[1]}_Hkv{c[2]}_{'i8V' if c[4] else 'bf16V'}_{'-'.join(map(str, c[3]))}")
+def test_decode_parity(qa, case, splits):
+    d, G, Hkv, ctx, v_int8 = case
+    say(f"decode {case} splits={splits}")
+    spec = PagedSpec("dec", 101 + d + G, len(ctx), G * Hkv, Hkv, d, ctx, [1] * len(ctx), k_bias_std=2.0,
+                     v_int8=v_int8, pool_blocks=sum(-(-c // 16) for c in ctx) + 3)
+    inp = paged_inputs(spec)
+    got = _decode_run(qa, inp, splits).cpu().numpy()
+    want = _decode_oracle(inp)
+    assert_close(got, want, f"decode splits={splits}")
+    for s, c in enumerate(ctx):
+        if c == 0:
+            assert np.all(got[s] == 0)
+
+
+def test_decode_tiny_full(qa):
+    spec = tiny_decode()
+    say(f"decode full size {spec.name}")
+    inp = paged_inputs(spec)
+    want = _decode_oracle(inp)
+    for splits in (1, 2, 0):
+        assert_close(_decode_run(qa, inp, splits).cpu().numpy(), want, f"{spec.name} splits={splits}")
+
+
+def test_decode_qwen27b_full(qa):
+    spec = qwen27b_decode()
+    say(f"decode full size {spec.name}")
+    inp = paged_inputs(spec)
+    want = _decode_oracle(inp)
+    for splits in (0, 1, 16):
+        got = _decode_run(qa, inp, splits).cpu().numpy()
+        assert_close(got, want, f"{spec.name} splits={splits}")
+    # reported: error of the quantized method against unquantized fp64 attention
+    from oracle.quant import widen
+    q = widen(inp.q, "bf16").astype(np.float64)[0]
+    k = widen(inp.k, "bf16").astype(np.float64)
+    v = widen(inp.v, "bf16").astype(np.float64)
+    ref = np.stack([oracle.attention_fp64(q[h:h + 1], k[:, h // 6], v[:, h // 6], 1 / 16.0)[0] for h in range(24)])
+    say(f"  vs unquantized fp64: rel_l2={rel_l2(got[0], ref):.3e}")
+
+
+def test_decode_batched_splitk_full(qa):
+    spec = batched_splitk_decode()
+    say(f"decode full size {spec.name}: contexts {spec.context_lens[:6]}...")
+    inp = paged_inputs(spec)
+    got = _decode_run(qa, inp, spec.num_splits).cpu().numpy()
+    sample = [0, 7, int(np.argmax(spec.context_lens)), int(np.argmin(spec.context_lens)), 31]
+    want = _decode_oracle(inp, seqs=sample)
+    assert_close(got[sample], want[sample], f"{spec.name} sampled seqs {sample}")
+
+
+def test_decode_bf16_output(qa):
+    spec = PagedSpec("dec_bf16", 5, 2, 12, 2, 128, [333, 64], [1, 1], k_bias_std=2.0, pool_blocks=30)
+    say("decode bf16 output")
+    inp = paged_inputs(spec)
+    got = _decode_run(qa, inp, 4, torch.bfloat16).float().cpu().numpy()
+    want = _decode_oracle(inp)
+    ulp = np.abs(want) * 2.0 ** -8
+    assert np.all(np.abs(got - want) <= ulp + 2e-4)
+
+
+def test_decode_deterministic(qa):
+    spec = PagedSpec("det", 9, 3, 24, 4, 256, [4000, 100, 2500], [1, 1, 1], k_bias_std=2.0, v_int8=True)
+    say("decode determinism")
+    inp = paged_inputs(spec)
+    a = _decode_run(qa, inp, 8)
+    b = _decode_run(qa, inp, 8)
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill
+# ---------------------------------------------------------------------------
+
+def _prefill_run(qa, inp, out_dtype=torch.float32):
+    spec = inp.spec
+    kc, ks, vc, vs = gpu_cache(qa, inp, spec.v_int8)
+    q8, qs = qa.quantize_q(dev_bits(inp.q, spec.dtype))
+    out = qa.chunked_prefill_attention(q8, qs, torch.from_numpy(inp.cu_seqlens_q).cuda(),
+                                       torch.from_numpy(inp.context_lens).cuda(), kc, ks, vc, vs,
+                                       torch.from_numpy(inp.block_tables).cuda(), max(spec.query_lens),
+                                       out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def _prefill_oracle(inp, rows=None, heads=None):
+    spec = inp.spec
+    c = oracle_cache(inp, spec.v_int8)
+    w8, ws = oracle.quantize_q(inp.q, spec.dtype)
+    return oracle.chunked_prefill(w8, ws, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables,
+                                  spec.num_kv_heads, rows=rows, heads=heads)
+
+
+PREFILL = [
+    # (d, G, Hkv, contexts, query_lens, v_int8)
+    (64, 6, 1, [50, 37], [20, 37], False),
+    (64, 1, 2, [1, 17, 300], [1, 5, 130], False),
+    (128, 2, 2, [257, 129], [200, 129], True),
+    (256, 6, 4, [600], [260], False),
+    (256, 6, 2, [140, 33], [140, 1], True),
+    (256, 3, 1, [100], [0], False),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: f"d{c[0]}_G{c[1]}_Hkv{c[2]}_{'i8V' if c[5] else 'bf16V'}_{'-'.join(map(str, c[3]))}")
+def test_prefill_parity(qa, case):
+    d, G, Hkv, ctx, ql, v_int8 = case
+    say(f"prefill {case}")
+    spec = PagedSpec("pf", 201 + d + G, len(ctx), G * Hkv, Hkv, d, ctx, ql, k_bias_std=2.0, v_int8=v_int8,
+                     pool_blocks=sum(-(-c // 16) for c in ctx) + 4)
+    inp = paged_inputs(spec)
+    if spec.total_q == 0:
+        return
+    got = _prefill_run(qa, inp).cpu().numpy()
+    assert_close(got, _prefill_oracle(inp), "prefill")
+
+
+def test_prefill_full_size_sampled(qa):
+    spec = chunked_prefill()
+    say(f"prefill full size {spec.name}")
+    inp = paged_inputs(spec)
+    got = _prefill_run(qa, inp).cpu().numpy()
+    rows = [0, 1, 127, 128, 1000, 1500, 2046, 2047]
+    want = _prefill_oracle(inp, rows=rows)
+    assert_close(got[rows], want[rows], f"{spec.name} rows {rows}")
+
+
+# ---------------------------------------------------------------------------
+# dense SageAttention-style
+# ---------------------------------------------------------------------------
+
+DENSE = [
+    # (B, Nq, Nk, Hq, Hkv, d, dtype, causal)
+    (1, 200, 200, 2, 2, 64, "f16", False),
+    (1, 200, 200, 2, 2, 64, "f16", True),
+    (2, 300, 257, 4, 2, 128, "f16", True),
+    (2, 129, 400, 2, 2, 128, "bf16", False),
+    (1, 256, 256, 2, 1, 256, "f16", True),
+    (1, 1, 1, 1, 1, 64, "f16", False),
+]
+
+
+@pytest.mark.parametrize("case", DENSE, ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{c[6]}_{'causal' if c[7] else 'full'}")
+def test_dense_parity(qa, case):
+    B, Nq, Nk, Hq, Hkv, d, dt, causal = case
+    say(f"dense {case}")
+    spec = DenseSpec("dn", 301 + d, B, Hq, Hkv, Nq, Nk, d, k_bias_std=3.0, dtype=dt)
+    inp = dense_inputs(spec)
+    got = qa.dense_sage_attention(dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt),
+                                  is_causal=causal).cpu().numpy()
+    quant = oracle.sage_quantize(inp.q, inp.k, dt)
+    want = oracle.dense_sage_attention(quant, inp.v, dt, causal=causal)
+    assert_close(got, want, "dense")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_full_size_sampled(qa, causal):
+    spec = dense_sage()
+    say(f"dense full size {spec.name} causal={causal}")
+    inp = dense_inputs(spec)
+    got = qa.dense_sage_attention(dev_bits(inp.q, "f16"), dev_bits(inp.k, "f16"), dev_bits(inp.v, "f16"),
+                                  is_causal=causal)
+    torch.cuda.synchronize()
+    quant = oracle.sage_quantize(inp.q, inp.k, "f16")
+    rows = np.array([0, 1, 127, 128, 4095, 8191])
+    want = oracle.dense_sage_attention(quant, inp.v, "f16", causal=causal, rows=rows, heads=[0, 17, 31])
+    g = got.cpu().numpy()
+    for b in range(2):
+        for h in (0, 17, 31):
+            assert_close(g[b, rows, h], want[b, rows, h], f"dense b={b} h={h}")
