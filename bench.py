@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the INT8-QK paged-attention hot path on one MI355X.
+
+Headline workload: Qwen3.5-27B-shaped decode (24 query heads over 4 KV heads,
+head_dim 256, 32768 cached tokens, INT8 K with per-token scales, bf16 V).
+One step = the fused producer (qa_quantize_q_write_kv: quantize the new
+query token and write its K/V into the paged cache), then paged decode
+attention with split-K and combine (qa_paged_attention_decode). The metric
+is algorithmic KV bytes per second.
+
+Steps rotate over several independently allocated KV pools, so together
+they exceed the 256 MB Infinity Cache and each step streams its cache from
+HBM.
+
+Prints one JSON line. Extra keys: the roofline of the decode kernel (HIP
+events around each launch inside the timed region), the oracle's CPU
+throughput on a bounded sample, and throughput of the prefill and dense
+paths on their own workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5033.0      # dense INT8 MFMA, 256 CU x 2.4 GHz x 8192 ops/clk
+FP16_PEAK_TFLOPS = 2516.0
+
+
+def decode_bytes(spec) -> dict:
+    """Algorithmic bytes of one decode call and of one full step."""
+    d, Hq, Hkv = spec.head_dim, spec.num_q_heads, spec.num_kv_heads
+    tok = sum(spec.context_lens)
+    v_elem = 1 if spec.v_int8 else 2
+    attn = (tok * Hkv * (d + 4 + d * v_elem + (4 if spec.v_int8 else 0))      # K, sK, V, sV
+            + spec.num_seqs * spec.max_blocks_per_seq * 4                      # block table
+            + spec.num_seqs * Hq * (d + 4)                                     # q_i8 + q_scale
+            + spec.num_seqs * Hq * d * 4)                                      # fp32 output
+    quant = spec.num_seqs * Hq * (2 * d + d + 4)                               # bf16 in, int8 + scale out
+    write = spec.num_seqs * (Hkv * (2 * d * 2 + d + 4 + d * v_elem + (4 if spec.v_int8 else 0)) + 8)
+    return {"attention": attn, "step": attn + quant + write}
+
+
+def flash_ops(q_lens, ctx_lens, Hq, d, causal=True):
+    """QK (INT8) and PV (fp16) operations of prefill/dense: 2*d each per
+    visible (query, key) pair."""
+    pairs = 0
+    for tq, c in zip(q_lens, ctx_lens):
+        if causal:
+            off = c - tq
+            pairs += sum(min(c, off + i + 1) for i in range(tq))
+        else:
+            pairs += tq * c
+    pairs *= Hq
+    return 2 * d * pairs, 2 * d * pairs
+
+
+def dev_bits(torch, bits: np.ndarray, dtype: str = "bf16"):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def gpu_cache(torch, qa, inp):
+    spec = inp.spec
+    kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, spec.num_kv_heads, spec.head_dim,
+                                       torch.int8 if spec.v_int8 else torch.bfloat16)
+    qa.write_kv_cache(dev_bits(torch, inp.k), dev_bits(torch, inp.v), torch.from_numpy(inp.slot_mapping).cuda(),
+                      kc, ks, vc, vs)
+    return kc, ks, vc, vs
+
+
+def _mk_stream_events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def run_decode(args, torch, qa, W):
+    from workloads import qwen27b_decode, paged_inputs
+    spec = qwen27b_decode(args.context)
+    inp = paged_inputs(spec)
+    dev = torch.device("cuda:0")
+    d, Hq, Hkv = spec.head_dim, spec.num_q_heads, spec.num_kv_heads
+    # pool 0: write every token; pools 1..R-1: device copies at other addresses
+    slots = torch.from_numpy(inp.slot_mapping).to(dev)
+    kb, vb = dev_bits(torch, inp.k), dev_bits(torch, inp.v)
+    pools = []
+    for r in range(args.pools):
+        kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, Hkv, d, torch.bfloat16, zero=False)
+        if r == 0:
+            qa.write_kv_cache(kb, vb, slots, kc, ks, vc, vs)
+        else:
+            kc.copy_(pools[0][0]); ks.copy_(pools[0][1]); vc.copy_(pools[0][2])
+        pools.append((kc, ks, vc, vs))
+    # the step's new token is the last one of the context
+    k_new, v_new = kb[-1:].contiguous(), vb[-1:].contiguous()
+    slot_new = slots[-1:].contiguous()
+    del kb, vb
+    q = dev_bits(torch, inp.q)
+    tables = torch.from_numpy(inp.block_tables).to(dev)
+    lens = torch.from_numpy(inp.context_lens).to(dev)
+    p = qa.decode_params(spec.num_seqs, Hq, Hkv, d, spec.max_blocks_per_seq, spec.num_blocks,
+                         num_splits=args.splits)
+    splits = qa.decode_num_splits(p)
+    ws = qa.decode_workspace(p, dev)
+    out = torch.empty((spec.num_seqs, Hq, d), dtype=torch.float32, device=dev)
+    q_i8 = torch.empty((spec.num_seqs, Hq, d), dtype=torch.int8, device=dev)
+    q_sc = torch.empty((spec.num_seqs, Hq), dtype=torch.float32, device=dev)
+    import ctypes
+    L = qa.lib
+
+    def step(i, ev=None):
+        kc, ks, vc, vs = pools[i % len(pools)]
+        st = qa._stream()
+        # fused producer: quantize the query and write the new token's K/V
+        qa._check(L.qa_quantize_q_write_kv(qa._ptr(q), spec.num_seqs, Hq, Hq * d, d, qa._ptr(k_new),
+                                           qa._ptr(v_new), 1, Hkv, Hkv * d, d, qa._ptr(slot_new),
+                                           qa.QA_DT_BF16, d, spec.num_blocks, 16, qa._ptr(q_i8), qa._ptr(q_sc),
+                                           qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), qa.QA_DT_BF16, None, st))
+        if ev is not None:
+            ev[0].record()
+        qa._check(L.qa_paged_attention_decode(ctypes.byref(p), qa._ptr(q_i8), qa._ptr(q_sc), qa._ptr(kc),
+                                              qa._ptr(ks), qa._ptr(vc), None, qa._ptr(tables), qa._ptr(lens),
+                                              qa._ptr(ws), ws.numel(), qa._ptr(out), st))
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+
+    # decode-kernel duration: events around each launch, same step loop
+    evs = _mk_stream_events(torch, K)
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = float(np.mean(kern_ms))
+    nbytes = decode_bytes(spec)
+    return spec, {
+        "ms_per_step": ms_step,
+        "value": nbytes["step"] / (ms_step * 1e-3) / 1e9,
+        "kernel_ms": kern_avg,
+        "kernel_ms_p10_p90": [float(np.percentile(kern_ms, 10)), float(np.percentile(kern_ms, 90))],
+        "attn_bytes": nbytes["attention"],
+        "step_bytes": nbytes["step"],
+        "splits": splits,
+        "inp": inp,
+    }
+
+
+def cpu_baseline(spec, inp, budget_s):
+    """The oracle, untuned, on the decode workload: quantize the query and
+    run unsplit paged decode over the cache the oracle writes itself."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    caches = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks)
+    n, t_total = 0, 0.0
+    while t_total < budget_s or n == 0:
+        t = time.perf_counter()
+        q8, qs = oracle.quantize_q(inp.q)
+        oracle.paged_decode(q8, qs, caches, inp.block_tables, inp.context_lens, spec.num_kv_heads)
+        t_total += time.perf_counter() - t
+        n += 1
+        if n >= 50:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    by = decode_bytes(spec)["step"]
+    return {"value": by * n / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full decode steps (quantize_q + unsplit paged decode, fp64) of the "
+                      f"{spec.context_lens[0]}-token workload; {t_total:.1f} s on {os.cpu_count()} host cpus, "
+                      f"BLAS threads {threads}"}
+
+
+def run_prefill(torch, qa, reps):
+    from workloads import chunked_prefill, paged_inputs
+    spec = chunked_prefill()
+    inp = paged_inputs(spec)
+    kc, ks, vc, vs = gpu_cache(torch, qa, inp)
+    q8, qs = qa.quantize_q(dev_bits(torch, inp.q))
+    cu = torch.from_numpy(inp.cu_seqlens_q).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    out = torch.empty((spec.total_q, spec.num_q_heads, spec.head_dim), device="cuda")
+    f = lambda: qa.chunked_prefill_attention(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0], out=out)
+    for _ in range(3):
+        f()
+    evs = _mk_stream_events(torch, reps)
+    for a, b in evs:
+        a.record(); f(); b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    qk, pv = flash_ops(spec.query_lens, spec.context_lens, spec.num_q_heads, spec.head_dim)
+    tops = (qk + pv) / (ms * 1e-3) / 1e12
+    mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
+    return {"workload": "chunked_prefill 2048 new tokens on 16384 history, 24/4 heads, d256",
+            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed}
+
+
+def run_dense(torch, qa, reps, causal):
+    from workloads import dense_sage, dense_inputs
+    spec = dense_sage()
+    inp = dense_inputs(spec)
+    q, k, v = (dev_bits(torch, x, "f16") for x in (inp.q, inp.k, inp.v))
+    p = qa.dense_params(q, k, True, causal)
+    ws = qa.dense_sage_workspace(p)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    f = lambda: qa.dense_sage_attention(q, k, v, is_causal=causal, workspace=ws, out=out)
+    for _ in range(3):
+        f()
+    evs = _mk_stream_events(torch, reps)
+    for a, b in evs:
+        a.record(); f(); b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    B, H, N, d = spec.batch, spec.num_q_heads, spec.seq_q, spec.head_dim
+    qk, pv = flash_ops([N] * B, [N] * B, H, d, causal)
+    tops = (qk + pv) / (ms * 1e-3) / 1e12
+    mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
+    return {"workload": f"dense_sage B2 H32 N8192 d128 {'causal' if causal else 'non-causal'} "
+                        "(full chain: smooth_k + per-block quantization + attention)",
+            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--splits", type=int, default=0, help="split-K segments (0 = library choice)")
+    ap.add_argument("--pools", type=int, default=6, help="KV pools rotated across steps")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the prefill/dense lines")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_attention_quantize_amd as qa
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    spec, r = run_decode(args, torch, qa, args.warmup)
+    achieved = r["attn_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    res = {
+        "metric": "INT8-QK paged attention: decode KV GB/s; prefill/dense INT8 TOPS (% peak)",
+        "value": round(r["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 QK / fp16 PV",
+        "data": "synthetic",
+        "config": {"workload": "qwen27b_decode", "num_seqs": 1, "q_heads": 24, "kv_heads": 4, "head_dim": 256,
+                   "context": args.context, "block_size": 16, "k_cache": "int8 + fp32 per-token scale",
+                   "v_cache": "bf16", "num_splits": r["splits"], "kv_pools_rotated": args.pools,
+                   "step": "quantize_q_write_kv (fused producer, 1 token) + paged_attention_decode (split-K, fused combine)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_decode (qa_paged_attention_decode: split-K partials and combine in one kernel)",
+                     "kernel_ms": round(r["kernel_ms"], 5),
+                     "kernel_ms_p10_p90": [round(x, 5) for x in r["kernel_ms_p10_p90"]],
+                     "algorithmic_bytes_per_launch": r["attn_bytes"]},
+    }
+    if not args.no_extras:
+        res["extra"] = {"chunked_prefill": run_prefill(torch, qa, 20),
+                        "dense_sage_noncausal": run_dense(torch, qa, 10, False),
+                        "dense_sage_causal": run_dense(torch, qa, 10, True)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, r["inp"], args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,6 +110,24 @@ qa_status_t qa_write_kv_cache(const void* k, const void* v, qa_dtype_t dtype,
                               void* v_cache, qa_dtype_t v_cache_dtype, float* v_scale,
                               qa_stream_t stream);
 
+/*
+ * Fused producer of one step: quantize the new query rows (exactly as
+ * qa_quantize_q) and write the new K/V tokens into the paged cache (exactly
+ * as qa_write_kv_cache) in a single launch. [QK-MMAC] §4: the query is
+ * quantized once, inside the producer that also writes the KV cache, and
+ * every split-K segment reuses it (rotary embedding is not part of this
+ * library). Arguments are those of the two calls above; either part may be
+ * empty (num_q_tokens == 0 or num_kv_tokens == 0). q, k and v share `dtype`.
+ */
+qa_status_t qa_quantize_q_write_kv(const void* q, int64_t num_q_tokens, int32_t num_q_heads,
+                                   int64_t q_stride_token, int64_t q_stride_head, const void* k,
+                                   const void* v, int64_t num_kv_tokens, int32_t num_kv_heads,
+                                   int64_t kv_stride_token, int64_t kv_stride_head,
+                                   const int64_t* slot_mapping, qa_dtype_t dtype, int32_t head_dim,
+                                   int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale,
+                                   int8_t* k_cache, float* k_scale, void* v_cache,
+                                   qa_dtype_t v_cache_dtype, float* v_scale, qa_stream_t stream);
+
 /* Shape and options of a decode call (one query token per sequence). */
 typedef struct {
   int32_t num_seqs;
@@ -128,7 +146,10 @@ typedef struct {
 /* Number of split-K segments a decode call with these parameters uses. */
 int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p);
 
-/* Workspace bytes a decode call needs (0 when it runs unsplit). */
+/* Workspace bytes a decode call needs (0 when it runs unsplit): the split
+ * partials (max, sum and unnormalized output per split and query head). Its
+ * contents need no initialization. Calls that share a workspace must not
+ * run concurrently. */
 size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
 
 /*
@@ -138,14 +159,16 @@ size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
  * INT8 matrix instructions with INT32 accumulation; §3: K read through the
  * block table in its INT8 paged layout; §4: long contexts are cut into
  * segments (split-K) that reuse one quantized query; §5.1: the query heads
- * of one KV head share the matrix rows. P.V uses fp16 matrix instructions
- * with fp32 accumulation (P rounded to fp16; bf16 V widened to fp16; INT8 V
- * as codes with sV folded into P).
+ * of one KV head share the matrix rows. P.V uses 16-bit matrix instructions
+ * with fp32 accumulation: bf16 V directly against P written as the sum of two
+ * bf16 numbers (hi = bf16(p), lo = bf16(p - hi)); INT8 V as fp16 codes against
+ * fp16 P with the per-token V scale folded into P.
  *
- * Split-K: segment j of a sequence with ctx tokens covers tokens
- * [j*L, min((j+1)*L, ctx)) with L = 16 * ceil(ceil(ctx/16) / S). Each segment
- * stores (max, sum, unnormalized output) in the workspace and a combine
- * step merges them. S = 1 writes the output directly.
+ * Split-K: with P = ceil(max_blocks_per_seq / S), split j of a sequence
+ * covers its tokens [16*j*P, min(16*(j+1)*P, ctx)) (possibly none). Each
+ * split stores (max, sum, unnormalized output) in the workspace and a second
+ * kernel merges them. S = 1 writes the output directly. Results are
+ * bit-identical from run to run.
  *
  *   q_i8          [num_seqs, num_q_heads, head_dim] int8 (from qa_quantize_q)
  *   q_scale       [num_seqs, num_q_heads] fp32

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libqattn.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libqattn.so not found at {LIB_PATH}; build it with "
-        "`python -m quantized_attention_quantize_amd.build` (hipcc, gfx950)")
+        "`python quantized_attention_quantize_amd/build.py` (hipcc, gfx950)")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -63,6 +63,10 @@ _SIGS = {
     "qa_write_kv_cache": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i32, _i32, _i64, _i64,
                                           _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, ctypes.c_int,
                                           _c_void_p, _c_void_p]),
+    "qa_quantize_q_write_kv": (ctypes.c_int, [_c_void_p, _i64, _i32, _i64, _i64, _c_void_p, _c_void_p, _i64,
+                                               _i32, _i64, _i64, _c_void_p, ctypes.c_int, _i32, _i64, _i32,
+                                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                               ctypes.c_int, _c_void_p, _c_void_p]),
     "qa_paged_decode_num_splits": (_i32, [_P(DecodeParams)]),
     "qa_paged_decode_workspace_size": (_size, [_P(DecodeParams)]),
     "qa_paged_attention_decode": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_size, _c_void_p,
@@ -76,7 +80,11 @@ _SIGS = {
                                                                                         _c_void_p]),
 }
 for _name, (_res, _args) in _SIGS.items():
-    _fn = getattr(lib, _name)
+    try:
+        _fn = getattr(lib, _name)
+    except AttributeError as e:
+        raise ImportError(f"{LIB_PATH} lacks {_name}: the library is stale, rebuild it with "
+                          "`python quantized_attention_quantize_amd/build.py`") from e
     _fn.restype = _res
     _fn.argtypes = _args
 
@@ -151,6 +159,27 @@ def write_kv_cache(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale=None):
                                  _ptr(v_cache), _dt(v_cache.dtype), _ptr(v_scale), _stream()))
 
 
+def quantize_q_write_kv(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale=None, q_i8=None,
+                        q_scale=None):
+    """Fused producer: quantize q [Tq, Hq, d] and write k/v [Tk, Hkv, d] into the
+    cache in one launch. Returns (q_i8, q_scale)."""
+    _require_cuda(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale)
+    Tq, Hq, d = q.shape
+    Tk, Hkv, _ = k.shape
+    if q_i8 is None:
+        q_i8 = torch.empty((Tq, Hq, d), dtype=torch.int8, device=q.device)
+    if q_scale is None:
+        q_scale = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    if k.stride() != v.stride() or k.stride(2) != 1 or q.stride(2) != 1:
+        raise ValueError("k and v must share strides; innermost dims must be contiguous")
+    _check(lib.qa_quantize_q_write_kv(_ptr(q), Tq, Hq, q.stride(0), q.stride(1), _ptr(k), _ptr(v), Tk, Hkv,
+                                      k.stride(0), k.stride(1), _ptr(slot_mapping), _dt(q.dtype), d,
+                                      k_cache.shape[0], 16, _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
+                                      _ptr(k_scale), _ptr(v_cache), _dt(v_cache.dtype), _ptr(v_scale),
+                                      _stream()))
+    return q_i8, q_scale
+
+
 def decode_params(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                   v_int8=False, out_dtype=torch.float32, softmax_scale=0.0, num_splits=0) -> DecodeParams:
     return DecodeParams(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_blocks_per_seq, num_blocks,
@@ -162,6 +191,7 @@ def decode_num_splits(p: DecodeParams) -> int:
 
 
 def decode_workspace(p: DecodeParams, device="cuda") -> torch.Tensor:
+    """Decode workspace (split-K partials; no initialization needed)."""
     n = lib.qa_paged_decode_workspace_size(ctypes.byref(p))
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 

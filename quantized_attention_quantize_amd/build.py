@@ -1,6 +1,7 @@
 """Build libqattn.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-Usage: python -m quantized_attention_quantize_amd.build [--verbose]
+Usage: python quantized_attention_quantize_amd/build.py [--verbose]
+(run by path: importing the package needs the library this builds)
 """
 from __future__ import annotations
 

@@ -68,12 +68,23 @@ int32_t splits_of(const qa_decode_params_t* p) {
   return qa::choose_decode_splits(p->num_seqs, p->num_kv_heads, p->max_blocks_per_seq);
 }
 
-size_t decode_ws(const qa_decode_params_t* p, int32_t S) {
-  if (S <= 1) return 0;
+// Decode workspace: [partial O][partial (max, sum)], each part 256-byte aligned.
+struct DecodeWs {
+  size_t o, ml, total;
+};
+
+DecodeWs decode_layout(const qa_decode_params_t* p, int32_t S) {
+  DecodeWs w{};
+  if (S <= 1) return w;
   const size_t units = (size_t)p->num_seqs * p->num_q_heads * S;
-  const size_t o = units * p->head_dim * sizeof(float);
-  return ((o + 255) & ~(size_t)255) + units * 2 * sizeof(float);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.o = 0;
+  w.ml = al(units * p->head_dim * sizeof(float));
+  w.total = w.ml + al(units * 2 * sizeof(float));
+  return w;
 }
+
+size_t decode_ws(const qa_decode_params_t* p, int32_t S) { return decode_layout(p, S).total; }
 
 qa_status_t check_dense(const qa_dense_params_t* p) {
   QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
@@ -169,6 +180,48 @@ qa_status_t qa_write_kv_cache(const void* k, const void* v, qa_dtype_t dtype, in
                     "qa_write_kv_cache launch");
 }
 
+qa_status_t qa_quantize_q_write_kv(const void* q, int64_t num_q_tokens, int32_t num_q_heads,
+                                   int64_t q_stride_token, int64_t q_stride_head, const void* k,
+                                   const void* v, int64_t num_kv_tokens, int32_t num_kv_heads,
+                                   int64_t kv_stride_token, int64_t kv_stride_head,
+                                   const int64_t* slot_mapping, qa_dtype_t dtype, int32_t head_dim,
+                                   int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale,
+                                   int8_t* k_cache, float* k_scale, void* v_cache,
+                                   qa_dtype_t v_cache_dtype, float* v_scale, qa_stream_t stream) {
+  QA_REQUIRE(num_q_tokens >= 0 && num_kv_tokens >= 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 &&
+                 num_blocks > 0,
+             QA_ERR_INVALID_ARG, "bad shape");
+  QA_REQUIRE(dtype == QA_DT_BF16 || dtype == QA_DT_F16, QA_ERR_UNSUPPORTED, "dtype must be BF16 or F16");
+  QA_REQUIRE(v_cache_dtype == dtype || v_cache_dtype == QA_DT_I8, QA_ERR_UNSUPPORTED,
+             "v_cache_dtype must equal dtype or be I8");
+  QA_REQUIRE(supported_dim(head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+  QA_REQUIRE(block_size == 16, QA_ERR_UNSUPPORTED, "block_size %d != 16", block_size);
+  if (num_q_tokens == 0 && num_kv_tokens == 0) return QA_OK;
+  if (num_q_tokens > 0) {
+    QA_REQUIRE(q && q_i8 && q_scale, QA_ERR_INVALID_ARG, "null query pointer");
+    QA_REQUIRE(aligned16(q) && q_stride_token % 8 == 0 && q_stride_head % 8 == 0 && q_stride_token >= 0 &&
+                   q_stride_head >= 0,
+               QA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  }
+  if (num_kv_tokens > 0) {
+    QA_REQUIRE(k && v && slot_mapping && k_cache && k_scale && v_cache, QA_ERR_INVALID_ARG, "null cache pointer");
+    QA_REQUIRE(v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+    QA_REQUIRE(aligned16(k) && aligned16(v) && kv_stride_token % 8 == 0 && kv_stride_head % 8 == 0 &&
+                   kv_stride_token >= 0 && kv_stride_head >= 0 && aligned16(k_cache),
+               QA_ERR_INVALID_ARG, "k/v must be 16-byte aligned with strides that are multiples of 8 elements");
+  }
+  QA_REQUIRE((num_q_tokens * num_q_heads + num_kv_tokens * num_kv_heads) / 4 < (int64_t)INT32_MAX,
+             QA_ERR_UNSUPPORTED, "too many rows");
+  qa::ProducerArgs a{};
+  a.q = q; a.k = k; a.v = v; a.slots = slot_mapping; a.bf16 = dtype == QA_DT_BF16;
+  a.v_int8 = v_cache_dtype == QA_DT_I8; a.D = head_dim; a.Hq = num_q_heads; a.Hkv = num_kv_heads;
+  a.q_rows = num_q_tokens * num_q_heads; a.kv_rows = num_kv_tokens * num_kv_heads;
+  a.q_st = q_stride_token; a.q_sh = q_stride_head; a.kv_st = kv_stride_token; a.kv_sh = kv_stride_head;
+  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_cache = k_cache; a.k_scale = k_scale; a.v_cache = v_cache;
+  a.v_scale = v_scale;
+  return hip_status(qa::launch_producer(a, (hipStream_t)stream), "qa_quantize_q_write_kv launch");
+}
+
 int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p) {
   if (check_decode(p) != QA_OK) return -1;
   return splits_of(p);
@@ -202,9 +255,9 @@ qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t*
   qa::DecodeArgs a{};
   a.q = q_i8; a.q_scale = q_scale; a.k_cache = k_cache; a.k_scale = k_scale; a.v_cache = v_cache;
   a.v_scale = v_scale; a.tables = block_tables; a.ctx_lens = context_lens; a.out = out;
-  const size_t units = (size_t)p->num_seqs * p->num_q_heads * S;
-  a.ws_o = (float*)workspace;
-  a.ws_ml = need ? (float*)((char*)workspace + ((units * p->head_dim * sizeof(float) + 255) & ~(size_t)255)) : nullptr;
+  const DecodeWs w = decode_layout(p, S);
+  a.ws_o = need ? (float*)((char*)workspace + w.o) : nullptr;
+  a.ws_ml = need ? (float*)((char*)workspace + w.ml) : nullptr;
   a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
   a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
   a.num_splits = S; a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);

@@ -16,6 +16,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -26,6 +27,21 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 
 __device__ __forceinline__ v4f mfma_f16(v8h a, v8h b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// p ~= hi + lo with hi = bf16(p) and lo = bf16(p - hi): a two-term bf16
+// expansion with relative error near 2^-16, so a bf16 matrix product of
+// (hi, lo) against bf16 data keeps about fp32-level accuracy for P.
+__device__ __forceinline__ void split_bf16x8(const float (&p)[8], v8bf& hi, v8bf& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    hi[j] = (__bf16)p[j];
+    lo[j] = (__bf16)(p[j] - (float)hi[j]);
+  }
 }
 
 // ---- 16-bit storage formats -------------------------------------------------

@@ -20,10 +20,173 @@
 namespace qa {
 namespace {
 
-constexpr int kWaves = 4;
+// Workgroup shape: waves per workgroup and 32-token tiles each wave keeps in
+// flight (loads of the next tile are issued before the current one is
+// consumed). Chosen by measurement on MI355X.
+#ifndef QA_DECODE_WAVES
+#define QA_DECODE_WAVES 8
+#endif
+#ifndef QA_DECODE_TILES_IN_FLIGHT
+#define QA_DECODE_TILES_IN_FLIGHT 1
+#endif
+constexpr int kWaves = QA_DECODE_WAVES;
+constexpr int kTP = QA_DECODE_TILES_IN_FLIGHT;
+
+// Mask words for 8 values held in 16-bit (bf16) or 8-bit (int8) lanes of
+// 32-bit words: keep the first `nvalid` values, zero the rest. Slots past
+// the context may hold anything (even NaN patterns), and 0 * NaN would
+// poison the matrix product, so they are cleared first.
+__device__ __forceinline__ uint32_t keep_mask16(int w, int nvalid) {
+  return (2 * w < nvalid ? 0x0000FFFFu : 0u) | (2 * w + 1 < nvalid ? 0xFFFF0000u : 0u);
+}
+__device__ __forceinline__ uint32_t keep_mask8(int w, int nvalid) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m |= (4 * w + b < nvalid ? 0xFFu : 0u) << (8 * b);
+  return m;
+}
+
+// Registers of one 32-token tile: K fragments, V^T fragments and scales.
+template <int D, bool V_I8>
+struct Tile {
+  static constexpr int KS = D / 64, CG = D / 16;
+  v4i kr[2][KS];
+  uint4 v16[V_I8 ? 1 : CG];
+  uint2 v8[V_I8 ? CG : 1];
+  float4 ska, skb, sva, svb;
+};
+
+struct DecodeLane {
+  int n, g, kvh, Hkv, tau0;
+};
+
+// Issue every load of one tile whose two blocks are p0, p1.
+template <int D, bool V_I8, bool EXPORT_QK>
+__device__ __forceinline__ void issue_tile(Tile<D, V_I8>& t, const DecodeArgs& a, const DecodeLane& L,
+                                           int p0, int p1) {
+  constexpr int KS = D / 64, CG = D / 16;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int tau = L.tau0 + 4 * u;
+    const int pb = tau >= 16 ? p1 : p0;
+    const int8_t* kp = a.k_cache + ((int64_t)pb * L.Hkv + L.kvh) * (D / 16) * 256 + (tau & 15) * 16 + L.g * 256;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) t.kr[u][s] = *reinterpret_cast<const v4i*>(kp + s * 1024);
+  }
+  if constexpr (!EXPORT_QK) {
+    // tokens 8g .. 8g+7 of the tile live in one block at slots so .. so+7
+    const int pbs = L.g >= 2 ? p1 : p0;
+    const int so = 8 * (L.g & 1);
+    const int64_t sidx = ((int64_t)pbs * L.Hkv + L.kvh) * 16 + so;
+    t.ska = *reinterpret_cast<const float4*>(a.k_scale + sidx);
+    t.skb = *reinterpret_cast<const float4*>(a.k_scale + sidx + 4);
+    if constexpr (V_I8) {
+      t.sva = *reinterpret_cast<const float4*>(a.v_scale + sidx);
+      t.svb = *reinterpret_cast<const float4*>(a.v_scale + sidx + 4);
+    }
+    const int64_t vbase = (((int64_t)pbs * L.Hkv + L.kvh) * D + L.n) * 16 + so;
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      if constexpr (V_I8)
+        t.v8[c] = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.v_cache) + vbase + c * 256);
+      else
+        t.v16[c] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v_cache) + vbase + c * 256);
+    }
+  }
+}
+
+// Per-wave online-softmax state.
+template <int D>
+struct Acc {
+  v4f O[D / 16];
+  float m, l;
+};
+
+// Consume one tile: INT8 QK, score recovery, online softmax, P.V.
+// tl = first token of this lane's 8-token slice, t1 = end of the segment.
+template <int D, bool V_I8, bool EXPORT_QK>
+__device__ __forceinline__ void consume_tile(Tile<D, V_I8>& t, Acc<D>& A, const v4i (&qf)[D / 64], float qsc,
+                                             int tl, int t1, int32_t* qk_dst) {
+  constexpr int KS = D / 64, CG = D / 16;
+  // ---- S^T = K Q^T ----------------------------------------------------------
+  v4i acc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    acc[u] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc[u] = mfma_i8(t.kr[u][s], qf[s], acc[u]);
+  }
+  if constexpr (EXPORT_QK) {
+    if (qk_dst != nullptr) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tl + j < t1) qk_dst[tl + j] = acc[j >> 2][j & 3];
+    }
+    return;
+  }
+  const int nvalid = min(max(t1 - tl, 0), 8);
+
+  // ---- [QK-MMAC] §1: recover each score before the softmax (base 2) -------
+  const float sk[8] = {t.ska.x, t.ska.y, t.ska.z, t.ska.w, t.skb.x, t.skb.y, t.skb.z, t.skb.w};
+  float sc[8];
+  float mt = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float v = (float)acc[j >> 2][j & 3] * qsc * sk[j];
+    sc[j] = j < nvalid ? v : kNegInf;
+    mt = fmaxf(mt, sc[j]);
+  }
+  mt = group4_max(mt);
+  const float m_new = fmaxf(A.m, mt);
+  const float mref = m_new == kNegInf ? 0.0f : m_new;
+  const float alpha = fast_exp2(A.m - mref);
+  float p[8], psum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = fast_exp2(sc[j] - mref);
+    psum += p[j];
+  }
+  A.l = A.l * alpha + psum;
+  A.m = m_new;
+
+  // P operand. INT8 V: fp16 P with the per-token V scale folded in, and
+  // fp16 codes. bf16 V: the raw bf16 values with P as a two-term bf16
+  // expansion (two products), so V needs no conversion.
+  v8h pf;
+  v8bf ph, pl;
+  if constexpr (V_I8) {
+    const float sv[8] = {t.sva.x, t.sva.y, t.sva.z, t.sva.w, t.svb.x, t.svb.y, t.svb.z, t.svb.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pf[j] = (_Float16)(j < nvalid ? p[j] * sv[j] : 0.0f);
+  } else {
+    split_bf16x8(p, ph, pl);
+  }
+#pragma unroll
+  for (int c = 0; c < CG; ++c) A.O[c] *= alpha;
+
+  // ---- O^T += V^T P^T: channel 16c+n, tokens 8g..8g+7 of the tile ---------
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if constexpr (V_I8) {
+      uint2 w = t.v8[c];
+      w.x &= keep_mask8(0, nvalid);
+      w.y &= keep_mask8(1, nvalid);
+      A.O[c] = mfma_f16(i8x8_to_f16x8(w), pf, A.O[c]);
+    } else {
+      uint4 w = t.v16[c];
+      w.x &= keep_mask16(0, nvalid);
+      w.y &= keep_mask16(1, nvalid);
+      w.z &= keep_mask16(2, nvalid);
+      w.w &= keep_mask16(3, nvalid);
+      const v8bf vb = __builtin_bit_cast(v8bf, w);
+      A.O[c] = mfma_bf16(vb, ph, A.O[c]);
+      A.O[c] = mfma_bf16(vb, pl, A.O[c]);
+    }
+  }
+}
 
 template <int D, bool V_I8, bool EXPORT_QK>
-__global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode(DecodeArgs a) {
   constexpr int KS = D / 64;   // INT8 K-steps
   constexpr int CG = D / 16;   // 16-channel groups of the output
   extern __shared__ float smem[];
@@ -33,12 +196,15 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int G = a.G, Hq = a.Hq, Hkv = a.Hkv, S = a.num_splits;
 
-  const int ctx = a.ctx_lens[seq];
-  const int nblk = (ctx + 15) >> 4;
-  const int per = (nblk + S - 1) / S;
-  const int t0 = min(split * per * 16, ctx);
-  const int t1 = min(t0 + per * 16, ctx);
-  const int ntiles = (t1 - t0 + 31) >> 5;
+  // Segment of this split: blocks [split*per, (split+1)*per) of the block
+  // table, cut at the context length. It depends only on host-known sizes, so
+  // the block-table entries are fetched together with the context length
+  // instead of after it.
+  const int per = (a.max_blocks + S - 1) / S;
+  const int blk0 = split * per;
+  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
+  // lane j: block (j & 1) of this wave's tile j/2 (first batch of 32 tiles)
+  int tab = trow[min(blk0 + 2 * (wave + kWaves * (lane >> 1)) + (lane & 1), a.max_blocks - 1)];
 
   // Query fragments (B operand): head n of this KV group, channels 64s+16g..+15.
   const int h = kvh * G + n;
@@ -52,134 +218,70 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
       qf[s] = v4i{0, 0, 0, 0};
   }
   const float qsc = live_col ? a.q_scale[(int64_t)seq * Hq + h] * a.scale_log2 : 0.0f;
+  const int ctx = a.ctx_lens[seq];
+  const int t0 = min(blk0 * 16, ctx);
+  const int t1 = min(t0 + per * 16, ctx);
+  const int ntiles = (t1 - t0 + 31) >> 5;
+  const int ntw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;   // this wave's tiles
 
-  float m_run = kNegInf, l_run = 0.0f;
-  v4f O[CG];
+  int32_t* qk_dst = nullptr;
+  if constexpr (EXPORT_QK)
+    if (live_col) qk_dst = a.acc_out + ((int64_t)seq * Hq + h) * (int64_t)a.max_blocks * 16;
+
+  Acc<D> A;
+  A.m = kNegInf;
+  A.l = 0.0f;
 #pragma unroll
-  for (int c = 0; c < CG; ++c) O[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CG; ++c) A.O[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  const DecodeLane L{n, g, kvh, Hkv, 8 * (n >> 2) + (n & 3)};
 
-  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
-  // token of matrix row n in instruction u, relative to the tile start
-  const int tau0 = 8 * (n >> 2) + (n & 3);
-
-  for (int tile = wave; tile < ntiles; tile += kWaves) {
-    const int tb = t0 + tile * 32;
-    const int lb = tb >> 4;
-    const int p0 = trow[lb];
-    const int p1 = (tb + 16 < t1) ? trow[lb + 1] : p0;
-
-    v4i acc[2];
+  for (int kb = 0; kb < ntw; kb += 32) {
+    if (kb > 0)
+      tab = trow[min(blk0 + 2 * (wave + kWaves * (kb + (lane >> 1))) + (lane & 1), a.max_blocks - 1)];
+    const int nk = min(32, ntw - kb);
+    for (int k = 0; k < nk; k += kTP) {
+      Tile<D, V_I8> T[kTP];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tau = tau0 + 4 * u;
-      const int pb = tau >= 16 ? p1 : p0;
-      const int8_t* kb = a.k_cache + ((int64_t)pb * Hkv + kvh) * (D / 16) * 256 + (tau & 15) * 16;
-      acc[u] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        v4i kf = *reinterpret_cast<const v4i*>(kb + (4 * s + g) * 256);
-        acc[u] = mfma_i8(kf, qf[s], acc[u]);
+      for (int i = 0; i < kTP; ++i) {
+        // a tile past the end re-reads the last one (cache hits) and is not consumed
+        const int ki = min(k + i, nk - 1);
+        const int tb = t0 + 32 * (wave + kWaves * (kb + ki));
+        const int p0 = __builtin_amdgcn_readlane(tab, 2 * ki);
+        // The second block exists only if the tile has tokens in it; table
+        // entries past the sequence are never used as addresses.
+        const int p1 = tb + 16 < t1 ? __builtin_amdgcn_readlane(tab, 2 * ki + 1) : p0;
+        issue_tile<D, V_I8, EXPORT_QK>(T[i], a, L, p0, p1);
       }
-    }
-
-    if constexpr (EXPORT_QK) {
-      if (live_col) {
-        int32_t* dst = a.acc_out + ((int64_t)seq * Hq + h) * (int64_t)a.max_blocks * 16;
+      // keep every load of the tile(s) issued before any of them is consumed
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = tb + 8 * g + j;
-          if (t < t1) dst[t] = acc[j >> 2][j & 3];
+      for (int i = 0; i < kTP; ++i) {
+        if (k + i < nk) {
+          const int tb = t0 + 32 * (wave + kWaves * (kb + k + i));
+          consume_tile<D, V_I8, EXPORT_QK>(T[i], A, qf, qsc, tb + 8 * g, t1, qk_dst);
         }
       }
-      continue;
-    }
-
-    // Tokens 8g .. 8g+7 of the tile live in one block at slots so .. so+7.
-    const int pbs = g >= 2 ? p1 : p0;
-    const int so = 8 * (g & 1);
-    const int64_t sidx = ((int64_t)pbs * Hkv + kvh) * 16 + so;
-    const float4 ska = *reinterpret_cast<const float4*>(a.k_scale + sidx);
-    const float4 skb = *reinterpret_cast<const float4*>(a.k_scale + sidx + 4);
-    const float sk[8] = {ska.x, ska.y, ska.z, ska.w, skb.x, skb.y, skb.z, skb.w};
-    const int tl = tb + 8 * g;   // first token of this lane's slice
-
-    // [QK-MMAC] §1: recover each score before the softmax (base-2 units).
-    float sc[8];
-    float mt = kNegInf;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = (float)acc[j >> 2][j & 3] * qsc * sk[j];
-      sc[j] = (tl + j < t1) ? v : kNegInf;
-      mt = fmaxf(mt, sc[j]);
-    }
-    mt = group4_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float mref = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - mref);
-    float p[8], psum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = fast_exp2(sc[j] - mref);
-      psum += p[j];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    v8h pf;
-    if constexpr (V_I8) {
-      // fold the per-token V scale into P: sum_t p_t (code_t * sV_t) v-code
-      const float4 sva = *reinterpret_cast<const float4*>(a.v_scale + sidx);
-      const float4 svb = *reinterpret_cast<const float4*>(a.v_scale + sidx + 4);
-      const float sv[8] = {sva.x, sva.y, sva.z, sva.w, svb.x, svb.y, svb.z, svb.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = (_Float16)((tl + j < t1) ? p[j] * sv[j] : 0.0f);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = (_Float16)p[j];
-    }
-
-#pragma unroll
-    for (int c = 0; c < CG; ++c) O[c] *= alpha;
-
-    // V^T operand: channel 16c+n, tokens 8g..8g+7 of the tile.
-    const bool full = tl + 8 <= t1;
-#pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      const int64_t vrow = (((int64_t)pbs * Hkv + kvh) * D + 16 * c + n) * 16 + so;
-      v8h vf;
-      if constexpr (V_I8) {
-        vf = i8x8_to_f16x8(*reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.v_cache) + vrow));
-      } else {
-        vf = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v_cache) + vrow));
-      }
-      if (!full) {
-        // slots past the context may hold anything (even NaN): zero them
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (tl + j >= t1) vf[j] = (_Float16)0.0f;
-      }
-      O[c] = mfma_f16(vf, pf, O[c]);
     }
   }
   if constexpr (EXPORT_QK) return;
 
   // ---- merge the waves of this workgroup ----------------------------------
-  l_run = group4_sum(l_run);
+  const float l_run = group4_sum(A.l);
   float* sm_ml = smem;                       // [kWaves][16][2]
   float* sm_o = smem + kWaves * 32;          // [kWaves][G][D]
   if (g == 0) {
-    sm_ml[(wave * 16 + n) * 2] = m_run;
+    sm_ml[(wave * 16 + n) * 2] = A.m;
     sm_ml[(wave * 16 + n) * 2 + 1] = l_run;
   }
   if (live_col) {
 #pragma unroll
     for (int c = 0; c < CG; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[((int64_t)wave * G + n) * D + 16 * c + 4 * g + i] = O[c][i];
+      *reinterpret_cast<float4*>(sm_o + ((int64_t)wave * G + n) * D + 16 * c + 4 * g) =
+          make_float4(A.O[c][0], A.O[c][1], A.O[c][2], A.O[c][3]);
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
     const int hn = idx / D, ch = idx - hn * D;
     float M = kNegInf;
 #pragma unroll
@@ -210,42 +312,94 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   }
 }
 
-// One workgroup of D threads per (query head, sequence): merges S partials.
+// Merge the S partials of each (query head, sequence):
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// A workgroup of 256 threads covers 16 float4 columns of one head; thread t
+// owns column t % 16 of share t / 16 of the splits and loads its (m, l, O)
+// values in batches of 16 independent loads with a running maximum; the
+// shares are merged through LDS.
+template <int D>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
-                                                 const float* __restrict__ ws_ml, int32_t Hq,
-                                                 int32_t D, int32_t S, bool out_bf16, void* out) {
-  const int h = blockIdx.x, seq = blockIdx.y, ch = threadIdx.x;
+                                                 const float* __restrict__ ws_ml, int32_t Hq, int32_t S,
+                                                 bool out_bf16, void* out) {
+  constexpr int CW = 16;                 // float4 columns per workgroup
+  constexpr int SH = 256 / CW;           // split shares
+  __shared__ float4 part[SH][CW];
+  __shared__ float2 mlpart[SH];
+  const int h = blockIdx.x, seq = blockIdx.y, t = threadIdx.x;
+  const int cw = t % CW, sh = t / CW;
+  const int c4 = blockIdx.z * CW + cw;
   const int64_t base = ((int64_t)seq * Hq + h) * S;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ws_ml[(base + s) * 2]);
-  float lsum = 0.0f, o = 0.0f;
-  if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float m = ws_ml[(base + s) * 2];
-      const float wt = fast_exp2(m - M);
-      lsum += wt * ws_ml[(base + s) * 2 + 1];
-      o += wt * ws_o[(base + s) * D + ch];
+  float m = kNegInf, lsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = sh; s0 < S; s0 += 16 * SH) {
+    float2 ml[16];
+    float4 o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = min(s0 + i * SH, S - 1);
+      ml[i] = *reinterpret_cast<const float2*>(ws_ml + (base + s) * 2);
+      o[i] = *reinterpret_cast<const float4*>(ws_o + (base + s) * D + 4 * c4);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (s0 + i * SH >= S || ml[i].x == kNegInf) continue;
+      const float mn = fmaxf(m, ml[i].x);
+      const float a0 = fast_exp2(m - mn), a1 = fast_exp2(ml[i].x - mn);
+      acc.x = acc.x * a0 + a1 * o[i].x; acc.y = acc.y * a0 + a1 * o[i].y;
+      acc.z = acc.z * a0 + a1 * o[i].z; acc.w = acc.w * a0 + a1 * o[i].w;
+      lsum = lsum * a0 + a1 * ml[i].y;
+      m = mn;
     }
   }
-  const float r = lsum > 0.0f ? o / lsum : 0.0f;
-  const int64_t oi = ((int64_t)seq * Hq + h) * D + ch;
-  if (out_bf16) reinterpret_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_bf16_bits(r);
-  else reinterpret_cast<float*>(out)[oi] = r;
+  part[sh][cw] = acc;
+  if (cw == 0) mlpart[sh] = make_float2(m, lsum);
+  __syncthreads();
+  if (sh == 0) {
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < SH; ++k) M = fmaxf(M, mlpart[k].x);
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int k = 0; k < SH; ++k) {
+        const float wt = fast_exp2(mlpart[k].x - M);
+        const float4 q = part[k][cw];
+        r.x += wt * q.x; r.y += wt * q.y; r.z += wt * q.z; r.w += wt * q.w;
+        l += wt * mlpart[k].y;
+      }
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int64_t oi = ((int64_t)seq * Hq + h) * D + 4 * c4;
+    if (out_bf16) {
+      uint2 w;
+      w.x = f32_to_bf16_bits(r.x * inv) | (f32_to_bf16_bits(r.y * inv) << 16);
+      w.y = f32_to_bf16_bits(r.z * inv) | (f32_to_bf16_bits(r.w * inv) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) = w;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    }
+  }
 }
 
 template <int D, bool V_I8, bool EXPORT_QK>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.Hkv, a.num_seqs);
+  // LDS: per-wave partials [kWaves][G][D] plus (max, sum) pairs.
   const size_t lds = EXPORT_QK ? 0 : (size_t)(kWaves * 32 + kWaves * a.G * D) * sizeof(float);
   auto kern = k_decode<D, V_I8, EXPORT_QK>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  kern<<<grid, 256, lds, st>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || EXPORT_QK || a.num_splits == 1) return e;
-  k_combine<<<dim3(a.Hq, a.num_seqs), D, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, D, a.num_splits, a.out_bf16, a.out);
+  kern<<<grid, kWaves * 64, lds, st>>>(a);
+  if (!EXPORT_QK && a.num_splits > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_combine<D><<<dim3(a.Hq, a.num_seqs, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
+                                                               a.out_bf16, a.out);
+  }
   return hipGetLastError();
 }
 
@@ -264,11 +418,11 @@ hipError_t dispatch(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks) {
-  // Aim for about two workgroups per compute unit (256 CUs), but keep at
-  // least 8 blocks (128 tokens, one 32-token tile per wave) per segment.
+  // Aim for one workgroup per compute unit (256 CUs), but keep at least
+  // 16 blocks (256 tokens) per segment.
   const int64_t units = (int64_t)num_seqs * Hkv;
-  int64_t s = (512 + units - 1) / units;
-  const int64_t cap = max_blocks / 8 > 0 ? max_blocks / 8 : 1;
+  int64_t s = (256 + units - 1) / units;
+  const int64_t cap = max_blocks / 16 > 0 ? max_blocks / 16 : 1;
   if (s > cap) s = cap;
   if (s > 256) s = 256;
   return (int32_t)(s < 1 ? 1 : s);

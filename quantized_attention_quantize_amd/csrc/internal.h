@@ -20,6 +20,24 @@ hipError_t launch_write_kv_cache(const void* k, const void* v, bool bf16, int64_
                                  float* k_scale, void* v_cache, bool v_int8, float* v_scale,
                                  hipStream_t st);
 
+struct ProducerArgs {
+  const void* q;           // [q_tokens, Hq, D] rows at q + t*q_st + h*q_sh
+  const void* k;           // [kv_tokens, Hkv, D] rows at k/v + t*kv_st + h*kv_sh
+  const void* v;
+  const int64_t* slots;
+  bool bf16, v_int8;
+  int32_t D, Hq, Hkv;
+  int64_t q_rows, kv_rows;  // tokens * heads
+  int64_t q_st, q_sh, kv_st, kv_sh;
+  int8_t* q_i8;
+  float* q_scale;
+  int8_t* k_cache;
+  float* k_scale;
+  void* v_cache;
+  float* v_scale;
+};
+hipError_t launch_producer(const ProducerArgs& a, hipStream_t st);
+
 struct SagePrepArgs {
   const void* q;
   const void* k;

@@ -46,15 +46,12 @@ __device__ __forceinline__ uint32_t quant_lane(const float (&v)[E], float amax, 
   return packed;
 }
 
-// One wave per (token, head) row; 4 rows per workgroup.
+// Quantize one (token, head) row of head_dim values with one wave.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
-                                                       int32_t H, int64_t st, int64_t sh,
-                                                       int8_t* __restrict__ q, float* __restrict__ scale) {
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ x, int64_t row, int32_t H, int64_t st,
+                                          int64_t sh, int8_t* __restrict__ q, float* __restrict__ scale,
+                                          int lane) {
   constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const int64_t t = row / H;
   const int h = (int)(row - t * H);
   float v[E];
@@ -68,19 +65,15 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restric
   if (lane == 0) scale[row] = s;
 }
 
-// One wave per (token, KV head): K -> INT8 codes in [blk, h, D/16, 16, 16] plus a
-// per-token scale; V copied (or quantized) into [blk, h, D, 16].
+// Write one (token, KV head) row: K -> INT8 codes in [blk, h, D/16, 16, 16] plus
+// a per-token scale; V copied (or quantized) into [blk, h, D, 16].
 template <int D, bool BF16, bool V_I8>
-__global__ __launch_bounds__(256) void k_write_kv(const uint16_t* __restrict__ k,
-                                                  const uint16_t* __restrict__ v, int64_t rows,
-                                                  int32_t H, int64_t st, int64_t sh,
-                                                  const int64_t* __restrict__ slots,
-                                                  int8_t* __restrict__ kc, float* __restrict__ ks,
-                                                  void* __restrict__ vc, float* __restrict__ vs) {
+__device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                             int64_t row, int32_t H, int64_t st, int64_t sh,
+                                             const int64_t* __restrict__ slots, int8_t* __restrict__ kc,
+                                             float* __restrict__ ks, void* __restrict__ vc,
+                                             float* __restrict__ vs, int lane) {
   constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const int64_t t = row / H;
   const int h = (int)(row - t * H);
   const int64_t slot = slots[t];
@@ -119,6 +112,45 @@ __global__ __launch_bounds__(256) void k_write_kv(const uint16_t* __restrict__ k
     uint16_t* vd = reinterpret_cast<uint16_t*>(vc);
 #pragma unroll
     for (int e = 0; e < E; ++e) vd[(bh * D + ch + e) * 16 + off] = v[src + e];
+  }
+}
+
+// One wave per (token, head) row; 4 rows per workgroup.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int32_t H, int64_t st, int64_t sh,
+                                                       int8_t* __restrict__ q, float* __restrict__ scale) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  quant_row<D, BF16>(x, row, H, st, sh, q, scale, threadIdx.x & 63);
+}
+
+template <int D, bool BF16, bool V_I8>
+__global__ __launch_bounds__(256) void k_write_kv(const uint16_t* __restrict__ k,
+                                                  const uint16_t* __restrict__ v, int64_t rows,
+                                                  int32_t H, int64_t st, int64_t sh,
+                                                  const int64_t* __restrict__ slots,
+                                                  int8_t* __restrict__ kc, float* __restrict__ ks,
+                                                  void* __restrict__ vc, float* __restrict__ vs) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  write_kv_row<D, BF16, V_I8>(k, v, row, H, st, sh, slots, kc, ks, vc, vs, threadIdx.x & 63);
+}
+
+// Fused producer: workgroups [0, qblocks) quantize query rows, the rest write
+// K/V rows into the cache (one launch for both).
+template <int D, bool BF16, bool V_I8>
+__global__ __launch_bounds__(256) void k_producer(ProducerArgs a, int64_t qblocks) {
+  const int lane = threadIdx.x & 63;
+  if ((int64_t)blockIdx.x < qblocks) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row < a.q_rows)
+      quant_row<D, BF16>((const uint16_t*)a.q, row, a.Hq, a.q_st, a.q_sh, a.q_i8, a.q_scale, lane);
+  } else {
+    const int64_t row = ((int64_t)blockIdx.x - qblocks) * 4 + (threadIdx.x >> 6);
+    if (row < a.kv_rows)
+      write_kv_row<D, BF16, V_I8>((const uint16_t*)a.k, (const uint16_t*)a.v, row, a.Hkv, a.kv_st, a.kv_sh,
+                                  a.slots, a.k_cache, a.k_scale, a.v_cache, a.v_scale, lane);
   }
 }
 
@@ -345,6 +377,27 @@ hipError_t launch_write_kv_cache(const void* k, const void* v, bool bf16, int64_
     default: QA_WKV(256);
   }
 #undef QA_WKV
+}
+
+template <int D, bool BF16>
+hipError_t producer_d(const ProducerArgs& a, hipStream_t s) {
+  const int64_t qb = (a.q_rows + 3) / 4, kb = (a.kv_rows + 3) / 4;
+  if (qb + kb == 0) return hipSuccess;
+  if (a.v_int8)
+    k_producer<D, BF16, true><<<(unsigned)(qb + kb), 256, 0, s>>>(a, qb);
+  else
+    k_producer<D, BF16, false><<<(unsigned)(qb + kb), 256, 0, s>>>(a, qb);
+  return hipGetLastError();
+}
+
+hipError_t launch_producer(const ProducerArgs& a, hipStream_t s) {
+#define QA_PROD(DD) return a.bf16 ? producer_d<DD, true>(a, s) : producer_d<DD, false>(a, s)
+  switch (a.D) {
+    case 64: QA_PROD(64);
+    case 128: QA_PROD(128);
+    default: QA_PROD(256);
+  }
+#undef QA_PROD
 }
 
 size_t sage_partial_bytes(int32_t B, int32_t Nk, int32_t Hkv, int32_t D) {

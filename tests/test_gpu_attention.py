@@ -226,3 +226,22 @@ def test_dense_full_size_sampled(qa, causal):
     for b in range(2):
         for h in (0, 17, 31):
             assert_close(g[b, rows, h], want[b, rows, h], f"dense b={b} h={h}")
+
+
+def test_decode_workspace_reuse_across_calls(qa):
+    # one workspace serves calls with different split counts; partials left
+    # by earlier calls must not leak into later results
+    say("decode workspace reuse")
+    spec = PagedSpec("reuse", 17, 3, 24, 4, 256, [3000, 77, 1500], [1, 1, 1], k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    kc, ks, vc, vs = gpu_cache(qa, inp, False)
+    q8, qs = qa.quantize_q(dev_bits(inp.q))
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    big = qa.decode_params(3, 24, 4, 256, inp.block_tables.shape[1], spec.num_blocks, num_splits=64)
+    ws = qa.decode_workspace(big)
+    want = _decode_oracle(inp)
+    for S in (64, 7, 64, 2, 13):
+        out = qa.paged_attention_decode(q8, qs, kc, ks, vc, vs, tables, lens, num_splits=S, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), want, f"reuse S={S}")

@@ -181,3 +181,24 @@ def test_named_workload_caches_bit_exact(qa, mk):
     assert np.array_equal(kc.cpu().numpy(), want["k_cache"])
     assert np.array_equal(ks.cpu().numpy(), want["k_scale"])
     assert np.array_equal(vc.cpu().view(torch.int16).numpy().view(np.uint16), want["v_cache"])
+
+
+@pytest.mark.parametrize("v_int8", [False, True])
+def test_fused_producer_bit_exact(qa, v_int8):
+    spec = PagedSpec("prod", 91, 2, 24, 4, 256, [300, 40], [5, 1], k_bias_std=2.0, v_int8=v_int8, pool_blocks=30)
+    say(f"quantize_q_write_kv v_int8={v_int8}")
+    inp = paged_inputs(spec)
+    kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, 4, 256, torch.int8 if v_int8 else torch.bfloat16)
+    q8, qs = qa.quantize_q_write_kv(dev_bits(inp.q), dev_bits(inp.k), dev_bits(inp.v),
+                                    torch.from_numpy(inp.slot_mapping).cuda(), kc, ks, vc, vs)
+    torch.cuda.synchronize()
+    w8, wsc = oracle.quantize_q(inp.q)
+    want = oracle_cache(inp, v_int8)
+    assert np.array_equal(q8.cpu().numpy(), w8) and np.array_equal(qs.cpu().numpy(), wsc)
+    assert np.array_equal(kc.cpu().numpy(), want["k_cache"])
+    assert np.array_equal(ks.cpu().numpy(), want["k_scale"])
+    if v_int8:
+        assert np.array_equal(vc.cpu().numpy(), want["v_cache"])
+        assert np.array_equal(vs.cpu().numpy(), want["v_scale"])
+    else:
+        assert np.array_equal(vc.cpu().view(torch.int16).numpy().view(np.uint16), want["v_cache"])
