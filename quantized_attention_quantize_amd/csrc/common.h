@@ -71,31 +71,39 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 }
 
 // 8 packed bf16 (one 16-byte load) -> 8 fp16 operands. Exact for |v| in the
-// fp16 normal range; smaller magnitudes round to fp16 subnormals.
+// fp16 normal range; smaller magnitudes round to fp16 subnormals. Pairs go
+// through one packed fp32 -> fp16 conversion each.
 __device__ __forceinline__ v8h bf16x8_to_f16x8(uint4 w) {
   v8h r;
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[2 * i] = (_Float16)__uint_as_float(ws[i] << 16);
-    r[2 * i + 1] = (_Float16)__uint_as_float(ws[i] & 0xFFFF0000u);
+    const v2h h = (v2h){(_Float16)__uint_as_float(ws[i] << 16), (_Float16)__uint_as_float(ws[i] & 0xFFFF0000u)};
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
   }
   return r;
 }
 
 __device__ __forceinline__ v8h f16x8_from_u4(uint4 w) { return __builtin_bit_cast(v8h, w); }
 
-// 8 int8 codes (one 8-byte load) -> 8 fp16 operands (exact).
+// 8 int8 codes (one 8-byte load) -> 8 fp16 operands (exact). Each code c is
+// biased to the byte c + 128 and placed under the fp16 exponent of 1024, which
+// gives the fp16 value 1152 + c exactly; one packed fp16 subtraction of 1152
+// per pair then leaves c.
 __device__ __forceinline__ v8h i8x8_to_f16x8(uint2 w) {
   v8h r;
-  const uint32_t ws[2] = {w.x, w.y};
+  const uint32_t ws[2] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u};
+  const v2h bias = (v2h){(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int v = (int)(int8_t)((ws[i] >> (8 * b)) & 0xFF);
-      r[4 * i + b] = (_Float16)v;
-    }
+    // bytes [u0, 0x64, u1, 0x64] and [u2, 0x64, u3, 0x64]
+    const v2h lo = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, ws[i], 0x04010400u)) - bias;
+    const v2h hi = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, ws[i], 0x04030402u)) - bias;
+    r[4 * i + 0] = lo[0];
+    r[4 * i + 1] = lo[1];
+    r[4 * i + 2] = hi[0];
+    r[4 * i + 3] = hi[1];
   }
   return r;
 }
@@ -108,17 +116,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48)
+// max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// v_permlane16_swap / v_permlane32_swap with both operands equal to v leave
+// the value of lane l^16 (resp. l^32) in one of the two results and v itself
+// in the other (lane layout checked on gfx950), so each step is two VALU
+// operations and no LDS traffic.
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -2,51 +2,124 @@
 // SageAttention-style forward ([SAGE-MACA] attention-kernel pipeline), one
 // kernel template.
 //
-// Workgroup = 4 waves = 128 query rows of one query head. Each 64-token
-// KV tile (4 blocks of 16) is staged in LDS and shared by the 4 waves.
+// Workgroup = 4 waves x (16*QG) query rows of one query head. 64-token KV
+// tiles are double-buffered in LDS: while the waves compute on one buffer,
+// every thread holds its share of the next tile in registers and writes it
+// to the other buffer afterwards (one barrier per tile). V is stored in LDS
+// as fp16 (bf16 rounded to fp16, INT8 codes exact) in the cache's
+// [block][channel][16 tokens] order.
+//
 // Matrix products are computed transposed, as in the decode kernel:
 //   S^T = K Q^T   (v_mfma_i32_16x16x64_i8; A = 16 keys from LDS, B = 16 queries
 //                  held in registers for the whole KV loop)
 //   O^T += V^T P^T (v_mfma_f32_16x16x32_f16; A = 16 channels x 32 keys from LDS,
 //                  B = P straight from the score registers)
-// Key rows are permuted within each 32-token half so that every lane owns
-// 8 consecutive keys of one query (see decode.hip).
+// Key rows are permuted within each 32-token half so that every lane owns 8
+// consecutive keys of one query. The softmax row sums run on the matrix
+// units as well: a product of P with an all-ones block sums exactly the fp16
+// P that multiplies V.
 //
-// The dense path reads its K codes and V from the same 16-token block layout
-// the cache uses, written by the preprocessing step, with block b*ceil(N/16) + t/16.
+// Online softmax in base 2 with lazy rescaling: the running maximum (and the
+// O/l rescale) is only moved when a tile's maximum exceeds it by more than
+// 2^8, so P stays below 256 (well inside fp16) and most tiles skip the
+// rescale. Masks are applied only on tiles that cross the end of the context
+// or the causal diagonal ([SAGE-MACA]: the causal mask is needed on the
+// diagonal tiles only; tiles above it are skipped).
+//
+// Tile staging is branch-free: the four physical blocks of a tile are
+// wave-uniform (scalar) loads, with the logical block clamped to the last
+// one of the sequence; keys past the context are masked in the scores and
+// their V rows cleared when the tile is written to LDS.
+//
+// Workgroup order is XCD-aware: the 8 XCDs receive workgroups round-robin,
+// so consecutive work items (the query tiles of one head, which read the
+// same K/V) are assigned to the same XCD and share its L2.
 #include "common.h"
 #include "internal.h"
 
 namespace qa {
 namespace {
 
-constexpr int QT = 128;    // query rows per workgroup
-constexpr int KT = 64;     // keys per LDS tile
+constexpr int KT = 64;      // keys per LDS tile
+constexpr int NW = 4;       // waves per workgroup
+constexpr int NT = NW * 64; // threads per workgroup
+constexpr float kRescaleSlack = 8.0f;   // lazy-rescale threshold (base-2 units)
 
 enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 
-template <int D, int VK, bool DENSE, bool CAUSAL>
-__global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
+#ifndef QA_FLASH_QG
+#define QA_FLASH_QG 2
+#endif
+#ifndef QA_FLASH_WPE
+#define QA_FLASH_WPE 2
+#endif
+#ifndef QA_FLASH_ROWSUM_MFMA
+#define QA_FLASH_ROWSUM_MFMA 1
+#endif
+
+// 8 fp32 -> 8 fp16 through four packed conversions
+__device__ __forceinline__ v8h pack8(const float (&p)[8]) {
+  v8h r;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const v2h h = (v2h){(_Float16)p[j], (_Float16)p[j + 1]};
+    r[j] = h[0];
+    r[j + 1] = h[1];
+  }
+  return r;
+}
+
+template <int D, int VK>
+struct Staged {
+  static constexpr int VB = VK == kVI8 ? 1 : 2;    // bytes per cached V element
+  static constexpr int KUB = D;                    // 16-byte K units per block
+  static constexpr int VUB = D * VB;               // 16-byte V units per block
+  static constexpr int KU = 4 * KUB / NT;          // K units per thread
+  static constexpr int VU = 4 * VUB / NT;          // V units per thread
+  uint4 k[KU];
+  uint4 v[VU];
+  float ks, vs;
+};
+
+template <int D, int QG, int VK, bool DENSE, bool CAUSAL>
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? QA_FLASH_WPE : 1))) void k_flash(FlashArgs a) {
+  using St = Staged<D, VK>;
   constexpr int KS = D / 64;
   constexpr int CG = D / 16;
-  constexpr int VB = VK == kVI8 ? 1 : 2;                 // bytes per V element
-  constexpr int K_BYTES = KT * D;                        // int8 K tile
-  constexpr int V_BYTES = KT * D * VB;
-  __shared__ __attribute__((aligned(16))) int8_t s_k[K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[V_BYTES];
-  __shared__ float s_ks[KT];
-  __shared__ float s_vs[KT];
+  constexpr int QT = NW * 16 * QG;                 // query rows per workgroup
+  constexpr int VB = St::VB, KUB = St::KUB, VUB = St::VUB, KU = St::KU, VU = St::VU;
+  // K: 4 blocks of D*16 bytes, each padded by 64 bytes so that the two
+  // blocks read by one 16-lane pass of ds_read_b128 fall on complementary
+  // banks. V: the two 16-byte halves of each channel's 16-token row are
+  // swapped when bit 3 of the channel is set, so 16 consecutive channels
+  // cover all banks.
+  constexpr int KBS = D * 16 + 64;
+  constexpr bool kRowSumMfma = QA_FLASH_ROWSUM_MFMA && VK != kVI8;         // INT8 V folds sV into P: sum P on the VALU
+  __shared__ __attribute__((aligned(16))) int8_t s_k[2][4 * KBS];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][KT * D];
+  __shared__ float s_ks[2][KT];
+  __shared__ float s_vs[2][KT];
 
-  const int qtile = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // ---- work item (XCD-aware order) ----------------------------------------
+  const int nqt = ((DENSE ? a.Nq : a.max_seqlen_q) + QT - 1) / QT;
+  const int total = (int)gridDim.x;
+  int wid = blockIdx.x;
+  if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int qtile = wid % nqt;
+  const int h = (wid / nqt) % a.Hq;
+  const int z = wid / (nqt * a.Hq);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int Hq = a.Hq, Hkv = a.Hkv;
   const int kvh = h / a.G;
 
-  int64_t q_row0;  // global row of query 0 of this sequence / batch
+  int64_t q_row0;
   int Tq, kv_len;
   const int32_t* trow = nullptr;
-  int64_t blk_base = 0;  // dense: first block of this batch
+  int64_t blk_base = 0;
   if constexpr (DENSE) {
     q_row0 = (int64_t)z * a.Nq;
     Tq = a.Nq;
@@ -61,183 +134,276 @@ __global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
   const int q0 = qtile * QT;
   if (q0 >= Tq) return;
   const int offset = kv_len - Tq;   // bottom-right causal alignment
+  const int last_blk = (kv_len + 15) / 16 - 1;
 
-  // ---- query fragments and scales -----------------------------------------
-  v4i qf[2][KS];
-  float qsc[2];
-  int qi[2];
+  // ---- query fragments and scales -------------------------------------------
+  v4i qf[QG][KS];
+  float qsc[QG];
+  int qi[QG];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
-    qi[qg] = q0 + 32 * wave + 16 * qg + n;
+  for (int qg = 0; qg < QG; ++qg) {
+    qi[qg] = q0 + wave * 16 * QG + 16 * qg + n;
     const bool ok = qi[qg] < Tq;
     const int8_t* qp = a.q + ((q_row0 + qi[qg]) * Hq + h) * D + 16 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qf[qg][s] = ok ? *reinterpret_cast<const v4i*>(qp + 64 * s) : v4i{0, 0, 0, 0};
     if constexpr (DENSE) {
-      const int nqb = (a.Nq + QT - 1) / QT;
-      qsc[qg] = a.q_scale[((int64_t)z * Hq + h) * nqb + qtile] * a.scale_log2;
+      const int nqb = (a.Nq + 127) / 128;
+      qsc[qg] = a.q_scale[((int64_t)z * Hq + h) * nqb + min(qi[qg] / 128, nqb - 1)] * a.scale_log2;
     } else {
       qsc[qg] = ok ? a.q_scale[(q_row0 + qi[qg]) * Hq + h] * a.scale_log2 : 0.0f;
     }
   }
+  const int wq_first = q0 + wave * 16 * QG;   // first query row of this wave
 
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-  v4f O[2][CG];
+  float m_run[QG], l_run[QG];
+  v4f O[QG][CG];
+  v4f Ls[QG];                                  // row sums from the matrix units
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg)
+  for (int qg = 0; qg < QG; ++qg) {
+    m_run[qg] = kNegInf;
+    l_run[qg] = 0.0f;
+    Ls[qg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < CG; ++c) O[qg][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  v8h ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.0f;
 
-  int kv_end = kv_len;
+  int kv_end = kv_len;   // keys past kv_end are hidden from every query of the workgroup
   if constexpr (CAUSAL) kv_end = min(kv_len, min(q0 + QT, Tq) - 1 + offset + 1);
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
-  const int nblk_seq = (kv_len + 15) / 16;
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int kbase = tile * KT;
-    // ---- stage K, V (and per-token scales) of 4 blocks into LDS -----------
-    {
-      // K: 4 blocks x D/16 chunks x 256 bytes, 16 bytes per thread per step
-      constexpr int KU = 4 * D;                  // 16-byte units
-      for (int u = threadIdx.x; u < KU; u += 256) {
-        const int b = u / D, r = u % D;          // r = 16-byte unit within the block
-        const int lb = kbase / 16 + b;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (lb < nblk_seq) {
-          const int64_t pb = DENSE ? blk_base + lb : (int64_t)trow[lb];
-          w = *reinterpret_cast<const uint4*>(a.k_blocks + (pb * Hkv + kvh) * (int64_t)D * 16 + (int64_t)r * 16);
-        }
-        *reinterpret_cast<uint4*>(s_k + u * 16) = w;
-      }
-      constexpr int VU = 4 * D * 16 * VB / 16;   // 16-byte units of V
-      constexpr int TPU = 16 / VB;               // tokens per unit
-      for (int u = threadIdx.x; u < VU; u += 256) {
-        const int b = u / (VU / 4), r = u % (VU / 4);
-        const int lb = kbase / 16 + b;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (lb < nblk_seq) {
-          const int64_t pb = DENSE ? blk_base + lb : (int64_t)trow[lb];
-          w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.v_blocks) +
-                                               (pb * Hkv + kvh) * (int64_t)D * 16 * VB + (int64_t)r * 16);
-          // zero the slots past the context (they may hold anything)
-          const int t_first = lb * 16 + (r % (16 / TPU)) * TPU;
-          if (t_first + TPU > kv_len) {
-            uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // ---- tile staging: global -> registers -> LDS ---------------------------
+  const int64_t k_head = (int64_t)kvh * D * 16;    // K bytes before this KV head in a block
+  const int64_t k_blk = (int64_t)Hkv * D * 16;     // K bytes per physical block
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same value, held in a scalar
+  auto fetch = [&](St& st, int tile) {
+    // unit i of this thread lies in block (i*NT + 64*wave) / units-per-block of
+    // the tile: wave-uniform, so its physical block is a scalar
+    auto phys = [&](int b) -> int64_t {
+      const int lb = min(tile * 4 + b, last_blk);
+      return DENSE ? blk_base + lb : (int64_t)trow[lb];
+    };
 #pragma unroll
-            for (int e = 0; e < TPU; ++e) {
-              if (t_first + e >= kv_len) {
-                const int bit = e * VB * 8;
-                ws[bit / 32] &= ~(((VB == 2) ? 0xFFFFu : 0xFFu) << (bit % 32));
-              }
-            }
-            w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
-          }
-        }
-        *reinterpret_cast<uint4*>(s_v + u * 16) = w;
-      }
-      if constexpr (!DENSE) {
-        if (threadIdx.x < KT) {
-          const int t = kbase + threadIdx.x;
-          const int lb = t / 16;
-          float ks = 0.0f, vs = 0.0f;
-          if (t < kv_len) {
-            const int64_t si = ((int64_t)trow[lb] * Hkv + kvh) * 16 + (t & 15);
-            ks = a.k_scale[si];
-            if constexpr (VK == kVI8) vs = a.v_scale[si];
-          }
-          s_ks[threadIdx.x] = ks;
-          s_vs[threadIdx.x] = vs;
-        }
+    for (int i = 0; i < KU; ++i) {
+      const int b = (i * NT + 64 * wave_s) / KUB;
+      const int8_t* base = a.k_blocks + phys(b) * k_blk + k_head;
+      st.k[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)((tid + i * NT) % KUB) * 16u);
+    }
+#pragma unroll
+    for (int i = 0; i < VU; ++i) {
+      const int b = (i * NT + 64 * wave_s) / VUB;
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * VB;
+      st.v[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)((tid + i * NT) % VUB) * 16u);
+    }
+    if constexpr (!DENSE) {
+      if (tid < KT) {
+        const int lb = min(tile * 4 + (tid >> 4), last_blk);
+        const int64_t si = ((int64_t)trow[lb] * Hkv + kvh) * 16 + (tid & 15);
+        st.ks = a.k_scale[si];
+        st.vs = VK == kVI8 ? a.v_scale[si] : 0.0f;
       }
     }
-    __syncthreads();
+  };
+  auto commit = [&](const St& st, int buf, int tile) {
+    const int kbase = tile * KT;
+    const bool tail = kbase + KT > kv_len;       // the tile reaches past the context
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + i * NT;
+      const int b = (i * NT + 64 * wave_s) / KUB;
+      *reinterpret_cast<uint4*>(&s_k[buf][b * KBS + (u % KUB) * 16]) = st.k[i];
+    }
+    // V rows of keys past the context are cleared (the cache may hold anything there)
+#pragma unroll
+    for (int i = 0; i < VU; ++i) {
+      const int u = tid + i * NT;
+      const int b = (i * NT + 64 * wave_s) / VUB, r = u % VUB;
+      const int ch = VB == 2 ? r >> 1 : r;          // channel of this unit
+      const int row = (b * D + ch) * 16;            // fp16 element index of the channel row
+      const int sw = (ch >> 3) & 1;                 // half swap for this channel
+      if constexpr (VB == 2) {
+        v8h f = VK == kVF16 ? f16x8_from_u4(st.v[i]) : bf16x8_to_f16x8(st.v[i]);
+        if (tail) {
+          const int t_first = kbase + b * 16 + (r & 1) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t_first + e >= kv_len) f[e] = (_Float16)0.0f;
+        }
+        *reinterpret_cast<v8h*>(&s_v[buf][row + (((r & 1) ^ sw) << 3)]) = f;
+      } else {
+        const uint4 w = st.v[i];
+        v8h f0 = i8x8_to_f16x8(make_uint2(w.x, w.y));
+        v8h f1 = i8x8_to_f16x8(make_uint2(w.z, w.w));
+        if (tail) {
+          const int t_first = kbase + b * 16;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (t_first + e >= kv_len) f0[e] = (_Float16)0.0f;
+            if (t_first + 8 + e >= kv_len) f1[e] = (_Float16)0.0f;
+          }
+        }
+        *reinterpret_cast<v8h*>(&s_v[buf][row + (sw << 3)]) = f0;
+        *reinterpret_cast<v8h*>(&s_v[buf][row + ((1 ^ sw) << 3)]) = f1;
+      }
+    }
+    if constexpr (!DENSE) {
+      if (tid < KT) {
+        const bool in = kbase + tid < kv_len;
+        s_ks[buf][tid] = in ? st.ks : 0.0f;
+        s_vs[buf][tid] = in ? st.vs : 0.0f;
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    St st;
+    fetch(st, 0);
+    commit(st, 0, 0);
+  }
+  __syncthreads();
+
+  const int nkb = DENSE ? (a.Nk + KT - 1) / KT : 1;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const int kbase = tile * KT;
+    // the next tile (past the last one the clamped blocks are re-read and the
+    // spare buffer written but never used)
+    St nxt;
+    fetch(nxt, tile + 1);
 
     float tsc = 1.0f;   // dense: key-block scale of this tile
-    if constexpr (DENSE) {
-      const int nkb = (a.Nk + KT - 1) / KT;
-      tsc = a.k_scale[((int64_t)z * Hkv + kvh) * nkb + tile];
+    if constexpr (DENSE) tsc = a.k_scale[((int64_t)z * Hkv + kvh) * nkb + tile];
+
+    // ---- S^T = K Q^T for the 64 keys x (16*QG) queries -------------------------
+    // acc[qg][2*half + u][i] holds key 32*half + 8*g + 4*u + i of query n
+    v4i acc[QG][4];
+#pragma unroll
+    for (int hu = 0; hu < 4; ++hu) {
+      const int tau = 32 * (hu >> 1) + 8 * (n >> 2) + 4 * (hu & 1) + (n & 3);
+      const int8_t* kp = &s_k[buf][(tau >> 4) * KBS + (tau & 15) * 16 + g * 256];
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) acc[qg][hu] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v4i kf = *reinterpret_cast<const v4i*>(kp + s * 1024);
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) acc[qg][hu] = mfma_i8(kf, qf[qg][s], acc[qg][hu]);
+      }
     }
 
+    // key of x[j] below: kbase + 32*(j/8) + 8*g + j%8
+    const int tl = 8 * g;
+    // masks only on tiles that cross the context end or the causal diagonal
+    bool need_mask = kbase + KT > kv_len;
+    if constexpr (CAUSAL) need_mask = need_mask || (kbase + KT - 1 > wq_first + offset);
+    float sk[16], sv[16];
+    if constexpr (!DENSE) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // ---- S^T = K Q^T for 32 keys x 32 queries --------------------------
-      v4i acc[2][2];   // [qg][u]
+      for (int j = 0; j < 16; ++j) sk[j] = s_ks[buf][32 * (j >> 3) + tl + (j & 7)];
+    }
+    if constexpr (VK == kVI8) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tau = 32 * half + 8 * (n >> 2) + 4 * u + (n & 3);
-        const int8_t* kp = s_k + (tau >> 4) * (D * 16) + (tau & 15) * 16;
+      for (int j = 0; j < 16; ++j) sv[j] = s_vs[buf][32 * (j >> 3) + tl + (j & 7)];
+    }
+
+    v8h pf[QG][2];
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) acc[qg][u] = v4i{0, 0, 0, 0};
+    for (int qg = 0; qg < QG; ++qg) {
+      // score_j = x[j] * f with one lane factor f >= 0 (dense: the Q and K
+      // block scales; paged: the Q scale, sK folded into x)
+      float x[16], f, mx;
+      if constexpr (DENSE) {
+        f = qsc[qg] * tsc;
+        int im = max(acc[qg][0][0], acc[qg][0][1]);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const v4i kf = *reinterpret_cast<const v4i*>(kp + (4 * s + g) * 256);
+        for (int j = 2; j < 16; j += 2) im = max(im, max(acc[qg][j >> 2][j & 3], acc[qg][j >> 2][(j & 3) + 1]));
 #pragma unroll
-          for (int qg = 0; qg < 2; ++qg) acc[qg][u] = mfma_i8(kf, qf[qg][s], acc[qg][u]);
+        for (int j = 0; j < 16; ++j) x[j] = (float)acc[qg][j >> 2][j & 3];
+        mx = (float)im;
+      } else {
+        f = qsc[qg];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = (float)acc[qg][j >> 2][j & 3] * sk[j];
+        mx = fmaxf(x[0], x[1]);
+#pragma unroll
+        for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
+      }
+      uint32_t vis = 0xFFFFu;   // visible keys of this lane (bit j: the key of x[j])
+      if (need_mask) {
+        const int pos = qi[qg] + offset;
+        vis = 0;
+        mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int tk = kbase + 32 * (j >> 3) + tl + (j & 7);
+          bool ok = tk < kv_len;
+          if constexpr (CAUSAL) ok = ok && tk <= pos;
+          vis |= ok ? 1u << j : 0u;
+          mx = ok ? fmaxf(mx, x[j]) : mx;
         }
       }
-
-      const int tl = 32 * half + 8 * g;     // this lane's first key within the tile
-      float sk[8], sv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sk[j] = DENSE ? 1.0f : s_ks[tl + j];
-        sv[j] = VK == kVI8 ? s_vs[tl + j] : 1.0f;
-      }
-
-      v8h pf[2];
-#pragma unroll
-      for (int qg = 0; qg < 2; ++qg) {
-        const int pos = qi[qg] + offset;    // newest visible key of this query
-        const float rs = DENSE ? qsc[qg] * tsc : qsc[qg];
-        float sc[8];
-        float mt = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = kbase + tl + j;
-          bool vis = t < kv_len;
-          if constexpr (CAUSAL) vis = vis && t <= pos;
-          const float v = (float)acc[qg][j >> 2][j & 3] * rs * sk[j];
-          sc[j] = vis ? v : kNegInf;
-          mt = fmaxf(mt, sc[j]);
-        }
-        mt = group4_max(mt);
+      float mt = mx == kNegInf ? kNegInf : mx * f;
+      mt = group4_max(mt);
+      // lazy rescale: move the reference only when it is exceeded by > 2^8
+      if (__any(mt > m_run[qg] + kRescaleSlack)) {
         const float m_new = fmaxf(m_run[qg], mt);
-        const float mref = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run[qg] - mref);
-        float psum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = fast_exp2(sc[j] - mref);
-          psum += p;
-          pf[qg][j] = (_Float16)(VK == kVI8 ? p * sv[j] : p);
-        }
-        l_run[qg] = l_run[qg] * alpha + psum;
-        m_run[qg] = m_new;
+        const float alpha = fast_exp2(m_run[qg] - (m_new == kNegInf ? 0.0f : m_new));
+        l_run[qg] *= alpha;
+        Ls[qg] *= alpha;
 #pragma unroll
         for (int c = 0; c < CG; ++c) O[qg][c] *= alpha;
+        m_run[qg] = m_new;
       }
+      const float mref = m_run[qg] == kNegInf ? 0.0f : m_run[qg];
+      float p[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, -mref));
+      if (need_mask) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = (vis >> j) & 1u ? p[j] : 0.0f;
+      }
+      if constexpr (!kRowSumMfma) {
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) psum += p[j];
+        l_run[qg] += psum;
+      }
+      if constexpr (VK == kVI8) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] *= sv[j];   // fold the per-token V scale into P
+      }
+      pf[qg][0] = pack8(*reinterpret_cast<const float(*)[8]>(&p[0]));
+      pf[qg][1] = pack8(*reinterpret_cast<const float(*)[8]>(&p[8]));
+    }
 
-      // ---- O^T += V^T P^T ----------------------------------------------------
-      const int vb = tl >> 4, so = tl & 15;
+    // ---- O^T += V^T P^T (and the row sums against an all-ones block) ---------
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
-        const uint8_t* vp = s_v + ((vb * D + 16 * c + n) * 16 + so) * VB;
-        v8h vf;
-        if constexpr (VK == kVI8) vf = i8x8_to_f16x8(*reinterpret_cast<const uint2*>(vp));
-        else if constexpr (VK == kVF16) vf = f16x8_from_u4(*reinterpret_cast<const uint4*>(vp));
-        else vf = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(vp));
+        const int chn = 16 * c + n;
+        const v8h vf = *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + chn) * 16 + (((so >> 3) ^ ((chn >> 3) & 1)) << 3)]);
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) O[qg][c] = mfma_f16(vf, pf[qg], O[qg][c]);
+        for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vf, pf[qg][half], O[qg][c]);
+      }
+      if constexpr (kRowSumMfma) {
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
       }
     }
+    commit(nxt, buf ^ 1, tile + 1);
     __syncthreads();
   }
 
   // ---- normalize and store ----------------------------------------------------
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
-    const float l = group4_sum(l_run[qg]);
+  for (int qg = 0; qg < QG; ++qg) {
+    const float l = kRowSumMfma ? Ls[qg][0] : group4_sum(l_run[qg]);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (qi[qg] >= Tq) continue;
     const int64_t ob = ((q_row0 + qi[qg]) * Hq + h) * D + 4 * g;
@@ -264,10 +430,13 @@ __global__ __launch_bounds__(256) void k_flash(FlashArgs a) {
 
 template <int D, int VK, bool DENSE, bool CAUSAL>
 hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
+  constexpr int QG = QA_FLASH_QG;
+  constexpr int QT = NW * 16 * QG;
   const int qtiles = ((DENSE ? a.Nq : a.max_seqlen_q) + QT - 1) / QT;
   if (qtiles == 0 || a.num_seqs == 0) return hipSuccess;
-  const dim3 grid(qtiles, a.Hq, a.num_seqs);
-  k_flash<D, VK, DENSE, CAUSAL><<<grid, 256, 0, st>>>(a);
+  const int64_t total = (int64_t)qtiles * a.Hq * a.num_seqs;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  k_flash<D, QG, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NT, 0, st>>>(a);
   return hipGetLastError();
 }
 
