@@ -12,8 +12,9 @@ Steps rotate over several independently allocated KV pools, so together
 they exceed the 256 MB Infinity Cache and each step streams its cache from
 HBM.
 
-Prints one JSON line. Extra keys: the roofline of the decode kernel (HIP
-events around each launch inside the timed region), the oracle's CPU
+Prints one JSON line. Extra keys: the roofline of the decode split kernel
+(HIP events around batches of back-to-back launches of the call's first
+phase, after the timed step loop), the oracle's CPU
 throughput on a bounded sample, and throughput of the prefill and dense
 paths on their own workloads.
 """
@@ -78,6 +79,35 @@ def gpu_cache(torch, qa, inp):
     return kc, ks, vc, vs
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen27b_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_quantize_amd", "csrc", f)
+                  for f in ("decode.hip", "common.h", "internal.h")]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    """HBM bytes per k_decode launch from the committed counter summary, or
+    None when the summary is missing or the kernel sources have changed
+    since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.split(":", 1) for line in fh if line.startswith(("traffic_bytes_per_launch:",
+                                                                            "kernel_source_sha256:")))
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256", "").strip() != kernel_source_digest():
+        return None
+    return int(kv["traffic_bytes_per_launch"].strip())
+
+
 def _mk_stream_events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
@@ -116,21 +146,26 @@ def run_decode(args, torch, qa, W):
     import ctypes
     L = qa.lib
 
-    def step(i, ev=None):
+    def produce(i):
         kc, ks, vc, vs = pools[i % len(pools)]
-        st = qa._stream()
         # fused producer: quantize the query and write the new token's K/V
         qa._check(L.qa_quantize_q_write_kv(qa._ptr(q), spec.num_seqs, Hq, Hq * d, d, qa._ptr(k_new),
                                            qa._ptr(v_new), 1, Hkv, Hkv * d, d, qa._ptr(slot_new),
                                            qa.QA_DT_BF16, d, spec.num_blocks, 16, qa._ptr(q_i8), qa._ptr(q_sc),
-                                           qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), qa.QA_DT_BF16, None, st))
-        if ev is not None:
-            ev[0].record()
+                                           qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), qa.QA_DT_BF16, None, qa._stream()))
+        return kc, ks, vc, vs
+
+    def step(i):
+        kc, ks, vc, vs = produce(i)
         qa._check(L.qa_paged_attention_decode(ctypes.byref(p), qa._ptr(q_i8), qa._ptr(q_sc), qa._ptr(kc),
                                               qa._ptr(ks), qa._ptr(vc), None, qa._ptr(tables), qa._ptr(lens),
-                                              qa._ptr(ws), ws.numel(), qa._ptr(out), st))
-        if ev is not None:
-            ev[1].record()
+                                              qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
+
+    def partials(i):
+        kc, ks, vc, vs = pools[i % len(pools)]
+        qa._check(L.qa_paged_attention_decode_partials(
+            ctypes.byref(p), qa._ptr(q_i8), qa._ptr(q_sc), qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), None,
+            qa._ptr(tables), qa._ptr(lens), qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
 
     for i in range(W):
         step(i)
@@ -147,19 +182,29 @@ def run_decode(args, torch, qa, W):
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / K
 
-    # decode-kernel duration: events around each launch, same step loop
-    evs = _mk_stream_events(torch, K)
-    torch.cuda.synchronize()
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    kern_avg = float(np.mean(kern_ms))
+    # k_decode alone: batches of back-to-back launches of the call's first
+    # phase (pools rotated as in the step loop) between two HIP events on
+    # torch's current stream, which the library launches on. The host
+    # enqueues a launch faster than the kernel runs, so the events see the
+    # kernels and the gaps between them, not the host.
+    def batches(fn, n_batches, per):
+        evs = _mk_stream_events(torch, n_batches)
+        torch.cuda.synchronize()
+        for b in range(n_batches):
+            evs[b][0].record()
+            for j in range(per):
+                fn(b * per + j)
+            evs[b][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(e) / per for a, e in evs]
+
+    per = 10
+    kern_ms = batches(partials, max(1, K // per), per)
     nbytes = decode_bytes(spec)
     return spec, {
         "ms_per_step": ms_step,
         "value": nbytes["step"] / (ms_step * 1e-3) / 1e9,
-        "kernel_ms": kern_avg,
+        "kernel_ms": float(np.mean(kern_ms)),
         "kernel_ms_p10_p90": [float(np.percentile(kern_ms, 10)), float(np.percentile(kern_ms, 90))],
         "attn_bytes": nbytes["attention"],
         "step_bytes": nbytes["step"],
@@ -252,6 +297,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill/dense lines")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device copy of BYTES (the reference for the memory counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -264,8 +311,19 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.copy_calibration:
+        n = args.copy_calibration // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
+
     spec, r = run_decode(args, torch, qa, args.warmup)
     achieved = r["attn_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    traffic = decode_traffic()
     res = {
         "metric": "INT8-QK paged attention: decode KV GB/s; prefill/dense INT8 TOPS (% peak)",
         "value": round(r["value"], 2),
@@ -282,10 +340,11 @@ def main():
         "config": {"workload": "qwen27b_decode", "num_seqs": 1, "q_heads": 24, "kv_heads": 4, "head_dim": 256,
                    "context": args.context, "block_size": 16, "k_cache": "int8 + fp32 per-token scale",
                    "v_cache": "bf16", "num_splits": r["splits"], "kv_pools_rotated": args.pools,
-                   "step": "quantize_q_write_kv (fused producer, 1 token) + paged_attention_decode (split-K, fused combine)"},
+                   "step": "quantize_q_write_kv (fused producer, 1 token) + paged_attention_decode "
+                           "(split kernel, then combine kernel)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_decode (qa_paged_attention_decode: split-K partials and combine in one kernel)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_decode (the split kernel of qa_paged_attention_decode)",
                      "kernel_ms": round(r["kernel_ms"], 5),
                      "kernel_ms_p10_p90": [round(x, 5) for x in r["kernel_ms_p10_p90"]],
                      "algorithmic_bytes_per_launch": r["attn_bytes"]},

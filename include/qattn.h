@@ -188,6 +188,25 @@ qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t*
                                       size_t workspace_bytes, void* out, qa_stream_t stream);
 
 /*
+ * The two phases of qa_paged_attention_decode as separate calls, for callers
+ * that schedule (or time) them apart: _partials launches the split kernel
+ * (with S = 1 it writes `out` directly and _combine does nothing); _combine
+ * merges the split partials of the workspace into `out` ([QK-MMAC] §4:
+ * segment results are merged with their running max and sum). Same
+ * arguments, layouts and errors as qa_paged_attention_decode; _partials then
+ * _combine on one stream gives its result bit for bit. `out` must be valid
+ * in both calls (_partials writes it only when S = 1).
+ */
+qa_status_t qa_paged_attention_decode_partials(const qa_decode_params_t* p, const int8_t* q_i8,
+                                               const float* q_scale, const int8_t* k_cache,
+                                               const float* k_scale, const void* v_cache,
+                                               const float* v_scale, const int32_t* block_tables,
+                                               const int32_t* context_lens, void* workspace,
+                                               size_t workspace_bytes, void* out, qa_stream_t stream);
+qa_status_t qa_paged_attention_decode_combine(const qa_decode_params_t* p, void* workspace,
+                                              size_t workspace_bytes, void* out, qa_stream_t stream);
+
+/*
  * Test hook: runs the decode kernel's own block-table gather and INT8
  * matrix product and stores the raw INT32 accumulators, so they can be
  * compared bit for bit. acc_out [num_seqs, num_q_heads, max_blocks_per_seq *

@@ -71,6 +71,9 @@ _SIGS = {
     "qa_paged_decode_workspace_size": (_size, [_P(DecodeParams)]),
     "qa_paged_attention_decode": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_size, _c_void_p,
                                                                                            _c_void_p]),
+    "qa_paged_attention_decode_partials": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 +
+                                           [_size, _c_void_p, _c_void_p]),
+    "qa_paged_attention_decode_combine": (ctypes.c_int, [_P(DecodeParams), _c_void_p, _size, _c_void_p, _c_void_p]),
     "qa_debug_paged_qk_int32": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 6),
     "qa_chunked_prefill_attention": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 11),
     "qa_dense_sage_quantize_workspace_size": (_size, [_P(DenseParams)]),
@@ -196,10 +199,8 @@ def decode_workspace(p: DecodeParams, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
-def paged_attention_decode(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
-                           num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
-                           workspace=None, out=None):
-    """Decode attention; returns out [num_seqs, Hq, d]."""
+def _decode(entry, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, num_kv_heads,
+            softmax_scale, num_splits, out_dtype, workspace, out):
     _require_cuda(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens)
     S, Hq, d = q_i8.shape
     Hkv = num_kv_heads or k_cache.shape[1]
@@ -209,10 +210,34 @@ def paged_attention_decode(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, bl
         workspace = decode_workspace(p, q_i8.device)
     if out is None:
         out = torch.empty((S, Hq, d), dtype=out_dtype, device=q_i8.device)
-    _check(lib.qa_paged_attention_decode(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
-                                         _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(block_tables),
-                                         _ptr(context_lens), _ptr(workspace), workspace.numel(), _ptr(out),
-                                         _stream()))
+    _check(entry(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                 _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), _ptr(workspace), workspace.numel(),
+                 _ptr(out), _stream()))
+    return out, workspace, p
+
+
+def paged_attention_decode(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
+                           num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
+                           workspace=None, out=None):
+    """Decode attention; returns out [num_seqs, Hq, d]."""
+    return _decode(lib.qa_paged_attention_decode, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables,
+                   context_lens, num_kv_heads, softmax_scale, num_splits, out_dtype, workspace, out)[0]
+
+
+def paged_attention_decode_partials(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
+                                    num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
+                                    workspace=None, out=None):
+    """First phase of decode (the split kernel). Returns (out, workspace,
+    params); pass the last two to paged_attention_decode_combine."""
+    return _decode(lib.qa_paged_attention_decode_partials, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale,
+                   block_tables, context_lens, num_kv_heads, softmax_scale, num_splits, out_dtype, workspace, out)
+
+
+def paged_attention_decode_combine(params, workspace, out):
+    """Second phase of decode: merge the split partials into out."""
+    _require_cuda(workspace, out)
+    _check(lib.qa_paged_attention_decode_combine(ctypes.byref(params), _ptr(workspace), workspace.numel(),
+                                                 _ptr(out), _stream()))
     return out
 
 

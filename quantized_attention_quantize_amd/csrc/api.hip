@@ -232,20 +232,26 @@ size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p) {
   return decode_ws(p, splits_of(p));
 }
 
-qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t* q_i8, const float* q_scale,
-                                      const int8_t* k_cache, const float* k_scale, const void* v_cache,
-                                      const float* v_scale, const int32_t* block_tables,
-                                      const int32_t* context_lens, void* workspace, size_t workspace_bytes,
-                                      void* out, qa_stream_t stream) {
+namespace {
+
+qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const float* q_scale,
+                        const int8_t* k_cache, const float* k_scale, const void* v_cache, const float* v_scale,
+                        const int32_t* block_tables, const int32_t* context_lens, void* workspace,
+                        size_t workspace_bytes, void* out, qa_stream_t stream, qa::DecodePhase phase,
+                        const char* what) {
   qa_status_t st = check_decode(p);
   if (st != QA_OK) return st;
   if (p->num_seqs == 0) return QA_OK;
-  QA_REQUIRE(q_i8 && q_scale && k_cache && k_scale && v_cache && block_tables && context_lens && out,
-             QA_ERR_INVALID_ARG, "null pointer");
-  QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
-  QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&
-                 (v_scale == nullptr || aligned16(v_scale)),
-             QA_ERR_INVALID_ARG, "q_i8, caches and scales must be 16-byte aligned");
+  const bool combine_only = phase == qa::DecodePhase::kCombine;
+  if (!combine_only) {
+    QA_REQUIRE(q_i8 && q_scale && k_cache && k_scale && v_cache && block_tables && context_lens,
+               QA_ERR_INVALID_ARG, "null pointer");
+    QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+    QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&
+                   (v_scale == nullptr || aligned16(v_scale)),
+               QA_ERR_INVALID_ARG, "q_i8, caches and scales must be 16-byte aligned");
+  }
+  QA_REQUIRE(out != nullptr, QA_ERR_INVALID_ARG, "null pointer");
   const int32_t S = splits_of(p);
   const size_t need = decode_ws(p, S);
   QA_REQUIRE(workspace_bytes >= need, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
@@ -262,7 +268,36 @@ qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t*
   a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
   a.num_splits = S; a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
   a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
-  return hip_status(qa::launch_decode(a, (hipStream_t)stream), "qa_paged_attention_decode launch");
+  return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t* q_i8, const float* q_scale,
+                                      const int8_t* k_cache, const float* k_scale, const void* v_cache,
+                                      const float* v_scale, const int32_t* block_tables,
+                                      const int32_t* context_lens, void* workspace, size_t workspace_bytes,
+                                      void* out, qa_stream_t stream) {
+  return decode_call(p, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kBoth, "qa_paged_attention_decode launch");
+}
+
+qa_status_t qa_paged_attention_decode_partials(const qa_decode_params_t* p, const int8_t* q_i8,
+                                               const float* q_scale, const int8_t* k_cache, const float* k_scale,
+                                               const void* v_cache, const float* v_scale,
+                                               const int32_t* block_tables, const int32_t* context_lens,
+                                               void* workspace, size_t workspace_bytes, void* out,
+                                               qa_stream_t stream) {
+  return decode_call(p, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kPartials,
+                     "qa_paged_attention_decode_partials launch");
+}
+
+qa_status_t qa_paged_attention_decode_combine(const qa_decode_params_t* p, void* workspace, size_t workspace_bytes,
+                                              void* out, qa_stream_t stream) {
+  return decode_call(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kCombine,
+                     "qa_paged_attention_decode_combine launch");
 }
 
 qa_status_t qa_debug_paged_qk_int32(const qa_decode_params_t* p, const int8_t* q_i8, const int8_t* k_cache,

@@ -384,7 +384,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
 }
 
 template <int D, bool V_I8, bool EXPORT_QK>
-hipError_t run_decode(const DecodeArgs& a, hipStream_t st) {
+hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
+  if (phase == DecodePhase::kCombine) {
+    if (a.num_splits > 1)
+      k_combine<D><<<dim3(a.Hq, a.num_seqs, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
+                                                                 a.out_bf16, a.out);
+    return hipGetLastError();
+  }
   const dim3 grid(a.num_splits, a.Hkv, a.num_seqs);
   // LDS: per-wave partials [kWaves][G][D] plus (max, sum) pairs.
   const size_t lds = EXPORT_QK ? 0 : (size_t)(kWaves * 32 + kWaves * a.G * D) * sizeof(float);
@@ -394,7 +400,7 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   kern<<<grid, kWaves * 64, lds, st>>>(a);
-  if (!EXPORT_QK && a.num_splits > 1) {
+  if (!EXPORT_QK && a.num_splits > 1 && phase == DecodePhase::kBoth) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_combine<D><<<dim3(a.Hq, a.num_seqs, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
@@ -404,9 +410,10 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <bool EXPORT_QK>
-hipError_t dispatch(const DecodeArgs& a, hipStream_t st) {
-#define QA_DEC(DD)                                                          \
-  return a.v_int8 ? run_decode<DD, true, EXPORT_QK>(a, st) : run_decode<DD, false, EXPORT_QK>(a, st)
+hipError_t dispatch(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
+#define QA_DEC(DD)                                                                     \
+  return a.v_int8 ? run_decode<DD, true, EXPORT_QK>(a, phase, st)                      \
+                  : run_decode<DD, false, EXPORT_QK>(a, phase, st)
   switch (a.D) {
     case 64: QA_DEC(64);
     case 128: QA_DEC(128);
@@ -428,12 +435,14 @@ int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks) 
   return (int32_t)(s < 1 ? 1 : s);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) { return dispatch<false>(a, st); }
+hipError_t launch_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
+  return dispatch<false>(a, phase, st);
+}
 
 hipError_t launch_debug_qk(const DecodeArgs& a, hipStream_t st) {
   DecodeArgs b = a;
   b.num_splits = 1;
-  return dispatch<true>(b, st);
+  return dispatch<true>(b, DecodePhase::kPartials, st);
 }
 
 }  // namespace qa

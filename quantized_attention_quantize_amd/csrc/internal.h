@@ -75,7 +75,10 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e)
   bool v_int8, out_bf16;
 };
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// kPartials: the split kernel only (with one split it writes the output);
+// kCombine: the merge of the split partials only; kBoth: one after the other.
+enum class DecodePhase { kBoth, kPartials, kCombine };
+hipError_t launch_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st);
 hipError_t launch_debug_qk(const DecodeArgs& a, hipStream_t st);
 int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks);
 

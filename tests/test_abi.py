@@ -98,6 +98,22 @@ def test_decode_validation(qa):
     assert L.qa_paged_decode_workspace_size(ctypes.byref(_dp(qa, num_splits=1))) == 0
 
 
+def test_decode_phase_validation(qa):
+    L = qa.lib
+    p = _dp(qa, num_splits=8)
+    need = L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    part = lambda p, ws_bytes, *ptrs: L.qa_paged_attention_decode_partials(
+        ctypes.byref(p), *ptrs, FAKE, ws_bytes, FAKE, None)
+    assert part(p, need - 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert part(p, need, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE) == qa.QA_ERR_INVALID_ARG
+    assert part(_dp(qa, head_dim=96), need, *([FAKE] * 5), None, FAKE, FAKE) == qa.QA_ERR_UNSUPPORTED
+    # combine needs only the workspace and the output
+    assert L.qa_paged_attention_decode_combine(ctypes.byref(p), FAKE, need - 1, FAKE, None) == \
+        qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert L.qa_paged_attention_decode_combine(ctypes.byref(p), None, need, FAKE, None) == qa.QA_ERR_INVALID_ARG
+    assert L.qa_paged_attention_decode_combine(ctypes.byref(p), FAKE, need, None, None) == qa.QA_ERR_INVALID_ARG
+
+
 def test_decode_split_heuristic(qa):
     f = lambda S, Hkv, mb: qa.lib.qa_paged_decode_num_splits(ctypes.byref(qa.decode_params(S, 6 * Hkv, Hkv, 256, mb, 10)))
     assert f(1, 4, 2048) == 64           # one long sequence: one workgroup per CU

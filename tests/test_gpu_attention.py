@@ -125,6 +125,24 @@ def test_decode_deterministic(qa):
     assert torch.equal(a, b)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("v_int8,splits", [(False, 8), (True, 5), (False, 1)])
+def test_decode_phases_match_single_call(qa, v_int8, splits):
+    """_partials then _combine equals the single decode call bit for bit."""
+    spec = PagedSpec("phases", 10, 3, 24, 4, 256, [3000, 17, 1600], [1, 1, 1], k_bias_std=2.0, v_int8=v_int8)
+    say(f"decode phases v_int8={v_int8} splits={splits}")
+    inp = paged_inputs(spec)
+    kc, ks, vc, vs = gpu_cache(qa, inp, v_int8)
+    q8, qs = qa.quantize_q(dev_bits(inp.q, spec.dtype))
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    whole = qa.paged_attention_decode(q8, qs, kc, ks, vc, vs, tables, lens, num_splits=splits)
+    out, ws, p = qa.paged_attention_decode_partials(q8, qs, kc, ks, vc, vs, tables, lens, num_splits=splits)
+    qa.paged_attention_decode_combine(p, ws, out)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, out)
+
+
 # ---------------------------------------------------------------------------
 # chunked prefill
 # ---------------------------------------------------------------------------
