@@ -413,7 +413,7 @@ qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, c
   a.num_seqs = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
   a.D = p->head_dim; a.max_blocks = 0; a.max_seqlen_q = p->seq_q; a.Nq = p->seq_q; a.Nk = p->seq_k;
   a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
-  a.dense = true; a.causal = p->is_causal != 0; a.v_int8 = false; a.v_f16 = p->dtype == QA_DT_F16;
+  a.dense = true; a.causal = p->is_causal != 0; a.v_int8 = false; a.v_f16 = true;  // V blocks are fp16
   a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = p->out_dtype == QA_DT_F16;
   return hip_status(qa::launch_flash(a, (hipStream_t)stream), "dense attention launch");
 }

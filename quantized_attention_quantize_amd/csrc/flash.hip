@@ -3,11 +3,14 @@
 // kernel template.
 //
 // Workgroup = 4 waves x (16*QG) query rows of one query head. 64-token KV
-// tiles are double-buffered in LDS: while the waves compute on one buffer,
-// every thread holds its share of the next tile in registers and writes it
-// to the other buffer afterwards (one barrier per tile). V is stored in LDS
-// as fp16 (bf16 rounded to fp16, INT8 codes exact) in the cache's
-// [block][channel][16 tokens] order.
+// tiles are double-buffered in LDS. Paged tiles are staged through
+// registers: while the waves compute on one buffer, every thread holds its
+// share of the next tile and writes it to the other buffer afterwards,
+// converting V to fp16 (bf16 rounded to fp16, INT8 codes exact). Dense tiles
+// come from this library's own preprocessing, already in the LDS layout with
+// fp16 V, and are copied global -> LDS directly (global_load_lds_dwordx4),
+// which frees the staging registers for a third wave per SIMD. One barrier
+// per tile.
 //
 // Matrix products are computed transposed, as in the decode kernel:
 //   S^T = K Q^T   (v_mfma_i32_16x16x64_i8; A = 16 keys from LDS, B = 16 queries
@@ -53,6 +56,9 @@ enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 #ifndef QA_FLASH_WPE
 #define QA_FLASH_WPE 2
 #endif
+#ifndef QA_FLASH_WPE_DENSE
+#define QA_FLASH_WPE_DENSE 3
+#endif
 #ifndef QA_FLASH_ROWSUM_MFMA
 #define QA_FLASH_ROWSUM_MFMA 1
 #endif
@@ -83,7 +89,8 @@ struct Staged {
 
 template <int D, int QG, int VK, bool DENSE, bool CAUSAL>
 __global__ __launch_bounds__(NT)
-__attribute__((amdgpu_waves_per_eu(D <= 128 ? QA_FLASH_WPE : 1))) void k_flash(FlashArgs a) {
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : 1))) void k_flash(
+    FlashArgs a) {
   using St = Staged<D, VK>;
   constexpr int KS = D / 64;
   constexpr int CG = D / 16;
@@ -259,10 +266,46 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? QA_FLASH_WPE : 1))) void k_flash(F
     }
   };
 
+  // Dense inputs come from this library's own preprocessing, whose K and V
+  // block layouts (V rows already half-swapped) equal the LDS layouts, so
+  // their tiles are copied straight from global memory into LDS by
+  // global_load_lds_dwordx4: each wave moves 1 KB chunks (lane l's 16 bytes
+  // land at chunk base + 16*l), with no staging registers and no LDS writes.
+  // Blocks past the last one are clamped to it, as in fetch().
+  auto dma = [&](int buf, int tile) {
+    constexpr int KC = D / 64;                     // 1 KB chunks per K block (per head)
+    constexpr int VC = D / 32;                     // 1 KB chunks per V block (per head)
+    auto phys = [&](int b) -> int64_t { return blk_base + min(tile * 4 + b, last_blk); };
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = wave_s + 4 * i, b = c / KC, part = c % KC;
+      const int8_t* src = a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)&s_k[buf][b * KBS + part * 1024],
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+      const int c = wave_s + 4 * i, b = c / VC, part = c % VC;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * 2 +
+                           part * 1024 + lane * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(s_v[buf]) +
+                                                                                  b * D * 32 + part * 1024),
+                                       16, 0, 0);
+    }
+  };
+  constexpr bool kDma = DENSE;
+
   if (ntiles > 0) {
-    St st;
-    fetch(st, 0);
-    commit(st, 0, 0);
+    if constexpr (kDma) {
+      dma(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      St st;
+      fetch(st, 0);
+      commit(st, 0, 0);
+    }
   }
   __syncthreads();
 
@@ -273,7 +316,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? QA_FLASH_WPE : 1))) void k_flash(F
     // the next tile (past the last one the clamped blocks are re-read and the
     // spare buffer written but never used)
     St nxt;
-    fetch(nxt, tile + 1);
+    if constexpr (kDma) dma(buf ^ 1, tile + 1);
+    else fetch(nxt, tile + 1);
 
     float tsc = 1.0f;   // dense: key-block scale of this tile
     if constexpr (DENSE) tsc = a.k_scale[((int64_t)z * Hkv + kvh) * nkb + tile];
@@ -396,7 +440,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? QA_FLASH_WPE : 1))) void k_flash(F
         for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
       }
     }
-    commit(nxt, buf ^ 1, tile + 1);
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else commit(nxt, buf ^ 1, tile + 1);
     __syncthreads();
   }
 
@@ -442,10 +487,8 @@ hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
 
 template <int D>
 hipError_t flash_d(const FlashArgs& a, hipStream_t st) {
-  if (a.dense) {
-    if (a.v_f16) return a.causal ? run_flash<D, kVF16, true, true>(a, st) : run_flash<D, kVF16, true, false>(a, st);
-    return a.causal ? run_flash<D, kVBf16, true, true>(a, st) : run_flash<D, kVBf16, true, false>(a, st);
-  }
+  // dense V blocks are always fp16 (the preprocessing converts bf16)
+  if (a.dense) return a.causal ? run_flash<D, kVF16, true, true>(a, st) : run_flash<D, kVF16, true, false>(a, st);
   return a.v_int8 ? run_flash<D, kVI8, false, true>(a, st) : run_flash<D, kVBf16, false, true>(a, st);
 }
 

@@ -278,24 +278,35 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   if (threadIdx.x == 0) scale[((int64_t)b * H + h) * nblk + blk] = s;
 }
 
-// V [B, N, H, D] (16-bit) -> [B*ceil(N/16), H, D, 16]: each channel's 16 tokens of a
-// block contiguous; padding tokens of the last block are zero.
-template <int D>
+// V [B, N, H, D] (bf16 or fp16) -> fp16 [B*ceil(N/16), H, D, 16]: row ch of a block
+// holds its 16 tokens of channel ch, with the two 8-token halves swapped when bit 3
+// of ch is set (the attention kernel's LDS layout, so its tiles are copied
+// unchanged); padding tokens of the last block are zero. bf16 values become the
+// nearest fp16 (exact in the fp16 normal range).
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, int32_t N, int32_t H,
                                                   uint16_t* __restrict__ vb) {
-  __shared__ uint16_t tile[16][D + 2];
+  constexpr int UPR = D / 8;                 // 16-byte units per token row
+  __shared__ __attribute__((aligned(16))) uint16_t tile[16][D + 8];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nb16 = (N + 15) / 16;
-  for (int i = threadIdx.x; i < 16 * D; i += 256) {
-    const int r = i / D, c = i % D;
+  for (int u = threadIdx.x; u < 16 * UPR; u += 256) {
+    const int r = u / UPR, c8 = (u % UPR) * 8;
     const int t = blk * 16 + r;
-    tile[r][c] = t < N ? v[(((int64_t)b * N + t) * H + h) * D + c] : (uint16_t)0;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (t < N) w = *reinterpret_cast<const uint4*>(v + (((int64_t)b * N + t) * H + h) * D + c8);
+    if constexpr (BF16) w = __builtin_bit_cast(uint4, bf16x8_to_f16x8(w));
+    *reinterpret_cast<uint4*>(&tile[r][c8]) = w;
   }
   __syncthreads();
   uint16_t* dst = vb + (((int64_t)b * nb16 + blk) * H + h) * D * 16;
-  for (int i = threadIdx.x; i < 16 * D; i += 256) {
-    const int c = i / 16, r = i % 16;
-    dst[i] = tile[r][c];
+  for (int u = threadIdx.x; u < 2 * D; u += 256) {   // output unit: channel u/2, half u%2
+    const int ch = u >> 1;
+    const int t0 = 8 * ((u & 1) ^ ((ch >> 3) & 1));
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tile[t0 + 2 * i][ch] | ((uint32_t)tile[t0 + 2 * i + 1][ch] << 16);
+    *reinterpret_cast<uint4*>(dst + u * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -347,7 +358,7 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
                                                   a.k_paged, a.k_scale);
     if (a.v_paged != nullptr) {
       dim3 gv((a.Nk + 15) / 16, a.Hkv, a.B);
-      k_v_blocks<D><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, a.Hkv, a.v_paged);
+      k_v_blocks<D, BF16><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, a.Hkv, a.v_paged);
     }
   }
   return hipGetLastError();
