@@ -44,8 +44,6 @@ namespace qa {
 namespace {
 
 constexpr int KT = 64;      // keys per LDS tile
-constexpr int NW = 4;       // waves per workgroup
-constexpr int NT = NW * 64; // threads per workgroup
 constexpr float kRescaleSlack = 8.0f;   // lazy-rescale threshold (base-2 units)
 
 enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
@@ -59,6 +57,7 @@ enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 #ifndef QA_FLASH_WPE_DENSE
 #define QA_FLASH_WPE_DENSE 3
 #endif
+
 #ifndef QA_FLASH_ROWSUM_MFMA
 #define QA_FLASH_ROWSUM_MFMA 1
 #endif
@@ -75,7 +74,7 @@ __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
   return r;
 }
 
-template <int D, int VK>
+template <int D, int VK, int NT>
 struct Staged {
   static constexpr int VB = VK == kVI8 ? 1 : 2;    // bytes per cached V element
   static constexpr int KUB = D;                    // 16-byte K units per block
@@ -87,11 +86,13 @@ struct Staged {
   float ks, vs;
 };
 
-template <int D, int QG, int VK, bool DENSE, bool CAUSAL>
-__global__ __launch_bounds__(NT)
-__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : 1))) void k_flash(
+// NW waves per workgroup, each with QG groups of 16 query rows.
+template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : (NW == 8 ? 2 : 1)))) void k_flash(
     FlashArgs a) {
-  using St = Staged<D, VK>;
+  constexpr int NT = NW * 64;
+  using St = Staged<D, VK, NT>;
   constexpr int KS = D / 64;
   constexpr int CG = D / 16;
   constexpr int QT = NW * 16 * QG;                 // query rows per workgroup
@@ -105,8 +106,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   constexpr bool kRowSumMfma = QA_FLASH_ROWSUM_MFMA && VK != kVI8;         // INT8 V folds sV into P: sum P on the VALU
   __shared__ __attribute__((aligned(16))) int8_t s_k[2][4 * KBS];
   __shared__ __attribute__((aligned(16))) _Float16 s_v[2][KT * D];
-  __shared__ float s_ks[2][KT];
-  __shared__ float s_vs[2][KT];
+  __shared__ float s_ks[DENSE ? 1 : 2][KT];
+  __shared__ float s_vs[DENSE ? 1 : 2][KT];
 
   // ---- work item (XCD-aware order) ----------------------------------------
   const int nqt = ((DENSE ? a.Nq : a.max_seqlen_q) + QT - 1) / QT;
@@ -277,16 +278,18 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     constexpr int VC = D / 32;                     // 1 KB chunks per V block (per head)
     auto phys = [&](int b) -> int64_t { return blk_base + min(tile * 4 + b, last_blk); };
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = wave_s + 4 * i, b = c / KC, part = c % KC;
+    for (int i = 0; i < (4 * KC + NW - 1) / NW; ++i) {
+      const int c = wave_s + NW * i, b = c / KC, part = c % KC;
+      if (4 * KC % NW != 0 && c >= 4 * KC) break;   // wave-uniform
       const int8_t* src = a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)&s_k[buf][b * KBS + part * 1024],
                                        16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < VC; ++i) {
-      const int c = wave_s + 4 * i, b = c / VC, part = c % VC;
+    for (int i = 0; i < (4 * VC + NW - 1) / NW; ++i) {
+      const int c = wave_s + NW * i, b = c / VC, part = c % VC;
+      if (4 * VC % NW != 0 && c >= 4 * VC) break;   // wave-uniform
       const uint8_t* src = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * 2 +
                            part * 1024 + lane * 16;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
@@ -440,7 +443,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
         for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
       }
     }
-    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next tile has landed
     else commit(nxt, buf ^ 1, tile + 1);
     __syncthreads();
   }
@@ -473,15 +476,28 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   }
 }
 
+#ifndef QA_FLASH_NW
+#define QA_FLASH_NW 4
+#endif
+#ifndef QA_FLASH_D256_QG
+#define QA_FLASH_D256_QG 1
+#endif
+#ifndef QA_FLASH_D256_NW
+#define QA_FLASH_D256_NW 8
+#endif
+
 template <int D, int VK, bool DENSE, bool CAUSAL>
 hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
-  constexpr int QG = QA_FLASH_QG;
+  // d = 256: eight waves of 16 rows (a 128-row workgroup) keep two waves per
+  // SIMD within the register file; smaller heads: four waves of 32 rows
+  constexpr int QG = D == 256 ? QA_FLASH_D256_QG : QA_FLASH_QG;
+  constexpr int NW = D == 256 ? QA_FLASH_D256_NW : QA_FLASH_NW;
   constexpr int QT = NW * 16 * QG;
   const int qtiles = ((DENSE ? a.Nq : a.max_seqlen_q) + QT - 1) / QT;
   if (qtiles == 0 || a.num_seqs == 0) return hipSuccess;
   const int64_t total = (int64_t)qtiles * a.Hq * a.num_seqs;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  k_flash<D, QG, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NT, 0, st>>>(a);
+  k_flash<D, QG, NW, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
