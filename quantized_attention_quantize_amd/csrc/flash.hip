@@ -54,6 +54,9 @@ enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 #ifndef QA_FLASH_WPE
 #define QA_FLASH_WPE 2
 #endif
+#ifndef QA_FLASH_SETPRIO
+#define QA_FLASH_SETPRIO 3   // dense kernels: bit 0 raises wave priority over QK, bit 1 over PV
+#endif
 #ifndef QA_FLASH_WPE_DENSE
 #define QA_FLASH_WPE_DENSE 3
 #endif
@@ -299,6 +302,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     }
   };
   constexpr bool kDma = DENSE;
+  // Raised wave priority (s_setprio) while a wave issues its matrix
+  // products: measured faster for the dense kernels, slower for the paged
+  // prefill, so dense only.
+  constexpr int kPrio = DENSE ? QA_FLASH_SETPRIO : 0;
 
   if (ntiles > 0) {
     if constexpr (kDma) {
@@ -328,6 +335,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     // ---- S^T = K Q^T for the 64 keys x (16*QG) queries -------------------------
     // acc[qg][2*half + u][i] holds key 32*half + 8*g + 4*u + i of query n
     v4i acc[QG][4];
+    if constexpr (kPrio & 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int hu = 0; hu < 4; ++hu) {
       const int tau = 32 * (hu >> 1) + 8 * (n >> 2) + 4 * (hu & 1) + (n & 3);
@@ -342,6 +350,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       }
     }
 
+    if constexpr (kPrio & 1) __builtin_amdgcn_s_setprio(0);
     // key of x[j] below: kbase + 32*(j/8) + 8*g + j%8
     const int tl = 8 * g;
     // masks only on tiles that cross the context end or the causal diagonal
@@ -428,6 +437,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     }
 
     // ---- O^T += V^T P^T (and the row sums against an all-ones block) ---------
+    if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
@@ -443,6 +453,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
         for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
       }
     }
+    if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(0);
     if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next tile has landed
     else commit(nxt, buf ^ 1, tile + 1);
     __syncthreads();

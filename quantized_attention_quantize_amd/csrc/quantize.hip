@@ -174,32 +174,57 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, Nk);
   const uint16_t* base = k + ((int64_t)b * Nk) * HD + c8;
-  for (int t = t0; t < t1; ++t) {
-    uint4 w = *reinterpret_cast<const uint4*>(base + (int64_t)t * HD);
+  auto add = [&](uint4 w) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += (double)half_to_f32<BF16>(ws[i] & 0xFFFFu);
       acc[2 * i + 1] += (double)half_to_f32<BF16>(ws[i] >> 16);
     }
+  };
+  int t = t0;
+  // eight independent loads in flight per thread
+  for (; t + 8 <= t1; t += 8) {
+    uint4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(t + j) * HD);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) add(w[j]);
   }
+  for (; t < t1; ++t) add(*reinterpret_cast<const uint4*>(base + (int64_t)t * HD));
   double* dst = partial + ((int64_t)b * chunks + chunk) * HD + c8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dst[i] = acc[i];
 }
 
-// mu[b][c] = fl32(fl64(sum / Nk)); zeros when smoothing is off.
+// mu[b][c] = fl32(fl64(sum / Nk)); zeros when smoothing is off. A workgroup
+// covers 64 columns: four threads per column each add every fourth chunk
+// partial, then the four sums are added through LDS (all sums are exact, so
+// the order does not matter).
 __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, int32_t B,
                                               int32_t Nk, int32_t HD, bool smooth,
                                               float* __restrict__ mean) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)B * HD) return;
-  if (!smooth || Nk == 0) { mean[i] = 0.0f; return; }
-  const int b = (int)(i / HD), c = (int)(i % HD);
-  const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
+  __shared__ double red[4][64];
+  const int col = threadIdx.x & 63, slice = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + col;   // b * HD + c
+  const bool live = i < (int64_t)B * HD;
   double s = 0.0;
-  for (int j = 0; j < chunks; ++j) s += partial[((int64_t)b * chunks + j) * HD + c];
-  mean[i] = (float)(s / (double)Nk);
+  if (live && smooth && Nk > 0) {
+    const int b = (int)(i / HD), c = (int)(i % HD);
+    const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
+    const double* p = partial + (int64_t)b * chunks * HD + c;
+    for (int j = slice; j < chunks; j += 4) s += p[(int64_t)j * HD];
+  }
+  red[slice][col] = s;
+  __syncthreads();
+  if (slice == 0 && live) {
+    if (!smooth || Nk == 0) {
+      mean[i] = 0.0f;
+    } else {
+      const double tot = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+      mean[i] = (float)(tot / (double)Nk);
+    }
+  }
 }
 
 // Per-block quantization of one (b, head, block) of ROWS tokens x D channels:
@@ -345,8 +370,8 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
     dim3 g((HD / 8 + 255) / 256, chunks, a.B);
     k_colsum<BF16><<<g, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, HD, a.partial);
   }
-  k_mean<<<(unsigned)(((int64_t)a.B * HD + 255) / 256), 256, 0, s>>>(a.partial, a.B, a.Nk, HD,
-                                                                        a.smooth_k, a.k_mean);
+  k_mean<<<(unsigned)(((int64_t)a.B * HD + 63) / 64), 256, 0, s>>>(a.partial, a.B, a.Nk, HD, a.smooth_k,
+                                                                      a.k_mean);
   if (a.Nq > 0) {
     dim3 gq((a.Nq + 127) / 128, a.Hq, a.B);
     k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.Nq, a.Hq, nullptr, a.q_i8,

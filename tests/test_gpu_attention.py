@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, tiny_decode, qwen27b_decode,
-                       batched_splitk_decode, chunked_prefill, dense_sage)
+from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs, tiny_decode,
+                       qwen27b_decode, batched_splitk_decode, chunked_prefill, dense_sage)
 from tests.gpu_helpers import say, dev_bits, gpu_cache, oracle_cache, assert_close, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -227,6 +227,20 @@ def test_dense_parity(qa, case):
     quant = oracle.sage_quantize(inp.q, inp.k, dt)
     want = oracle.dense_sage_attention(quant, inp.v, dt, causal=causal)
     assert_close(got, want, "dense")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_zero_scales(qa, causal, dt):
+    """Zero key-block scales (constant keys) and a zero query block: finite
+    output equal to the oracle's (uniform attention for those rows)."""
+    say(f"dense zero scales causal={causal} {dt}")
+    inp = dense_zero_scale_inputs(N=300, d=128, dtype=dt)
+    got = qa.dense_sage_attention(dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt),
+                                  is_causal=causal).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    want = oracle.dense_sage_attention(oracle.sage_quantize(inp.q, inp.k, dt), inp.v, dt, causal=causal)
+    assert_close(got, want, "dense zero scales")
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -11,7 +11,7 @@ from scipy.special import softmax as sp_softmax
 
 import oracle
 from oracle import quant as oq
-from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, to_bf16_bits,
+from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs, to_bf16_bits,
                        to_f16_bits)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -448,6 +448,26 @@ def test_dense_causal_first_row_is_first_value():
     got = oracle.dense_sage_attention(qz, inp.v, "f16", causal=True)
     v = oq.widen(inp.v, "f16").astype(np.float64)
     np.testing.assert_array_equal(got[0, 0], v[0, 0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_zero_scales_give_uniform_attention(causal):
+    # a zero K' block scale or a zero query-block scale makes every score of
+    # that row 0: the output is the plain mean of V over the visible keys
+    inp = dense_zero_scale_inputs()
+    spec = inp.spec
+    qz = oracle.sage_quantize(inp.q, inp.k, "f16")
+    assert np.all(qz["k_scale"][:, 0] == 0) and np.all(qz["k_i8"][:, :, 0] == 0)
+    assert np.all(qz["q_scale"][:, 1, 1] == 0)
+    got = oracle.dense_sage_attention(qz, inp.v, "f16", causal=causal)
+    assert np.all(np.isfinite(got))
+    v = oq.widen(inp.v, "f16").astype(np.float64)[0]
+    N = spec.seq_k
+    cnt = np.arange(1, N + 1)[:, None, None] if causal else N
+    mean = (np.cumsum(v, axis=0) / cnt) if causal else np.broadcast_to(v.mean(axis=0), v.shape)
+    for h in (0, 1):   # query heads of KV head 0
+        np.testing.assert_allclose(got[0, :, h], mean[:, 0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(got[0, 128:256, 1], mean[128:256, 0], rtol=1e-12, atol=1e-13)
 
 
 def test_smoothing_leaves_unquantized_attention_unchanged():

@@ -211,6 +211,18 @@ def dense_inputs(spec: DenseSpec) -> DenseInputs:
     return DenseInputs(spec, q, k, v)
 
 
+def dense_zero_scale_inputs(N: int = 200, d: int = 64, dtype: str = "f16") -> DenseInputs:
+    """Degenerate dense inputs: KV head 0 holds the same key at every position
+    (smoothing then leaves all-zero keys, so every key-block scale is 0) and
+    query head 1 has an all-zero block of query rows 128..255 (query scale 0).
+    B 1, 4 query heads over 2 KV heads."""
+    spec = DenseSpec("dense_zero_scale", 41, 1, 4, 2, N, N, d, k_bias_std=1.0, dtype=dtype)
+    inp = dense_inputs(spec)
+    inp.k[:, :, 0, :] = inp.k[:, :1, 0, :]
+    inp.q[:, 128:256, 1, :] = 0
+    return inp
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------
