@@ -3,18 +3,18 @@
 
 Headline workload: Qwen3.5-27B-shaped decode (24 query heads over 4 KV heads,
 head_dim 256, 32768 cached tokens, INT8 K with per-token scales, bf16 V).
-One step = the fused producer (qa_quantize_q_write_kv: quantize the new
-query token and write its K/V into the paged cache), then paged decode
-attention with split-K and combine (qa_paged_attention_decode). The metric
-is algorithmic KV bytes per second.
+One step = qa_paged_decode_step: quantize the new query token, write the
+new token's K/V into the paged cache and run split-K paged decode attention
+(one kernel), then merge the splits (a second kernel). The metric is
+algorithmic bytes per second.
 
 Steps rotate over several independently allocated KV pools, so together
 they exceed the 256 MB Infinity Cache and each step streams its cache from
 HBM.
 
-Prints one JSON line. Extra keys: the roofline of the decode split kernel
-(HIP events around batches of back-to-back launches of the call's first
-phase, after the timed step loop), the oracle's CPU
+Prints one JSON line. Extra keys: the roofline of the split kernel (HIP
+events around batches of back-to-back launches of the step's first phase,
+after the timed step loop), the oracle's CPU
 throughput on a bounded sample, and throughput of the prefill and dense
 paths on their own workloads.
 """
@@ -38,17 +38,20 @@ FP16_PEAK_TFLOPS = 2516.0
 
 
 def decode_bytes(spec) -> dict:
-    """Algorithmic bytes of one decode call and of one full step."""
+    """Algorithmic bytes of one decode step (one new token per sequence):
+    the cached K codes, K scales and V (and V scales) of every context token,
+    the block table, the bf16 query, the new token's bf16 K/V and its slot,
+    the new token's cache row (written), and the fp32 output."""
     d, Hq, Hkv = spec.head_dim, spec.num_q_heads, spec.num_kv_heads
     tok = sum(spec.context_lens)
     v_elem = 1 if spec.v_int8 else 2
-    attn = (tok * Hkv * (d + 4 + d * v_elem + (4 if spec.v_int8 else 0))      # K, sK, V, sV
-            + spec.num_seqs * spec.max_blocks_per_seq * 4                      # block table
-            + spec.num_seqs * Hq * (d + 4)                                     # q_i8 + q_scale
-            + spec.num_seqs * Hq * d * 4)                                      # fp32 output
-    quant = spec.num_seqs * Hq * (2 * d + d + 4)                               # bf16 in, int8 + scale out
-    write = spec.num_seqs * (Hkv * (2 * d * 2 + d + 4 + d * v_elem + (4 if spec.v_int8 else 0)) + 8)
-    return {"attention": attn, "step": attn + quant + write}
+    row = d + 4 + d * v_elem + (4 if spec.v_int8 else 0)      # one (token, KV head) in the cache
+    hist = (tok * Hkv * row                                     # K, sK, V (, sV)
+            + spec.num_seqs * spec.max_blocks_per_seq * 4       # block table
+            + spec.num_seqs * Hq * d * 4)                       # fp32 output
+    step = (hist + spec.num_seqs * Hq * 2 * d                   # bf16 query
+            + spec.num_seqs * (Hkv * (4 * d + row) + 8))        # new K/V in, its cache row out, slot
+    return {"history": hist, "step": step}
 
 
 def flash_ops(q_lens, ctx_lens, Hq, d, causal=True):
@@ -141,31 +144,23 @@ def run_decode(args, torch, qa, W):
     splits = qa.decode_num_splits(p)
     ws = qa.decode_workspace(p, dev)
     out = torch.empty((spec.num_seqs, Hq, d), dtype=torch.float32, device=dev)
-    q_i8 = torch.empty((spec.num_seqs, Hq, d), dtype=torch.int8, device=dev)
-    q_sc = torch.empty((spec.num_seqs, Hq), dtype=torch.float32, device=dev)
     import ctypes
     L = qa.lib
 
-    def produce(i):
-        kc, ks, vc, vs = pools[i % len(pools)]
-        # fused producer: quantize the query and write the new token's K/V
-        qa._check(L.qa_quantize_q_write_kv(qa._ptr(q), spec.num_seqs, Hq, Hq * d, d, qa._ptr(k_new),
-                                           qa._ptr(v_new), 1, Hkv, Hkv * d, d, qa._ptr(slot_new),
-                                           qa.QA_DT_BF16, d, spec.num_blocks, 16, qa._ptr(q_i8), qa._ptr(q_sc),
-                                           qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), qa.QA_DT_BF16, None, qa._stream()))
-        return kc, ks, vc, vs
-
     def step(i):
-        kc, ks, vc, vs = produce(i)
-        qa._check(L.qa_paged_attention_decode(ctypes.byref(p), qa._ptr(q_i8), qa._ptr(q_sc), qa._ptr(kc),
-                                              qa._ptr(ks), qa._ptr(vc), None, qa._ptr(tables), qa._ptr(lens),
-                                              qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
+        # one call: quantize the query, write the new token's K/V, attend
+        kc, ks, vc, vs = pools[i % len(pools)]
+        qa._check(L.qa_paged_decode_step(
+            ctypes.byref(p), qa._ptr(q), Hq * d, d, qa._ptr(k_new), qa._ptr(v_new), Hkv * d, d, qa.QA_DT_BF16,
+            qa._ptr(slot_new), qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), None, qa._ptr(tables), qa._ptr(lens),
+            qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
 
     def partials(i):
         kc, ks, vc, vs = pools[i % len(pools)]
-        qa._check(L.qa_paged_attention_decode_partials(
-            ctypes.byref(p), qa._ptr(q_i8), qa._ptr(q_sc), qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), None,
-            qa._ptr(tables), qa._ptr(lens), qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
+        qa._check(L.qa_paged_decode_step_partials(
+            ctypes.byref(p), qa._ptr(q), Hq * d, d, qa._ptr(k_new), qa._ptr(v_new), Hkv * d, d, qa.QA_DT_BF16,
+            qa._ptr(slot_new), qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), None, qa._ptr(tables), qa._ptr(lens),
+            qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
 
     for i in range(W):
         step(i)
@@ -182,7 +177,7 @@ def run_decode(args, torch, qa, W):
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / K
 
-    # k_decode alone: batches of back-to-back launches of the call's first
+    # k_decode alone: batches of back-to-back launches of the step's first
     # phase (pools rotated as in the step loop) between two HIP events on
     # torch's current stream, which the library launches on. The host
     # enqueues a launch faster than the kernel runs, so the events see the
@@ -206,7 +201,6 @@ def run_decode(args, torch, qa, W):
         "value": nbytes["step"] / (ms_step * 1e-3) / 1e9,
         "kernel_ms": float(np.mean(kern_ms)),
         "kernel_ms_p10_p90": [float(np.percentile(kern_ms, 10)), float(np.percentile(kern_ms, 90))],
-        "attn_bytes": nbytes["attention"],
         "step_bytes": nbytes["step"],
         "splits": splits,
         "inp": inp,
@@ -322,7 +316,7 @@ def main():
         return
 
     spec, r = run_decode(args, torch, qa, args.warmup)
-    achieved = r["attn_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    achieved = r["step_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
     traffic = decode_traffic()
     res = {
         "metric": "INT8-QK paged attention: decode KV GB/s; prefill/dense INT8 TOPS (% peak)",
@@ -340,14 +334,14 @@ def main():
         "config": {"workload": "qwen27b_decode", "num_seqs": 1, "q_heads": 24, "kv_heads": 4, "head_dim": 256,
                    "context": args.context, "block_size": 16, "k_cache": "int8 + fp32 per-token scale",
                    "v_cache": "bf16", "num_splits": r["splits"], "kv_pools_rotated": args.pools,
-                   "step": "quantize_q_write_kv (fused producer, 1 token) + paged_attention_decode "
-                           "(split kernel, then combine kernel)"},
+                   "step": "paged_decode_step: quantize the query, write the new token, split-K attention "
+                           "(one kernel), then the combine kernel"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_decode (the split kernel of qa_paged_attention_decode)",
+                     "kernel": "k_decode (the split kernel of qa_paged_decode_step, new-token write included)",
                      "kernel_ms": round(r["kernel_ms"], 5),
                      "kernel_ms_p10_p90": [round(x, 5) for x in r["kernel_ms_p10_p90"]],
-                     "algorithmic_bytes_per_launch": r["attn_bytes"]},
+                     "algorithmic_bytes_per_launch": r["step_bytes"]},
     }
     if not args.no_extras:
         res["extra"] = {"chunked_prefill": run_prefill(torch, qa, 20),

@@ -188,6 +188,47 @@ qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t*
                                       size_t workspace_bytes, void* out, qa_stream_t stream);
 
 /*
+ * One decode step in a single call: exactly qa_quantize_q_write_kv for one
+ * new token per sequence followed by qa_paged_attention_decode, with the
+ * same results bit for bit ([QK-MMAC] §4: the query is quantized once per
+ * step and shared by every segment; §1/§3: the new token's K is quantized
+ * per token into the paged layout). The split kernel quantizes the query
+ * rows itself, and the workgroup whose segment holds the new token
+ * quantizes its K (and INT8 V) row, writes it to the cache and uses it
+ * directly, so no separate producer launch is needed. The quantized query
+ * is not stored.
+ *
+ *   q             [num_seqs, num_q_heads, head_dim] bf16/f16, row (s, h) at
+ *                 q + s*q_stride_token + h*q_stride_head (elements)
+ *   k, v          [num_seqs, num_kv_heads, head_dim] the new token's K/V, rows
+ *                 at + s*kv_stride_token + h*kv_stride_head (elements)
+ *   dtype         QA_DT_BF16 or QA_DT_F16 (BF16 when v_cache_dtype is BF16)
+ *   slot_mapping  [num_seqs] int64 cache slot of sequence s's new token; it
+ *                 must be the slot of position context_lens[s] - 1 in
+ *                 block_tables (not checked); < 0: nothing is written
+ *   other arguments as in qa_paged_attention_decode (context_lens include
+ *   the new token); the caches are written, so they are non-const.
+ */
+qa_status_t qa_paged_decode_step(const qa_decode_params_t* p, const void* q, int64_t q_stride_token,
+                                 int64_t q_stride_head, const void* k, const void* v,
+                                 int64_t kv_stride_token, int64_t kv_stride_head, qa_dtype_t dtype,
+                                 const int64_t* slot_mapping, int8_t* k_cache, float* k_scale,
+                                 void* v_cache, float* v_scale, const int32_t* block_tables,
+                                 const int32_t* context_lens, void* workspace,
+                                 size_t workspace_bytes, void* out, qa_stream_t stream);
+/* Its first phase alone (the split kernel, new-token write included); finish
+ * with qa_paged_attention_decode_combine. Same arguments and errors. */
+qa_status_t qa_paged_decode_step_partials(const qa_decode_params_t* p, const void* q,
+                                          int64_t q_stride_token, int64_t q_stride_head,
+                                          const void* k, const void* v, int64_t kv_stride_token,
+                                          int64_t kv_stride_head, qa_dtype_t dtype,
+                                          const int64_t* slot_mapping, int8_t* k_cache,
+                                          float* k_scale, void* v_cache, float* v_scale,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          void* workspace, size_t workspace_bytes, void* out,
+                                          qa_stream_t stream);
+
+/*
  * The two phases of qa_paged_attention_decode as separate calls, for callers
  * that schedule (or time) them apart: _partials launches the split kernel
  * (with S = 1 it writes `out` directly and _combine does nothing); _combine

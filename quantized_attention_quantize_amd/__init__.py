@@ -55,6 +55,9 @@ class DenseParams(ctypes.Structure):
 
 
 _P = ctypes.POINTER
+_STEP_ARGS = ([_P(DecodeParams), _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64, ctypes.c_int]
+              + [_c_void_p] * 8 + [_size, _c_void_p, _c_void_p])
+
 _SIGS = {
     "qa_abi_version": (ctypes.c_int, []),
     "qa_last_error": (ctypes.c_char_p, []),
@@ -68,6 +71,8 @@ _SIGS = {
                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                ctypes.c_int, _c_void_p, _c_void_p]),
     "qa_paged_decode_num_splits": (_i32, [_P(DecodeParams)]),
+    "qa_paged_decode_step": (ctypes.c_int, _STEP_ARGS),
+    "qa_paged_decode_step_partials": (ctypes.c_int, _STEP_ARGS),
     "qa_paged_decode_workspace_size": (_size, [_P(DecodeParams)]),
     "qa_paged_attention_decode": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_size, _c_void_p,
                                                                                            _c_void_p]),
@@ -238,6 +243,30 @@ def paged_attention_decode_combine(params, workspace, out):
     _require_cuda(workspace, out)
     _check(lib.qa_paged_attention_decode_combine(ctypes.byref(params), _ptr(workspace), workspace.numel(),
                                                  _ptr(out), _stream()))
+    return out
+
+
+def paged_decode_step(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
+                      num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
+                      workspace=None, out=None):
+    """One decode step in one call: quantize q [num_seqs, Hq, d], write the new
+    token's k/v [num_seqs, Hkv, d] at slot_mapping, and attend over the cache
+    (context_lens include the new token). Returns out [num_seqs, Hq, d]."""
+    _require_cuda(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens)
+    S, Hq, d = q.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    if k.stride() != v.stride() or k.stride(2) != 1 or q.stride(2) != 1:
+        raise ValueError("k and v must share strides; innermost dims must be contiguous")
+    p = decode_params(S, Hq, Hkv, d, block_tables.shape[1], k_cache.shape[0], v_cache.dtype == torch.int8,
+                      out_dtype, softmax_scale, num_splits)
+    if workspace is None:
+        workspace = decode_workspace(p, q.device)
+    if out is None:
+        out = torch.empty((S, Hq, d), dtype=out_dtype, device=q.device)
+    _check(lib.qa_paged_decode_step(ctypes.byref(p), _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v),
+                                    k.stride(0), k.stride(1), _dt(q.dtype), _ptr(slot_mapping), _ptr(k_cache),
+                                    _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(block_tables),
+                                    _ptr(context_lens), _ptr(workspace), workspace.numel(), _ptr(out), _stream()))
     return out
 
 

@@ -273,6 +273,79 @@ qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const f
 
 }  // namespace
 
+namespace {
+
+qa_status_t decode_step(const qa_decode_params_t* p, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                        const void* k, const void* v, int64_t kv_stride_token, int64_t kv_stride_head,
+                        qa_dtype_t dtype, const int64_t* slot_mapping, int8_t* k_cache, float* k_scale,
+                        void* v_cache, float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                        void* workspace, size_t workspace_bytes, void* out, qa_stream_t stream,
+                        qa::DecodePhase phase, const char* what) {
+  qa_status_t st = check_decode(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0) return QA_OK;
+  QA_REQUIRE(dtype == QA_DT_BF16 || dtype == QA_DT_F16, QA_ERR_UNSUPPORTED, "dtype must be BF16 or F16");
+  QA_REQUIRE(p->v_cache_dtype == QA_DT_I8 || dtype == QA_DT_BF16, QA_ERR_UNSUPPORTED,
+             "a BF16 V cache needs BF16 inputs");
+  QA_REQUIRE(q && k && v && slot_mapping && k_cache && k_scale && v_cache && block_tables && context_lens && out,
+             QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+  QA_REQUIRE(q_stride_token >= 0 && q_stride_head >= 0 && kv_stride_token >= 0 && kv_stride_head >= 0,
+             QA_ERR_INVALID_ARG, "negative stride");
+  QA_REQUIRE(((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) % 2 == 0, QA_ERR_INVALID_ARG,
+             "q, k and v must be 2-byte aligned");
+  QA_REQUIRE(aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&
+                 (v_scale == nullptr || aligned16(v_scale)),
+             QA_ERR_INVALID_ARG, "caches and scales must be 16-byte aligned");
+  const int32_t S = splits_of(p);
+  const size_t need = decode_ws(p, S);
+  QA_REQUIRE(workspace_bytes >= need, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+             workspace_bytes, need);
+  QA_REQUIRE(need == 0 || workspace != nullptr, QA_ERR_INVALID_ARG, "workspace is NULL");
+  QA_REQUIRE(need == 0 || aligned16(workspace), QA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  qa::DecodeArgs a{};
+  a.k_cache = k_cache; a.k_scale = k_scale; a.v_cache = v_cache; a.v_scale = v_scale;
+  a.tables = block_tables; a.ctx_lens = context_lens; a.out = out;
+  const DecodeWs w = decode_layout(p, S);
+  a.ws_o = need ? (float*)((char*)workspace + w.o) : nullptr;
+  a.ws_ml = need ? (float*)((char*)workspace + w.ml) : nullptr;
+  a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
+  a.num_splits = S; a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
+  a.q_in = (const uint16_t*)q; a.k_new = (const uint16_t*)k; a.v_new = (const uint16_t*)v;
+  a.q_st = q_stride_token; a.q_sh = q_stride_head; a.kv_st = kv_stride_token; a.kv_sh = kv_stride_head;
+  a.slots = slot_mapping; a.kc_w = k_cache; a.ks_w = k_scale; a.vc_w = v_cache; a.vs_w = v_scale;
+  a.in_bf16 = dtype == QA_DT_BF16;
+  return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+qa_status_t qa_paged_decode_step(const qa_decode_params_t* p, const void* q, int64_t q_stride_token,
+                                 int64_t q_stride_head, const void* k, const void* v, int64_t kv_stride_token,
+                                 int64_t kv_stride_head, qa_dtype_t dtype, const int64_t* slot_mapping,
+                                 int8_t* k_cache, float* k_scale, void* v_cache, float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens, void* workspace,
+                                 size_t workspace_bytes, void* out, qa_stream_t stream) {
+  return decode_step(p, q, q_stride_token, q_stride_head, k, v, kv_stride_token, kv_stride_head, dtype,
+                     slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kBoth, "qa_paged_decode_step launch");
+}
+
+qa_status_t qa_paged_decode_step_partials(const qa_decode_params_t* p, const void* q, int64_t q_stride_token,
+                                          int64_t q_stride_head, const void* k, const void* v,
+                                          int64_t kv_stride_token, int64_t kv_stride_head, qa_dtype_t dtype,
+                                          const int64_t* slot_mapping, int8_t* k_cache, float* k_scale,
+                                          void* v_cache, float* v_scale, const int32_t* block_tables,
+                                          const int32_t* context_lens, void* workspace, size_t workspace_bytes,
+                                          void* out, qa_stream_t stream) {
+  return decode_step(p, q, q_stride_token, q_stride_head, k, v, kv_stride_token, kv_stride_head, dtype,
+                     slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kPartials,
+                     "qa_paged_decode_step_partials launch");
+}
+
 qa_status_t qa_paged_attention_decode(const qa_decode_params_t* p, const int8_t* q_i8, const float* q_scale,
                                       const int8_t* k_cache, const float* k_scale, const void* v_cache,
                                       const float* v_scale, const int32_t* block_tables,

@@ -20,17 +20,12 @@
 namespace qa {
 namespace {
 
-// Workgroup shape: waves per workgroup and 32-token tiles each wave keeps in
-// flight (loads of the next tile are issued before the current one is
-// consumed). Chosen by measurement on MI355X.
+// Workgroup shape: waves per workgroup, each with one 32-token tile in
+// flight (more waves, or two tiles per wave, measured slower on MI355X).
 #ifndef QA_DECODE_WAVES
 #define QA_DECODE_WAVES 8
 #endif
-#ifndef QA_DECODE_TILES_IN_FLIGHT
-#define QA_DECODE_TILES_IN_FLIGHT 1
-#endif
 constexpr int kWaves = QA_DECODE_WAVES;
-constexpr int kTP = QA_DECODE_TILES_IN_FLIGHT;
 
 // Mask words for 8 values held in 16-bit (bf16) or 8-bit (int8) lanes of
 // 32-bit words: keep the first `nvalid` values, zero the rest. Slots past
@@ -185,7 +180,48 @@ __device__ __forceinline__ void consume_tile(Tile<D, V_I8>& t, Acc<D>& A, const 
   }
 }
 
-template <int D, bool V_I8, bool EXPORT_QK>
+// Fused decode step: the query rows and the new token's K/V row are
+// quantized inside the split kernel ([QK-MMAC] §4: the producer quantizes Q
+// once; here every workgroup re-derives its G rows, which is cheaper than a
+// separate launch). Job j < G of a workgroup quantizes query head kvh*G + j
+// into LDS; in the workgroup whose segment holds the new token (position
+// ctx - 1) job G quantizes its K row and job G + 1 its V row, writes them to
+// the cache slot and keeps them in LDS, and the wave whose tile holds that
+// position substitutes them for what it loaded from the cache. Same
+// arithmetic as the producer kernel, so the results are bit-identical.
+template <int D, bool V_I8>
+struct NewToken {
+  int8_t q[16][D];          // query codes, one row per head of the group
+  float qs[16];             // query scales
+  uint32_t k[D / 4];        // K codes of the new token
+  uint16_t v[D];            // its V: bf16 bits, or INT8 codes (low byte)
+  float ks, vs;             // its K and V scales
+};
+
+// One wave quantizes a row of D 16-bit values, E = D/64 per lane (bits as
+// loaded): returns this lane's E codes packed in bytes and the row scale.
+template <int D>
+__device__ __forceinline__ uint32_t quant_row_wave(const uint16_t (&bits)[D / 64], bool bf16, float& scale) {
+  constexpr int E = D / 64;
+  float x[E];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = bf16 ? bf16_to_f32(bits[e]) : f16_to_f32(bits[e]);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+  amax = wave_max(amax);
+  scale = quant_scale(amax);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = amax > 0.0f ? quant_code(x[e], scale) : 0;
+    packed |= ((uint32_t)c & 0xFFu) << (8 * e);
+  }
+  return packed;
+}
+
+template <int D, bool V_I8, bool EXPORT_QK, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode(DecodeArgs a) {
   constexpr int KS = D / 64;   // INT8 K-steps
   constexpr int CG = D / 16;   // 16-channel groups of the output
@@ -203,21 +239,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   const int per = (a.max_blocks + S - 1) / S;
   const int blk0 = split * per;
   const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
-  // lane j: block (j & 1) of this wave's tile j/2 (first batch of 32 tiles)
+  // lane j: block (j & 1) of this wave's tile j/2 (tiles k .. k+31)
   int tab = trow[min(blk0 + 2 * (wave + kWaves * (lane >> 1)) + (lane & 1), a.max_blocks - 1)];
 
   // Query fragments (B operand): head n of this KV group, channels 64s+16g..+15.
   const int h = kvh * G + n;
   const bool live_col = n < G;
   v4i qf[KS];
+  float qsc = 0.0f;
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (live_col)
-      qf[s] = *reinterpret_cast<const v4i*>(a.q + ((int64_t)seq * Hq + h) * D + 64 * s + 16 * g);
-    else
-      qf[s] = v4i{0, 0, 0, 0};
+    for (int s = 0; s < KS; ++s) {
+      if (live_col)
+        qf[s] = *reinterpret_cast<const v4i*>(a.q + ((int64_t)seq * Hq + h) * D + 64 * s + 16 * g);
+      else
+        qf[s] = v4i{0, 0, 0, 0};
+    }
+    qsc = live_col ? a.q_scale[(int64_t)seq * Hq + h] * a.scale_log2 : 0.0f;
   }
-  const float qsc = live_col ? a.q_scale[(int64_t)seq * Hq + h] * a.scale_log2 : 0.0f;
   const int ctx = a.ctx_lens[seq];
   const int t0 = min(blk0 * 16, ctx);
   const int t1 = min(t0 + per * 16, ctx);
@@ -235,31 +274,169 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   for (int c = 0; c < CG; ++c) A.O[c] = v4f{0.f, 0.f, 0.f, 0.f};
   const DecodeLane L{n, g, kvh, Hkv, 8 * (n >> 2) + (n & 3)};
 
-  for (int kb = 0; kb < ntw; kb += 32) {
-    if (kb > 0)
-      tab = trow[min(blk0 + 2 * (wave + kWaves * (kb + (lane >> 1))) + (lane & 1), a.max_blocks - 1)];
-    const int nk = min(32, ntw - kb);
-    for (int k = 0; k < nk; k += kTP) {
-      Tile<D, V_I8> T[kTP];
+  // Issue every load of this wave's tile k (tiles go round-robin over the
+  // waves); the block-table entries come 32 tiles at a time.
+  auto issue_k = [&](Tile<D, V_I8>& T, int k) {
+    if (k > 0 && (k & 31) == 0)
+      tab = trow[min(blk0 + 2 * (wave + kWaves * (k + (lane >> 1))) + (lane & 1), a.max_blocks - 1)];
+    const int ki = k & 31;
+    const int tb = t0 + 32 * (wave + kWaves * k);
+    const int p0 = __builtin_amdgcn_readlane(tab, 2 * ki);
+    // The second block exists only if the tile has tokens in it; table
+    // entries past the sequence are never used as addresses.
+    const int p1 = tb + 16 < t1 ? __builtin_amdgcn_readlane(tab, 2 * ki + 1) : p0;
+    issue_tile<D, V_I8, EXPORT_QK>(T, a, L, p0, p1);
+  };
+
+  // ---- fused step: which rows this workgroup quantizes --------------------
+  const int pnew = ctx - 1;                                   // position of the new token
+  const bool writer = ctx > 0 ? (pnew >> 4) >= blk0 && (pnew >> 4) < blk0 + per : split == 0;
+  const int jobs = FUSED ? G + (writer ? 2 : 0) : 0;
+  auto job_row = [&](int j) -> const uint16_t* {
+    if (j < G) return a.q_in + seq * a.q_st + (int64_t)(kvh * G + j) * a.q_sh;
+    return (j == G ? a.k_new : a.v_new) + seq * a.kv_st + (int64_t)kvh * a.kv_sh;
+  };
+  // the first job's row is loaded before the first tile, so waiting for it
+  // does not wait for the tile
+  uint16_t pre[KS];
+  if (FUSED && (wave < G || wave < jobs)) {   // (wave < G needs no context length)
+    const uint16_t* row = job_row(wave);
 #pragma unroll
-      for (int i = 0; i < kTP; ++i) {
-        // a tile past the end re-reads the last one (cache hits) and is not consumed
-        const int ki = min(k + i, nk - 1);
-        const int tb = t0 + 32 * (wave + kWaves * (kb + ki));
-        const int p0 = __builtin_amdgcn_readlane(tab, 2 * ki);
-        // The second block exists only if the tile has tokens in it; table
-        // entries past the sequence are never used as addresses.
-        const int p1 = tb + 16 < t1 ? __builtin_amdgcn_readlane(tab, 2 * ki + 1) : p0;
-        issue_tile<D, V_I8, EXPORT_QK>(T[i], a, L, p0, p1);
+    for (int e = 0; e < KS; ++e) pre[e] = row[lane * KS + e];
+  }
+
+  Tile<D, V_I8> T;
+  if (ntw > 0) issue_k(T, 0);
+  // keep the loads of the first tile ahead of the query work below
+  __builtin_amdgcn_sched_barrier(0);
+
+  int64_t slot = -1;
+  if constexpr (FUSED) {
+    __shared__ NewToken<D, V_I8> nt;
+    slot = a.slots[seq];
+    for (int j = wave; j < jobs; j += kWaves) {
+      uint16_t bits[KS];
+      if (j == wave) {
+#pragma unroll
+        for (int e = 0; e < KS; ++e) bits[e] = pre[e];
+      } else {
+        const uint16_t* row = job_row(j);
+#pragma unroll
+        for (int e = 0; e < KS; ++e) bits[e] = row[lane * KS + e];
       }
-      // keep every load of the tile(s) issued before any of them is consumed
-      __builtin_amdgcn_sched_barrier(0);
+      float sc;
+      if (j < G) {
+        const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc);
 #pragma unroll
-      for (int i = 0; i < kTP; ++i) {
-        if (k + i < nk) {
-          const int tb = t0 + 32 * (wave + kWaves * (kb + k + i));
-          consume_tile<D, V_I8, EXPORT_QK>(T[i], A, qf, qsc, tb + 8 * g, t1, qk_dst);
+        for (int e = 0; e < KS; ++e) nt.q[j][lane * KS + e] = (int8_t)(codes >> (8 * e));
+        if (lane == 0) nt.qs[j] = sc;
+      } else if (j == G) {
+        const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc);
+#pragma unroll
+        for (int e = 0; e < KS; ++e) reinterpret_cast<int8_t*>(nt.k)[lane * KS + e] = (int8_t)(codes >> (8 * e));
+        if (lane == 0) nt.ks = sc;
+        if (slot >= 0) {
+          const int64_t bh = (slot >> 4) * Hkv + kvh;
+          const int off = (int)(slot & 15), ch = lane * KS;
+          int8_t* dst = a.kc_w + (bh * (D / 16) + ch / 16) * 256 + off * 16 + (ch % 16);
+          if constexpr (KS == 4) *reinterpret_cast<uint32_t*>(dst) = codes;
+          else if constexpr (KS == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes;
+          else *dst = (int8_t)codes;
+          if (lane == 0) a.ks_w[bh * 16 + off] = sc;
         }
+      } else {
+        const int64_t bh = (slot >> 4) * Hkv + kvh;
+        const int off = (int)(slot & 15);
+        if constexpr (V_I8) {
+          const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc);
+#pragma unroll
+          for (int e = 0; e < KS; ++e) nt.v[lane * KS + e] = (uint16_t)((codes >> (8 * e)) & 0xFFu);
+          if (lane == 0) nt.vs = sc;
+          if (slot >= 0) {
+#pragma unroll
+            for (int e = 0; e < KS; ++e)
+              reinterpret_cast<int8_t*>(a.vc_w)[(bh * D + lane * KS + e) * 16 + off] = (int8_t)(codes >> (8 * e));
+            if (lane == 0) a.vs_w[bh * 16 + off] = sc;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < KS; ++e) {
+            nt.v[lane * KS + e] = bits[e];
+            if (slot >= 0) reinterpret_cast<uint16_t*>(a.vc_w)[(bh * D + lane * KS + e) * 16 + off] = bits[e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = live_col ? *reinterpret_cast<const v4i*>(&nt.q[n][64 * s + 16 * g]) : v4i{0, 0, 0, 0};
+    qsc = live_col ? nt.qs[n] * a.scale_log2 : 0.0f;
+
+    // ---- main loop, with the new token substituted in its tile ----------
+    for (int k = 0; k < ntw; ++k) {
+      const int tb = t0 + 32 * (wave + kWaves * k);
+      if (writer && slot >= 0 && pnew >= tb && pnew < tb + 32) {
+        const int i = pnew - tb;       // the new token's row in this tile
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (L.tau0 + 4 * u == i) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+              T.kr[u][s] = *reinterpret_cast<const v4i*>(reinterpret_cast<const int8_t*>(nt.k) + 64 * s + 16 * g);
+          }
+        const int j = i - 8 * g;       // its slot among this lane's 8 tokens, if any
+        if (j >= 0 && j < 8) {
+          float* ska = reinterpret_cast<float*>(&T.ska);
+          float* skb = reinterpret_cast<float*>(&T.skb);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (j == e) ska[e] = nt.ks;
+            if (j == 4 + e) skb[e] = nt.ks;
+          }
+          if constexpr (V_I8) {
+            float* sva = reinterpret_cast<float*>(&T.sva);
+            float* svb = reinterpret_cast<float*>(&T.svb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (j == e) sva[e] = nt.vs;
+              if (j == 4 + e) svb[e] = nt.vs;
+            }
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              const uint32_t code = nt.v[16 * c + n] & 0xFFu;
+              uint32_t* w = reinterpret_cast<uint32_t*>(&T.v8[c]);
+              const int wi = j >> 2, sh = 8 * (j & 3);
+#pragma unroll
+              for (int q = 0; q < 2; ++q)
+                if (q == wi) w[q] = (w[q] & ~(0xFFu << sh)) | (code << sh);
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              const uint32_t bits = nt.v[16 * c + n];
+              uint32_t* w = reinterpret_cast<uint32_t*>(&T.v16[c]);
+              const int wi = j >> 1, sh = 16 * (j & 1);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (q == wi) w[q] = (w[q] & ~(0xFFFFu << sh)) | (bits << sh);
+            }
+          }
+        }
+      }
+      consume_tile<D, V_I8, EXPORT_QK>(T, A, qf, qsc, tb + 8 * g, t1, qk_dst);
+      if (k + 1 < ntw) {
+        issue_k(T, k + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    for (int k = 0; k < ntw; ++k) {
+      const int tb = t0 + 32 * (wave + kWaves * k);
+      consume_tile<D, V_I8, EXPORT_QK>(T, A, qf, qsc, tb + 8 * g, t1, qk_dst);
+      if (k + 1 < ntw) {
+        issue_k(T, k + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -383,7 +560,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
   }
 }
 
-template <int D, bool V_I8, bool EXPORT_QK>
+template <int D, bool V_I8, bool EXPORT_QK, bool FUSED>
 hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   if (phase == DecodePhase::kCombine) {
     if (a.num_splits > 1)
@@ -394,7 +571,7 @@ hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   const dim3 grid(a.num_splits, a.Hkv, a.num_seqs);
   // LDS: per-wave partials [kWaves][G][D] plus (max, sum) pairs.
   const size_t lds = EXPORT_QK ? 0 : (size_t)(kWaves * 32 + kWaves * a.G * D) * sizeof(float);
-  auto kern = k_decode<D, V_I8, EXPORT_QK>;
+  auto kern = k_decode<D, V_I8, EXPORT_QK, FUSED>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -411,9 +588,12 @@ hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
 
 template <bool EXPORT_QK>
 hipError_t dispatch(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
-#define QA_DEC(DD)                                                                     \
-  return a.v_int8 ? run_decode<DD, true, EXPORT_QK>(a, phase, st)                      \
-                  : run_decode<DD, false, EXPORT_QK>(a, phase, st)
+#define QA_DEC(DD)                                                                                  \
+  if (a.q_in != nullptr)                                                                            \
+    return a.v_int8 ? run_decode<DD, true, false, true>(a, phase, st)                               \
+                    : run_decode<DD, false, false, true>(a, phase, st);                             \
+  return a.v_int8 ? run_decode<DD, true, EXPORT_QK, false>(a, phase, st)                            \
+                  : run_decode<DD, false, EXPORT_QK, false>(a, phase, st)
   switch (a.D) {
     case 64: QA_DEC(64);
     case 128: QA_DEC(128);

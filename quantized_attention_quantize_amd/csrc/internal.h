@@ -74,6 +74,18 @@ struct DecodeArgs {
   int32_t num_seqs, Hq, Hkv, G, D, max_blocks, num_splits;
   float scale_log2;       // softmax_scale * log2(e)
   bool v_int8, out_bf16;
+  // fused step (q_in != nullptr): the split kernel quantizes the query rows
+  // and writes the new token's K/V (position ctx-1 of each sequence) itself
+  const uint16_t* q_in;   // [num_seqs] rows of [Hq, D] at q_in + s*q_st + h*q_sh
+  const uint16_t* k_new;  // [num_seqs] rows of [Hkv, D] at k_new/v_new + s*kv_st + h*kv_sh
+  const uint16_t* v_new;
+  int64_t q_st, q_sh, kv_st, kv_sh;
+  const int64_t* slots;   // cache slot of each sequence's new token (< 0: not written)
+  int8_t* kc_w;           // the caches again, writable
+  float* ks_w;
+  void* vc_w;
+  float* vs_w;
+  bool in_bf16;           // q_in/k_new/v_new are bf16 (else f16)
 };
 // kPartials: the split kernel only (with one split it writes the output);
 // kCombine: the merge of the split partials only; kBoth: one after the other.

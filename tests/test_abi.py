@@ -39,6 +39,22 @@ def test_exports_every_declared_symbol(qa):
     assert set(names) == set(qa.EXPORTED)
 
 
+def _param_counts():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(qa_[a-z0-9_]+)\s*\(([^()]*)\)\s*;", src):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header(qa):
+    counts = _param_counts()
+    assert set(counts) == set(qa.EXPORTED)
+    for name, (_, args) in qa._SIGS.items():
+        assert len(args) == counts[name], f"{name}: binding passes {len(args)} arguments, header declares {counts[name]}"
+
+
 def test_abi_version(qa):
     assert qa.lib.qa_abi_version() == 1
 
@@ -96,6 +112,22 @@ def test_decode_validation(qa):
     assert call(p, need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
     assert b"needed" in L.qa_last_error()
     assert L.qa_paged_decode_workspace_size(ctypes.byref(_dp(qa, num_splits=1))) == 0
+
+
+def test_decode_step_validation(qa):
+    L = qa.lib
+    p = _dp(qa, num_splits=8)
+    need = L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    for fn in (L.qa_paged_decode_step, L.qa_paged_decode_step_partials):
+        call = lambda p, dt=qa.QA_DT_BF16, ws_bytes=need, q=FAKE, vs=None: fn(
+            ctypes.byref(p), q, 6144, 256, FAKE, FAKE, 1024, 256, dt, FAKE, FAKE, FAKE, FAKE, vs, FAKE, FAKE,
+            FAKE, ws_bytes, FAKE, None)
+        assert call(p, dt=qa.QA_DT_F32) == qa.QA_ERR_UNSUPPORTED
+        assert call(p, dt=qa.QA_DT_F16) == qa.QA_ERR_UNSUPPORTED          # bf16 V cache needs bf16 inputs
+        assert call(p, ws_bytes=need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+        assert call(p, q=None) == qa.QA_ERR_INVALID_ARG
+        assert call(_dp(qa, v_cache_dtype=qa.QA_DT_I8), dt=qa.QA_DT_F16) == qa.QA_ERR_INVALID_ARG   # v_scale
+        assert call(_dp(qa, head_dim=96)) == qa.QA_ERR_UNSUPPORTED
 
 
 def test_decode_phase_validation(qa):

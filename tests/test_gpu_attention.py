@@ -143,6 +143,69 @@ def test_decode_phases_match_single_call(qa, v_int8, splits):
     assert torch.equal(whole, out)
 
 
+STEP_CASES = [
+    # (v_int8, splits, context lens, dtype)
+    (False, 8, [3000, 17, 1600], "bf16"),
+    (False, 0, [4096, 32, 1], "bf16"),
+    (False, 1, [700, 33], "bf16"),
+    (True, 5, [3000, 17, 1600], "bf16"),
+    (True, 0, [257, 2048], "f16"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", STEP_CASES)
+def test_decode_step_matches_producer_then_decode(qa, case):
+    """qa_paged_decode_step == qa_quantize_q_write_kv + qa_paged_attention_decode,
+    bit for bit: output and every cache byte."""
+    v_int8, splits, ctx, dt = case
+    spec = PagedSpec("step", 12, len(ctx), 24, 4, 256, ctx, [1] * len(ctx), k_bias_std=2.0, v_int8=v_int8,
+                     dtype=dt)
+    say(f"decode step {case}")
+    inp = paged_inputs(spec)
+    last = inp.cu_seqlens_kv[1:] - 1                      # each sequence's new token
+    hist = inp.slot_mapping.copy()
+    hist[last] = -1
+    kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, 4, 256, torch.int8 if v_int8 else torch.bfloat16)
+    qa.write_kv_cache(dev_bits(inp.k, dt), dev_bits(inp.v, dt), torch.from_numpy(hist).cuda(), kc, ks, vc, vs)
+    q = dev_bits(inp.q, dt)
+    k_new, v_new = dev_bits(inp.k[last], dt), dev_bits(inp.v[last], dt)
+    slots = torch.from_numpy(inp.slot_mapping[last].copy()).cuda()
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    c1 = [t if t is None else t.clone() for t in (kc, ks, vc, vs)]
+    c2 = [t if t is None else t.clone() for t in (kc, ks, vc, vs)]
+    q8, qs = qa.quantize_q_write_kv(q, k_new, v_new, slots, *c1)
+    ref = qa.paged_attention_decode(q8, qs, *c1, tables, lens, num_splits=splits)
+    got = qa.paged_decode_step(q, k_new, v_new, slots, *c2, tables, lens, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    for a, b in zip(c1, c2):
+        assert a is b is None or torch.equal(a, b)
+
+
+@pytest.mark.gpu
+def test_decode_step_unwritten_slot(qa):
+    """A negative slot writes nothing; both paths then read the cached value."""
+    spec = PagedSpec("step_neg", 13, 2, 24, 4, 256, [900, 40], [1, 1], k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    last = inp.cu_seqlens_kv[1:] - 1
+    kc, ks, vc, vs = gpu_cache(qa, inp, False)          # every token, the new ones included
+    q = dev_bits(inp.q)
+    k_new = torch.zeros((2, 4, 256), dtype=torch.bfloat16, device="cuda")   # must not be used
+    slots = torch.full((2,), -1, dtype=torch.int64, device="cuda")
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    before = [t if t is None else t.clone() for t in (kc, ks, vc, vs)]
+    q8, qs = qa.quantize_q(q)
+    ref = qa.paged_attention_decode(q8, qs, kc, ks, vc, vs, tables, lens, num_splits=4)
+    got = qa.paged_decode_step(q, k_new, k_new, slots, kc, ks, vc, vs, tables, lens, num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    for a, b in zip(before, (kc, ks, vc, vs)):
+        assert a is b is None or torch.equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # chunked prefill
 # ---------------------------------------------------------------------------
