@@ -2,7 +2,8 @@
 // SageAttention-style forward ([SAGE-MACA] attention-kernel pipeline), one
 // kernel template.
 //
-// Workgroup = 4 waves x (16*QG) query rows of one query head. 64-token KV
+// Workgroup = NW waves x (16*QG) query rows (dense: of one query head;
+// paged: (token, head) rows of one KV head, see k_flash). 64-token KV
 // tiles are double-buffered in LDS. Paged tiles are staged through
 // registers: while the waves compute on one buffer, every thread holds its
 // share of the next tile and writes it to the other buffer afterwards,
@@ -82,17 +83,22 @@ struct Staged {
   static constexpr int VB = VK == kVI8 ? 1 : 2;    // bytes per cached V element
   static constexpr int KUB = D;                    // 16-byte K units per block
   static constexpr int VUB = D * VB;               // 16-byte V units per block
-  static constexpr int KU = 4 * KUB / NT;          // K units per thread
-  static constexpr int VU = 4 * VUB / NT;          // V units per thread
+  static constexpr int KU = (4 * KUB + NT - 1) / NT;   // K units per thread (the last one
+  static constexpr int VU = (4 * VUB + NT - 1) / NT;   // may cover only some waves)
   uint4 k[KU];
   uint4 v[VU];
   float ks, vs;
 };
 
-// NW waves per workgroup, each with QG groups of 16 query rows.
+// NW waves per workgroup, each with QG groups of 16 query rows. Paged
+// prefill packs the G query heads of one KV head into the rows ([QK-MMAC]
+// §5.2 packs tokens; here tokens and heads): row r of a (sequence, KV head)
+// is query token r / G of query head kvh*G + r % G, so one workgroup's K/V
+// tiles serve all G heads and the row space G*Tq is cut into equal
+// workgroups.
 template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : (NW == 8 ? 2 : 1)))) void k_flash(
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : NW / 4))) void k_flash(
     FlashArgs a) {
   constexpr int NT = NW * 64;
   using St = Staged<D, VK, NT>;
@@ -113,19 +119,22 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   __shared__ float s_vs[DENSE ? 1 : 2][KT];
 
   // ---- work item (XCD-aware order) ----------------------------------------
-  const int nqt = ((DENSE ? a.Nq : a.max_seqlen_q) + QT - 1) / QT;
+  // dense: (query tile, query head, batch); paged: (row tile, KV head, sequence)
+  const int G = DENSE ? 1 : a.G;
+  const int nunits = DENSE ? a.Hq : a.Hkv;
+  const int nqt = ((DENSE ? a.Nq : a.max_seqlen_q) * G + QT - 1) / QT;
   const int total = (int)gridDim.x;
   int wid = blockIdx.x;
   if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int qtile = wid % nqt;
-  const int h = (wid / nqt) % a.Hq;
-  const int z = wid / (nqt * a.Hq);
+  const int hu_ = (wid / nqt) % nunits;
+  const int z = wid / (nqt * nunits);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int Hq = a.Hq, Hkv = a.Hkv;
-  const int kvh = h / a.G;
+  const int kvh = DENSE ? hu_ / a.G : hu_;
 
   int64_t q_row0;
   int Tq, kv_len;
@@ -142,31 +151,33 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     kv_len = a.ctx_lens[z];
     trow = a.tables + (int64_t)z * a.max_blocks;
   }
-  const int q0 = qtile * QT;
-  if (q0 >= Tq) return;
+  const int r0 = qtile * QT;        // first row of the workgroup
+  if (r0 >= Tq * G) return;
   const int offset = kv_len - Tq;   // bottom-right causal alignment
   const int last_blk = (kv_len + 15) / 16 - 1;
 
   // ---- query fragments and scales -------------------------------------------
   v4i qf[QG][KS];
   float qsc[QG];
-  int qi[QG];
+  int qi[QG], qh[QG];               // query token and query head of this lane's row
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
-    qi[qg] = q0 + wave * 16 * QG + 16 * qg + n;
+    const int r = r0 + wave * 16 * QG + 16 * qg + n;
+    qi[qg] = DENSE ? r : r / G;
+    qh[qg] = DENSE ? hu_ : kvh * G + (r - qi[qg] * G);
     const bool ok = qi[qg] < Tq;
-    const int8_t* qp = a.q + ((q_row0 + qi[qg]) * Hq + h) * D + 16 * g;
+    const int8_t* qp = a.q + ((q_row0 + qi[qg]) * Hq + qh[qg]) * D + 16 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qf[qg][s] = ok ? *reinterpret_cast<const v4i*>(qp + 64 * s) : v4i{0, 0, 0, 0};
     if constexpr (DENSE) {
       const int nqb = (a.Nq + 127) / 128;
-      qsc[qg] = a.q_scale[((int64_t)z * Hq + h) * nqb + min(qi[qg] / 128, nqb - 1)] * a.scale_log2;
+      qsc[qg] = a.q_scale[((int64_t)z * Hq + qh[qg]) * nqb + min(qi[qg] / 128, nqb - 1)] * a.scale_log2;
     } else {
-      qsc[qg] = ok ? a.q_scale[(q_row0 + qi[qg]) * Hq + h] * a.scale_log2 : 0.0f;
+      qsc[qg] = ok ? a.q_scale[(q_row0 + qi[qg]) * Hq + qh[qg]] * a.scale_log2 : 0.0f;
     }
   }
-  const int wq_first = q0 + wave * 16 * QG;   // first query row of this wave
+  const int wq_first = (r0 + wave * 16 * QG) / G;   // first query token of this wave
 
   float m_run[QG], l_run[QG];
   v4f O[QG][CG];
@@ -184,7 +195,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.0f;
 
   int kv_end = kv_len;   // keys past kv_end are hidden from every query of the workgroup
-  if constexpr (CAUSAL) kv_end = min(kv_len, min(q0 + QT, Tq) - 1 + offset + 1);
+  if constexpr (CAUSAL) kv_end = min(kv_len, (min(r0 + QT, Tq * G) - 1) / G + offset + 1);
   const int ntiles = kv_end > 0 ? (kv_end + KT - 1) / KT : 0;
 
   // ---- tile staging: global -> registers -> LDS ---------------------------
@@ -200,12 +211,14 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     };
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
+      if ((4 * KUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * KUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / KUB;
       const int8_t* base = a.k_blocks + phys(b) * k_blk + k_head;
       st.k[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)((tid + i * NT) % KUB) * 16u);
     }
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
+      if ((4 * VUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * VUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / VUB;
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * VB;
       st.v[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)((tid + i * NT) % VUB) * 16u);
@@ -224,6 +237,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     const bool tail = kbase + KT > kv_len;       // the tile reaches past the context
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
+      if ((4 * KUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * KUB) break;   // wave-uniform
       const int u = tid + i * NT;
       const int b = (i * NT + 64 * wave_s) / KUB;
       *reinterpret_cast<uint4*>(&s_k[buf][b * KBS + (u % KUB) * 16]) = st.k[i];
@@ -231,6 +245,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     // V rows of keys past the context are cleared (the cache may hold anything there)
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
+      if ((4 * VUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * VUB) break;   // wave-uniform
       const int u = tid + i * NT;
       const int b = (i * NT + 64 * wave_s) / VUB, r = u % VUB;
       const int ch = VB == 2 ? r >> 1 : r;          // channel of this unit
@@ -465,7 +480,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     const float l = kRowSumMfma ? Ls[qg][0] : group4_sum(l_run[qg]);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (qi[qg] >= Tq) continue;
-    const int64_t ob = ((q_row0 + qi[qg]) * Hq + h) * D + 4 * g;
+    const int64_t ob = ((q_row0 + qi[qg]) * Hq + qh[qg]) * D + 4 * g;
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
       const v4f o = O[qg][c] * inv;
@@ -496,17 +511,24 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
 #ifndef QA_FLASH_D256_NW
 #define QA_FLASH_D256_NW 8
 #endif
+#ifndef QA_FLASH_D256_NW_PAGED
+#define QA_FLASH_D256_NW_PAGED 12
+#endif
 
 template <int D, int VK, bool DENSE, bool CAUSAL>
 hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
-  // d = 256: eight waves of 16 rows (a 128-row workgroup) keep two waves per
-  // SIMD within the register file; smaller heads: four waves of 32 rows
+  // d = 256: waves of 16 rows (one workgroup per CU: its double-buffered
+  // tiles take 99 KB of LDS), 8 waves for dense, 12 for the paged prefill,
+  // whose 192-row workgroups (32 tokens x 6 heads for 6:1 GQA) cut 2048
+  // tokens x 24 heads into exactly one round of 256 workgroups; smaller
+  // heads: four waves of 32 rows
   constexpr int QG = D == 256 ? QA_FLASH_D256_QG : QA_FLASH_QG;
-  constexpr int NW = D == 256 ? QA_FLASH_D256_NW : QA_FLASH_NW;
+  constexpr int NW = D == 256 ? (DENSE ? QA_FLASH_D256_NW : QA_FLASH_D256_NW_PAGED) : QA_FLASH_NW;
   constexpr int QT = NW * 16 * QG;
-  const int qtiles = ((DENSE ? a.Nq : a.max_seqlen_q) + QT - 1) / QT;
+  const int G = DENSE ? 1 : a.G;
+  const int qtiles = (int)(((int64_t)(DENSE ? a.Nq : a.max_seqlen_q) * G + QT - 1) / QT);
   if (qtiles == 0 || a.num_seqs == 0) return hipSuccess;
-  const int64_t total = (int64_t)qtiles * a.Hq * a.num_seqs;
+  const int64_t total = (int64_t)qtiles * (DENSE ? a.Hq : a.Hkv) * a.num_seqs;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   k_flash<D, QG, NW, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
   return hipGetLastError();

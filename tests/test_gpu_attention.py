@@ -238,6 +238,9 @@ PREFILL = [
     (256, 6, 4, [600], [260], False),
     (256, 6, 2, [140, 33], [140, 1], True),
     (256, 3, 1, [100], [0], False),
+    # workgroups of packed (token, head) rows that start and end inside a token
+    (256, 5, 1, [300, 90], [250, 7], False),
+    (128, 3, 2, [190, 64], [190, 50], False),
 ]
 
 
