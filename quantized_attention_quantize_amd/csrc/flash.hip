@@ -31,8 +31,8 @@
 // diagonal tiles only; tiles above it are skipped).
 //
 // Tile staging is branch-free: the four physical blocks of a tile are
-// wave-uniform (scalar) loads, with the logical block clamped to the last
-// one of the sequence; keys past the context are masked in the scores and
+// wave-uniform (scalar) loads, issued one tile ahead, with the logical block
+// clamped to the last one of the sequence; keys past the context are masked in the scores and
 // their V rows cleared when the tile is written to LDS.
 //
 // Workgroup order is XCD-aware: the 8 XCDs receive workgroups round-robin,
@@ -62,6 +62,13 @@ enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 #define QA_FLASH_WPE_DENSE 3
 #endif
 
+#ifndef QA_FLASH_Q_LDS
+#define QA_FLASH_Q_LDS 1
+#endif
+#ifndef QA_FLASH_PAGED_KDMA
+#define QA_FLASH_PAGED_KDMA 1
+#endif
+
 #ifndef QA_FLASH_ROWSUM_MFMA
 #define QA_FLASH_ROWSUM_MFMA 1
 #endif
@@ -78,15 +85,26 @@ __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
   return r;
 }
 
-template <int D, int VK, int NT>
+// One lane's 16 bytes global -> LDS (global_load_lds_dwordx4): the wave's
+// 64 lanes fill the 1 KB at the wave-uniform LDS address `lds`. Issued as
+// inline assembly, so the compiler does not treat the LDS destination as
+// aliasing the reads of the other buffer; the caller waits (vmcnt) before
+// the barrier.
+__device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+}
+
+template <int D, int VK, int NT, bool KDMA>
 struct Staged {
   static constexpr int VB = VK == kVI8 ? 1 : 2;    // bytes per cached V element
   static constexpr int KUB = D;                    // 16-byte K units per block
   static constexpr int VUB = D * VB;               // 16-byte V units per block
   static constexpr int KU = (4 * KUB + NT - 1) / NT;   // K units per thread (the last one
   static constexpr int VU = (4 * VUB + NT - 1) / NT;   // may cover only some waves)
-  uint4 k[KU];
-  uint4 v[VU];
+  v4i k[KDMA ? 1 : KU];   // (unused when K goes straight to LDS) plain vector types: a uint4 struct copy under the
+  v4i v[VU];     // partial-round guards left an array in memory
   float ks, vs;
 };
 
@@ -101,7 +119,10 @@ __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : NW / 4))) void k_flash(
     FlashArgs a) {
   constexpr int NT = NW * 64;
-  using St = Staged<D, VK, NT>;
+  // At 12 waves the register file has no room to stage K as well: paged K
+  // tiles (INT8, already in the LDS layout) are copied straight into LDS.
+  constexpr bool KDMA = !DENSE && NW == 12 && QA_FLASH_PAGED_KDMA;
+  using St = Staged<D, VK, NT, KDMA>;
   constexpr int KS = D / 64;
   constexpr int CG = D / 16;
   constexpr int QT = NW * 16 * QG;                 // query rows per workgroup
@@ -117,6 +138,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   __shared__ __attribute__((aligned(16))) _Float16 s_v[2][KT * D];
   __shared__ float s_ks[DENSE ? 1 : 2][KT];
   __shared__ float s_vs[DENSE ? 1 : 2][KT];
+  // With 12 waves the query fragments are parked in LDS (each lane re-reads
+  // its 16 bytes per K step of every tile) to free registers.
+  constexpr bool QLDS = KDMA && QA_FLASH_Q_LDS;
+  __shared__ __attribute__((aligned(16))) v4i s_q[QLDS ? NW * QG * KS : 1][64];
 
   // ---- work item (XCD-aware order) ----------------------------------------
   // dense: (query tile, query head, batch); paged: (row tile, KV head, sequence)
@@ -178,6 +203,12 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     }
   }
   const int wq_first = (r0 + wave * 16 * QG) / G;   // first query token of this wave
+  if constexpr (QLDS) {
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) s_q[(wave * QG + qg) * KS + s][lane] = qf[qg][s];
+  }
 
   float m_run[QG], l_run[QG];
   v4f O[QG][CG];
@@ -202,31 +233,53 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   const int64_t k_head = (int64_t)kvh * D * 16;    // K bytes before this KV head in a block
   const int64_t k_blk = (int64_t)Hkv * D * 16;     // K bytes per physical block
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same value, held in a scalar
-  auto fetch = [&](St& st, int tile) {
+  // Physical blocks of a paged tile: lanes 0..3 read the four block-table
+  // entries with one vector load, issued one tile ahead of the fetch that
+  // uses them (a vector load, so that waiting for LDS reads - lgkmcnt - never
+  // waits for it), and the fetch reads them out with readlane.
+  auto load_blocks = [&](int tile) -> int {
+    if constexpr (DENSE) return 0;
+    else return trow[min(tile * 4 + (lane & 3), last_blk)];
+  };
+  using Blocks = v4i;
+  auto unpack = [](int v) -> Blocks {
+    return Blocks{__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 1),
+                  __builtin_amdgcn_readlane(v, 2), __builtin_amdgcn_readlane(v, 3)};
+  };
+  auto pick = [](Blocks pb, int b) { return (b & 2) ? ((b & 1) ? pb[3] : pb[2]) : ((b & 1) ? pb[1] : pb[0]); };
+  auto fetch = [&](St& st, int tile, Blocks pb, int kbuf) {
     // unit i of this thread lies in block (i*NT + 64*wave) / units-per-block of
     // the tile: wave-uniform, so its physical block is a scalar
     auto phys = [&](int b) -> int64_t {
-      const int lb = min(tile * 4 + b, last_blk);
-      return DENSE ? blk_base + lb : (int64_t)trow[lb];
+      return DENSE ? blk_base + min(tile * 4 + b, last_blk) : (int64_t)pick(pb, b);
     };
+    if constexpr (KDMA) {
+      constexpr int KC = D / 64;                   // 1 KB chunks per K block (per head)
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
+      for (int i = 0; i < (4 * KC + NW - 1) / NW; ++i) {
+        const int c = wave_s + NW * i, b = c / KC, part = c % KC;
+        if (4 * KC % NW != 0 && c >= 4 * KC) break;   // wave-uniform
+        copy16_to_lds(a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16,
+                      &s_k[kbuf][b * KBS + part * 1024]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (KDMA ? 0 : KU); ++i) {
       if ((4 * KUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * KUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / KUB;
       const int8_t* base = a.k_blocks + phys(b) * k_blk + k_head;
-      st.k[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)((tid + i * NT) % KUB) * 16u);
+      st.k[i] = *reinterpret_cast<const v4i*>(base + (uint32_t)((tid + i * NT) % KUB) * 16u);
     }
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
       if ((4 * VUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * VUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / VUB;
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * VB;
-      st.v[i] = *reinterpret_cast<const uint4*>(base + (uint32_t)((tid + i * NT) % VUB) * 16u);
+      st.v[i] = *reinterpret_cast<const v4i*>(base + (uint32_t)((tid + i * NT) % VUB) * 16u);
     }
     if constexpr (!DENSE) {
       if (tid < KT) {
-        const int lb = min(tile * 4 + (tid >> 4), last_blk);
-        const int64_t si = ((int64_t)trow[lb] * Hkv + kvh) * 16 + (tid & 15);
+        const int64_t si = ((int64_t)pick(pb, tid >> 4) * Hkv + kvh) * 16 + (tid & 15);
         st.ks = a.k_scale[si];
         st.vs = VK == kVI8 ? a.v_scale[si] : 0.0f;
       }
@@ -236,11 +289,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     const int kbase = tile * KT;
     const bool tail = kbase + KT > kv_len;       // the tile reaches past the context
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
+    for (int i = 0; i < (KDMA ? 0 : KU); ++i) {
       if ((4 * KUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * KUB) break;   // wave-uniform
       const int u = tid + i * NT;
       const int b = (i * NT + 64 * wave_s) / KUB;
-      *reinterpret_cast<uint4*>(&s_k[buf][b * KBS + (u % KUB) * 16]) = st.k[i];
+      *reinterpret_cast<v4i*>(&s_k[buf][b * KBS + (u % KUB) * 16]) = st.k[i];
     }
     // V rows of keys past the context are cleared (the cache may hold anything there)
 #pragma unroll
@@ -252,7 +305,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       const int row = (b * D + ch) * 16;            // fp16 element index of the channel row
       const int sw = (ch >> 3) & 1;                 // half swap for this channel
       if constexpr (VB == 2) {
-        v8h f = VK == kVF16 ? f16x8_from_u4(st.v[i]) : bf16x8_to_f16x8(st.v[i]);
+        const uint4 w = make_uint4(st.v[i][0], st.v[i][1], st.v[i][2], st.v[i][3]);
+        v8h f = VK == kVF16 ? f16x8_from_u4(w) : bf16x8_to_f16x8(w);
         if (tail) {
           const int t_first = kbase + b * 16 + (r & 1) * 8;
 #pragma unroll
@@ -261,7 +315,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
         }
         *reinterpret_cast<v8h*>(&s_v[buf][row + (((r & 1) ^ sw) << 3)]) = f;
       } else {
-        const uint4 w = st.v[i];
+        const uint4 w = make_uint4(st.v[i][0], st.v[i][1], st.v[i][2], st.v[i][3]);
         v8h f0 = i8x8_to_f16x8(make_uint2(w.x, w.y));
         v8h f1 = i8x8_to_f16x8(make_uint2(w.z, w.w));
         if (tail) {
@@ -328,21 +382,28 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
       St st;
-      fetch(st, 0);
+      fetch(st, 0, unpack(load_blocks(0)), 0);
       commit(st, 0, 0);
+      if constexpr (KDMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   }
   __syncthreads();
 
   const int nkb = DENSE ? (a.Nk + KT - 1) / KT : 1;
+  int pb_next = load_blocks(1);
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     const int kbase = tile * KT;
     // the next tile (past the last one the clamped blocks are re-read and the
     // spare buffer written but never used)
     St nxt;
-    if constexpr (kDma) dma(buf ^ 1, tile + 1);
-    else fetch(nxt, tile + 1);
+    if constexpr (kDma) {
+      dma(buf ^ 1, tile + 1);
+    } else {
+      const Blocks pb = unpack(pb_next);
+      pb_next = load_blocks(tile + 2);
+      fetch(nxt, tile + 1, pb, buf ^ 1);
+    }
 
     float tsc = 1.0f;   // dense: key-block scale of this tile
     if constexpr (DENSE) tsc = a.k_scale[((int64_t)z * Hkv + kvh) * nkb + tile];
@@ -361,7 +422,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       for (int s = 0; s < KS; ++s) {
         const v4i kf = *reinterpret_cast<const v4i*>(kp + s * 1024);
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) acc[qg][hu] = mfma_i8(kf, qf[qg][s], acc[qg][hu]);
+        for (int qg = 0; qg < QG; ++qg)
+          acc[qg][hu] = mfma_i8(kf, QLDS ? s_q[(wave * QG + qg) * KS + s][lane] : qf[qg][s], acc[qg][hu]);
       }
     }
 
@@ -471,6 +533,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(0);
     if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next tile has landed
     else commit(nxt, buf ^ 1, tile + 1);
+    if constexpr (KDMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K of the next tile has landed
     __syncthreads();
   }
 
