@@ -390,6 +390,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   __syncthreads();
 
   const int nkb = DENSE ? (a.Nk + KT - 1) / KT : 1;
+  // dense: key-block scales, read one tile ahead (a load issued and used in
+  // the same tile would expose its latency every tile)
+  const float* ksc = DENSE ? a.k_scale + ((int64_t)z * Hkv + kvh) * nkb : nullptr;
+  float tsc_next = 1.0f;
+  if constexpr (DENSE) tsc_next = ntiles > 0 ? ksc[0] : 1.0f;
   int pb_next = load_blocks(1);
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
@@ -406,7 +411,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     }
 
     float tsc = 1.0f;   // dense: key-block scale of this tile
-    if constexpr (DENSE) tsc = a.k_scale[((int64_t)z * Hkv + kvh) * nkb + tile];
+    if constexpr (DENSE) {
+      tsc = tsc_next;
+      tsc_next = ksc[min(tile + 1, nkb - 1)];
+    }
 
     // ---- S^T = K Q^T for the 64 keys x (16*QG) queries -------------------------
     // acc[qg][2*half + u][i] holds key 32*half + 8*g + 4*u + i of query n
