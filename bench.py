@@ -252,7 +252,8 @@ def run_prefill(torch, qa, reps):
     tops = (qk + pv) / (ms * 1e-3) / 1e12
     mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
     return {"workload": "chunked_prefill 2048 new tokens on 16384 history, 24/4 heads, d256",
-            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed}
+            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
+            "_ops": (qk, pv)}
 
 
 def run_dense(torch, qa, reps, causal):
@@ -277,7 +278,66 @@ def run_dense(torch, qa, reps, causal):
     mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
     return {"workload": f"dense_sage B2 H32 N8192 d128 {'causal' if causal else 'non-causal'} "
                         "(full chain: smooth_k + per-block quantization + attention)",
-            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed}
+            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
+            "_ops": (qk, pv)}
+
+
+def run_practical_peaks(torch, step_bytes: int, pools: int) -> dict:
+    """Practical ceilings measured on this GPU with the probes of qa_probe.h:
+    a plain streaming read (1 GiB, and the decode step's byte count rotated
+    over `pools` buffers as the decode bench does) and matrix-instruction
+    loops of the 32x32 and 16x16 INT8/fp16 forms (best grid, median of the
+    launches)."""
+    from quantized_attention_quantize_amd import probes
+    st = torch.cuda.current_stream()
+    raw = st.cuda_stream
+
+    def timed(fn, reps):
+        fn()
+        evs = _mk_stream_events(torch, reps)
+        for a, b in evs:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    out = {}
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")          # 1 GiB
+    best = 0.0
+    for wgs in (1024, 2048, 4096):
+        ms = timed(lambda: probes.stream_read(big, wgs, sink, raw), 10)
+        best = max(best, big.numel() * 4 / (ms * 1e-3) / 1e9)
+    out["stream_read_1GiB_GBps"] = round(best, 1)
+    del big
+    n = step_bytes // 16 * 16
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(pools)]
+    best = 0.0
+    for wgs in (256, 512, 1024):
+        i = [0]
+
+        def one():
+            probes.stream_read(bufs[i[0] % pools], wgs, sink, raw)
+            i[0] += 1
+        ms = timed(one, 30)
+        best = max(best, n / (ms * 1e-3) / 1e9)
+    out["stream_read_step_bytes_GBps"] = round(best, 1)
+    out["stream_read_step_bytes"] = n
+    del bufs
+    for kind, (name, _) in probes.MFMA_KINDS.items():
+        best = 0.0
+        for wgs in (512, 1024):
+            ops = [0.0]
+
+            def one():
+                ops[0] = probes.mfma(kind, 4000, wgs, sink, raw)
+            ms = timed(one, 5)
+            best = max(best, ops[0] / (ms * 1e-3) / 1e12)
+        out[f"mfma_{name}_T"] = round(best, 1)
+    out["note"] = ("T = TOPS (int8) or TFLOP/s (fp16), include/qa_probe.h; the attention kernels issue the "
+                   "16x16 forms")
+    return out
 
 
 def main():
@@ -344,9 +404,21 @@ def main():
                      "algorithmic_bytes_per_launch": r["step_bytes"]},
     }
     if not args.no_extras:
+        pk = run_practical_peaks(torch, r["step_bytes"], args.pools)
+        res["practical_peak"] = pk
+        res["roofline"]["frac_of_practical_stream"] = round(achieved / pk["stream_read_1GiB_GBps"], 4)
         res["extra"] = {"chunked_prefill": run_prefill(torch, qa, 20),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True)}
+        for e in res["extra"].values():
+            # fraction of the mixed roofline at the measured matrix rates: the
+            # 32x32 forms (the chip's best) and the 16x16 forms the kernels issue
+            qk, pv = e.pop("_ops")
+            t = e["ms"] * 1e-3
+            e["frac_practical_mixed_32x32"] = round((qk / (pk["mfma_i8_32x32x32_T"] * 1e12) +
+                                                     pv / (pk["mfma_f16_32x32x16_T"] * 1e12)) / t, 4)
+            e["frac_practical_mixed_16x16"] = round((qk / (pk["mfma_i8_16x16x64_T"] * 1e12) +
+                                                     pv / (pk["mfma_f16_16x16x32_T"] * 1e12)) / t, 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, r["inp"], args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -1,0 +1,41 @@
+/* Measurement probes for MI355X (gfx950): a plain streaming read and
+ * matrix-instruction throughput loops. They set the practical ceilings that
+ * the attention kernels' throughputs are compared against (HBM bandwidth
+ * for decode, matrix rates for prefill and dense attention); they are not
+ * part of the attention computation.
+ *
+ * Conventions: device pointers owned by the caller; every call is
+ * asynchronous on `stream` (NULL: the default stream); the return value is
+ * 0 on success, 1 for an invalid argument (checked on the host before any
+ * HIP call), 4 for a launch error. */
+#ifndef QA_PROBE_H
+#define QA_PROBE_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` (a multiple of 16) at `src` with 16-byte loads, grid-stride,
+ * in `wgs` workgroups of 256 threads (1 <= wgs <= 65535), and writes one int
+ * per workgroup to `sink[wgs]` so that the reads are not elided. */
+int qa_probe_stream_read(const void* src, size_t bytes, int wgs, int* sink, hipStream_t stream);
+
+/* Matrix-instruction throughput: every wave of `wgs` workgroups (4 waves
+ * each, 1 <= wgs <= 65535) issues `iters` (>= 1) rounds of independent
+ * accumulations with operands held in registers:
+ *   kind 0: 4 x v_mfma_i32_32x32x32_i8   (4 x 65536 ops per round)
+ *   kind 1: 4 x v_mfma_f32_32x32x16_f16  (4 x 32768 flops per round)
+ *   kind 2: 8 x v_mfma_i32_16x16x64_i8   (8 x 32768 ops per round)
+ *   kind 3: 8 x v_mfma_f32_16x16x32_f16  (8 x 16384 flops per round)
+ * Total work = per-round ops x iters x 4 x wgs. One float per thread goes to
+ * `sink[wgs * 256]`. */
+int qa_probe_mfma(int kind, int iters, int wgs, float* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QA_PROBE_H */

@@ -1,4 +1,5 @@
-"""Build libqattn.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build libqattn.so (the HIP kernels and the C ABI) and libqaprobe.so (the
+measurement probes of qa_probe.h) in-tree for gfx950.
 
 Usage: python quantized_attention_quantize_amd/build.py [--verbose]
 (run by path: importing the package needs the library this builds)
@@ -17,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
 SOURCES = ["api.hip", "quantize.hip", "decode.hip", "flash.hip"]
+PROBE_LIB = os.path.join(PKG, "libqaprobe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -45,20 +48,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every kernel source for gfx950 and link libqattn.so (always
-    rebuilds). Returns the library path."""
-    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
-        raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs: list) -> None:
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source for gfx950 and link libqattn.so and
+    libqaprobe.so (always rebuilds). Returns the attention library's path."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link(LIB, [objs[s] for s in SOURCES])
+    _link(PROBE_LIB, [objs[s] for s in PROBE_SOURCES])
     return LIB
 
 

@@ -189,3 +189,24 @@ def test_last_error_is_thread_local(qa):
     t.start(); t.join()
     assert b"null" in seen["msg"]
     assert b"head_dim 96" in L.qa_last_error()
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "qa_probe.h")
+
+
+def test_probe_library_exports_and_rejects():
+    """The measurement probes (qa_probe.h) load, export what the header
+    declares and reject bad arguments on the host."""
+    from quantized_attention_quantize_amd import probes
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(qa_probe_[a-z0-9_]+)\s*\(", src)))
+    assert declared == sorted(probes.EXPORTED)
+    L = probes.lib
+    assert L.qa_probe_stream_read(None, 16, 4, FAKE, None) == 1
+    assert L.qa_probe_stream_read(FAKE, 15, 4, FAKE, None) == 1        # not a multiple of 16
+    assert L.qa_probe_stream_read(FAKE, 16, 0, FAKE, None) == 1
+    assert L.qa_probe_stream_read(FAKE, 16, 70000, FAKE, None) == 1
+    assert L.qa_probe_stream_read(FAKE, 0, 4, FAKE, None) == 0         # nothing to read
+    assert L.qa_probe_mfma(4, 10, 4, FAKE, None) == 1
+    assert L.qa_probe_mfma(0, 0, 4, FAKE, None) == 1
+    assert L.qa_probe_mfma(0, 10, 4, None, None) == 1
