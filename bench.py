@@ -220,7 +220,7 @@ def cpu_baseline(spec, inp, budget_s):
         oracle.paged_decode(q8, qs, caches, inp.block_tables, inp.context_lens, spec.num_kv_heads)
         t_total += time.perf_counter() - t
         n += 1
-        if n >= 50:
+        if n >= 1000:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     by = decode_bytes(spec)["step"]
