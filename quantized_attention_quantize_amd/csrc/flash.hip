@@ -69,6 +69,10 @@ enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 #define QA_FLASH_PAGED_KDMA 1
 #endif
 
+#ifndef QA_FLASH_MAGIC
+#define QA_FLASH_MAGIC 1
+#endif
+
 #ifndef QA_FLASH_ROWSUM_MFMA
 #define QA_FLASH_ROWSUM_MFMA 1
 #endif
@@ -134,6 +138,9 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // cover all banks.
   constexpr int KBS = D * 16 + 64;
   constexpr bool kRowSumMfma = QA_FLASH_ROWSUM_MFMA && VK != kVI8;         // INT8 V folds sV into P: sum P on the VALU
+  constexpr bool kMagic = DENSE && QA_FLASH_MAGIC;                          // dense scores read as floats, see QK
+  constexpr int kAcc0 = kMagic ? 0x4B400000 : 0;                            // bit pattern of 1.5 * 2^23
+  constexpr float kOffset = 12582912.0f;                                     // 1.5 * 2^23
   __shared__ __attribute__((aligned(16))) int8_t s_k[2][4 * KBS];
   __shared__ __attribute__((aligned(16))) _Float16 s_v[2][KT * D];
   __shared__ float s_ks[DENSE ? 1 : 2][KT];
@@ -417,7 +424,12 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     }
 
     // ---- S^T = K Q^T for the 64 keys x (16*QG) queries -------------------------
-    // acc[qg][2*half + u][i] holds key 32*half + 8*g + 4*u + i of query n
+    // acc[qg][2*half + u][i] holds key 32*half + 8*g + 4*u + i of query n.
+    // Dense: the accumulators start at the bit pattern of 1.5 * 2^23, so the
+    // INT32 sum read as a float is 1.5 * 2^23 + dot exactly (the sum stays in
+    // [2^23, 2^24), where floats are the integers, because |dot| <=
+    // 127*127*256 = 4,129,024 < 2^22): no conversion instruction per score;
+    // the offset is folded into the exponent's constant term.
     v4i acc[QG][4];
     if constexpr (kPrio & 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -425,7 +437,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       const int tau = 32 * (hu >> 1) + 8 * (n >> 2) + 4 * (hu & 1) + (n & 3);
       const int8_t* kp = &s_k[buf][(tau >> 4) * KBS + (tau & 15) * 16 + g * 256];
 #pragma unroll
-      for (int qg = 0; qg < QG; ++qg) acc[qg][hu] = v4i{0, 0, 0, 0};
+      for (int qg = 0; qg < QG; ++qg) acc[qg][hu] = v4i{kAcc0, kAcc0, kAcc0, kAcc0};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const v4i kf = *reinterpret_cast<const v4i*>(kp + s * 1024);
@@ -463,8 +475,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
 #pragma unroll
         for (int j = 2; j < 16; j += 2) im = max(im, max(acc[qg][j >> 2][j & 3], acc[qg][j >> 2][(j & 3) + 1]));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = (float)acc[qg][j >> 2][j & 3];
-        mx = (float)im;
+        for (int j = 0; j < 16; ++j) x[j] = kMagic ? __int_as_float(acc[qg][j >> 2][j & 3]) : (float)acc[qg][j >> 2][j & 3];
+        mx = kMagic ? __int_as_float(im) : (float)im;
       } else {
         f = qsc[qg];
 #pragma unroll
@@ -487,7 +499,18 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
           mx = ok ? fmaxf(mx, x[j]) : mx;
         }
       }
-      float mt = mx == kNegInf ? kNegInf : mx * f;
+      // The folded offset costs half an ulp of offset*f in the exponent; when
+      // offset*f > 2^12 (scores of large-magnitude inputs) the offset is
+      // subtracted exactly instead. f is the same for the whole workgroup
+      // (one 128-row query block, one key block), so this branch is uniform.
+      float off = kMagic ? kOffset : 0.0f;
+      if (kMagic && !(kOffset * f <= 4096.0f)) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] -= kOffset;
+        mx -= kOffset;
+        off = 0.0f;
+      }
+      float mt = mx == kNegInf ? kNegInf : (mx - off) * f;
       mt = group4_max(mt);
       // lazy rescale: move the reference only when it is exceeded by > 2^8
       if (__any(mt > m_run[qg] + kRescaleSlack)) {
@@ -500,9 +523,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
         m_run[qg] = m_new;
       }
       const float mref = m_run[qg] == kNegInf ? 0.0f : m_run[qg];
+      const float cterm = -fmaf(off, f, mref);   // x*f + cterm = score - mref
       float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, -mref));
+      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, cterm));
       if (need_mask) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) p[j] = (vis >> j) & 1u ? p[j] : 0.0f;

@@ -309,6 +309,25 @@ def test_dense_zero_scales(qa, causal, dt):
     assert_close(got, want, "dense zero scales")
 
 
+@pytest.mark.parametrize("scale", [1.5, 12.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_large_magnitude(qa, causal, scale):
+    """Q and K scaled up so that the per-tile score factor crosses (1.5) or
+    far exceeds (12) the bound under which the kernel folds its accumulator
+    offset into the exponent's constant; both ways must match the oracle."""
+    say(f"dense large magnitude scale={scale} causal={causal}")
+    spec = DenseSpec("dn_big", 407, 1, 2, 2, 300, 300, 128, k_bias_std=3.0, dtype="f16")
+    inp = dense_inputs(spec)
+
+    def scaled(bits):
+        return (bits.view(np.float16).astype(np.float32) * scale).astype(np.float16).view(np.uint16)
+    q, k = scaled(inp.q), scaled(inp.k)
+    got = qa.dense_sage_attention(dev_bits(q, "f16"), dev_bits(k, "f16"), dev_bits(inp.v, "f16"),
+                                  is_causal=causal).cpu().numpy()
+    want = oracle.dense_sage_attention(oracle.sage_quantize(q, k, "f16"), inp.v, "f16", causal=causal)
+    assert_close(got, want, f"dense x{scale}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_dense_full_size_sampled(qa, causal):
     spec = dense_sage()
