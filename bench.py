@@ -195,6 +195,9 @@ def run_decode(args, torch, qa, W):
 
     per = 10
     kern_ms = batches(partials, max(1, K // per), per)
+    step(0)                            # the output checked against the oracle (cpu_baseline leg)
+    torch.cuda.synchronize()
+    out_host = out.cpu().numpy()
     nbytes = decode_bytes(spec)
     return spec, {
         "ms_per_step": ms_step,
@@ -204,30 +207,78 @@ def run_decode(args, torch, qa, W):
         "step_bytes": nbytes["step"],
         "splits": splits,
         "inp": inp,
+        "out": out_host,
     }
 
 
-def cpu_baseline(spec, inp, budget_s):
+def cpu_baseline(spec, inp, budget_s, gpu_out=None):
     """The oracle, untuned, on the decode workload: quantize the query and
-    run unsplit paged decode over the cache the oracle writes itself."""
+    run unsplit paged decode over the cache the oracle writes itself. Also
+    reports the GPU step's output against the oracle's (same inputs)."""
     import oracle
     from threadpoolctl import threadpool_info
     caches = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks)
     n, t_total = 0, 0.0
+    ref = None
     while t_total < budget_s or n == 0:
         t = time.perf_counter()
         q8, qs = oracle.quantize_q(inp.q)
-        oracle.paged_decode(q8, qs, caches, inp.block_tables, inp.context_lens, spec.num_kv_heads)
+        ref = oracle.paged_decode(q8, qs, caches, inp.block_tables, inp.context_lens, spec.num_kv_heads)
         t_total += time.perf_counter() - t
         n += 1
         if n >= 1000:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     by = decode_bytes(spec)["step"]
-    return {"value": by * n / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full decode steps (quantize_q + unsplit paged decode, fp64) of the "
-                      f"{spec.context_lens[0]}-token workload; {t_total:.1f} s on {os.cpu_count()} host cpus, "
-                      f"BLAS threads {threads}"}
+    res = {"value": by * n / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} full decode steps (quantize_q + unsplit paged decode, fp64) of the "
+                     f"{spec.context_lens[0]}-token workload; {t_total:.1f} s on {os.cpu_count()} host cpus, "
+                     f"BLAS threads {threads}"}
+    if gpu_out is not None:
+        want = np.asarray(ref, np.float64).reshape(gpu_out.shape)
+        got = gpu_out.astype(np.float64)
+        res["gpu_parity"] = {"rel_l2": float(np.linalg.norm(got - want) / np.linalg.norm(want)),
+                             "max_abs": float(np.max(np.abs(got - want))),
+                             "bar": "rel L2 <= 1e-3, max abs <= 2e-3 (fp32 output)"}
+    return res
+
+
+def run_decode_mt(torch, qa, context, T, pools, reps=50):
+    """Multi-token decode on the Qwen3.5-27B shape: T query tokens per step
+    (24 query heads x T in the 16 matrix columns of each KV head), the cache
+    already holding them; pools rotated as in the decode bench. Bytes per
+    call: the cache rows of every context token (as in decode), the block
+    table, the INT8 query codes and scales, and the fp32 output."""
+    from workloads import PagedSpec, paged_inputs
+    spec = PagedSpec("qwen27b_decode_mt", 2, 1, 24, 4, 256, [context], [T], k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    kc, ks, vc, vs = gpu_cache(torch, qa, inp)
+    caches = [(kc, ks, vc, vs)]
+    for _ in range(pools - 1):
+        caches.append((kc.clone(), ks.clone(), vc.clone(), vs))
+    q8, qs = qa.quantize_q(dev_bits(torch, inp.q))
+    S, Hq, d = 1, 24, 256
+    q8, qs = q8.view(S, T, Hq, d), qs.view(S, T, Hq)
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    out = torch.empty((S, T, Hq, d), device="cuda")
+    f = lambda i: qa.paged_attention_decode_mt(q8, qs, *caches[i % pools], tables, lens, out=out)
+    for i in range(10):
+        f(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(reps):
+        f(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    row = d + 4 + 2 * d
+    nbytes = context * 4 * row + spec.max_blocks_per_seq * 4 + T * Hq * (d + 4) + T * Hq * d * 4
+    return {"workload": f"qwen27b decode, {T} query tokens per step, context {context} "
+                        f"(G x T = {6 * T} of 16 matrix columns)",
+            "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes": nbytes, "note": "one call: split kernel + combine (query already quantized)"}
 
 
 def run_prefill(torch, qa, reps):
@@ -407,10 +458,13 @@ def main():
         pk = run_practical_peaks(torch, r["step_bytes"], args.pools)
         res["practical_peak"] = pk
         res["roofline"]["frac_of_practical_stream"] = round(achieved / pk["stream_read_1GiB_GBps"], 4)
-        res["extra"] = {"chunked_prefill": run_prefill(torch, qa, 20),
+        res["extra"] = {"decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
+                        "chunked_prefill": run_prefill(torch, qa, 20),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True)}
         for e in res["extra"].values():
+            if "_ops" not in e:
+                continue
             # fraction of the mixed roofline at the measured matrix rates: the
             # 32x32 forms (the chip's best) and the 16x16 forms the kernels issue
             qk, pv = e.pop("_ops")
@@ -420,7 +474,9 @@ def main():
             e["frac_practical_mixed_16x16"] = round((qk / (pk["mfma_i8_16x16x64_T"] * 1e12) +
                                                      pv / (pk["mfma_f16_16x16x32_T"] * 1e12)) / t, 4)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(spec, r["inp"], args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(spec, r["inp"], args.cpu_budget, r["out"])
+    pr = torch.cuda.get_device_properties(0)
+    res["device"] = {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count}
     print(json.dumps(res), flush=True)
 
 

@@ -248,6 +248,37 @@ qa_status_t qa_paged_attention_decode_combine(const qa_decode_params_t* p, void*
                                               size_t workspace_bytes, void* out, qa_stream_t stream);
 
 /*
+ * Multi-token decode (speculative or multi-token prediction steps): T new
+ * query tokens per sequence attend to the paged cache, which already holds
+ * them; token j of sequence s sits at position context_lens[s] - T + j and
+ * sees the keys up to that position (causal among the new tokens, as in a
+ * chunk of qa_chunked_prefill_attention). [QK-MMAC] §5.1 counts 6 distinct
+ * query rows of 16 for one-token decode with 6:1 GQA; §7 asks that the rows
+ * be filled by tokens or by several GQA groups: here the G heads of a KV
+ * head times the T tokens share the 16 columns of the matrix instruction
+ * (G*T <= 16, e.g. 12 of 16 for G = 6, T = 2), so the K/V bytes of a step
+ * are read once for all T tokens. T = 1 is qa_paged_attention_decode, bit
+ * for bit.
+ *
+ *   tokens_per_seq  T >= 1 with G*T <= 16 (else QA_ERR_UNSUPPORTED) and
+ *                   num_seqs*T <= 65535
+ *   q_i8            [num_seqs, T, num_q_heads, head_dim] int8
+ *   q_scale         [num_seqs, T, num_q_heads] fp32
+ *   out             [num_seqs, T, num_q_heads, head_dim] fp32 or bf16
+ *   workspace       >= qa_paged_decode_mt_workspace_size bytes
+ *   other arguments and the split-K segments as in qa_paged_attention_decode.
+ * A token with no visible key (context_lens[s] - T + j < 0) gives zeros.
+ */
+size_t qa_paged_decode_mt_workspace_size(const qa_decode_params_t* p, int32_t tokens_per_seq);
+qa_status_t qa_paged_attention_decode_mt(const qa_decode_params_t* p, int32_t tokens_per_seq,
+                                         const int8_t* q_i8, const float* q_scale,
+                                         const int8_t* k_cache, const float* k_scale,
+                                         const void* v_cache, const float* v_scale,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         void* workspace, size_t workspace_bytes, void* out,
+                                         qa_stream_t stream);
+
+/*
  * Test hook: runs the decode kernel's own block-table gather and INT8
  * matrix product and stores the raw INT32 accumulators, so they can be
  * compared bit for bit. acc_out [num_seqs, num_q_heads, max_blocks_per_seq *

@@ -79,6 +79,9 @@ _SIGS = {
     "qa_paged_attention_decode_partials": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 +
                                            [_size, _c_void_p, _c_void_p]),
     "qa_paged_attention_decode_combine": (ctypes.c_int, [_P(DecodeParams), _c_void_p, _size, _c_void_p, _c_void_p]),
+    "qa_paged_decode_mt_workspace_size": (_size, [_P(DecodeParams), _i32]),
+    "qa_paged_attention_decode_mt": (ctypes.c_int, [_P(DecodeParams), _i32] + [_c_void_p] * 9 +
+                                     [_size, _c_void_p, _c_void_p]),
     "qa_debug_paged_qk_int32": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 6),
     "qa_chunked_prefill_attention": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 11),
     "qa_dense_sage_quantize_workspace_size": (_size, [_P(DenseParams)]),
@@ -243,6 +246,29 @@ def paged_attention_decode_combine(params, workspace, out):
     _require_cuda(workspace, out)
     _check(lib.qa_paged_attention_decode_combine(ctypes.byref(params), _ptr(workspace), workspace.numel(),
                                                  _ptr(out), _stream()))
+    return out
+
+
+def paged_attention_decode_mt(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
+                              num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
+                              workspace=None, out=None):
+    """Multi-token decode: q_i8 [num_seqs, T, Hq, d], q_scale [num_seqs, T, Hq];
+    token j of sequence s sits at position context_lens[s] - T + j. Returns
+    out [num_seqs, T, Hq, d]."""
+    _require_cuda(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens)
+    S, T, Hq, d = q_i8.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    p = decode_params(S, Hq, Hkv, d, block_tables.shape[1], k_cache.shape[0], v_cache.dtype == torch.int8,
+                      out_dtype, softmax_scale, num_splits)
+    if workspace is None:
+        n = lib.qa_paged_decode_mt_workspace_size(ctypes.byref(p), T)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q_i8.device)
+    if out is None:
+        out = torch.empty((S, T, Hq, d), dtype=out_dtype, device=q_i8.device)
+    _check(lib.qa_paged_attention_decode_mt(ctypes.byref(p), T, _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
+                                            _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(block_tables),
+                                            _ptr(context_lens), _ptr(workspace), workspace.numel(), _ptr(out),
+                                            _stream()))
     return out
 
 

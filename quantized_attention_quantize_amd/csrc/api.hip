@@ -73,10 +73,10 @@ struct DecodeWs {
   size_t o, ml, total;
 };
 
-DecodeWs decode_layout(const qa_decode_params_t* p, int32_t S) {
+DecodeWs decode_layout(const qa_decode_params_t* p, int32_t S, int32_t T = 1) {
   DecodeWs w{};
   if (S <= 1) return w;
-  const size_t units = (size_t)p->num_seqs * p->num_q_heads * S;
+  const size_t units = (size_t)p->num_seqs * T * p->num_q_heads * S;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.o = 0;
   w.ml = al(units * p->head_dim * sizeof(float));
@@ -84,7 +84,17 @@ DecodeWs decode_layout(const qa_decode_params_t* p, int32_t S) {
   return w;
 }
 
-size_t decode_ws(const qa_decode_params_t* p, int32_t S) { return decode_layout(p, S).total; }
+size_t decode_ws(const qa_decode_params_t* p, int32_t S, int32_t T = 1) { return decode_layout(p, S, T).total; }
+
+// query tokens per sequence of a multi-token decode: G*T columns must fit
+// the 16 columns of the matrix instruction
+qa_status_t check_tokens(const qa_decode_params_t* p, int32_t T) {
+  QA_REQUIRE(T >= 1, QA_ERR_INVALID_ARG, "tokens_per_seq %d < 1", T);
+  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  QA_REQUIRE((int64_t)G * T <= 16, QA_ERR_UNSUPPORTED, "group %d x %d tokens > 16 query columns", G, T);
+  QA_REQUIRE((int64_t)p->num_seqs * T <= 65535, QA_ERR_UNSUPPORTED, "num_seqs x tokens > 65535");
+  return QA_OK;
+}
 
 qa_status_t check_dense(const qa_dense_params_t* p) {
   QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
@@ -238,8 +248,10 @@ qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const f
                         const int8_t* k_cache, const float* k_scale, const void* v_cache, const float* v_scale,
                         const int32_t* block_tables, const int32_t* context_lens, void* workspace,
                         size_t workspace_bytes, void* out, qa_stream_t stream, qa::DecodePhase phase,
-                        const char* what) {
+                        const char* what, int32_t T = 1) {
   qa_status_t st = check_decode(p);
+  if (st != QA_OK) return st;
+  st = check_tokens(p, T);
   if (st != QA_OK) return st;
   if (p->num_seqs == 0) return QA_OK;
   const bool combine_only = phase == qa::DecodePhase::kCombine;
@@ -253,7 +265,7 @@ qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const f
   }
   QA_REQUIRE(out != nullptr, QA_ERR_INVALID_ARG, "null pointer");
   const int32_t S = splits_of(p);
-  const size_t need = decode_ws(p, S);
+  const size_t need = decode_ws(p, S, T);
   QA_REQUIRE(workspace_bytes >= need, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
              workspace_bytes, need);
   QA_REQUIRE(need == 0 || workspace != nullptr, QA_ERR_INVALID_ARG, "workspace is NULL");
@@ -261,13 +273,14 @@ qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const f
   qa::DecodeArgs a{};
   a.q = q_i8; a.q_scale = q_scale; a.k_cache = k_cache; a.k_scale = k_scale; a.v_cache = v_cache;
   a.v_scale = v_scale; a.tables = block_tables; a.ctx_lens = context_lens; a.out = out;
-  const DecodeWs w = decode_layout(p, S);
+  const DecodeWs w = decode_layout(p, S, T);
   a.ws_o = need ? (float*)((char*)workspace + w.o) : nullptr;
   a.ws_ml = need ? (float*)((char*)workspace + w.ml) : nullptr;
   a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
   a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
   a.num_splits = S; a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
   a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
+  a.tq = T;
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }
 
@@ -317,6 +330,7 @@ qa_status_t decode_step(const qa_decode_params_t* p, const void* q, int64_t q_st
   a.q_st = q_stride_token; a.q_sh = q_stride_head; a.kv_st = kv_stride_token; a.kv_sh = kv_stride_head;
   a.slots = slot_mapping; a.kc_w = k_cache; a.ks_w = k_scale; a.vc_w = v_cache; a.vs_w = v_scale;
   a.in_bf16 = dtype == QA_DT_BF16;
+  a.tq = 1;
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }
 
@@ -366,6 +380,21 @@ qa_status_t qa_paged_attention_decode_partials(const qa_decode_params_t* p, cons
                      "qa_paged_attention_decode_partials launch");
 }
 
+size_t qa_paged_decode_mt_workspace_size(const qa_decode_params_t* p, int32_t tokens_per_seq) {
+  if (check_decode(p) != QA_OK || check_tokens(p, tokens_per_seq) != QA_OK) return 0;
+  return decode_ws(p, splits_of(p), tokens_per_seq);
+}
+
+qa_status_t qa_paged_attention_decode_mt(const qa_decode_params_t* p, int32_t tokens_per_seq, const int8_t* q_i8,
+                                         const float* q_scale, const int8_t* k_cache, const float* k_scale,
+                                         const void* v_cache, const float* v_scale, const int32_t* block_tables,
+                                         const int32_t* context_lens, void* workspace, size_t workspace_bytes,
+                                         void* out, qa_stream_t stream) {
+  return decode_call(p, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kBoth, "qa_paged_attention_decode_mt launch",
+                     tokens_per_seq);
+}
+
 qa_status_t qa_paged_attention_decode_combine(const qa_decode_params_t* p, void* workspace, size_t workspace_bytes,
                                               void* out, qa_stream_t stream) {
   return decode_call(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, workspace,
@@ -385,7 +414,7 @@ qa_status_t qa_debug_paged_qk_int32(const qa_decode_params_t* p, const int8_t* q
   a.q = q_i8; a.k_cache = k_cache; a.tables = block_tables; a.ctx_lens = context_lens; a.acc_out = acc_out;
   a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
   a.G = p->num_q_heads / p->num_kv_heads; a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq;
-  a.num_splits = 1; a.scale_log2 = 1.0f; a.v_int8 = false;
+  a.num_splits = 1; a.scale_log2 = 1.0f; a.v_int8 = false; a.tq = 1;
   return hip_status(qa::launch_debug_qk(a, (hipStream_t)stream), "qa_debug_paged_qk_int32 launch");
 }
 

@@ -5,8 +5,10 @@
 // Mapping onto v_mfma_i32_16x16x64_i8 (see common.h for the lane layout).
 // The kernel computes S^T = K Q^T per 32-token tile:
 //   A operand = 16 key tokens x 64 channels (INT8, straight from the cache)
-//   B operand = 64 channels x 16 query heads (the G heads of one KV head,
-//               [QK-MMAC] §5.1; columns >= G are zero)
+//   B operand = 64 channels x 16 query columns: the G heads of one KV head
+//               ([QK-MMAC] §5.1), times the tq query tokens of a multi-token
+//               step (column n = token n / G, head n % G); columns >= G*tq
+//               are zero
 // A tile covers 32 tokens with two instructions u = 0, 1; matrix row r of
 // instruction u holds token 8*(r/4) + 4u + (r%4). With that permutation the
 // result lane l (column = head l%16, group g = l/16) owns tokens
@@ -98,10 +100,12 @@ struct Acc {
 };
 
 // Consume one tile: INT8 QK, score recovery, online softmax, P.V.
-// tl = first token of this lane's 8-token slice, t1 = end of the segment.
+// tl = first token of this lane's 8-token slice, t1 = end of the segment,
+// t1c = end of the keys this lane's query column sees (<= t1; less for the
+// earlier tokens of a multi-token step).
 template <int D, bool V_I8, bool EXPORT_QK>
 __device__ __forceinline__ void consume_tile(Tile<D, V_I8>& t, Acc<D>& A, const v4i (&qf)[D / 64], float qsc,
-                                             int tl, int t1, int32_t* qk_dst) {
+                                             int tl, int t1, int t1c, int32_t* qk_dst) {
   constexpr int KS = D / 64, CG = D / 16;
   // ---- S^T = K Q^T ----------------------------------------------------------
   v4i acc[2];
@@ -119,7 +123,8 @@ __device__ __forceinline__ void consume_tile(Tile<D, V_I8>& t, Acc<D>& A, const 
     }
     return;
   }
-  const int nvalid = min(max(t1 - tl, 0), 8);
+  const int nvalid = min(max(t1 - tl, 0), 8);     // slots holding keys of the context (V kept)
+  const int nvis = min(max(t1c - tl, 0), 8);       // keys this query column sees
 
   // ---- [QK-MMAC] §1: recover each score before the softmax (base 2) -------
   const float sk[8] = {t.ska.x, t.ska.y, t.ska.z, t.ska.w, t.skb.x, t.skb.y, t.skb.z, t.skb.w};
@@ -128,7 +133,7 @@ __device__ __forceinline__ void consume_tile(Tile<D, V_I8>& t, Acc<D>& A, const 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float v = (float)acc[j >> 2][j & 3] * qsc * sk[j];
-    sc[j] = j < nvalid ? v : kNegInf;
+    sc[j] = j < nvis ? v : kNegInf;
     mt = fmaxf(mt, sc[j]);
   }
   mt = group4_max(mt);
@@ -221,7 +226,9 @@ __device__ __forceinline__ uint32_t quant_row_wave(const uint16_t (&bits)[D / 64
   return packed;
 }
 
-template <int D, bool V_I8, bool EXPORT_QK, bool FUSED>
+// MT: several query tokens per sequence (a.tq > 1); the one-token kernels
+// are compiled without the per-column bookkeeping.
+template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode(DecodeArgs a) {
   constexpr int KS = D / 64;   // INT8 K-steps
   constexpr int CG = D / 16;   // 16-channel groups of the output
@@ -242,25 +249,32 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   // lane j: block (j & 1) of this wave's tile j/2 (tiles k .. k+31)
   int tab = trow[min(blk0 + 2 * (wave + kWaves * (lane >> 1)) + (lane & 1), a.max_blocks - 1)];
 
-  // Query fragments (B operand): head n of this KV group, channels 64s+16g..+15.
-  const int h = kvh * G + n;
-  const bool live_col = n < G;
+  // Query fragments (B operand): column n = token jt, head kvh*G + hn of this
+  // KV group, channels 64s+16g..+15.
+  const int Tq = MT ? a.tq : 1, ncol = G * Tq;
+  const int jt = MT ? n / G : 0, hn = n - jt * G;
+  const int h = kvh * G + hn;
+  const int qrow = seq * Tq + jt;                  // query row (sequence, token)
+  const bool live_col = n < ncol;
   v4i qf[KS];
   float qsc = 0.0f;
   if constexpr (!FUSED) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (live_col)
-        qf[s] = *reinterpret_cast<const v4i*>(a.q + ((int64_t)seq * Hq + h) * D + 64 * s + 16 * g);
+        qf[s] = *reinterpret_cast<const v4i*>(a.q + ((int64_t)qrow * Hq + h) * D + 64 * s + 16 * g);
       else
         qf[s] = v4i{0, 0, 0, 0};
     }
-    qsc = live_col ? a.q_scale[(int64_t)seq * Hq + h] * a.scale_log2 : 0.0f;
+    qsc = live_col ? a.q_scale[(int64_t)qrow * Hq + h] * a.scale_log2 : 0.0f;
   }
   const int ctx = a.ctx_lens[seq];
   const int t0 = min(blk0 * 16, ctx);
   const int t1 = min(t0 + per * 16, ctx);
   const int ntiles = (t1 - t0 + 31) >> 5;
+  // token jt of a tq-token step sits at position ctx - tq + jt and sees the
+  // keys up to it
+  const int t1c = MT ? min(t1, ctx - Tq + jt + 1) : t1;
   const int ntw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;   // this wave's tiles
 
   int32_t* qk_dst = nullptr;
@@ -424,7 +438,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
           }
         }
       }
-      consume_tile<D, V_I8, EXPORT_QK>(T, A, qf, qsc, tb + 8 * g, t1, qk_dst);
+      consume_tile<D, V_I8, EXPORT_QK>(T, A, qf, qsc, tb + 8 * g, t1, t1c, qk_dst);
       if (k + 1 < ntw) {
         issue_k(T, k + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -433,7 +447,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   } else {
     for (int k = 0; k < ntw; ++k) {
       const int tb = t0 + 32 * (wave + kWaves * k);
-      consume_tile<D, V_I8, EXPORT_QK>(T, A, qf, qsc, tb + 8 * g, t1, qk_dst);
+      consume_tile<D, V_I8, EXPORT_QK>(T, A, qf, qsc, tb + 8 * g, t1, t1c, qk_dst);
       if (k + 1 < ntw) {
         issue_k(T, k + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   // ---- merge the waves of this workgroup ----------------------------------
   const float l_run = group4_sum(A.l);
   float* sm_ml = smem;                       // [kWaves][16][2]
-  float* sm_o = smem + kWaves * 32;          // [kWaves][G][D]
+  float* sm_o = smem + kWaves * 32;          // [kWaves][G*tq][D]
   if (g == 0) {
     sm_ml[(wave * 16 + n) * 2] = A.m;
     sm_ml[(wave * 16 + n) * 2 + 1] = l_run;
@@ -453,33 +467,35 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   if (live_col) {
 #pragma unroll
     for (int c = 0; c < CG; ++c)
-      *reinterpret_cast<float4*>(sm_o + ((int64_t)wave * G + n) * D + 16 * c + 4 * g) =
+      *reinterpret_cast<float4*>(sm_o + ((int64_t)wave * ncol + n) * D + 16 * c + 4 * g) =
           make_float4(A.O[c][0], A.O[c][1], A.O[c][2], A.O[c][3]);
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
-    const int hn = idx / D, ch = idx - hn * D;
+  for (int idx = threadIdx.x; idx < ncol * D; idx += kWaves * 64) {
+    const int cn = idx / D, ch = idx - cn * D;     // column cn = token cn / G, head cn % G
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[(w * 16 + hn) * 2]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[(w * 16 + cn) * 2]);
     float lsum = 0.0f, o = 0.0f;
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float wt = fast_exp2(sm_ml[(w * 16 + hn) * 2] - M);
-        lsum += wt * sm_ml[(w * 16 + hn) * 2 + 1];
-        o += wt * sm_o[((int64_t)w * G + hn) * D + ch];
+        const float wt = fast_exp2(sm_ml[(w * 16 + cn) * 2] - M);
+        lsum += wt * sm_ml[(w * 16 + cn) * 2 + 1];
+        o += wt * sm_o[((int64_t)w * ncol + cn) * D + ch];
       }
     }
-    const int hh = kvh * G + hn;
+    const int ct = MT ? cn / G : 0;
+    const int hh = kvh * G + (cn - ct * G);
+    const int row = seq * Tq + ct;
     if (S == 1) {
       const float r = lsum > 0.0f ? o / lsum : 0.0f;
-      const int64_t oi = ((int64_t)seq * Hq + hh) * D + ch;
+      const int64_t oi = ((int64_t)row * Hq + hh) * D + ch;
       if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = (uint16_t)f32_to_bf16_bits(r);
       else reinterpret_cast<float*>(a.out)[oi] = r;
     } else {
-      const int64_t pi = ((int64_t)seq * Hq + hh) * S + split;
+      const int64_t pi = ((int64_t)row * Hq + hh) * S + split;
       a.ws_o[pi * D + ch] = o;
       if (ch == 0) {
         a.ws_ml[pi * 2] = M;
@@ -560,18 +576,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
   }
 }
 
-template <int D, bool V_I8, bool EXPORT_QK, bool FUSED>
+template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT>
 hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   if (phase == DecodePhase::kCombine) {
     if (a.num_splits > 1)
-      k_combine<D><<<dim3(a.Hq, a.num_seqs, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
-                                                                 a.out_bf16, a.out);
+      k_combine<D><<<dim3(a.Hq, a.num_seqs * a.tq, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
+                                                                        a.out_bf16, a.out);
     return hipGetLastError();
   }
   const dim3 grid(a.num_splits, a.Hkv, a.num_seqs);
   // LDS: per-wave partials [kWaves][G][D] plus (max, sum) pairs.
-  const size_t lds = EXPORT_QK ? 0 : (size_t)(kWaves * 32 + kWaves * a.G * D) * sizeof(float);
-  auto kern = k_decode<D, V_I8, EXPORT_QK, FUSED>;
+  const size_t lds = EXPORT_QK ? 0 : (size_t)(kWaves * 32 + kWaves * a.G * a.tq * D) * sizeof(float);
+  auto kern = k_decode<D, V_I8, EXPORT_QK, FUSED, MT>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -580,8 +596,8 @@ hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   if (!EXPORT_QK && a.num_splits > 1 && phase == DecodePhase::kBoth) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_combine<D><<<dim3(a.Hq, a.num_seqs, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
-                                                               a.out_bf16, a.out);
+    k_combine<D><<<dim3(a.Hq, a.num_seqs * a.tq, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
+                                                                      a.out_bf16, a.out);
   }
   return hipGetLastError();
 }
@@ -590,10 +606,13 @@ template <bool EXPORT_QK>
 hipError_t dispatch(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
 #define QA_DEC(DD)                                                                                  \
   if (a.q_in != nullptr)                                                                            \
-    return a.v_int8 ? run_decode<DD, true, false, true>(a, phase, st)                               \
-                    : run_decode<DD, false, false, true>(a, phase, st);                             \
-  return a.v_int8 ? run_decode<DD, true, EXPORT_QK, false>(a, phase, st)                            \
-                  : run_decode<DD, false, EXPORT_QK, false>(a, phase, st)
+    return a.v_int8 ? run_decode<DD, true, false, true, false>(a, phase, st)                        \
+                    : run_decode<DD, false, false, true, false>(a, phase, st);                      \
+  if (!EXPORT_QK && a.tq > 1)                                                                       \
+    return a.v_int8 ? run_decode<DD, true, false, false, true>(a, phase, st)                        \
+                    : run_decode<DD, false, false, false, true>(a, phase, st);                      \
+  return a.v_int8 ? run_decode<DD, true, EXPORT_QK, false, false>(a, phase, st)                     \
+                  : run_decode<DD, false, EXPORT_QK, false, false>(a, phase, st)
   switch (a.D) {
     case 64: QA_DEC(64);
     case 128: QA_DEC(128);

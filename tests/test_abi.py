@@ -210,3 +210,21 @@ def test_probe_library_exports_and_rejects():
     assert L.qa_probe_mfma(4, 10, 4, FAKE, None) == 1
     assert L.qa_probe_mfma(0, 0, 4, FAKE, None) == 1
     assert L.qa_probe_mfma(0, 10, 4, None, None) == 1
+
+
+def test_decode_mt_validation(qa):
+    L = qa.lib
+    p = _dp(qa, num_splits=8)                        # 24 query heads over 4 KV heads: G = 6
+    call = lambda p, T, ws_bytes=1 << 30: L.qa_paged_attention_decode_mt(
+        ctypes.byref(p), T, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws_bytes, FAKE, None)
+    assert call(p, 0) == qa.QA_ERR_INVALID_ARG
+    assert call(p, 3) == qa.QA_ERR_UNSUPPORTED       # 6 x 3 > 16 columns
+    need = L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 2)
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(2 * 2 * 24 * 8 * 256 * 4) + al(2 * 2 * 24 * 8 * 2 * 4)
+    assert L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 1) == L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    assert L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 3) == 0
+    assert call(p, 2, need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert call(_dp(qa, head_dim=96), 1) == qa.QA_ERR_UNSUPPORTED
+    assert L.qa_paged_attention_decode_mt(ctypes.byref(p), 2, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                          FAKE, need, FAKE, None) == qa.QA_ERR_INVALID_ARG

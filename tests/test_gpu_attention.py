@@ -207,6 +207,56 @@ def test_decode_step_unwritten_slot(qa):
 
 
 # ---------------------------------------------------------------------------
+# multi-token decode (T new query tokens per sequence in the decode kernel)
+# ---------------------------------------------------------------------------
+
+MT_CASES = [
+    # (d, G, Hkv, T, contexts, v_int8, splits)
+    (256, 6, 4, 2, [3000, 17, 1600], False, 0),
+    (256, 6, 2, 2, [500, 2], True, 8),
+    (128, 4, 2, 4, [700, 33], False, 3),
+    (64, 1, 2, 16, [300, 16, 5], False, 0),     # context 5 < 16 tokens: early tokens see nothing
+    (64, 8, 1, 2, [129], True, 1),              # one split: the kernel writes the output
+    (128, 16, 1, 1, [640], False, 0),
+]
+
+
+def _mt_run(qa, inp, T, splits):
+    spec = inp.spec
+    kc, ks, vc, vs = gpu_cache(qa, inp, spec.v_int8)
+    q8, qs = qa.quantize_q(dev_bits(inp.q, spec.dtype))
+    S, Hq, d = spec.num_seqs, spec.num_q_heads, spec.head_dim
+    out = qa.paged_attention_decode_mt(q8.view(S, T, Hq, d), qs.view(S, T, Hq), kc, ks, vc, vs,
+                                       torch.from_numpy(inp.block_tables).cuda(),
+                                       torch.from_numpy(inp.context_lens).cuda(), num_splits=splits)
+    torch.cuda.synchronize()
+    return out, (q8, qs, kc, ks, vc, vs)
+
+
+@pytest.mark.parametrize("case", MT_CASES, ids=lambda c: f"d{c[0]}_G{c[1]}_Hkv{c[2]}_T{c[3]}_{'i8V' if c[5] else 'bf16V'}_S{c[6]}")
+def test_decode_mt_parity(qa, case):
+    d, G, Hkv, T, ctx, v_int8, splits = case
+    say(f"multi-token decode {case}")
+    spec = PagedSpec("mt", 501 + d + G + T, len(ctx), G * Hkv, Hkv, d, ctx, [T] * len(ctx), k_bias_std=2.0,
+                     v_int8=v_int8, pool_blocks=sum(-(-c // 16) for c in ctx) + 4)
+    inp = paged_inputs(spec)
+    got, _ = _mt_run(qa, inp, T, splits)
+    want = _prefill_oracle(inp).reshape(got.shape)
+    assert_close(got.cpu().numpy(), want, "multi-token decode")
+
+
+def test_decode_mt_one_token_is_decode(qa):
+    """T = 1 gives qa_paged_attention_decode's result bit for bit."""
+    spec = PagedSpec("mt1", 77, 3, 24, 4, 256, [1500, 40, 999], [1, 1, 1], k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    got, (q8, qs, kc, ks, vc, vs) = _mt_run(qa, inp, 1, 0)
+    ref = qa.paged_attention_decode(q8, qs, kc, ks, vc, vs, torch.from_numpy(inp.block_tables).cuda(),
+                                    torch.from_numpy(inp.context_lens).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(ref.shape), ref)
+
+
+# ---------------------------------------------------------------------------
 # chunked prefill
 # ---------------------------------------------------------------------------
 

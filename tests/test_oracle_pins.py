@@ -375,6 +375,30 @@ def test_prefill_last_row_equals_decode_and_first_row_of_fresh_chunk():
         np.testing.assert_array_equal(got[0, h], vv[0, h // 3])
 
 
+def test_multi_token_decode_equals_per_token_decodes():
+    """A T-token step (the chunk form of the prefill oracle, T tokens per
+    sequence) equals T one-token decodes, token j with the context cut after
+    its own position ctx - T + j: pins the causal offset the multi-token
+    decode kernel applies per query column. Contexts shorter than T leave
+    the earliest tokens with no key (zeros)."""
+    T = 4
+    ctx = [40, 17, 3]
+    spec = PagedSpec("mtp", 91, len(ctx), 8, 2, 64, ctx, [T] * len(ctx), k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    c = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks)
+    q_i8, q_s = oracle.quantize_q(inp.q)
+    got = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    for s_, cl in enumerate(ctx):
+        for j in range(T):
+            r = s_ * T + j
+            lens = np.zeros(len(ctx), np.int32)
+            lens[s_] = max(cl - T + j + 1, 0)
+            dec = oracle.paged_decode(np.repeat(q_i8[r:r + 1], len(ctx), 0), np.repeat(q_s[r:r + 1], len(ctx), 0),
+                                      c, inp.block_tables, lens, 2)
+            np.testing.assert_allclose(got[r], dec[s_], rtol=1e-12, atol=1e-14)
+    assert np.all(got[2 * T:2 * T + 1] == 0)          # sequence 2 (ctx 3): token 0 sits at position -1
+
+
 def test_prefill_row_subset_matches_full():
     spec, inp, c, q_i8, q_s = _prefill_setup([90], [33])
     full = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
