@@ -53,6 +53,18 @@ def _softmax_pv(s: np.ndarray, v: np.ndarray) -> np.ndarray:
     return out
 
 
+def _logsumexp_rows(s: np.ndarray) -> np.ndarray:
+    """ln(sum_j exp(s_j)) per row of s (masked entries -inf) in fp64, as
+    m + ln(sum_j exp(s_j - m)); a row with no visible entry gives -inf."""
+    if s.shape[-1] == 0:
+        return np.full(s.shape[:-1], -np.inf)
+    m = np.max(s, axis=-1)
+    live = np.isfinite(m)
+    mm = np.where(live, m, 0.0)
+    l = np.exp(s - mm[..., None]).sum(axis=-1)
+    return np.where(live, mm + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+
+
 def paged_qk_int32(q_i8, caches, block_tables, context_lens, num_kv_heads):
     """INT32 QK accumulators of decode: one query token per sequence.
 
@@ -194,7 +206,8 @@ def chunked_prefill(q_i8, q_scale, cu_seqlens_q, context_lens, caches, block_tab
 
 
 def dense_sage_attention(quant, v_bits, dtype="f16", causal=False, scale=None,
-                         q_block=128, k_block=64, rows=None, heads=None, batches=None):
+                         q_block=128, k_block=64, rows=None, heads=None, batches=None,
+                         return_lse=False):
     """SageAttention-style dense attention on pre-quantized NHD inputs.
 
     ``quant`` is the dict from ``sage_quantize``. [SAGE-MACA] (compute
@@ -203,7 +216,9 @@ def dense_sage_attention(quant, v_bits, dtype="f16", causal=False, scale=None,
     softmax; P.V with fp16 V. Here the softmax and P.V are exact fp64 on the
     same recovered scores. Causal: query i sees key j <= i + (Nk - Nq)
     (bottom-right alignment; identical to top-left when Nq == Nk).
-    Returns fp64 [B, Nq, Hq, d].
+    Returns fp64 [B, Nq, Hq, d]; with ``return_lse`` also the natural-log
+    sum of exponentials of each row's visible scores, fp64 [B, Hq, Nq] (-inf
+    for a row that sees no key): [SAGE-MACA] feature matrix "LSE return".
     """
     q_i8, k_i8 = quant["q_i8"], quant["k_i8"]
     B, Nq, Hq, d = q_i8.shape
@@ -212,6 +227,7 @@ def dense_sage_attention(quant, v_bits, dtype="f16", causal=False, scale=None,
     sc = _scale(scale, d)
     v = widen(v_bits, dtype).astype(np.float64)
     out = np.zeros((B, Nq, Hq, d), np.float64)
+    lse = np.full((B, Hq, Nq), -np.inf)
     qr = np.arange(Nq) if rows is None else np.asarray(rows)
     qblk = qr // q_block
     kblk = np.arange(Nk) // k_block
@@ -231,7 +247,71 @@ def dense_sage_attention(quant, v_bits, dtype="f16", causal=False, scale=None,
             if vis is not None:
                 s_ = np.where(vis, s_, -np.inf)
             out[b, qr, h] = _softmax_pv(s_, v[b, :, kvh])
-    return out
+            if return_lse:
+                lse[b, h, qr] = _logsumexp_rows(s_)
+    return (out, lse) if return_lse else out
+
+
+def sage_smooth_v(v_bits, dtype="f16"):
+    """V mean fusion ([SAGE-MACA] feature matrix "smooth_v"; the V mean
+    subtraction kernel; compute-pipeline step 8 adds the mean back).
+
+    The pages fix neither precision; reading taken, as for smooth_k: the
+    per-(b, h, c) sum over all N tokens in fp64, divided by N in fp64 and
+    rounded to fp32 (mu_v); V' = fl16(fl32(V) - mu_v), i.e. the fp32
+    difference rounded to the fp16 operand of the P.V product. Since every
+    softmax row sums to 1, attention(P, V) = attention(P, V') + mu_v up to
+    the fp16 rounding of V'. Returns (V' as fp16 bit patterns, mu_v fp32
+    [B, Hkv, d])."""
+    v = widen(v_bits, dtype)
+    B, N, H, d = v.shape
+    if N > 0:
+        mu = (v.astype(np.float64).sum(axis=1) / np.float64(N)).astype(np.float32)
+    else:
+        mu = np.zeros((B, H, d), np.float32)
+    vp = (v - mu[:, None, :, :]).astype(np.float32)
+    return vp.astype(np.float16).view(np.uint16), mu
+
+
+def sage_lse_correction(q_bits, k_mean, dtype="f16", scale=None):
+    """smooth_k shifts every score of query row i by -q_i . mu * scale
+    (K' = K - mu), so the LSE of the smoothed scores is corrected by adding
+    it back ([SAGE-MACA] feature matrix: smooth_k "with LSE correction"):
+    corr[b, h, i] = scale * sum_c q[b, i, h, c] * mu[b, h // G, c], with the
+    unquantized q (fp32 values) and mu (fp32), evaluated in fp64.
+    Returns fp64 [B, Hq, Nq]."""
+    q = widen(q_bits, dtype).astype(np.float64)
+    B, Nq, Hq, d = q.shape
+    Hkv = k_mean.shape[1]
+    G = Hq // Hkv
+    sc = _scale(scale, d)
+    mu = np.repeat(np.asarray(k_mean, np.float64), G, axis=1)        # [B, Hq, d]
+    return np.einsum("bnhc,bhc->bhn", q, mu) * sc
+
+
+def sage_forward(q_bits, k_bits, v_bits, dtype="f16", causal=False, smooth_k=True, smooth_v=False,
+                 return_lse=False, scale=None):
+    """The whole dense call with its options ([SAGE-MACA] API: smooth_k,
+    smooth_v, return_lse; NHD inputs, the HND layout is the same tensors
+    transposed): quantize (smooth_k), optionally smooth V, attend, add the V
+    mean back on rows that see a key, and correct the LSE for the K mean.
+    Returns out fp64 [B, Nq, Hq, d] (and lse fp64 [B, Hq, Nq])."""
+    from .quant import sage_quantize
+    quant = sage_quantize(q_bits, k_bits, dtype, smooth_k=smooth_k)
+    vb, vdt = v_bits, dtype
+    if smooth_v:
+        vb, mu_v = sage_smooth_v(v_bits, dtype)
+        vdt = "f16"
+    out, lse = dense_sage_attention(quant, vb, vdt, causal=causal, scale=scale, return_lse=True)
+    if smooth_v:
+        B, Nq, Hq, d = out.shape
+        G = Hq // mu_v.shape[1]
+        mu = np.repeat(mu_v.astype(np.float64), G, axis=1)            # [B, Hq, d]
+        live = np.isfinite(lse).transpose(0, 2, 1)[..., None]         # [B, Nq, Hq, 1]
+        out = out + np.where(live, mu[:, None, :, :], 0.0)
+    if smooth_k:
+        lse = lse + sage_lse_correction(q_bits, quant["k_mean"], dtype, scale)
+    return (out, lse) if return_lse else out
 
 
 def attention_fp64(q, k, v, scale, visible=None):

@@ -88,6 +88,18 @@ MUTATIONS = [
      pins.test_sage_per_block_scales_brute_force, ()),
     ("q_block_rows_64", oq, "sage_quantize", "q_i8, q_scale = per_block(q, q_block)",
      "q_i8, q_scale = per_block(q, 64)", pins.test_sage_per_block_scales_brute_force, ()),
+    ("lse_log2_instead_of_ln", oa, "_logsumexp_rows", "mm + np.log(", "mm + np.log2(",
+     pins.test_lse_of_equal_scores_is_log_of_visible_count, (False, None)),
+    ("lse_drops_max_shift", oa, "_logsumexp_rows", "return np.where(live, mm + np.log(", "return np.where(live, np.log(",
+     pins.test_lse_equals_direct_sum_over_scores, ()),
+    ("lse_correction_sign", oa, "sage_forward", "lse = lse + sage_lse_correction(", "lse = lse - sage_lse_correction(",
+     pins.test_lse_correction_restores_constant_key_scores, ()),
+    ("lse_correction_head_of_group", oa, "sage_lse_correction", "np.repeat(np.asarray(k_mean, np.float64), G, axis=1)",
+     "np.tile(np.asarray(k_mean, np.float64), (1, G, 1))", pins.test_lse_correction_restores_constant_key_scores, ()),
+    ("smooth_v_no_add_back", oa, "sage_forward", "out = out + np.where(live", "out = out + 0 * np.where(live",
+     pins.test_smooth_v_adds_the_mean_back, ()),
+    ("smooth_v_mean_divisor", oa, "sage_smooth_v", "/ np.float64(N))", "/ np.float64(N - 1))",
+     pins.test_smooth_v_adds_the_mean_back, ()),
 ]
 
 

@@ -494,6 +494,71 @@ def test_dense_zero_scales_give_uniform_attention(causal):
     np.testing.assert_allclose(got[0, 128:256, 1], mean[128:256, 0], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal,Nk", [(False, None), (True, None), (True, 90)])
+def test_lse_of_equal_scores_is_log_of_visible_count(causal, Nk):
+    """Zero queries make every score 0, so each row's LSE is ln(#visible keys)
+    exactly (-inf for a row that sees none): bottom-right causal rows see
+    i + 1 + (Nk - Nq) keys."""
+    spec, inp = _dense(B=1, H=2, Hkv=1, N=130, Nk=Nk)
+    q0 = np.zeros_like(inp.q)
+    out, lse = oracle.sage_forward(q0, inp.k, inp.v, "f16", causal=causal, return_lse=True)
+    Nq, Nk_ = spec.seq_q, spec.seq_k
+    cnt = np.minimum(np.arange(Nq) + 1 + (Nk_ - Nq), Nk_) if causal else np.full(Nq, Nk_)
+    want = np.where(cnt > 0, np.log(np.maximum(cnt, 1).astype(np.float64)), -np.inf)
+    for h in range(2):
+        np.testing.assert_allclose(lse[0, h], want, rtol=0, atol=1e-13)
+
+
+def test_lse_correction_restores_constant_key_scores():
+    """Keys equal to a constant c at every token: smooth_k removes them
+    entirely (K' = 0, all smoothed scores 0), and the corrected LSE must be
+    the unsmoothed one, q.c*scale + ln(#visible), in closed form."""
+    spec, inp = _dense(B=1, H=4, Hkv=2, N=100, d=64)
+    k = np.broadcast_to(inp.k[:, :1], inp.k.shape).copy()           # token 0's row everywhere
+    out, lse = oracle.sage_forward(inp.q, k, inp.v, "f16", causal=True, return_lse=True)
+    q = oq.widen(inp.q, "f16").astype(np.float64)
+    c = oq.widen(k, "f16").astype(np.float64)[0, 0]                # [Hkv, d]
+    for h in range(4):
+        want = (q[0, :, h] @ c[h // 2]) / 8.0 + np.log(np.arange(1, 101, dtype=np.float64))
+        np.testing.assert_allclose(lse[0, h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_lse_equals_direct_sum_over_scores():
+    """The LSE is ln(sum exp) of the same recovered scores the softmax uses:
+    exp(lse) equals the brute-force sum of exp(score) (fp64), and with
+    smooth_k off no correction is added."""
+    spec, inp = _dense(B=1, H=2, Hkv=2, N=70, d=64)
+    qz = oracle.sage_quantize(inp.q, inp.k, "f16", smooth_k=False)
+    _, lse = oracle.sage_forward(inp.q, inp.k, inp.v, "f16", smooth_k=False, return_lse=True)
+    for h in range(2):
+        qd = qz["q_i8"][0, :, h].astype(np.float64) * qz["q_scale"][0, h, 0]
+        s = np.zeros((70, 70))
+        for j in range(70):
+            kd = qz["k_i8"][0, j, h].astype(np.float64) * qz["k_scale"][0, h, j // 64]
+            s[:, j] = (qd @ kd) / 8.0
+        np.testing.assert_allclose(np.exp(lse[0, h]), np.exp(s).sum(axis=1), rtol=1e-12)
+
+
+def test_smooth_v_adds_the_mean_back():
+    """With V carrying a large channel bias, smooth_v (subtract the mean,
+    attend, add it back) reproduces the unsmoothed output within the fp16
+    rounding of V' = V - mu (half an fp16 ulp of |V'| per element, averaged
+    by the softmax), while forgetting the add-back would be off by mu."""
+    spec, inp = _dense(B=1, H=2, Hkv=2, N=120, d=64)
+    v = oq.widen(inp.v, "f16") + np.float32(6.0) * (np.arange(64, dtype=np.float32) % 3 - 1)
+    vb = v.astype(np.float16).view(np.uint16)
+    for causal in (False, True):
+        a = oracle.sage_forward(inp.q, inp.k, vb, "f16", causal=causal)
+        b = oracle.sage_forward(inp.q, inp.k, vb, "f16", causal=causal, smooth_v=True)
+        vp, mu = oracle.sage_smooth_v(vb, "f16")
+        bound = np.max(np.abs(oq.widen(vp, "f16"))) * 2.0 ** -11 + 1e-12
+        assert np.max(np.abs(a - b)) <= bound
+        assert np.max(np.abs(mu)) > 100 * bound            # the add-back is what makes them agree
+    # the mean is the exact fp64 mean rounded to fp32
+    exact = oq.widen(vb, "f16").astype(np.float64).sum(axis=1) / 120.0
+    np.testing.assert_array_equal(mu, exact.astype(np.float32))
+
+
 def test_smoothing_leaves_unquantized_attention_unchanged():
     # softmax is invariant to adding q.mu to every score of a row
     spec, inp = _dense(N=100, d=64)
