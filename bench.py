@@ -88,11 +88,18 @@ KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_quantize_amd", "csrc",
 
 
 def kernel_source_digest() -> str:
+    """sha256 over what the decode kernel is built from: decode.hip,
+    common.h and the DecodeArgs declaration of internal.h (the header's
+    other structs belong to other kernels)."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(f, "rb") as fh:
-            h.update(fh.read())
+            text = fh.read()
+        if f.endswith("internal.h"):
+            i = text.index(b"struct DecodeArgs {")
+            text = text[i:text.index(b"};", i) + 2]
+        h.update(text)
     return h.hexdigest()
 
 

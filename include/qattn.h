@@ -390,6 +390,40 @@ qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, c
                                     const void* v, void* workspace, size_t workspace_bytes,
                                     void* out, qa_stream_t stream);
 
+/* Tensor layouts of the dense call: NHD = [batch, seq, heads, head_dim],
+ * HND = [batch, heads, seq, head_dim] ([SAGE-MACA] API, tensor_layout). */
+typedef enum { QA_LAYOUT_NHD = 0, QA_LAYOUT_HND = 1 } qa_layout_t;
+
+typedef struct {
+  int32_t layout;    /* qa_layout_t of q, k, v and out (all four alike) */
+  int32_t smooth_v;  /* nonzero: V' = fl16(fl32(V) - mu_v), mu_v the per-(batch, KV head,
+                        channel) mean of V over seq_k (fp64 sum, fp32 result); mu_v is added
+                        back in fp32 to every output row that sees at least one key */
+} qa_dense_options_t;
+
+/*
+ * The dense forward with its options ([SAGE-MACA] API: tensor_layout,
+ * smooth_k, smooth_v, return_lse). Same computation as
+ * qa_dense_sage_attention, plus:
+ *   layout    HND inputs and output are accepted as they are (no transpose
+ *             pass; the kernels read and write with the layout's strides)
+ *   smooth_v  as described in qa_dense_options_t
+ *   lse       NULL, or out [batch, num_q_heads, seq_q] fp32: the natural-log
+ *             log-sum-exp of each row's scores softmax_scale * q . k over
+ *             the keys it sees; with smooth_k the kernel sees K' = K - mu, and
+ *             softmax_scale * q . mu (unquantized q, fp32) is added back
+ *             (the "LSE correction"), so lse is that of the unsmoothed
+ *             scores. Rows that see no key get -inf.
+ * options NULL means NHD without smooth_v. workspace >=
+ * qa_dense_sage_ex_workspace_size bytes (a superset of the plain call's).
+ * Errors as qa_dense_sage_attention; QA_ERR_INVALID_ARG for an unknown layout.
+ */
+size_t qa_dense_sage_ex_workspace_size(const qa_dense_params_t* p, const qa_dense_options_t* options);
+qa_status_t qa_dense_sage_attention_ex(const qa_dense_params_t* p, const qa_dense_options_t* options,
+                                       const void* q, const void* k, const void* v, void* workspace,
+                                       size_t workspace_bytes, void* out, float* lse,
+                                       qa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,13 @@ class DenseParams(ctypes.Structure):
                 ("is_causal", _i32), ("softmax_scale", _f32), ("out_dtype", ctypes.c_int)]
 
 
+class DenseOptions(ctypes.Structure):
+    _fields_ = [("layout", _i32), ("smooth_v", _i32)]
+
+
+QA_LAYOUT_NHD, QA_LAYOUT_HND = 0, 1
+_LAYOUTS = {"NHD": QA_LAYOUT_NHD, "HND": QA_LAYOUT_HND}
+
 _P = ctypes.POINTER
 _STEP_ARGS = ([_P(DecodeParams), _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64, _i64, ctypes.c_int]
               + [_c_void_p] * 8 + [_size, _c_void_p, _c_void_p])
@@ -89,6 +96,9 @@ _SIGS = {
     "qa_dense_sage_workspace_size": (_size, [_P(DenseParams)]),
     "qa_dense_sage_attention": (ctypes.c_int, [_P(DenseParams)] + [_c_void_p] * 4 + [_size, _c_void_p,
                                                                                         _c_void_p]),
+    "qa_dense_sage_ex_workspace_size": (_size, [_P(DenseParams), _P(DenseOptions)]),
+    "qa_dense_sage_attention_ex": (ctypes.c_int, [_P(DenseParams), _P(DenseOptions)] + [_c_void_p] * 4 +
+                                   [_size, _c_void_p, _c_void_p, _c_void_p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     try:
@@ -371,3 +381,38 @@ def dense_sage_attention(q, k, v, is_causal=False, smooth_k=True, softmax_scale=
     _check(lib.qa_dense_sage_attention(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
                                        workspace.numel(), _ptr(out), _stream()))
     return out
+
+
+def dense_sage_attention_ex(q, k, v, tensor_layout="NHD", is_causal=False, smooth_k=True, smooth_v=False,
+                            return_lse=False, softmax_scale=0.0, out_dtype=torch.float32, workspace=None,
+                            out=None, lse=None):
+    """The dense forward with its options: tensor_layout "NHD" ([B, N, H, d])
+    or "HND" ([B, H, N, d]) for q, k, v and out; smooth_v; return_lse (fp32
+    [B, Hq, Nq], natural log, corrected for the K mean under smooth_k).
+    Returns out, or (out, lse) with return_lse."""
+    _require_cuda(q, k, v)
+    if tensor_layout not in _LAYOUTS:
+        raise ValueError(f"tensor_layout must be NHD or HND, not {tensor_layout!r}")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous in their layout")
+    if tensor_layout == "HND":
+        B, Hq, Nq, d = q.shape
+        Hkv, Nk = k.shape[1], k.shape[2]
+    else:
+        B, Nq, Hq, d = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+    p = DenseParams(B, Nq, Nk, Hq, Hkv, d, _dt(q.dtype), int(bool(smooth_k)), int(bool(is_causal)),
+                    softmax_scale, _dt(out_dtype))
+    o = DenseOptions(_LAYOUTS[tensor_layout], int(bool(smooth_v)))
+    if workspace is None:
+        workspace = torch.empty(max(lib.qa_dense_sage_ex_workspace_size(ctypes.byref(p), ctypes.byref(o)), 16),
+                                dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.qa_dense_sage_attention_ex(ctypes.byref(p), ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(workspace), workspace.numel(), _ptr(out),
+                                          _ptr(lse) if return_lse else None, _stream()))
+    return (out, lse) if return_lse else out

@@ -35,6 +35,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
     if (!(cond)) return fail(st, __VA_ARGS__); \
   } while (0)
 
+float natural_scale(float softmax_scale, int32_t d) {
+  return softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)d));
+}
+
 float log2_scale(float softmax_scale, int32_t d) {
   const double s = softmax_scale > 0.0f ? (double)softmax_scale : 1.0 / std::sqrt((double)d);
   return (float)(s * 1.4426950408889634);
@@ -112,13 +116,14 @@ qa_status_t check_dense(const qa_dense_params_t* p) {
 }
 
 // Dense workspace: [partial sums][q_i8][k blocks][v blocks][q_scale][k_scale][k_mean], 256-aligned.
+// The options call appends [v_mean][lse_corr].
 struct DenseWs {
-  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, total;
+  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DenseWs dense_layout(const qa_dense_params_t* p, bool with_attention) {
+DenseWs dense_layout(const qa_dense_params_t* p, bool with_attention, bool ex = false) {
   DenseWs w{};
   const size_t B = p->batch, Nq = p->seq_q, Nk = p->seq_k, Hq = p->num_q_heads, Hkv = p->num_kv_heads,
                D = p->head_dim;
@@ -132,9 +137,74 @@ DenseWs dense_layout(const qa_dense_params_t* p, bool with_attention) {
     w.q_scale = off; off += al(B * Hq * ((Nq + 127) / 128) * sizeof(float));
     w.k_scale = off; off += al(B * Hkv * ((Nk + 63) / 64) * sizeof(float));
     w.k_mean = off; off += al(B * Hkv * D * sizeof(float));
+    if (ex) {
+      w.v_mean = off; off += al(B * Hkv * D * sizeof(float));
+      w.lse_corr = off; off += al(B * Hq * Nq * sizeof(float));
+    }
   }
   w.total = off;
   return w;
+}
+
+// Element strides (batch, token, head) of a [batch, N, H, D] (NHD) or
+// [batch, H, N, D] (HND) tensor.
+struct Strides {
+  int64_t b, t, h;
+};
+Strides layout_strides(int32_t layout, int64_t N, int64_t H, int64_t D) {
+  if (layout == QA_LAYOUT_HND) return {H * N * D, D, N * D};
+  return {N * H * D, H * D, D};
+}
+
+qa_status_t dense_attention_impl(const qa_dense_params_t* p, const qa_dense_options_t* o, const void* q,
+                                 const void* k, const void* v, void* workspace, size_t workspace_bytes,
+                                 void* out, float* lse, qa_stream_t stream, bool ex) {
+  qa_status_t st = check_dense(p);
+  if (st != QA_OK) return st;
+  const int32_t layout = o ? o->layout : QA_LAYOUT_NHD;
+  const bool smooth_v = o && o->smooth_v != 0;
+  QA_REQUIRE(layout == QA_LAYOUT_NHD || layout == QA_LAYOUT_HND, QA_ERR_INVALID_ARG, "unknown layout %d",
+             layout);
+  if (p->batch == 0 || p->seq_q == 0) return QA_OK;
+  QA_REQUIRE(q && k && v && out && workspace, QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(workspace),
+             QA_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
+  QA_REQUIRE(((uintptr_t)lse & 3u) == 0, QA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const DenseWs w = dense_layout(p, true, ex);
+  QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+             workspace_bytes, w.total);
+  const int64_t D = p->head_dim;
+  const Strides sq = layout_strides(layout, p->seq_q, p->num_q_heads, D);
+  const Strides sk = layout_strides(layout, p->seq_k, p->num_kv_heads, D);
+  char* ws = (char*)workspace;
+  qa::SagePrepArgs pa{};
+  pa.q = q; pa.k = k; pa.v = v; pa.bf16 = p->dtype == QA_DT_BF16;
+  pa.q_sb = sq.b; pa.q_st = sq.t; pa.q_sh = sq.h;
+  pa.k_sb = sk.b; pa.k_st = sk.t; pa.k_sh = sk.h;
+  pa.v_sb = sk.b; pa.v_st = sk.t; pa.v_sh = sk.h;
+  pa.B = p->batch; pa.Nq = p->seq_q; pa.Nk = p->seq_k; pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads;
+  pa.D = p->head_dim; pa.smooth_k = p->smooth_k != 0;
+  pa.smooth_v = smooth_v && p->seq_k > 0;
+  pa.v_mean = pa.smooth_v ? (float*)(ws + w.v_mean) : nullptr;
+  pa.lse_corr = lse != nullptr && pa.smooth_k ? (float*)(ws + w.lse_corr) : nullptr;
+  pa.corr_scale = natural_scale(p->softmax_scale, p->head_dim);
+  pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
+  pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
+  pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
+  st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
+  if (st != QA_OK) return st;
+  const Strides so = layout_strides(layout, p->seq_q, p->num_q_heads, D);
+  qa::FlashArgs a{};
+  a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
+  a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
+  a.o_sb = so.b; a.o_st = so.t; a.o_sh = so.h;
+  a.v_mean = pa.v_mean; a.lse = lse; a.lse_corr = pa.lse_corr;
+  a.num_seqs = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
+  a.D = p->head_dim; a.max_blocks = 0; a.max_seqlen_q = p->seq_q; a.Nq = p->seq_q; a.Nk = p->seq_k;
+  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.dense = true; a.causal = p->is_causal != 0; a.v_int8 = false; a.v_f16 = true;  // V blocks are fp16
+  a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = p->out_dtype == QA_DT_F16;
+  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "dense attention launch");
 }
 
 }  // namespace
@@ -478,6 +548,10 @@ qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, co
   a.q = q; a.k = k; a.v = nullptr; a.bf16 = p->dtype == QA_DT_BF16;
   a.B = p->batch; a.Nq = p->seq_q; a.Nk = p->seq_k; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
   a.D = p->head_dim; a.smooth_k = p->smooth_k != 0;
+  const Strides sq = layout_strides(QA_LAYOUT_NHD, p->seq_q, p->num_q_heads, p->head_dim);
+  const Strides sk = layout_strides(QA_LAYOUT_NHD, p->seq_k, p->num_kv_heads, p->head_dim);
+  a.q_sb = sq.b; a.q_st = sq.t; a.q_sh = sq.h;
+  a.k_sb = sk.b; a.k_st = sk.t; a.k_sh = sk.h;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_paged = nullptr; a.k_scale = k_scale;
   a.k_mean = k_mean; a.partial = (double*)((char*)workspace + w.partial); a.v_paged = nullptr;
   return hip_status(qa::launch_sage_prep(a, (hipStream_t)stream), "qa_dense_sage_quantize launch");
@@ -490,34 +564,19 @@ size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p) {
 
 qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, const void* k, const void* v,
                                     void* workspace, size_t workspace_bytes, void* out, qa_stream_t stream) {
-  qa_status_t st = check_dense(p);
-  if (st != QA_OK) return st;
-  if (p->batch == 0 || p->seq_q == 0) return QA_OK;
-  QA_REQUIRE(q && k && v && out && workspace, QA_ERR_INVALID_ARG, "null pointer");
-  QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(workspace),
-             QA_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
-  const DenseWs w = dense_layout(p, true);
-  QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
-             workspace_bytes, w.total);
-  char* ws = (char*)workspace;
-  qa::SagePrepArgs pa{};
-  pa.q = q; pa.k = k; pa.v = v; pa.bf16 = p->dtype == QA_DT_BF16;
-  pa.B = p->batch; pa.Nq = p->seq_q; pa.Nk = p->seq_k; pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads;
-  pa.D = p->head_dim; pa.smooth_k = p->smooth_k != 0;
-  pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
-  pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
-  pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
-  st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
-  if (st != QA_OK) return st;
-  qa::FlashArgs a{};
-  a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
-  a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
-  a.num_seqs = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
-  a.D = p->head_dim; a.max_blocks = 0; a.max_seqlen_q = p->seq_q; a.Nq = p->seq_q; a.Nk = p->seq_k;
-  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
-  a.dense = true; a.causal = p->is_causal != 0; a.v_int8 = false; a.v_f16 = true;  // V blocks are fp16
-  a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = p->out_dtype == QA_DT_F16;
-  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "dense attention launch");
+  return dense_attention_impl(p, nullptr, q, k, v, workspace, workspace_bytes, out, nullptr, stream, false);
+}
+
+size_t qa_dense_sage_ex_workspace_size(const qa_dense_params_t* p, const qa_dense_options_t* options) {
+  (void)options;
+  if (check_dense(p) != QA_OK) return 0;
+  return dense_layout(p, true, true).total;
+}
+
+qa_status_t qa_dense_sage_attention_ex(const qa_dense_params_t* p, const qa_dense_options_t* options,
+                                       const void* q, const void* k, const void* v, void* workspace,
+                                       size_t workspace_bytes, void* out, float* lse, qa_stream_t stream) {
+  return dense_attention_impl(p, options, q, k, v, workspace, workspace_bytes, out, lse, stream, true);
 }
 
 }  // extern "C"

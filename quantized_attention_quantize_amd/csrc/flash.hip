@@ -575,10 +575,32 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     const float l = kRowSumMfma ? Ls[qg][0] : group4_sum(l_run[qg]);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (qi[qg] >= Tq) continue;
-    const int64_t ob = ((q_row0 + qi[qg]) * Hq + qh[qg]) * D + 4 * g;
+    int64_t ob;
+    const float* vmu = nullptr;   // dense smooth_v: the V mean returns on rows that see a key
+    if constexpr (DENSE) {
+      ob = (int64_t)z * a.o_sb + (int64_t)qi[qg] * a.o_st + (int64_t)qh[qg] * a.o_sh + 4 * g;
+      if (a.v_mean != nullptr && l > 0.0f) vmu = a.v_mean + ((int64_t)z * Hkv + kvh) * D + 4 * g;
+      if (a.lse != nullptr && g == 0) {
+        // p = exp2(score * log2(e) - m_run) summed to l, so the natural-log
+        // sum of exp(score) is ln2 * (m_run + log2 l)
+        const int64_t li = ((int64_t)z * Hq + qh[qg]) * Tq + qi[qg];
+        float lse = l > 0.0f ? 0.69314718055994531f * (m_run[qg] + log2f(l)) : kNegInf;
+        if (a.lse_corr != nullptr) lse += a.lse_corr[li];
+        a.lse[li] = lse;
+      }
+    } else {
+      ob = ((q_row0 + qi[qg]) * Hq + qh[qg]) * D + 4 * g;
+    }
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
-      const v4f o = O[qg][c] * inv;
+      v4f o = O[qg][c] * inv;
+      if (DENSE && vmu != nullptr) {
+        const float4 mu = *reinterpret_cast<const float4*>(vmu + 16 * c);
+        o[0] += mu.x;
+        o[1] += mu.y;
+        o[2] += mu.z;
+        o[3] += mu.w;
+      }
       const int64_t oi = ob + 16 * c;
       if (a.out_bf16) {
         uint2 w;

@@ -42,9 +42,16 @@ struct SagePrepArgs {
   const void* q;
   const void* k;
   const void* v;          // only for the V transpose
+  // element strides of (batch, token, head) in q, k and v (channels contiguous):
+  // NHD = (N*H*D, H*D, D), HND = (H*N*D, D, N*D)
+  int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh;
   bool bf16;
   int32_t B, Nq, Nk, Hq, Hkv, D;
   bool smooth_k;
+  bool smooth_v;          // subtract the per-channel V mean (v_mean) in the V blocks
+  float* v_mean;          // [B, Hkv, D] (smooth_v)
+  float* lse_corr;        // [B, Hq, Nq] smooth_k correction of the LSE, or nullptr
+  float corr_scale;       // softmax scale (natural-log units) for lse_corr
   int8_t* q_i8;           // NHD codes
   float* q_scale;         // [B, Hq, ceil(Nq/128)]
   int8_t* k_i8;           // NHD codes (public layout) or nullptr
@@ -106,7 +113,11 @@ struct FlashArgs {
   const int32_t* tables;   // [num_seqs, max_blocks] (paged) or nullptr (dense: identity)
   const int32_t* cu_q;     // [num_seqs+1] (paged) or nullptr (dense: b*Nq)
   const int32_t* ctx_lens; // [num_seqs] (paged) or nullptr (dense: Nk)
-  void* out;               // [rows, Hq, D]
+  void* out;               // [rows, Hq, D] (dense: element (b, i, h, c) at b*o_sb + i*o_st + h*o_sh + c)
+  int64_t o_sb, o_st, o_sh; // dense output strides
+  const float* v_mean;     // dense smooth_v: [B, Hkv, D] added back on rows that see a key, or nullptr
+  float* lse;              // dense: [B, Hq, Nq] natural-log LSE of each row, or nullptr
+  const float* lse_corr;   // dense: [B, Hq, Nq] added to lse (smooth_k correction), or nullptr
   int32_t num_seqs, Hq, Hkv, G, D, max_blocks, max_seqlen_q;
   int32_t Nq, Nk;          // dense only
   float scale_log2;

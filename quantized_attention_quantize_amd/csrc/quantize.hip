@@ -164,16 +164,18 @@ constexpr int kSumChunk = 64;  // tokens per partial column sum
 // accumulated in fp64. Every K value is a multiple of 2^-24 (f16) or of a power
 // of two bounded by its exponent (bf16), and the sums stay far below 2^53 units,
 // so every partial sum is exact and the total does not depend on the order.
+// (b, t, h, c) of k lives at b*sb + t*st + h*sh + c.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, int32_t Nk,
-                                                int32_t HD, double* __restrict__ partial) {
+__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, int32_t Nk, int32_t D,
+                                                int32_t HD, int64_t sb, int64_t st, int64_t sh,
+                                                double* __restrict__ partial) {
   const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
   const int b = blockIdx.z, chunk = blockIdx.y;
   const int c8 = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (c8 >= HD) return;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, Nk);
-  const uint16_t* base = k + ((int64_t)b * Nk) * HD + c8;
+  const uint16_t* base = k + (int64_t)b * sb + (int64_t)(c8 / D) * sh + c8 % D;
   auto add = [&](uint4 w) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -187,11 +189,11 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
   for (; t + 8 <= t1; t += 8) {
     uint4 w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(t + j) * HD);
+    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(t + j) * st);
 #pragma unroll
     for (int j = 0; j < 8; ++j) add(w[j]);
   }
-  for (; t < t1; ++t) add(*reinterpret_cast<const uint4*>(base + (int64_t)t * HD));
+  for (; t < t1; ++t) add(*reinterpret_cast<const uint4*>(base + (int64_t)t * st));
   double* dst = partial + ((int64_t)b * chunks + chunk) * HD + c8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dst[i] = acc[i];
@@ -230,12 +232,19 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
 // Per-block quantization of one (b, head, block) of ROWS tokens x D channels:
 // one scale over all ROWS*D values (after subtracting mu when given).
 // Writes NHD codes (codes_nhd) and/or the blocked K layout (codes_blk).
+// (b, t, h, c) of x lives at b*sb + t*st + h*sh + c. With corr != nullptr
+// (query blocks, smooth_k with an LSE output) it also stores, per row,
+// corr_scale * sum_c x_c * corr_mu[b, h / corr_G, c] (fp32, the D/8 threads
+// of a row reduce their partial sums with shuffles).
 template <int D, int ROWS, bool BF16>
 __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict__ x, int32_t N,
-                                                     int32_t H, const float* __restrict__ mean,
+                                                     int32_t H, int64_t sb, int64_t st, int64_t sh,
+                                                     const float* __restrict__ mean,
                                                      int8_t* __restrict__ codes_nhd,
                                                      int8_t* __restrict__ codes_blk,
-                                                     float* __restrict__ scale) {
+                                                     float* __restrict__ scale,
+                                                     const float* __restrict__ corr_mu, int32_t corr_G,
+                                                     float corr_scale, float* __restrict__ corr) {
   constexpr int G8 = D / 8;                // 8-channel groups per row
   constexpr int PER = ROWS * G8 / 256;     // groups per thread
   static_assert(ROWS * G8 % 256 == 0, "block must tile the workgroup");
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     const int r = gi / G8, c = (gi % G8) * 8;
     const int t = blk * ROWS + r;
     if (t < N) {
-      uint4 w = *reinterpret_cast<const uint4*>(x + (((int64_t)b * N + t) * H + h) * D + c);
+      uint4 w = *reinterpret_cast<const uint4*>(x + (int64_t)b * sb + (int64_t)t * st + (int64_t)h * sh + c);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -269,6 +278,23 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) val[k][i] = 0.0f;
+    }
+  }
+  if (corr != nullptr) {
+    const int Hm = H / corr_G;   // heads of the mean
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int gi = threadIdx.x + 256 * k;
+      const int r = gi / G8, c = (gi % G8) * 8;
+      const int t = blk * ROWS + r;
+      const float* mu = corr_mu + ((int64_t)b * Hm + h / corr_G) * D + c;
+      float dsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dsum = fmaf(val[k][i], mu[i], dsum);
+      // the G8 threads of row r are consecutive lanes of one wave (G8 divides 64)
+#pragma unroll
+      for (int o = 1; o < G8; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
+      if (gi % G8 == 0 && t < N) corr[((int64_t)b * H + h) * N + t] = dsum * corr_scale;
     }
   }
   amax = wave_max(amax);
@@ -308,9 +334,12 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
 // of ch is set (the attention kernel's LDS layout, so its tiles are copied
 // unchanged); padding tokens of the last block are zero. bf16 values become the
 // nearest fp16 (exact in the fp16 normal range).
+// (b, t, h, c) of v lives at b*sb + t*st + h*sh + c. With vmean (smooth_v)
+// each value becomes fl16(fl32(v) - vmean[b, h, c]).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, int32_t N, int32_t H,
-                                                  uint16_t* __restrict__ vb) {
+                                                  int64_t sb, int64_t st, int64_t sh,
+                                                  const float* __restrict__ vmean, uint16_t* __restrict__ vb) {
   constexpr int UPR = D / 8;                 // 16-byte units per token row
   __shared__ __attribute__((aligned(16))) uint16_t tile[16][D + 8];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -319,8 +348,23 @@ __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v
     const int r = u / UPR, c8 = (u % UPR) * 8;
     const int t = blk * 16 + r;
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (t < N) w = *reinterpret_cast<const uint4*>(v + (((int64_t)b * N + t) * H + h) * D + c8);
-    if constexpr (BF16) w = __builtin_bit_cast(uint4, bf16x8_to_f16x8(w));
+    if (t < N) {
+      w = *reinterpret_cast<const uint4*>(v + (int64_t)b * sb + (int64_t)t * st + (int64_t)h * sh + c8);
+      if (vmean != nullptr) {
+        const float* mu = vmean + ((int64_t)b * H + h) * D + c8;
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = half_to_f32<BF16>(ws[i] & 0xFFFFu) - mu[2 * i];
+          const float hi = half_to_f32<BF16>(ws[i] >> 16) - mu[2 * i + 1];
+          o[i] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+        }
+        w = make_uint4(o[0], o[1], o[2], o[3]);
+      } else if constexpr (BF16) {
+        w = __builtin_bit_cast(uint4, bf16x8_to_f16x8(w));
+      }
+    }
     *reinterpret_cast<uint4*>(&tile[r][c8]) = w;
   }
   __syncthreads();
@@ -366,24 +410,33 @@ template <int D, bool BF16>
 hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
   const int HD = a.Hkv * D;
   const int chunks = (a.Nk + kSumChunk - 1) / kSumChunk;
-  if (a.smooth_k && a.Nk > 0) {
-    dim3 g((HD / 8 + 255) / 256, chunks, a.B);
-    k_colsum<BF16><<<g, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, HD, a.partial);
-  }
-  k_mean<<<(unsigned)(((int64_t)a.B * HD + 63) / 64), 256, 0, s>>>(a.partial, a.B, a.Nk, HD, a.smooth_k,
-                                                                      a.k_mean);
+  const dim3 gsum((HD / 8 + 255) / 256, chunks, a.B);
+  const unsigned gmean = (unsigned)(((int64_t)a.B * HD + 63) / 64);
+  if (a.smooth_k && a.Nk > 0)
+    k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, D, HD, a.k_sb, a.k_st, a.k_sh, a.partial);
+  k_mean<<<gmean, 256, 0, s>>>(a.partial, a.B, a.Nk, HD, a.smooth_k, a.k_mean);
   if (a.Nq > 0) {
     dim3 gq((a.Nq + 127) / 128, a.Hq, a.B);
-    k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.Nq, a.Hq, nullptr, a.q_i8,
-                                                   nullptr, a.q_scale);
+    float* corr = a.smooth_k ? a.lse_corr : nullptr;
+    k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.Nq, a.Hq, a.q_sb, a.q_st, a.q_sh,
+                                                   nullptr, a.q_i8, nullptr, a.q_scale, a.k_mean,
+                                                   a.Hq / a.Hkv, a.corr_scale, corr);
   }
   if (a.Nk > 0) {
     dim3 gk((a.Nk + 63) / 64, a.Hkv, a.B);
-    k_block_quant<D, 64, BF16><<<gk, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, a.Hkv, a.k_mean, a.k_i8,
-                                                  a.k_paged, a.k_scale);
+    k_block_quant<D, 64, BF16><<<gk, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, a.Hkv, a.k_sb, a.k_st, a.k_sh,
+                                                  a.k_mean, a.k_i8, a.k_paged, a.k_scale, nullptr, 1, 0.0f,
+                                                  nullptr);
     if (a.v_paged != nullptr) {
+      if (a.smooth_v) {
+        // the column sums of K are consumed: the buffer takes those of V
+        k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, D, HD, a.v_sb, a.v_st, a.v_sh,
+                                            a.partial);
+        k_mean<<<gmean, 256, 0, s>>>(a.partial, a.B, a.Nk, HD, true, a.v_mean);
+      }
       dim3 gv((a.Nk + 15) / 16, a.Hkv, a.B);
-      k_v_blocks<D, BF16><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, a.Hkv, a.v_paged);
+      k_v_blocks<D, BF16><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, a.Hkv, a.v_sb, a.v_st, a.v_sh,
+                                             a.smooth_v ? a.v_mean : nullptr, a.v_paged);
     }
   }
   return hipGetLastError();

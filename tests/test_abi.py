@@ -176,6 +176,28 @@ def test_prefill_and_dense_validation(qa):
         qa.QA_ERR_UNSUPPORTED
 
 
+def test_dense_options_validation(qa):
+    L = qa.lib
+    d = qa.DenseParams(2, 100, 90, 8, 4, 128, qa.QA_DT_BF16, 1, 0, 0.0, qa.QA_DT_F32)
+    o = qa.DenseOptions(qa.QA_LAYOUT_HND, 1)
+    plain = L.qa_dense_sage_workspace_size(ctypes.byref(d))
+    need = L.qa_dense_sage_ex_workspace_size(ctypes.byref(d), ctypes.byref(o))
+    # the options call adds the V mean (2 x 4 x 128 fp32) and the LSE correction (2 x 8 x 100 fp32)
+    assert need == plain + 4096 + 6400
+    assert L.qa_dense_sage_ex_workspace_size(ctypes.byref(d), None) == need
+    ex = lambda opts, ws_bytes, lse: L.qa_dense_sage_attention_ex(
+        ctypes.byref(d), opts, FAKE, FAKE, FAKE, FAKE, ws_bytes, FAKE, lse, None)
+    assert ex(ctypes.byref(o), need - 1, FAKE) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert ex(None, plain, None) == qa.QA_ERR_WORKSPACE_TOO_SMALL      # the plain call's size is not enough
+    assert ex(ctypes.byref(o), need, ctypes.c_void_p(0x10002)) == qa.QA_ERR_INVALID_ARG  # lse not 4-byte aligned
+    assert b"lse" in L.qa_last_error()
+    o.layout = 7
+    assert ex(ctypes.byref(o), need, None) == qa.QA_ERR_INVALID_ARG
+    assert b"layout 7" in L.qa_last_error()
+    assert L.qa_dense_sage_attention_ex(ctypes.byref(d), ctypes.byref(o), FAKE, None, FAKE, FAKE, need, FAKE,
+                                        None, None) == qa.QA_ERR_INVALID_ARG
+
+
 def test_last_error_is_thread_local(qa):
     import threading
     L = qa.lib

@@ -395,6 +395,79 @@ def test_dense_full_size_sampled(qa, causal):
             assert_close(g[b, rows, h], want[b, rows, h], f"dense b={b} h={h}")
 
 
+# the dense call with its options: HND layout, smooth_v, LSE output
+DENSE_EX = [
+    # (B, Nq, Nk, Hq, Hkv, d, dtype, causal)
+    (1, 200, 200, 2, 2, 64, "f16", False),
+    (2, 300, 257, 4, 2, 128, "bf16", True),      # causal with Nq > Nk: 43 rows see no key
+    (1, 129, 400, 6, 1, 256, "f16", True),
+    (2, 77, 150, 4, 4, 128, "f16", False),
+]
+
+
+def _lse_close(got, want, what):
+    dead = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), dead), f"{what}: rows without keys differ"
+    err = np.abs(got[~dead] - want[~dead])
+    assert err.size == 0 or err.max() <= 1e-3 * max(1.0, np.abs(want[~dead]).max()), \
+        f"{what}: LSE error {err.max():.3g}"
+
+
+@pytest.mark.parametrize("smooth_k", [True, False])
+@pytest.mark.parametrize("smooth_v", [True, False])
+@pytest.mark.parametrize("case", DENSE_EX, ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{c[6]}_{'causal' if c[7] else 'full'}")
+def test_dense_options_parity(qa, case, smooth_v, smooth_k):
+    """Output and LSE of the options call against the oracle's whole dense
+    forward, in both layouts; the HND result must be the NHD one transposed,
+    bit for bit (same arithmetic, other strides)."""
+    B, Nq, Nk, Hq, Hkv, d, dt, causal = case
+    say(f"dense options {case} smooth_v={smooth_v} smooth_k={smooth_k}")
+    spec = DenseSpec("dn_ex", 509 + d, B, Hq, Hkv, Nq, Nk, d, k_bias_std=3.0, dtype=dt, v_bias_std=2.0)
+    inp = dense_inputs(spec)
+    q, k, v = dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt)
+    out_n, lse_n = qa.dense_sage_attention_ex(q, k, v, "NHD", is_causal=causal, smooth_k=smooth_k,
+                                              smooth_v=smooth_v, return_lse=True)
+    hnd = lambda t: t.transpose(1, 2).contiguous()
+    out_h, lse_h = qa.dense_sage_attention_ex(hnd(q), hnd(k), hnd(v), "HND", is_causal=causal,
+                                              smooth_k=smooth_k, smooth_v=smooth_v, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_h.transpose(1, 2), out_n), "HND output differs from NHD"
+    assert torch.equal(lse_h, lse_n), "HND LSE differs from NHD"
+    want, want_lse = oracle.sage_forward(inp.q, inp.k, inp.v, dt, causal=causal, smooth_k=smooth_k,
+                                         smooth_v=smooth_v, return_lse=True)
+    assert_close(out_n.cpu().numpy(), want, "dense options")
+    _lse_close(lse_n.cpu().numpy(), want_lse, "dense options LSE")
+    if not smooth_v:   # the plain call is the options call without options
+        plain = qa.dense_sage_attention(q, k, v, is_causal=causal, smooth_k=smooth_k)
+        assert torch.equal(plain, out_n)
+
+
+def test_dense_options_full_size_sampled(qa):
+    """The dense workload (2 x 8192 x 32 heads, d 128) through the options
+    call in HND with smooth_v and the LSE, sampled rows and heads against the
+    oracle's steps (quantize, smooth V, attend, add the mean back, correct
+    the LSE)."""
+    spec = dense_sage()
+    say(f"dense options full size {spec.name}")
+    inp = dense_inputs(spec)
+    hnd = lambda bits: dev_bits(np.ascontiguousarray(bits.transpose(0, 2, 1, 3)), "f16")
+    out, lse = qa.dense_sage_attention_ex(hnd(inp.q), hnd(inp.k), hnd(inp.v), "HND", is_causal=True,
+                                          smooth_v=True, return_lse=True)
+    torch.cuda.synchronize()
+    quant = oracle.sage_quantize(inp.q, inp.k, "f16")
+    vb, mu = oracle.sage_smooth_v(inp.v, "f16")
+    rows, heads = np.array([0, 1, 127, 128, 4095, 8191]), [0, 17, 31]
+    want, want_lse = oracle.dense_sage_attention(quant, vb, "f16", causal=True, rows=rows, heads=heads,
+                                                 return_lse=True)
+    corr = oracle.sage_lse_correction(inp.q, quant["k_mean"], "f16")
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(2):
+        for h in heads:
+            assert_close(o[b, h, rows], want[b, rows, h] + mu[b, h // (spec.num_q_heads // spec.num_kv_heads)],
+                         f"dense options b={b} h={h}")
+            _lse_close(l[b, h, rows], want_lse[b, h, rows] + corr[b, h, rows], f"dense options LSE b={b} h={h}")
+
+
 def test_decode_workspace_reuse_across_calls(qa):
     # one workspace serves calls with different split counts; partials left
     # by earlier calls must not leak into later results

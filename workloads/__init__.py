@@ -185,6 +185,7 @@ class DenseSpec:
     k_bias_std: float = 0.0
     dtype: str = "f16"
     layout: str = "NHD"
+    v_bias_std: float = 0.0   # per-(KV head, channel) offset of V, drawn from its own stream
 
 
 @dataclass
@@ -196,10 +197,12 @@ class DenseInputs:
 
 
 def dense_inputs(spec: DenseSpec) -> DenseInputs:
-    """Q, V ~ N(0,1); K ~ N(0,1) + bias[head, channel], bias ~ N(0, k_bias_std).
-    Stored NHD (batch, seq, head, dim)."""
+    """Q ~ N(0,1); K ~ N(0,1) + bias[head, channel], bias ~ N(0, k_bias_std);
+    V ~ N(0,1) (+ a per-(head, channel) offset ~ N(0, v_bias_std) when that is
+    set). Stored NHD (batch, seq, head, dim)."""
     B, Hq, Hkv, d = spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     bias = _rng(spec.seed, 1).standard_normal((Hkv, d), dtype=np.float32) * np.float32(spec.k_bias_std)
+    vbias = _rng(spec.seed, 3).standard_normal((Hkv, d), dtype=np.float32) * np.float32(spec.v_bias_std)
     q = np.empty((B, spec.seq_q, Hq, d), np.uint16)
     k = np.empty((B, spec.seq_k, Hkv, d), np.uint16)
     v = np.empty((B, spec.seq_k, Hkv, d), np.uint16)
@@ -207,7 +210,8 @@ def dense_inputs(spec: DenseSpec) -> DenseInputs:
         g = _rng(spec.seed, 2, b)
         q[b] = _store(g.standard_normal((spec.seq_q, Hq, d), dtype=np.float32), spec.dtype)
         k[b] = _store(g.standard_normal((spec.seq_k, Hkv, d), dtype=np.float32) + bias[None], spec.dtype)
-        v[b] = _store(g.standard_normal((spec.seq_k, Hkv, d), dtype=np.float32), spec.dtype)
+        vx = g.standard_normal((spec.seq_k, Hkv, d), dtype=np.float32)
+        v[b] = _store(vx + vbias[None] if spec.v_bias_std else vx, spec.dtype)
     return DenseInputs(spec, q, k, v)
 
 
