@@ -21,6 +21,7 @@ paths on their own workloads.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -314,15 +315,27 @@ def run_prefill(torch, qa, reps):
             "_ops": (qk, pv)}
 
 
-def run_dense(torch, qa, reps, causal):
+def run_dense(torch, qa, reps, causal, options=False):
+    """The dense workload; with options, through the options call in the HND
+    layout with smooth_v and the LSE output."""
     from workloads import dense_sage, dense_inputs
     spec = dense_sage()
     inp = dense_inputs(spec)
     q, k, v = (dev_bits(torch, x, "f16") for x in (inp.q, inp.k, inp.v))
     p = qa.dense_params(q, k, True, causal)
-    ws = qa.dense_sage_workspace(p)
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    f = lambda: qa.dense_sage_attention(q, k, v, is_causal=causal, workspace=ws, out=out)
+    if options:
+        q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+        o = qa.DenseOptions(qa.QA_LAYOUT_HND, 1)
+        ws = torch.empty(qa.lib.qa_dense_sage_ex_workspace_size(ctypes.byref(p), ctypes.byref(o)),
+                         dtype=torch.uint8, device="cuda")
+        out = out.transpose(1, 2).contiguous()
+        lse = torch.empty((spec.batch, spec.num_q_heads, spec.seq_q), dtype=torch.float32, device="cuda")
+        f = lambda: qa.dense_sage_attention_ex(q, k, v, "HND", is_causal=causal, smooth_v=True, return_lse=True,
+                                               workspace=ws, out=out, lse=lse)
+    else:
+        ws = qa.dense_sage_workspace(p)
+        f = lambda: qa.dense_sage_attention(q, k, v, is_causal=causal, workspace=ws, out=out)
     for _ in range(3):
         f()
     evs = _mk_stream_events(torch, reps)
@@ -335,7 +348,8 @@ def run_dense(torch, qa, reps, causal):
     tops = (qk + pv) / (ms * 1e-3) / 1e12
     mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
     return {"workload": f"dense_sage B2 H32 N8192 d128 {'causal' if causal else 'non-causal'} "
-                        "(full chain: smooth_k + per-block quantization + attention)",
+                        "(full chain: smooth_k + per-block quantization + attention"
+                        + (", HND, smooth_v, LSE output)" if options else ")"),
             "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
             "_ops": (qk, pv)}
 
@@ -468,7 +482,8 @@ def main():
         res["extra"] = {"decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
                         "chunked_prefill": run_prefill(torch, qa, 20),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
-                        "dense_sage_causal": run_dense(torch, qa, 10, True)}
+                        "dense_sage_causal": run_dense(torch, qa, 10, True),
+                        "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True)}
         for e in res["extra"].values():
             if "_ops" not in e:
                 continue
