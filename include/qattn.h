@@ -424,6 +424,53 @@ qa_status_t qa_dense_sage_attention_ex(const qa_dense_params_t* p, const qa_dens
                                        size_t workspace_bytes, void* out, float* lse,
                                        qa_stream_t stream);
 
+/*
+ * Variable-length dense forward ([SAGE-MACA] API sageattn_varlen, packed
+ * format): B independent sequences whose rows are packed one after another,
+ * each attended exactly as one sequence of qa_dense_sage_attention_ex would
+ * be — smooth_k and smooth_v means per sequence, Q blocks of 128 and K blocks
+ * of 64 rows counted from each sequence's first row, causal alignment
+ * bottom-right within each sequence — but in one batched launch per pass
+ * instead of a loop over sequences (the pages' implementation loops on the
+ * host and launches once per sequence).
+ *
+ *   q     [total_q, num_q_heads, head_dim], k and v [total_k, num_kv_heads, head_dim]
+ *         (bf16/f16 dtype, contiguous); sequence b is rows cu_seqlens_q[b] ..
+ *         cu_seqlens_q[b+1]-1 of q and cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *         of k and v
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [batch+1]: nondecreasing, from 0
+ *         to total_q / total_k, no sequence longer than max_seqlen_q /
+ *         max_seqlen_k (device data: not checked; rows past max_seqlen are not
+ *         computed)
+ *   out   [total_q, num_q_heads, head_dim] in out_dtype
+ *   lse   NULL or [num_q_heads, total_q] fp32 (natural log, smooth_k
+ *         corrected as in qa_dense_sage_attention_ex; -inf for rows that see
+ *         no key)
+ *   workspace >= qa_dense_sage_varlen_workspace_size bytes (grows with
+ *         total_q, total_k, batch and max_seqlen_k)
+ * A sequence with no query rows writes nothing; one with queries but no
+ * keys gets zero rows. Errors: QA_ERR_INVALID_ARG (null or misaligned
+ * pointers, negative sizes), QA_ERR_UNSUPPORTED (dtype, head_dim, GQA ratio,
+ * batch or sizes beyond int32 indexing), QA_ERR_WORKSPACE_TOO_SMALL.
+ */
+typedef struct {
+  int32_t batch;
+  int64_t total_q, total_k;
+  int32_t max_seqlen_q, max_seqlen_k;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  qa_dtype_t dtype;            /* QA_DT_F16 or QA_DT_BF16 */
+  int32_t smooth_k, smooth_v, is_causal;
+  float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
+  qa_dtype_t out_dtype;        /* QA_DT_F32, QA_DT_F16 or QA_DT_BF16 */
+} qa_varlen_params_t;
+
+size_t qa_dense_sage_varlen_workspace_size(const qa_varlen_params_t* p);
+qa_status_t qa_dense_sage_attention_varlen(const qa_varlen_params_t* p, const void* q, const void* k,
+                                           const void* v, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, void* workspace,
+                                           size_t workspace_bytes, void* out, float* lse,
+                                           qa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

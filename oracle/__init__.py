@@ -34,16 +34,19 @@ Parity status, function by function (pins live in tests/test_oracle_pins.py):
   (closed forms: LSE of equal scores is ln(#visible); constant keys make the
   corrected LSE q.c*scale + ln(#visible); the V mean added back reproduces
   the unsmoothed output within the fp16 rounding of V').
+* sage_varlen_forward: pinned (equal lengths reproduce the batched forward;
+  a sequence's rows do not depend on its neighbours; empty sequences).
 """
 from .quant import (widen, quant_rows, quantize_q, write_kv_cache, sage_quantize,
                     gather_kv)
 from .attention import (paged_qk_int32, paged_decode, paged_decode_split,
                         chunked_prefill, dense_sage_attention, attention_fp64,
-                        default_scale, sage_smooth_v, sage_lse_correction, sage_forward)
+                        default_scale, sage_smooth_v, sage_lse_correction, sage_forward,
+                        sage_varlen_forward)
 
 __all__ = [
     "widen", "quant_rows", "quantize_q", "write_kv_cache", "sage_quantize", "gather_kv",
     "paged_qk_int32", "paged_decode", "paged_decode_split", "chunked_prefill",
     "dense_sage_attention", "attention_fp64", "default_scale",
-    "sage_smooth_v", "sage_lse_correction", "sage_forward",
+    "sage_smooth_v", "sage_lse_correction", "sage_forward", "sage_varlen_forward",
 ]

@@ -314,6 +314,35 @@ def sage_forward(q_bits, k_bits, v_bits, dtype="f16", causal=False, smooth_k=Tru
     return (out, lse) if return_lse else out
 
 
+def sage_varlen_forward(q_bits, k_bits, v_bits, cu_seqlens_q, cu_seqlens_k, dtype="f16", causal=False,
+                        smooth_k=True, smooth_v=False, return_lse=False, scale=None):
+    """Variable-length dense forward on packed rows ([SAGE-MACA] API
+    sageattn_varlen; its implementation section: every batch element is
+    sliced out and attended on its own). q [total_q, Hq, d], k and v
+    [total_k, Hkv, d]; sequence b is rows cu_q[b]:cu_q[b+1] of q and
+    cu_k[b]:cu_k[b+1] of k and v, attended exactly as a one-sequence
+    ``sage_forward`` (its own smoothing means, its own 128/64-row quantization
+    blocks, causal alignment within the sequence). Returns out fp64
+    [total_q, Hq, d] (and lse fp64 [Hq, total_q])."""
+    q = np.asarray(q_bits)
+    k = np.asarray(k_bits)
+    v = np.asarray(v_bits)
+    cq = np.asarray(cu_seqlens_q, np.int64)
+    ck = np.asarray(cu_seqlens_k, np.int64)
+    Tq, Hq, d = q.shape
+    out = np.zeros((Tq, Hq, d), np.float64)
+    lse = np.full((Hq, Tq), -np.inf)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 == q0:
+            continue
+        o, l = sage_forward(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype, causal=causal,
+                            smooth_k=smooth_k, smooth_v=smooth_v, return_lse=True, scale=scale)
+        out[q0:q1] = o[0]
+        lse[:, q0:q1] = l[0]
+    return (out, lse) if return_lse else out
+
+
 def attention_fp64(q, k, v, scale, visible=None):
     """Textbook softmax(q k^T * scale) v in fp64 for [N, d] operands, with an
     optional boolean visibility mask [Nq, Nk]. Used for pins and for the

@@ -54,6 +54,13 @@ class DenseParams(ctypes.Structure):
                 ("is_causal", _i32), ("softmax_scale", _f32), ("out_dtype", ctypes.c_int)]
 
 
+class VarlenParams(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("total_q", _i64), ("total_k", _i64), ("max_seqlen_q", _i32),
+                ("max_seqlen_k", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
+                ("dtype", ctypes.c_int), ("smooth_k", _i32), ("smooth_v", _i32), ("is_causal", _i32),
+                ("softmax_scale", _f32), ("out_dtype", ctypes.c_int)]
+
+
 class DenseOptions(ctypes.Structure):
     _fields_ = [("layout", _i32), ("smooth_v", _i32)]
 
@@ -99,6 +106,9 @@ _SIGS = {
     "qa_dense_sage_ex_workspace_size": (_size, [_P(DenseParams), _P(DenseOptions)]),
     "qa_dense_sage_attention_ex": (ctypes.c_int, [_P(DenseParams), _P(DenseOptions)] + [_c_void_p] * 4 +
                                    [_size, _c_void_p, _c_void_p, _c_void_p]),
+    "qa_dense_sage_varlen_workspace_size": (_size, [_P(VarlenParams)]),
+    "qa_dense_sage_attention_varlen": (ctypes.c_int, [_P(VarlenParams)] + [_c_void_p] * 6 +
+                                       [_size, _c_void_p, _c_void_p, _c_void_p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     try:
@@ -415,4 +425,41 @@ def dense_sage_attention_ex(q, k, v, tensor_layout="NHD", is_causal=False, smoot
     _check(lib.qa_dense_sage_attention_ex(ctypes.byref(p), ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(workspace), workspace.numel(), _ptr(out),
                                           _ptr(lse) if return_lse else None, _stream()))
+    return (out, lse) if return_lse else out
+
+
+def varlen_params(q, k, max_seqlen_q, max_seqlen_k, batch, is_causal=False, smooth_k=True, smooth_v=False,
+                  softmax_scale=0.0, out_dtype=torch.float32) -> VarlenParams:
+    return VarlenParams(batch, q.shape[0], k.shape[0], max_seqlen_q, max_seqlen_k, q.shape[1], k.shape[1],
+                        q.shape[2], _dt(q.dtype), int(bool(smooth_k)), int(bool(smooth_v)), int(bool(is_causal)),
+                        softmax_scale, _dt(out_dtype))
+
+
+def dense_sage_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False,
+                                smooth_k=True, smooth_v=False, return_lse=False, softmax_scale=0.0,
+                                out_dtype=torch.float32, workspace=None, out=None, lse=None):
+    """Packed variable-length dense forward: q [total_q, Hq, d], k and v
+    [total_k, Hkv, d]; cu_seqlens_q/k int32 [B+1] on the GPU. Returns out
+    [total_q, Hq, d], or (out, lse [Hq, total_q]) with return_lse."""
+    _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k and v must be contiguous")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    batch = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    p = varlen_params(q, k, max_seqlen_q, max_seqlen_k, batch, is_causal, smooth_k, smooth_v, softmax_scale,
+                      out_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(lib.qa_dense_sage_varlen_workspace_size(ctypes.byref(p)), 16),
+                                dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    _check(lib.qa_dense_sage_attention_varlen(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                              _ptr(cu_seqlens_k), _ptr(workspace), workspace.numel(), _ptr(out),
+                                              _ptr(lse) if return_lse else None, _stream()))
     return (out, lse) if return_lse else out

@@ -115,37 +115,6 @@ qa_status_t check_dense(const qa_dense_params_t* p) {
   return QA_OK;
 }
 
-// Dense workspace: [partial sums][q_i8][k blocks][v blocks][q_scale][k_scale][k_mean], 256-aligned.
-// The options call appends [v_mean][lse_corr].
-struct DenseWs {
-  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, total;
-};
-
-size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
-
-DenseWs dense_layout(const qa_dense_params_t* p, bool with_attention, bool ex = false) {
-  DenseWs w{};
-  const size_t B = p->batch, Nq = p->seq_q, Nk = p->seq_k, Hq = p->num_q_heads, Hkv = p->num_kv_heads,
-               D = p->head_dim;
-  const size_t nb16 = (Nk + 15) / 16;
-  size_t off = 0;
-  w.partial = off; off += al(qa::sage_partial_bytes(p->batch, p->seq_k, p->num_kv_heads, p->head_dim));
-  if (with_attention) {
-    w.q_i8 = off; off += al(B * Nq * Hq * D);
-    w.k_blk = off; off += al(B * nb16 * Hkv * D * 16);
-    w.v_blk = off; off += al(B * nb16 * Hkv * D * 16 * 2);
-    w.q_scale = off; off += al(B * Hq * ((Nq + 127) / 128) * sizeof(float));
-    w.k_scale = off; off += al(B * Hkv * ((Nk + 63) / 64) * sizeof(float));
-    w.k_mean = off; off += al(B * Hkv * D * sizeof(float));
-    if (ex) {
-      w.v_mean = off; off += al(B * Hkv * D * sizeof(float));
-      w.lse_corr = off; off += al(B * Hq * Nq * sizeof(float));
-    }
-  }
-  w.total = off;
-  return w;
-}
-
 // Element strides (batch, token, head) of a [batch, N, H, D] (NHD) or
 // [batch, H, N, D] (HND) tensor.
 struct Strides {
@@ -156,13 +125,101 @@ Strides layout_strides(int32_t layout, int64_t N, int64_t H, int64_t D) {
   return {N * H * D, H * D, D};
 }
 
+// One validated dense call, batched or varlen (packed rows).
+struct DenseCall {
+  qa::Rows q, k;               // sequence geometry; N = length (batched) or the longest (varlen)
+  int32_t Hq, Hkv, D;
+  bool bf16, smooth_k, smooth_v, causal;
+  float softmax_scale;
+  qa_dtype_t out_dtype;
+  Strides sq, sk, so;          // q, k/v, out
+  int64_t q_rows() const { return q.packed ? q.total : (int64_t)q.B * q.N; }
+};
+
+DenseCall dense_call(const qa_dense_params_t* p, int32_t layout, bool smooth_v) {
+  DenseCall c{};
+  c.q = qa::Rows{nullptr, p->batch, p->seq_q, 0, false};
+  c.k = qa::Rows{nullptr, p->batch, p->seq_k, 0, false};
+  c.Hq = p->num_q_heads; c.Hkv = p->num_kv_heads; c.D = p->head_dim;
+  c.bf16 = p->dtype == QA_DT_BF16; c.smooth_k = p->smooth_k != 0; c.smooth_v = smooth_v;
+  c.causal = p->is_causal != 0; c.softmax_scale = p->softmax_scale; c.out_dtype = p->out_dtype;
+  c.sq = layout_strides(layout, p->seq_q, p->num_q_heads, p->head_dim);
+  c.sk = layout_strides(layout, p->seq_k, p->num_kv_heads, p->head_dim);
+  c.so = c.sq;
+  return c;
+}
+
+// Dense workspace: [partial sums][q_i8][k blocks][v blocks][q_scale][k_scale][k_mean], 256-aligned.
+// The options and varlen calls append [v_mean][lse_corr].
+struct DenseWs {
+  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, total;
+};
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DenseWs dense_layout(const DenseCall& c, bool with_attention, bool ex) {
+  DenseWs w{};
+  const size_t B = c.q.B, Hq = c.Hq, Hkv = c.Hkv, D = c.D, rows_q = c.q_rows();
+  const size_t nb16 = c.k.nblocks(16);
+  size_t off = 0;
+  w.partial = off; off += al(qa::sage_partial_bytes(c.k.B, c.k.N, c.Hkv, c.D));
+  if (with_attention) {
+    w.q_i8 = off; off += al(rows_q * Hq * D);
+    w.k_blk = off; off += al(nb16 * Hkv * D * 16);
+    w.v_blk = off; off += al(nb16 * Hkv * D * 16 * 2);
+    w.q_scale = off; off += al(Hq * c.q.nblocks(128) * sizeof(float));
+    w.k_scale = off; off += al(Hkv * c.k.nblocks(64) * sizeof(float));
+    w.k_mean = off; off += al(B * Hkv * D * sizeof(float));
+    if (ex) {
+      w.v_mean = off; off += al(B * Hkv * D * sizeof(float));
+      w.lse_corr = off; off += al(Hq * rows_q * sizeof(float));
+    }
+  }
+  w.total = off;
+  return w;
+}
+
+// Preprocessing (smooth_k, per-block quantization, V blocks) then attention.
+// Pointers, alignment and the workspace size are checked by the caller.
+qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const void* v, char* ws,
+                      const DenseWs& w, void* out, float* lse, qa_stream_t stream) {
+  qa::SagePrepArgs pa{};
+  pa.q = q; pa.k = k; pa.v = v; pa.bf16 = c.bf16;
+  pa.q_sb = c.sq.b; pa.q_st = c.sq.t; pa.q_sh = c.sq.h;
+  pa.k_sb = c.sk.b; pa.k_st = c.sk.t; pa.k_sh = c.sk.h;
+  pa.v_sb = c.sk.b; pa.v_st = c.sk.t; pa.v_sh = c.sk.h;
+  pa.q_rows = c.q; pa.k_rows = c.k;
+  pa.B = c.q.B; pa.Nq = c.q.N; pa.Nk = c.k.N; pa.Hq = c.Hq; pa.Hkv = c.Hkv; pa.D = c.D;
+  pa.smooth_k = c.smooth_k;
+  pa.smooth_v = c.smooth_v && c.k.N > 0;
+  pa.v_mean = pa.smooth_v ? (float*)(ws + w.v_mean) : nullptr;
+  pa.lse_corr = lse != nullptr && pa.smooth_k ? (float*)(ws + w.lse_corr) : nullptr;
+  pa.corr_scale = natural_scale(c.softmax_scale, c.D);
+  pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
+  pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
+  pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
+  qa_status_t st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
+  if (st != QA_OK) return st;
+  qa::FlashArgs a{};
+  a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
+  a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
+  a.o_sb = c.so.b; a.o_st = c.so.t; a.o_sh = c.so.h;
+  a.v_mean = pa.v_mean; a.lse = lse; a.lse_corr = pa.lse_corr;
+  a.q_rows = c.q; a.k_rows = c.k;
+  a.num_seqs = c.q.B; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv;
+  a.D = c.D; a.max_blocks = 0; a.max_seqlen_q = c.q.N; a.Nq = c.q.N; a.Nk = c.k.N;
+  a.scale_log2 = log2_scale(c.softmax_scale, c.D);
+  a.dense = true; a.causal = c.causal; a.v_int8 = false; a.v_f16 = true;  // V blocks are fp16
+  a.out_bf16 = c.out_dtype == QA_DT_BF16; a.out_f16 = c.out_dtype == QA_DT_F16;
+  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "dense attention launch");
+}
+
 qa_status_t dense_attention_impl(const qa_dense_params_t* p, const qa_dense_options_t* o, const void* q,
                                  const void* k, const void* v, void* workspace, size_t workspace_bytes,
                                  void* out, float* lse, qa_stream_t stream, bool ex) {
   qa_status_t st = check_dense(p);
   if (st != QA_OK) return st;
   const int32_t layout = o ? o->layout : QA_LAYOUT_NHD;
-  const bool smooth_v = o && o->smooth_v != 0;
   QA_REQUIRE(layout == QA_LAYOUT_NHD || layout == QA_LAYOUT_HND, QA_ERR_INVALID_ARG, "unknown layout %d",
              layout);
   if (p->batch == 0 || p->seq_q == 0) return QA_OK;
@@ -170,41 +227,42 @@ qa_status_t dense_attention_impl(const qa_dense_params_t* p, const qa_dense_opti
   QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(workspace),
              QA_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
   QA_REQUIRE(((uintptr_t)lse & 3u) == 0, QA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const DenseWs w = dense_layout(p, true, ex);
+  const DenseCall c = dense_call(p, layout, o && o->smooth_v != 0);
+  const DenseWs w = dense_layout(c, true, ex);
   QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
              workspace_bytes, w.total);
+  return run_dense(c, q, k, v, (char*)workspace, w, out, lse, stream);
+}
+
+qa_status_t check_varlen(const qa_varlen_params_t* p) {
+  QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
+  QA_REQUIRE(p->batch >= 0 && p->total_q >= 0 && p->total_k >= 0 && p->max_seqlen_q >= 0 &&
+                 p->max_seqlen_k >= 0 && p->num_q_heads > 0 && p->num_kv_heads > 0 && p->head_dim > 0,
+             QA_ERR_INVALID_ARG, "bad varlen shape");
+  QA_REQUIRE(p->num_q_heads % p->num_kv_heads == 0, QA_ERR_INVALID_ARG,
+             "num_q_heads (%d) not a multiple of num_kv_heads (%d)", p->num_q_heads, p->num_kv_heads);
+  QA_REQUIRE(p->dtype == QA_DT_F16 || p->dtype == QA_DT_BF16, QA_ERR_UNSUPPORTED, "dtype must be F16 or BF16");
+  QA_REQUIRE(p->out_dtype == QA_DT_F32 || p->out_dtype == QA_DT_F16 || p->out_dtype == QA_DT_BF16,
+             QA_ERR_UNSUPPORTED, "out_dtype must be F32, F16 or BF16");
+  QA_REQUIRE(supported_dim(p->head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", p->head_dim);
+  QA_REQUIRE(p->batch <= 65535 && p->num_q_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
+  QA_REQUIRE(p->total_q <= INT32_MAX && p->total_k <= INT32_MAX, QA_ERR_UNSUPPORTED,
+             "total rows beyond int32 offsets");
+  return QA_OK;
+}
+
+DenseCall varlen_call(const qa_varlen_params_t* p, const int32_t* cu_q, const int32_t* cu_k) {
+  DenseCall c{};
+  c.q = qa::Rows{cu_q, p->batch, p->max_seqlen_q, p->total_q, true};
+  c.k = qa::Rows{cu_k, p->batch, p->max_seqlen_k, p->total_k, true};
+  c.Hq = p->num_q_heads; c.Hkv = p->num_kv_heads; c.D = p->head_dim;
+  c.bf16 = p->dtype == QA_DT_BF16; c.smooth_k = p->smooth_k != 0; c.smooth_v = p->smooth_v != 0;
+  c.causal = p->is_causal != 0; c.softmax_scale = p->softmax_scale; c.out_dtype = p->out_dtype;
   const int64_t D = p->head_dim;
-  const Strides sq = layout_strides(layout, p->seq_q, p->num_q_heads, D);
-  const Strides sk = layout_strides(layout, p->seq_k, p->num_kv_heads, D);
-  char* ws = (char*)workspace;
-  qa::SagePrepArgs pa{};
-  pa.q = q; pa.k = k; pa.v = v; pa.bf16 = p->dtype == QA_DT_BF16;
-  pa.q_sb = sq.b; pa.q_st = sq.t; pa.q_sh = sq.h;
-  pa.k_sb = sk.b; pa.k_st = sk.t; pa.k_sh = sk.h;
-  pa.v_sb = sk.b; pa.v_st = sk.t; pa.v_sh = sk.h;
-  pa.B = p->batch; pa.Nq = p->seq_q; pa.Nk = p->seq_k; pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads;
-  pa.D = p->head_dim; pa.smooth_k = p->smooth_k != 0;
-  pa.smooth_v = smooth_v && p->seq_k > 0;
-  pa.v_mean = pa.smooth_v ? (float*)(ws + w.v_mean) : nullptr;
-  pa.lse_corr = lse != nullptr && pa.smooth_k ? (float*)(ws + w.lse_corr) : nullptr;
-  pa.corr_scale = natural_scale(p->softmax_scale, p->head_dim);
-  pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
-  pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
-  pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
-  st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
-  if (st != QA_OK) return st;
-  const Strides so = layout_strides(layout, p->seq_q, p->num_q_heads, D);
-  qa::FlashArgs a{};
-  a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
-  a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
-  a.o_sb = so.b; a.o_st = so.t; a.o_sh = so.h;
-  a.v_mean = pa.v_mean; a.lse = lse; a.lse_corr = pa.lse_corr;
-  a.num_seqs = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
-  a.D = p->head_dim; a.max_blocks = 0; a.max_seqlen_q = p->seq_q; a.Nq = p->seq_q; a.Nk = p->seq_k;
-  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
-  a.dense = true; a.causal = p->is_causal != 0; a.v_int8 = false; a.v_f16 = true;  // V blocks are fp16
-  a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = p->out_dtype == QA_DT_F16;
-  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "dense attention launch");
+  c.sq = Strides{0, p->num_q_heads * D, D};     // packed [total, H, D] rows
+  c.sk = Strides{0, p->num_kv_heads * D, D};
+  c.so = c.sq;
+  return c;
 }
 
 }  // namespace
@@ -527,7 +585,7 @@ qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int
 
 size_t qa_dense_sage_quantize_workspace_size(const qa_dense_params_t* p) {
   if (check_dense(p) != QA_OK) return 0;
-  return dense_layout(p, false).total;
+  return dense_layout(dense_call(p, QA_LAYOUT_NHD, false), false, false).total;
 }
 
 qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, const void* k, int8_t* q_i8,
@@ -541,17 +599,17 @@ qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, co
   QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(workspace) && ((uintptr_t)q_i8 & 7u) == 0 &&
                  ((uintptr_t)k_i8 & 7u) == 0,
              QA_ERR_INVALID_ARG, "q, k, workspace must be 16-byte aligned and codes 8-byte aligned");
-  const DenseWs w = dense_layout(p, false);
+  const DenseCall c = dense_call(p, QA_LAYOUT_NHD, false);
+  const DenseWs w = dense_layout(c, false, false);
   QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
              workspace_bytes, w.total);
   qa::SagePrepArgs a{};
+  a.q_rows = c.q; a.k_rows = c.k;
   a.q = q; a.k = k; a.v = nullptr; a.bf16 = p->dtype == QA_DT_BF16;
   a.B = p->batch; a.Nq = p->seq_q; a.Nk = p->seq_k; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
   a.D = p->head_dim; a.smooth_k = p->smooth_k != 0;
-  const Strides sq = layout_strides(QA_LAYOUT_NHD, p->seq_q, p->num_q_heads, p->head_dim);
-  const Strides sk = layout_strides(QA_LAYOUT_NHD, p->seq_k, p->num_kv_heads, p->head_dim);
-  a.q_sb = sq.b; a.q_st = sq.t; a.q_sh = sq.h;
-  a.k_sb = sk.b; a.k_st = sk.t; a.k_sh = sk.h;
+  a.q_sb = c.sq.b; a.q_st = c.sq.t; a.q_sh = c.sq.h;
+  a.k_sb = c.sk.b; a.k_st = c.sk.t; a.k_sh = c.sk.h;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_paged = nullptr; a.k_scale = k_scale;
   a.k_mean = k_mean; a.partial = (double*)((char*)workspace + w.partial); a.v_paged = nullptr;
   return hip_status(qa::launch_sage_prep(a, (hipStream_t)stream), "qa_dense_sage_quantize launch");
@@ -559,7 +617,7 @@ qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, co
 
 size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p) {
   if (check_dense(p) != QA_OK) return 0;
-  return dense_layout(p, true).total;
+  return dense_layout(dense_call(p, QA_LAYOUT_NHD, false), true, false).total;
 }
 
 qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, const void* k, const void* v,
@@ -570,13 +628,40 @@ qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, c
 size_t qa_dense_sage_ex_workspace_size(const qa_dense_params_t* p, const qa_dense_options_t* options) {
   (void)options;
   if (check_dense(p) != QA_OK) return 0;
-  return dense_layout(p, true, true).total;
+  return dense_layout(dense_call(p, QA_LAYOUT_NHD, false), true, true).total;
 }
 
 qa_status_t qa_dense_sage_attention_ex(const qa_dense_params_t* p, const qa_dense_options_t* options,
                                        const void* q, const void* k, const void* v, void* workspace,
                                        size_t workspace_bytes, void* out, float* lse, qa_stream_t stream) {
   return dense_attention_impl(p, options, q, k, v, workspace, workspace_bytes, out, lse, stream, true);
+}
+
+size_t qa_dense_sage_varlen_workspace_size(const qa_varlen_params_t* p) {
+  if (check_varlen(p) != QA_OK) return 0;
+  return dense_layout(varlen_call(p, nullptr, nullptr), true, true).total;
+}
+
+qa_status_t qa_dense_sage_attention_varlen(const qa_varlen_params_t* p, const void* q, const void* k,
+                                           const void* v, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, void* workspace,
+                                           size_t workspace_bytes, void* out, float* lse,
+                                           qa_stream_t stream) {
+  qa_status_t st = check_varlen(p);
+  if (st != QA_OK) return st;
+  if (p->batch == 0 || p->total_q == 0 || p->max_seqlen_q == 0) return QA_OK;
+  QA_REQUIRE(q && k && v && out && workspace && cu_seqlens_q && cu_seqlens_k, QA_ERR_INVALID_ARG,
+             "null pointer");
+  QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(workspace),
+             QA_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
+  QA_REQUIRE(((uintptr_t)lse & 3u) == 0 && ((uintptr_t)cu_seqlens_q & 3u) == 0 &&
+                 ((uintptr_t)cu_seqlens_k & 3u) == 0,
+             QA_ERR_INVALID_ARG, "lse and cu_seqlens must be 4-byte aligned");
+  const DenseCall c = varlen_call(p, cu_seqlens_q, cu_seqlens_k);
+  const DenseWs w = dense_layout(c, true, true);
+  QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
+             workspace_bytes, w.total);
+  return run_dense(c, q, k, v, (char*)workspace, w, out, lse, stream);
 }
 
 }  // extern "C"

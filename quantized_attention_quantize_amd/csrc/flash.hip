@@ -173,10 +173,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   const int32_t* trow = nullptr;
   int64_t blk_base = 0;
   if constexpr (DENSE) {
-    q_row0 = (int64_t)z * a.Nq;
-    Tq = a.Nq;
-    kv_len = a.Nk;
-    blk_base = (int64_t)z * ((a.Nk + 15) / 16);
+    // batched: every sequence has Nq queries and Nk keys; varlen: packed rows
+    q_row0 = a.q_rows.start(z);
+    Tq = a.q_rows.len(z);
+    kv_len = a.k_rows.len(z);
+    blk_base = a.k_rows.block0(z, 16);
   } else {
     q_row0 = a.cu_q[z];
     Tq = a.cu_q[z + 1] - (int)q_row0;
@@ -203,8 +204,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     for (int s = 0; s < KS; ++s)
       qf[qg][s] = ok ? *reinterpret_cast<const v4i*>(qp + 64 * s) : v4i{0, 0, 0, 0};
     if constexpr (DENSE) {
-      const int nqb = (a.Nq + 127) / 128;
-      qsc[qg] = a.q_scale[((int64_t)z * Hq + qh[qg]) * nqb + min(qi[qg] / 128, nqb - 1)] * a.scale_log2;
+      const int nqb = (Tq + 127) / 128;   // >= 1: the workgroup holds a row of the sequence
+      qsc[qg] = a.q_scale[a.q_rows.scale_at(z, qh[qg], Hq, min(qi[qg] / 128, nqb - 1), 128)] * a.scale_log2;
     } else {
       qsc[qg] = ok ? a.q_scale[(q_row0 + qi[qg]) * Hq + qh[qg]] * a.scale_log2 : 0.0f;
     }
@@ -396,10 +397,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   }
   __syncthreads();
 
-  const int nkb = DENSE ? (a.Nk + KT - 1) / KT : 1;
+  const int nkb = DENSE ? (kv_len + KT - 1) / KT : 1;
   // dense: key-block scales, read one tile ahead (a load issued and used in
   // the same tile would expose its latency every tile)
-  const float* ksc = DENSE ? a.k_scale + ((int64_t)z * Hkv + kvh) * nkb : nullptr;
+  const float* ksc = DENSE ? a.k_scale + a.k_rows.scale_at(z, kvh, Hkv, 0, KT) : nullptr;
   float tsc_next = 1.0f;
   if constexpr (DENSE) tsc_next = ntiles > 0 ? ksc[0] : 1.0f;
   int pb_next = load_blocks(1);
@@ -578,12 +579,13 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     int64_t ob;
     const float* vmu = nullptr;   // dense smooth_v: the V mean returns on rows that see a key
     if constexpr (DENSE) {
-      ob = (int64_t)z * a.o_sb + (int64_t)qi[qg] * a.o_st + (int64_t)qh[qg] * a.o_sh + 4 * g;
+      const int64_t orow = a.q_rows.packed ? (q_row0 + qi[qg]) * a.o_st : (int64_t)z * a.o_sb + (int64_t)qi[qg] * a.o_st;
+      ob = orow + (int64_t)qh[qg] * a.o_sh + 4 * g;
       if (a.v_mean != nullptr && l > 0.0f) vmu = a.v_mean + ((int64_t)z * Hkv + kvh) * D + 4 * g;
       if (a.lse != nullptr && g == 0) {
         // p = exp2(score * log2(e) - m_run) summed to l, so the natural-log
         // sum of exp(score) is ln2 * (m_run + log2 l)
-        const int64_t li = ((int64_t)z * Hq + qh[qg]) * Tq + qi[qg];
+        const int64_t li = a.q_rows.row_at(z, qh[qg], Hq, qi[qg]);
         float lse = l > 0.0f ? 0.69314718055994531f * (m_run[qg] + log2f(l)) : kNegInf;
         if (a.lse_corr != nullptr) lse += a.lse_corr[li];
         a.lse[li] = lse;

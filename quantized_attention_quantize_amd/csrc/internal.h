@@ -38,28 +38,60 @@ struct ProducerArgs {
 };
 hipError_t launch_producer(const ProducerArgs& a, hipStream_t st);
 
+// Where the tokens of sequence b of a dense call live. Batched (cu == nullptr):
+// every sequence has N tokens, token t of sequence b is row b*N + t, and its
+// R-token blocks start at b*ceil(N/R). Varlen (packed rows): sequence b is rows
+// cu[b] .. cu[b+1]-1 and N is the largest length; its blocks start at
+// cu[b]/R + b, so each sequence begins a fresh block and all of them fit in
+// total/R + B blocks (the gap left before each sequence is under one block).
+struct Rows {
+  const int32_t* cu;   // [B+1] device row offsets (varlen) or nullptr
+  int32_t B, N;
+  int64_t total;       // varlen: number of rows (cu[B])
+  bool packed;         // varlen (cu is set in every launch; the host sizes buffers without it)
+  __device__ __forceinline__ int64_t start(int b) const { return packed ? (int64_t)cu[b] : (int64_t)b * N; }
+  __device__ __forceinline__ int len(int b) const { return packed ? cu[b + 1] - cu[b] : N; }
+  __host__ __device__ __forceinline__ int64_t nblocks(int R) const {
+    return packed ? total / R + B : (int64_t)B * ((N + R - 1) / R);
+  }
+  __device__ __forceinline__ int64_t block0(int b, int R) const {
+    return packed ? (int64_t)(cu[b] / R) + b : (int64_t)b * ((N + R - 1) / R);
+  }
+  // per-(sequence, head) block scales: batched [B, H, ceil(N/R)], varlen [H, total/R + B]
+  __device__ __forceinline__ int64_t scale_at(int b, int h, int H, int blk, int R) const {
+    return packed ? (int64_t)h * nblocks(R) + block0(b, R) + blk : ((int64_t)b * H + h) * ((N + R - 1) / R) + blk;
+  }
+  // per-(sequence, head, token) values (LSE): batched [B, H, N], varlen [H, total]
+  __device__ __forceinline__ int64_t row_at(int b, int h, int H, int t) const {
+    return packed ? (int64_t)h * total + cu[b] + t : ((int64_t)b * H + h) * N + t;
+  }
+};
+
 struct SagePrepArgs {
   const void* q;
   const void* k;
   const void* v;          // only for the V transpose
   // element strides of (batch, token, head) in q, k and v (channels contiguous):
-  // NHD = (N*H*D, H*D, D), HND = (H*N*D, D, N*D)
+  // NHD = (N*H*D, H*D, D), HND = (H*N*D, D, N*D); varlen rows (q_rows.cu set)
+  // are packed [total, H, D]: token t of sequence b is row start(b) + t and the
+  // batch strides are unused
   int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh;
+  Rows q_rows, k_rows;    // sequence geometry of q and of k/v (N = Nq / Nk)
   bool bf16;
   int32_t B, Nq, Nk, Hq, Hkv, D;
   bool smooth_k;
   bool smooth_v;          // subtract the per-channel V mean (v_mean) in the V blocks
   float* v_mean;          // [B, Hkv, D] (smooth_v)
-  float* lse_corr;        // [B, Hq, Nq] smooth_k correction of the LSE, or nullptr
+  float* lse_corr;        // q_rows.row_at layout: smooth_k correction of the LSE, or nullptr
   float corr_scale;       // softmax scale (natural-log units) for lse_corr
   int8_t* q_i8;           // NHD codes
-  float* q_scale;         // [B, Hq, ceil(Nq/128)]
+  float* q_scale;         // q_rows.scale_at(.., 128) layout
   int8_t* k_i8;           // NHD codes (public layout) or nullptr
-  int8_t* k_paged;        // blocked layout [B*Nk16, Hkv, D/16, 16, 16] or nullptr
-  float* k_scale;         // [B, Hkv, ceil(Nk/64)]
+  int8_t* k_paged;        // blocked layout [k_rows.nblocks(16), Hkv, D/16, 16, 16] or nullptr
+  float* k_scale;         // k_rows.scale_at(.., 64) layout
   float* k_mean;          // [B, Hkv, D]
   double* partial;        // fp64 column sums [B, chunks, Hkv*D]
-  uint16_t* v_paged;      // V transposed into [B*Nk16, Hkv, D, 16] or nullptr
+  uint16_t* v_paged;      // V transposed into [k_rows.nblocks(16), Hkv, D, 16] or nullptr
 };
 size_t sage_partial_bytes(int32_t B, int32_t Nk, int32_t Hkv, int32_t D);
 hipError_t launch_sage_prep(const SagePrepArgs& a, hipStream_t st);
@@ -116,8 +148,9 @@ struct FlashArgs {
   void* out;               // [rows, Hq, D] (dense: element (b, i, h, c) at b*o_sb + i*o_st + h*o_sh + c)
   int64_t o_sb, o_st, o_sh; // dense output strides
   const float* v_mean;     // dense smooth_v: [B, Hkv, D] added back on rows that see a key, or nullptr
-  float* lse;              // dense: [B, Hq, Nq] natural-log LSE of each row, or nullptr
-  const float* lse_corr;   // dense: [B, Hq, Nq] added to lse (smooth_k correction), or nullptr
+  float* lse;              // dense: natural-log LSE of each row (q_rows.row_at layout), or nullptr
+  const float* lse_corr;   // dense: added to lse (smooth_k correction, same layout), or nullptr
+  Rows q_rows, k_rows;     // dense: sequence geometry (varlen when q_rows.cu is set)
   int32_t num_seqs, Hq, Hkv, G, D, max_blocks, max_seqlen_q;
   int32_t Nq, Nk;          // dense only
   float scale_log2;

@@ -164,18 +164,21 @@ constexpr int kSumChunk = 64;  // tokens per partial column sum
 // accumulated in fp64. Every K value is a multiple of 2^-24 (f16) or of a power
 // of two bounded by its exponent (bf16), and the sums stay far below 2^53 units,
 // so every partial sum is exact and the total does not depend on the order.
-// (b, t, h, c) of k lives at b*sb + t*st + h*sh + c.
+// (b, t, h, c) of k lives at b*sb + t*st + h*sh + c (batched) or at
+// (rows.start(b) + t)*st + h*sh + c (varlen). Chunks are counted from the
+// start of each sequence; chunks past its end hold zeros.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, int32_t Nk, int32_t D,
+__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, Rows rows, int32_t D,
                                                 int32_t HD, int64_t sb, int64_t st, int64_t sh,
                                                 double* __restrict__ partial) {
-  const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
+  const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
   const int b = blockIdx.z, chunk = blockIdx.y;
   const int c8 = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (c8 >= HD) return;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, Nk);
-  const uint16_t* base = k + (int64_t)b * sb + (int64_t)(c8 / D) * sh + c8 % D;
+  const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, rows.len(b));
+  const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
+  const uint16_t* base = k + seq0 + (int64_t)(c8 / D) * sh + c8 % D;
   auto add = [&](uint4 w) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -199,28 +202,30 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
   for (int i = 0; i < 8; ++i) dst[i] = acc[i];
 }
 
-// mu[b][c] = fl32(fl64(sum / Nk)); zeros when smoothing is off. A workgroup
-// covers 64 columns: four threads per column each add every fourth chunk
-// partial, then the four sums are added through LDS (all sums are exact, so
-// the order does not matter).
-__global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, int32_t B,
-                                              int32_t Nk, int32_t HD, bool smooth,
-                                              float* __restrict__ mean) {
+// mu[b][c] = fl32(fl64(sum / Nk_b)); zeros when smoothing is off or the
+// sequence is empty. A workgroup covers 64 columns: four threads per column
+// each add every fourth chunk partial, then the four sums are added through
+// LDS (all sums are exact, so the order does not matter).
+__global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, Rows rows,
+                                              int32_t HD, bool smooth, float* __restrict__ mean) {
   __shared__ double red[4][64];
   const int col = threadIdx.x & 63, slice = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.x * 64 + col;   // b * HD + c
-  const bool live = i < (int64_t)B * HD;
+  const bool live = i < (int64_t)rows.B * HD;
+  const int b = live ? (int)(i / HD) : 0;
+  const int Nk = live ? rows.len(b) : 0;
   double s = 0.0;
   if (live && smooth && Nk > 0) {
-    const int b = (int)(i / HD), c = (int)(i % HD);
-    const int chunks = (Nk + kSumChunk - 1) / kSumChunk;
+    const int c = (int)(i % HD);
+    const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
     const double* p = partial + (int64_t)b * chunks * HD + c;
-    for (int j = slice; j < chunks; j += 4) s += p[(int64_t)j * HD];
+    const int used = (Nk + kSumChunk - 1) / kSumChunk;
+    for (int j = slice; j < used; j += 4) s += p[(int64_t)j * HD];
   }
   red[slice][col] = s;
   __syncthreads();
   if (slice == 0 && live) {
-    if (!smooth || Nk == 0) {
+    if (!smooth || Nk <= 0) {
       mean[i] = 0.0f;
     } else {
       const double tot = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
 // corr_scale * sum_c x_c * corr_mu[b, h / corr_G, c] (fp32, the D/8 threads
 // of a row reduce their partial sums with shuffles).
 template <int D, int ROWS, bool BF16>
-__global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict__ x, int32_t N,
+__global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict__ x, Rows rows,
                                                      int32_t H, int64_t sb, int64_t st, int64_t sh,
                                                      const float* __restrict__ mean,
                                                      int8_t* __restrict__ codes_nhd,
@@ -248,9 +253,11 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   constexpr int G8 = D / 8;                // 8-channel groups per row
   constexpr int PER = ROWS * G8 / 256;     // groups per thread
   static_assert(ROWS * G8 % 256 == 0, "block must tile the workgroup");
-  const int nblk = (N + ROWS - 1) / ROWS;
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int N = rows.len(b);                 // tokens of this sequence
+  if (blk * ROWS >= N) return;               // the grid covers the longest sequence
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
   __shared__ float red[4];
 
   float val[PER][8];
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     const int r = gi / G8, c = (gi % G8) * 8;
     const int t = blk * ROWS + r;
     if (t < N) {
-      uint4 w = *reinterpret_cast<const uint4*>(x + (int64_t)b * sb + (int64_t)t * st + (int64_t)h * sh + c);
+      uint4 w = *reinterpret_cast<const uint4*>(x + seq0 + (int64_t)t * st + (int64_t)h * sh + c);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
       // the G8 threads of row r are consecutive lanes of one wave (G8 divides 64)
 #pragma unroll
       for (int o = 1; o < G8; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
-      if (gi % G8 == 0 && t < N) corr[((int64_t)b * H + h) * N + t] = dsum * corr_scale;
+      if (gi % G8 == 0 && t < N) corr[rows.row_at(b, h, H, t)] = dsum * corr_scale;
     }
   }
   amax = wave_max(amax);
@@ -317,16 +324,16 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     }
     if (t >= N) lo = hi = 0;
     if (codes_nhd != nullptr && t < N)
-      *reinterpret_cast<uint2*>(codes_nhd + (((int64_t)b * N + t) * H + h) * D + c) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(codes_nhd + ((rows.start(b) + t) * H + h) * D + c) = make_uint2(lo, hi);
     if (codes_blk != nullptr) {
-      // blocked layout: block (b * ceil(N/16) + t/16), head h, chunk c/16, slot t%16
-      const int64_t pb = (int64_t)b * ((N + 15) / 16) + t / 16;
+      // blocked layout: block (block0 + t/16), head h, chunk c/16, slot t%16
+      const int64_t pb = rows.block0(b, 16) + t / 16;
       if (t / 16 < (N + 15) / 16)
         *reinterpret_cast<uint2*>(codes_blk + ((pb * H + h) * (D / 16) + c / 16) * 256 + (t % 16) * 16 + (c % 16)) =
             make_uint2(lo, hi);
     }
   }
-  if (threadIdx.x == 0) scale[((int64_t)b * H + h) * nblk + blk] = s;
+  if (threadIdx.x == 0) scale[rows.scale_at(b, h, H, blk, ROWS)] = s;
 }
 
 // V [B, N, H, D] (bf16 or fp16) -> fp16 [B*ceil(N/16), H, D, 16]: row ch of a block
@@ -337,19 +344,21 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
 // (b, t, h, c) of v lives at b*sb + t*st + h*sh + c. With vmean (smooth_v)
 // each value becomes fl16(fl32(v) - vmean[b, h, c]).
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, int32_t N, int32_t H,
+__global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, Rows rows, int32_t H,
                                                   int64_t sb, int64_t st, int64_t sh,
                                                   const float* __restrict__ vmean, uint16_t* __restrict__ vb) {
   constexpr int UPR = D / 8;                 // 16-byte units per token row
   __shared__ __attribute__((aligned(16))) uint16_t tile[16][D + 8];
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int nb16 = (N + 15) / 16;
+  const int N = rows.len(b);
+  if (blk * 16 >= N) return;                 // the grid covers the longest sequence
+  const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
   for (int u = threadIdx.x; u < 16 * UPR; u += 256) {
     const int r = u / UPR, c8 = (u % UPR) * 8;
     const int t = blk * 16 + r;
     uint4 w = make_uint4(0, 0, 0, 0);
     if (t < N) {
-      w = *reinterpret_cast<const uint4*>(v + (int64_t)b * sb + (int64_t)t * st + (int64_t)h * sh + c8);
+      w = *reinterpret_cast<const uint4*>(v + seq0 + (int64_t)t * st + (int64_t)h * sh + c8);
       if (vmean != nullptr) {
         const float* mu = vmean + ((int64_t)b * H + h) * D + c8;
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -368,7 +377,7 @@ __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v
     *reinterpret_cast<uint4*>(&tile[r][c8]) = w;
   }
   __syncthreads();
-  uint16_t* dst = vb + (((int64_t)b * nb16 + blk) * H + h) * D * 16;
+  uint16_t* dst = vb + ((rows.block0(b, 16) + blk) * H + h) * D * 16;
   for (int u = threadIdx.x; u < 2 * D; u += 256) {   // output unit: channel u/2, half u%2
     const int ch = u >> 1;
     const int t0 = 8 * ((u & 1) ^ ((ch >> 3) & 1));
@@ -413,29 +422,30 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
   const dim3 gsum((HD / 8 + 255) / 256, chunks, a.B);
   const unsigned gmean = (unsigned)(((int64_t)a.B * HD + 63) / 64);
   if (a.smooth_k && a.Nk > 0)
-    k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, D, HD, a.k_sb, a.k_st, a.k_sh, a.partial);
-  k_mean<<<gmean, 256, 0, s>>>(a.partial, a.B, a.Nk, HD, a.smooth_k, a.k_mean);
+    k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, D, HD, a.k_sb, a.k_st, a.k_sh,
+                                        a.partial);
+  k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, a.smooth_k, a.k_mean);
   if (a.Nq > 0) {
     dim3 gq((a.Nq + 127) / 128, a.Hq, a.B);
     float* corr = a.smooth_k ? a.lse_corr : nullptr;
-    k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.Nq, a.Hq, a.q_sb, a.q_st, a.q_sh,
-                                                   nullptr, a.q_i8, nullptr, a.q_scale, a.k_mean,
+    k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.q_rows, a.Hq, a.q_sb, a.q_st,
+                                                   a.q_sh, nullptr, a.q_i8, nullptr, a.q_scale, a.k_mean,
                                                    a.Hq / a.Hkv, a.corr_scale, corr);
   }
   if (a.Nk > 0) {
     dim3 gk((a.Nk + 63) / 64, a.Hkv, a.B);
-    k_block_quant<D, 64, BF16><<<gk, 256, 0, s>>>((const uint16_t*)a.k, a.Nk, a.Hkv, a.k_sb, a.k_st, a.k_sh,
-                                                  a.k_mean, a.k_i8, a.k_paged, a.k_scale, nullptr, 1, 0.0f,
-                                                  nullptr);
+    k_block_quant<D, 64, BF16><<<gk, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, a.Hkv, a.k_sb, a.k_st,
+                                                  a.k_sh, a.k_mean, a.k_i8, a.k_paged, a.k_scale, nullptr, 1,
+                                                  0.0f, nullptr);
     if (a.v_paged != nullptr) {
       if (a.smooth_v) {
         // the column sums of K are consumed: the buffer takes those of V
-        k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, D, HD, a.v_sb, a.v_st, a.v_sh,
+        k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, D, HD, a.v_sb, a.v_st, a.v_sh,
                                             a.partial);
-        k_mean<<<gmean, 256, 0, s>>>(a.partial, a.B, a.Nk, HD, true, a.v_mean);
+        k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, true, a.v_mean);
       }
       dim3 gv((a.Nk + 15) / 16, a.Hkv, a.B);
-      k_v_blocks<D, BF16><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.Nk, a.Hkv, a.v_sb, a.v_st, a.v_sh,
+      k_v_blocks<D, BF16><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.Hkv, a.v_sb, a.v_st, a.v_sh,
                                              a.smooth_v ? a.v_mean : nullptr, a.v_paged);
     }
   }

@@ -198,6 +198,27 @@ def test_dense_options_validation(qa):
                                         None, None) == qa.QA_ERR_INVALID_ARG
 
 
+def test_dense_varlen_validation(qa):
+    L = qa.lib
+    p = qa.VarlenParams(3, 700, 900, 400, 500, 8, 2, 128, qa.QA_DT_F16, 1, 1, 1, 0.0, qa.QA_DT_F32)
+    need = L.qa_dense_sage_varlen_workspace_size(ctypes.byref(p))
+    # packed blocks: 900/16 + 3 = 59 K blocks of 2 x 128 x 16 (int8 codes + fp16 V); Q codes 700 x 8 x 128
+    assert need >= 700 * 8 * 128 + 59 * 2 * 128 * 16 * 3
+    call = lambda ws_bytes, *ptrs: L.qa_dense_sage_attention_varlen(ctypes.byref(p), *ptrs, FAKE, ws_bytes, FAKE,
+                                                                    None, None)
+    assert call(need - 1, FAKE, FAKE, FAKE, FAKE, FAKE) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert call(need, FAKE, FAKE, FAKE, None, FAKE) == qa.QA_ERR_INVALID_ARG              # no cu_seqlens_q
+    assert call(need, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002)) == qa.QA_ERR_INVALID_ARG  # misaligned
+    p.num_kv_heads = 3
+    assert call(need, FAKE, FAKE, FAKE, FAKE, FAKE) == qa.QA_ERR_INVALID_ARG              # 8 % 3
+    p.num_kv_heads, p.head_dim = 2, 96
+    assert call(need, FAKE, FAKE, FAKE, FAKE, FAKE) == qa.QA_ERR_UNSUPPORTED
+    p.head_dim, p.total_q = 128, -1
+    assert call(need, FAKE, FAKE, FAKE, FAKE, FAKE) == qa.QA_ERR_INVALID_ARG
+    p.total_q, p.batch = 700, 0
+    assert call(0, None, None, None, None, None) == qa.QA_OK                              # nothing to do
+
+
 def test_last_error_is_thread_local(qa):
     import threading
     L = qa.lib

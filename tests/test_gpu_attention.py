@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs, tiny_decode,
-                       qwen27b_decode, batched_splitk_decode, chunked_prefill, dense_sage)
+from workloads import (PagedSpec, DenseSpec, VarlenSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs,
+                       varlen_inputs, tiny_decode, qwen27b_decode, batched_splitk_decode, chunked_prefill, dense_sage)
 from tests.gpu_helpers import say, dev_bits, gpu_cache, oracle_cache, assert_close, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -466,6 +466,79 @@ def test_dense_options_full_size_sampled(qa):
             assert_close(o[b, h, rows], want[b, rows, h] + mu[b, h // (spec.num_q_heads // spec.num_kv_heads)],
                          f"dense options b={b} h={h}")
             _lse_close(l[b, h, rows], want_lse[b, h, rows] + corr[b, h, rows], f"dense options LSE b={b} h={h}")
+
+
+# packed variable-length dense
+VARLEN = [
+    # (seq_q, seq_k, Hq, Hkv, d, dtype, causal, smooth_v)
+    ([1, 50, 64, 97, 128, 300], [1, 50, 64, 97, 128, 300], 4, 2, 128, "f16", True, True),
+    ([130, 7, 0, 260], [200, 7, 30, 260], 8, 1, 64, "bf16", False, False),
+    ([300, 5, 16], [100, 0, 16], 2, 2, 256, "f16", True, True),     # Nq > Nk, a sequence without keys
+    ([129, 255, 1], [513, 64, 2], 6, 2, 128, "bf16", True, False),
+]
+
+
+def _varlen_run(qa, inp, causal, smooth_v):
+    sp = inp.spec
+    dt = sp.dtype
+    cu_q, cu_k = torch.from_numpy(inp.cu_q).cuda(), torch.from_numpy(inp.cu_k).cuda()
+    return qa.dense_sage_attention_varlen(dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt), cu_q, cu_k,
+                                          max(sp.seq_q), max(sp.seq_k), is_causal=causal, smooth_v=smooth_v,
+                                          return_lse=True)
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: f"{'-'.join(map(str, c[0]))}_on_{'-'.join(map(str, c[1]))}_H{c[2]}/{c[3]}_d{c[4]}_{c[5]}_{'causal' if c[6] else 'full'}{'_sv' if c[7] else ''}")
+def test_dense_varlen_parity(qa, case):
+    """Packed sequences in one batched call: output and LSE against the
+    oracle's per-sequence forward, and every sequence bit-identical to the
+    one-sequence options call on its slice."""
+    seq_q, seq_k, Hq, Hkv, d, dt, causal, smooth_v = case
+    say(f"dense varlen {case}")
+    spec = VarlenSpec("vl", 71 + d, seq_q, seq_k, Hq, Hkv, d, dtype=dt, v_bias_std=2.0)
+    inp = varlen_inputs(spec)
+    out, lse = _varlen_run(qa, inp, causal, smooth_v)
+    torch.cuda.synchronize()
+    want, want_lse = oracle.sage_varlen_forward(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, dt, causal=causal,
+                                                smooth_v=smooth_v, return_lse=True)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert_close(o, want, "dense varlen")
+    _lse_close(l, want_lse, "dense varlen LSE")
+    for b in range(len(seq_q)):
+        q0, q1, k0, k1 = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        if q1 == q0 or k1 == k0:
+            continue
+        one, one_lse = qa.dense_sage_attention_ex(dev_bits(inp.q[None, q0:q1], dt), dev_bits(inp.k[None, k0:k1], dt),
+                                                  dev_bits(inp.v[None, k0:k1], dt), is_causal=causal,
+                                                  smooth_v=smooth_v, return_lse=True)
+        assert torch.equal(one[0], out[q0:q1]), f"sequence {b} differs from its one-sequence call"
+        assert torch.equal(one_lse[0], lse[:, q0:q1]), f"sequence {b} LSE differs"
+
+
+def test_dense_varlen_extreme_mix_sampled(qa):
+    """Lengths 1 : 8192 in one call (the pages' extreme varlen mix): the
+    short sequences in full and sampled rows of the long one against the
+    oracle's steps on that slice."""
+    spec = VarlenSpec("vl_mix", 83, [1, 8192, 33], [1, 8192, 40], 4, 4, 128, dtype="f16")
+    inp = varlen_inputs(spec)
+    say("dense varlen 1 : 8192 mix")
+    out, lse = _varlen_run(qa, inp, True, False)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for b in (0, 2):
+        q0, q1, k0, k1 = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        w, wl = oracle.sage_forward(inp.q[None, q0:q1], inp.k[None, k0:k1], inp.v[None, k0:k1], "f16", causal=True,
+                                    return_lse=True)
+        assert_close(o[q0:q1], w[0], f"varlen sequence {b}")
+        _lse_close(l[:, q0:q1], wl[0], f"varlen sequence {b} LSE")
+    q0, k0 = inp.cu_q[1], inp.cu_k[1]
+    quant = oracle.sage_quantize(inp.q[None, q0:q0 + 8192], inp.k[None, k0:k0 + 8192], "f16")
+    rows = np.array([0, 127, 128, 4000, 8191])
+    w, wl = oracle.dense_sage_attention(quant, inp.v[None, k0:k0 + 8192], "f16", causal=True, rows=rows,
+                                        heads=[0, 3], return_lse=True)
+    corr = oracle.sage_lse_correction(inp.q[None, q0:q0 + 8192], quant["k_mean"], "f16")
+    for h in (0, 3):
+        assert_close(o[q0 + rows, h], w[0, rows, h], f"varlen long sequence head {h}")
+        _lse_close(l[h, q0 + rows], wl[0, h, rows] + corr[0, h, rows], f"varlen long sequence LSE head {h}")
 
 
 def test_decode_workspace_reuse_across_calls(qa):

@@ -100,6 +100,14 @@ MUTATIONS = [
      pins.test_smooth_v_adds_the_mean_back, ()),
     ("smooth_v_mean_divisor", oa, "sage_smooth_v", "/ np.float64(N))", "/ np.float64(N - 1))",
      pins.test_smooth_v_adds_the_mean_back, ()),
+    ("varlen_keys_at_query_offsets", oa, "sage_varlen_forward", "k[None, k0:k1], v[None, k0:k1]",
+     "k[None, q0:q0 + (k1 - k0)], v[None, q0:q0 + (k1 - k0)]", pins.test_varlen_equal_lengths_is_the_batched_forward,
+     (False,)),
+    ("varlen_lse_rows_by_key_offset", oa, "sage_varlen_forward", "lse[:, q0:q1] = l[0]",
+     "lse[:, q0:q1] = l[0][:, ::-1]", pins.test_varlen_equal_lengths_is_the_batched_forward, (True,)),
+    ("mean_over_all_sequences", oq, "sage_quantize", "total = k.astype(np.float64).sum(axis=1)",
+     "total = k.astype(np.float64).sum(axis=1).mean(axis=0, keepdims=True) + 0 * k[:, 0]",
+     pins.test_varlen_equal_lengths_is_the_batched_forward, (False,)),
 ]
 
 

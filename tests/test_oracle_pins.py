@@ -11,8 +11,8 @@ from scipy.special import softmax as sp_softmax
 
 import oracle
 from oracle import quant as oq
-from workloads import (PagedSpec, DenseSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs, to_bf16_bits,
-                       to_f16_bits)
+from workloads import (PagedSpec, DenseSpec, VarlenSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs,
+                       varlen_inputs, to_bf16_bits, to_f16_bits)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -557,6 +557,54 @@ def test_smooth_v_adds_the_mean_back():
     # the mean is the exact fp64 mean rounded to fp32
     exact = oq.widen(vb, "f16").astype(np.float64).sum(axis=1) / 120.0
     np.testing.assert_array_equal(mu, exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_is_the_batched_forward(causal):
+    """Packing B equal-length sequences row after row and attending them as
+    varlen gives the batched forward (outputs [B, N, H, d] -> [B*N, H, d],
+    LSE [B, H, N] -> [H, B*N]); query and key lengths differ, so an offset
+    taken from the wrong side shows."""
+    spec, inp = _dense(B=3, H=4, Hkv=2, N=150, Nk=170, d=64)
+    want, wl = oracle.sage_forward(inp.q, inp.k, inp.v, "f16", causal=causal, smooth_v=True, return_lse=True)
+    cu_q, cu_k = [0, 150, 300, 450], [0, 170, 340, 510]
+    got, gl = oracle.sage_varlen_forward(inp.q.reshape(450, 4, 64), inp.k.reshape(510, 2, 64),
+                                         inp.v.reshape(510, 2, 64), cu_q, cu_k, "f16", causal=causal,
+                                         smooth_v=True, return_lse=True)
+    np.testing.assert_allclose(got, want.reshape(450, 4, 64), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gl, wl.transpose(1, 0, 2).reshape(4, 450), rtol=1e-12, atol=1e-13)
+
+
+def test_varlen_sequences_are_independent():
+    """A sequence's rows do not change when its neighbours' values change
+    (its means, block scales and softmax are its own); a sequence with no
+    keys gets zero rows and an LSE of -inf; one with no queries adds no rows."""
+    spec = VarlenSpec("vl", 61, [40, 0, 130, 7, 5], [90, 30, 130, 7, 0], 4, 2, 64, v_bias_std=2.0)
+    inp = varlen_inputs(spec)
+    run = lambda k, v: oracle.sage_varlen_forward(inp.q, k, v, inp.cu_q, inp.cu_k, "f16", causal=True,
+                                                  smooth_v=True, return_lse=True)
+    out, lse = run(inp.k, inp.v)
+    rows0, rows2, rows3 = slice(0, 40), slice(40, 170), slice(170, 177)
+    k2 = inp.k.copy()
+    k2[:90] = to_f16_bits(oq.widen(k2[:90], "f16") * np.float32(3.0) + np.float32(1.0))   # keys of sequence 0
+    out2, lse2 = run(k2, inp.v)
+    assert not np.allclose(out[rows0], out2[rows0])           # the change shows where it belongs
+    np.testing.assert_array_equal(out2[40:], out[40:])        # and nowhere else
+    np.testing.assert_array_equal(lse2[:, 40:], lse[:, 40:])
+    v2 = inp.v.copy()
+    v2[120:250] = to_f16_bits(oq.widen(v2[120:250], "f16") - np.float32(5.0))           # values of sequence 2
+    out3, _ = run(inp.k, v2)
+    assert not np.allclose(out[rows2], out3[rows2])
+    np.testing.assert_array_equal(out3[rows0], out[rows0])
+    np.testing.assert_array_equal(out3[rows3], out[rows3])
+    np.testing.assert_array_equal(out[177:], 0.0)                # sequence 4: no keys
+    assert np.all(np.isneginf(lse[:, 177:]))
+    assert np.all(np.isfinite(lse[:, :177]))
+    # the one-sequence forward on each slice
+    for b, (q0, q1, k0, k1) in enumerate([(0, 40, 0, 90), (40, 170, 120, 250), (170, 177, 250, 257)]):
+        one = oracle.sage_forward(inp.q[None, q0:q1], inp.k[None, k0:k1], inp.v[None, k0:k1], "f16", causal=True,
+                                  smooth_v=True)
+        np.testing.assert_array_equal(out[q0:q1], one[0])
 
 
 def test_smoothing_leaves_unquantized_attention_unchanged():

@@ -215,6 +215,51 @@ def dense_inputs(spec: DenseSpec) -> DenseInputs:
     return DenseInputs(spec, q, k, v)
 
 
+@dataclass
+class VarlenSpec:
+    """Packed variable-length dense inputs: sequence b has seq_q[b] query
+    rows and seq_k[b] key/value rows."""
+    name: str
+    seed: int
+    seq_q: list
+    seq_k: list
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    k_bias_std: float = 3.0
+    dtype: str = "f16"
+    v_bias_std: float = 0.0
+
+
+@dataclass
+class VarlenInputs:
+    spec: VarlenSpec
+    q: np.ndarray       # [total_q, Hq, d] uint16 bits
+    k: np.ndarray       # [total_k, Hkv, d]
+    v: np.ndarray
+    cu_q: np.ndarray    # [B+1] int32 row offsets
+    cu_k: np.ndarray
+
+
+def varlen_inputs(spec: VarlenSpec) -> VarlenInputs:
+    """The dense recipe per sequence (Q ~ N(0,1); K ~ N(0,1) + a per-(head,
+    channel) bias shared by all sequences; V ~ N(0,1) + optional offset),
+    packed row after row."""
+    Hq, Hkv, d = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    bias = _rng(spec.seed, 1).standard_normal((Hkv, d), dtype=np.float32) * np.float32(spec.k_bias_std)
+    vbias = _rng(spec.seed, 3).standard_normal((Hkv, d), dtype=np.float32) * np.float32(spec.v_bias_std)
+    qs, ks, vs = [], [], []
+    for b, (nq, nk) in enumerate(zip(spec.seq_q, spec.seq_k)):
+        g = _rng(spec.seed, 2, b)
+        qs.append(_store(g.standard_normal((nq, Hq, d), dtype=np.float32), spec.dtype))
+        ks.append(_store(g.standard_normal((nk, Hkv, d), dtype=np.float32) + bias[None], spec.dtype))
+        vx = g.standard_normal((nk, Hkv, d), dtype=np.float32)
+        vs.append(_store(vx + vbias[None] if spec.v_bias_std else vx, spec.dtype))
+    cu = lambda n: np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    cat = lambda xs, H: np.concatenate(xs) if xs else np.zeros((0, H, d), np.uint16)
+    return VarlenInputs(spec, cat(qs, Hq), cat(ks, Hkv), cat(vs, Hkv), cu(spec.seq_q), cu(spec.seq_k))
+
+
 def dense_zero_scale_inputs(N: int = 200, d: int = 64, dtype: str = "f16") -> DenseInputs:
     """Degenerate dense inputs: KV head 0 holds the same key at every position
     (smoothing then leaves all-zero keys, so every key-block scale is 0) and
