@@ -354,6 +354,47 @@ def run_dense(torch, qa, reps, causal, options=False):
             "_ops": (qk, pv)}
 
 
+VARLEN_MIX = [8192, 4096, 2048, 1024, 512, 256, 128, 64, 32, 16, 8, 4, 2, 1, 1, 1]
+
+
+def run_varlen(torch, qa, reps):
+    """Packed sequences of 8192 down to 1 token (the pages' mixed-length
+    varlen case), 32 heads, d 128, fp16, causal, in one call; beside it the
+    same sequences as one dense call each (the per-sequence loop)."""
+    from workloads import VarlenSpec, varlen_inputs
+    spec = VarlenSpec("varlen_mix", 9, VARLEN_MIX, VARLEN_MIX, 32, 32, 128, dtype="f16")
+    inp = varlen_inputs(spec)
+    q, k, v = (dev_bits(torch, x, "f16") for x in (inp.q, inp.k, inp.v))
+    cu_q, cu_k = torch.from_numpy(inp.cu_q).cuda(), torch.from_numpy(inp.cu_k).cuda()
+    mx = max(VARLEN_MIX)
+    p = qa.varlen_params(q, k, mx, mx, len(VARLEN_MIX), True)
+    ws = torch.empty(qa.lib.qa_dense_sage_varlen_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    f = lambda: qa.dense_sage_attention_varlen(q, k, v, cu_q, cu_k, mx, mx, is_causal=True, workspace=ws, out=out)
+    slices = [(int(a), int(b)) for a, b in zip(inp.cu_q[:-1], inp.cu_q[1:])]
+    views = [(q[a:b].unsqueeze(0), k[a:b].unsqueeze(0), v[a:b].unsqueeze(0), out[a:b].unsqueeze(0))
+             for a, b in slices]
+    wss = [qa.dense_sage_workspace(qa.dense_params(qq, kk, True, True)) for qq, kk, _, _ in views]
+    loop = lambda: [qa.dense_sage_attention(qq, kk, vv, is_causal=True, workspace=w, out=oo)
+                    for (qq, kk, vv, oo), w in zip(views, wss)]
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        evs = _mk_stream_events(torch, reps)
+        for a, b in evs:
+            a.record(); fn(); b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+    ms, loop_ms = timed(f), timed(loop)
+    qk, pv = flash_ops(VARLEN_MIX, VARLEN_MIX, 32, 128, True)
+    tops = (qk + pv) / (ms * 1e-3) / 1e12
+    return {"workload": f"dense_sage varlen, {len(VARLEN_MIX)} packed sequences of 8192 down to 1 token "
+                        f"({sum(VARLEN_MIX)} rows), H32 d128 causal, one call (full chain)",
+            "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS,
+            "per_sequence_loop_ms": loop_ms, "speedup_vs_loop": loop_ms / ms}
+
+
 def run_practical_peaks(torch, step_bytes: int, pools: int) -> dict:
     """Practical ceilings measured on this GPU with the probes of qa_probe.h:
     a plain streaming read (1 GiB, and the decode step's byte count rotated
@@ -483,7 +524,8 @@ def main():
                         "chunked_prefill": run_prefill(torch, qa, 20),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True),
-                        "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True)}
+                        "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True),
+                        "dense_sage_varlen_mix": run_varlen(torch, qa, 10)}
         for e in res["extra"].values():
             if "_ops" not in e:
                 continue

@@ -150,9 +150,10 @@ DenseCall dense_call(const qa_dense_params_t* p, int32_t layout, bool smooth_v) 
 }
 
 // Dense workspace: [partial sums][q_i8][k blocks][v blocks][q_scale][k_scale][k_mean], 256-aligned.
-// The options and varlen calls append [v_mean][lse_corr].
+// The options and varlen calls append [v_mean][lse_corr]; varlen then adds the
+// packed-block maps [q 128-row][k 64-row][k 16-row].
 struct DenseWs {
-  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, total;
+  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, q_map, k_map64, k_map16, total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -173,6 +174,11 @@ DenseWs dense_layout(const DenseCall& c, bool with_attention, bool ex) {
     if (ex) {
       w.v_mean = off; off += al(B * Hkv * D * sizeof(float));
       w.lse_corr = off; off += al(Hq * rows_q * sizeof(float));
+    }
+    if (c.q.packed) {
+      w.q_map = off; off += al(c.q.nblocks(128) * sizeof(int32_t));
+      w.k_map64 = off; off += al(c.k.nblocks(64) * sizeof(int32_t));
+      w.k_map16 = off; off += al(nb16 * sizeof(int32_t));
     }
   }
   w.total = off;
@@ -198,6 +204,10 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
   pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
   pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
   pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
+  if (c.q.packed) {
+    pa.q_map = (int32_t*)(ws + w.q_map); pa.k_map64 = (int32_t*)(ws + w.k_map64);
+    pa.k_map16 = (int32_t*)(ws + w.k_map16);
+  }
   qa_status_t st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
   if (st != QA_OK) return st;
   qa::FlashArgs a{};
@@ -205,7 +215,7 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
   a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
   a.o_sb = c.so.b; a.o_st = c.so.t; a.o_sh = c.so.h;
   a.v_mean = pa.v_mean; a.lse = lse; a.lse_corr = pa.lse_corr;
-  a.q_rows = c.q; a.k_rows = c.k;
+  a.q_rows = c.q; a.k_rows = c.k; a.q_map = pa.q_map;
   a.num_seqs = c.q.B; a.Hq = c.Hq; a.Hkv = c.Hkv; a.G = c.Hq / c.Hkv;
   a.D = c.D; a.max_blocks = 0; a.max_seqlen_q = c.q.N; a.Nq = c.q.N; a.Nk = c.k.N;
   a.scale_log2 = log2_scale(c.softmax_scale, c.D);

@@ -151,16 +151,30 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   __shared__ __attribute__((aligned(16))) v4i s_q[QLDS ? NW * QG * KS : 1][64];
 
   // ---- work item (XCD-aware order) ----------------------------------------
-  // dense: (query tile, query head, batch); paged: (row tile, KV head, sequence)
+  // Consecutive work items go to one XCD (they share K/V in its L2); each
+  // XCD takes one contiguous eighth of the items. Paged: (row tile, KV head,
+  // sequence), row tile fastest. Dense: (query tile, sequence, query head):
+  // head-major, so every eighth holds heads of all sequences and a long
+  // sequence of a varlen batch is spread over all XCDs.
   const int G = DENSE ? 1 : a.G;
   const int nunits = DENSE ? a.Hq : a.Hkv;
   const int nqt = ((DENSE ? a.Nq : a.max_seqlen_q) * G + QT - 1) / QT;
   const int total = (int)gridDim.x;
   int wid = blockIdx.x;
   if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int qtile = wid % nqt;
-  const int hu_ = (wid / nqt) % nunits;
-  const int z = wid / (nqt * nunits);
+  // causal: the longest rows (last tiles) start first, the short ones fill the tail
+  int qtile = CAUSAL ? nqt - 1 - wid % nqt : wid % nqt;
+  int hu_ = DENSE ? wid / (nqt * a.num_seqs) : (wid / nqt) % nunits;
+  int z = DENSE ? (wid / nqt) % a.num_seqs : wid / (nqt * nunits);
+  if (DENSE && a.q_rows.packed) {
+    // varlen: (packed 128-row block, query head), the block's sequence from the map
+    const int nblk = (int)a.q_rows.nblocks(QT);
+    const int j = CAUSAL ? nblk - 1 - wid % nblk : wid % nblk;
+    hu_ = wid / nblk;
+    z = a.q_map[j];
+    if (z < 0 || z >= a.num_seqs) return;
+    qtile = j - (int)a.q_rows.block0(z, QT);
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -647,7 +661,11 @@ hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
   const int G = DENSE ? 1 : a.G;
   const int qtiles = (int)(((int64_t)(DENSE ? a.Nq : a.max_seqlen_q) * G + QT - 1) / QT);
   if (qtiles == 0 || a.num_seqs == 0) return hipSuccess;
-  const int64_t total = (int64_t)qtiles * (DENSE ? a.Hq : a.Hkv) * a.num_seqs;
+  int64_t total = (int64_t)qtiles * (DENSE ? a.Hq : a.Hkv) * a.num_seqs;
+  if (DENSE && a.q_rows.packed) {
+    if (QT != 128) return hipErrorInvalidValue;   // the map is of 128-row query blocks
+    total = a.q_rows.nblocks(QT) * a.Hq;
+  }
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   k_flash<D, QG, NW, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
   return hipGetLastError();

@@ -77,6 +77,11 @@ struct SagePrepArgs {
   // batch strides are unused
   int64_t q_sb, q_st, q_sh, k_sb, k_st, k_sh, v_sb, v_st, v_sh;
   Rows q_rows, k_rows;    // sequence geometry of q and of k/v (N = Nq / Nk)
+  // varlen: sequence of each packed block (-1 for the gap before a sequence),
+  // written here: q_map [q_rows.nblocks(128)], k_map64 and k_map16 likewise
+  int32_t* q_map;
+  int32_t* k_map64;
+  int32_t* k_map16;
   bool bf16;
   int32_t B, Nq, Nk, Hq, Hkv, D;
   bool smooth_k;
@@ -150,7 +155,8 @@ struct FlashArgs {
   const float* v_mean;     // dense smooth_v: [B, Hkv, D] added back on rows that see a key, or nullptr
   float* lse;              // dense: natural-log LSE of each row (q_rows.row_at layout), or nullptr
   const float* lse_corr;   // dense: added to lse (smooth_k correction, same layout), or nullptr
-  Rows q_rows, k_rows;     // dense: sequence geometry (varlen when q_rows.cu is set)
+  Rows q_rows, k_rows;     // dense: sequence geometry (varlen when q_rows.packed)
+  const int32_t* q_map;    // varlen: sequence of each packed 128-row query block, -1 for gaps
   int32_t num_seqs, Hq, Hkv, G, D, max_blocks, max_seqlen_q;
   int32_t Nq, Nk;          // dense only
   float scale_log2;

@@ -158,7 +158,32 @@ __global__ __launch_bounds__(256) void k_producer(ProducerArgs a, int64_t qblock
 // SageAttention-style preprocessing
 // ---------------------------------------------------------------------------
 
-constexpr int kSumChunk = 64;  // tokens per partial column sum
+constexpr int kSumChunk = 64;  // tokens per partial column sum (= the K block, so varlen chunks share its map)
+
+// Sequence and block of this workgroup. Batched grids are (blocks, heads, B);
+// varlen grids run over all packed blocks, (rows.nblocks(R), heads), and
+// map[j] names the sequence of packed block j (-1 for the gap before a
+// sequence): only workgroups with work are launched beyond one per gap.
+struct BlockRef {
+  int b, blk;
+};
+__device__ __forceinline__ BlockRef block_of(const Rows& rows, const int32_t* map, int R, int zdim_b) {
+  if (!rows.packed) return {zdim_b, (int)blockIdx.x};
+  const int b = map[blockIdx.x];
+  if (b < 0 || b >= rows.B) return {-1, 0};
+  return {b, (int)(blockIdx.x - rows.block0(b, R))};
+}
+
+// map[j] = b for the packed R-row blocks j of sequence b, -1 for the blocks of
+// the gap before the next sequence; one workgroup per sequence, and the
+// ranges of the sequences partition [0, rows.nblocks(R)).
+__global__ __launch_bounds__(256) void k_block_map(Rows rows, int32_t R, int32_t* __restrict__ map) {
+  const int b = blockIdx.x;
+  const int64_t j0 = rows.block0(b, R);
+  const int64_t j1 = b + 1 < rows.B ? rows.block0(b + 1, R) : rows.nblocks(R);
+  const int64_t nb = (rows.len(b) + R - 1) / R;
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) map[j] = j - j0 < nb ? b : -1;
+}
 
 // partial[b][chunk][c] = sum over the chunk's tokens of K[b, t, c], c in [0, Hkv*D),
 // accumulated in fp64. Every K value is a multiple of 2^-24 (f16) or of a power
@@ -168,12 +193,20 @@ constexpr int kSumChunk = 64;  // tokens per partial column sum
 // (rows.start(b) + t)*st + h*sh + c (varlen). Chunks are counted from the
 // start of each sequence; chunks past its end hold zeros.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, Rows rows, int32_t D,
-                                                int32_t HD, int64_t sb, int64_t st, int64_t sh,
+__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, Rows rows, const int32_t* map,
+                                                int32_t D, int32_t HD, int64_t sb, int64_t st, int64_t sh,
                                                 double* __restrict__ partial) {
   const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
-  const int b = blockIdx.z, chunk = blockIdx.y;
-  const int c8 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  // batched grid (column groups, chunks, B); varlen (packed chunks, column groups)
+  int b = blockIdx.z, chunk = blockIdx.y, cg = blockIdx.x;
+  if (rows.packed) {
+    const int j = blockIdx.x;
+    b = map[j];
+    if (b < 0 || b >= rows.B) return;
+    chunk = (int)(j - rows.block0(b, kSumChunk));
+    cg = blockIdx.y;
+  }
+  const int c8 = (cg * 256 + threadIdx.x) * 8;
   if (c8 >= HD) return;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, rows.len(b));
@@ -243,7 +276,8 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
 // of a row reduce their partial sums with shuffles).
 template <int D, int ROWS, bool BF16>
 __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict__ x, Rows rows,
-                                                     int32_t H, int64_t sb, int64_t st, int64_t sh,
+                                                     const int32_t* map, int32_t H, int64_t sb, int64_t st,
+                                                     int64_t sh,
                                                      const float* __restrict__ mean,
                                                      int8_t* __restrict__ codes_nhd,
                                                      int8_t* __restrict__ codes_blk,
@@ -253,9 +287,11 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   constexpr int G8 = D / 8;                // 8-channel groups per row
   constexpr int PER = ROWS * G8 / 256;     // groups per thread
   static_assert(ROWS * G8 % 256 == 0, "block must tile the workgroup");
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const BlockRef br = block_of(rows, map, ROWS, blockIdx.z);
+  if (br.b < 0) return;
+  const int blk = br.blk, h = blockIdx.y, b = br.b;
   const int N = rows.len(b);                 // tokens of this sequence
-  if (blk * ROWS >= N) return;               // the grid covers the longest sequence
+  if (blk * ROWS >= N) return;               // batched grids cover the longest sequence
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
   __shared__ float red[4];
@@ -344,14 +380,17 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
 // (b, t, h, c) of v lives at b*sb + t*st + h*sh + c. With vmean (smooth_v)
 // each value becomes fl16(fl32(v) - vmean[b, h, c]).
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, Rows rows, int32_t H,
-                                                  int64_t sb, int64_t st, int64_t sh,
+__global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v, Rows rows,
+                                                  const int32_t* map, int32_t H, int64_t sb, int64_t st,
+                                                  int64_t sh,
                                                   const float* __restrict__ vmean, uint16_t* __restrict__ vb) {
   constexpr int UPR = D / 8;                 // 16-byte units per token row
   __shared__ __attribute__((aligned(16))) uint16_t tile[16][D + 8];
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const BlockRef br = block_of(rows, map, 16, blockIdx.z);
+  if (br.b < 0) return;
+  const int blk = br.blk, h = blockIdx.y, b = br.b;
   const int N = rows.len(b);
-  if (blk * 16 >= N) return;                 // the grid covers the longest sequence
+  if (blk * 16 >= N) return;                 // batched grids cover the longest sequence
   const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
   for (int u = threadIdx.x; u < 16 * UPR; u += 256) {
     const int r = u / UPR, c8 = (u % UPR) * 8;
@@ -419,34 +458,43 @@ template <int D, bool BF16>
 hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
   const int HD = a.Hkv * D;
   const int chunks = (a.Nk + kSumChunk - 1) / kSumChunk;
-  const dim3 gsum((HD / 8 + 255) / 256, chunks, a.B);
+  const int cgs = (HD / 8 + 255) / 256;   // column groups of the sums
+  const bool vl = a.k_rows.packed;
+  // varlen grids run over the packed blocks of all sequences (block maps first)
+  auto grid = [&](const Rows& r, int R, int heads) {
+    return vl ? dim3((unsigned)r.nblocks(R), heads, 1) : dim3((unsigned)((r.N + R - 1) / R), heads, a.B);
+  };
+  if (vl) {
+    k_block_map<<<a.B, 256, 0, s>>>(a.q_rows, 128, a.q_map);
+    k_block_map<<<a.B, 256, 0, s>>>(a.k_rows, 64, a.k_map64);
+    k_block_map<<<a.B, 256, 0, s>>>(a.k_rows, 16, a.k_map16);
+  }
+  const dim3 gsum = vl ? dim3((unsigned)a.k_rows.nblocks(kSumChunk), cgs, 1) : dim3(cgs, chunks, a.B);
   const unsigned gmean = (unsigned)(((int64_t)a.B * HD + 63) / 64);
   if (a.smooth_k && a.Nk > 0)
-    k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, D, HD, a.k_sb, a.k_st, a.k_sh,
+    k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, a.k_map64, D, HD, a.k_sb, a.k_st, a.k_sh,
                                         a.partial);
   k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, a.smooth_k, a.k_mean);
   if (a.Nq > 0) {
-    dim3 gq((a.Nq + 127) / 128, a.Hq, a.B);
     float* corr = a.smooth_k ? a.lse_corr : nullptr;
-    k_block_quant<D, 128, BF16><<<gq, 256, 0, s>>>((const uint16_t*)a.q, a.q_rows, a.Hq, a.q_sb, a.q_st,
-                                                   a.q_sh, nullptr, a.q_i8, nullptr, a.q_scale, a.k_mean,
-                                                   a.Hq / a.Hkv, a.corr_scale, corr);
+    k_block_quant<D, 128, BF16><<<grid(a.q_rows, 128, a.Hq), 256, 0, s>>>(
+        (const uint16_t*)a.q, a.q_rows, a.q_map, a.Hq, a.q_sb, a.q_st, a.q_sh, nullptr, a.q_i8, nullptr, a.q_scale,
+        a.k_mean, a.Hq / a.Hkv, a.corr_scale, corr);
   }
   if (a.Nk > 0) {
-    dim3 gk((a.Nk + 63) / 64, a.Hkv, a.B);
-    k_block_quant<D, 64, BF16><<<gk, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, a.Hkv, a.k_sb, a.k_st,
-                                                  a.k_sh, a.k_mean, a.k_i8, a.k_paged, a.k_scale, nullptr, 1,
-                                                  0.0f, nullptr);
+    k_block_quant<D, 64, BF16><<<grid(a.k_rows, 64, a.Hkv), 256, 0, s>>>(
+        (const uint16_t*)a.k, a.k_rows, a.k_map64, a.Hkv, a.k_sb, a.k_st, a.k_sh, a.k_mean, a.k_i8, a.k_paged,
+        a.k_scale, nullptr, 1, 0.0f, nullptr);
     if (a.v_paged != nullptr) {
       if (a.smooth_v) {
         // the column sums of K are consumed: the buffer takes those of V
-        k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, D, HD, a.v_sb, a.v_st, a.v_sh,
-                                            a.partial);
+        k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.k_map64, D, HD, a.v_sb, a.v_st,
+                                            a.v_sh, a.partial);
         k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, true, a.v_mean);
       }
-      dim3 gv((a.Nk + 15) / 16, a.Hkv, a.B);
-      k_v_blocks<D, BF16><<<gv, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.Hkv, a.v_sb, a.v_st, a.v_sh,
-                                             a.smooth_v ? a.v_mean : nullptr, a.v_paged);
+      k_v_blocks<D, BF16><<<grid(a.k_rows, 16, a.Hkv), 256, 0, s>>>(
+          (const uint16_t*)a.v, a.k_rows, a.k_map16, a.Hkv, a.v_sb, a.v_st, a.v_sh,
+          a.smooth_v ? a.v_mean : nullptr, a.v_paged);
     }
   }
   return hipGetLastError();
