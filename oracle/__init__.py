@@ -34,18 +34,25 @@ Parity status, function by function (pins live in tests/test_oracle_pins.py):
   (closed forms: LSE of equal scores is ln(#visible); constant keys make the
   corrected LSE q.c*scale + ln(#visible); the V mean added back reproduces
   the unsmoothed output within the fp16 rounding of V').
+* apply_rope, rope_quantize_q, rope_write_kv_cache: pinned (position 0 is
+  the identity; pairs rotate as complex numbers times e^(i theta); the
+  interleaved pairing is the half pairing of permuted channels; channels
+  past rot_dim pass through; rotated dot products depend only on the
+  position difference).
 * sage_varlen_forward: pinned (equal lengths reproduce the batched forward;
   a sequence's rows do not depend on its neighbours; empty sequences).
 """
-from .quant import (widen, quant_rows, quantize_q, write_kv_cache, sage_quantize,
+from .quant import (widen, quant_rows, quantize_q, write_kv_cache, write_kv_values, sage_quantize,
                     gather_kv)
+from .rope import apply_rope, rope_quantize_q, rope_write_kv_cache
 from .attention import (paged_qk_int32, paged_decode, paged_decode_split,
                         chunked_prefill, dense_sage_attention, attention_fp64,
                         default_scale, sage_smooth_v, sage_lse_correction, sage_forward,
                         sage_varlen_forward)
 
 __all__ = [
-    "widen", "quant_rows", "quantize_q", "write_kv_cache", "sage_quantize", "gather_kv",
+    "widen", "quant_rows", "quantize_q", "write_kv_cache", "write_kv_values", "sage_quantize", "gather_kv",
+    "apply_rope", "rope_quantize_q", "rope_write_kv_cache",
     "paged_qk_int32", "paged_decode", "paged_decode_split", "chunked_prefill",
     "dense_sage_attention", "attention_fp64", "default_scale",
     "sage_smooth_v", "sage_lse_correction", "sage_forward", "sage_varlen_forward",

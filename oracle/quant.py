@@ -77,8 +77,15 @@ def write_kv_cache(k_bits, v_bits, dtype, slot_mapping, num_blocks, v_int8=False
     skipped. Slots must be distinct. ``caches`` (a dict returned by an earlier
     call) is updated in place; otherwise zero-filled caches are created.
     """
-    k_bits = np.asarray(k_bits, np.uint16)
-    T, H, d = k_bits.shape
+    return write_kv_values(widen(np.asarray(k_bits, np.uint16), dtype), v_bits, dtype, slot_mapping, num_blocks,
+                           v_int8=v_int8, caches=caches)
+
+
+def write_kv_values(k_vals, v_bits, dtype, slot_mapping, num_blocks, v_int8=False, caches=None):
+    """write_kv_cache from fp32 K values (the 16-bit inputs widened, or
+    values computed from them, such as rotated keys)."""
+    k_vals = np.asarray(k_vals, np.float32)
+    T, H, d = k_vals.shape
     assert d % 16 == 0
     if caches is None:
         caches = {
@@ -90,7 +97,7 @@ def write_kv_cache(k_bits, v_bits, dtype, slot_mapping, num_blocks, v_int8=False
     slots = np.asarray(slot_mapping, np.int64)
     keep = slots >= 0
     blk, off = slots[keep] // BLOCK, slots[keep] % BLOCK
-    kq, ks = quant_rows(widen(k_bits[keep], dtype))                 # [T', H, d], [T', H]
+    kq, ks = quant_rows(k_vals[keep])                               # [T', H, d], [T', H]
     caches["k_cache"][blk, :, :, off, :] = kq.reshape(-1, H, d // 16, 16)
     caches["k_scale"][blk, :, off] = ks
     v_sel = np.asarray(v_bits, np.uint16)[keep]

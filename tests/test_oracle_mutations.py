@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.attention as oa
 import oracle.quant as oq
+import oracle.rope as orope
 import tests.test_oracle_pins as pins
 
 
@@ -28,6 +29,8 @@ def _plant(monkeypatch, module, fname, old, new):
     monkeypatch.setattr(module, fname, m)
     if module is oq and hasattr(oa, fname):
         monkeypatch.setattr(oa, fname, m)
+    if module is oq and hasattr(orope, fname):
+        monkeypatch.setattr(orope, fname, m)
     if hasattr(oracle, fname):
         monkeypatch.setattr(oracle, fname, m)
 
@@ -48,9 +51,9 @@ MUTATIONS = [
      pins.test_quant_properties, ()),
     ("scale_reciprocal_multiply", oq, "quant_rows", "r = (x / denom)",
      "r = (x * (np.float32(1.0) / denom))", pins.test_quant_near_ties_against_fp64_quotient, ()),
-    ("k_scale_wrong_slot", oq, "write_kv_cache", 'caches["k_scale"][blk, :, off] = ks',
+    ("k_scale_wrong_slot", oq, "write_kv_values", 'caches["k_scale"][blk, :, off] = ks',
      'caches["k_scale"][blk, :, (off + 1) % BLOCK] = ks', pins.test_cache_layout_elementwise, (False,)),
-    ("v_not_transposed", oq, "write_kv_cache", 'caches["v_cache"][blk, :, :, off] = v_sel',
+    ("v_not_transposed", oq, "write_kv_values", 'caches["v_cache"][blk, :, :, off] = v_sel',
      'caches["v_cache"][blk, :, :, off] = v_sel[:, :, ::-1]', pins.test_cache_layout_elementwise, (False,)),
     ("gather_skips_token_chunk_swap", oq, "gather_kv", ".transpose(0, 2, 1, 3)", "",
      pins.test_qk_brute_force_int64, (33,)),
@@ -108,6 +111,22 @@ MUTATIONS = [
     ("mean_over_all_sequences", oq, "sage_quantize", "total = k.astype(np.float64).sum(axis=1)",
      "total = k.astype(np.float64).sum(axis=1).mean(axis=0, keepdims=True) + 0 * k[:, 0]",
      pins.test_varlen_equal_lengths_is_the_batched_forward, (False,)),
+    ("rope_sign", orope, "apply_rope", "- (b * s).astype(np.float32)", "+ (b * s).astype(np.float32)",
+     pins.test_rope_pairs_rotate_as_complex_numbers, (True,)),
+    ("rope_cos_sin_swapped", orope, "apply_rope", "c, s = cs[:, None, :half], cs[:, None, half:rot_dim]",
+     "s, c = cs[:, None, :half], cs[:, None, half:rot_dim]", pins.test_rope_position_zero_is_identity, (True,)),
+    ("rope_pairs_adjacent_for_neox", orope, "_pairs", "return np.arange(half), np.arange(half, rot_dim)",
+     "return np.arange(0, rot_dim, 2), np.arange(1, rot_dim, 2)", pins.test_rope_interleaved_is_half_pairing_of_permuted_channels,
+     ()),
+    ("rope_drops_pass_through", orope, "apply_rope", "out = x.copy()", "out = np.zeros_like(x)",
+     pins.test_rope_pairs_rotate_as_complex_numbers, (False,)),
+    ("rope_frequency_of_pair_reversed", orope, "apply_rope", "c, s = cs[:, None, :half], cs[:, None, half:rot_dim]",
+     "c, s = cs[:, None, :half][..., ::-1], cs[:, None, half:rot_dim][..., ::-1]",
+     pins.test_rope_pairs_rotate_as_complex_numbers, (True,)),
+    ("rope_positions_off_by_one", orope, "apply_rope", "[np.asarray(positions, np.int64)]",
+     "[np.maximum(np.asarray(positions, np.int64) - 1, 0)]", pins.test_rope_pairs_rotate_as_complex_numbers, (False,)),
+    ("rope_cache_unrotated", orope, "rope_write_kv_cache", "k_rot = apply_rope(k_bits, dtype, positions, cos_sin, rot_dim, neox)",
+     "k_rot = widen(k_bits, dtype)", pins.test_rope_cache_write_holds_rotated_keys, ()),
 ]
 
 

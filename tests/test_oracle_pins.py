@@ -12,7 +12,7 @@ from scipy.special import softmax as sp_softmax
 import oracle
 from oracle import quant as oq
 from workloads import (PagedSpec, DenseSpec, VarlenSpec, paged_inputs, dense_inputs, dense_zero_scale_inputs,
-                       varlen_inputs, to_bf16_bits, to_f16_bits)
+                       varlen_inputs, rope_table, to_bf16_bits, to_f16_bits)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -642,3 +642,84 @@ def test_attention_fp64_matches_scipy():
     q, k, v = rng.standard_normal((3, 20, 16))
     got = oracle.attention_fp64(q, k, v, 0.25)
     np.testing.assert_allclose(got, sp_softmax(q @ k.T * 0.25, axis=1) @ v, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# rotary embedding in the producer
+
+
+def _rope_x(T=6, H=3, d=64, seed=91, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return to_bf16_bits(rng.standard_normal((T, H, d)).astype(np.float32) * np.float32(scale))
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_rope_position_zero_is_identity(neox):
+    x = _rope_x()
+    tab = rope_table(16, 64)
+    np.testing.assert_array_equal(oracle.apply_rope(x, "bf16", np.zeros(6, np.int64), tab, 64, neox),
+                                  oq.widen(x, "bf16"))
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_rope_pairs_rotate_as_complex_numbers(neox):
+    """Each channel pair (a, b) with frequency i becomes (a + ib) e^(i theta)
+    (complex128 product; fp32 rounding bound), channels past rot_dim are
+    untouched (partial rotary, 32 of 64)."""
+    x = _rope_x(T=8)
+    tab = rope_table(5000, 32)
+    pos = np.array([0, 1, 2, 17, 100, 999, 4095, 4999])
+    got = oracle.apply_rope(x, "bf16", pos, tab, 32, neox)
+    xv = oq.widen(x, "bf16").astype(np.float64)
+    ia = np.arange(16) if neox else np.arange(0, 32, 2)
+    ib = ia + 16 if neox else ia + 1
+    z = (xv[..., ia] + 1j * xv[..., ib]) * (tab[pos, :16].astype(np.float64) + 1j * tab[pos, 16:].astype(np.float64))[:, None, :]
+    bound = 2.0 ** -22 * (np.abs(xv[..., ia]) + np.abs(xv[..., ib]))
+    assert np.all(np.abs(got[..., ia] - z.real) <= bound)
+    assert np.all(np.abs(got[..., ib] - z.imag) <= bound)
+    np.testing.assert_array_equal(got[..., 32:], oq.widen(x, "bf16")[..., 32:])
+
+
+def test_rope_interleaved_is_half_pairing_of_permuted_channels():
+    x = _rope_x()
+    tab = rope_table(300, 64)
+    pos = np.array([3, 5, 8, 13, 21, 299])
+    perm = np.concatenate([np.arange(0, 64, 2), np.arange(1, 64, 2)])   # interleaved -> halves
+    a = oracle.apply_rope(x, "bf16", pos, tab, 64, neox=False)
+    b = oracle.apply_rope(x[..., perm], "bf16", pos, tab, 64, neox=True)
+    np.testing.assert_array_equal(a[..., perm], b)
+
+
+@pytest.mark.parametrize("neox", [True, False])
+def test_rope_dot_products_depend_on_position_difference(neox):
+    q, k = _rope_x(T=1, H=1, seed=5), _rope_x(T=1, H=1, seed=6)
+    tab = rope_table(4096, 64, base=1e4)
+    dots = []
+    for m, n in [(40, 10), (47, 17), (3030, 3000)]:
+        qr = oracle.apply_rope(q, "bf16", [m], tab, 64, neox).astype(np.float64)
+        kr = oracle.apply_rope(k, "bf16", [n], tab, 64, neox).astype(np.float64)
+        dots.append(float(np.sum(qr * kr)))
+    np.testing.assert_allclose(dots[1:], dots[0], rtol=2e-5, atol=2e-5)
+    unrot = float(np.sum(oq.widen(q, "bf16").astype(np.float64) * oq.widen(k, "bf16")))
+    assert abs(dots[0] - unrot) > 1e-3                       # the rotation does change it
+
+
+def test_rope_cache_write_holds_rotated_keys():
+    """The K cache written by the rotary producer dequantizes to the rotated
+    keys within half a quantization step; at position 0 it is the plain
+    write byte for byte."""
+    k, v = _rope_x(T=20, H=2, seed=7, scale=3.0), _rope_x(T=20, H=2, seed=8)
+    tab = rope_table(64, 64)
+    slots = np.arange(20) + 5
+    pos = np.arange(20) * 3 + 1
+    c = oracle.rope_write_kv_cache(k, v, "bf16", slots, 4, pos, tab, 64, neox=True)
+    kq, sk, _ = oracle.gather_kv(c, np.array([0, 1, 2, 3]), 25, 1)
+    rot = oracle.apply_rope(k, "bf16", pos, tab, 64, True)[:, 1]
+    err = np.abs(kq[5:].astype(np.float64) * sk[5:, None] - rot)
+    assert np.all(err <= sk[5:, None] * 0.5 * (1 + 1e-6))
+    assert np.max(np.abs(rot - oq.widen(k, "bf16")[:, 1])) > 10 * np.max(sk)   # and rotation is visible
+    c0 = oracle.rope_write_kv_cache(k, v, "bf16", slots, 4, np.zeros(20, np.int64), tab, 64)
+    c1 = oracle.write_kv_cache(k, v, "bf16", slots, 4)
+    for key in ("k_cache", "k_scale", "v_cache"):
+        np.testing.assert_array_equal(c0[key], c1[key])
+

@@ -260,6 +260,17 @@ def varlen_inputs(spec: VarlenSpec) -> VarlenInputs:
     return VarlenInputs(spec, cat(qs, Hq), cat(ks, Hkv), cat(vs, Hkv), cu(spec.seq_q), cu(spec.seq_k))
 
 
+def rope_table(max_position: int, rot_dim: int, base: float = 1.0e6) -> np.ndarray:
+    """Rotary-embedding input table [max_position, rot_dim] fp32: cos(p * w_i)
+    in columns [0, rot_dim/2), sin(p * w_i) in [rot_dim/2, rot_dim), with
+    w_i = base^(-2i / rot_dim), evaluated in fp64 and rounded to fp32. The
+    pages give no rotary parameters; base 1e6 is a stand-in."""
+    half = rot_dim // 2
+    w = base ** (-np.arange(half, dtype=np.float64) * 2.0 / rot_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * w[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
 def dense_zero_scale_inputs(N: int = 200, d: int = 64, dtype: str = "f16") -> DenseInputs:
     """Degenerate dense inputs: KV head 0 holds the same key at every position
     (smoothing then leaves all-zero keys, so every key-block scale is 0) and
