@@ -115,8 +115,8 @@ qa_status_t qa_write_kv_cache(const void* k, const void* v, qa_dtype_t dtype,
  * qa_quantize_q) and write the new K/V tokens into the paged cache (exactly
  * as qa_write_kv_cache) in a single launch. [QK-MMAC] §4: the query is
  * quantized once, inside the producer that also writes the KV cache, and
- * every split-K segment reuses it (rotary embedding is not part of this
- * library). Arguments are those of the two calls above; either part may be
+ * every split-K segment reuses it (qa_rope_quantize_q_write_kv adds the
+ * rotary embedding). Arguments are those of the two calls above; either part may be
  * empty (num_q_tokens == 0 or num_kv_tokens == 0). q, k and v share `dtype`.
  */
 qa_status_t qa_quantize_q_write_kv(const void* q, int64_t num_q_tokens, int32_t num_q_heads,
@@ -127,6 +127,48 @@ qa_status_t qa_quantize_q_write_kv(const void* q, int64_t num_q_tokens, int32_t 
                                    int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale,
                                    int8_t* k_cache, float* k_scale, void* v_cache,
                                    qa_dtype_t v_cache_dtype, float* v_scale, qa_stream_t stream);
+
+/*
+ * Rotary position embedding applied by the producer ahead of quantization
+ * ([QK-MMAC] §4: the producer that quantizes the query is the RoPE/KV
+ * producer). The pages give no rotary parameters; the table is an input.
+ *   positions  device int64 [tokens]: position of token t (query row t and
+ *              K row t use the same entry); each < the table's row count
+ *              (device data: not checked)
+ *   cos_sin    device fp32 [max_position, rot_dim]: cos(p w_i) in column i,
+ *              sin(p w_i) in column rot_dim/2 + i
+ *   rot_dim    rotated channels: even, 2 <= rot_dim <= head_dim; channels
+ *              from rot_dim on pass through (partial rotary)
+ *   neox       nonzero: pair i is channels (i, i + rot_dim/2); zero: (2i, 2i+1)
+ * Pair (a, b) becomes (fl32(fl32(a cos) - fl32(b sin)), fl32(fl32(b cos) +
+ * fl32(a sin))) in fp32 from the widened 16-bit inputs (no fused
+ * multiply-add), and those fp32 values are quantized (no rounding back to
+ * 16 bits). V is not rotated.
+ */
+typedef struct {
+  const int64_t* positions;
+  const float* cos_sin;
+  int32_t rot_dim;
+  int32_t neox;
+} qa_rope_t;
+
+/*
+ * qa_quantize_q_write_kv with the rotary embedding of `rope` applied to the
+ * query rows and K rows before they are quantized: RoPE, query quantization
+ * and the KV-cache write in one launch. Same arguments and errors, plus
+ * QA_ERR_INVALID_ARG for a NULL rope, table or positions, or a rot_dim that is
+ * odd, < 2 or > head_dim.
+ */
+qa_status_t qa_rope_quantize_q_write_kv(const qa_rope_t* rope, const void* q, int64_t num_q_tokens,
+                                        int32_t num_q_heads, int64_t q_stride_token,
+                                        int64_t q_stride_head, const void* k, const void* v,
+                                        int64_t num_kv_tokens, int32_t num_kv_heads,
+                                        int64_t kv_stride_token, int64_t kv_stride_head,
+                                        const int64_t* slot_mapping, qa_dtype_t dtype,
+                                        int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                                        int8_t* q_i8, float* q_scale, int8_t* k_cache,
+                                        float* k_scale, void* v_cache, qa_dtype_t v_cache_dtype,
+                                        float* v_scale, qa_stream_t stream);
 
 /* Shape and options of a decode call (one query token per sequence). */
 typedef struct {

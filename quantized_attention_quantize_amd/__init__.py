@@ -54,6 +54,10 @@ class DenseParams(ctypes.Structure):
                 ("is_causal", _i32), ("softmax_scale", _f32), ("out_dtype", ctypes.c_int)]
 
 
+class RopeParams(ctypes.Structure):
+    _fields_ = [("positions", _c_void_p), ("cos_sin", _c_void_p), ("rot_dim", _i32), ("neox", _i32)]
+
+
 class VarlenParams(ctypes.Structure):
     _fields_ = [("batch", _i32), ("total_q", _i64), ("total_k", _i64), ("max_seqlen_q", _i32),
                 ("max_seqlen_k", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
@@ -84,6 +88,10 @@ _SIGS = {
                                                _i32, _i64, _i64, _c_void_p, ctypes.c_int, _i32, _i64, _i32,
                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                ctypes.c_int, _c_void_p, _c_void_p]),
+    "qa_rope_quantize_q_write_kv": (ctypes.c_int, [_P(RopeParams), _c_void_p, _i64, _i32, _i64, _i64, _c_void_p,
+                                                    _c_void_p, _i64, _i32, _i64, _i64, _c_void_p, ctypes.c_int,
+                                                    _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                    _c_void_p, ctypes.c_int, _c_void_p, _c_void_p]),
     "qa_paged_decode_num_splits": (_i32, [_P(DecodeParams)]),
     "qa_paged_decode_step": (ctypes.c_int, _STEP_ARGS),
     "qa_paged_decode_step_partials": (ctypes.c_int, _STEP_ARGS),
@@ -191,9 +199,11 @@ def write_kv_cache(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale=None):
 
 
 def quantize_q_write_kv(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale=None, q_i8=None,
-                        q_scale=None):
+                        q_scale=None, rope=None):
     """Fused producer: quantize q [Tq, Hq, d] and write k/v [Tk, Hkv, d] into the
-    cache in one launch. Returns (q_i8, q_scale)."""
+    cache in one launch. With rope = (positions int64 [T], cos_sin fp32
+    [max_position, rot_dim], rot_dim, neox), q and k are rotated first (one
+    launch for all three). Returns (q_i8, q_scale)."""
     _require_cuda(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale)
     Tq, Hq, d = q.shape
     Tk, Hkv, _ = k.shape
@@ -203,11 +213,18 @@ def quantize_q_write_kv(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scal
         q_scale = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
     if k.stride() != v.stride() or k.stride(2) != 1 or q.stride(2) != 1:
         raise ValueError("k and v must share strides; innermost dims must be contiguous")
-    _check(lib.qa_quantize_q_write_kv(_ptr(q), Tq, Hq, q.stride(0), q.stride(1), _ptr(k), _ptr(v), Tk, Hkv,
-                                      k.stride(0), k.stride(1), _ptr(slot_mapping), _dt(q.dtype), d,
-                                      k_cache.shape[0], 16, _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
-                                      _ptr(k_scale), _ptr(v_cache), _dt(v_cache.dtype), _ptr(v_scale),
-                                      _stream()))
+    args = (_ptr(q), Tq, Hq, q.stride(0), q.stride(1), _ptr(k), _ptr(v), Tk, Hkv, k.stride(0), k.stride(1),
+            _ptr(slot_mapping), _dt(q.dtype), d, k_cache.shape[0], 16, _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
+            _ptr(k_scale), _ptr(v_cache), _dt(v_cache.dtype), _ptr(v_scale), _stream())
+    if rope is None:
+        _check(lib.qa_quantize_q_write_kv(*args))
+    else:
+        positions, cos_sin, rot_dim, neox = rope
+        _require_cuda(positions, cos_sin)
+        if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous():
+            raise ValueError("positions must be int64 and cos_sin contiguous fp32")
+        rp = RopeParams(_ptr(positions), _ptr(cos_sin), rot_dim, int(bool(neox)))
+        _check(lib.qa_rope_quantize_q_write_kv(ctypes.byref(rp), *args))
     return q_i8, q_scale
 
 

@@ -100,6 +100,14 @@ qa_status_t check_tokens(const qa_decode_params_t* p, int32_t T) {
   return QA_OK;
 }
 
+qa_status_t producer_impl(const qa_rope_t* rope, const void* q, int64_t num_q_tokens, int32_t num_q_heads,
+                          int64_t q_stride_token, int64_t q_stride_head, const void* k, const void* v,
+                          int64_t num_kv_tokens, int32_t num_kv_heads, int64_t kv_stride_token,
+                          int64_t kv_stride_head, const int64_t* slot_mapping, qa_dtype_t dtype, int32_t head_dim,
+                          int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale, int8_t* k_cache,
+                          float* k_scale, void* v_cache, qa_dtype_t v_cache_dtype, float* v_scale,
+                          qa_stream_t stream);
+
 qa_status_t check_dense(const qa_dense_params_t* p) {
   QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
   QA_REQUIRE(p->batch >= 0 && p->seq_q >= 0 && p->seq_k >= 0 && p->num_q_heads > 0 &&
@@ -336,6 +344,39 @@ qa_status_t qa_quantize_q_write_kv(const void* q, int64_t num_q_tokens, int32_t 
                                    int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale,
                                    int8_t* k_cache, float* k_scale, void* v_cache,
                                    qa_dtype_t v_cache_dtype, float* v_scale, qa_stream_t stream) {
+  return producer_impl(nullptr, q, num_q_tokens, num_q_heads, q_stride_token, q_stride_head, k, v, num_kv_tokens,
+                       num_kv_heads, kv_stride_token, kv_stride_head, slot_mapping, dtype, head_dim, num_blocks,
+                       block_size, q_i8, q_scale, k_cache, k_scale, v_cache, v_cache_dtype, v_scale, stream);
+}
+
+qa_status_t qa_rope_quantize_q_write_kv(const qa_rope_t* rope, const void* q, int64_t num_q_tokens,
+                                        int32_t num_q_heads, int64_t q_stride_token, int64_t q_stride_head,
+                                        const void* k, const void* v, int64_t num_kv_tokens, int32_t num_kv_heads,
+                                        int64_t kv_stride_token, int64_t kv_stride_head,
+                                        const int64_t* slot_mapping, qa_dtype_t dtype, int32_t head_dim,
+                                        int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale,
+                                        int8_t* k_cache, float* k_scale, void* v_cache, qa_dtype_t v_cache_dtype,
+                                        float* v_scale, qa_stream_t stream) {
+  QA_REQUIRE(rope != nullptr && rope->positions != nullptr && rope->cos_sin != nullptr, QA_ERR_INVALID_ARG,
+             "rope, its positions and its table must be given");
+  QA_REQUIRE(rope->rot_dim >= 2 && rope->rot_dim % 2 == 0 && rope->rot_dim <= head_dim, QA_ERR_INVALID_ARG,
+             "rot_dim %d must be even and in [2, head_dim]", rope->rot_dim);
+  return producer_impl(rope, q, num_q_tokens, num_q_heads, q_stride_token, q_stride_head, k, v, num_kv_tokens,
+                       num_kv_heads, kv_stride_token, kv_stride_head, slot_mapping, dtype, head_dim, num_blocks,
+                       block_size, q_i8, q_scale, k_cache, k_scale, v_cache, v_cache_dtype, v_scale, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+qa_status_t producer_impl(const qa_rope_t* rope, const void* q, int64_t num_q_tokens, int32_t num_q_heads,
+                          int64_t q_stride_token, int64_t q_stride_head, const void* k, const void* v,
+                          int64_t num_kv_tokens, int32_t num_kv_heads, int64_t kv_stride_token,
+                          int64_t kv_stride_head, const int64_t* slot_mapping, qa_dtype_t dtype, int32_t head_dim,
+                          int64_t num_blocks, int32_t block_size, int8_t* q_i8, float* q_scale, int8_t* k_cache,
+                          float* k_scale, void* v_cache, qa_dtype_t v_cache_dtype, float* v_scale,
+                          qa_stream_t stream) {
   QA_REQUIRE(num_q_tokens >= 0 && num_kv_tokens >= 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 &&
                  num_blocks > 0,
              QA_ERR_INVALID_ARG, "bad shape");
@@ -367,8 +408,13 @@ qa_status_t qa_quantize_q_write_kv(const void* q, int64_t num_q_tokens, int32_t 
   a.q_st = q_stride_token; a.q_sh = q_stride_head; a.kv_st = kv_stride_token; a.kv_sh = kv_stride_head;
   a.q_i8 = q_i8; a.q_scale = q_scale; a.k_cache = k_cache; a.k_scale = k_scale; a.v_cache = v_cache;
   a.v_scale = v_scale;
-  return hip_status(qa::launch_producer(a, (hipStream_t)stream), "qa_quantize_q_write_kv launch");
+  if (rope != nullptr) a.rope = qa::Rope{rope->positions, rope->cos_sin, rope->rot_dim, rope->neox != 0};
+  return hip_status(qa::launch_producer(a, (hipStream_t)stream), "producer launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p) {
   if (check_decode(p) != QA_OK) return -1;

@@ -20,6 +20,17 @@ hipError_t launch_write_kv_cache(const void* k, const void* v, bool bf16, int64_
                                  float* k_scale, void* v_cache, bool v_int8, float* v_scale,
                                  hipStream_t st);
 
+// Rotary embedding applied ahead of quantization (pos == nullptr: none).
+// Table row p holds cos(p w_i) at i and sin(p w_i) at rot/2 + i; neox pairs
+// channel i with i + rot/2, otherwise 2i with 2i + 1 (pair i uses w_i);
+// channels from rot on pass through.
+struct Rope {
+  const int64_t* pos;   // [tokens] position of each token
+  const float* cs;      // [max_position, rot] fp32
+  int32_t rot;
+  bool neox;
+};
+
 struct ProducerArgs {
   const void* q;           // [q_tokens, Hq, D] rows at q + t*q_st + h*q_sh
   const void* k;           // [kv_tokens, Hkv, D] rows at k/v + t*kv_st + h*kv_sh
@@ -35,6 +46,7 @@ struct ProducerArgs {
   float* k_scale;
   void* v_cache;
   float* v_scale;
+  Rope rope;               // rotates query rows and K rows (token t at rope.pos[t])
 };
 hipError_t launch_producer(const ProducerArgs& a, hipStream_t st);
 

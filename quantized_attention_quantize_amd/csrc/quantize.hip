@@ -34,6 +34,31 @@ __device__ __forceinline__ void store_codes(int8_t* p, uint32_t packed) {
   else *reinterpret_cast<uint8_t*>(p) = (uint8_t)packed;
 }
 
+// Rotate the E channels ch .. ch+E-1 of one row (values in v, the row's 16-bit
+// inputs at `row`) by the table row of position p. Each output is
+// fl32(fl32(x cos) -+ fl32(y sin)) with y the pair partner: no fused
+// multiply-add, so the rotated values (and the codes taken from them) are
+// the same on every implementation that rounds each operation.
+template <int E, bool BF16>
+__device__ __forceinline__ void rope_lane(const uint16_t* __restrict__ row, int ch, float (&v)[E], const Rope& r,
+                                          int64_t p) {
+#pragma clang fp contract(off)
+  const int half = r.rot >> 1;
+  const float* cs = r.cs + p * r.rot;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = ch + e;
+    if (c >= r.rot) continue;
+    const bool first = r.neox ? c < half : (c & 1) == 0;
+    const int i = r.neox ? (first ? c : c - half) : c >> 1;
+    const int pc = r.neox ? (first ? c + half : c - half) : c ^ 1;
+    const float y = half_to_f32<BF16>(row[pc]);
+    const float xc = v[e] * cs[i];
+    const float ys = y * cs[half + i];
+    v[e] = first ? xc - ys : xc + ys;
+  }
+}
+
 // Quantize E values held by one lane against the wave-wide scale of its row.
 template <int E>
 __device__ __forceinline__ uint32_t quant_lane(const float (&v)[E], float amax, float s) {
@@ -50,12 +75,14 @@ __device__ __forceinline__ uint32_t quant_lane(const float (&v)[E], float amax, 
 template <int D, bool BF16>
 __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ x, int64_t row, int32_t H, int64_t st,
                                           int64_t sh, int8_t* __restrict__ q, float* __restrict__ scale,
-                                          int lane) {
+                                          int lane, const Rope& rope = Rope{}) {
   constexpr int E = D / 64;
   const int64_t t = row / H;
   const int h = (int)(row - t * H);
   float v[E];
-  load_halves<E, BF16>(x + t * st + (int64_t)h * sh + lane * E, v);
+  const uint16_t* src = x + t * st + (int64_t)h * sh;
+  load_halves<E, BF16>(src + lane * E, v);
+  if (rope.pos != nullptr) rope_lane<E, BF16>(src, lane * E, v, rope, rope.pos[t]);
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
@@ -72,7 +99,7 @@ __device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, con
                                              int64_t row, int32_t H, int64_t st, int64_t sh,
                                              const int64_t* __restrict__ slots, int8_t* __restrict__ kc,
                                              float* __restrict__ ks, void* __restrict__ vc,
-                                             float* __restrict__ vs, int lane) {
+                                             float* __restrict__ vs, int lane, const Rope& rope = Rope{}) {
   constexpr int E = D / 64;
   const int64_t t = row / H;
   const int h = (int)(row - t * H);
@@ -85,6 +112,7 @@ __device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, con
 
   float kv[E];
   load_halves<E, BF16>(k + src, kv);
+  if (rope.pos != nullptr) rope_lane<E, BF16>(k + (src - lane * E), lane * E, kv, rope, rope.pos[t]);
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(kv[e]));
@@ -145,12 +173,12 @@ __global__ __launch_bounds__(256) void k_producer(ProducerArgs a, int64_t qblock
   if ((int64_t)blockIdx.x < qblocks) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row < a.q_rows)
-      quant_row<D, BF16>((const uint16_t*)a.q, row, a.Hq, a.q_st, a.q_sh, a.q_i8, a.q_scale, lane);
+      quant_row<D, BF16>((const uint16_t*)a.q, row, a.Hq, a.q_st, a.q_sh, a.q_i8, a.q_scale, lane, a.rope);
   } else {
     const int64_t row = ((int64_t)blockIdx.x - qblocks) * 4 + (threadIdx.x >> 6);
     if (row < a.kv_rows)
       write_kv_row<D, BF16, V_I8>((const uint16_t*)a.k, (const uint16_t*)a.v, row, a.Hkv, a.kv_st, a.kv_sh,
-                                  a.slots, a.k_cache, a.k_scale, a.v_cache, a.v_scale, lane);
+                                  a.slots, a.k_cache, a.k_scale, a.v_cache, a.v_scale, lane, a.rope);
   }
 }
 

@@ -219,6 +219,22 @@ def test_dense_varlen_validation(qa):
     assert call(0, None, None, None, None, None) == qa.QA_OK                              # nothing to do
 
 
+def test_rope_producer_validation(qa):
+    L = qa.lib
+    args = lambda d: (FAKE, 4, 8, 8 * d, d, FAKE, FAKE, 4, 2, 2 * d, d, FAKE, qa.QA_DT_BF16, d, 10, 16,
+                      FAKE, FAKE, FAKE, FAKE, FAKE, qa.QA_DT_BF16, None, None)
+    r = qa.RopeParams(FAKE, FAKE, 64, 1)
+    for rot in (0, 63, 130):
+        r.rot_dim = rot
+        assert L.qa_rope_quantize_q_write_kv(ctypes.byref(r), *args(128)) == qa.QA_ERR_INVALID_ARG
+        assert b"rot_dim" in L.qa_last_error()
+    r.rot_dim, r.positions = 64, None
+    assert L.qa_rope_quantize_q_write_kv(ctypes.byref(r), *args(128)) == qa.QA_ERR_INVALID_ARG
+    assert L.qa_rope_quantize_q_write_kv(None, *args(128)) == qa.QA_ERR_INVALID_ARG
+    r.positions = FAKE
+    assert L.qa_rope_quantize_q_write_kv(ctypes.byref(r), *args(96)) == qa.QA_ERR_UNSUPPORTED   # head_dim 96
+
+
 def test_last_error_is_thread_local(qa):
     import threading
     L = qa.lib

@@ -202,3 +202,49 @@ def test_fused_producer_bit_exact(qa, v_int8):
         assert np.array_equal(vs.cpu().numpy(), want["v_scale"])
     else:
         assert np.array_equal(vc.cpu().view(torch.int16).numpy().view(np.uint16), want["v_cache"])
+
+
+ROPE_CASES = [
+    # (d, rot_dim, neox, dtype, v_int8)
+    (256, 64, True, "bf16", False),     # partial rotary, as in models that rotate a quarter of the head
+    (256, 256, False, "bf16", True),
+    (128, 128, True, "f16", False),
+    (64, 32, False, "f16", True),
+    (64, 64, True, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: f"d{c[0]}_rot{c[1]}_{'neox' if c[2] else 'gptj'}_{c[3]}_{'i8V' if c[4] else '16V'}")
+def test_rope_producer_bit_exact(qa, case):
+    """RoPE + query quantization + cache write in one launch: codes, scales
+    and every cache byte equal the oracle's (rotation in fp32 with one
+    rounding per operation, then the row rule)."""
+    from workloads import rope_table
+    d, rot, neox, dt, v_int8 = case
+    say(f"rope producer {case}")
+    T, Hq, Hkv, nb = 37, 6, 2, 8
+    q = _q_bits(T, Hq, d, dt, 301 + d)
+    k = _q_bits(T, Hkv, d, dt, 302 + d)
+    v = _q_bits(T, Hkv, d, dt, 303 + d)
+    rng = np.random.default_rng(d + rot)
+    pos = rng.integers(0, 4096, T).astype(np.int64)
+    pos[:3] = [0, 1, 4095]
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[5] = -1                                      # skipped token
+    tab = rope_table(4096, rot)
+    kc, ks, vc, vs = qa.alloc_kv_cache(nb, Hkv, d, torch.int8 if v_int8 else (torch.bfloat16 if dt == "bf16" else torch.float16))
+    q8, qs = qa.quantize_q_write_kv(dev_bits(q, dt), dev_bits(k, dt), dev_bits(v, dt), torch.from_numpy(slots).cuda(),
+                                    kc, ks, vc, vs, rope=(torch.from_numpy(pos).cuda(), torch.from_numpy(tab).cuda(),
+                                                          rot, neox))
+    torch.cuda.synchronize()
+    w8, wsc = oracle.rope_quantize_q(q, dt, pos, tab, rot, neox)
+    assert np.array_equal(q8.cpu().numpy(), w8), "query codes"
+    assert np.array_equal(qs.cpu().numpy(), wsc), "query scales"
+    want = oracle.rope_write_kv_cache(k, v, dt, slots, nb, pos, tab, rot, neox, v_int8=v_int8)
+    assert np.array_equal(kc.cpu().numpy(), want["k_cache"]), "K cache"
+    assert np.array_equal(ks.cpu().numpy(), want["k_scale"]), "K scales"
+    if v_int8:
+        assert np.array_equal(vc.cpu().numpy(), want["v_cache"])
+        assert np.array_equal(vs.cpu().numpy(), want["v_scale"])
+    else:
+        assert np.array_equal(vc.cpu().view(torch.int16).numpy().view(np.uint16), want["v_cache"])
