@@ -203,6 +203,32 @@ def run_decode(args, torch, qa, W):
 
     per = 10
     kern_ms = batches(partials, max(1, K // per), per)
+
+    rope_ms = None
+    if not args.no_extras:
+        # the same step with rotary embedding in the split kernel (a quarter
+        # of the head rotated, half pairing; positions = context - 1)
+        from workloads import rope_table
+        tab = torch.from_numpy(rope_table(args.context, 64)).to(dev)
+        pos = (lens - 1).to(torch.int64)
+        rp = qa.RopeParams(qa._ptr(pos), qa._ptr(tab), 64, 1)
+
+        def step_rope(i):
+            kc, ks, vc, vs = pools[i % len(pools)]
+            qa._check(L.qa_paged_decode_step_rope(
+                ctypes.byref(rp), ctypes.byref(p), qa._ptr(q), Hq * d, d, qa._ptr(k_new), qa._ptr(v_new), Hkv * d,
+                d, qa.QA_DT_BF16, qa._ptr(slot_new), qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), None, qa._ptr(tables),
+                qa._ptr(lens), qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
+        for i in range(W):
+            step_rope(i)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(K):
+            step_rope(i)
+        t1.record()
+        torch.cuda.synchronize()
+        rope_ms = t0.elapsed_time(t1) / K
+
     step(0)                            # the output checked against the oracle (cpu_baseline leg)
     torch.cuda.synchronize()
     out_host = out.cpu().numpy()
@@ -214,6 +240,7 @@ def run_decode(args, torch, qa, W):
         "kernel_ms_p10_p90": [float(np.percentile(kern_ms, 10)), float(np.percentile(kern_ms, 90))],
         "step_bytes": nbytes["step"],
         "splits": splits,
+        "rope_ms_per_step": rope_ms,
         "inp": inp,
         "out": out_host,
     }
@@ -520,7 +547,14 @@ def main():
         pk = run_practical_peaks(torch, r["step_bytes"], args.pools)
         res["practical_peak"] = pk
         res["roofline"]["frac_of_practical_stream"] = round(achieved / pk["stream_read_1GiB_GBps"], 4)
-        res["extra"] = {"decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
+        rms = r["rope_ms_per_step"]
+        res["extra"] = {"decode_step_rope": {
+                            "workload": "qwen27b decode step with rotary embedding in the split kernel (64 of 256 "
+                                        "channels rotated): rotate + quantize the query, rotate + write the new token, "
+                                        "split-K attention, combine",
+                            "ms": rms, "GBps": r["step_bytes"] / (rms * 1e-3) / 1e9,
+                            "frac_hbm_peak": r["step_bytes"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                        "decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
                         "chunked_prefill": run_prefill(torch, qa, 20),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True),

@@ -271,6 +271,25 @@ qa_status_t qa_paged_decode_step_partials(const qa_decode_params_t* p, const voi
                                           qa_stream_t stream);
 
 /*
+ * qa_paged_decode_step with the rotary embedding of `rope` (see qa_rope_t)
+ * applied to each sequence's query rows and new K row before they are
+ * quantized: rotary embedding, query quantization, the new token's cache
+ * write and split-K attention in one kernel ([QK-MMAC] §4), then the combine.
+ * rope->positions has one entry per sequence: the position of its new token.
+ * Bit-identical to qa_rope_quantize_q_write_kv + qa_paged_attention_decode.
+ * Errors as qa_paged_decode_step, plus QA_ERR_INVALID_ARG for a NULL rope,
+ * table or positions, or a rot_dim that is odd, < 2 or > head_dim.
+ */
+qa_status_t qa_paged_decode_step_rope(const qa_rope_t* rope, const qa_decode_params_t* p, const void* q,
+                                      int64_t q_stride_token, int64_t q_stride_head, const void* k,
+                                      const void* v, int64_t kv_stride_token, int64_t kv_stride_head,
+                                      qa_dtype_t dtype, const int64_t* slot_mapping, int8_t* k_cache,
+                                      float* k_scale, void* v_cache, float* v_scale,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      void* workspace, size_t workspace_bytes, void* out,
+                                      qa_stream_t stream);
+
+/*
  * The two phases of qa_paged_attention_decode as separate calls, for callers
  * that schedule (or time) them apart: _partials launches the split kernel
  * (with S = 1 it writes `out` directly and _combine does nothing); _combine

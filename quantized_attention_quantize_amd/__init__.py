@@ -94,6 +94,7 @@ _SIGS = {
                                                     _c_void_p, ctypes.c_int, _c_void_p, _c_void_p]),
     "qa_paged_decode_num_splits": (_i32, [_P(DecodeParams)]),
     "qa_paged_decode_step": (ctypes.c_int, _STEP_ARGS),
+    "qa_paged_decode_step_rope": (ctypes.c_int, [_P(RopeParams)] + _STEP_ARGS),
     "qa_paged_decode_step_partials": (ctypes.c_int, _STEP_ARGS),
     "qa_paged_decode_workspace_size": (_size, [_P(DecodeParams)]),
     "qa_paged_attention_decode": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_size, _c_void_p,
@@ -219,12 +220,7 @@ def quantize_q_write_kv(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scal
     if rope is None:
         _check(lib.qa_quantize_q_write_kv(*args))
     else:
-        positions, cos_sin, rot_dim, neox = rope
-        _require_cuda(positions, cos_sin)
-        if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous():
-            raise ValueError("positions must be int64 and cos_sin contiguous fp32")
-        rp = RopeParams(_ptr(positions), _ptr(cos_sin), rot_dim, int(bool(neox)))
-        _check(lib.qa_rope_quantize_q_write_kv(ctypes.byref(rp), *args))
+        _check(lib.qa_rope_quantize_q_write_kv(ctypes.byref(_rope_params(rope)), *args))
     return q_i8, q_scale
 
 
@@ -309,12 +305,22 @@ def paged_attention_decode_mt(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale,
     return out
 
 
+def _rope_params(rope):
+    positions, cos_sin, rot_dim, neox = rope
+    _require_cuda(positions, cos_sin)
+    if positions.dtype != torch.int64 or cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous():
+        raise ValueError("positions must be int64 and cos_sin contiguous fp32")
+    return RopeParams(_ptr(positions), _ptr(cos_sin), rot_dim, int(bool(neox)))
+
+
 def paged_decode_step(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
                       num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
-                      workspace=None, out=None):
+                      workspace=None, out=None, rope=None):
     """One decode step in one call: quantize q [num_seqs, Hq, d], write the new
     token's k/v [num_seqs, Hkv, d] at slot_mapping, and attend over the cache
-    (context_lens include the new token). Returns out [num_seqs, Hq, d]."""
+    (context_lens include the new token). With rope = (positions int64
+    [num_seqs], cos_sin, rot_dim, neox) q and k are rotated first, in the
+    same kernel. Returns out [num_seqs, Hq, d]."""
     _require_cuda(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens)
     S, Hq, d = q.shape
     Hkv = num_kv_heads or k_cache.shape[1]
@@ -326,10 +332,13 @@ def paged_decode_step(q, k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale,
         workspace = decode_workspace(p, q.device)
     if out is None:
         out = torch.empty((S, Hq, d), dtype=out_dtype, device=q.device)
-    _check(lib.qa_paged_decode_step(ctypes.byref(p), _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v),
-                                    k.stride(0), k.stride(1), _dt(q.dtype), _ptr(slot_mapping), _ptr(k_cache),
-                                    _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(block_tables),
-                                    _ptr(context_lens), _ptr(workspace), workspace.numel(), _ptr(out), _stream()))
+    args = (ctypes.byref(p), _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+            _dt(q.dtype), _ptr(slot_mapping), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+            _ptr(block_tables), _ptr(context_lens), _ptr(workspace), workspace.numel(), _ptr(out), _stream())
+    if rope is None:
+        _check(lib.qa_paged_decode_step(*args))
+    else:
+        _check(lib.qa_paged_decode_step_rope(ctypes.byref(_rope_params(rope)), *args))
     return out
 
 

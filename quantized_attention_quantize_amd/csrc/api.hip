@@ -477,9 +477,15 @@ qa_status_t decode_step(const qa_decode_params_t* p, const void* q, int64_t q_st
                         qa_dtype_t dtype, const int64_t* slot_mapping, int8_t* k_cache, float* k_scale,
                         void* v_cache, float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
                         void* workspace, size_t workspace_bytes, void* out, qa_stream_t stream,
-                        qa::DecodePhase phase, const char* what) {
+                        qa::DecodePhase phase, const char* what, const qa_rope_t* rope = nullptr) {
   qa_status_t st = check_decode(p);
   if (st != QA_OK) return st;
+  if (rope != nullptr) {
+    QA_REQUIRE(rope->positions != nullptr && rope->cos_sin != nullptr, QA_ERR_INVALID_ARG,
+               "rope positions and table must be given");
+    QA_REQUIRE(rope->rot_dim >= 2 && rope->rot_dim % 2 == 0 && rope->rot_dim <= p->head_dim, QA_ERR_INVALID_ARG,
+               "rot_dim %d must be even and in [2, head_dim]", rope->rot_dim);
+  }
   if (p->num_seqs == 0) return QA_OK;
   QA_REQUIRE(dtype == QA_DT_BF16 || dtype == QA_DT_F16, QA_ERR_UNSUPPORTED, "dtype must be BF16 or F16");
   QA_REQUIRE(p->v_cache_dtype == QA_DT_I8 || dtype == QA_DT_BF16, QA_ERR_UNSUPPORTED,
@@ -515,6 +521,7 @@ qa_status_t decode_step(const qa_decode_params_t* p, const void* q, int64_t q_st
   a.slots = slot_mapping; a.kc_w = k_cache; a.ks_w = k_scale; a.vc_w = v_cache; a.vs_w = v_scale;
   a.in_bf16 = dtype == QA_DT_BF16;
   a.tq = 1;
+  if (rope != nullptr) a.rope = qa::Rope{rope->positions, rope->cos_sin, rope->rot_dim, rope->neox != 0};
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }
 
@@ -529,6 +536,18 @@ qa_status_t qa_paged_decode_step(const qa_decode_params_t* p, const void* q, int
   return decode_step(p, q, q_stride_token, q_stride_head, k, v, kv_stride_token, kv_stride_head, dtype,
                      slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
                      workspace_bytes, out, stream, qa::DecodePhase::kBoth, "qa_paged_decode_step launch");
+}
+
+qa_status_t qa_paged_decode_step_rope(const qa_rope_t* rope, const qa_decode_params_t* p, const void* q,
+                                      int64_t q_stride_token, int64_t q_stride_head, const void* k, const void* v,
+                                      int64_t kv_stride_token, int64_t kv_stride_head, qa_dtype_t dtype,
+                                      const int64_t* slot_mapping, int8_t* k_cache, float* k_scale, void* v_cache,
+                                      float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                                      void* workspace, size_t workspace_bytes, void* out, qa_stream_t stream) {
+  QA_REQUIRE(rope != nullptr, QA_ERR_INVALID_ARG, "rope is NULL");
+  return decode_step(p, q, q_stride_token, q_stride_head, k, v, kv_stride_token, kv_stride_head, dtype,
+                     slot_mapping, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, workspace,
+                     workspace_bytes, out, stream, qa::DecodePhase::kBoth, "qa_paged_decode_step_rope launch", rope);
 }
 
 qa_status_t qa_paged_decode_step_partials(const qa_decode_params_t* p, const void* q, int64_t q_stride_token,

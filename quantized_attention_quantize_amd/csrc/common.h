@@ -148,4 +148,30 @@ __device__ __forceinline__ int quant_code(float x, float s) {
 
 __device__ __forceinline__ float quant_scale(float amax) { return __fdiv_rn(amax, 127.0f); }
 
+// Rotary embedding of the E channels ch .. ch+E-1 of one row (values in v,
+// the row's 16-bit inputs at `row`) by table row cs (cos(p w_i) at i, sin at
+// rot/2 + i). neox pairs channel c with c +- rot/2, otherwise with c ^ 1;
+// channels from rot on are left alone. Each output is
+// fl32(fl32(x cos) -+ fl32(y sin)), y the pair partner: no fused multiply-add,
+// so the rotated values (and the codes taken from them) do not depend on
+// the compiler's contraction choices.
+template <int E, bool BF16>
+__device__ __forceinline__ void rope_lane(const uint16_t* __restrict__ row, int ch, float (&v)[E],
+                                          const float* __restrict__ cs, int rot, bool neox) {
+#pragma clang fp contract(off)
+  const int half = rot >> 1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = ch + e;
+    if (c >= rot) continue;
+    const bool first = neox ? c < half : (c & 1) == 0;
+    const int i = neox ? (first ? c : c - half) : c >> 1;
+    const int pc = neox ? (first ? c + half : c - half) : c ^ 1;
+    const float y = half_to_f32<BF16>(row[pc]);
+    const float xc = v[e] * cs[i];
+    const float ys = y * cs[half + i];
+    v[e] = first ? xc - ys : xc + ys;
+  }
+}
+
 }  // namespace qa

@@ -205,16 +205,25 @@ struct NewToken {
 
 // One wave quantizes a row of D 16-bit values, E = D/64 per lane (bits as
 // loaded): returns this lane's E codes packed in bytes and the row scale.
+// With rope.pos set, the row (16-bit inputs at `row`) is first rotated by the
+// table row of position p.
 template <int D>
-__device__ __forceinline__ uint32_t quant_row_wave(const uint16_t (&bits)[D / 64], bool bf16, float& scale) {
+__device__ __forceinline__ uint32_t quant_row_wave(const uint16_t (&bits)[D / 64], bool bf16, float& scale,
+                                                   const Rope& rope = Rope{}, const uint16_t* row = nullptr,
+                                                   int64_t p = 0) {
   constexpr int E = D / 64;
   float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = bf16 ? bf16_to_f32(bits[e]) : f16_to_f32(bits[e]);
+  if (rope.pos != nullptr) {
+    const int lane = threadIdx.x & 63;
+    const float* cs = rope.cs + p * rope.rot;
+    if (bf16) rope_lane<E, true>(row, lane * E, x, cs, rope.rot, rope.neox);
+    else rope_lane<E, false>(row, lane * E, x, cs, rope.rot, rope.neox);
+  }
   float amax = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    x[e] = bf16 ? bf16_to_f32(bits[e]) : f16_to_f32(bits[e]);
-    amax = fmaxf(amax, fabsf(x[e]));
-  }
+  for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(x[e]));
   amax = wave_max(amax);
   scale = quant_scale(amax);
   uint32_t packed = 0;
@@ -227,8 +236,9 @@ __device__ __forceinline__ uint32_t quant_row_wave(const uint16_t (&bits)[D / 64
 }
 
 // MT: several query tokens per sequence (a.tq > 1); the one-token kernels
-// are compiled without the per-column bookkeeping.
-template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT>
+// are compiled without the per-column bookkeeping. ROPE (fused step only):
+// rotate the query rows and the new K row first.
+template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT, bool ROPE = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode(DecodeArgs a) {
   constexpr int KS = D / 64;   // INT8 K-steps
   constexpr int CG = D / 16;   // 16-channel groups of the output
@@ -339,13 +349,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
         for (int e = 0; e < KS; ++e) bits[e] = row[lane * KS + e];
       }
       float sc;
+      const Rope rope = ROPE ? a.rope : Rope{};
+      const int64_t rpos = ROPE ? a.rope.pos[seq] : 0;
       if (j < G) {
-        const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc);
+        const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc, rope, job_row(j), rpos);
 #pragma unroll
         for (int e = 0; e < KS; ++e) nt.q[j][lane * KS + e] = (int8_t)(codes >> (8 * e));
         if (lane == 0) nt.qs[j] = sc;
       } else if (j == G) {
-        const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc);
+        const uint32_t codes = quant_row_wave<D>(bits, a.in_bf16, sc, rope, job_row(j), rpos);
 #pragma unroll
         for (int e = 0; e < KS; ++e) reinterpret_cast<int8_t*>(nt.k)[lane * KS + e] = (int8_t)(codes >> (8 * e));
         if (lane == 0) nt.ks = sc;
@@ -576,7 +588,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
   }
 }
 
-template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT>
+template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT, bool ROPE = false>
 hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   if (phase == DecodePhase::kCombine) {
     if (a.num_splits > 1)
@@ -587,7 +599,7 @@ hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   const dim3 grid(a.num_splits, a.Hkv, a.num_seqs);
   // LDS: per-wave partials [kWaves][G][D] plus (max, sum) pairs.
   const size_t lds = EXPORT_QK ? 0 : (size_t)(kWaves * 32 + kWaves * a.G * a.tq * D) * sizeof(float);
-  auto kern = k_decode<D, V_I8, EXPORT_QK, FUSED, MT>;
+  auto kern = k_decode<D, V_I8, EXPORT_QK, FUSED, MT, ROPE>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -605,6 +617,9 @@ hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
 template <bool EXPORT_QK>
 hipError_t dispatch(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
 #define QA_DEC(DD)                                                                                  \
+  if (a.q_in != nullptr && a.rope.pos != nullptr)                                                   \
+    return a.v_int8 ? run_decode<DD, true, false, true, false, true>(a, phase, st)                  \
+                    : run_decode<DD, false, false, true, false, true>(a, phase, st);                \
   if (a.q_in != nullptr)                                                                            \
     return a.v_int8 ? run_decode<DD, true, false, true, false>(a, phase, st)                        \
                     : run_decode<DD, false, false, true, false>(a, phase, st);                      \

@@ -143,6 +143,8 @@ struct DecodeArgs {
   void* vc_w;
   float* vs_w;
   bool in_bf16;           // q_in/k_new/v_new are bf16 (else f16)
+  Rope rope;              // fused step: rotate the query rows and the new K row
+                          // (position rope.pos[seq]) before quantizing them
 };
 // kPartials: the split kernel only (with one split it writes the output);
 // kCombine: the merge of the split partials only; kBoth: one after the other.

@@ -34,31 +34,6 @@ __device__ __forceinline__ void store_codes(int8_t* p, uint32_t packed) {
   else *reinterpret_cast<uint8_t*>(p) = (uint8_t)packed;
 }
 
-// Rotate the E channels ch .. ch+E-1 of one row (values in v, the row's 16-bit
-// inputs at `row`) by the table row of position p. Each output is
-// fl32(fl32(x cos) -+ fl32(y sin)) with y the pair partner: no fused
-// multiply-add, so the rotated values (and the codes taken from them) are
-// the same on every implementation that rounds each operation.
-template <int E, bool BF16>
-__device__ __forceinline__ void rope_lane(const uint16_t* __restrict__ row, int ch, float (&v)[E], const Rope& r,
-                                          int64_t p) {
-#pragma clang fp contract(off)
-  const int half = r.rot >> 1;
-  const float* cs = r.cs + p * r.rot;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = ch + e;
-    if (c >= r.rot) continue;
-    const bool first = r.neox ? c < half : (c & 1) == 0;
-    const int i = r.neox ? (first ? c : c - half) : c >> 1;
-    const int pc = r.neox ? (first ? c + half : c - half) : c ^ 1;
-    const float y = half_to_f32<BF16>(row[pc]);
-    const float xc = v[e] * cs[i];
-    const float ys = y * cs[half + i];
-    v[e] = first ? xc - ys : xc + ys;
-  }
-}
-
 // Quantize E values held by one lane against the wave-wide scale of its row.
 template <int E>
 __device__ __forceinline__ uint32_t quant_lane(const float (&v)[E], float amax, float s) {
@@ -82,7 +57,7 @@ __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ x, int64_
   float v[E];
   const uint16_t* src = x + t * st + (int64_t)h * sh;
   load_halves<E, BF16>(src + lane * E, v);
-  if (rope.pos != nullptr) rope_lane<E, BF16>(src, lane * E, v, rope, rope.pos[t]);
+  if (rope.pos != nullptr) rope_lane<E, BF16>(src, lane * E, v, rope.cs + rope.pos[t] * rope.rot, rope.rot, rope.neox);
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
@@ -112,7 +87,8 @@ __device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, con
 
   float kv[E];
   load_halves<E, BF16>(k + src, kv);
-  if (rope.pos != nullptr) rope_lane<E, BF16>(k + (src - lane * E), lane * E, kv, rope, rope.pos[t]);
+  if (rope.pos != nullptr)
+    rope_lane<E, BF16>(k + (src - lane * E), lane * E, kv, rope.cs + rope.pos[t] * rope.rot, rope.rot, rope.neox);
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(kv[e]));

@@ -233,6 +233,13 @@ def test_rope_producer_validation(qa):
     assert L.qa_rope_quantize_q_write_kv(None, *args(128)) == qa.QA_ERR_INVALID_ARG
     r.positions = FAKE
     assert L.qa_rope_quantize_q_write_kv(ctypes.byref(r), *args(96)) == qa.QA_ERR_UNSUPPORTED   # head_dim 96
+    # the step with rotary embedding checks rope before anything is launched
+    p = qa.decode_params(2, 24, 4, 256, 100, 1000)
+    step = lambda rp: L.qa_paged_decode_step_rope(rp, ctypes.byref(p), FAKE, 6144, 256, FAKE, FAKE, 1024, 256,
+                                                  qa.QA_DT_BF16, *([FAKE] * 8), 1 << 30, FAKE, None)
+    assert step(None) == qa.QA_ERR_INVALID_ARG
+    r.rot_dim = 258
+    assert step(ctypes.byref(r)) == qa.QA_ERR_INVALID_ARG
 
 
 def test_last_error_is_thread_local(qa):

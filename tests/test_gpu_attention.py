@@ -184,6 +184,58 @@ def test_decode_step_matches_producer_then_decode(qa, case):
         assert a is b is None or torch.equal(a, b)
 
 
+ROPE_STEP_CASES = [
+    # (v_int8, splits, context lens, dtype, rot_dim, neox)
+    (False, 8, [3000, 17, 1600], "bf16", 64, True),
+    (True, 0, [257, 2048], "f16", 256, False),
+    (False, 1, [700, 33], "bf16", 128, True),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ROPE_STEP_CASES)
+def test_decode_step_rope(qa, case):
+    """The step with rotary embedding (rotation, quantization, cache write
+    and attention in the split kernel) equals the rotary producer followed
+    by the decode call bit for bit (output and cache bytes), and the oracle
+    (rotate, quantize, write, decode) within tolerance."""
+    from workloads import rope_table
+    v_int8, splits, ctx, dt, rot, neox = case
+    spec = PagedSpec("step_rope", 14, len(ctx), 24, 4, 256, ctx, [1] * len(ctx), k_bias_std=2.0, v_int8=v_int8,
+                     dtype=dt)
+    say(f"decode step rope {case}")
+    inp = paged_inputs(spec)
+    last = inp.cu_seqlens_kv[1:] - 1
+    hist = inp.slot_mapping.copy()
+    hist[last] = -1
+    kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, 4, 256, torch.int8 if v_int8 else torch.bfloat16)
+    qa.write_kv_cache(dev_bits(inp.k, dt), dev_bits(inp.v, dt), torch.from_numpy(hist).cuda(), kc, ks, vc, vs)
+    q = dev_bits(inp.q, dt)
+    k_new, v_new = dev_bits(inp.k[last], dt), dev_bits(inp.v[last], dt)
+    slots = torch.from_numpy(inp.slot_mapping[last].copy()).cuda()
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.context_lens).cuda()
+    pos = (inp.context_lens - 1).astype(np.int64)
+    tab = rope_table(4096, rot)
+    rope = (torch.from_numpy(pos).cuda(), torch.from_numpy(tab).cuda(), rot, neox)
+    c1 = [t if t is None else t.clone() for t in (kc, ks, vc, vs)]
+    c2 = [t if t is None else t.clone() for t in (kc, ks, vc, vs)]
+    q8, qs = qa.quantize_q_write_kv(q, k_new, v_new, slots, *c1, rope=rope)
+    ref = qa.paged_attention_decode(q8, qs, *c1, tables, lens, num_splits=splits)
+    got = qa.paged_decode_step(q, k_new, v_new, slots, *c2, tables, lens, num_splits=splits, rope=rope)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    for a, b in zip(c1, c2):
+        assert a is b is None or torch.equal(a, b)
+    caches = oracle.write_kv_cache(inp.k, inp.v, dt, hist, spec.num_blocks, v_int8=v_int8)
+    caches = oracle.rope_write_kv_cache(inp.k[last], inp.v[last], dt, inp.slot_mapping[last], spec.num_blocks, pos, tab,
+                                        rot, neox, v_int8=v_int8, caches=caches)
+    w8, wsc = oracle.rope_quantize_q(inp.q, dt, pos, tab, rot, neox)
+    assert np.array_equal(q8.cpu().numpy(), w8)
+    want = oracle.paged_decode(w8, wsc, caches, inp.block_tables, inp.context_lens, 4)
+    assert_close(got.cpu().numpy(), want, "decode step rope")
+
+
 @pytest.mark.gpu
 def test_decode_step_unwritten_slot(qa):
     """A negative slot writes nothing; both paths then read the cached value."""
