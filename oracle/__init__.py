@@ -39,12 +39,19 @@ Parity status, function by function (pins live in tests/test_oracle_pins.py):
   interleaved pairing is the half pairing of permuted channels; channels
   past rot_dim pass through; rotated dot products depend only on the
   position difference).
+* e4m3_encode / e4m3_decode: pinned (the format's landmark values, ties to
+  even at midpoints, saturation, and torch's float8_e4m3fn conversion).
+* dense_sage_attention_fp8pv: pinned (constant V comes back exactly; one
+  visible key returns its FP8-rounded value; a two-key closed form through
+  the pinned codec; rescaling across tiles; within the FP8 error bound of
+  the 16-bit P path).
 * sage_varlen_forward: pinned (equal lengths reproduce the batched forward;
   a sequence's rows do not depend on its neighbours; empty sequences).
 """
 from .quant import (widen, quant_rows, quantize_q, write_kv_cache, write_kv_values, sage_quantize,
                     gather_kv)
 from .rope import apply_rope, rope_quantize_q, rope_write_kv_cache
+from .fp8 import e4m3_encode, e4m3_decode, e4m3_round, v_fp8_per_channel, dense_sage_attention_fp8pv
 from .attention import (paged_qk_int32, paged_decode, paged_decode_split,
                         chunked_prefill, dense_sage_attention, attention_fp64,
                         default_scale, sage_smooth_v, sage_lse_correction, sage_forward,
@@ -53,6 +60,7 @@ from .attention import (paged_qk_int32, paged_decode, paged_decode_split,
 __all__ = [
     "widen", "quant_rows", "quantize_q", "write_kv_cache", "write_kv_values", "sage_quantize", "gather_kv",
     "apply_rope", "rope_quantize_q", "rope_write_kv_cache",
+    "e4m3_encode", "e4m3_decode", "e4m3_round", "v_fp8_per_channel", "dense_sage_attention_fp8pv",
     "paged_qk_int32", "paged_decode", "paged_decode_split", "chunked_prefill",
     "dense_sage_attention", "attention_fp64", "default_scale",
     "sage_smooth_v", "sage_lse_correction", "sage_forward", "sage_varlen_forward",

@@ -13,6 +13,7 @@ import oracle
 import oracle.attention as oa
 import oracle.quant as oq
 import oracle.rope as orope
+import oracle.fp8 as ofp8
 import tests.test_oracle_pins as pins
 
 
@@ -127,6 +128,16 @@ MUTATIONS = [
      "[np.maximum(np.asarray(positions, np.int64) - 1, 0)]", pins.test_rope_pairs_rotate_as_complex_numbers, (False,)),
     ("rope_cache_unrotated", orope, "rope_write_kv_cache", "k_rot = apply_rope(k_bits, dtype, positions, cos_sin, rot_dim, neox)",
      "k_rot = widen(k_bits, dtype)", pins.test_rope_cache_write_holds_rotated_keys, ()),
+    ("fp8_no_rescale_of_o", ofp8, "dense_sage_attention_fp8pv", "o = o * alpha[:, None] + p8 @", "o = o + p8 @",
+     pins.test_fp8pv_is_within_fp8_error_of_the_16bit_path, ()),
+    ("fp8_v_scale_dropped", ofp8, "dense_sage_attention_fp8pv", "* sv[b, kvh].astype(np.float64)", "* 1.0",
+     pins.test_fp8pv_constant_values_come_back, ()),
+    ("fp8_p_not_rounded", ofp8, "dense_sage_attention_fp8pv", "e4m3_round(E4M3_MAX * np.exp(", "(E4M3_MAX * np.exp(",
+     pins.test_fp8pv_one_visible_key_and_two_key_closed_form, ()),
+    ("fp8_v_not_rounded", ofp8, "v_fp8_per_channel", "vals = np.where(live[:, None], e4m3_round(r), 0.0)",
+     "vals = np.where(live[:, None], r, 0.0)", pins.test_v_fp8_per_channel_codes, ()),
+    ("fp8_ties_away", ofp8, "e4m3_encode", "((dhi == dlo) & (_POS_CODES[hi] % 2 == 0))", "(dhi == dlo)",
+     pins.test_e4m3_landmarks_ties_and_saturation, ()),
 ]
 
 

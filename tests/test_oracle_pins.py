@@ -723,3 +723,91 @@ def test_rope_cache_write_holds_rotated_keys():
     for key in ("k_cache", "k_scale", "v_cache"):
         np.testing.assert_array_equal(c0[key], c1[key])
 
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) P.V
+
+
+def test_e4m3_landmarks_ties_and_saturation():
+    dec = oracle.e4m3_decode
+    assert dec(0x38) == 1.0 and dec(0x7E) == 448.0 and dec(0x01) == 2.0 ** -9 and dec(0x08) == 2.0 ** -6
+    assert dec(0x07) == 7 * 2.0 ** -9 and np.isnan(dec(0x7F)) and dec(0xB8) == -1.0
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_encode(dec(finite)), finite)
+    # midpoints go to the even code
+    assert oracle.e4m3_encode(1.0625) == 0x38 and oracle.e4m3_encode(1.1875) == 0x3A
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00 and oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02
+    assert oracle.e4m3_encode(460.0) == 0x7E and oracle.e4m3_encode(-1e-12) == 0x80
+
+
+def test_e4m3_matches_torch_conversion():
+    import torch
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(200000) * 60, rng.standard_normal(50000) * 1e-3,
+                        np.float32(2.0) ** np.arange(-12, 9)]).astype(np.float32)
+    got = oracle.e4m3_encode(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, want)
+
+
+def _fp8_case(N=200, Nk=None, d=64, causal=False, seed=77, vfun=None):
+    spec, inp = _dense(N=N, Nk=Nk, d=d, seed=seed)
+    v = inp.v if vfun is None else to_f16_bits(vfun(oq.widen(inp.v, "f16")))
+    quant = oracle.sage_quantize(inp.q, inp.k, "f16")
+    return inp, quant, v
+
+
+def test_fp8pv_constant_values_come_back():
+    # every token holds the same V row: whatever P is, the output is that row
+    c = (np.arange(64, dtype=np.float32) - 20.0) * np.float32(0.37)
+    inp, quant, v = _fp8_case(N=150, vfun=lambda x: np.broadcast_to(c, x.shape).copy())
+    out = oracle.dense_sage_attention_fp8pv(quant, v, "f16", causal=True)
+    cv = oq.widen(to_f16_bits(c), "f16").astype(np.float64)
+    np.testing.assert_allclose(out, np.broadcast_to(cv, out.shape), rtol=2e-7, atol=1e-12)
+
+
+def test_fp8pv_one_visible_key_and_two_key_closed_form():
+    inp, quant, v = _fp8_case(N=130, causal=True)
+    out = oracle.dense_sage_attention_fp8pv(quant, v, "f16", causal=True)
+    v8, sv = oracle.v_fp8_per_channel(oq.widen(v, "f16"))
+    # row 0 sees key 0 only: its FP8-rounded value times the channel scale
+    np.testing.assert_allclose(out[0, 0], v8[0, 0] * sv[0], rtol=1e-12)
+    # row 1 sees keys 0 and 1: P8 = (E4M3(448 e^(s0 - m)), E4M3(448 e^(s1 - m)))
+    s = _int_dot_scores(quant, 0, 1, [0, 1])
+    p = oracle.e4m3_round(448.0 * np.exp(s - s.max()))
+    want = (p[0] * v8[0, 0, 0] + p[1] * v8[0, 1, 0]) / p.sum() * sv[0, 0]
+    np.testing.assert_allclose(out[0, 1, 0], want, rtol=1e-12)
+
+
+def _int_dot_scores(quant, b, row, keys, h=0):
+    q = quant["q_i8"][b, row, h].astype(np.float64)
+    k = quant["k_i8"][b, keys, h].astype(np.float64)
+    return (k @ q) * float(quant["q_scale"][b, h, row // 128]) * quant["k_scale"][b, h, np.asarray(keys) // 64] / 8.0
+
+
+def test_fp8pv_is_within_fp8_error_of_the_16bit_path():
+    """Against the exact-P path: relative L2 of order the E4M3 step (2^-4
+    per rounded term, averaged over keys) and not identical; rows whose
+    maximum moves between tiles are included (keys beyond 64, growing bias)."""
+    inp, quant, v = _fp8_case(N=300, Nk=260, causal=False, vfun=lambda x: x + np.float32(0.5))
+    for causal in (False, True):
+        a = oracle.dense_sage_attention_fp8pv(quant, v, "f16", causal=causal)
+        b = oracle.dense_sage_attention(quant, v, "f16", causal=causal)
+        r = np.linalg.norm(a - b) / np.linalg.norm(b)
+        assert 1e-4 < r < 3e-2, r
+
+
+def test_v_fp8_per_channel_codes():
+    """Every channel's largest magnitude maps to 448; all values are E4M3
+    values; each is within half an E4M3 step of V / s."""
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal((2, 90, 3, 64)) * rng.uniform(0.1, 30, (1, 1, 3, 64))).astype(np.float32)
+    v[:, :, 1, 7] = 0.0                                   # an all-zero channel: scale 0, codes 0
+    vals, s = oracle.v_fp8_per_channel(v)
+    np.testing.assert_array_equal(oracle.e4m3_round(vals), vals)
+    amax = np.abs(vals).max(axis=1)
+    assert np.all((amax == 448.0) | (s == 0)) and s[0, 1, 7] == 0 and np.all(vals[:, :, 1, 7] == 0)
+    r = v / np.where(s > 0, s, 1)[:, None]
+    step = np.where(np.abs(r) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(vals - r) <= step / 2 * (1 + 1e-9))
