@@ -342,9 +342,10 @@ def run_prefill(torch, qa, reps):
             "_ops": (qk, pv)}
 
 
-def run_dense(torch, qa, reps, causal, options=False):
+def run_dense(torch, qa, reps, causal, options=False, pv_fp8=False):
     """The dense workload; with options, through the options call in the HND
-    layout with smooth_v and the LSE output."""
+    layout with smooth_v and the LSE output; with pv_fp8, the options call
+    (NHD) with the P.V product in FP8."""
     from workloads import dense_sage, dense_inputs
     spec = dense_sage()
     inp = dense_inputs(spec)
@@ -360,6 +361,11 @@ def run_dense(torch, qa, reps, causal, options=False):
         lse = torch.empty((spec.batch, spec.num_q_heads, spec.seq_q), dtype=torch.float32, device="cuda")
         f = lambda: qa.dense_sage_attention_ex(q, k, v, "HND", is_causal=causal, smooth_v=True, return_lse=True,
                                                workspace=ws, out=out, lse=lse)
+    elif pv_fp8:
+        o = qa.DenseOptions(qa.QA_LAYOUT_NHD, 0, 1)
+        ws = torch.empty(qa.lib.qa_dense_sage_ex_workspace_size(ctypes.byref(p), ctypes.byref(o)),
+                         dtype=torch.uint8, device="cuda")
+        f = lambda: qa.dense_sage_attention_ex(q, k, v, is_causal=causal, pv_fp8=True, workspace=ws, out=out)
     else:
         ws = qa.dense_sage_workspace(p)
         f = lambda: qa.dense_sage_attention(q, k, v, is_causal=causal, workspace=ws, out=out)
@@ -376,7 +382,7 @@ def run_dense(torch, qa, reps, causal, options=False):
     mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
     return {"workload": f"dense_sage B2 H32 N8192 d128 {'causal' if causal else 'non-causal'} "
                         "(full chain: smooth_k + per-block quantization + attention"
-                        + (", HND, smooth_v, LSE output)" if options else ")"),
+                        + (", HND, smooth_v, LSE output)" if options else ", FP8 E4M3 P.V)" if pv_fp8 else ")"),
             "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
             "_ops": (qk, pv)}
 
@@ -559,6 +565,8 @@ def main():
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True),
                         "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True),
+                        "dense_sage_noncausal_fp8pv": run_dense(torch, qa, 10, False, pv_fp8=True),
+                        "dense_sage_causal_fp8pv": run_dense(torch, qa, 10, True, pv_fp8=True),
                         "dense_sage_varlen_mix": run_varlen(torch, qa, 10)}
         for e in res["extra"].values():
             if "_ops" not in e:

@@ -460,6 +460,16 @@ typedef struct {
   int32_t smooth_v;  /* nonzero: V' = fl16(fl32(V) - mu_v), mu_v the per-(batch, KV head,
                         channel) mean of V over seq_k (fp64 sum, fp32 result); mu_v is added
                         back in fp32 to every output row that sees at least one key */
+  int32_t pv_fp8;    /* nonzero: P.V in FP8 E4M3 on the matrix units (head_dim 64 or 128;
+                        else QA_ERR_UNSUPPORTED). V (or V' with smooth_v) is quantized per
+                        (batch, KV head, channel): s_c = fl32(max |V| / 448), codes
+                        E4M3(fl32(V / s_c)) rounded to nearest even; over 64-key tiles the
+                        softmax reference m moves to the running row maximum when a tile
+                        exceeds it by more than 3 (base 2), and each P is rounded to
+                        E4M3(56 exp(score - m)) (56 = 448 / 2^3); O and the row sum accumulate
+                        those rounded values in fp32; out = O / l * s_c. Accuracy is that
+                        of the E4M3 step (about 2^-4 per rounded term), not of the 16-bit
+                        path; the LSE, when asked for, is that of the rounded P */
 } qa_dense_options_t;
 
 /*
@@ -523,6 +533,7 @@ typedef struct {
   int32_t smooth_k, smooth_v, is_causal;
   float softmax_scale;         /* <= 0 selects 1/sqrt(head_dim) */
   qa_dtype_t out_dtype;        /* QA_DT_F32, QA_DT_F16 or QA_DT_BF16 */
+  int32_t pv_fp8;              /* FP8 P.V as in qa_dense_options_t */
 } qa_varlen_params_t;
 
 size_t qa_dense_sage_varlen_workspace_size(const qa_varlen_params_t* p);

@@ -70,20 +70,23 @@ def v_fp8_per_channel(v_vals):
 
 
 def dense_sage_attention_fp8pv(quant, v_bits, dtype="f16", causal=False, scale=None, smooth_v=False,
-                               tile=64, rows=None, heads=None, return_lse=False):
+                               tile=64, slack=3.0, rows=None, heads=None, return_lse=False):
     """Dense attention with the P.V product in FP8 (the pages' next step for
     P.V: [SAGE-MACA] lists FP8 P.V of later SageAttention versions as not
     portable to its hardware; gfx950 has it natively).
 
     Scores as dense_sage_attention. Readings (the pages fix none of this):
-    online softmax over tiles of `tile` keys in order, with the exact running
-    row maximum m_t after tile t; each probability of tile t is
-    P8 = E4M3(448 * exp(s - m_t)) (so the largest is 448); V per channel in
-    FP8 (v_fp8_per_channel, of V - mu_v with smooth_v); the row sum l and the
-    output accumulate the rounded P8 exactly, rescaled by exp(m_{t-1} - m_t)
-    when the maximum moves; out = (O / l) * s_V (+ mu_v with smooth_v, on
-    rows that see a key). Products and sums in fp64. With return_lse: the
-    natural log of l / 448 * exp(m) (the sum of the rounded probabilities).
+    online softmax over tiles of `tile` keys in order with a reference m_t
+    per row: m_t = m_{t-1} unless the tile's largest score exceeds it by more
+    than `slack` in base-2 units (slack * ln 2 in scores), then m_t is the
+    running maximum (slack 0: the exact running maximum); each probability of
+    tile t is P8 = E4M3(448 * 2^-slack * exp(s - m_t)), so the largest
+    possible is 448; V per channel in FP8 (v_fp8_per_channel, of V - mu_v
+    with smooth_v); the row sum l and the output accumulate the rounded P8
+    exactly, rescaled by exp(m_{t-1} - m_t) when the reference moves;
+    out = (O / l) * s_V (+ mu_v with smooth_v, on rows that see a key).
+    Products and sums in fp64. With return_lse: the natural log of
+    l / (448 * 2^-slack) * exp(m) (the sum of the rounded probabilities).
     Returns fp64 [B, Nq, Hq, d] (and lse [B, Hq, Nq])."""
     q_i8, k_i8 = quant["q_i8"], quant["k_i8"]
     B, Nq, Hq, d = q_i8.shape
@@ -114,12 +117,15 @@ def dense_sage_attention_fp8pv(quant, v_bits, dtype="f16", causal=False, scale=N
             m = np.full(len(qr), -np.inf)
             l = np.zeros(len(qr))
             o = np.zeros((len(qr), d))
+            top = E4M3_MAX * 2.0 ** -slack
             for t0 in range(0, Nk, tile):
                 st = s[:, t0:t0 + tile]
-                m_new = np.maximum(m, st.max(axis=1))
+                mt = st.max(axis=1)
+                move = mt > m + slack * np.log(2.0)
+                m_new = np.where(move, np.maximum(m, mt), m)
                 live = np.isfinite(m_new)
                 alpha = np.where(np.isfinite(m), np.exp(m - np.where(live, m_new, 0.0)), 0.0)
-                p8 = np.where(live[:, None], e4m3_round(E4M3_MAX * np.exp(st - np.where(live, m_new, 0.0)[:, None])), 0.0)
+                p8 = np.where(live[:, None], e4m3_round(top * np.exp(st - np.where(live, m_new, 0.0)[:, None])), 0.0)
                 l = l * alpha + p8.sum(axis=1)
                 o = o * alpha[:, None] + p8 @ v8[b, t0:t0 + tile, kvh]
                 m = m_new
@@ -128,5 +134,5 @@ def dense_sage_attention_fp8pv(quant, v_bits, dtype="f16", causal=False, scale=N
             if smooth_v:
                 res = res + np.where(ok[:, None], mu[b, kvh].astype(np.float64), 0.0)
             out[b, qr, h] = res
-            lse[b, h, qr] = np.where(ok, m + np.log(np.where(ok, l, 1.0) / E4M3_MAX), -np.inf)
+            lse[b, h, qr] = np.where(ok, m + np.log(np.where(ok, l, 1.0) / top), -np.inf)
     return (out, lse) if return_lse else out

@@ -62,11 +62,11 @@ class VarlenParams(ctypes.Structure):
     _fields_ = [("batch", _i32), ("total_q", _i64), ("total_k", _i64), ("max_seqlen_q", _i32),
                 ("max_seqlen_k", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
                 ("dtype", ctypes.c_int), ("smooth_k", _i32), ("smooth_v", _i32), ("is_causal", _i32),
-                ("softmax_scale", _f32), ("out_dtype", ctypes.c_int)]
+                ("softmax_scale", _f32), ("out_dtype", ctypes.c_int), ("pv_fp8", _i32)]
 
 
 class DenseOptions(ctypes.Structure):
-    _fields_ = [("layout", _i32), ("smooth_v", _i32)]
+    _fields_ = [("layout", _i32), ("smooth_v", _i32), ("pv_fp8", _i32)]
 
 
 QA_LAYOUT_NHD, QA_LAYOUT_HND = 0, 1
@@ -421,10 +421,11 @@ def dense_sage_attention(q, k, v, is_causal=False, smooth_k=True, softmax_scale=
 
 def dense_sage_attention_ex(q, k, v, tensor_layout="NHD", is_causal=False, smooth_k=True, smooth_v=False,
                             return_lse=False, softmax_scale=0.0, out_dtype=torch.float32, workspace=None,
-                            out=None, lse=None):
+                            out=None, lse=None, pv_fp8=False):
     """The dense forward with its options: tensor_layout "NHD" ([B, N, H, d])
     or "HND" ([B, H, N, d]) for q, k, v and out; smooth_v; return_lse (fp32
-    [B, Hq, Nq], natural log, corrected for the K mean under smooth_k).
+    [B, Hq, Nq], natural log, corrected for the K mean under smooth_k);
+    pv_fp8 (the P.V product in FP8 E4M3, head_dim 64 or 128).
     Returns out, or (out, lse) with return_lse."""
     _require_cuda(q, k, v)
     if tensor_layout not in _LAYOUTS:
@@ -440,7 +441,7 @@ def dense_sage_attention_ex(q, k, v, tensor_layout="NHD", is_causal=False, smoot
         Nk, Hkv = k.shape[1], k.shape[2]
     p = DenseParams(B, Nq, Nk, Hq, Hkv, d, _dt(q.dtype), int(bool(smooth_k)), int(bool(is_causal)),
                     softmax_scale, _dt(out_dtype))
-    o = DenseOptions(_LAYOUTS[tensor_layout], int(bool(smooth_v)))
+    o = DenseOptions(_LAYOUTS[tensor_layout], int(bool(smooth_v)), int(bool(pv_fp8)))
     if workspace is None:
         workspace = torch.empty(max(lib.qa_dense_sage_ex_workspace_size(ctypes.byref(p), ctypes.byref(o)), 16),
                                 dtype=torch.uint8, device=q.device)
@@ -455,15 +456,15 @@ def dense_sage_attention_ex(q, k, v, tensor_layout="NHD", is_causal=False, smoot
 
 
 def varlen_params(q, k, max_seqlen_q, max_seqlen_k, batch, is_causal=False, smooth_k=True, smooth_v=False,
-                  softmax_scale=0.0, out_dtype=torch.float32) -> VarlenParams:
+                  softmax_scale=0.0, out_dtype=torch.float32, pv_fp8=False) -> VarlenParams:
     return VarlenParams(batch, q.shape[0], k.shape[0], max_seqlen_q, max_seqlen_k, q.shape[1], k.shape[1],
                         q.shape[2], _dt(q.dtype), int(bool(smooth_k)), int(bool(smooth_v)), int(bool(is_causal)),
-                        softmax_scale, _dt(out_dtype))
+                        softmax_scale, _dt(out_dtype), int(bool(pv_fp8)))
 
 
 def dense_sage_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=False,
                                 smooth_k=True, smooth_v=False, return_lse=False, softmax_scale=0.0,
-                                out_dtype=torch.float32, workspace=None, out=None, lse=None):
+                                out_dtype=torch.float32, workspace=None, out=None, lse=None, pv_fp8=False):
     """Packed variable-length dense forward: q [total_q, Hq, d], k and v
     [total_k, Hkv, d]; cu_seqlens_q/k int32 [B+1] on the GPU. Returns out
     [total_q, Hq, d], or (out, lse [Hq, total_q]) with return_lse."""
@@ -477,7 +478,7 @@ def dense_sage_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     if cu_seqlens_k.numel() != batch + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     p = varlen_params(q, k, max_seqlen_q, max_seqlen_k, batch, is_causal, smooth_k, smooth_v, softmax_scale,
-                      out_dtype)
+                      out_dtype, pv_fp8)
     if workspace is None:
         workspace = torch.empty(max(lib.qa_dense_sage_varlen_workspace_size(ctypes.byref(p)), 16),
                                 dtype=torch.uint8, device=q.device)

@@ -137,15 +137,16 @@ Strides layout_strides(int32_t layout, int64_t N, int64_t H, int64_t D) {
 struct DenseCall {
   qa::Rows q, k;               // sequence geometry; N = length (batched) or the longest (varlen)
   int32_t Hq, Hkv, D;
-  bool bf16, smooth_k, smooth_v, causal;
+  bool bf16, smooth_k, smooth_v, causal, pv_fp8;
   float softmax_scale;
   qa_dtype_t out_dtype;
   Strides sq, sk, so;          // q, k/v, out
   int64_t q_rows() const { return q.packed ? q.total : (int64_t)q.B * q.N; }
 };
 
-DenseCall dense_call(const qa_dense_params_t* p, int32_t layout, bool smooth_v) {
+DenseCall dense_call(const qa_dense_params_t* p, int32_t layout, bool smooth_v, bool pv_fp8 = false) {
   DenseCall c{};
+  c.pv_fp8 = pv_fp8;
   c.q = qa::Rows{nullptr, p->batch, p->seq_q, 0, false};
   c.k = qa::Rows{nullptr, p->batch, p->seq_k, 0, false};
   c.Hq = p->num_q_heads; c.Hkv = p->num_kv_heads; c.D = p->head_dim;
@@ -161,7 +162,8 @@ DenseCall dense_call(const qa_dense_params_t* p, int32_t layout, bool smooth_v) 
 // The options and varlen calls append [v_mean][lse_corr]; varlen then adds the
 // packed-block maps [q 128-row][k 64-row][k 16-row].
 struct DenseWs {
-  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, q_map, k_map64, k_map16, total;
+  size_t partial, q_i8, k_blk, v_blk, q_scale, k_scale, k_mean, v_mean, lse_corr, q_map, k_map64, k_map16, v8_scale,
+      total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -175,13 +177,17 @@ DenseWs dense_layout(const DenseCall& c, bool with_attention, bool ex) {
   if (with_attention) {
     w.q_i8 = off; off += al(rows_q * Hq * D);
     w.k_blk = off; off += al(nb16 * Hkv * D * 16);
-    w.v_blk = off; off += al(nb16 * Hkv * D * 16 * 2);
+    // 16-bit V blocks, or E4M3 blocks of 64 keys for the FP8 P.V
+    w.v_blk = off; off += al(c.pv_fp8 ? c.k.nblocks(64) * Hkv * D * 64 : nb16 * Hkv * D * 16 * 2);
     w.q_scale = off; off += al(Hq * c.q.nblocks(128) * sizeof(float));
     w.k_scale = off; off += al(Hkv * c.k.nblocks(64) * sizeof(float));
     w.k_mean = off; off += al(B * Hkv * D * sizeof(float));
     if (ex) {
       w.v_mean = off; off += al(B * Hkv * D * sizeof(float));
       w.lse_corr = off; off += al(Hq * rows_q * sizeof(float));
+    }
+    if (c.pv_fp8) {
+      w.v8_scale = off; off += al(B * Hkv * D * sizeof(float));
     }
     if (c.q.packed) {
       w.q_map = off; off += al(c.q.nblocks(128) * sizeof(int32_t));
@@ -212,6 +218,11 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
   pa.q_i8 = (int8_t*)(ws + w.q_i8); pa.q_scale = (float*)(ws + w.q_scale); pa.k_i8 = nullptr;
   pa.k_paged = (int8_t*)(ws + w.k_blk); pa.k_scale = (float*)(ws + w.k_scale); pa.k_mean = (float*)(ws + w.k_mean);
   pa.partial = (double*)(ws + w.partial); pa.v_paged = (uint16_t*)(ws + w.v_blk);
+  if (c.pv_fp8) {
+    pa.v_paged = nullptr;
+    pa.v8 = (uint8_t*)(ws + w.v_blk);
+    pa.v8_scale = (float*)(ws + w.v8_scale);
+  }
   if (c.q.packed) {
     pa.q_map = (int32_t*)(ws + w.q_map); pa.k_map64 = (int32_t*)(ws + w.k_map64);
     pa.k_map16 = (int32_t*)(ws + w.k_map16);
@@ -220,6 +231,7 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
   if (st != QA_OK) return st;
   qa::FlashArgs a{};
   a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
+  if (c.pv_fp8) { a.v_blocks = pa.v8; a.v8_scale = pa.v8_scale; a.pv_fp8 = true; }
   a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
   a.o_sb = c.so.b; a.o_st = c.so.t; a.o_sh = c.so.h;
   a.v_mean = pa.v_mean; a.lse = lse; a.lse_corr = pa.lse_corr;
@@ -245,7 +257,9 @@ qa_status_t dense_attention_impl(const qa_dense_params_t* p, const qa_dense_opti
   QA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned16(workspace),
              QA_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
   QA_REQUIRE(((uintptr_t)lse & 3u) == 0, QA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const DenseCall c = dense_call(p, layout, o && o->smooth_v != 0);
+  const bool fp8 = o && o->pv_fp8 != 0;
+  QA_REQUIRE(!fp8 || p->head_dim <= 128, QA_ERR_UNSUPPORTED, "FP8 P.V needs head_dim 64 or 128");
+  const DenseCall c = dense_call(p, layout, o && o->smooth_v != 0, fp8);
   const DenseWs w = dense_layout(c, true, ex);
   QA_REQUIRE(workspace_bytes >= w.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed",
              workspace_bytes, w.total);
@@ -266,6 +280,7 @@ qa_status_t check_varlen(const qa_varlen_params_t* p) {
   QA_REQUIRE(p->batch <= 65535 && p->num_q_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
   QA_REQUIRE(p->total_q <= INT32_MAX && p->total_k <= INT32_MAX, QA_ERR_UNSUPPORTED,
              "total rows beyond int32 offsets");
+  QA_REQUIRE(p->pv_fp8 == 0 || p->head_dim <= 128, QA_ERR_UNSUPPORTED, "FP8 P.V needs head_dim 64 or 128");
   return QA_OK;
 }
 
@@ -276,6 +291,7 @@ DenseCall varlen_call(const qa_varlen_params_t* p, const int32_t* cu_q, const in
   c.Hq = p->num_q_heads; c.Hkv = p->num_kv_heads; c.D = p->head_dim;
   c.bf16 = p->dtype == QA_DT_BF16; c.smooth_k = p->smooth_k != 0; c.smooth_v = p->smooth_v != 0;
   c.causal = p->is_causal != 0; c.softmax_scale = p->softmax_scale; c.out_dtype = p->out_dtype;
+  c.pv_fp8 = p->pv_fp8 != 0;
   const int64_t D = p->head_dim;
   c.sq = Strides{0, p->num_q_heads * D, D};     // packed [total, H, D] rows
   c.sk = Strides{0, p->num_kv_heads * D, D};
@@ -701,9 +717,9 @@ qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, c
 }
 
 size_t qa_dense_sage_ex_workspace_size(const qa_dense_params_t* p, const qa_dense_options_t* options) {
-  (void)options;
   if (check_dense(p) != QA_OK) return 0;
-  return dense_layout(dense_call(p, QA_LAYOUT_NHD, false), true, true).total;
+  const bool fp8 = options != nullptr && options->pv_fp8 != 0;
+  return dense_layout(dense_call(p, QA_LAYOUT_NHD, false, fp8), true, true).total;
 }
 
 qa_status_t qa_dense_sage_attention_ex(const qa_dense_params_t* p, const qa_dense_options_t* options,

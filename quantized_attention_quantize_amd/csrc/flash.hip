@@ -46,6 +46,10 @@ namespace {
 
 constexpr int KT = 64;      // keys per LDS tile
 constexpr float kRescaleSlack = 8.0f;   // lazy-rescale threshold (base-2 units)
+// FP8 P.V: threshold 3 and P scaled by 448 * 2^-3, so the largest P (the
+// reference exceeded by 3) is the largest E4M3 value, 448
+constexpr float kFp8Slack = 3.0f;
+constexpr float kFp8Log2Top = 5.807354922057604f;   // log2(448) - 3
 
 enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 
@@ -89,6 +93,17 @@ __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
   return r;
 }
 
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// O^T (32 channels x 32 queries) += V^T P^T over 64 keys, E4M3 operands,
+// fp32 accumulation. Lane l holds A row l % 32 and B column l % 32, keys
+// 32 * (l / 32) .. +31 as bytes (layout checked on gfx950). Zero scale
+// operands select the unscaled instruction (checked equal to unit scales).
+__device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i_t a, v8i_t b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // One lane's 16 bytes global -> LDS (global_load_lds_dwordx4): the wave's
 // 64 lanes fill the 1 KB at the wave-uniform LDS address `lds`. Issued as
 // inline assembly, so the compiler does not treat the LDS destination as
@@ -118,7 +133,9 @@ struct Staged {
 // is query token r / G of query head kvh*G + r % G, so one workgroup's K/V
 // tiles serve all G heads and the row space G*Tq is cut into equal
 // workgroups.
-template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL>
+// PV8 (dense, two query groups per wave): P and V in FP8 (E4M3) for the
+// second product, a 32x32x64 matrix instruction per 32 channels and tile.
+template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL, bool PV8 = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : NW / 4))) void k_flash(
     FlashArgs a) {
@@ -127,6 +144,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // tiles (INT8, already in the LDS layout) are copied straight into LDS.
   constexpr bool KDMA = !DENSE && NW == 12 && QA_FLASH_PAGED_KDMA;
   using St = Staged<D, VK, NT, KDMA>;
+  static_assert(!PV8 || (DENSE && QG == 2 && D <= 128), "FP8 P.V: dense, 32 queries per wave");
   constexpr int KS = D / 64;
   constexpr int CG = D / 16;
   constexpr int QT = NW * 16 * QG;                 // query rows per workgroup
@@ -234,6 +252,14 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
 
   float m_run[QG], l_run[QG];
   v4f O[QG][CG];
+  v16f O8[PV8 ? D / 32 : 1];                   // FP8 P.V: 32 channels x the wave's 32 queries
+  v16f L8;                                     // row sums of the FP8 P (every element of lane l: query l % 32)
+#pragma unroll
+  for (int c = 0; c < (PV8 ? D / 32 : 1); ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) O8[c][e] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) L8[e] = 0.0f;
   v4f Ls[QG];                                  // row sums from the matrix units
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
@@ -380,8 +406,23 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
                                        (__attribute__((address_space(3))) void*)&s_k[buf][b * KBS + part * 1024],
                                        16, 0, 0);
     }
+    if constexpr (PV8) {
+      // one E4M3 block of 64 keys: D rows of 64 bytes, D/16 chunks of 1 KB
+      constexpr int V8C = D / 16;
+      const int64_t vb8 = a.k_rows.block0(z, 64) + min(tile, (kv_len + KT - 1) / KT - 1);
+      const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.v_blocks) + (vb8 * Hkv + kvh) * (int64_t)D * 64;
 #pragma unroll
-    for (int i = 0; i < (4 * VC + NW - 1) / NW; ++i) {
+      for (int i = 0; i < (V8C + NW - 1) / NW; ++i) {
+        const int c = wave_s + NW * i;
+        if (V8C % NW != 0 && c >= V8C) break;   // wave-uniform
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc + c * 1024 + lane * 16),
+                                         (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(s_v[buf]) +
+                                                                                    c * 1024),
+                                         16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (PV8 ? 0 : (4 * VC + NW - 1) / NW); ++i) {
       const int c = wave_s + NW * i, b = c / VC, part = c % VC;
       if (4 * VC % NW != 0 && c >= 4 * VC) break;   // wave-uniform
       const uint8_t* src = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * 2 +
@@ -479,6 +520,9 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     }
 
     v8h pf[QG][2];
+    uint32_t pk[QG][4];                          // FP8 P.V: byte j of word w is p[4w + j]
+    float al8 = 1.0f;                            // FP8 P.V: rescale of this lane's query (32x32 layout)
+    bool resc8 = false;
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
       // score_j = x[j] * f with one lane factor f >= 0 (dense: the Q and K
@@ -528,17 +572,25 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       float mt = mx == kNegInf ? kNegInf : (mx - off) * f;
       mt = group4_max(mt);
       // lazy rescale: move the reference only when it is exceeded by > 2^8
-      if (__any(mt > m_run[qg] + kRescaleSlack)) {
+      if (__any(mt > m_run[qg] + (PV8 ? kFp8Slack : kRescaleSlack))) {
         const float m_new = fmaxf(m_run[qg], mt);
         const float alpha = fast_exp2(m_run[qg] - (m_new == kNegInf ? 0.0f : m_new));
         l_run[qg] *= alpha;
-        Ls[qg] *= alpha;
+        if constexpr (PV8) {
+          // lane l holds query l % 32 of the wave in the 32x32 accumulators;
+          // both query groups are applied in one pass after this loop
+          if (((lane >> 4) & 1) == qg) al8 = alpha;
+          resc8 = true;
+        } else {
+          Ls[qg] *= alpha;
 #pragma unroll
-        for (int c = 0; c < CG; ++c) O[qg][c] *= alpha;
+          for (int c = 0; c < CG; ++c) O[qg][c] *= alpha;
+        }
         m_run[qg] = m_new;
       }
       const float mref = m_run[qg] == kNegInf ? 0.0f : m_run[qg];
-      const float cterm = -fmaf(off, f, mref);   // x*f + cterm = score - mref
+      // x*f + cterm = score - mref (FP8 P.V: + log2(448) - 3)
+      const float cterm = -fmaf(off, f, mref) + (PV8 ? kFp8Log2Top : 0.0f);
       float p[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, cterm));
@@ -556,14 +608,59 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
 #pragma unroll
         for (int j = 0; j < 16; ++j) p[j] *= sv[j];   // fold the per-token V scale into P
       }
-      pf[qg][0] = pack8(*reinterpret_cast<const float(*)[8]>(&p[0]));
-      pf[qg][1] = pack8(*reinterpret_cast<const float(*)[8]>(&p[8]));
+      if constexpr (PV8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
+          pk[qg][w] = (uint32_t)word;
+        }
+      } else {
+        pf[qg][0] = pack8(*reinterpret_cast<const float(*)[8]>(&p[0]));
+        pf[qg][1] = pack8(*reinterpret_cast<const float(*)[8]>(&p[8]));
+      }
     }
 
     // ---- O^T += V^T P^T (and the row sums against an all-ones block) ---------
-    if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(1);
+    if constexpr (PV8) {
+      if (resc8) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+        for (int c = 0; c < D / 32; ++c) O8[c] *= al8;
+        L8 *= al8;
+      }
+    }
+    if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(1);
+    if constexpr (PV8) {
+      // B = P^T for the wave's 32 queries: rows 0/1 of the 16-lane groups
+      // exchange with rows 2/3 so that lane l holds query l % 32 (query group
+      // (l / 16) % 2) and keys of lane groups 2*(l/32), 2*(l/32)+1 as bytes
+      // 0..15 and 16..31 (v_permlane16_swap: odd rows of the first operand
+      // trade places with even rows of the second).
+      v8i_t bop;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const auto xy = __builtin_amdgcn_permlane16_swap(pk[0][w], pk[1][w], false, false);
+        bop[w] = (int)xy[0];
+        bop[4 + w] = (int)xy[1];
+      }
+      // A = V^T: lane l reads channel 32*cb + l%32, the same key chunks (the
+      // V blocks store them swizzled by (channel / 4) % 4)
+      const uint8_t* vt = reinterpret_cast<const uint8_t*>(s_v[buf]);
+      const int hh = lane >> 5;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const int ch = 32 * cb + (lane & 31), sw = (ch >> 2) & 3;
+        const v4i lo = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh) ^ sw));
+        const v4i hi = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh + 1) ^ sw));
+        const v8i_t aop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        O8[cb] = mfma_fp8_32x32x64(aop, bop, O8[cb]);
+      }
+      const v8i_t ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                           0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+      L8 = mfma_fp8_32x32x64(ones8, bop, L8);
+    }
+#pragma unroll
+    for (int half = 0; half < (PV8 ? 0 : 2); ++half) {
       const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
@@ -585,6 +682,59 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   }
 
   // ---- normalize and store ----------------------------------------------------
+  if constexpr (PV8) {
+    // lane l: query l % 32 (group (l/16) % 2, row l % 16); element 4*i4 + e of
+    // O8[cb] is channel 32*cb + 8*i4 + 4*(l/32) + e
+    const int qgl = (lane >> 4) & 1;
+    const float l = L8[0];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (qi[qgl] < Tq) {
+      const int64_t orow = a.q_rows.packed ? (q_row0 + qi[qgl]) * a.o_st
+                                           : (int64_t)z * a.o_sb + (int64_t)qi[qgl] * a.o_st;
+      const int64_t ob = orow + (int64_t)qh[qgl] * a.o_sh;
+      const float* vsc = a.v8_scale + ((int64_t)z * Hkv + kvh) * D;
+      const float* vmu = a.v_mean != nullptr && l > 0.0f ? a.v_mean + ((int64_t)z * Hkv + kvh) * D : nullptr;
+      if (a.lse != nullptr && lane < 32) {
+        const int64_t li = a.q_rows.row_at(z, qh[qgl], Hq, qi[qgl]);
+        // l sums P * 448 * 2^-3: ln(sum exp(score)) = ln2 * (m + log2(l) - log2(448) + 3)
+        float lse = l > 0.0f ? 0.69314718055994531f * (m_run[qgl] + log2f(l) - kFp8Log2Top) : kNegInf;
+        if (a.lse_corr != nullptr) lse += a.lse_corr[li];
+        a.lse[li] = lse;
+      }
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int c0 = 32 * cb + 8 * i4 + 4 * (lane >> 5);
+          const float4 sc4 = *reinterpret_cast<const float4*>(vsc + c0);
+          v4f o = {O8[cb][4 * i4] * inv * sc4.x, O8[cb][4 * i4 + 1] * inv * sc4.y,
+                   O8[cb][4 * i4 + 2] * inv * sc4.z, O8[cb][4 * i4 + 3] * inv * sc4.w};
+          if (vmu != nullptr) {
+            const float4 mu = *reinterpret_cast<const float4*>(vmu + c0);
+            o[0] += mu.x;
+            o[1] += mu.y;
+            o[2] += mu.z;
+            o[3] += mu.w;
+          }
+          const int64_t oi = ob + c0;
+          if (a.out_bf16) {
+            uint2 w;
+            w.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+            w.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = w;
+          } else if (a.out_f16) {
+            uint2 w;
+            w.x = f32_to_f16_bits(o[0]) | (f32_to_f16_bits(o[1]) << 16);
+            w.y = f32_to_f16_bits(o[2]) | (f32_to_f16_bits(o[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = w;
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     const float l = kRowSumMfma ? Ls[qg][0] : group4_sum(l_run[qg]);
@@ -648,7 +798,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
 #define QA_FLASH_D256_NW_PAGED 12
 #endif
 
-template <int D, int VK, bool DENSE, bool CAUSAL>
+template <int D, int VK, bool DENSE, bool CAUSAL, bool PV8 = false>
 hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
   // d = 256: waves of 16 rows (one workgroup per CU: its double-buffered
   // tiles take 99 KB of LDS), 8 waves for dense, 12 for the paged prefill,
@@ -667,13 +817,20 @@ hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
     total = a.q_rows.nblocks(QT) * a.Hq;
   }
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  k_flash<D, QG, NW, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
+  if constexpr (PV8) {
+    if constexpr (QG == 2 && D <= 128) k_flash<D, QG, NW, VK, DENSE, CAUSAL, true><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
+    else return hipErrorInvalidValue;    // FP8 P.V needs two query groups per wave
+  } else {
+    k_flash<D, QG, NW, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t flash_d(const FlashArgs& a, hipStream_t st) {
-  // dense V blocks are always fp16 (the preprocessing converts bf16)
+  // dense V blocks are always fp16 (the preprocessing converts bf16), or E4M3
+  if (a.dense && a.pv_fp8)
+    return a.causal ? run_flash<D, kVF16, true, true, true>(a, st) : run_flash<D, kVF16, true, false, true>(a, st);
   if (a.dense) return a.causal ? run_flash<D, kVF16, true, true>(a, st) : run_flash<D, kVF16, true, false>(a, st);
   return a.v_int8 ? run_flash<D, kVI8, false, true>(a, st) : run_flash<D, kVBf16, false, true>(a, st);
 }

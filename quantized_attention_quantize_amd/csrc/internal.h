@@ -109,6 +109,10 @@ struct SagePrepArgs {
   float* k_mean;          // [B, Hkv, D]
   double* partial;        // fp64 column sums [B, chunks, Hkv*D]
   uint16_t* v_paged;      // V transposed into [k_rows.nblocks(16), Hkv, D, 16] or nullptr
+  // FP8 P.V instead: V in E4M3 blocks [k_rows.nblocks(64), Hkv, D, 64] (v8)
+  // with per-(b, KV head, channel) scales v8_scale [B, Hkv, D]
+  uint8_t* v8;
+  float* v8_scale;
 };
 size_t sage_partial_bytes(int32_t B, int32_t Nk, int32_t Hkv, int32_t D);
 hipError_t launch_sage_prep(const SagePrepArgs& a, hipStream_t st);
@@ -171,10 +175,12 @@ struct FlashArgs {
   const float* lse_corr;   // dense: added to lse (smooth_k correction, same layout), or nullptr
   Rows q_rows, k_rows;     // dense: sequence geometry (varlen when q_rows.packed)
   const int32_t* q_map;    // varlen: sequence of each packed 128-row query block, -1 for gaps
+  const float* v8_scale;   // dense FP8 P.V: per-(b, KV head, channel) V scales (v_blocks holds E4M3 blocks)
   int32_t num_seqs, Hq, Hkv, G, D, max_blocks, max_seqlen_q;
   int32_t Nq, Nk;          // dense only
   float scale_log2;
   bool dense, causal, v_int8, v_f16, out_bf16, out_f16;
+  bool pv_fp8;             // dense: FP8 P.V (head_dim 64 or 128)
 };
 hipError_t launch_flash(const FlashArgs& a, hipStream_t st);
 

@@ -196,10 +196,12 @@ __global__ __launch_bounds__(256) void k_block_map(Rows rows, int32_t R, int32_t
 // (b, t, h, c) of k lives at b*sb + t*st + h*sh + c (batched) or at
 // (rows.start(b) + t)*st + h*sh + c (varlen). Chunks are counted from the
 // start of each sequence; chunks past its end hold zeros.
-template <bool BF16>
+// ABSMAX: the chunk's largest |fl32(x - mu[b, c])| instead of the sum (mu
+// optional), for the per-channel FP8 scale of V.
+template <bool BF16, bool ABSMAX = false>
 __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, Rows rows, const int32_t* map,
                                                 int32_t D, int32_t HD, int64_t sb, int64_t st, int64_t sh,
-                                                double* __restrict__ partial) {
+                                                double* __restrict__ partial, const float* __restrict__ mu = nullptr) {
   const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
   // batched grid (column groups, chunks, B); varlen (packed chunks, column groups)
   int b = blockIdx.z, chunk = blockIdx.y, cg = blockIdx.x;
@@ -216,12 +218,23 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
   const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, rows.len(b));
   const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
   const uint16_t* base = k + seq0 + (int64_t)(c8 / D) * sh + c8 % D;
+  float m8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ABSMAX && mu != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m8[i] = mu[(int64_t)b * HD + c8 + i];
+  }
   auto add = [&](uint4 w) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += (double)half_to_f32<BF16>(ws[i] & 0xFFFFu);
-      acc[2 * i + 1] += (double)half_to_f32<BF16>(ws[i] >> 16);
+      const float lo = half_to_f32<BF16>(ws[i] & 0xFFFFu), hi = half_to_f32<BF16>(ws[i] >> 16);
+      if constexpr (ABSMAX) {
+        acc[2 * i] = fmax(acc[2 * i], (double)fabsf(lo - m8[2 * i]));
+        acc[2 * i + 1] = fmax(acc[2 * i + 1], (double)fabsf(hi - m8[2 * i + 1]));
+      } else {
+        acc[2 * i] += (double)lo;
+        acc[2 * i + 1] += (double)hi;
+      }
     }
   };
   int t = t0;
@@ -268,6 +281,95 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
       const double tot = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
       mean[i] = (float)(tot / (double)Nk);
     }
+  }
+}
+
+// FP8 scale of V per (b, KV head, channel): fl32(max |V'| / 448) from the
+// chunk maxima of k_colsum<.., true> (0 for an empty sequence). As k_mean:
+// 64 columns per workgroup, four threads per column.
+__global__ __launch_bounds__(256) void k_vscale(const double* __restrict__ partial, Rows rows, int32_t HD,
+                                                float* __restrict__ vscale) {
+  __shared__ double red[4][64];
+  const int col = threadIdx.x & 63, slice = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + col;   // b * HD + c
+  const bool live = i < (int64_t)rows.B * HD;
+  double m = 0.0;
+  if (live) {
+    const int b = (int)(i / HD), c = (int)(i % HD);
+    const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
+    const int used = (rows.len(b) + kSumChunk - 1) / kSumChunk;
+    const double* p = partial + (int64_t)b * chunks * HD + c;
+    for (int j = slice; j < used; j += 4) m = fmax(m, p[(int64_t)j * HD]);
+  }
+  red[slice][col] = m;
+  __syncthreads();
+  if (slice == 0 && live)
+    vscale[i] = __fdiv_rn((float)fmax(fmax(red[0][col], red[1][col]), fmax(red[2][col], red[3][col])), 448.0f);
+}
+
+// V -> FP8 (E4M3) blocks of 64 tokens for the FP8 P.V product:
+// [block64][H][D channels][64 bytes]; code = E4M3(fl32(fl32(V - mu) / s_c))
+// (hardware conversion: round to nearest even), 0 where s_c = 0 and for
+// tokens past the sequence. Within a channel's 64 bytes, 16-byte chunk q holds
+// the keys the attention kernel's lane group q owns after its S^T product,
+// key(q, j) = 32*(j/8) + 8*q + j%8, stored at chunk q ^ ((c/4) % 4) so that the
+// kernel's 16-byte LDS reads of 16 consecutive channels hit distinct banks.
+// Thread (8-channel group, q) reads those 16 token rows of its 8 channels and
+// writes the 8 chunks directly (no LDS); a workgroup covers D/32 blocks x heads
+// worth of threads: 256 threads = 256 / (4 * D/8) (block, head) units.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_v8_blocks(const uint16_t* __restrict__ v, Rows rows, const int32_t* map,
+                                                   int32_t H, int64_t sb, int64_t st, int64_t sh,
+                                                   const float* __restrict__ vmean, const float* __restrict__ vscale,
+                                                   uint8_t* __restrict__ out) {
+  constexpr int TPU = 4 * (D / 8);                 // threads per (block, head)
+  constexpr int UPW = 256 / TPU;                   // (block, head) units per workgroup
+  const int unit = threadIdx.x / TPU, r = threadIdx.x % TPU;
+  const int q = r & 3, c8 = (r >> 2) * 8;
+  const int h = blockIdx.y * UPW + unit;
+  if (h >= H) return;
+  const BlockRef br = block_of(rows, map, 64, blockIdx.z);
+  if (br.b < 0) return;
+  const int blk = br.blk, b = br.b;
+  const int N = rows.len(b);
+  if (blk * 64 >= N) return;
+  const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
+  float mu[8], sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    mu[i] = vmean != nullptr ? vmean[((int64_t)b * H + h) * D + c8 + i] : 0.0f;
+    sc[i] = vscale[((int64_t)b * H + h) * D + c8 + i];
+  }
+  float x[16][8];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int t = blk * 64 + 32 * (j >> 3) + 8 * q + (j & 7);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (t < N) w = *reinterpret_cast<const uint4*>(v + seq0 + (int64_t)t * st + (int64_t)h * sh + c8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[j][2 * i] = half_to_f32<BF16>(ws[i] & 0xFFFFu);
+      x[j][2 * i + 1] = half_to_f32<BF16>(ws[i] >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float val = vmean != nullptr ? x[j][i] - mu[i] : x[j][i];
+      x[j][i] = (t < N && sc[i] > 0.0f) ? __fdiv_rn(val, sc[i]) : 0.0f;
+    }
+  }
+  uint8_t* dst = out + ((rows.block0(b, 64) + blk) * H + h) * (int64_t)D * 64;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c8 + i;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k][i], x[4 * k + 1][i], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2][i], x[4 * k + 3][i], word, true);
+      w[k] = (uint32_t)word;
+    }
+    *reinterpret_cast<uint4*>(dst + c * 64 + 16 * (q ^ ((c >> 2) & 3))) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -489,16 +591,27 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
     k_block_quant<D, 64, BF16><<<grid(a.k_rows, 64, a.Hkv), 256, 0, s>>>(
         (const uint16_t*)a.k, a.k_rows, a.k_map64, a.Hkv, a.k_sb, a.k_st, a.k_sh, a.k_mean, a.k_i8, a.k_paged,
         a.k_scale, nullptr, 1, 0.0f, nullptr);
-    if (a.v_paged != nullptr) {
+    if (a.v_paged != nullptr || a.v8 != nullptr) {
       if (a.smooth_v) {
         // the column sums of K are consumed: the buffer takes those of V
         k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.k_map64, D, HD, a.v_sb, a.v_st,
                                             a.v_sh, a.partial);
         k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, true, a.v_mean);
       }
-      k_v_blocks<D, BF16><<<grid(a.k_rows, 16, a.Hkv), 256, 0, s>>>(
-          (const uint16_t*)a.v, a.k_rows, a.k_map16, a.Hkv, a.v_sb, a.v_st, a.v_sh,
-          a.smooth_v ? a.v_mean : nullptr, a.v_paged);
+      const float* vmu = a.smooth_v ? a.v_mean : nullptr;
+      if (a.v8 != nullptr) {
+        // per-channel maxima of V (- mu), the FP8 scales, then the E4M3 blocks
+        k_colsum<BF16, true><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.k_map64, D, HD, a.v_sb,
+                                                  a.v_st, a.v_sh, a.partial, vmu);
+        k_vscale<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, a.v8_scale);
+        constexpr int UPW = 256 / (4 * (D / 8));     // heads per workgroup
+        dim3 g8 = grid(a.k_rows, 64, (a.Hkv + UPW - 1) / UPW);
+        k_v8_blocks<D, BF16><<<g8, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.k_map64, a.Hkv, a.v_sb, a.v_st,
+                                               a.v_sh, vmu, a.v8_scale, a.v8);
+      } else {
+        k_v_blocks<D, BF16><<<grid(a.k_rows, 16, a.Hkv), 256, 0, s>>>(
+            (const uint16_t*)a.v, a.k_rows, a.k_map16, a.Hkv, a.v_sb, a.v_st, a.v_sh, vmu, a.v_paged);
+      }
     }
   }
   return hipGetLastError();

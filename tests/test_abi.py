@@ -179,7 +179,7 @@ def test_prefill_and_dense_validation(qa):
 def test_dense_options_validation(qa):
     L = qa.lib
     d = qa.DenseParams(2, 100, 90, 8, 4, 128, qa.QA_DT_BF16, 1, 0, 0.0, qa.QA_DT_F32)
-    o = qa.DenseOptions(qa.QA_LAYOUT_HND, 1)
+    o = qa.DenseOptions(qa.QA_LAYOUT_HND, 1, 0)
     plain = L.qa_dense_sage_workspace_size(ctypes.byref(d))
     need = L.qa_dense_sage_ex_workspace_size(ctypes.byref(d), ctypes.byref(o))
     # the options call adds the V mean (2 x 4 x 128 fp32) and the LSE correction (2 x 8 x 100 fp32)
@@ -191,6 +191,13 @@ def test_dense_options_validation(qa):
     assert ex(None, plain, None) == qa.QA_ERR_WORKSPACE_TOO_SMALL      # the plain call's size is not enough
     assert ex(ctypes.byref(o), need, ctypes.c_void_p(0x10002)) == qa.QA_ERR_INVALID_ARG  # lse not 4-byte aligned
     assert b"lse" in L.qa_last_error()
+    o.pv_fp8 = 1                                           # FP8 P.V: E4M3 V blocks of 64 keys + channel scales
+    need8 = L.qa_dense_sage_ex_workspace_size(ctypes.byref(d), ctypes.byref(o))
+    # 90 keys: 6 blocks of 16 (fp16) give way to 2 blocks of 64 (E4M3), plus 2 x 4 x 128 fp32 channel scales
+    assert need8 == need - 2 * 6 * 4 * 128 * 16 * 2 + 2 * 2 * 4 * 128 * 64 + 2 * 4 * 128 * 4
+    d.head_dim = 256
+    assert ex(ctypes.byref(o), 1 << 40, None) == qa.QA_ERR_UNSUPPORTED
+    d.head_dim, o.pv_fp8 = 128, 0
     o.layout = 7
     assert ex(ctypes.byref(o), need, None) == qa.QA_ERR_INVALID_ARG
     assert b"layout 7" in L.qa_last_error()
@@ -200,7 +207,7 @@ def test_dense_options_validation(qa):
 
 def test_dense_varlen_validation(qa):
     L = qa.lib
-    p = qa.VarlenParams(3, 700, 900, 400, 500, 8, 2, 128, qa.QA_DT_F16, 1, 1, 1, 0.0, qa.QA_DT_F32)
+    p = qa.VarlenParams(3, 700, 900, 400, 500, 8, 2, 128, qa.QA_DT_F16, 1, 1, 1, 0.0, qa.QA_DT_F32, 0)
     need = L.qa_dense_sage_varlen_workspace_size(ctypes.byref(p))
     # packed blocks: 900/16 + 3 = 59 K blocks of 2 x 128 x 16 (int8 codes + fp16 V); Q codes 700 x 8 x 128
     assert need >= 700 * 8 * 128 + 59 * 2 * 128 * 16 * 3

@@ -520,6 +520,81 @@ def test_dense_options_full_size_sampled(qa):
             _lse_close(l[b, h, rows], want_lse[b, h, rows] + corr[b, h, rows], f"dense options LSE b={b} h={h}")
 
 
+# FP8 (E4M3) P.V: parity with the oracle's FP8 forward (same roundings; the
+# GPU's P differs from the oracle's in the last fp32 bits, which moves an
+# E4M3 rounding now and then), and distance to the 16-bit path of the order
+# of the E4M3 step
+FP8_REL_L2, FP8_MAX_ABS = 2e-3, 2e-2
+
+FP8_CASES = [
+    # (B, Nq, Nk, Hq, Hkv, d, dtype, causal, smooth_v)
+    (1, 200, 200, 2, 2, 64, "f16", False, False),
+    (2, 300, 257, 4, 2, 128, "bf16", True, True),
+    (1, 129, 400, 6, 1, 128, "f16", True, False),
+    (2, 77, 150, 4, 4, 64, "f16", False, True),
+]
+
+
+def _fp8_close(got, want, what):
+    r = rel_l2(got, want)
+    m = float(np.max(np.abs(got - want)))
+    say(f"  {what}: rel_l2={r:.3e} max_abs={m:.3e}")
+    assert np.all(np.isfinite(got)) and r <= FP8_REL_L2 and m <= FP8_MAX_ABS, f"{what}: rel L2 {r:.3e}, max abs {m:.3e}"
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{c[6]}_{'causal' if c[7] else 'full'}{'_sv' if c[8] else ''}")
+def test_dense_fp8pv_parity(qa, case):
+    B, Nq, Nk, Hq, Hkv, d, dt, causal, smooth_v = case
+    say(f"dense fp8 P.V {case}")
+    spec = DenseSpec("dn_fp8", 611 + d, B, Hq, Hkv, Nq, Nk, d, k_bias_std=3.0, dtype=dt, v_bias_std=2.0)
+    inp = dense_inputs(spec)
+    out, lse = qa.dense_sage_attention_ex(dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt),
+                                          is_causal=causal, smooth_v=smooth_v, return_lse=True, pv_fp8=True)
+    torch.cuda.synchronize()
+    quant = oracle.sage_quantize(inp.q, inp.k, dt)
+    want, want_lse = oracle.dense_sage_attention_fp8pv(quant, inp.v, dt, causal=causal, smooth_v=smooth_v,
+                                                       return_lse=True)
+    got = out.cpu().numpy()
+    _fp8_close(got, want, "fp8 P.V vs oracle")
+    corr = oracle.sage_lse_correction(inp.q, quant["k_mean"], dt)
+    _lse_close(lse.cpu().numpy(), want_lse + corr, "fp8 P.V LSE")
+    exact = oracle.sage_forward(inp.q, inp.k, inp.v, dt, causal=causal, smooth_v=smooth_v)
+    r = rel_l2(got, exact)
+    say(f"  fp8 P.V vs 16-bit P path: rel_l2={r:.3e}")
+    assert r < 3e-2
+
+
+def test_dense_fp8pv_full_size_sampled(qa):
+    spec = dense_sage()
+    say(f"dense fp8 P.V full size {spec.name}")
+    inp = dense_inputs(spec)
+    out = qa.dense_sage_attention_ex(dev_bits(inp.q, "f16"), dev_bits(inp.k, "f16"), dev_bits(inp.v, "f16"),
+                                     is_causal=True, pv_fp8=True)
+    torch.cuda.synchronize()
+    quant = oracle.sage_quantize(inp.q, inp.k, "f16")
+    rows = np.array([0, 1, 127, 128, 4095, 8191])
+    want = oracle.dense_sage_attention_fp8pv(quant, inp.v, "f16", causal=True, rows=rows, heads=[0, 17, 31])
+    g = out.cpu().numpy()
+    for b in range(2):
+        for h in (0, 17, 31):
+            _fp8_close(g[b, rows, h], want[b, rows, h], f"fp8 P.V b={b} h={h}")
+
+
+def test_dense_fp8pv_varlen_matches_one_sequence_calls(qa):
+    spec = VarlenSpec("vl8", 93, [130, 7, 300], [200, 7, 260], 4, 2, 128, dtype="bf16", v_bias_std=2.0)
+    inp = varlen_inputs(spec)
+    say("dense fp8 P.V varlen")
+    dt = "bf16"
+    cu_q, cu_k = torch.from_numpy(inp.cu_q).cuda(), torch.from_numpy(inp.cu_k).cuda()
+    out = qa.dense_sage_attention_varlen(dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt), cu_q, cu_k,
+                                         300, 260, is_causal=True, pv_fp8=True)
+    for b in range(3):
+        q0, q1, k0, k1 = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        one = qa.dense_sage_attention_ex(dev_bits(inp.q[None, q0:q1], dt), dev_bits(inp.k[None, k0:k1], dt),
+                                         dev_bits(inp.v[None, k0:k1], dt), is_causal=True, pv_fp8=True)
+        assert torch.equal(one[0], out[q0:q1]), f"sequence {b}"
+
+
 # packed variable-length dense
 VARLEN = [
     # (seq_q, seq_k, Hq, Hkv, d, dtype, causal, smooth_v)

@@ -132,10 +132,12 @@ MUTATIONS = [
      pins.test_fp8pv_is_within_fp8_error_of_the_16bit_path, ()),
     ("fp8_v_scale_dropped", ofp8, "dense_sage_attention_fp8pv", "* sv[b, kvh].astype(np.float64)", "* 1.0",
      pins.test_fp8pv_constant_values_come_back, ()),
-    ("fp8_p_not_rounded", ofp8, "dense_sage_attention_fp8pv", "e4m3_round(E4M3_MAX * np.exp(", "(E4M3_MAX * np.exp(",
+    ("fp8_p_not_rounded", ofp8, "dense_sage_attention_fp8pv", "e4m3_round(top * np.exp(", "(top * np.exp(",
      pins.test_fp8pv_one_visible_key_and_two_key_closed_form, ()),
     ("fp8_v_not_rounded", ofp8, "v_fp8_per_channel", "vals = np.where(live[:, None], e4m3_round(r), 0.0)",
      "vals = np.where(live[:, None], r, 0.0)", pins.test_v_fp8_per_channel_codes, ()),
+    ("fp8_slack_in_natural_units", ofp8, "dense_sage_attention_fp8pv", "move = mt > m + slack * np.log(2.0)",
+     "move = mt > m + slack * 8", pins.test_fp8pv_slack_changes_only_the_rounding, ()),
     ("fp8_ties_away", ofp8, "e4m3_encode", "((dhi == dlo) & (_POS_CODES[hi] % 2 == 0))", "(dhi == dlo)",
      pins.test_e4m3_landmarks_ties_and_saturation, ()),
 ]

@@ -773,9 +773,10 @@ def test_fp8pv_one_visible_key_and_two_key_closed_form():
     v8, sv = oracle.v_fp8_per_channel(oq.widen(v, "f16"))
     # row 0 sees key 0 only: its FP8-rounded value times the channel scale
     np.testing.assert_allclose(out[0, 0], v8[0, 0] * sv[0], rtol=1e-12)
-    # row 1 sees keys 0 and 1: P8 = (E4M3(448 e^(s0 - m)), E4M3(448 e^(s1 - m)))
+    # row 1 sees keys 0 and 1 (one tile, reference = their maximum):
+    # P8 = E4M3(56 e^(s - m)), 56 = 448 * 2^-3 under the default slack of 3
     s = _int_dot_scores(quant, 0, 1, [0, 1])
-    p = oracle.e4m3_round(448.0 * np.exp(s - s.max()))
+    p = oracle.e4m3_round(56.0 * np.exp(s - s.max()))
     want = (p[0] * v8[0, 0, 0] + p[1] * v8[0, 1, 0]) / p.sum() * sv[0, 0]
     np.testing.assert_allclose(out[0, 1, 0], want, rtol=1e-12)
 
@@ -784,6 +785,21 @@ def _int_dot_scores(quant, b, row, keys, h=0):
     q = quant["q_i8"][b, row, h].astype(np.float64)
     k = quant["k_i8"][b, keys, h].astype(np.float64)
     return (k @ q) * float(quant["q_scale"][b, h, row // 128]) * quant["k_scale"][b, h, np.asarray(keys) // 64] / 8.0
+
+
+def test_fp8pv_slack_changes_only_the_rounding():
+    """The reference slack only moves where P is rounded: against the
+    16-bit P path every slack has the error of the E4M3 step, within 10% of
+    the exact-running-maximum variant (slack 0), and a huge slack (the first
+    tile's maximum stays the reference) too, as long as nothing overflows."""
+    inp, quant, v = _fp8_case(N=200, Nk=300)
+    exact = oracle.dense_sage_attention(quant, v, "f16")
+    err = lambda x: np.linalg.norm(x - exact) / np.linalg.norm(exact)
+    e0 = err(oracle.dense_sage_attention_fp8pv(quant, v, "f16", slack=0.0))
+    assert 1e-3 < e0 < 5e-2
+    for sl in (0.5, 3.0):
+        a = oracle.dense_sage_attention_fp8pv(quant, v, "f16", slack=sl)
+        assert err(a) < 1.1 * e0 and not np.array_equal(a, exact)
 
 
 def test_fp8pv_is_within_fp8_error_of_the_16bit_path():
