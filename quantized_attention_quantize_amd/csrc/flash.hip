@@ -93,6 +93,19 @@ __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
   return r;
 }
 
+// max across the four 16-lane groups of an integer (no float canonicalization)
+__device__ __forceinline__ int group4_max_i32(int v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)b[0], (int)b[1]);
+}
+
+// Initial softmax reference: finite, so that no step needs a test for an
+// empty row (exp2 of anything minus it is 0, and a row's first visible key
+// always moves it).
+constexpr float kMRunInit = -1.0e30f;
+
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -263,7 +276,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   v4f Ls[QG];                                  // row sums from the matrix units
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
-    m_run[qg] = kNegInf;
+    m_run[qg] = kMRunInit;
     l_run[qg] = 0.0f;
     Ls[qg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -519,6 +532,17 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       for (int j = 0; j < 16; ++j) sv[j] = s_vs[buf][32 * (j >> 3) + tl + (j & 7)];
     }
 
+    // dense: one factor sQ_blk * sK_blk * scale for the whole workgroup and
+    // tile (one 128-row query block, one key block), held as a scalar; the
+    // folded accumulator offset costs half an ulp of offset*f in the
+    // exponent, so when offset*f > 2^12 (scores of large-magnitude inputs)
+    // the offset is subtracted exactly instead
+    float fw = 0.0f;
+    bool exact_off = false;
+    if constexpr (DENSE) {
+      fw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qsc[0] * tsc)));
+      exact_off = kMagic && !(kOffset * fw <= 4096.0f);
+    }
     v8h pf[QG][2];
     uint32_t pk[QG][4];                          // FP8 P.V: byte j of word w is p[4w + j]
     float al8 = 1.0f;                            // FP8 P.V: rescale of this lane's query (32x32 layout)
@@ -528,9 +552,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       // score_j = x[j] * f with one lane factor f >= 0 (dense: the Q and K
       // block scales; paged: the Q scale, sK folded into x)
       float x[16], f, mx;
+      int im = 0;
       if constexpr (DENSE) {
-        f = qsc[qg] * tsc;
-        int im = max(acc[qg][0][0], acc[qg][0][1]);
+        f = fw;
+        im = max(acc[qg][0][0], acc[qg][0][1]);
 #pragma unroll
         for (int j = 2; j < 16; j += 2) im = max(im, max(acc[qg][j >> 2][j & 3], acc[qg][j >> 2][(j & 3) + 1]));
 #pragma unroll
@@ -558,23 +583,26 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
           mx = ok ? fmaxf(mx, x[j]) : mx;
         }
       }
-      // The folded offset costs half an ulp of offset*f in the exponent; when
-      // offset*f > 2^12 (scores of large-magnitude inputs) the offset is
-      // subtracted exactly instead. f is the same for the whole workgroup
-      // (one 128-row query block, one key block), so this branch is uniform.
       float off = kMagic ? kOffset : 0.0f;
-      if (kMagic && !(kOffset * f <= 4096.0f)) {
+      if (exact_off) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] -= kOffset;
         mx -= kOffset;
         off = 0.0f;
       }
-      float mt = mx == kNegInf ? kNegInf : (mx - off) * f;
-      mt = group4_max(mt);
+      float mt;
+      if (DENSE && kMagic && !need_mask) {
+        // row maximum of the raw accumulators (floats in [2^23, 2^24) order
+        // like their bit patterns), across the four lane groups, then scaled
+        mt = (__int_as_float(group4_max_i32(im)) - kOffset) * f;
+      } else {
+        mt = mx == kNegInf ? kNegInf : (mx - off) * f;
+        mt = group4_max(mt);
+      }
       // lazy rescale: move the reference only when it is exceeded by > 2^8
       if (__any(mt > m_run[qg] + (PV8 ? kFp8Slack : kRescaleSlack))) {
         const float m_new = fmaxf(m_run[qg], mt);
-        const float alpha = fast_exp2(m_run[qg] - (m_new == kNegInf ? 0.0f : m_new));
+        const float alpha = fast_exp2(m_run[qg] - m_new);
         l_run[qg] *= alpha;
         if constexpr (PV8) {
           // lane l holds query l % 32 of the wave in the 32x32 accumulators;
@@ -588,7 +616,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
         }
         m_run[qg] = m_new;
       }
-      const float mref = m_run[qg] == kNegInf ? 0.0f : m_run[qg];
+      const float mref = m_run[qg];
       // x*f + cterm = score - mref (FP8 P.V: + log2(448) - 3)
       const float cterm = -fmaf(off, f, mref) + (PV8 ? kFp8Log2Top : 0.0f);
       float p[16];
