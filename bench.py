@@ -275,6 +275,18 @@ def cpu_baseline(spec, inp, budget_s, gpu_out=None):
         res["gpu_parity"] = {"rel_l2": float(np.linalg.norm(got - want) / np.linalg.norm(want)),
                              "max_abs": float(np.max(np.abs(got - want))),
                              "bar": "rel L2 <= 1e-3, max abs <= 2e-3 (fp32 output)"}
+        # the method's own error: the GPU output against textbook fp64
+        # attention of the unquantized bf16 query, keys and values
+        G = spec.num_q_heads // spec.num_kv_heads
+        q = oracle.widen(inp.q, "bf16").astype(np.float64)[0]                  # [Hq, d]
+        k = oracle.widen(inp.k, "bf16").astype(np.float64)                      # [ctx, Hkv, d]
+        v = oracle.widen(inp.v, "bf16").astype(np.float64)
+        sc = 1.0 / np.sqrt(spec.head_dim)
+        exact = np.stack([oracle.attention_fp64(q[h:h + 1], k[:, h // G], v[:, h // G], sc)[0]
+                          for h in range(spec.num_q_heads)])
+        g0 = got.reshape(exact.shape)
+        res["gpu_vs_unquantized_fp64"] = {"rel_l2": float(np.linalg.norm(g0 - exact) / np.linalg.norm(exact)),
+                                          "max_abs": float(np.max(np.abs(g0 - exact)))}
     return res
 
 
