@@ -440,7 +440,9 @@ qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, co
  * causal mask is applied on the diagonal tiles only and tiles above the
  * diagonal are skipped. Causal alignment is bottom-right: query i sees keys
  * j <= i + (seq_k - seq_q). Runs the preprocessing above into the workspace
- * first (full chain). num_q_heads % num_kv_heads == 0.
+ * first (full chain). num_q_heads % num_kv_heads == 0; seq_q and seq_k at
+ * most 65535 * 16 = 1,048,560 (QA_ERR_UNSUPPORTED beyond; the varlen call
+ * has no such bound).
  *
  *   q, k, v   NHD bf16/f16 (dtype); v [batch, seq_k, num_kv_heads, head_dim]
  *   out       [batch, seq_q, num_q_heads, head_dim] in out_dtype

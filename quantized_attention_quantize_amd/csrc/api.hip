@@ -120,6 +120,9 @@ qa_status_t check_dense(const qa_dense_params_t* p) {
              QA_ERR_UNSUPPORTED, "out_dtype must be F32, F16 or BF16");
   QA_REQUIRE(supported_dim(p->head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", p->head_dim);
   QA_REQUIRE(p->batch <= 65535 && p->num_q_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
+  // the preprocessing grids put 16-token blocks in their second dimension
+  QA_REQUIRE(p->seq_q <= 65535 * 16 && p->seq_k <= 65535 * 16, QA_ERR_UNSUPPORTED, "sequence longer than %d tokens",
+             65535 * 16);
   return QA_OK;
 }
 

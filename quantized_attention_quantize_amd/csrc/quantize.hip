@@ -164,15 +164,18 @@ __global__ __launch_bounds__(256) void k_producer(ProducerArgs a, int64_t qblock
 
 constexpr int kSumChunk = 64;  // tokens per partial column sum (= the K block, so varlen chunks share its map)
 
-// Sequence and block of this workgroup. Batched grids are (blocks, heads, B);
-// varlen grids run over all packed blocks, (rows.nblocks(R), heads), and
-// map[j] names the sequence of packed block j (-1 for the gap before a
-// sequence): only workgroups with work are launched beyond one per gap.
+// Sequence and block of this workgroup. Batched grids are (heads, blocks, B),
+// heads fastest so that consecutive workgroups read neighbouring pieces of the
+// same token rows; varlen grids run over all packed blocks,
+// (rows.nblocks(R), heads), and map[j] names the sequence of packed block j
+// (-1 for the gap before a sequence): only workgroups with work are launched
+// beyond one per gap. head_of gives the head index of either grid.
 struct BlockRef {
   int b, blk;
 };
+__device__ __forceinline__ int head_of(const Rows& rows) { return rows.packed ? (int)blockIdx.y : (int)blockIdx.x; }
 __device__ __forceinline__ BlockRef block_of(const Rows& rows, const int32_t* map, int R, int zdim_b) {
-  if (!rows.packed) return {zdim_b, (int)blockIdx.x};
+  if (!rows.packed) return {zdim_b, (int)blockIdx.y};
   const int b = map[blockIdx.x];
   if (b < 0 || b >= rows.B) return {-1, 0};
   return {b, (int)(blockIdx.x - rows.block0(b, R))};
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(256) void k_v8_blocks(const uint16_t* __restrict__ 
   constexpr int UPW = 256 / TPU;                   // (block, head) units per workgroup
   const int unit = threadIdx.x / TPU, r = threadIdx.x % TPU;
   const int q = r & 3, c8 = (r >> 2) * 8;
-  const int h = blockIdx.y * UPW + unit;
+  const int h = head_of(rows) * UPW + unit;
   if (h >= H) return;
   const BlockRef br = block_of(rows, map, 64, blockIdx.z);
   if (br.b < 0) return;
@@ -373,6 +376,23 @@ __global__ __launch_bounds__(256) void k_v8_blocks(const uint16_t* __restrict__ 
   }
 }
 
+// quant_code (clamp(rne(fl32(x / s)), -127, 127)) without a division per
+// value, for |x| <= the block's max (so |x / s| <= 127 and no clamp is
+// needed): with rs = fl32(1/s), y = fl32(x * rs) lies within
+// 1.5 * 2^-23 * |x/s| <= 2.3e-5 of fl32(x / s), so the nearest integer to y
+// is the code unless y is within 6.1e-5 of a half-integer; those rare values
+// take the exact quotient. Adding 1.5 * 2^23 rounds to the nearest integer
+// (ties to even) and leaves the code in the low byte of the float's bits.
+// Callers use it only while rs is finite and below 3e38.
+__device__ __forceinline__ uint32_t quant_byte_rcp(float x, float s, float rs) {
+#pragma clang fp contract(off)
+  constexpr float kM = 12582912.0f;   // 1.5 * 2^23
+  const float y = x * rs;
+  float t = y + kM;
+  if (fabsf(y - (t - kM)) > 0.49993896484375f) t = rintf(__fdiv_rn(x, s)) + kM;
+  return __float_as_uint(t) & 0xFFu;
+}
+
 // Per-block quantization of one (b, head, block) of ROWS tokens x D channels:
 // one scale over all ROWS*D values (after subtracting mu when given).
 // Writes NHD codes (codes_nhd) and/or the blocked K layout (codes_blk).
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   static_assert(ROWS * G8 % 256 == 0, "block must tile the workgroup");
   const BlockRef br = block_of(rows, map, ROWS, blockIdx.z);
   if (br.b < 0) return;
-  const int blk = br.blk, h = blockIdx.y, b = br.b;
+  const int blk = br.blk, h = head_of(rows), b = br.b;
   const int N = rows.len(b);                 // tokens of this sequence
   if (blk * ROWS >= N) return;               // batched grids cover the longest sequence
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -451,6 +471,8 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = quant_scale(amax);
+  const float rs = __fdiv_rn(1.0f, s);
+  const bool fast = rs <= 3.0e38f;         // workgroup-uniform
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int gi = threadIdx.x + 256 * k;
@@ -459,10 +481,13 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int c0 = amax > 0.0f ? quant_code(val[k][i], s) : 0;
-      int c1 = amax > 0.0f ? quant_code(val[k][4 + i], s) : 0;
-      lo |= ((uint32_t)c0 & 0xFFu) << (8 * i);
-      hi |= ((uint32_t)c1 & 0xFFu) << (8 * i);
+      uint32_t c0 = 0, c1 = 0;
+      if (amax > 0.0f) {
+        c0 = fast ? quant_byte_rcp(val[k][i], s, rs) : (uint32_t)quant_code(val[k][i], s) & 0xFFu;
+        c1 = fast ? quant_byte_rcp(val[k][4 + i], s, rs) : (uint32_t)quant_code(val[k][4 + i], s) & 0xFFu;
+      }
+      lo |= c0 << (8 * i);
+      hi |= c1 << (8 * i);
     }
     if (t >= N) lo = hi = 0;
     if (codes_nhd != nullptr && t < N)
@@ -494,7 +519,7 @@ __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v
   __shared__ __attribute__((aligned(16))) uint16_t tile[16][D + 8];
   const BlockRef br = block_of(rows, map, 16, blockIdx.z);
   if (br.b < 0) return;
-  const int blk = br.blk, h = blockIdx.y, b = br.b;
+  const int blk = br.blk, h = head_of(rows), b = br.b;
   const int N = rows.len(b);
   if (blk * 16 >= N) return;                 // batched grids cover the longest sequence
   const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
@@ -568,7 +593,7 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
   const bool vl = a.k_rows.packed;
   // varlen grids run over the packed blocks of all sequences (block maps first)
   auto grid = [&](const Rows& r, int R, int heads) {
-    return vl ? dim3((unsigned)r.nblocks(R), heads, 1) : dim3((unsigned)((r.N + R - 1) / R), heads, a.B);
+    return vl ? dim3((unsigned)r.nblocks(R), heads, 1) : dim3(heads, (unsigned)((r.N + R - 1) / R), a.B);
   };
   if (vl) {
     k_block_map<<<a.B, 256, 0, s>>>(a.q_rows, 128, a.q_map);
