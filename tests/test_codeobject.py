@@ -1,0 +1,90 @@
+"""The device code this repository builds, read back from libqattn.so (CPU
+only): the hot kernels contain the matrix instructions the design relies on,
+the decode kernels use no scratch memory, and no packed fp32 arithmetic was
+generated (the build disables it). Uses the ROCm LLVM tools on our own
+build's code objects; skipped where they are missing."""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "quantized_attention_quantize_amd", "libqattn.so")
+LLVM = "/opt/rocm/llvm/bin"
+TOOLS = {t: os.path.join(LLVM, t) for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")}
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    if not os.path.exists(LIB):
+        pytest.skip("libqattn.so not built")
+    for t in TOOLS.values():
+        if not os.path.exists(t):
+            pytest.skip(f"{t} missing")
+    out = {}
+    with tempfile.TemporaryDirectory() as d:
+        fat = os.path.join(d, "fat.bin")
+        subprocess.run([TOOLS["llvm-objcopy"], "--dump-section", f".hip_fatbin={fat}", LIB, os.path.join(d, "x")],
+                       check=True, capture_output=True)
+        data = open(fat, "rb").read()
+        starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+        assert starts, "no offload bundle in .hip_fatbin"
+        for i, s in enumerate(starts):
+            piece = data[s:starts[i + 1] if i + 1 < len(starts) else len(data)]
+            b = os.path.join(d, f"b{i}.bundle")
+            co = os.path.join(d, f"b{i}.co")
+            open(b, "wb").write(piece)
+            r = subprocess.run([TOOLS["clang-offload-bundler"], "--unbundle", "--type=o", f"--input={b}",
+                                "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], capture_output=True)
+            if r.returncode != 0 or not os.path.exists(co) or os.path.getsize(co) == 0:
+                continue
+            dis = subprocess.run([TOOLS["llvm-objdump"], "-d", "--mcpu=gfx950", co], check=True,
+                                 capture_output=True, text=True).stdout
+            name = None
+            for line in dis.splitlines():
+                m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+                if m:
+                    name = m.group(1)
+                    out[name] = set()
+                    continue
+                if name is not None:
+                    t = line.strip().split()
+                    if t and re.match(r"^[sv]_|^global_|^buffer_|^ds_|^scratch_|^flat_", t[0]):
+                        out[name].add(t[0])
+    assert out, "no gfx950 code object found"
+    return out
+
+
+def _has(ins, op):
+    return any(x == op or x.startswith(op + "_") for x in ins)
+
+
+def _with(kernels, part):
+    ks = {n: ins for n, ins in kernels.items() if part in n}
+    assert ks, f"no kernel named like {part}"
+    return ks
+
+
+def test_decode_kernels_use_int8_and_bf16_matrix_units_and_no_scratch(kernels):
+    ks = _with(kernels, "k_decode")
+    assert any(_has(i, "v_mfma_i32_16x16x64_i8") and _has(i, "v_mfma_f32_16x16x32_bf16") for i in ks.values())
+    for n, ins in ks.items():
+        assert not any(x.startswith("scratch_") for x in ins), f"{n} spills to scratch"
+
+
+def test_flash_kernels_use_the_matrix_units(kernels):
+    ks = _with(kernels, "k_flash")
+    assert all(_has(i, "v_mfma_i32_16x16x64_i8") for i in ks.values())        # INT8 QK in every variant
+    assert any(_has(i, "v_mfma_f32_16x16x32_f16") for i in ks.values())       # fp16 P.V
+    fp8 = [i for i in ks.values() if _has(i, "v_mfma_f32_32x32x64_f8f6f4")]   # FP8 P.V
+    assert fp8 and all(_has(i, "v_cvt_pk_fp8_f32") and _has(i, "v_permlane16_swap_b32") for i in fp8)
+
+
+def test_no_packed_fp32_arithmetic(kernels):
+    bad = {n: sorted(x for x in ins if x.startswith(("v_pk_fma_f32", "v_pk_add_f32", "v_pk_mul_f32")))
+           for n, ins in kernels.items()}
+    bad = {n: v for n, v in bad.items() if v}
+    assert not bad, bad
