@@ -685,3 +685,26 @@ def test_decode_workspace_reuse_across_calls(qa):
         out = qa.paged_attention_decode(q8, qs, kc, ks, vc, vs, tables, lens, num_splits=S, workspace=ws)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), want, f"reuse S={S}")
+
+
+@pytest.mark.parametrize("pv_fp8", [False, True])
+def test_dense_and_varlen_are_deterministic(qa, pv_fp8):
+    """Repeat calls give bit-identical outputs and LSE (no atomics in any
+    reduction): dense causal with smooth_v, and a varlen batch."""
+    say(f"dense determinism fp8={pv_fp8}")
+    spec = DenseSpec("dn_det", 711, 2, 4, 2, 300, 257, 128, k_bias_std=3.0, dtype="bf16", v_bias_std=1.0)
+    inp = dense_inputs(spec)
+    q, k, v = (dev_bits(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    runs = [qa.dense_sage_attention_ex(q, k, v, is_causal=True, smooth_v=True, return_lse=True, pv_fp8=pv_fp8)
+            for _ in range(5)]
+    vs = VarlenSpec("vl_det", 712, [130, 1, 260], [200, 9, 260], 4, 2, 128, dtype="bf16")
+    vin = varlen_inputs(vs)
+    cu_q, cu_k = torch.from_numpy(vin.cu_q).cuda(), torch.from_numpy(vin.cu_k).cuda()
+    vq, vk, vv = (dev_bits(x, "bf16") for x in (vin.q, vin.k, vin.v))
+    vruns = [qa.dense_sage_attention_varlen(vq, vk, vv, cu_q, cu_k, 260, 260, is_causal=True, return_lse=True,
+                                            pv_fp8=pv_fp8) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o, l in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(l, runs[0][1])
+    for o, l in vruns[1:]:
+        assert torch.equal(o, vruns[0][0]) and torch.equal(l, vruns[0][1])
