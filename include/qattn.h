@@ -487,7 +487,7 @@ typedef struct {
  *             softmax_scale * q . mu (unquantized q, fp32) is added back
  *             (the "LSE correction"), so lse is that of the unsmoothed
  *             scores. Rows that see no key get -inf.
- * options NULL means NHD without smooth_v. workspace >=
+ * options NULL means NHD without smooth_v or FP8 P.V. workspace >=
  * qa_dense_sage_ex_workspace_size bytes (a superset of the plain call's).
  * Errors as qa_dense_sage_attention; QA_ERR_INVALID_ARG for an unknown layout.
  */
