@@ -406,6 +406,9 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // global_load_lds_dwordx4: each wave moves 1 KB chunks (lane l's 16 bytes
   // land at chunk base + 16*l), with no staging registers and no LDS writes.
   // Blocks past the last one are clamped to it, as in fetch().
+  // first E4M3 V block of this sequence (read before the loop: a varlen
+  // offset loaded inside it would be waited for together with the tile copies)
+  const int64_t v8_base = PV8 ? a.k_rows.block0(z, 64) : 0;
   auto dma = [&](int buf, int tile) {
     constexpr int KC = D / 64;                     // 1 KB chunks per K block (per head)
     constexpr int VC = D / 32;                     // 1 KB chunks per V block (per head)
@@ -422,7 +425,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     if constexpr (PV8) {
       // one E4M3 block of 64 keys: D rows of 64 bytes, D/16 chunks of 1 KB
       constexpr int V8C = D / 16;
-      const int64_t vb8 = a.k_rows.block0(z, 64) + min(tile, (kv_len + KT - 1) / KT - 1);
+      const int64_t vb8 = v8_base + min(tile, (kv_len + KT - 1) / KT - 1);
       const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.v_blocks) + (vb8 * Hkv + kvh) * (int64_t)D * 64;
 #pragma unroll
       for (int i = 0; i < (V8C + NW - 1) / NW; ++i) {
