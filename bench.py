@@ -444,7 +444,8 @@ def run_practical_peaks(torch, step_bytes: int, pools: int) -> dict:
     """Practical ceilings measured on this GPU with the probes of qa_probe.h:
     a plain streaming read (1 GiB, and the decode step's byte count rotated
     over `pools` buffers as the decode bench does) and matrix-instruction
-    loops of the 32x32 and 16x16 INT8/fp16 forms (best grid, median of the
+    loops of the 32x32 and 16x16 INT8/fp16 forms, and the vector-ALU rates of
+    the exponential and of the fused multiply-add (best grid, median of the
     launches)."""
     from quantized_attention_quantize_amd import probes
     st = torch.cuda.current_stream()
@@ -461,7 +462,7 @@ def run_practical_peaks(torch, step_bytes: int, pools: int) -> dict:
         return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
     out = {}
-    sink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    sink = torch.empty(8192 * 256, dtype=torch.float32, device="cuda")
     big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")          # 1 GiB
     best = 0.0
     for wgs in (1024, 2048, 4096):
@@ -493,8 +494,18 @@ def run_practical_peaks(torch, step_bytes: int, pools: int) -> dict:
             ms = timed(one, 5)
             best = max(best, ops[0] / (ms * 1e-3) / 1e12)
         out[f"mfma_{name}_T"] = round(best, 1)
+    for kind, name in probes.VALU_KINDS.items():
+        best = 0.0
+        for wgs in (4096, 8192):
+            ops = [0.0]
+
+            def one():
+                ops[0] = probes.valu(kind, 2048, wgs, sink, raw)
+            ms = timed(one, 5)
+            best = max(best, ops[0] / (ms * 1e-3) / 1e12)
+        out[f"valu_{name}_T_lane_ops"] = round(best, 2)
     out["note"] = ("T = TOPS (int8) or TFLOP/s (fp16), include/qa_probe.h; the attention kernels issue the "
-                   "16x16 forms")
+                   "16x16 forms; valu_* in tera lane operations per second (one exponential per score)")
     return out
 
 

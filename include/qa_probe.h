@@ -1,5 +1,5 @@
-/* Measurement probes for MI355X (gfx950): a plain streaming read and
- * matrix-instruction throughput loops. They set the practical ceilings that
+/* Measurement probes for MI355X (gfx950): a plain streaming read,
+ * matrix-instruction throughput loops and vector-ALU throughput loops. They set the practical ceilings that
  * the attention kernels' throughputs are compared against (HBM bandwidth
  * for decode, matrix rates for prefill and dense attention); they are not
  * part of the attention computation.
@@ -33,6 +33,15 @@ int qa_probe_stream_read(const void* src, size_t bytes, int wgs, int* sink, hipS
  * Total work = per-round ops x iters x 4 x wgs. One float per thread goes to
  * `sink[wgs * 256]`. */
 int qa_probe_mfma(int kind, int iters, int wgs, float* sink, hipStream_t stream);
+
+/* Vector-ALU throughput: every lane of `wgs` workgroups of 256 threads
+ * (1 <= wgs <= 65535) runs `iters` (>= 1) rounds of 8 independent
+ * single-operation chains:
+ *   kind 0: v_exp_f32 (the base-2 exponential of the softmax)
+ *   kind 1: v_fma_f32
+ * Total lane operations = 8 x iters x 256 x wgs. One float per thread goes
+ * to `sink[wgs * 256]`. */
+int qa_probe_valu(int kind, int iters, int wgs, float* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

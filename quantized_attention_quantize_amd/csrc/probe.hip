@@ -1,5 +1,5 @@
-// Measurement probes: a grid-stride streaming read and matrix-instruction
-// throughput loops (declared in qa_probe.h). Separate from the attention
+// Measurement probes: a grid-stride streaming read, matrix-instruction
+// throughput loops and vector-ALU loops (declared in qa_probe.h). Separate from the attention
 // library; used to state the practical ceilings next to the kernels'
 // throughputs.
 #include <hip/hip_runtime.h>
@@ -72,6 +72,28 @@ __global__ __launch_bounds__(256) void k_mfma(int iters, float* sink) {
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
 }
 
+// 8 independent chains per lane of one vector operation: the base-2
+// exponential (v_exp_f32, x -> 2^-x with the negation as a source modifier,
+// so every value stays in (0.5, 1]) or the fused multiply-add (v_fma_f32,
+// x -> 0.999 x + 1e-7).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_valu(int iters, float* sink) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 1e-6f * (float)(threadIdx.x + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (KIND == 0) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+      else x[i] = __builtin_fmaf(x[i], 0.999f, 1e-7f);
+    }
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r += x[i];
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
+}
+
 }  // namespace
 
 extern "C" int qa_probe_stream_read(const void* src, size_t bytes, int wgs, int* sink, hipStream_t stream) {
@@ -89,5 +111,12 @@ extern "C" int qa_probe_mfma(int kind, int iters, int wgs, float* sink, hipStrea
     case 2: k_mfma<2><<<wgs, 256, 0, stream>>>(iters, sink); break;
     default: k_mfma<3><<<wgs, 256, 0, stream>>>(iters, sink); break;
   }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int qa_probe_valu(int kind, int iters, int wgs, float* sink, hipStream_t stream) {
+  if (sink == nullptr || kind < 0 || kind > 1 || iters < 1 || wgs < 1 || wgs > 65535) return 1;
+  if (kind == 0) k_valu<0><<<wgs, 256, 0, stream>>>(iters, sink);
+  else k_valu<1><<<wgs, 256, 0, stream>>>(iters, sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

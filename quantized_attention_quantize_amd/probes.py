@@ -13,7 +13,9 @@ lib.qa_probe_stream_read.restype = ctypes.c_int
 lib.qa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
 lib.qa_probe_mfma.restype = ctypes.c_int
 lib.qa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-EXPORTED = ("qa_probe_stream_read", "qa_probe_mfma")
+lib.qa_probe_valu.restype = ctypes.c_int
+lib.qa_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+EXPORTED = ("qa_probe_stream_read", "qa_probe_mfma", "qa_probe_valu")
 
 # ops per round of one wave, by kind (see qa_probe.h)
 MFMA_KINDS = {
@@ -22,6 +24,8 @@ MFMA_KINDS = {
     2: ("i8_16x16x64", 8 * 32768),
     3: ("f16_16x16x32", 8 * 16384),
 }
+
+VALU_KINDS = {0: "exp_f32", 1: "fma_f32"}
 
 
 def _check(rc: int, what: str) -> None:
@@ -41,3 +45,10 @@ def mfma(kind: int, iters: int, wgs: int, sink, stream) -> float:
     >= wgs * 256 float32."""
     _check(lib.qa_probe_mfma(kind, iters, wgs, sink.data_ptr(), stream), "qa_probe_mfma")
     return float(MFMA_KINDS[kind][1]) * iters * 4 * wgs
+
+
+def valu(kind: int, iters: int, wgs: int, sink, stream) -> float:
+    """Launch one vector-ALU throughput loop; returns its total lane
+    operations. `sink` holds >= wgs * 256 float32."""
+    _check(lib.qa_probe_valu(kind, iters, wgs, sink.data_ptr(), stream), "qa_probe_valu")
+    return 8.0 * iters * 256 * wgs

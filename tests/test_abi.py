@@ -283,6 +283,12 @@ def test_probe_library_exports_and_rejects():
     assert L.qa_probe_mfma(4, 10, 4, FAKE, None) == 1
     assert L.qa_probe_mfma(0, 0, 4, FAKE, None) == 1
     assert L.qa_probe_mfma(0, 10, 4, None, None) == 1
+    assert L.qa_probe_valu(2, 10, 4, FAKE, None) == 1
+    assert L.qa_probe_valu(-1, 10, 4, FAKE, None) == 1
+    assert L.qa_probe_valu(0, 0, 4, FAKE, None) == 1
+    assert L.qa_probe_valu(1, 10, 0, FAKE, None) == 1
+    assert L.qa_probe_valu(1, 10, 65536, FAKE, None) == 1
+    assert L.qa_probe_valu(0, 10, 4, None, None) == 1
 
 
 def test_decode_mt_validation(qa):

@@ -1,6 +1,6 @@
 """GPU checks of the measurement probes (qa_probe.h): the streaming read
 returns the exact XOR of what thread 0 of each workgroup visits, and every
-matrix-throughput kind runs and leaves finite values."""
+matrix- and vector-throughput kind runs and leaves finite values."""
 import numpy as np
 import pytest
 import torch
@@ -37,3 +37,17 @@ def test_mfma_probe_runs(kind):
     torch.cuda.synchronize()
     assert ops == probes.MFMA_KINDS[kind][1] * 10 * 4 * 4
     assert torch.isfinite(sink).all()
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_valu_probe_runs(kind):
+    from quantized_attention_quantize_amd import probes
+    sink = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    say("probe valu kind", kind)
+    ops = probes.valu(kind, 10, 4, sink, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert ops == 8 * 10 * 256 * 4
+    s = sink.cpu()
+    assert torch.isfinite(s).all()
+    if kind == 0:
+        assert ((s > 8 * 0.5) & (s <= 8.0)).all()     # eight values of 2^-x, each in (0.5, 1]
