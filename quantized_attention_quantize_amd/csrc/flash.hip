@@ -128,6 +128,14 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
 }
 
+// Wait until every vector memory operation of the wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima, gfx9
+// encoding). The builtin, unlike inline assembly, is seen by the compiler's
+// wait insertion, which then knows that the loads issued before it (query
+// fragments, scales) are complete and places no waits for them in the tile
+// loop, where any vmcnt wait would also wait for the copies in flight.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int D, int VK, int NT, bool KDMA>
 struct Staged {
   static constexpr int VB = VK == kVI8 ? 1 : 2;    // bytes per cached V element
@@ -405,10 +413,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // their tiles are copied straight from global memory into LDS by
   // global_load_lds_dwordx4: each wave moves 1 KB chunks (lane l's 16 bytes
   // land at chunk base + 16*l), with no staging registers and no LDS writes.
-  // Blocks past the last one are clamped to it, as in fetch().
-  // first E4M3 V block of this sequence (read before the loop: a varlen
-  // offset loaded inside it would be waited for together with the tile copies)
-  const int64_t v8_base = PV8 ? a.k_rows.block0(z, 64) : 0;
+  // Blocks past the last one are clamped to it, as in fetch(). The copies go
+  // through copy16_to_lds (inline assembly): issued with the builtin, the
+  // compiler cannot tell the two LDS buffers apart and waits for the next
+  // tile's copies before the first LDS read of the current one. The wait
+  // before the end-of-tile barrier covers them.
   auto dma = [&](int buf, int tile) {
     constexpr int KC = D / 64;                     // 1 KB chunks per K block (per head)
     constexpr int VC = D / 32;                     // 1 KB chunks per V block (per head)
@@ -417,36 +426,33 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
     for (int i = 0; i < (4 * KC + NW - 1) / NW; ++i) {
       const int c = wave_s + NW * i, b = c / KC, part = c % KC;
       if (4 * KC % NW != 0 && c >= 4 * KC) break;   // wave-uniform
-      const int8_t* src = a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)&s_k[buf][b * KBS + part * 1024],
-                                       16, 0, 0);
+      copy16_to_lds(a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16, &s_k[buf][b * KBS + part * 1024]);
     }
     if constexpr (PV8) {
       // one E4M3 block of 64 keys: D rows of 64 bytes, D/16 chunks of 1 KB
       constexpr int V8C = D / 16;
-      const int64_t vb8 = v8_base + min(tile, (kv_len + KT - 1) / KT - 1);
+      // The sequence's first block (Rows::block0 with 64-token blocks) is
+      // derived here, per tile: a value kept across the loop costs the causal
+      // d = 128 kernel spill reloads in it. The varlen offset is a scalar
+      // (constant-memory) load, so that waiting for it waits for no copy.
+      typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+      const int64_t seq0 = a.k_rows.packed ? (int64_t)(((const_i32_ptr)a.k_rows.cu)[z] / KT) + z
+                                           : (int64_t)z * ((a.k_rows.N + KT - 1) / KT);
+      const int64_t vb8 = seq0 + min(tile, (kv_len + KT - 1) / KT - 1);
       const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.v_blocks) + (vb8 * Hkv + kvh) * (int64_t)D * 64;
 #pragma unroll
       for (int i = 0; i < (V8C + NW - 1) / NW; ++i) {
         const int c = wave_s + NW * i;
         if (V8C % NW != 0 && c >= V8C) break;   // wave-uniform
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc + c * 1024 + lane * 16),
-                                         (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(s_v[buf]) +
-                                                                                    c * 1024),
-                                         16, 0, 0);
+        copy16_to_lds(vsrc + c * 1024 + lane * 16, reinterpret_cast<const char*>(s_v[buf]) + c * 1024);
       }
     }
 #pragma unroll
     for (int i = 0; i < (PV8 ? 0 : (4 * VC + NW - 1) / NW); ++i) {
       const int c = wave_s + NW * i, b = c / VC, part = c % VC;
       if (4 * VC % NW != 0 && c >= 4 * VC) break;   // wave-uniform
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * 2 +
-                           part * 1024 + lane * 16;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(s_v[buf]) +
-                                                                                  b * D * 32 + part * 1024),
-                                       16, 0, 0);
+      copy16_to_lds(reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * 2 + part * 1024 + lane * 16,
+                    reinterpret_cast<const char*>(s_v[buf]) + b * D * 32 + part * 1024);
     }
   };
   constexpr bool kDma = DENSE;
@@ -458,20 +464,25 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   if (ntiles > 0) {
     if constexpr (kDma) {
       dma(0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
       St st;
       fetch(st, 0, unpack(load_blocks(0)), 0);
       commit(st, 0, 0);
-      if constexpr (KDMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   }
+  // on every path (the tile loop is reached from both), so that no load
+  // issued so far is waited for inside the loop
+  if constexpr (kDma || KDMA) wait_vmem_all();
   __syncthreads();
 
   const int nkb = DENSE ? (kv_len + KT - 1) / KT : 1;
   // dense: key-block scales, read one tile ahead (a load issued and used in
-  // the same tile would expose its latency every tile)
-  const float* ksc = DENSE ? a.k_scale + a.k_rows.scale_at(z, kvh, Hkv, 0, KT) : nullptr;
+  // the same tile would expose its latency every tile). Read as constant
+  // memory (written before this kernel), so they come through scalar loads:
+  // the wait for a vector load would also wait for the tile copies issued
+  // after it.
+  typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+  const const_f32_ptr ksc = DENSE ? (const_f32_ptr)(a.k_scale + a.k_rows.scale_at(z, kvh, Hkv, 0, KT)) : nullptr;
   float tsc_next = 1.0f;
   if constexpr (DENSE) tsc_next = ntiles > 0 ? ksc[0] : 1.0f;
   int pb_next = load_blocks(1);
@@ -706,9 +717,9 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
       }
     }
     if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(0);
-    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next tile has landed
+    if constexpr (kDma) wait_vmem_all();   // the next tile has landed
     else commit(nxt, buf ^ 1, tile + 1);
-    if constexpr (KDMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // K of the next tile has landed
+    if constexpr (KDMA) wait_vmem_all();   // K of the next tile has landed
     __syncthreads();
   }
 
