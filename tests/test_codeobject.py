@@ -1,6 +1,7 @@
 """The device code this repository builds, read back from libqattn.so (CPU
 only): the hot kernels contain the matrix instructions the design relies on,
-the decode kernels use no scratch memory, and no packed fp32 arithmetic was
+the decode kernels use no scratch memory, the dense tile loops keep a single
+vector-memory wait and no scratch access, and no packed fp32 arithmetic was
 generated (the build disables it). Uses the ROCm LLVM tools on our own
 build's code objects; skipped where they are missing."""
 import os
@@ -18,13 +19,15 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 
 @pytest.fixture(scope="module")
-def kernels():
+def disassembly():
+    """(opcode set per kernel, instruction list per kernel); an instruction is
+    (address, opcode, operand text, branch target address or None)."""
     if not os.path.exists(LIB):
         pytest.skip("libqattn.so not built")
     for t in TOOLS.values():
         if not os.path.exists(t):
             pytest.skip(f"{t} missing")
-    out = {}
+    out, listing = {}, {}
     with tempfile.TemporaryDirectory() as d:
         fat = os.path.join(d, "fat.bin")
         subprocess.run([TOOLS["llvm-objcopy"], "--dump-section", f".hip_fatbin={fat}", LIB, os.path.join(d, "x")],
@@ -45,17 +48,27 @@ def kernels():
                                  capture_output=True, text=True).stdout
             name = None
             for line in dis.splitlines():
-                m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+                m = re.match(r"^([0-9a-f]+) <(\S+)>:", line)
                 if m:
-                    name = m.group(1)
-                    out[name] = set()
+                    name, base = m.group(2), int(m.group(1), 16)
+                    out[name], listing[name] = set(), []
                     continue
                 if name is not None:
                     t = line.strip().split()
                     if t and re.match(r"^[sv]_|^global_|^buffer_|^ds_|^scratch_|^flat_", t[0]):
                         out[name].add(t[0])
+                        a = re.search(r"// ([0-9A-Fa-f]+):", line)
+                        tg = re.search(r"<" + re.escape(name) + r"\+0x([0-9a-f]+)>", line)
+                        if a:
+                            listing[name].append((int(a.group(1), 16), t[0], line.split("//")[0],
+                                                  base + int(tg.group(1), 16) if tg else None))
     assert out, "no gfx950 code object found"
-    return out
+    return out, listing
+
+
+@pytest.fixture(scope="module")
+def kernels(disassembly):
+    return disassembly[0]
 
 
 def _has(ins, op):
@@ -88,3 +101,32 @@ def test_no_packed_fp32_arithmetic(kernels):
            for n, ins in kernels.items()}
     bad = {n: v for n, v in bad.items() if v}
     assert not bad, bad
+
+
+def _main_loop(ins):
+    """The instructions of the loop (a backward branch's range) that holds the
+    most matrix instructions."""
+    best, best_n = [], -1
+    for addr, op, _, tgt in ins:
+        if op.startswith(("s_cbranch", "s_branch")) and tgt is not None and tgt < addr:
+            body = [x for x in ins if tgt <= x[0] <= addr]
+            n = sum(1 for x in body if x[1].startswith("v_mfma"))
+            if n > best_n:
+                best, best_n = body, n
+    return best
+
+
+def test_dense_tile_loops_wait_once_for_memory(disassembly):
+    """The dense kernels copy the next tile global -> LDS while computing on
+    the current one; the end-of-tile wait before the barrier must be the
+    loop's only vector-memory wait (any other one also waits for the copies
+    in flight), and the loop must not reload spilled registers."""
+    dense = {n: ins for n, ins in disassembly[1].items()
+             if re.search(r"k_flashILi\d+ELi\d+ELi\d+ELi\d+ELb1E", n)}
+    assert len(dense) >= 10, sorted(dense)
+    for n, ins in dense.items():
+        body = _main_loop(ins)
+        assert body, f"{n}: no loop found"
+        waits = [x[2].strip() for x in body if x[1] == "s_waitcnt" and "vmcnt" in x[2]]
+        assert len(waits) == 1, (n, waits)
+        assert not [x for x in body if x[1].startswith("scratch_")], f"{n} touches scratch in its tile loop"
