@@ -558,7 +558,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 QK / fp16 PV",
+        "dtype": "int8 QK (int32 acc) / bf16 PV (fp32 acc)",   # decode: bf16 V, P as two bf16 terms
         "data": "synthetic",
         "config": {"workload": "qwen27b_decode", "num_seqs": 1, "q_heads": 24, "kv_heads": 4, "head_dim": 256,
                    "context": args.context, "block_size": 16, "k_cache": "int8 + fp32 per-token scale",
