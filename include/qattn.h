@@ -189,9 +189,13 @@ typedef struct {
 int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p);
 
 /* Workspace bytes a decode call needs (0 when it runs unsplit): the split
- * partials (max, sum and unnormalized output per split and query head). Its
+ * partials (max, sum and unnormalized output per split and query head),
+ * S*num_seqs*num_q_heads*(head_dim + 2)*4 bytes plus alignment ([QK-MMAC] §4:
+ * each segment keeps its running max, sum and output for the merge). Its
  * contents need no initialization. Calls that share a workspace must not
- * run concurrently. */
+ * run concurrently. 0 for parameters the decode call would reject. */
+size_t qa_paged_decode_workspace_bytes(const qa_decode_params_t* p);
+/* The same value under its earlier name. */
 size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
 
 /*
@@ -218,7 +222,7 @@ size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
  *                 (v_scale NULL unless v_cache_dtype == QA_DT_I8)
  *   block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids
  *   context_lens  [num_seqs] int32 visible keys per sequence (0 gives zeros)
- *   workspace     device scratch of >= qa_paged_decode_workspace_size bytes
+ *   workspace     device scratch of >= qa_paged_decode_workspace_bytes bytes
  *   out           [num_seqs, num_q_heads, head_dim] fp32 or bf16
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
@@ -446,8 +450,13 @@ qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, co
  *
  *   q, k, v   NHD bf16/f16 (dtype); v [batch, seq_k, num_kv_heads, head_dim]
  *   out       [batch, seq_q, num_q_heads, head_dim] in out_dtype
- *   workspace >= qa_dense_sage_workspace_size bytes
+ *   workspace >= qa_dense_sage_workspace_bytes bytes: the preprocessing's fp64
+ *             column sums, the Q and K' codes, the V blocks and the block scales
+ *             ([SAGE-MACA] quantization-kernel table); no initialization needed.
+ *             0 for parameters the call would reject.
  */
+size_t qa_dense_sage_workspace_bytes(const qa_dense_params_t* p);
+/* The same value under its earlier name. */
 size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p);
 qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, const void* k,
                                     const void* v, void* workspace, size_t workspace_bytes,
@@ -488,7 +497,7 @@ typedef struct {
  *             (the "LSE correction"), so lse is that of the unsmoothed
  *             scores. Rows that see no key get -inf.
  * options NULL means NHD without smooth_v or FP8 P.V. workspace >=
- * qa_dense_sage_ex_workspace_size bytes (a superset of the plain call's).
+ * qa_dense_sage_ex_workspace_size bytes (a superset of qa_dense_sage_workspace_bytes).
  * Errors as qa_dense_sage_attention; QA_ERR_INVALID_ARG for an unknown layout.
  */
 size_t qa_dense_sage_ex_workspace_size(const qa_dense_params_t* p, const qa_dense_options_t* options);

@@ -96,6 +96,7 @@ _SIGS = {
     "qa_paged_decode_step": (ctypes.c_int, _STEP_ARGS),
     "qa_paged_decode_step_rope": (ctypes.c_int, [_P(RopeParams)] + _STEP_ARGS),
     "qa_paged_decode_step_partials": (ctypes.c_int, _STEP_ARGS),
+    "qa_paged_decode_workspace_bytes": (_size, [_P(DecodeParams)]),
     "qa_paged_decode_workspace_size": (_size, [_P(DecodeParams)]),
     "qa_paged_attention_decode": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_size, _c_void_p,
                                                                                            _c_void_p]),
@@ -109,6 +110,7 @@ _SIGS = {
     "qa_chunked_prefill_attention": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 11),
     "qa_dense_sage_quantize_workspace_size": (_size, [_P(DenseParams)]),
     "qa_dense_sage_quantize": (ctypes.c_int, [_P(DenseParams)] + [_c_void_p] * 8 + [_size, _c_void_p]),
+    "qa_dense_sage_workspace_bytes": (_size, [_P(DenseParams)]),
     "qa_dense_sage_workspace_size": (_size, [_P(DenseParams)]),
     "qa_dense_sage_attention": (ctypes.c_int, [_P(DenseParams)] + [_c_void_p] * 4 + [_size, _c_void_p,
                                                                                         _c_void_p]),
@@ -236,7 +238,7 @@ def decode_num_splits(p: DecodeParams) -> int:
 
 def decode_workspace(p: DecodeParams, device="cuda") -> torch.Tensor:
     """Decode workspace (split-K partials; no initialization needed)."""
-    n = lib.qa_paged_decode_workspace_size(ctypes.byref(p))
+    n = lib.qa_paged_decode_workspace_bytes(ctypes.byref(p))
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -402,7 +404,7 @@ def dense_sage_quantize(q, k, smooth_k=True):
 
 
 def dense_sage_workspace(p: DenseParams, device="cuda") -> torch.Tensor:
-    return torch.empty(max(lib.qa_dense_sage_workspace_size(ctypes.byref(p)), 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(lib.qa_dense_sage_workspace_bytes(ctypes.byref(p)), 16), dtype=torch.uint8, device=device)
 
 
 def dense_sage_attention(q, k, v, is_causal=False, smooth_k=True, softmax_scale=0.0, out_dtype=torch.float32,

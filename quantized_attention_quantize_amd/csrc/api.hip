@@ -440,10 +440,12 @@ int32_t qa_paged_decode_num_splits(const qa_decode_params_t* p) {
   return splits_of(p);
 }
 
-size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p) {
+size_t qa_paged_decode_workspace_bytes(const qa_decode_params_t* p) {
   if (check_decode(p) != QA_OK) return 0;
   return decode_ws(p, splits_of(p));
 }
+
+size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p) { return qa_paged_decode_workspace_bytes(p); }
 
 namespace {
 
@@ -709,10 +711,12 @@ qa_status_t qa_dense_sage_quantize(const qa_dense_params_t* p, const void* q, co
   return hip_status(qa::launch_sage_prep(a, (hipStream_t)stream), "qa_dense_sage_quantize launch");
 }
 
-size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p) {
+size_t qa_dense_sage_workspace_bytes(const qa_dense_params_t* p) {
   if (check_dense(p) != QA_OK) return 0;
   return dense_layout(dense_call(p, QA_LAYOUT_NHD, false), true, false).total;
 }
+
+size_t qa_dense_sage_workspace_size(const qa_dense_params_t* p) { return qa_dense_sage_workspace_bytes(p); }
 
 qa_status_t qa_dense_sage_attention(const qa_dense_params_t* p, const void* q, const void* k, const void* v,
                                     void* workspace, size_t workspace_bytes, void* out, qa_stream_t stream) {

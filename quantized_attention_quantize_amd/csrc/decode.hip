@@ -24,10 +24,7 @@ namespace {
 
 // Workgroup shape: waves per workgroup, each with one 32-token tile in
 // flight (more waves, or two tiles per wave, measured slower on MI355X).
-#ifndef QA_DECODE_WAVES
-#define QA_DECODE_WAVES 8
-#endif
-constexpr int kWaves = QA_DECODE_WAVES;
+constexpr int kWaves = 8;
 
 // Mask words for 8 values held in 16-bit (bf16) or 8-bit (int8) lanes of
 // 32-bit words: keep the first `nvalid` values, zero the rest. Slots past

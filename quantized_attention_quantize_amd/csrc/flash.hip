@@ -53,33 +53,14 @@ constexpr float kFp8Log2Top = 5.807354922057604f;   // log2(448) - 3
 
 enum VKind { kVBf16 = 0, kVF16 = 1, kVI8 = 2 };
 
-#ifndef QA_FLASH_QG
-#define QA_FLASH_QG 2
-#endif
-#ifndef QA_FLASH_WPE
-#define QA_FLASH_WPE 2
-#endif
-#ifndef QA_FLASH_SETPRIO
-#define QA_FLASH_SETPRIO 3   // dense kernels: bit 0 raises wave priority over QK, bit 1 over PV
-#endif
-#ifndef QA_FLASH_WPE_DENSE
-#define QA_FLASH_WPE_DENSE 3
-#endif
-
-#ifndef QA_FLASH_Q_LDS
-#define QA_FLASH_Q_LDS 1
-#endif
-#ifndef QA_FLASH_PAGED_KDMA
-#define QA_FLASH_PAGED_KDMA 1
-#endif
-
-#ifndef QA_FLASH_MAGIC
-#define QA_FLASH_MAGIC 1
-#endif
-
-#ifndef QA_FLASH_ROWSUM_MFMA
-#define QA_FLASH_ROWSUM_MFMA 1
-#endif
+// Fixed tuning choices (each measured against its alternatives on MI355X):
+constexpr int kQG = 2;            // query groups of 16 rows per wave (d <= 128)
+constexpr int kWpe = 2;           // waves per SIMD, paged prefill d <= 128
+constexpr int kWpeDense = 3;      // waves per SIMD, dense d <= 128
+constexpr int kSetprio = 3;       // dense: bit 0 raises wave priority over QK, bit 1 over P.V
+constexpr int kNW = 4;            // waves per workgroup, d <= 128
+constexpr int kNWD256Dense = 8;   // waves per workgroup, dense d = 256
+constexpr int kNWD256Paged = 12;  // waves per workgroup, paged prefill d = 256 (192-row workgroups)
 
 // 8 fp32 -> 8 fp16 through four packed conversions
 __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
@@ -121,11 +102,12 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i_t a, v8i_t b, v16f c) {
 // 64 lanes fill the 1 KB at the wave-uniform LDS address `lds`. Issued as
 // inline assembly, so the compiler does not treat the LDS destination as
 // aliasing the reads of the other buffer; the caller waits (vmcnt) before
-// the barrier.
+// the barrier. GFX9 parts need one wait state between an SALU write of M0
+// and an LDS-DMA instruction that reads it: the s_nop provides it.
 __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
 }
 
 // Wait until every vector memory operation of the wave has completed
@@ -158,12 +140,12 @@ struct Staged {
 // second product, a 32x32x64 matrix instruction per 32 channels and tile.
 template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL, bool PV8 = false>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_FLASH_WPE) : NW / 4))) void k_flash(
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 4))) void k_flash(
     FlashArgs a) {
   constexpr int NT = NW * 64;
   // At 12 waves the register file has no room to stage K as well: paged K
   // tiles (INT8, already in the LDS layout) are copied straight into LDS.
-  constexpr bool KDMA = !DENSE && NW == 12 && QA_FLASH_PAGED_KDMA;
+  constexpr bool KDMA = !DENSE && NW == 12;
   using St = Staged<D, VK, NT, KDMA>;
   static_assert(!PV8 || (DENSE && QG == 2 && D <= 128), "FP8 P.V: dense, 32 queries per wave");
   constexpr int KS = D / 64;
@@ -176,8 +158,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // swapped when bit 3 of the channel is set, so 16 consecutive channels
   // cover all banks.
   constexpr int KBS = D * 16 + 64;
-  constexpr bool kRowSumMfma = QA_FLASH_ROWSUM_MFMA && VK != kVI8;         // INT8 V folds sV into P: sum P on the VALU
-  constexpr bool kMagic = DENSE && QA_FLASH_MAGIC;                          // dense scores read as floats, see QK
+  constexpr bool kRowSumMfma = VK != kVI8;         // INT8 V folds sV into P: sum P on the VALU
+  constexpr bool kMagic = DENSE;                          // dense scores read as floats, see QK
   constexpr int kAcc0 = kMagic ? 0x4B400000 : 0;                            // bit pattern of 1.5 * 2^23
   constexpr float kOffset = 12582912.0f;                                     // 1.5 * 2^23
   __shared__ __attribute__((aligned(16))) int8_t s_k[2][4 * KBS];
@@ -186,7 +168,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   __shared__ float s_vs[DENSE ? 1 : 2][KT];
   // With 12 waves the query fragments are parked in LDS (each lane re-reads
   // its 16 bytes per K step of every tile) to free registers.
-  constexpr bool QLDS = KDMA && QA_FLASH_Q_LDS;
+  constexpr bool QLDS = KDMA;
   __shared__ __attribute__((aligned(16))) v4i s_q[QLDS ? NW * QG * KS : 1][64];
 
   // ---- work item (XCD-aware order) ----------------------------------------
@@ -306,9 +288,14 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // entries with one vector load, issued one tile ahead of the fetch that
   // uses them (a vector load, so that waiting for LDS reads - lgkmcnt - never
   // waits for it), and the fetch reads them out with readlane.
+  // The logical block is clamped to the sequence's last block and to the
+  // table row, so no entry outside the row is read (context_lens beyond
+  // max_blocks_per_seq * 16 breaks a documented precondition, but still reads
+  // inside the row).
+  const int blk_hi = DENSE ? 0 : min(last_blk, a.max_blocks - 1);
   auto load_blocks = [&](int tile) -> int {
     if constexpr (DENSE) return 0;
-    else return trow[min(tile * 4 + (lane & 3), last_blk)];
+    else return trow[max(min(tile * 4 + (lane & 3), blk_hi), 0)];
   };
   using Blocks = v4i;
   auto unpack = [](int v) -> Blocks {
@@ -459,7 +446,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   // Raised wave priority (s_setprio) while a wave issues its matrix
   // products: measured faster for the dense kernels, slower for the paged
   // prefill, so dense only.
-  constexpr int kPrio = DENSE ? QA_FLASH_SETPRIO : 0;
+  constexpr int kPrio = DENSE ? kSetprio : 0;
 
   if (ntiles > 0) {
     if constexpr (kDma) {
@@ -485,7 +472,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   const const_f32_ptr ksc = DENSE ? (const_f32_ptr)(a.k_scale + a.k_rows.scale_at(z, kvh, Hkv, 0, KT)) : nullptr;
   float tsc_next = 1.0f;
   if constexpr (DENSE) tsc_next = ntiles > 0 ? ksc[0] : 1.0f;
-  int pb_next = load_blocks(1);
+  int pb_next = ntiles > 0 ? load_blocks(1) : 0;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     const int kbase = tile * KT;
@@ -827,19 +814,6 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? QA_FLASH_WPE_DENSE : QA_F
   }
 }
 
-#ifndef QA_FLASH_NW
-#define QA_FLASH_NW 4
-#endif
-#ifndef QA_FLASH_D256_QG
-#define QA_FLASH_D256_QG 1
-#endif
-#ifndef QA_FLASH_D256_NW
-#define QA_FLASH_D256_NW 8
-#endif
-#ifndef QA_FLASH_D256_NW_PAGED
-#define QA_FLASH_D256_NW_PAGED 12
-#endif
-
 template <int D, int VK, bool DENSE, bool CAUSAL, bool PV8 = false>
 hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
   // d = 256: waves of 16 rows (one workgroup per CU: its double-buffered
@@ -847,8 +821,8 @@ hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
   // whose 192-row workgroups (32 tokens x 6 heads for 6:1 GQA) cut 2048
   // tokens x 24 heads into exactly one round of 256 workgroups; smaller
   // heads: four waves of 32 rows
-  constexpr int QG = D == 256 ? QA_FLASH_D256_QG : QA_FLASH_QG;
-  constexpr int NW = D == 256 ? (DENSE ? QA_FLASH_D256_NW : QA_FLASH_D256_NW_PAGED) : QA_FLASH_NW;
+  constexpr int QG = D == 256 ? 1 : kQG;
+  constexpr int NW = D == 256 ? (DENSE ? kNWD256Dense : kNWD256Paged) : kNW;
   constexpr int QT = NW * 16 * QG;
   const int G = DENSE ? 1 : a.G;
   const int qtiles = (int)(((int64_t)(DENSE ? a.Nq : a.max_seqlen_q) * G + QT - 1) / QT);

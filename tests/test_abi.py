@@ -106,18 +106,18 @@ def test_decode_validation(qa):
     assert call(_dp(qa, v_cache_dtype=qa.QA_DT_I8)) == qa.QA_ERR_INVALID_ARG           # v_scale missing
     assert call(_dp(qa, out_dtype=qa.QA_DT_F16)) == qa.QA_ERR_UNSUPPORTED
     p = _dp(qa, num_splits=8)
-    need = L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    need = L.qa_paged_decode_workspace_bytes(ctypes.byref(p))
     al = lambda x: (x + 255) // 256 * 256
     assert need == al(2 * 24 * 8 * 256 * 4) + al(2 * 24 * 8 * 2 * 4)   # partial O + (max, sum)
     assert call(p, need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
     assert b"needed" in L.qa_last_error()
-    assert L.qa_paged_decode_workspace_size(ctypes.byref(_dp(qa, num_splits=1))) == 0
+    assert L.qa_paged_decode_workspace_bytes(ctypes.byref(_dp(qa, num_splits=1))) == 0
 
 
 def test_decode_step_validation(qa):
     L = qa.lib
     p = _dp(qa, num_splits=8)
-    need = L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    need = L.qa_paged_decode_workspace_bytes(ctypes.byref(p))
     for fn in (L.qa_paged_decode_step, L.qa_paged_decode_step_partials):
         call = lambda p, dt=qa.QA_DT_BF16, ws_bytes=need, q=FAKE, vs=None: fn(
             ctypes.byref(p), q, 6144, 256, FAKE, FAKE, 1024, 256, dt, FAKE, FAKE, FAKE, FAKE, vs, FAKE, FAKE,
@@ -133,7 +133,7 @@ def test_decode_step_validation(qa):
 def test_decode_phase_validation(qa):
     L = qa.lib
     p = _dp(qa, num_splits=8)
-    need = L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    need = L.qa_paged_decode_workspace_bytes(ctypes.byref(p))
     part = lambda p, ws_bytes, *ptrs: L.qa_paged_attention_decode_partials(
         ctypes.byref(p), *ptrs, FAKE, ws_bytes, FAKE, None)
     assert part(p, need - 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE) == qa.QA_ERR_WORKSPACE_TOO_SMALL
@@ -167,7 +167,7 @@ def test_prefill_and_dense_validation(qa):
     assert L.qa_dense_sage_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None) == \
         qa.QA_ERR_INVALID_ARG                                                   # 8 % 3 != 0
     d.num_kv_heads = 4
-    need = L.qa_dense_sage_workspace_size(ctypes.byref(d))
+    need = L.qa_dense_sage_workspace_bytes(ctypes.byref(d))
     assert need > 0
     assert L.qa_dense_sage_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need - 1, FAKE, None) == \
         qa.QA_ERR_WORKSPACE_TOO_SMALL
@@ -180,7 +180,7 @@ def test_dense_options_validation(qa):
     L = qa.lib
     d = qa.DenseParams(2, 100, 90, 8, 4, 128, qa.QA_DT_BF16, 1, 0, 0.0, qa.QA_DT_F32)
     o = qa.DenseOptions(qa.QA_LAYOUT_HND, 1, 0)
-    plain = L.qa_dense_sage_workspace_size(ctypes.byref(d))
+    plain = L.qa_dense_sage_workspace_bytes(ctypes.byref(d))
     need = L.qa_dense_sage_ex_workspace_size(ctypes.byref(d), ctypes.byref(o))
     # the options call adds the V mean (2 x 4 x 128 fp32) and the LSE correction (2 x 8 x 100 fp32)
     assert need == plain + 4096 + 6400
@@ -301,9 +301,26 @@ def test_decode_mt_validation(qa):
     need = L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 2)
     al = lambda x: (x + 255) // 256 * 256
     assert need == al(2 * 2 * 24 * 8 * 256 * 4) + al(2 * 2 * 24 * 8 * 2 * 4)
-    assert L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 1) == L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    assert L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 1) == L.qa_paged_decode_workspace_bytes(ctypes.byref(p))
     assert L.qa_paged_decode_mt_workspace_size(ctypes.byref(p), 3) == 0
     assert call(p, 2, need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
     assert call(_dp(qa, head_dim=96), 1) == qa.QA_ERR_UNSUPPORTED
     assert L.qa_paged_attention_decode_mt(ctypes.byref(p), 2, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                           FAKE, need, FAKE, None) == qa.QA_ERR_INVALID_ARG
+
+
+def test_workspace_bytes_names_and_their_aliases(qa):
+    """The workspace queries under their fixed names (..._bytes); the earlier
+    ..._size names return the same values, also 0 for rejected parameters."""
+    L = qa.lib
+    for S in (0, 1, 8, 64):
+        p = _dp(qa, num_splits=S)
+        assert L.qa_paged_decode_workspace_bytes(ctypes.byref(p)) == L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    p = _dp(qa, head_dim=96)
+    assert L.qa_paged_decode_workspace_bytes(ctypes.byref(p)) == 0 == L.qa_paged_decode_workspace_size(ctypes.byref(p))
+    for causal in (0, 1):
+        d = qa.DenseParams(2, 300, 200, 8, 4, 128, qa.QA_DT_F16, 1, causal, 0.0, qa.QA_DT_F32)
+        n = L.qa_dense_sage_workspace_bytes(ctypes.byref(d))
+        assert n > 0 and n == L.qa_dense_sage_workspace_size(ctypes.byref(d))
+    d.head_dim = 80
+    assert L.qa_dense_sage_workspace_bytes(ctypes.byref(d)) == 0

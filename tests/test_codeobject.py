@@ -130,3 +130,21 @@ def test_dense_tile_loops_wait_once_for_memory(disassembly):
         waits = [x[2].strip() for x in body if x[1] == "s_waitcnt" and "vmcnt" in x[2]]
         assert len(waits) == 1, (n, waits)
         assert not [x for x in body if x[1].startswith("scratch_")], f"{n} touches scratch in its tile loop"
+
+
+def test_lds_dma_never_directly_follows_an_m0_write(disassembly):
+    """GFX9 parts, gfx950 included, need one wait state between an SALU write
+    of M0 and an LDS-DMA load (global_load_lds_*, buffer_load_* ... lds) that
+    takes its LDS address from M0. Every such load in the library must be
+    separated from the instruction that writes M0 by at least one other
+    instruction (the copies issue an s_nop)."""
+    n_dma = 0
+    for name, ins in disassembly[1].items():
+        for prev, cur in zip(ins, ins[1:]):
+            is_dma = cur[1].startswith("global_load_lds") or (cur[1].startswith("buffer_load") and " lds" in cur[2])
+            if not is_dma:
+                continue
+            n_dma += 1
+            writes_m0 = re.match(r"\s*s_\w+\s+m0\b", prev[2]) is not None
+            assert not writes_m0, f"{name} @{cur[0]:#x}: {cur[1]} right after '{prev[2].strip()}'"
+    assert n_dma > 0, "no LDS-DMA loads found: the dense and 12-wave prefill kernels use them"
