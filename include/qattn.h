@@ -312,6 +312,35 @@ qa_status_t qa_paged_attention_decode_partials(const qa_decode_params_t* p, cons
 qa_status_t qa_paged_attention_decode_combine(const qa_decode_params_t* p, void* workspace,
                                               size_t workspace_bytes, void* out, qa_stream_t stream);
 
+/* Size of the library's static device scratch used by
+ * qa_paged_attention_decode_noalloc (one copy per GPU, held until the process
+ * ends). */
+#define QA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * qa_paged_attention_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and the same result bit for bit, but the
+ * split partials live in a static device array of QA_DECODE_SCRATCH_BYTES
+ * owned by the library instead of a caller workspace. Nothing is allocated:
+ * the first call on a device looks up that device's copy of the array once
+ * (hipGetSymbolAddress; the calling thread's current device must be the
+ * stream's device). Its contents need no initialization.
+ *   Limit: qa_paged_decode_workspace_bytes(p) <= QA_DECODE_SCRATCH_BYTES, else
+ *   QA_ERR_WORKSPACE_TOO_SMALL (checked on the host before any HIP call;
+ *   lower num_splits or num_seqs).
+ *   Every call on one GPU shares that GPU's array: calls that can overlap on
+ *   one device (other streams, other threads) race and give undefined
+ *   results; calls queued in order on one stream are safe.
+ * Other arguments, layouts and errors as qa_paged_attention_decode.
+ */
+qa_status_t qa_paged_attention_decode_noalloc(const qa_decode_params_t* p, const int8_t* q_i8,
+                                              const float* q_scale, const int8_t* k_cache,
+                                              const float* k_scale, const void* v_cache,
+                                              const float* v_scale, const int32_t* block_tables,
+                                              const int32_t* context_lens, void* out,
+                                              qa_stream_t stream);
+
 /*
  * Multi-token decode (speculative or multi-token prediction steps): T new
  * query tokens per sequence attend to the paged cache, which already holds

@@ -103,6 +103,7 @@ _SIGS = {
     "qa_paged_attention_decode_partials": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 +
                                            [_size, _c_void_p, _c_void_p]),
     "qa_paged_attention_decode_combine": (ctypes.c_int, [_P(DecodeParams), _c_void_p, _size, _c_void_p, _c_void_p]),
+    "qa_paged_attention_decode_noalloc": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 9 + [_c_void_p]),
     "qa_paged_decode_mt_workspace_size": (_size, [_P(DecodeParams), _i32]),
     "qa_paged_attention_decode_mt": (ctypes.c_int, [_P(DecodeParams), _i32] + [_c_void_p] * 9 +
                                      [_size, _c_void_p, _c_void_p]),
@@ -265,6 +266,25 @@ def paged_attention_decode(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, bl
     """Decode attention; returns out [num_seqs, Hq, d]."""
     return _decode(lib.qa_paged_attention_decode, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables,
                    context_lens, num_kv_heads, softmax_scale, num_splits, out_dtype, workspace, out)[0]
+
+
+def paged_attention_decode_noalloc(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,
+                                   num_kv_heads=None, softmax_scale=0.0, num_splits=0, out_dtype=torch.float32,
+                                   out=None):
+    """Decode attention through the allocation-free entry point (split
+    partials in the library's static device scratch); same result as
+    paged_attention_decode. Returns out [num_seqs, Hq, d]."""
+    _require_cuda(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, out)
+    S, Hq, d = q_i8.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    p = decode_params(S, Hq, Hkv, d, block_tables.shape[1], k_cache.shape[0], v_cache.dtype == torch.int8,
+                      out_dtype, softmax_scale, num_splits)
+    if out is None:
+        out = torch.empty((S, Hq, d), dtype=out_dtype, device=q_i8.device)
+    _check(lib.qa_paged_attention_decode_noalloc(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_cache),
+                                                 _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(block_tables),
+                                                 _ptr(context_lens), _ptr(out), _stream()))
+    return out
 
 
 def paged_attention_decode_partials(q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens,

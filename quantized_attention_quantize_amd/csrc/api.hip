@@ -604,6 +604,35 @@ qa_status_t qa_paged_attention_decode_partials(const qa_decode_params_t* p, cons
                      "qa_paged_attention_decode_partials launch");
 }
 
+qa_status_t qa_paged_attention_decode_noalloc(const qa_decode_params_t* p, const int8_t* q_i8, const float* q_scale,
+                                              const int8_t* k_cache, const float* k_scale, const void* v_cache,
+                                              const float* v_scale, const int32_t* block_tables,
+                                              const int32_t* context_lens, void* out, qa_stream_t stream) {
+  static_assert(QA_DECODE_SCRATCH_BYTES == qa::kDecodeScratchBytes, "scratch size in the header");
+  qa_status_t st = check_decode(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0) return QA_OK;
+  const size_t need = decode_ws(p, splits_of(p));
+  QA_REQUIRE(need <= qa::kDecodeScratchBytes, QA_ERR_WORKSPACE_TOO_SMALL,
+             "split partials need %zu bytes; the static decode scratch holds %zu (lower num_splits or num_seqs)",
+             need, (size_t)qa::kDecodeScratchBytes);
+  // the checks of the workspace call, before the scratch lookup (the first HIP call)
+  QA_REQUIRE(q_i8 && q_scale && k_cache && k_scale && v_cache && block_tables && context_lens && out,
+             QA_ERR_INVALID_ARG, "null pointer");
+  QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
+  QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache) && aligned16(k_scale) && aligned16(v_cache) &&
+                 (v_scale == nullptr || aligned16(v_scale)),
+             QA_ERR_INVALID_ARG, "q_i8, caches and scales must be 16-byte aligned");
+  void* ws = nullptr;
+  if (need > 0) {
+    st = hip_status(qa::decode_scratch(&ws), "decode scratch lookup");
+    if (st != QA_OK) return st;
+  }
+  return decode_call(p, q_i8, q_scale, k_cache, k_scale, v_cache, v_scale, block_tables, context_lens, ws,
+                     qa::kDecodeScratchBytes, out, stream, qa::DecodePhase::kBoth,
+                     "qa_paged_attention_decode_noalloc launch");
+}
+
 size_t qa_paged_decode_mt_workspace_size(const qa_decode_params_t* p, int32_t tokens_per_seq) {
   if (check_decode(p) != QA_OK || check_tokens(p, tokens_per_seq) != QA_OK) return 0;
   return decode_ws(p, splits_of(p), tokens_per_seq);

@@ -16,8 +16,17 @@
 // the B operand of the fp16 product O^T = V^T P^T. So P never leaves the
 // registers, and the per-token key scale ([QK-MMAC] §1, "per column" of S)
 // is read as 8 consecutive floats that follow the result layout.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
+
+// Scratch for the allocation-free decode entry point: the split partials
+// live here instead of in a caller workspace. Each GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` names a
+// host-side stand-in, not a device address: host code only ever uses the
+// address decode_scratch() obtains for the current device.
+static __device__ __attribute__((aligned(256))) char scratch[qa::kDecodeScratchBytes];
 
 namespace qa {
 namespace {
@@ -644,6 +653,28 @@ int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks) 
   if (s > cap) s = cap;
   if (s > 256) s = 256;
   return (int32_t)(s < 1 ? 1 : s);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  // Device addresses of `scratch`, one per device, looked up on the first
+  // call made with that device current.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {

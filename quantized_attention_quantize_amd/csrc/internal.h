@@ -156,6 +156,11 @@ enum class DecodePhase { kBoth, kPartials, kCombine };
 hipError_t launch_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st);
 hipError_t launch_debug_qk(const DecodeArgs& a, hipStream_t st);
 int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks);
+// The decode kernels' static scratch for callers that cannot allocate (the
+// split partials): kDecodeScratchBytes per GPU. decode_scratch returns the
+// current device's copy of it (looked up once per device; no allocation).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
 
 // flash.hip (chunked prefill and dense) --------------------------------------
 struct FlashArgs {

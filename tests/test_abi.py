@@ -324,3 +324,24 @@ def test_workspace_bytes_names_and_their_aliases(qa):
         assert n > 0 and n == L.qa_dense_sage_workspace_size(ctypes.byref(d))
     d.head_dim = 80
     assert L.qa_dense_sage_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_decode_noalloc_validation(qa):
+    """The allocation-free decode rejects, on the host and before any HIP call,
+    parameters whose split partials do not fit the static scratch, and the
+    same bad arguments as the workspace call."""
+    L = qa.lib
+    assert qa.lib is not None
+    call = lambda p, q=FAKE, vs=None: L.qa_paged_attention_decode_noalloc(
+        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, vs, FAKE, FAKE, FAKE, None)
+    big = _dp(qa, num_seqs=64, num_splits=64)
+    need = L.qa_paged_decode_workspace_bytes(ctypes.byref(big))
+    assert need > (16 << 20)
+    assert call(big) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert b"static decode scratch" in L.qa_last_error()
+    ok = _dp(qa, num_seqs=32, num_splits=8)
+    assert L.qa_paged_decode_workspace_bytes(ctypes.byref(ok)) <= (16 << 20)
+    assert call(ok, q=None) == qa.QA_ERR_INVALID_ARG
+    assert call(_dp(qa, v_cache_dtype=qa.QA_DT_I8)) == qa.QA_ERR_INVALID_ARG      # v_scale missing
+    assert call(_dp(qa, head_dim=96)) == qa.QA_ERR_UNSUPPORTED
+    assert L.qa_paged_attention_decode_noalloc(ctypes.byref(_dp(qa, num_seqs=0)), *([None] * 10)) == qa.QA_OK
