@@ -246,29 +246,53 @@ def run_decode(args, torch, qa, W):
     }
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, inp, budget_s, gpu_out=None):
-    """The oracle, untuned, on the decode workload: quantize the query and
-    run unsplit paged decode over the cache the oracle writes itself. Also
-    reports the GPU step's output against the oracle's (same inputs)."""
+    """The oracle (C++17, oracle/), untuned, on the decode workload: quantize
+    the query and run unsplit paged decode over the cache the oracle writes
+    itself, once with one OpenMP thread per host cpu (its parallel units are
+    the (sequence, query head) pairs) and once on one thread. Also reports
+    the GPU step's output against the oracle's (same inputs)."""
     import oracle
-    from threadpoolctl import threadpool_info
     caches = oracle.write_kv_cache(inp.k, inp.v, "bf16", inp.slot_mapping, spec.num_blocks)
-    n, t_total = 0, 0.0
-    ref = None
-    while t_total < budget_s or n == 0:
-        t = time.perf_counter()
-        q8, qs = oracle.quantize_q(inp.q)
-        ref = oracle.paged_decode(q8, qs, caches, inp.block_tables, inp.context_lens, spec.num_kv_heads)
-        t_total += time.perf_counter() - t
-        n += 1
-        if n >= 1000:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    nproc = len(os.sched_getaffinity(0))
+    units = spec.num_seqs * spec.num_q_heads
+
+    def run(threads, budget):
+        oracle.set_num_threads(threads)
+        n, t_total, out = 0, 0.0, None
+        while t_total < budget or n == 0:
+            t = time.perf_counter()
+            q8, qs = oracle.quantize_q(inp.q)
+            out = oracle.paged_decode(q8, qs, caches, inp.block_tables, inp.context_lens, spec.num_kv_heads)
+            t_total += time.perf_counter() - t
+            n += 1
+            if n >= 1000:
+                break
+        return n, t_total, out
+
+    n, t_total, ref = run(nproc, 0.6 * budget_s)
+    n1, t1, _ = run(1, 0.4 * budget_s)
+    oracle.set_num_threads(nproc)
     by = decode_bytes(spec)["step"]
-    res = {"value": by * n / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-           "sample": f"{n} full decode steps (quantize_q + unsplit paged decode, fp64) of the "
-                     f"{spec.context_lens[0]}-token workload; {t_total:.1f} s on {os.cpu_count()} host cpus, "
-                     f"BLAS threads {threads}"}
+    used = min(nproc, units)
+    model = _cpu_model()
+    res = {"value": by * n / t_total / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle",
+           "sample": f"{n} full decode steps (C++ oracle: quantize_q + unsplit paged decode in fp64) of the "
+                     f"{spec.context_lens[0]}-token workload in {t_total:.1f} s with {used} OpenMP threads "
+                     f"(one per (sequence, query head) unit, {nproc} host cpus: {model})",
+           "one_thread": {"value": by * n1 / t1 / 1e9, "unit": "GB/s", "steps": n1, "seconds": round(t1, 2)},
+           "host": {"nproc": nproc, "cpu_model": model}}
     if gpu_out is not None:
         want = np.asarray(ref, np.float64).reshape(gpu_out.shape)
         got = gpu_out.astype(np.float64)

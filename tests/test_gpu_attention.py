@@ -88,7 +88,7 @@ def test_decode_qwen27b_full(qa):
         got = _decode_run(qa, inp, splits).cpu().numpy()
         assert_close(got, want, f"{spec.name} splits={splits}")
     # reported: error of the quantized method against unquantized fp64 attention
-    from oracle.quant import widen
+    widen = oracle.widen
     q = widen(inp.q, "bf16").astype(np.float64)[0]
     k = widen(inp.k, "bf16").astype(np.float64)
     v = widen(inp.v, "bf16").astype(np.float64)
@@ -520,11 +520,16 @@ def test_dense_options_full_size_sampled(qa):
             _lse_close(l[b, h, rows], want_lse[b, h, rows] + corr[b, h, rows], f"dense options LSE b={b} h={h}")
 
 
-# FP8 (E4M3) P.V: parity with the oracle's FP8 forward (same roundings; the
-# GPU's P differs from the oracle's in the last fp32 bits, which moves an
-# E4M3 rounding now and then), and distance to the 16-bit path of the order
-# of the E4M3 step
-FP8_REL_L2, FP8_MAX_ABS = 2e-3, 2e-2
+# FP8 (E4M3) P.V against the oracle's plain definition (P8 = E4M3(448
+# exp(s - m)) at the exact row maximum m). The kernel rounds P from a lazily
+# moved reference instead (56 exp(s - m'), m' <= m), so the two results
+# differ by independent E4M3 roundings; the oracle returns the standard
+# deviation sigma of that difference per element and per LSE (2^-4 relative
+# per normal E4M3 value, 2^-10 absolute per subnormal one, propagated through
+# the normalized sum). The bar: no element beyond 6 sigma and an RMS of
+# |difference| / sigma of at most 1, with a floor for the fp32 arithmetic
+# (rows that see one key have sigma 0).
+FP8_MAX_Z, FP8_RMS_Z = 6.0, 1.0
 
 FP8_CASES = [
     # (B, Nq, Nk, Hq, Hkv, d, dtype, causal, smooth_v)
@@ -535,11 +540,20 @@ FP8_CASES = [
 ]
 
 
-def _fp8_close(got, want, what):
-    r = rel_l2(got, want)
-    m = float(np.max(np.abs(got - want)))
-    say(f"  {what}: rel_l2={r:.3e} max_abs={m:.3e}")
-    assert np.all(np.isfinite(got)) and r <= FP8_REL_L2 and m <= FP8_MAX_ABS, f"{what}: rel L2 {r:.3e}, max abs {m:.3e}"
+def _fp8_close(got, want, sig, what):
+    got, want, sig = (np.asarray(x, np.float64) for x in (got, want, sig))
+    floor = 2e-6 * float(np.max(np.abs(want))) + 1e-7
+    z = np.abs(got - want) / np.maximum(sig, floor)
+    zmax, zrms = float(np.max(z)), float(np.sqrt(np.mean(z ** 2)))
+    say(f"  {what}: rel_l2={rel_l2(got, want):.3e} max|d|/sigma={zmax:.2f} rms|d|/sigma={zrms:.3f}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert zmax <= FP8_MAX_Z and zrms <= FP8_RMS_Z, f"{what}: max z {zmax:.2f}, rms z {zrms:.3f}"
+
+
+def _fp8_lse_close(got, want, sig, what):
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: -inf pattern differs"
+    _fp8_close(got[fin], want[fin], sig[fin] + 1e-6 * np.abs(want[fin]), what)
 
 
 @pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{c[6]}_{'causal' if c[7] else 'full'}{'_sv' if c[8] else ''}")
@@ -552,16 +566,24 @@ def test_dense_fp8pv_parity(qa, case):
                                           is_causal=causal, smooth_v=smooth_v, return_lse=True, pv_fp8=True)
     torch.cuda.synchronize()
     quant = oracle.sage_quantize(inp.q, inp.k, dt)
-    want, want_lse = oracle.dense_sage_attention_fp8pv(quant, inp.v, dt, causal=causal, smooth_v=smooth_v,
-                                                       return_lse=True)
+    want, want_lse, sig, sig_lse = oracle.dense_sage_attention_fp8pv(quant, inp.v, dt, causal=causal,
+                                                                     smooth_v=smooth_v, return_sigma=True)
     got = out.cpu().numpy()
-    _fp8_close(got, want, "fp8 P.V vs oracle")
+    _fp8_close(got, want, sig, "fp8 P.V vs oracle")
     corr = oracle.sage_lse_correction(inp.q, quant["k_mean"], dt)
-    _lse_close(lse.cpu().numpy(), want_lse + corr, "fp8 P.V LSE")
+    _fp8_lse_close(lse.cpu().numpy().astype(np.float64), want_lse + corr, sig_lse, "fp8 P.V LSE")
     exact = oracle.sage_forward(inp.q, inp.k, inp.v, dt, causal=causal, smooth_v=smooth_v)
     r = rel_l2(got, exact)
     say(f"  fp8 P.V vs 16-bit P path: rel_l2={r:.3e}")
     assert r < 3e-2
+    # reported: error against fp64 attention of the unquantized inputs
+    qv, kv, vv = (oracle.widen(x, dt).astype(np.float64) for x in (inp.q, inp.k, inp.v))
+    G = Hq // Hkv
+    vis = (np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)) if causal else None
+    ref = np.stack([np.stack([oracle.attention_fp64(qv[b, :, h], kv[b, :, h // G], vv[b, :, h // G], d ** -0.5, vis)
+                              for h in range(Hq)], axis=1) for b in range(B)])
+    live = np.isfinite(want_lse).transpose(0, 2, 1)[..., None]
+    say(f"  fp8 P.V vs unquantized fp64 attention: rel_l2={rel_l2(np.where(live, got, 0), np.where(live, ref, 0)):.3e}")
 
 
 def test_dense_fp8pv_full_size_sampled(qa):
@@ -573,11 +595,12 @@ def test_dense_fp8pv_full_size_sampled(qa):
     torch.cuda.synchronize()
     quant = oracle.sage_quantize(inp.q, inp.k, "f16")
     rows = np.array([0, 1, 127, 128, 4095, 8191])
-    want = oracle.dense_sage_attention_fp8pv(quant, inp.v, "f16", causal=True, rows=rows, heads=[0, 17, 31])
+    want, _, sig, _ = oracle.dense_sage_attention_fp8pv(quant, inp.v, "f16", causal=True, rows=rows,
+                                                        heads=[0, 17, 31], return_sigma=True)
     g = out.cpu().numpy()
     for b in range(2):
         for h in (0, 17, 31):
-            _fp8_close(g[b, rows, h], want[b, rows, h], f"fp8 P.V b={b} h={h}")
+            _fp8_close(g[b, rows, h], want[b, rows, h], sig[b, rows, h], f"fp8 P.V b={b} h={h}")
 
 
 def test_dense_fp8pv_varlen_matches_one_sequence_calls(qa):
