@@ -48,7 +48,7 @@ def decode_bytes(spec) -> dict:
     v_elem = 1 if spec.v_int8 else 2
     row = d + 4 + d * v_elem + (4 if spec.v_int8 else 0)      # one (token, KV head) in the cache
     hist = (tok * Hkv * row                                     # K, sK, V (, sV)
-            + spec.num_seqs * spec.max_blocks_per_seq * 4       # block table
+            + sum(spec.blocks_per_seq) * 4                       # the block-table entries in use
             + spec.num_seqs * Hq * d * 4)                       # fp32 output
     step = (hist + spec.num_seqs * Hq * 2 * d                   # bf16 query
             + spec.num_seqs * (Hkv * (4 * d + row) + 8))        # new K/V in, its cache row out, slot
@@ -423,6 +423,156 @@ def run_dense(torch, qa, reps, causal, options=False, pv_fp8=False):
             "_ops": (qk, pv)}
 
 
+def _timed_ms(torch, fn, reps, warm=3):
+    """Median of `reps` launches of fn between HIP events on torch's current
+    stream (the stream the library launches on)."""
+    for _ in range(warm):
+        fn(0)
+    evs = _mk_stream_events(torch, reps)
+    for i, (a, b) in enumerate(evs):
+        a.record(); fn(i); b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def _step_call(torch, qa, spec, inp, pools_n, splits):
+    """A decode-step closure over `pools_n` separately allocated copies of the
+    cache (the new token of every sequence is its last one)."""
+    dev = torch.device("cuda:0")
+    d, Hq, Hkv = spec.head_dim, spec.num_q_heads, spec.num_kv_heads
+    v_dt = torch.int8 if spec.v_int8 else torch.bfloat16
+    slots = torch.from_numpy(inp.slot_mapping).to(dev)
+    kb, vb = dev_bits(torch, inp.k), dev_bits(torch, inp.v)
+    pools = []
+    for r in range(pools_n):
+        kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, Hkv, d, v_dt, zero=False)
+        if r == 0:
+            qa.write_kv_cache(kb, vb, slots, kc, ks, vc, vs)
+        else:
+            kc.copy_(pools[0][0]); ks.copy_(pools[0][1]); vc.copy_(pools[0][2])
+            if vs is not None:
+                vs.copy_(pools[0][3])
+        pools.append((kc, ks, vc, vs))
+    last = torch.from_numpy(inp.cu_seqlens_kv[1:] - 1).to(dev)          # each sequence's last token
+    k_new, v_new, slot_new = kb[last].contiguous(), vb[last].contiguous(), slots[last].contiguous()
+    del kb, vb
+    q = dev_bits(torch, inp.q)
+    tables = torch.from_numpy(inp.block_tables).to(dev)
+    lens = torch.from_numpy(inp.context_lens).to(dev)
+    p = qa.decode_params(spec.num_seqs, Hq, Hkv, d, spec.max_blocks_per_seq, spec.num_blocks,
+                         v_int8=spec.v_int8, num_splits=splits)
+    ws = qa.decode_workspace(p, dev)
+    out = torch.empty((spec.num_seqs, Hq, d), dtype=torch.float32, device=dev)
+    L = qa.lib
+
+    def step(i, fn=None):
+        kc, ks, vc, vs = pools[i % len(pools)]
+        qa._check((fn or L.qa_paged_decode_step)(
+            ctypes.byref(p), qa._ptr(q), Hq * d, d, qa._ptr(k_new), qa._ptr(v_new), Hkv * d, d, qa.QA_DT_BF16,
+            qa._ptr(slot_new), qa._ptr(kc), qa._ptr(ks), qa._ptr(vc), qa._ptr(vs), qa._ptr(tables), qa._ptr(lens),
+            qa._ptr(ws), ws.numel(), qa._ptr(out), qa._stream()))
+    return step, p, out
+
+
+def run_decode_batched(torch, qa, reps=30, pools=2):
+    """Batched split-K decode: 32 sequences with contexts uniform on [1024,
+    32768] (seeded), 24/4 heads, d 256, INT8 K and INT8 V with per-token
+    scales, 8 splits per sequence. One step = qa_paged_decode_step (query
+    quantized inside the split kernel, new token written) + the combine.
+    Two cache copies (1.1 GB each) alternate, more than the 256 MB
+    Infinity Cache holds. Bytes as decode_bytes: the exact sum over the
+    seeded contexts."""
+    from workloads import batched_splitk_decode, paged_inputs
+    spec = batched_splitk_decode()
+    inp = paged_inputs(spec)
+    step, p, _ = _step_call(torch, qa, spec, inp, pools, spec.num_splits)
+    ms = _timed_ms(torch, step, reps)
+    part = _timed_ms(torch, lambda i: step(i, qa.lib.qa_paged_decode_step_partials), reps)
+    by = decode_bytes(spec)["step"]
+    return {"workload": f"batched split-K decode: 32 sequences, contexts U[1024, 32768] (sum {sum(spec.context_lens)}), "
+                        "24/4 heads, d256, INT8 K + INT8 V, 8 splits; step = fused quantize/write/split kernel + combine",
+            "ms": ms, "GBps": by / (ms * 1e-3) / 1e9, "frac_hbm_peak": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes": by, "split_kernel_ms": part, "split_kernel_frac_hbm_peak": by / (part * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kv_pools": pools}
+
+
+def run_decode_tiny(torch, qa, reps=200):
+    """The tiny decode (6/1 heads, d 64, context 256): latency of one step."""
+    from workloads import tiny_decode, paged_inputs
+    spec = tiny_decode()
+    inp = paged_inputs(spec)
+    step, p, _ = _step_call(torch, qa, spec, inp, 1, 0)
+    # back-to-back steps between two events (one step alone would time the
+    # host's launch latency, not the GPU)
+    for i in range(10):
+        step(i)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(reps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    by = decode_bytes(spec)["step"]
+    return {"workload": "tiny decode: 1 sequence, 6/1 heads, d64, context 256, bf16 V; one step "
+                        f"({qa.decode_num_splits(p)} splits)", "us": ms * 1e3, "bytes": by}
+
+
+def run_producers(torch, qa, reps=50):
+    """quantize_q and write_kv_cache on their own, on the chunked-prefill
+    shapes: 2048 query tokens x 24 heads x 256 (bf16 in, INT8 codes + fp32
+    scales out) and 2048 new tokens x 4 KV heads written into the paged cache
+    (K quantized, bf16 V copied). Bytes read + written."""
+    from workloads import chunked_prefill, paged_inputs
+    spec = chunked_prefill()
+    inp = paged_inputs(spec)
+    T, Hq, Hkv, d = spec.total_q, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    q = dev_bits(torch, inp.q)
+    q8 = torch.empty((T, Hq, d), dtype=torch.int8, device="cuda")
+    qs = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    L = qa.lib
+    fq = lambda i: qa._check(L.qa_quantize_q(qa._ptr(q), qa.QA_DT_BF16, T, Hq, d, Hq * d, d, qa._ptr(q8),
+                                             qa._ptr(qs), qa._stream()))
+    ms_q = _timed_ms(torch, fq, reps)
+    bq = T * Hq * (2 * d + d + 4)
+    kc, ks, vc, vs = qa.alloc_kv_cache(spec.num_blocks, Hkv, d, torch.bfloat16)
+    kb = dev_bits(torch, inp.k[-T:])
+    vb = dev_bits(torch, inp.v[-T:])
+    slots = torch.from_numpy(inp.slot_mapping[-T:].copy()).cuda()
+    fw = lambda i: qa.write_kv_cache(kb, vb, slots, kc, ks, vc, vs)
+    ms_w = _timed_ms(torch, fw, reps)
+    bw = T * Hkv * (2 * d + 2 * d + d + 4 + 2 * d) + 8 * T
+    return {"quantize_q": {"workload": f"{T} tokens x {Hq} heads x {d}, bf16 -> INT8 + fp32 scale",
+                           "us": ms_q * 1e3, "GBps": bq / (ms_q * 1e-3) / 1e9,
+                           "frac_hbm_peak": bq / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": bq},
+            "write_kv_cache": {"workload": f"{T} tokens x {Hkv} KV heads x {d}: K quantized into the paged INT8 "
+                                           "layout with per-token scales, bf16 V copied",
+                               "us": ms_w * 1e3, "GBps": bw / (ms_w * 1e-3) / 1e9,
+                               "frac_hbm_peak": bw / (ms_w * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": bw}}
+
+
+def run_mfma_sweep(torch):
+    """The matrix-instruction probes (qa_probe.h) at 1, 2, 4 and 8 waves per
+    SIMD (256 workgroups of 4 waves per step): rate of every kind."""
+    from quantized_attention_quantize_amd import probes
+    st = torch.cuda.current_stream()
+    raw = st.cuda_stream
+    sink = torch.empty(8192 * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for kind, (name, _) in probes.MFMA_KINDS.items():
+        row = {}
+        for wps in (1, 2, 4, 8):
+            ops = [0.0]
+
+            def one(i):
+                ops[0] = probes.mfma(kind, 2000, 256 * wps, sink, raw)
+            ms = _timed_ms(torch, one, 5, warm=1)
+            row[f"{wps}_waves_per_simd"] = round(ops[0] / (ms * 1e-3) / 1e12, 1)
+        res[name] = row
+    return res
+
+
 VARLEN_MIX = [8192, 4096, 2048, 1024, 512, 256, 128, 64, 32, 16, 8, 4, 2, 1, 1, 1]
 
 
@@ -544,6 +694,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill/dense lines")
+    ap.add_argument("--only", choices=["decode-batched", "decode-tiny", "producers", "prefill", "dense",
+                                       "dense-causal", "dense-fp8", "mfma-sweep"],
+                    help="run one workload alone and print its line (profiling runs)")
+    ap.add_argument("--reps", type=int, default=20, help="launches timed by --only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run one plain device copy of BYTES (the reference for the memory counters)")
     args = ap.parse_args()
@@ -566,6 +720,21 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
+
+    if args.only:
+        fns = {"decode-batched": lambda: run_decode_batched(torch, qa, args.reps),
+               "decode-tiny": lambda: run_decode_tiny(torch, qa, args.reps),
+               "producers": lambda: run_producers(torch, qa, args.reps),
+               "prefill": lambda: run_prefill(torch, qa, args.reps),
+               "dense": lambda: run_dense(torch, qa, args.reps, False),
+               "dense-causal": lambda: run_dense(torch, qa, args.reps, True),
+               "dense-fp8": lambda: run_dense(torch, qa, args.reps, False, pv_fp8=True),
+               "mfma-sweep": lambda: run_mfma_sweep(torch)}
+        r = fns[args.only]()
+        if isinstance(r, dict):
+            r.pop("_ops", None)
+        print(json.dumps({"only": args.only, **r}), flush=True)
         return
 
     spec, r = run_decode(args, torch, qa, args.warmup)
@@ -614,7 +783,10 @@ def main():
                         "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True),
                         "dense_sage_noncausal_fp8pv": run_dense(torch, qa, 10, False, pv_fp8=True),
                         "dense_sage_causal_fp8pv": run_dense(torch, qa, 10, True, pv_fp8=True),
-                        "dense_sage_varlen_mix": run_varlen(torch, qa, 10)}
+                        "dense_sage_varlen_mix": run_varlen(torch, qa, 10),
+                        "decode_batched_splitk": run_decode_batched(torch, qa, 20),
+                        "decode_tiny": run_decode_tiny(torch, qa, 100),
+                        **run_producers(torch, qa, 30)}
         for e in res["extra"].values():
             if "_ops" not in e:
                 continue

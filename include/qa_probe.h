@@ -24,14 +24,20 @@ extern "C" {
 int qa_probe_stream_read(const void* src, size_t bytes, int wgs, int* sink, hipStream_t stream);
 
 /* Matrix-instruction throughput: every wave of `wgs` workgroups (4 waves
- * each, 1 <= wgs <= 65535) issues `iters` (>= 1) rounds of independent
- * accumulations with operands held in registers:
- *   kind 0: 4 x v_mfma_i32_32x32x32_i8   (4 x 65536 ops per round)
- *   kind 1: 4 x v_mfma_f32_32x32x16_f16  (4 x 32768 flops per round)
- *   kind 2: 8 x v_mfma_i32_16x16x64_i8   (8 x 32768 ops per round)
- *   kind 3: 8 x v_mfma_f32_16x16x32_f16  (8 x 16384 flops per round)
- * Total work = per-round ops x iters x 4 x wgs. One float per thread goes to
- * `sink[wgs * 256]`. */
+ * each, one per SIMD; 1 <= wgs <= 65535) issues `iters` (>= 1) rounds of
+ * independent accumulations with operands held in registers:
+ *   kind 0: 4 x v_mfma_i32_32x32x32_i8          (4 x 65536 ops per round)
+ *   kind 1: 4 x v_mfma_f32_32x32x16_f16         (4 x 32768 flops per round)
+ *   kind 2: 8 x v_mfma_i32_16x16x64_i8          (8 x 32768 ops per round)
+ *   kind 3: 8 x v_mfma_f32_16x16x32_f16         (8 x 16384 flops per round)
+ *   kind 4: 16 x v_mfma_i32_16x16x64_i8         (16 x 32768)
+ *   kind 5: 16 x v_mfma_f32_16x16x32_f16        (16 x 16384)
+ *   kind 6: 4 x v_mfma_i32_16x16x64_i8          (4 x 32768)
+ *   kind 7: 4 x v_mfma_f32_16x16x32_f16         (4 x 16384)
+ *   kind 8: 4 x v_mfma_f32_32x32x64_f8f6f4, E4M3 (4 x 131072)
+ * Total work = per-round ops x iters x 4 x wgs; wgs = 256 k puts k waves on
+ * every SIMD of the 256 compute units. One float per thread (the sum of all
+ * accumulator elements) goes to `sink[wgs * 256]`. */
 int qa_probe_mfma(int kind, int iters, int wgs, float* sink, hipStream_t stream);
 
 /* Vector-ALU throughput: every lane of `wgs` workgroups of 256 threads

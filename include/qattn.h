@@ -210,8 +210,12 @@ size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
  * bf16 numbers (hi = bf16(p), lo = bf16(p - hi)); INT8 V as fp16 codes against
  * fp16 P with the per-token V scale folded into P.
  *
- * Split-K: with P = ceil(max_blocks_per_seq / S), split j of a sequence
- * covers its tokens [16*j*P, min(16*(j+1)*P, ctx)) (possibly none). Each
+ * Split-K ([QK-MMAC] §4 cuts long contexts into segments): split j of a
+ * sequence covers its tokens [16*j*P, min(16*(j+1)*P, ctx)) (possibly none),
+ * with P = ceil(ceil(ctx / 16) / S) blocks, the sequence's own blocks cut
+ * into S equal segments, when num_seqs > 1, and P = ceil(max_blocks_per_seq
+ * / S) for a single sequence (there the table is read without waiting for
+ * the context length). Each
  * split stores (max, sum, unnormalized output) in the workspace and a second
  * kernel merges them. S = 1 writes the output directly. Results are
  * bit-identical from run to run.

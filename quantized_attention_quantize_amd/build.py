@@ -32,9 +32,15 @@ FLAGS = [
 ]
 
 
+# The probes measure instruction rates: their accumulators live in ordinary
+# VGPRs (with AGPR accumulators the compiler rotates the 16x16 accumulators
+# through copies inside the loops, which then measure the copies).
+EXTRA = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

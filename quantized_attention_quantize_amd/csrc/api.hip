@@ -486,6 +486,7 @@ qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const f
   a.num_splits = S; a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
   a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
   a.tq = T;
+  a.seq_split = p->num_seqs > 1;
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }
 
@@ -542,6 +543,7 @@ qa_status_t decode_step(const qa_decode_params_t* p, const void* q, int64_t q_st
   a.slots = slot_mapping; a.kc_w = k_cache; a.ks_w = k_scale; a.vc_w = v_cache; a.vs_w = v_scale;
   a.in_bf16 = dtype == QA_DT_BF16;
   a.tq = 1;
+  a.seq_split = p->num_seqs > 1;
   if (rope != nullptr) a.rope = qa::Rope{rope->positions, rope->cos_sin, rope->rot_dim, rope->neox != 0};
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }

@@ -256,10 +256,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   const int G = a.G, Hq = a.Hq, Hkv = a.Hkv, S = a.num_splits;
 
   // Segment of this split: blocks [split*per, (split+1)*per) of the block
-  // table, cut at the context length. It depends only on host-known sizes, so
-  // the block-table entries are fetched together with the context length
-  // instead of after it.
-  const int per = (a.max_blocks + S - 1) / S;
+  // table, cut at the context length. With seq_split the sequence's own
+  // blocks are cut into S equal segments (per = ceil(ceil(ctx/16)/S): every
+  // split of a sequence gets the same share, whatever the other sequences'
+  // lengths), so the table fetch waits for the context length; otherwise
+  // per = ceil(max_blocks/S) depends only on host-known sizes and the
+  // block-table entries are fetched together with the context length.
+  const int ctx = a.ctx_lens[seq];
+  const int per = a.seq_split ? max(((ctx + 15) / 16 + S - 1) / S, 1) : (a.max_blocks + S - 1) / S;
   const int blk0 = split * per;
   const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
   // lane j: block (j & 1) of this wave's tile j/2 (tiles k .. k+31)
@@ -284,7 +288,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
     }
     qsc = live_col ? a.q_scale[(int64_t)qrow * Hq + h] * a.scale_log2 : 0.0f;
   }
-  const int ctx = a.ctx_lens[seq];
   const int t0 = min(blk0 * 16, ctx);
   const int t1 = min(t0 + per * 16, ctx);
   const int ntiles = (t1 - t0 + 31) >> 5;

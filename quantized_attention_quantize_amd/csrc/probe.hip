@@ -28,47 +28,69 @@ __global__ __launch_bounds__(256) void k_stream_read(const int4* __restrict__ p,
   if (threadIdx.x == 0) sink[blockIdx.x] = acc;
 }
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// One matrix instruction of each measured form, on register operands.
 template <int KIND>
+struct Mfma;
+template <>
+struct Mfma<0> {   // v_mfma_i32_32x32x32_i8: 65536 ops
+  typedef v16i C;
+  static constexpr double kOps = 32.0 * 32 * 32 * 2;
+  static __device__ C run(v4i a, v4i b, v8h, v8h, v8i, v8i, C c) { return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0); }
+};
+template <>
+struct Mfma<1> {   // v_mfma_f32_32x32x16_f16: 32768 flops
+  typedef v16f C;
+  static __device__ C run(v4i, v4i, v8h a, v8h b, v8i, v8i, C c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
+template <>
+struct Mfma<2> {   // v_mfma_i32_16x16x64_i8: 32768 ops
+  typedef v4i C;
+  static __device__ C run(v4i a, v4i b, v8h, v8h, v8i, v8i, C c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
+};
+template <>
+struct Mfma<3> {   // v_mfma_f32_16x16x32_f16: 16384 flops
+  typedef v4f C;
+  static __device__ C run(v4i, v4i, v8h a, v8h b, v8i, v8i, C c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+};
+template <>
+struct Mfma<4> {   // v_mfma_f32_32x32x64_f8f6f4, E4M3 operands (zero scales: unscaled): 131072 flops
+  typedef v16f C;
+  static __device__ C run(v4i, v4i, v8h, v8h, v8i a, v8i b, C c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+// NACC independent accumulator chains per wave; every element of every
+// accumulator feeds the value written at the end (an accumulator element
+// left unread lets the compiler overlap and copy accumulator registers
+// inside the loop, which then measures the copies).
+template <int KIND, int NACC>
 __global__ __launch_bounds__(256) void k_mfma(int iters, float* sink) {
   const int l = threadIdx.x & 63;
   const v4i a = {l, l + 1, l + 2, l + 3}, b = {l * 3, l ^ 5, l + 7, l * 11};
   v8h ha, hb;
+  v8i fa, fb;
   for (int j = 0; j < 8; ++j) {
     ha[j] = (_Float16)(0.001f * (l + j));
     hb[j] = (_Float16)(0.002f * (l - j));
+    fa[j] = 0x38383838 ^ (((l + j) & 7) * 0x01010101);       // E4M3 1.0 .. 1.875 (mantissa bits only)
+    fb[j] = 0x30303030 ^ (((l * 7 + j) & 7) * 0x01010101);   // E4M3 0.5 .. 0.9375
+  }
+  typedef typename Mfma<KIND>::C C;
+  C c[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k)
+    for (int j = 0; j < (int)(sizeof(C) / 4); ++j) c[k][j] = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < NACC; ++k) c[k] = Mfma<KIND>::run(a, b, ha, hb, fa, fb, c[k]);
   }
   float r = 0.0f;
-  if constexpr (KIND == 0) {
-    v16i c[4];
-    for (int k = 0; k < 4; ++k)
-      for (int j = 0; j < 16; ++j) c[k][j] = 0;
-    for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[k], 0, 0, 0);
-    for (int k = 0; k < 4; ++k) r += (float)(c[k][0] + c[k][15]);
-  } else if constexpr (KIND == 1) {
-    v16f c[4];
-    for (int k = 0; k < 4; ++k)
-      for (int j = 0; j < 16; ++j) c[k][j] = 0.0f;
-    for (int it = 0; it < iters; ++it)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha, hb, c[k], 0, 0, 0);
-    for (int k = 0; k < 4; ++k) r += c[k][0] + c[k][15];
-  } else if constexpr (KIND == 2) {
-    v4i c[8];
-    for (int k = 0; k < 8; ++k) c[k] = v4i{0, 0, 0, 0};
-    for (int it = 0; it < iters; ++it)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c[k], 0, 0, 0);
-    for (int k = 0; k < 8; ++k) r += (float)(c[k][0] + c[k][3]);
-  } else {
-    v4f c[8];
-    for (int k = 0; k < 8; ++k) c[k] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int it = 0; it < iters; ++it)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha, hb, c[k], 0, 0, 0);
-    for (int k = 0; k < 8; ++k) r += c[k][0] + c[k][3];
-  }
+  for (int k = 0; k < NACC; ++k)
+    for (int j = 0; j < (int)(sizeof(C) / 4); ++j) r += (float)c[k][j];
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
 }
 
@@ -104,12 +126,17 @@ extern "C" int qa_probe_stream_read(const void* src, size_t bytes, int wgs, int*
 }
 
 extern "C" int qa_probe_mfma(int kind, int iters, int wgs, float* sink, hipStream_t stream) {
-  if (sink == nullptr || kind < 0 || kind > 3 || iters < 1 || wgs < 1 || wgs > 65535) return 1;
+  if (sink == nullptr || kind < 0 || kind > 8 || iters < 1 || wgs < 1 || wgs > 65535) return 1;
   switch (kind) {
-    case 0: k_mfma<0><<<wgs, 256, 0, stream>>>(iters, sink); break;
-    case 1: k_mfma<1><<<wgs, 256, 0, stream>>>(iters, sink); break;
-    case 2: k_mfma<2><<<wgs, 256, 0, stream>>>(iters, sink); break;
-    default: k_mfma<3><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 0: k_mfma<0, 4><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 1: k_mfma<1, 4><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 2: k_mfma<2, 8><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 3: k_mfma<3, 8><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 4: k_mfma<2, 16><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 5: k_mfma<3, 16><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 6: k_mfma<2, 4><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    case 7: k_mfma<3, 4><<<wgs, 256, 0, stream>>>(iters, sink); break;
+    default: k_mfma<4, 4><<<wgs, 256, 0, stream>>>(iters, sink); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

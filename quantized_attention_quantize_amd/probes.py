@@ -23,6 +23,11 @@ MFMA_KINDS = {
     1: ("f16_32x32x16", 4 * 32768),
     2: ("i8_16x16x64", 8 * 32768),
     3: ("f16_16x16x32", 8 * 16384),
+    4: ("i8_16x16x64_acc16", 16 * 32768),
+    5: ("f16_16x16x32_acc16", 16 * 16384),
+    6: ("i8_16x16x64_acc4", 4 * 32768),
+    7: ("f16_16x16x32_acc4", 4 * 16384),
+    8: ("fp8_32x32x64", 4 * 131072),
 }
 
 VALU_KINDS = {0: "exp_f32", 1: "fma_f32"}

@@ -280,7 +280,8 @@ def test_probe_library_exports_and_rejects():
     assert L.qa_probe_stream_read(FAKE, 16, 0, FAKE, None) == 1
     assert L.qa_probe_stream_read(FAKE, 16, 70000, FAKE, None) == 1
     assert L.qa_probe_stream_read(FAKE, 0, 4, FAKE, None) == 0         # nothing to read
-    assert L.qa_probe_mfma(4, 10, 4, FAKE, None) == 1
+    assert L.qa_probe_mfma(9, 10, 4, FAKE, None) == 1
+    assert L.qa_probe_mfma(-1, 10, 4, FAKE, None) == 1
     assert L.qa_probe_mfma(0, 0, 4, FAKE, None) == 1
     assert L.qa_probe_mfma(0, 10, 4, None, None) == 1
     assert L.qa_probe_valu(2, 10, 4, FAKE, None) == 1

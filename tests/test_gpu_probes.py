@@ -28,7 +28,7 @@ def test_stream_read_visits_every_element():
     assert sink.cpu().numpy().tolist() == want
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+@pytest.mark.parametrize("kind", list(range(9)))
 def test_mfma_probe_runs(kind):
     from quantized_attention_quantize_amd import probes
     sink = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device="cuda")

@@ -32,10 +32,13 @@ BLOCK_SIZE = 16
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return the
     raw 16-bit patterns as uint16. Inputs are finite draws."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
-    return r.astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
 
 
 def to_f16_bits(x: np.ndarray) -> np.ndarray:
@@ -158,7 +161,8 @@ def paged_inputs(spec: PagedSpec, seqs: Optional[list] = None) -> PagedInputs:
         if seqs is not None and s not in seqs:
             continue
         g = _rng(spec.seed, 2, s)
-        kf = g.standard_normal((c, Hkv, d), dtype=np.float32) + bias[None]
+        kf = g.standard_normal((c, Hkv, d), dtype=np.float32)
+        kf += bias[None]
         k[cu_kv[s]:cu_kv[s + 1]] = _store(kf, spec.dtype)
         del kf
         v[cu_kv[s]:cu_kv[s + 1]] = _store(g.standard_normal((c, Hkv, d), dtype=np.float32), spec.dtype)
