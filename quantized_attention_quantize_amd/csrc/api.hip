@@ -64,6 +64,8 @@ qa_status_t check_decode(const qa_decode_params_t* p) {
              "GQA group %d > 16 query heads per KV head", p->num_q_heads / p->num_kv_heads);
   QA_REQUIRE(p->num_splits <= 65535, QA_ERR_UNSUPPORTED, "num_splits %d too large", p->num_splits);
   QA_REQUIRE(p->num_seqs <= 65535 && p->num_kv_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
+  QA_REQUIRE((int64_t)p->num_seqs * p->num_q_heads <= (1 << 24), QA_ERR_UNSUPPORTED,
+             "num_seqs x num_q_heads %lld > 2^24", (long long)p->num_seqs * p->num_q_heads);
   return QA_OK;
 }
 

@@ -597,13 +597,74 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
   }
 }
 
+// The merge for few splits (S <= kFewSplits): one thread per (query row,
+// head, 4 channels) walks the S partials with every load of a batch of 8
+// issued before the merge; many sequences fill the grid.
+constexpr int kFewSplits = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_combine_few(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+                                                     int32_t Hq, int32_t S, int32_t rows, bool out_bf16,
+                                                     void* out) {
+  constexpr int C4 = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)rows * Hq * C4) return;
+  const int c4 = (int)(t % C4);
+  const int64_t rh = t / C4;                  // row * Hq + head
+  const int64_t base = rh * S;
+  float m = kNegInf, lsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float2 ml[8];
+    float4 o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sp = min(s0 + i, S - 1);
+      ml[i] = *reinterpret_cast<const float2*>(ws_ml + (base + sp) * 2);
+      o[i] = *reinterpret_cast<const float4*>(ws_o + (base + sp) * D + 4 * c4);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i >= S || ml[i].x == kNegInf) continue;
+      const float mn = fmaxf(m, ml[i].x);
+      const float a0 = fast_exp2(m - mn), a1 = fast_exp2(ml[i].x - mn);
+      acc.x = acc.x * a0 + a1 * o[i].x; acc.y = acc.y * a0 + a1 * o[i].y;
+      acc.z = acc.z * a0 + a1 * o[i].z; acc.w = acc.w * a0 + a1 * o[i].w;
+      lsum = lsum * a0 + a1 * ml[i].y;
+      m = mn;
+    }
+  }
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  const int64_t oi = rh * D + 4 * c4;
+  if (out_bf16) {
+    uint2 w;
+    w.x = f32_to_bf16_bits(acc.x * inv) | (f32_to_bf16_bits(acc.y * inv) << 16);
+    w.y = f32_to_bf16_bits(acc.z * inv) | (f32_to_bf16_bits(acc.w * inv) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) = w;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+}
+
+template <int D>
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+  const int rows = a.num_seqs * a.tq;
+  if (a.num_splits <= kFewSplits) {
+    const int64_t threads = (int64_t)rows * a.Hq * (D / 4);
+    k_combine_few<D><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
+                                                                             rows, a.out_bf16, a.out);
+  } else {
+    k_combine<D><<<dim3(a.Hq, rows, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits, a.out_bf16, a.out);
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool V_I8, bool EXPORT_QK, bool FUSED, bool MT, bool ROPE = false>
 hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   if (phase == DecodePhase::kCombine) {
-    if (a.num_splits > 1)
-      k_combine<D><<<dim3(a.Hq, a.num_seqs * a.tq, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
-                                                                        a.out_bf16, a.out);
-    return hipGetLastError();
+    if (a.num_splits > 1) return launch_combine<D>(a, st);
+    return hipSuccess;
   }
   const dim3 grid(a.num_splits, a.Hkv, a.num_seqs);
   // LDS: per-wave partials [kWaves][G][D] plus (max, sum) pairs.
@@ -617,8 +678,7 @@ hipError_t run_decode(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
   if (!EXPORT_QK && a.num_splits > 1 && phase == DecodePhase::kBoth) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_combine<D><<<dim3(a.Hq, a.num_seqs * a.tq, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
-                                                                      a.out_bf16, a.out);
+    return launch_combine<D>(a, st);
   }
   return hipGetLastError();
 }

@@ -104,10 +104,22 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i_t a, v8i_t b, v16f c) {
 // aliasing the reads of the other buffer; the caller waits (vmcnt) before
 // the barrier. GFX9 parts need one wait state between an SALU write of M0
 // and an LDS-DMA instruction that reads it: the s_nop provides it.
-__device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(src) : "memory", "m0");
+// The source is a wave-uniform base (scalar registers) plus each lane's own
+// 32-bit offset (`voff`, 16 * lane for a 1 KB chunk), so the address math
+// of a copy is scalar.
+// LDS byte address of a __shared__ object (a constant: no generic-pointer
+// null check at run time).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
 }
 
 // Wait until every vector memory operation of the wave has completed
@@ -283,7 +295,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   // ---- tile staging: global -> registers -> LDS ---------------------------
   const int64_t k_head = (int64_t)kvh * D * 16;    // K bytes before this KV head in a block
   const int64_t k_blk = (int64_t)Hkv * D * 16;     // K bytes per physical block
+  const uint32_t kblk32 = (uint32_t)k_blk;         // (< 2^32: Hkv <= 65535, D <= 256)
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same value, held in a scalar
+  const uint32_t lane16 = (uint32_t)lane * 16u;                // each lane's 16 bytes of a 1 KB copy
+  const uint32_t sk_lds = lds_addr(&s_k[0][0]), sv_lds = lds_addr(&s_v[0][0]);
   // Physical blocks of a paged tile: lanes 0..3 read the four block-table
   // entries with one vector load, issued one tile ahead of the fetch that
   // uses them (a vector load, so that waiting for LDS reads - lgkmcnt - never
@@ -315,22 +330,22 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       for (int i = 0; i < (4 * KC + NW - 1) / NW; ++i) {
         const int c = wave_s + NW * i, b = c / KC, part = c % KC;
         if (4 * KC % NW != 0 && c >= 4 * KC) break;   // wave-uniform
-        copy16_to_lds(a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16,
-                      &s_k[kbuf][b * KBS + part * 1024]);
+        copy16_to_lds(a.k_blocks + (uint64_t)(uint32_t)pick(pb, b) * kblk32 + k_head + part * 1024, lane16,
+                      sk_lds + (uint32_t)(kbuf * 4 * KBS + b * KBS + part * 1024));
       }
     }
 #pragma unroll
     for (int i = 0; i < (KDMA ? 0 : KU); ++i) {
       if ((4 * KUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * KUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / KUB;
-      const int8_t* base = a.k_blocks + phys(b) * k_blk + k_head;
+      const int8_t* base = a.k_blocks + (uint64_t)(uint32_t)phys(b) * kblk32 + k_head;
       st.k[i] = *reinterpret_cast<const v4i*>(base + (uint32_t)((tid + i * NT) % KUB) * 16u);
     }
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
       if ((4 * VUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * VUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / VUB;
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * VB;
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(a.v_blocks) + ((uint64_t)(uint32_t)phys(b) * kblk32 + k_head) * VB;
       st.v[i] = *reinterpret_cast<const v4i*>(base + (uint32_t)((tid + i * NT) % VUB) * 16u);
     }
     if constexpr (!DENSE) {
@@ -405,15 +420,20 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   // compiler cannot tell the two LDS buffers apart and waits for the next
   // tile's copies before the first LDS read of the current one. The wait
   // before the end-of-tile barrier covers them.
+  // Block b of tile t is the sequence's block min(4t + b, last_blk): a 32-bit
+  // index times the per-block stride, added to the sequence's first block
+  // (scalar arithmetic, no 64 x 64-bit products per copy).
+  const int8_t* kseq = a.k_blocks + blk_base * k_blk + k_head;
+  const uint8_t* vseq = reinterpret_cast<const uint8_t*>(a.v_blocks) + (blk_base * k_blk + k_head) * 2;
   auto dma = [&](int buf, int tile) {
     constexpr int KC = D / 64;                     // 1 KB chunks per K block (per head)
     constexpr int VC = D / 32;                     // 1 KB chunks per V block (per head)
-    auto phys = [&](int b) -> int64_t { return blk_base + min(tile * 4 + b, last_blk); };
+    auto blk = [&](int b) -> uint64_t { return (uint64_t)(uint32_t)min(tile * 4 + b, last_blk) * kblk32; };
 #pragma unroll
     for (int i = 0; i < (4 * KC + NW - 1) / NW; ++i) {
       const int c = wave_s + NW * i, b = c / KC, part = c % KC;
       if (4 * KC % NW != 0 && c >= 4 * KC) break;   // wave-uniform
-      copy16_to_lds(a.k_blocks + phys(b) * k_blk + k_head + part * 1024 + lane * 16, &s_k[buf][b * KBS + part * 1024]);
+      copy16_to_lds(kseq + blk(b) + part * 1024, lane16, sk_lds + (uint32_t)(buf * 4 * KBS + b * KBS + part * 1024));
     }
     if constexpr (PV8) {
       // one E4M3 block of 64 keys: D rows of 64 bytes, D/16 chunks of 1 KB
@@ -431,15 +451,14 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       for (int i = 0; i < (V8C + NW - 1) / NW; ++i) {
         const int c = wave_s + NW * i;
         if (V8C % NW != 0 && c >= V8C) break;   // wave-uniform
-        copy16_to_lds(vsrc + c * 1024 + lane * 16, reinterpret_cast<const char*>(s_v[buf]) + c * 1024);
+        copy16_to_lds(vsrc + c * 1024, lane16, sv_lds + (uint32_t)(buf * KT * D * 2 + c * 1024));
       }
     }
 #pragma unroll
     for (int i = 0; i < (PV8 ? 0 : (4 * VC + NW - 1) / NW); ++i) {
       const int c = wave_s + NW * i, b = c / VC, part = c % VC;
       if (4 * VC % NW != 0 && c >= 4 * VC) break;   // wave-uniform
-      copy16_to_lds(reinterpret_cast<const uint8_t*>(a.v_blocks) + (phys(b) * k_blk + k_head) * 2 + part * 1024 + lane * 16,
-                    reinterpret_cast<const char*>(s_v[buf]) + b * D * 32 + part * 1024);
+      copy16_to_lds(vseq + 2 * blk(b) + part * 1024, lane16, sv_lds + (uint32_t)(buf * KT * D * 2 + b * D * 32 + part * 1024));
     }
   };
   constexpr bool kDma = DENSE;
