@@ -34,8 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-INT8_PEAK_TOPS = 5033.0      # dense INT8 MFMA, 256 CU x 2.4 GHz x 8192 ops/clk
-FP16_PEAK_TFLOPS = 2516.0
+# MI355X published dense matrix peaks (no sparsity)
+INT8_PEAK_TOPS = 5000.0
+FP16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def decode_bytes(spec) -> dict:
@@ -375,7 +377,7 @@ def run_prefill(torch, qa, reps):
     mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
     return {"workload": "chunked_prefill 2048 new tokens on 16384 history, 24/4 heads, d256",
             "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
-            "_ops": (qk, pv)}
+            "_ops": (qk, pv, "f16")}
 
 
 def run_dense(torch, qa, reps, causal, options=False, pv_fp8=False):
@@ -415,12 +417,13 @@ def run_dense(torch, qa, reps, causal, options=False, pv_fp8=False):
     B, H, N, d = spec.batch, spec.num_q_heads, spec.seq_q, spec.head_dim
     qk, pv = flash_ops([N] * B, [N] * B, H, d, causal)
     tops = (qk + pv) / (ms * 1e-3) / 1e12
-    mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
+    pv_peak = FP8_PEAK_TFLOPS if pv_fp8 else FP16_PEAK_TFLOPS
+    mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (pv_peak * 1e12)) / (ms * 1e-3)
     return {"workload": f"dense_sage B2 H32 N8192 d128 {'causal' if causal else 'non-causal'} "
                         "(full chain: smooth_k + per-block quantization + attention"
                         + (", HND, smooth_v, LSE output)" if options else ", FP8 E4M3 P.V)" if pv_fp8 else ")"),
             "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
-            "_ops": (qk, pv)}
+            "_ops": (qk, pv, "fp8" if pv_fp8 else "f16")}
 
 
 def _timed_ms(torch, fn, reps, warm=3):
@@ -678,8 +681,8 @@ def run_practical_peaks(torch, step_bytes: int, pools: int) -> dict:
             ms = timed(one, 5)
             best = max(best, ops[0] / (ms * 1e-3) / 1e12)
         out[f"valu_{name}_T_lane_ops"] = round(best, 2)
-    out["note"] = ("T = TOPS (int8) or TFLOP/s (fp16), include/qa_probe.h; the attention kernels issue the "
-                   "16x16 forms; valu_* in tera lane operations per second (one exponential per score)")
+    out["note"] = ("T = TOPS (int8) or TFLOP/s (fp16, fp8), include/qa_probe.h; valu_* in tera lane "
+                   "operations per second (one exponential per score)")
     return out
 
 
@@ -790,14 +793,14 @@ def main():
         for e in res["extra"].values():
             if "_ops" not in e:
                 continue
-            # fraction of the mixed roofline at the measured matrix rates: the
-            # 32x32 forms (the chip's best) and the 16x16 forms the kernels issue
-            qk, pv = e.pop("_ops")
+            # fraction of the mixed roofline at the best measured rate of each
+            # operand type over the probe forms (the 16x16 forms with 16
+            # independent accumulators are the fastest measured)
+            qk, pv, pv_type = e.pop("_ops")
             t = e["ms"] * 1e-3
-            e["frac_practical_mixed_32x32"] = round((qk / (pk["mfma_i8_32x32x32_T"] * 1e12) +
-                                                     pv / (pk["mfma_f16_32x32x16_T"] * 1e12)) / t, 4)
-            e["frac_practical_mixed_16x16"] = round((qk / (pk["mfma_i8_16x16x64_T"] * 1e12) +
-                                                     pv / (pk["mfma_f16_16x16x32_T"] * 1e12)) / t, 4)
+            best = lambda pre: max(v for k_, v in pk.items() if k_.startswith(pre))
+            e["frac_practical_mixed"] = round((qk / (best("mfma_i8_") * 1e12) +
+                                               pv / (best(f"mfma_{pv_type}_") * 1e12)) / t, 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, r["inp"], args.cpu_budget, r["out"])
     pr = torch.cuda.get_device_properties(0)

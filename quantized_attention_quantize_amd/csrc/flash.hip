@@ -164,11 +164,13 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   constexpr int CG = D / 16;
   constexpr int QT = NW * 16 * QG;                 // query rows per workgroup
   constexpr int VB = St::VB, KUB = St::KUB, VUB = St::VUB, KU = St::KU, VU = St::VU;
-  // K: 4 blocks of D*16 bytes, each padded by 64 bytes so that the two
-  // blocks read by one 16-lane pass of ds_read_b128 fall on complementary
-  // banks. V: the two 16-byte halves of each channel's 16-token row are
-  // swapped when bit 3 of the channel is set, so 16 consecutive channels
-  // cover all banks.
+  // ds_read_b128 serves a half-wave in two passes of 16 lanes, chosen by the
+  // parity of lane bits 2..4 (quads 0,3,5,6 and quads 1,2,4,7); a pass with
+  // 16 distinct 16-byte bank slots (of 64 four-byte banks) is conflict-free.
+  // K: 4 blocks of D*16 bytes, each padded by 64 bytes, so the blocks that
+  // one pass reads fall on complementary banks. V: channel rows of 32 bytes
+  // in plain order; a pass reads 8 channels at one key half and 8 at the
+  // other, which covers all 16 slots.
   constexpr int KBS = D * 16 + 64;
   constexpr bool kRowSumMfma = VK != kVI8;         // INT8 V folds sV into P: sum P on the VALU
   constexpr bool kMagic = DENSE;                          // dense scores read as floats, see QK
@@ -374,7 +376,6 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       const int b = (i * NT + 64 * wave_s) / VUB, r = u % VUB;
       const int ch = VB == 2 ? r >> 1 : r;          // channel of this unit
       const int row = (b * D + ch) * 16;            // fp16 element index of the channel row
-      const int sw = (ch >> 3) & 1;                 // half swap for this channel
       if constexpr (VB == 2) {
         const uint4 w = make_uint4(st.v[i][0], st.v[i][1], st.v[i][2], st.v[i][3]);
         v8h f = VK == kVF16 ? f16x8_from_u4(w) : bf16x8_to_f16x8(w);
@@ -384,7 +385,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
           for (int e = 0; e < 8; ++e)
             if (t_first + e >= kv_len) f[e] = (_Float16)0.0f;
         }
-        *reinterpret_cast<v8h*>(&s_v[buf][row + (((r & 1) ^ sw) << 3)]) = f;
+        *reinterpret_cast<v8h*>(&s_v[buf][row + ((r & 1) << 3)]) = f;
       } else {
         const uint4 w = make_uint4(st.v[i][0], st.v[i][1], st.v[i][2], st.v[i][3]);
         v8h f0 = i8x8_to_f16x8(make_uint2(w.x, w.y));
@@ -397,8 +398,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
             if (t_first + 8 + e >= kv_len) f1[e] = (_Float16)0.0f;
           }
         }
-        *reinterpret_cast<v8h*>(&s_v[buf][row + (sw << 3)]) = f0;
-        *reinterpret_cast<v8h*>(&s_v[buf][row + ((1 ^ sw) << 3)]) = f1;
+        *reinterpret_cast<v8h*>(&s_v[buf][row]) = f0;
+        *reinterpret_cast<v8h*>(&s_v[buf][row + 8]) = f1;
       }
     }
     if constexpr (!DENSE) {
@@ -411,7 +412,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   };
 
   // Dense inputs come from this library's own preprocessing, whose K and V
-  // block layouts (V rows already half-swapped) equal the LDS layouts, so
+  // block layouts equal the LDS layouts, so
   // their tiles are copied straight from global memory into LDS by
   // global_load_lds_dwordx4: each wave moves 1 KB chunks (lane l's 16 bytes
   // land at chunk base + 16*l), with no staging registers and no LDS writes.
@@ -713,7 +714,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
         const int chn = 16 * c + n;
-        const v8h vf = *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + chn) * 16 + (((so >> 3) ^ ((chn >> 3) & 1)) << 3)]);
+        const v8h vf = *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + chn) * 16 + so]);
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vf, pf[qg][half], O[qg][c]);
       }

@@ -504,9 +504,8 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
 }
 
 // V [B, N, H, D] (bf16 or fp16) -> fp16 [B*ceil(N/16), H, D, 16]: row ch of a block
-// holds its 16 tokens of channel ch, with the two 8-token halves swapped when bit 3
-// of ch is set (the attention kernel's LDS layout, so its tiles are copied
-// unchanged); padding tokens of the last block are zero. bf16 values become the
+// holds its 16 tokens of channel ch in order (the attention kernel's LDS layout,
+// so its tiles are copied unchanged); padding tokens of the last block are zero. bf16 values become the
 // nearest fp16 (exact in the fp16 normal range).
 // (b, t, h, c) of v lives at b*sb + t*st + h*sh + c. With vmean (smooth_v)
 // each value becomes fl16(fl32(v) - vmean[b, h, c]).
@@ -550,7 +549,7 @@ __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v
   uint16_t* dst = vb + ((rows.block0(b, 16) + blk) * H + h) * D * 16;
   for (int u = threadIdx.x; u < 2 * D; u += 256) {   // output unit: channel u/2, half u%2
     const int ch = u >> 1;
-    const int t0 = 8 * ((u & 1) ^ ((ch >> 3) & 1));
+    const int t0 = 8 * (u & 1);
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tile[t0 + 2 * i][ch] | ((uint32_t)tile[t0 + 2 * i + 1][ch] << 16);
