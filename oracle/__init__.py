@@ -89,6 +89,8 @@ _SIGS = {
     "or_paged_decode_split": [_P(_Paged), _vp, _vp, _vp, _f64, _i32, _vp],
     "or_chunked_prefill": [_P(_Paged), _vp, _vp, _vp, _vp, _i64, _f64, _vp, _vp, _vp],
     "or_attention_fp64": [_vp, _vp, _vp, _i64, _i64, _i32, _f64, _vp, _vp],
+    "or_paged_v_fp8": [_P(_Paged), _i32, _i32, _i32, _vp, _vp],
+    "or_chunked_prefill_fp8pv": [_P(_Paged), _vp, _vp, _vp, _vp, _i64, _f64, _vp, _vp, _vp, _vp],
     "or_set_num_threads": [_i32],
     "or_max_threads": [],
     "or_sage_quantize": [_P(_Dense), _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
@@ -408,6 +410,37 @@ def chunked_prefill(q_i8, q_scale, cu_seqlens_q, context_lens, caches, block_tab
     return out
 
 
+def paged_v_fp8(caches, block_tables, seq, ctx, kv_head, num_seqs, num_kv_heads, d, v_dtype="bf16"):
+    """E4M3 codes [ctx, d] (uint8) and channel scales [d] (fp32) of the V of
+    one (sequence, KV head) for the FP8 P.V product."""
+    st, keep = _paged(caches, block_tables, num_seqs, num_kv_heads, num_kv_heads, d, v_dtype)
+    codes = np.empty((int(ctx), d), np.uint8)
+    scales = np.empty(d, np.float32)
+    _L().or_paged_v_fp8(ctypes.byref(st), int(seq), int(ctx), int(kv_head), _p(codes), _p(scales))
+    return codes, scales
+
+
+def chunked_prefill_fp8pv(q_i8, q_scale, cu_seqlens_q, context_lens, caches, block_tables, num_kv_heads,
+                          scale=None, v_dtype="bf16", rows=None, heads=None, return_sigma=False):
+    """Chunked prefill with the P.V product in FP8 (E4M3): V per (sequence,
+    KV head, channel) scaled to E4M3 over the sequence's cached tokens, per
+    row P8 = E4M3(448 exp(s - m)) at the exact maximum m, out = sum P8 V8 /
+    sum P8 * s_c. Returns fp64 [Tq_total, Hq, d]; with return_sigma also the
+    standard deviations of the lazily referenced implementation."""
+    q = _c(q_i8, np.int8)
+    T, Hq, d = q.shape
+    qs = _c(q_scale, np.float32)
+    cu = _c(cu_seqlens_q, np.int32)
+    ctx = _c(context_lens, np.int32)
+    st, keep = _paged(caches, block_tables, len(ctx), Hq, num_kv_heads, d, v_dtype)
+    rm, hm = _mask(rows, T), _mask(heads, Hq)
+    out = np.empty((T, Hq, d), np.float64)
+    sig = np.empty_like(out) if return_sigma else None
+    _L().or_chunked_prefill_fp8pv(ctypes.byref(st), _p(q), _p(qs), _p(cu), _p(ctx), T, _scale_arg(scale), _p(rm),
+                                  _p(hm), _p(out), _p(sig))
+    return (out, sig) if return_sigma else out
+
+
 def attention_fp64(q, k, v, scale, visible=None):
     """Textbook softmax(q k^T * scale) v in fp64 for [N, d] operands with an
     optional boolean visibility mask [Nq, Nk]."""
@@ -585,6 +618,7 @@ __all__ = [
     "e4m3_encode", "e4m3_decode", "e4m3_round", "v_fp8_per_channel", "dense_sage_attention_fp8pv",
     "dense_sage_attention_fp8pv_lazy",
     "paged_qk_int32", "paged_decode", "paged_decode_split", "split_segments", "chunked_prefill",
+    "paged_v_fp8", "chunked_prefill_fp8pv",
     "dense_sage_attention", "attention_fp64", "default_scale",
     "sage_quantize", "sage_smooth_v", "sage_lse_correction", "sage_forward", "sage_varlen_forward",
     "build_library", "load_library", "use_library", "set_num_threads", "max_threads",

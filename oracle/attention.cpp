@@ -67,6 +67,15 @@ int32_t int_dot(const int8_t* a, const int8_t* b, int32_t d) {
   return acc;
 }
 
+// Keys seen by row r of a chunk of tq new tokens at the end of a context of
+// n tokens: the row sits at position n - tq + r and sees keys t <= that
+// position; a row placed before the first key sees none.
+int32_t chunk_visible_keys(int32_t n, int32_t tq, int32_t r) {
+  const int64_t pos = (int64_t)n - tq + r;
+  if (pos < 0) return 0;
+  return (int32_t)std::min<int64_t>(pos + 1, n);
+}
+
 // [QK-MMAC] §1: the recovered score of every key for one query row.
 void scores_row(const int8_t* q, float q_scale, const Gathered& g, int32_t n, int32_t d, double scale,
                 double* s) {
@@ -208,12 +217,112 @@ void or_chunked_prefill(const or_paged_t* c, const int8_t* q_i8, const float* q_
       std::vector<double> sr(n);
       for (int32_t i = a; i < b; ++i) {
         if (row_mask != nullptr && !row_mask[i]) continue;
-        const int64_t pos = (int64_t)n - tq + (i - a);
-        if (pos < 0) continue;                   // a token placed before the first key sees none
-        const int32_t nvis = (int32_t)std::min<int64_t>(pos + 1, n);
+        const int32_t nvis = chunk_visible_keys(n, tq, i - a);
+        if (nvis == 0) continue;
         const int64_t row = (int64_t)i * c->Hq + h;
         scores_row(q_i8 + row * d, q_scale[row], g, nvis, d, sc, sr.data());
         softmax_pv(sr.data(), nvis, g.v.data(), d, d, out + row * d);
+      }
+    }
+  }
+}
+
+// ---- chunked prefill with the P.V product in FP8 (E4M3) -----------------------
+// [SAGE-MACA] names the FP8 P.V product of later SageAttention versions (not
+// portable to its hardware); the pages fix none of its arithmetic. Reading:
+// the dense FP8 definition (or_dense_attention_fp8pv) applied to a paged
+// sequence. V of a (sequence, KV head) is taken over all ctx cached tokens as
+// fp32 values (16-bit V exactly, INT8 V as fl32(code * scale)); per channel
+// s_c = fl32(max_t |v| / 448) and V8 = E4M3(fl32(v / s_c)), 0 where s_c = 0.
+// Per query row, m = the exact maximum of its visible scores,
+// P8_j = E4M3(448 exp(s_j - m)) and out = sum_j P8_j V8_j / sum_j P8_j * s_c.
+// Sums and products in fp64.
+
+// E4M3 values and channel scales of the first ctx V tokens of one (sequence,
+// KV head): codes [ctx, d], scales [d].
+void or_paged_v_fp8(const or_paged_t* c, int32_t seq, int32_t ctx, int32_t kvh, uint8_t* codes, float* scales) {
+  const int32_t d = c->d;
+  const Gathered g = gather(c, seq, ctx, kvh);
+  std::vector<float> v((size_t)ctx * d);
+  for (size_t i = 0; i < v.size(); ++i) v[i] = (float)g.v[i];   // fl32(code * scale) for INT8 V
+  for (int32_t ch = 0; ch < d; ++ch) {
+    float amax = 0.0f;
+    for (int32_t t = 0; t < ctx; ++t) amax = std::max(amax, std::fabs(v[(int64_t)t * d + ch]));
+    const float sc = amax / 448.0f;
+    scales[ch] = sc;
+    for (int32_t t = 0; t < ctx; ++t)
+      codes[(int64_t)t * d + ch] = sc > 0.0f ? e4m3_encode1((double)(v[(int64_t)t * d + ch] / sc)) : 0;
+  }
+}
+
+// The definition above for the rows of or_chunked_prefill (row_mask,
+// head_mask, out the same). sigma (NULL = not computed) [total_q, Hq, d]:
+// the standard deviation of an implementation that rounds P from a lazily
+// moved reference, as in or_dense_attention_fp8pv (its model and bounds).
+void or_chunked_prefill_fp8pv(const or_paged_t* c, const int8_t* q_i8, const float* q_scale, const int32_t* cu_q,
+                              const int32_t* ctx, int64_t total_q, double scale, const uint8_t* row_mask,
+                              const uint8_t* head_mask, double* out, double* sigma) {
+  const int32_t G = c->Hq / c->Hkv, d = c->d;
+  const double sc = resolve_scale(scale, d);
+  const double u = std::ldexp(1.0, -4), sub = std::ldexp(1.0, -6), sub_err = std::ldexp(1.0, -10);
+  std::fill(out, out + total_q * c->Hq * d, 0.0);
+  if (sigma != nullptr) std::fill(sigma, sigma + total_q * c->Hq * d, 0.0);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int32_t s = 0; s < c->num_seqs; ++s) {
+    for (int32_t h = 0; h < c->Hq; ++h) {
+      const int32_t a = cu_q[s], b = cu_q[s + 1], n = ctx[s], tq = b - a;
+      if (n <= 0 || tq <= 0 || (head_mask != nullptr && !head_mask[h])) continue;
+      bool any = row_mask == nullptr;
+      for (int32_t i = a; i < b && !any; ++i) any = row_mask[i] != 0;
+      if (!any) continue;
+      const Gathered g = gather(c, s, n, h / G);
+      std::vector<uint8_t> codes((size_t)n * d);
+      std::vector<float> svc(d);
+      or_paged_v_fp8(c, s, n, h / G, codes.data(), svc.data());
+      std::vector<double> v8((size_t)n * d);
+      for (size_t i = 0; i < v8.size(); ++i) v8[i] = e4m3_decode1(codes[i]);
+      std::vector<double> sr(n), p(n), p8(n), o(d), oe(d);
+      for (int32_t i = a; i < b; ++i) {
+        if (row_mask != nullptr && !row_mask[i]) continue;
+        const int32_t nvis = chunk_visible_keys(n, tq, i - a);
+        if (nvis == 0) continue;
+        const int64_t row = (int64_t)i * c->Hq + h;
+        scores_row(q_i8 + row * d, q_scale[row], g, nvis, d, sc, sr.data());
+        double m = -kInf;
+        for (int32_t j = 0; j < nvis; ++j) m = std::max(m, sr[j]);
+        double l8 = 0.0, lp = 0.0;
+        for (int32_t j = 0; j < nvis; ++j) {
+          p[j] = std::exp(sr[j] - m);
+          p8[j] = p[j] > 0.0 ? e4m3_decode1(e4m3_encode1(448.0 * p[j])) : 0.0;
+          l8 += p8[j];
+          lp += p[j];
+        }
+        std::fill(o.begin(), o.end(), 0.0);
+        std::fill(oe.begin(), oe.end(), 0.0);
+        for (int32_t j = 0; j < nvis; ++j) {
+          const double* vj = v8.data() + (int64_t)j * d;
+          for (int32_t ch = 0; ch < d; ++ch) {
+            o[ch] += p8[j] * vj[ch];
+            oe[ch] += p[j] * vj[ch];
+          }
+        }
+        for (int32_t ch = 0; ch < d; ++ch) out[row * d + ch] = o[ch] / l8 * (double)svc[ch];
+        if (sigma != nullptr) {
+          std::vector<double> var(d, 0.0);
+          for (int32_t j = 0; j < nvis; ++j) {
+            if (p[j] == 0.0) continue;
+            const double w = p[j] / lp;
+            const double e56 = 56.0 * p[j] >= sub ? u * w : sub_err / (56.0 * lp);
+            const double e448 = 448.0 * p[j] >= sub ? u * w : sub_err / (448.0 * lp);
+            const double ee = e56 * e56 + e448 * e448;
+            const double* vj = v8.data() + (int64_t)j * d;
+            for (int32_t ch = 0; ch < d; ++ch) {
+              const double dv = (vj[ch] - oe[ch] / lp) * (double)svc[ch];
+              var[ch] += dv * dv * ee;
+            }
+          }
+          for (int32_t ch = 0; ch < d; ++ch) sigma[row * d + ch] = std::sqrt(var[ch] / 3.0);
+        }
       }
     }
   }

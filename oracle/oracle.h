@@ -71,6 +71,13 @@ void or_chunked_prefill(const or_paged_t* c, const int8_t* q_i8, const float* q_
                         const uint8_t* head_mask, double* out);
 void or_attention_fp64(const double* q, const double* k, const double* v, int64_t nq, int64_t nk, int32_t d,
                        double scale, const uint8_t* visible, double* out);
+/* chunked prefill with the P.V product in FP8 (E4M3): the V scales and codes of
+   one (sequence, KV head), codes [ctx, d] and scales [d]; the attention with
+   its tolerance model (sigma may be NULL) */
+void or_paged_v_fp8(const or_paged_t* c, int32_t seq, int32_t ctx, int32_t kvh, uint8_t* codes, float* scales);
+void or_chunked_prefill_fp8pv(const or_paged_t* c, const int8_t* q_i8, const float* q_scale, const int32_t* cu_q,
+                              const int32_t* ctx, int64_t total_q, double scale, const uint8_t* row_mask,
+                              const uint8_t* head_mask, double* out, double* sigma);
 
 /* threads of the parallel loops (for timing the oracle) */
 void or_set_num_threads(int32_t n);

@@ -66,8 +66,29 @@ MUTATIONS = [
      "bounds[2 * j + 1] = std::min((j + 1) * L - 16, ctx);", pins.test_split_segments_cover_context, ()),
     ("prefill_causal_off_by_one", "attention.cpp", "std::min<int64_t>(pos + 1, n);", "std::min<int64_t>(pos, n);",
      pins.test_prefill_equals_textbook_masked_attention, ()),
-    ("prefill_top_left_alignment", "attention.cpp", "const int64_t pos = (int64_t)n - tq + (i - a);",
-     "const int64_t pos = (i - a);", pins.test_prefill_equals_textbook_masked_attention, ()),
+    ("prefill_top_left_alignment", "attention.cpp", "const int64_t pos = (int64_t)n - tq + r;",
+     "const int64_t pos = r;", pins.test_prefill_equals_textbook_masked_attention, ()),
+    # ---- chunked prefill with the FP8 P.V product
+    ("prefill_fp8_scale_divisor_256", "attention.cpp", "const float sc = amax / 448.0f;\n    scales[ch] = sc;",
+     "const float sc = amax / 256.0f;\n    scales[ch] = sc;",
+     pins.test_prefill_fp8_v_codes_are_per_channel_over_the_whole_context, (False,)),
+    ("prefill_fp8_scale_skips_last_token", "attention.cpp",
+     "for (int32_t t = 0; t < ctx; ++t) amax = std::max(amax, std::fabs(v[(int64_t)t * d + ch]));",
+     "for (int32_t t = 0; t < ctx - 1; ++t) amax = std::max(amax, std::fabs(v[(int64_t)t * d + ch]));",
+     pins.test_prefill_fp8_a_late_key_sets_the_channel_scale, ()),
+    ("prefill_fp8_p_scale_256", "attention.cpp", "e4m3_encode1(448.0 * p[j])", "e4m3_encode1(256.0 * p[j])",
+     pins.test_prefill_fp8_first_rows_of_a_fresh_chunk_closed_form, ()),
+    ("prefill_fp8_exact_p_in_numerator", "attention.cpp", "o[ch] += p8[j] * vj[ch];",
+     "o[ch] += 448.0 * p[j] * vj[ch];", pins.test_prefill_fp8_first_rows_of_a_fresh_chunk_closed_form, ()),
+    ("prefill_fp8_output_unscaled", "attention.cpp", "out[row * d + ch] = o[ch] / l8 * (double)svc[ch];",
+     "out[row * d + ch] = o[ch] / l8;", pins.test_prefill_fp8_first_rows_of_a_fresh_chunk_closed_form, ()),
+    ("prefill_fp8_gqa_interleaved_heads", "attention.cpp", "or_paged_v_fp8(c, s, n, h / G, codes.data(), svc.data());",
+     "or_paged_v_fp8(c, s, n, h % c->Hkv, codes.data(), svc.data());",
+     pins.test_prefill_fp8_zero_queries_give_the_mean_of_the_visible_rounded_values, ()),
+    ("prefill_fp8_sigma_one_rounding", "attention.cpp",
+     "const double ee = e56 * e56 + e448 * e448;\n            const double* vj = v8.data()",
+     "const double ee = e448 * e448;\n            const double* vj = v8.data()",
+     pins.test_prefill_fp8_tolerance_model_is_calibrated_by_random_references, ()),
     # ---- dense SageAttention-style path
     ("dense_key_block_size", "sage.cpp", "* nkb + j / g->k_block]", "* nkb + j / g->q_block]",
      pins.test_dense_equals_textbook_attention_of_dequantized, (False, None)),

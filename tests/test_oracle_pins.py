@@ -888,6 +888,135 @@ def test_v_fp8_per_channel_codes():
     assert np.all(np.abs(vals - r) <= step / 2 * (1 + 1e-9))
 
 
+# --------------------------------------------------------------------------
+# chunked prefill with the P.V product in FP8 (E4M3)
+# --------------------------------------------------------------------------
+
+def _prefill_fp8_setup(ctxs, qls, G=3, d=64, seed=43, v_int8=False, vfun=None):
+    spec = PagedSpec("pf8", seed, len(ctxs), 2 * G, 2, d, ctxs, qls, k_bias_std=2.0, v_int8=v_int8)
+    inp = paged_inputs(spec)
+    v = inp.v if vfun is None else to_bf16_bits(vfun(oq.widen(inp.v, "bf16")))
+    c = oracle.write_kv_cache(inp.k, v, "bf16", inp.slot_mapping, spec.num_blocks, v_int8)
+    q_i8, q_s = oracle.quantize_q(inp.q)
+    return spec, inp, c, q_i8, q_s, v
+
+
+def _token_v_values(inp, v_bits, s, v_int8):
+    """fp32 V of sequence s's tokens from the unpaged arrays ([ctx, Hkv, d]):
+    16-bit V exactly, INT8 V as fl32(code * scale) of its row quantization."""
+    a, b = int(inp.cu_seqlens_kv[s]), int(inp.cu_seqlens_kv[s + 1])
+    v = oq.widen(v_bits[a:b], "bf16")
+    if v_int8:
+        vq, vs = oracle.quant_rows(v)
+        v = (vq.astype(np.float32) * vs[..., None]).astype(np.float32)
+    return v
+
+
+@pytest.mark.parametrize("v_int8", [False, True])
+def test_prefill_fp8_v_codes_are_per_channel_over_the_whole_context(v_int8):
+    """The paged V codes and scales of a (sequence, KV head) equal the
+    per-channel E4M3 of that sequence's unpaged token values (every cached
+    token counts, not only those a row sees)."""
+    spec, inp, c, q_i8, q_s, v = _prefill_fp8_setup([70, 33], [20, 33], v_int8=v_int8)
+    for s_ in range(2):
+        vals = _token_v_values(inp, v, s_, v_int8)
+        want_v, want_s = oracle.v_fp8_per_channel(vals[None])
+        for h in range(2):
+            codes, sc = oracle.paged_v_fp8(c, inp.block_tables, s_, int(inp.context_lens[s_]), h, 2, 2,
+                                           spec.head_dim)
+            np.testing.assert_array_equal(sc, want_s[0, h])
+            np.testing.assert_array_equal(oracle.e4m3_decode(codes), want_v[0, :, h])
+
+
+def test_prefill_fp8_first_rows_of_a_fresh_chunk_closed_form():
+    """No history: row 0 sees key 0 only (out = V8[0] s); row 1 sees keys 0
+    and 1 with P8 = E4M3(448 exp(s - m)) at their exact maximum."""
+    spec, inp, c, q_i8, q_s, v = _prefill_fp8_setup([40], [40])
+    out = oracle.chunked_prefill_fp8pv(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    kq, ks = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    for h in range(6):
+        codes, sc = oracle.paged_v_fp8(c, inp.block_tables, 0, 40, h // 3, 1, 2, 64)
+        v8 = oracle.e4m3_decode(codes)
+        np.testing.assert_allclose(out[0, h], v8[0] * sc, rtol=1e-15, atol=0)
+        qd = q_i8[1, h].astype(np.float64) * float(q_s[1, h])
+        sco = np.array([kq[t, h // 3].astype(np.float64) @ qd * float(ks[t, h // 3]) / 8.0 for t in (0, 1)])
+        p = oracle.e4m3_round(448.0 * np.exp(sco - sco.max()))
+        want = (p[0] * v8[0] + p[1] * v8[1]) / p.sum() * sc
+        np.testing.assert_allclose(out[1, h], want, rtol=1e-12, atol=1e-15)
+
+
+def test_prefill_fp8_zero_queries_give_the_mean_of_the_visible_rounded_values():
+    """Zero queries: all scores 0, every P8 = 448, so row i of a chunk of Tq
+    on ctx tokens is the mean of V8 s over keys 0 .. ctx - Tq + i (pins the
+    bottom-right causal offset and the key count)."""
+    spec, inp, c, q_i8, q_s, v = _prefill_fp8_setup([90, 21], [30, 21])
+    q0 = np.zeros_like(q_i8)
+    out = oracle.chunked_prefill_fp8pv(q0, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    for s_, (ctx, tq) in enumerate([(90, 30), (21, 21)]):
+        qa = int(inp.cu_seqlens_q[s_])
+        for kvh in range(2):
+            codes, sc = oracle.paged_v_fp8(c, inp.block_tables, s_, ctx, kvh, 2, 2, 64)
+            cs = np.cumsum(oracle.e4m3_decode(codes), axis=0)
+            for i in range(tq):
+                nvis = ctx - tq + i + 1
+                for h in range(3 * kvh, 3 * kvh + 3):
+                    np.testing.assert_allclose(out[qa + i, h], cs[nvis - 1] / nvis * sc, rtol=1e-12, atol=1e-15)
+
+
+def test_prefill_fp8_a_late_key_sets_the_channel_scale():
+    """A large value on channel 5 at the last token (seen by the last row
+    only) sets that channel's scale for every row: row 0 of the chunk reads
+    its channel-5 value rounded on that coarse grid, away from the exact one."""
+    def vfun(x):
+        x = x.copy()
+        x[-1, :, 5] = np.float32(900.0)
+        return x
+    spec, inp, c, q_i8, q_s, v = _prefill_fp8_setup([48], [48], vfun=vfun)
+    out = oracle.chunked_prefill_fp8pv(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    vals = _token_v_values(inp, v, 0, False)
+    sc5 = np.float32(np.abs(vals[:, 0, 5]).max() / np.float32(448.0))
+    want = oracle.e4m3_round(np.float64(np.float32(vals[0, 0, 5] / sc5))) * np.float64(sc5)
+    assert out[0, 0, 5] == pytest.approx(want, rel=1e-15)
+    assert abs(out[0, 0, 5] - vals[0, 0, 5]) > 1e-3
+
+
+def test_prefill_fp8_is_within_fp8_error_of_the_16bit_path():
+    """Against the exact-P prefill: relative L2 of order the E4M3 step and
+    not identical (V offset by 0.5, so that outputs are not averages near 0)."""
+    spec, inp, c, q_i8, q_s, v = _prefill_fp8_setup([300, 130], [64, 130], d=128, vfun=lambda x: x + np.float32(0.5))
+    a = oracle.chunked_prefill_fp8pv(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    b = oracle.chunked_prefill(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2)
+    r = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert 1e-4 < r < 3e-2, r
+
+
+def test_prefill_fp8_tolerance_model_is_calibrated_by_random_references():
+    """As for the dense FP8 path: each key's P rounded at a random reference
+    m' in [m - 3 ln 2, m] (scaled back), against the plain definition, lands
+    within 6 sigma everywhere with an RMS z near 0.7."""
+    spec, inp, c, q_i8, q_s, v = _prefill_fp8_setup([260], [60], G=1, seed=47)
+    out, sig = oracle.chunked_prefill_fp8pv(q_i8, q_s, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables, 2,
+                                            return_sigma=True)
+    kq, ks = oracle.quant_rows(oq.widen(inp.k, "bf16"))
+    codes, sc = oracle.paged_v_fp8(c, inp.block_tables, 0, 260, 0, 1, 2, 64)
+    v8 = oracle.e4m3_decode(codes)
+    rng = np.random.default_rng(11)
+    zs = []
+    for i in range(60):
+        nvis = 200 + i + 1
+        qd = q_i8[i, 0].astype(np.float64) * float(q_s[i, 0])
+        sco = (kq[:nvis, 0].astype(np.float64) @ qd) * ks[:nvis, 0].astype(np.float64) / 8.0
+        m = sco.max()
+        mp = m - rng.uniform(0.0, 3.0 * np.log(2.0), size=nvis)
+        p = oracle.e4m3_round(56.0 * np.exp(sco - mp)) * np.exp(mp - m)
+        alt = (p @ v8[:nvis]) / p.sum() * sc
+        zs.append(np.abs(alt - out[i, 0]) / np.maximum(sig[i, 0], 1e-12))
+    zs = np.concatenate(zs)
+    assert np.max(zs) <= 6.0, np.max(zs)
+    rms = float(np.sqrt(np.mean(zs ** 2)))
+    assert 0.6 <= rms <= 0.82, rms
+
+
 def test_f32_to_f16_bits_matches_numpy_rounding():
     """fp32 -> fp16 (the V' operand of smooth_v) equals numpy's
     round-to-nearest-even cast, including subnormals, ties, the largest
