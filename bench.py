@@ -354,7 +354,9 @@ def run_decode_mt(torch, qa, context, T, pools, reps=50):
             "bytes": nbytes, "note": "one call: split kernel + combine (query already quantized)"}
 
 
-def run_prefill(torch, qa, reps):
+def run_prefill(torch, qa, reps, pv_fp8=False):
+    """The chunked prefill workload; with pv_fp8 the FP8 P.V call (its two
+    V passes included in the time)."""
     from workloads import chunked_prefill, paged_inputs
     spec = chunked_prefill()
     inp = paged_inputs(spec)
@@ -364,7 +366,13 @@ def run_prefill(torch, qa, reps):
     lens = torch.from_numpy(inp.context_lens).cuda()
     tables = torch.from_numpy(inp.block_tables).cuda()
     out = torch.empty((spec.total_q, spec.num_q_heads, spec.head_dim), device="cuda")
-    f = lambda: qa.chunked_prefill_attention(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0], out=out)
+    if pv_fp8:
+        ws = qa.chunked_prefill_fp8pv_workspace(qa.prefill_params(q8, lens, kc, vc, tables, spec.query_lens[0]))
+        f = lambda: qa.chunked_prefill_attention_fp8pv(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0],
+                                                       workspace=ws, out=out)
+    else:
+        f = lambda: qa.chunked_prefill_attention(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0],
+                                                 out=out)
     for _ in range(3):
         f()
     evs = _mk_stream_events(torch, reps)
@@ -374,10 +382,11 @@ def run_prefill(torch, qa, reps):
     ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     qk, pv = flash_ops(spec.query_lens, spec.context_lens, spec.num_q_heads, spec.head_dim)
     tops = (qk + pv) / (ms * 1e-3) / 1e12
-    mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / (FP16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3)
-    return {"workload": "chunked_prefill 2048 new tokens on 16384 history, 24/4 heads, d256",
+    mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / ((FP8_PEAK_TFLOPS if pv_fp8 else FP16_PEAK_TFLOPS) * 1e12)) / (ms * 1e-3)
+    return {"workload": "chunked_prefill 2048 new tokens on 16384 history, 24/4 heads, d256"
+                        + (", FP8 E4M3 P.V (V scale and E4M3 passes included)" if pv_fp8 else ""),
             "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
-            "_ops": (qk, pv, "f16")}
+            "_ops": (qk, pv, "fp8" if pv_fp8 else "f16")}
 
 
 def run_dense(torch, qa, reps, causal, options=False, pv_fp8=False):
@@ -697,7 +706,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill/dense lines")
-    ap.add_argument("--only", choices=["decode-batched", "decode-tiny", "producers", "prefill", "dense",
+    ap.add_argument("--only", choices=["decode-batched", "decode-tiny", "producers", "prefill", "prefill-fp8", "dense",
                                        "dense-causal", "dense-fp8", "mfma-sweep"],
                     help="run one workload alone and print its line (profiling runs)")
     ap.add_argument("--reps", type=int, default=20, help="launches timed by --only")
@@ -730,6 +739,7 @@ def main():
                "decode-tiny": lambda: run_decode_tiny(torch, qa, args.reps),
                "producers": lambda: run_producers(torch, qa, args.reps),
                "prefill": lambda: run_prefill(torch, qa, args.reps),
+               "prefill-fp8": lambda: run_prefill(torch, qa, args.reps, pv_fp8=True),
                "dense": lambda: run_dense(torch, qa, args.reps, False),
                "dense-causal": lambda: run_dense(torch, qa, args.reps, True),
                "dense-fp8": lambda: run_dense(torch, qa, args.reps, False, pv_fp8=True),
@@ -781,6 +791,7 @@ def main():
                             "frac_hbm_peak": r["step_bytes"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS},
                         "decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
                         "chunked_prefill": run_prefill(torch, qa, 20),
+                        "chunked_prefill_fp8pv": run_prefill(torch, qa, 20, pv_fp8=True),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True),
                         "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True),

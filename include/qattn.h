@@ -426,6 +426,40 @@ qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int
                                          const float* v_scale, const int32_t* block_tables,
                                          void* out, qa_stream_t stream);
 
+/*
+ * Chunked prefill with the P.V product in FP8 (E4M3) ([SAGE-MACA] lists the
+ * FP8 P.V product of later SageAttention versions among the features its
+ * hardware cannot run; the rows, masks and arguments are those of
+ * qa_chunked_prefill_attention, [QK-MMAC] §5.2). V of each (sequence, KV
+ * head) is scaled per channel over the sequence's context_lens[s] cached
+ * tokens, s_c = fl32(max|V| / 448) (INT8 V as fl32(code * scale)), and
+ * rounded to E4M3(fl32(V / s_c)); P is rounded to E4M3 at 448 * 2^-3 times
+ * exp(score - reference), the reference being moved only when a 128-key tile
+ * exceeds it by more than 3 (base 2); out = (sum P8 V8 / sum P8) * s_c. The
+ * error is of the order of the E4M3 step (about 2^-4 per rounded term), not
+ * of the 16-bit path.
+ *
+ *   workspace  >= qa_chunked_prefill_fp8pv_workspace_bytes(p) bytes of device
+ *              memory, 16-byte aligned; no initialization needed. After the
+ *              call it holds, from offset 0, the E4M3 codes as [num_seqs, T,
+ *              num_kv_heads, 4, head_dim, 32] bytes (T = ceil(16 *
+ *              max_blocks_per_seq / 128); key 32*j + 16*h + e of tile t sits
+ *              in group j, byte 16 * (h XOR bit 3 of the channel) + e; zero
+ *              past the context), then, at the next multiple of 256 bytes,
+ *              the channel scales [num_seqs, num_kv_heads, head_dim] fp32
+ *              (left unset for a sequence with no cached token). Calls that
+ *              share a workspace must not overlap.
+ * Errors as qa_chunked_prefill_attention; QA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t qa_chunked_prefill_fp8pv_workspace_bytes(const qa_prefill_params_t* p);
+qa_status_t qa_chunked_prefill_attention_fp8pv(const qa_prefill_params_t* p, const int8_t* q_i8,
+                                               const float* q_scale, const int32_t* cu_seqlens_q,
+                                               const int32_t* context_lens, const int8_t* k_cache,
+                                               const float* k_scale, const void* v_cache,
+                                               const float* v_scale, const int32_t* block_tables,
+                                               void* workspace, size_t workspace_bytes, void* out,
+                                               qa_stream_t stream);
+
 /* Shape and options of a dense SageAttention-style call (NHD layout). */
 typedef struct {
   int32_t batch;

@@ -109,6 +109,9 @@ _SIGS = {
                                      [_size, _c_void_p, _c_void_p]),
     "qa_debug_paged_qk_int32": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 6),
     "qa_chunked_prefill_attention": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 11),
+    "qa_chunked_prefill_fp8pv_workspace_bytes": (_size, [_P(PrefillParams)]),
+    "qa_chunked_prefill_attention_fp8pv": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 10 +
+                                           [_size, _c_void_p, _c_void_p]),
     "qa_dense_sage_quantize_workspace_size": (_size, [_P(DenseParams)]),
     "qa_dense_sage_quantize": (ctypes.c_int, [_P(DenseParams)] + [_c_void_p] * 8 + [_size, _c_void_p]),
     "qa_dense_sage_workspace_bytes": (_size, [_P(DenseParams)]),
@@ -376,21 +379,53 @@ def debug_paged_qk_int32(q_i8, k_cache, block_tables, context_lens, num_kv_heads
     return acc
 
 
+def prefill_params(q_i8, context_lens, k_cache, v_cache, block_tables, max_seqlen_q, num_kv_heads=None,
+                   softmax_scale=0.0, out_dtype=torch.float32) -> PrefillParams:
+    T, Hq, d = q_i8.shape
+    Hkv = num_kv_heads or k_cache.shape[1]
+    return PrefillParams(context_lens.shape[0], Hq, Hkv, d, 16, block_tables.shape[1], k_cache.shape[0], T,
+                         int(max_seqlen_q), QA_DT_I8 if v_cache.dtype == torch.int8 else QA_DT_BF16,
+                         _dt(out_dtype), softmax_scale)
+
+
 def chunked_prefill_attention(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
                               block_tables, max_seqlen_q, num_kv_heads=None, softmax_scale=0.0,
                               out_dtype=torch.float32, out=None):
     """Chunked prefill over the paged cache; returns out [total_q, Hq, d]."""
     _require_cuda(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale, block_tables)
-    T, Hq, d = q_i8.shape
-    Hkv = num_kv_heads or k_cache.shape[1]
-    p = PrefillParams(context_lens.shape[0], Hq, Hkv, d, 16, block_tables.shape[1], k_cache.shape[0], T,
-                      int(max_seqlen_q), QA_DT_I8 if v_cache.dtype == torch.int8 else QA_DT_BF16,
-                      _dt(out_dtype), softmax_scale)
+    p = prefill_params(q_i8, context_lens, k_cache, v_cache, block_tables, max_seqlen_q, num_kv_heads,
+                       softmax_scale, out_dtype)
     if out is None:
-        out = torch.empty((T, Hq, d), dtype=out_dtype, device=q_i8.device)
+        out = torch.empty(q_i8.shape, dtype=out_dtype, device=q_i8.device)
     _check(lib.qa_chunked_prefill_attention(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(cu_seqlens_q),
                                             _ptr(context_lens), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                                             _ptr(v_scale), _ptr(block_tables), _ptr(out), _stream()))
+    return out
+
+
+def chunked_prefill_fp8pv_workspace(p: PrefillParams):
+    """A device workspace for qa_chunked_prefill_attention_fp8pv."""
+    return torch.empty(lib.qa_chunked_prefill_fp8pv_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8,
+                       device="cuda")
+
+
+def chunked_prefill_attention_fp8pv(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
+                                    block_tables, max_seqlen_q, num_kv_heads=None, softmax_scale=0.0,
+                                    out_dtype=torch.float32, workspace=None, out=None):
+    """Chunked prefill with the P.V product in FP8 (E4M3); returns out
+    [total_q, Hq, d]. The workspace (allocated when None) holds the E4M3 V
+    tiles and channel scales afterwards (include/qattn.h)."""
+    _require_cuda(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale, block_tables)
+    p = prefill_params(q_i8, context_lens, k_cache, v_cache, block_tables, max_seqlen_q, num_kv_heads,
+                       softmax_scale, out_dtype)
+    if workspace is None:
+        workspace = chunked_prefill_fp8pv_workspace(p)
+    if out is None:
+        out = torch.empty(q_i8.shape, dtype=out_dtype, device=q_i8.device)
+    _check(lib.qa_chunked_prefill_attention_fp8pv(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(cu_seqlens_q),
+                                                  _ptr(context_lens), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                                                  _ptr(v_scale), _ptr(block_tables), _ptr(workspace),
+                                                  workspace.numel(), _ptr(out), _stream()))
     return out
 
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "flash.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "flash.hip", "prefill_fp8.hip"]
 PROBE_LIB = os.path.join(PKG, "libqaprobe.so")
 PROBE_SOURCES = ["probe.hip"]
 

@@ -675,11 +675,9 @@ qa_status_t qa_debug_paged_qk_int32(const qa_decode_params_t* p, const int8_t* q
   return hip_status(qa::launch_debug_qk(a, (hipStream_t)stream), "qa_debug_paged_qk_int32 launch");
 }
 
-qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int8_t* q_i8, const float* q_scale,
-                                         const int32_t* cu_seqlens_q, const int32_t* context_lens,
-                                         const int8_t* k_cache, const float* k_scale, const void* v_cache,
-                                         const float* v_scale, const int32_t* block_tables, void* out,
-                                         qa_stream_t stream) {
+namespace {
+
+qa_status_t check_prefill(const qa_prefill_params_t* p) {
   QA_REQUIRE(p != nullptr, QA_ERR_INVALID_ARG, "params is NULL");
   QA_REQUIRE(p->num_seqs >= 0 && p->num_q_heads > 0 && p->num_kv_heads > 0 && p->head_dim > 0 &&
                  p->total_q >= 0 && p->max_seqlen_q >= 0,
@@ -695,12 +693,56 @@ qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int
   QA_REQUIRE(supported_dim(p->head_dim), QA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,256}", p->head_dim);
   QA_REQUIRE(p->block_size == 16, QA_ERR_UNSUPPORTED, "block_size %d != 16", p->block_size);
   QA_REQUIRE(p->num_seqs <= 65535 && p->num_q_heads <= 65535, QA_ERR_UNSUPPORTED, "grid too large");
-  if (p->num_seqs == 0 || p->total_q == 0) return QA_OK;
+  return QA_OK;
+}
+
+qa_status_t check_prefill_ptrs(const qa_prefill_params_t* p, const int8_t* q_i8, const float* q_scale,
+                               const int32_t* cu_seqlens_q, const int32_t* context_lens, const int8_t* k_cache,
+                               const float* k_scale, const void* v_cache, const float* v_scale,
+                               const int32_t* block_tables, const void* out) {
   QA_REQUIRE(q_i8 && q_scale && cu_seqlens_q && context_lens && k_cache && k_scale && v_cache && block_tables && out,
              QA_ERR_INVALID_ARG, "null pointer");
   QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || v_scale != nullptr, QA_ERR_INVALID_ARG, "INT8 V needs v_scale");
   QA_REQUIRE(aligned16(q_i8) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), QA_ERR_INVALID_ARG,
              "q_i8, caches and out must be 16-byte aligned");
+  QA_REQUIRE(p->v_cache_dtype != QA_DT_I8 || aligned16(v_scale), QA_ERR_INVALID_ARG,
+             "v_scale must be 16-byte aligned");
+  return QA_OK;
+}
+
+// FP8 P.V prefill workspace: E4M3 tiles [num_seqs, T, Hkv, 128 * head_dim]
+// (T = ceil(16 * max_blocks_per_seq / 128)), channel scales [num_seqs, Hkv,
+// head_dim] fp32, partial maxima [num_seqs, Hkv, kV8Parts, head_dim] fp32;
+// each region starts on a 256-byte boundary.
+struct PrefillFp8Layout {
+  int32_t tiles;
+  size_t v8, sv, part, total;
+};
+
+PrefillFp8Layout prefill_fp8_layout(const qa_prefill_params_t* p) {
+  PrefillFp8Layout l{};
+  l.tiles = (int32_t)(((int64_t)p->max_blocks_per_seq * 16 + 127) / 128);
+  const size_t units = (size_t)p->num_seqs * (size_t)p->num_kv_heads;
+  l.v8 = 0;
+  l.sv = al(l.v8 + units * (size_t)l.tiles * 128 * (size_t)p->head_dim);
+  l.part = al(l.sv + units * (size_t)p->head_dim * 4);
+  l.total = al(l.part + units * (size_t)qa::kV8Parts * (size_t)p->head_dim * 4);
+  return l;
+}
+
+}  // namespace
+
+qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int8_t* q_i8, const float* q_scale,
+                                         const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                         const int8_t* k_cache, const float* k_scale, const void* v_cache,
+                                         const float* v_scale, const int32_t* block_tables, void* out,
+                                         qa_stream_t stream) {
+  qa_status_t st = check_prefill(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0 || p->total_q == 0) return QA_OK;
+  st = check_prefill_ptrs(p, q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
+                          block_tables, out);
+  if (st != QA_OK) return st;
   qa::FlashArgs a{};
   a.q = q_i8; a.q_scale = q_scale; a.k_blocks = k_cache; a.k_scale = k_scale; a.v_blocks = v_cache;
   a.v_scale = v_scale; a.tables = block_tables; a.cu_q = cu_seqlens_q; a.ctx_lens = context_lens; a.out = out;
@@ -710,6 +752,42 @@ qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int
   a.dense = false; a.causal = true; a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.v_f16 = false;
   a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = false;
   return hip_status(qa::launch_flash(a, (hipStream_t)stream), "qa_chunked_prefill_attention launch");
+}
+
+size_t qa_chunked_prefill_fp8pv_workspace_bytes(const qa_prefill_params_t* p) {
+  if (check_prefill(p) != QA_OK) return 0;
+  return prefill_fp8_layout(p).total;
+}
+
+qa_status_t qa_chunked_prefill_attention_fp8pv(const qa_prefill_params_t* p, const int8_t* q_i8,
+                                               const float* q_scale, const int32_t* cu_seqlens_q,
+                                               const int32_t* context_lens, const int8_t* k_cache,
+                                               const float* k_scale, const void* v_cache, const float* v_scale,
+                                               const int32_t* block_tables, void* workspace,
+                                               size_t workspace_bytes, void* out, qa_stream_t stream) {
+  qa_status_t st = check_prefill(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0 || p->total_q == 0) return QA_OK;
+  st = check_prefill_ptrs(p, q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
+                          block_tables, out);
+  if (st != QA_OK) return st;
+  const PrefillFp8Layout l = prefill_fp8_layout(p);
+  QA_REQUIRE(workspace != nullptr && aligned16(workspace), QA_ERR_INVALID_ARG,
+             "workspace must be a 16-byte aligned device pointer");
+  QA_REQUIRE(workspace_bytes >= l.total, QA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu",
+             workspace_bytes, l.total);
+  char* ws = static_cast<char*>(workspace);
+  qa::PrefillFp8Args a{};
+  a.q = q_i8; a.q_scale = q_scale; a.k_blocks = k_cache; a.k_scale = k_scale; a.v_cache = v_cache;
+  a.v_scale = v_scale; a.tables = block_tables; a.cu_q = cu_seqlens_q; a.ctx_lens = context_lens; a.out = out;
+  a.v8 = reinterpret_cast<uint8_t*>(ws + l.v8); a.v8_scale = reinterpret_cast<float*>(ws + l.sv);
+  a.partial = reinterpret_cast<float*>(ws + l.part);
+  a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
+  a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq; a.max_seqlen_q = p->max_seqlen_q;
+  a.v8_seq_tiles = l.tiles;
+  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
+  return hip_status(qa::launch_prefill_fp8(a, (hipStream_t)stream), "qa_chunked_prefill_attention_fp8pv launch");
 }
 
 size_t qa_dense_sage_quantize_workspace_size(const qa_dense_params_t* p) {

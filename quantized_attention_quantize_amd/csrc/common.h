@@ -174,4 +174,36 @@ __device__ __forceinline__ void rope_lane(const uint16_t* __restrict__ row, int 
   }
 }
 
+// LDS byte address of a __shared__ object (a constant: no generic-pointer
+// null check at run time).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One lane's 16 bytes global -> LDS (global_load_lds_dwordx4): the wave's
+// 64 lanes fill the 1 KB at the wave-uniform LDS address `lds`. Issued as
+// inline assembly, so the compiler does not treat the LDS destination as
+// aliasing the reads of the other buffer; the caller waits (vmcnt) before
+// the barrier. GFX9 parts need one wait state between an SALU write of M0
+// and an LDS-DMA instruction that reads it: the s_nop provides it.
+// The source is a wave-uniform base (scalar registers) plus each lane's own
+// 32-bit offset (`voff`, 16 * lane for a 1 KB chunk), so the address math
+// of a copy is scalar.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// Wait until every vector memory operation of the wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima, gfx9
+// encoding). The builtin, unlike inline assembly, is seen by the compiler's
+// wait insertion, which then knows that the loads issued before it (query
+// fragments, scales) are complete and places no waits for them in the tile
+// loop, where any vmcnt wait would also wait for the copies in flight.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace qa

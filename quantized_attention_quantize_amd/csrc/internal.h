@@ -190,4 +190,28 @@ struct FlashArgs {
 };
 hipError_t launch_flash(const FlashArgs& a, hipStream_t st);
 
+// Chunked prefill with the FP8 (E4M3) P.V product: two passes over V into the
+// workspace (partial maxima, then channel scales and E4M3 tiles of 128 keys in
+// the kernel's LDS layout), then the attention.
+constexpr int kV8Parts = 32;   // token slices of the partial-maximum pass
+struct PrefillFp8Args {
+  const int8_t* q;         // [total_q, Hq, D] codes
+  const float* q_scale;    // [total_q, Hq]
+  const int8_t* k_blocks;  // [blocks, Hkv, D/16, 16, 16]
+  const float* k_scale;    // [blocks, Hkv, 16]
+  const void* v_cache;     // [blocks, Hkv, D, 16] bf16 or int8
+  const float* v_scale;    // [blocks, Hkv, 16] (int8 V)
+  const int32_t* tables;   // [num_seqs, max_blocks]
+  const int32_t* cu_q;     // [num_seqs + 1]
+  const int32_t* ctx_lens; // [num_seqs]
+  void* out;               // [total_q, Hq, D] fp32 or bf16
+  uint8_t* v8;             // workspace: [num_seqs, v8_seq_tiles, Hkv, 4, D, 32] E4M3
+  float* v8_scale;         // workspace: [num_seqs, Hkv, D]
+  float* partial;          // workspace: [num_seqs, Hkv, kV8Parts, D]
+  int32_t num_seqs, Hq, Hkv, G, D, max_blocks, max_seqlen_q, v8_seq_tiles;
+  float scale_log2;
+  bool v_int8, out_bf16;
+};
+hipError_t launch_prefill_fp8(const PrefillFp8Args& a, hipStream_t st);
+
 }  // namespace qa

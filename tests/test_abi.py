@@ -176,6 +176,33 @@ def test_prefill_and_dense_validation(qa):
         qa.QA_ERR_UNSUPPORTED
 
 
+def test_prefill_fp8pv_validation_and_workspace(qa):
+    """The FP8 P.V prefill: the same shape and pointer checks as the 16-bit
+    entry, a workspace of E4M3 tiles (128 keys x head_dim bytes per tile, KV
+    head and sequence), channel scales and partial maxima, and a refusal of
+    a smaller workspace."""
+    L = qa.lib
+    p = qa.PrefillParams(2, 24, 4, 256, 16, 100, 1000, 10, 10, qa.QA_DT_BF16, qa.QA_DT_F32, 0.0)
+    need = L.qa_chunked_prefill_fp8pv_workspace_bytes(ctypes.byref(p))
+    tiles = -(-100 * 16 // 128)
+    v8 = 2 * tiles * 4 * 128 * 256
+    al = lambda x: -(-x // 256) * 256
+    assert need == al(al(al(v8) + 2 * 4 * 256 * 4) + 2 * 4 * 32 * 256 * 4)
+    call = lambda p, ws=FAKE, nb=need, q=FAKE: L.qa_chunked_prefill_attention_fp8pv(
+        ctypes.byref(p), q, *([FAKE] * 6), None, FAKE, ws, nb, FAKE, None)   # v_scale NULL
+    assert call(p, nb=need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert call(p, ws=None) == qa.QA_ERR_INVALID_ARG
+    assert call(p, q=None) == qa.QA_ERR_INVALID_ARG
+    p.head_dim = 80
+    assert L.qa_chunked_prefill_fp8pv_workspace_bytes(ctypes.byref(p)) == 0
+    assert call(p) == qa.QA_ERR_UNSUPPORTED
+    p.head_dim = 256
+    p.v_cache_dtype = qa.QA_DT_I8
+    assert call(p) == qa.QA_ERR_INVALID_ARG                # INT8 V needs v_scale
+    p.num_seqs = 0
+    assert L.qa_chunked_prefill_attention_fp8pv(ctypes.byref(p), *([None] * 10), 0, None, None) == qa.QA_OK
+
+
 def test_dense_options_validation(qa):
     L = qa.lib
     d = qa.DenseParams(2, 100, 90, 8, 4, 128, qa.QA_DT_BF16, 1, 0, 0.0, qa.QA_DT_F32)

@@ -370,6 +370,109 @@ def test_prefill_full_size_sampled(qa):
 
 
 # ---------------------------------------------------------------------------
+# chunked prefill with the P.V product in FP8 (E4M3): the tolerance model of
+# the dense FP8 path below (sigma of the difference to the plain definition),
+# and the E4M3 V codes and channel scales the call leaves in its workspace,
+# bit-exact against the oracle's
+# ---------------------------------------------------------------------------
+
+def _prefill_fp8_run(qa, inp, out_dtype=torch.float32):
+    spec = inp.spec
+    kc, ks, vc, vs = gpu_cache(qa, inp, spec.v_int8)
+    q8, qs = qa.quantize_q(dev_bits(inp.q, spec.dtype))
+    tables = torch.from_numpy(inp.block_tables).cuda()
+    ctx = torch.from_numpy(inp.context_lens).cuda()
+    p = qa.prefill_params(q8, ctx, kc, vc, tables, max(spec.query_lens), out_dtype=out_dtype)
+    ws = qa.chunked_prefill_fp8pv_workspace(p)
+    out = qa.chunked_prefill_attention_fp8pv(q8, qs, torch.from_numpy(inp.cu_seqlens_q).cuda(), ctx, kc, ks, vc, vs,
+                                             tables, max(spec.query_lens), out_dtype=out_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def _prefill_fp8_oracle(inp, rows=None):
+    spec = inp.spec
+    c = oracle_cache(inp, spec.v_int8)
+    w8, wsc = oracle.quantize_q(inp.q, spec.dtype)
+    return oracle.chunked_prefill_fp8pv(w8, wsc, inp.cu_seqlens_q, inp.context_lens, c, inp.block_tables,
+                                        spec.num_kv_heads, rows=rows, return_sigma=True)
+
+
+def _fp8_workspace_values(ws, spec, inp_blocks):
+    """E4M3 values [S, T*128, Hkv, d] and scales [S, Hkv, d] from the
+    workspace layout of qa_chunked_prefill_attention_fp8pv (inp_blocks: the
+    block-table width, max_blocks_per_seq)."""
+    S, Hkv, d = spec.num_seqs, spec.num_kv_heads, spec.head_dim
+    T = -(-inp_blocks * 16 // 128)
+    raw = ws.cpu().numpy()
+    nv8 = S * T * Hkv * 128 * d
+    v8 = raw[:nv8].reshape(S, T, Hkv, 4, d, 32)
+    key = np.arange(128)
+    ch = np.arange(d)
+    j, h, e = key // 32, (key % 32) // 16, key % 16
+    byte = 16 * (h[:, None] ^ ((ch[None, :] >> 3) & 1)) + e[:, None]        # [128, d]
+    codes = v8[:, :, :, j[:, None], ch[None, :], byte]                         # [S, T, Hkv, 128, d]
+    codes = codes.transpose(0, 1, 3, 2, 4).reshape(S, T * 128, Hkv, d)
+    off = -(-nv8 // 256) * 256
+    sc = raw[off:off + S * Hkv * d * 4].view(np.float32).reshape(S, Hkv, d)
+    return oracle.e4m3_decode(codes), sc
+
+
+PREFILL_FP8 = PREFILL + [
+    # several 128-key tiles with a ragged tail, history plus a chunk
+    (256, 6, 2, [1000], [300], False),
+    (256, 6, 1, [385, 129], [128, 129], True),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_FP8, ids=lambda c: f"d{c[0]}_G{c[1]}_Hkv{c[2]}_{'i8V' if c[5] else 'bf16V'}_{'-'.join(map(str, c[3]))}")
+def test_prefill_fp8pv_parity(qa, case):
+    d, G, Hkv, ctx, ql, v_int8 = case
+    say(f"prefill fp8 P.V {case}")
+    spec = PagedSpec("pf8", 231 + d + G, len(ctx), G * Hkv, Hkv, d, ctx, ql, k_bias_std=2.0, v_int8=v_int8,
+                     pool_blocks=sum(-(-c // 16) for c in ctx) + 4)
+    inp = paged_inputs(spec)
+    if spec.total_q == 0:
+        return
+    got, ws = _prefill_fp8_run(qa, inp)
+    want, sig = _prefill_fp8_oracle(inp)
+    _fp8_close(got.cpu().numpy(), want, sig, "prefill fp8 P.V vs oracle")
+    # the workspace: E4M3 V values and channel scales of every (sequence, KV head)
+    vals, sc = _fp8_workspace_values(ws, spec, inp.block_tables.shape[1])
+    c = oracle_cache(inp, v_int8)
+    for s_, n in enumerate(ctx):
+        for h in range(Hkv):
+            codes, wsc = oracle.paged_v_fp8(c, inp.block_tables, s_, n, h, len(ctx), Hkv, d)
+            if n > 0:
+                np.testing.assert_array_equal(sc[s_, h], wsc)
+            np.testing.assert_array_equal(vals[s_, :n, h], oracle.e4m3_decode(codes))
+            tail = -(-n // 128) * 128
+            assert np.all(vals[s_, n:tail, h] == 0)
+
+
+def test_prefill_fp8pv_bf16_output(qa):
+    spec = PagedSpec("pf8b", 241, 1, 12, 2, 128, [300], [100], k_bias_std=2.0)
+    inp = paged_inputs(spec)
+    got, _ = _prefill_fp8_run(qa, inp, out_dtype=torch.bfloat16)
+    want, sig = _prefill_fp8_oracle(inp)
+    g = got.float().cpu().numpy()
+    # bf16 output: the rounding (2^-9 relative) joins the E4M3 deviation
+    _fp8_close(g, want, np.sqrt(sig ** 2 + (np.abs(want) * 2.0 ** -9) ** 2), "prefill fp8 P.V bf16 out")
+
+
+def test_prefill_fp8pv_full_size_sampled(qa):
+    spec = chunked_prefill()
+    say(f"prefill fp8 P.V full size {spec.name}")
+    inp = paged_inputs(spec)
+    got, _ = _prefill_fp8_run(qa, inp)
+    rows = [0, 1, 127, 128, 1000, 1500, 2046, 2047]
+    want, sig = _prefill_fp8_oracle(inp, rows=rows)
+    _fp8_close(got.cpu().numpy()[rows], want[rows], sig[rows], f"{spec.name} fp8 P.V rows {rows}")
+    ref = _prefill_oracle(inp, rows=rows)
+    say(f"  fp8 P.V vs 16-bit P definition: rel_l2={rel_l2(got.cpu().numpy()[rows], ref[rows]):.3e}")
+
+
+# ---------------------------------------------------------------------------
 # dense SageAttention-style
 # ---------------------------------------------------------------------------
 
