@@ -35,7 +35,11 @@ FLAGS = [
 # The probes measure instruction rates: their accumulators live in ordinary
 # VGPRs (with AGPR accumulators the compiler rotates the 16x16 accumulators
 # through copies inside the loops, which then measure the copies).
-EXTRA = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # the softmax maxima: IEEE mode off lets v_max_f32 take its inputs as
+         # they are, instead of quieting possible signaling NaNs first (one
+         # extra instruction per score); the kernels never see a NaN score
+         "prefill_fp8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -192,9 +192,17 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
 // of a copy is scalar.
 __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  // the base is wave-uniform by contract; readfirstlane states it to the
+  // compiler (free when it already sits in scalar registers)
+  // (readfirstlane returns a signed int: each half is widened through
+  // uint32_t, so the low half is not sign-extended into the high one)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t sb = (hi << 32) | lo;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(m0), "v"(voff), "s"(sbase)
+               : "s"(m0), "v"(voff), "s"(sb)
                : "memory", "m0");
 }
 

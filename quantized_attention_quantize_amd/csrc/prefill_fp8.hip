@@ -199,9 +199,11 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
   const int total = (int)gridDim.x;
   int wid = blockIdx.x;
   if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int qtile = nqt - 1 - wid % nqt;
-  const int kvh = (wid / nqt) % a.Hkv;
-  const int z = wid / (nqt * a.Hkv);
+  // (uniform: readfirstlane keeps the divisions' results, and all that is
+  // derived from them, in scalar registers)
+  const int qtile = __builtin_amdgcn_readfirstlane(nqt - 1 - wid % nqt);
+  const int kvh = __builtin_amdgcn_readfirstlane((wid / nqt) % a.Hkv);
+  const int z = __builtin_amdgcn_readfirstlane(wid / (nqt * a.Hkv));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -226,7 +228,12 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = row_ok ? *reinterpret_cast<const v4i*>(qp + 64 * s) : v4i{0, 0, 0, 0};
   }
-  const float f = row_ok ? a.q_scale[(q_row0 + qi) * Hq + qh] * a.scale_log2 : 0.0f;
+  // score = x * f in base 2. f is kept >= the smallest normal float, so that
+  // a hidden key's x = -inf gives -inf, never NaN: only a query row with
+  // q_scale * scale below 1.2e-38 is affected, whose codes and hence x are 0
+  // when its scale is 0 (a zero row), and whose scores are 0 to fp32
+  // precision otherwise, unless K is of order 1e30
+  const float f = fmaxf(row_ok ? a.q_scale[(q_row0 + qi) * Hq + qh] * a.scale_log2 : 0.0f, 1.17549435e-38f);
   const int pos = qi + offset;                     // the row sees keys <= pos
   const int wq_first = (r0 + wave * 16) / G;       // first query token of this wave
 
@@ -343,20 +350,18 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
       for (int i = 0; i < 4; ++i) x[4 * q4 + i] = (float)acc[q4][i] * sk[i];
     }
     // masks only on tiles that cross the context end or the causal diagonal:
-    // key 32g + k of this lane is visible when k < vis_end
+    // key 32g + k of this lane is visible when k < vis_end; hidden keys get
+    // x = -inf, so that their P is exp2(-inf) = 0 (f > 0, see above)
     const bool need_mask = kbase + KT8 > kv_len || kbase + KT8 - 1 > wq_first + offset;
-    const int vis_end = min(kv_len, pos + 1) - kbase - 32 * g;
     if (need_mask) {
+      const int vis_end = min(kv_len, pos + 1) - kbase - 32 * g;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) x[k] = k < vis_end ? x[k] : -3.0e38f;
+      for (int k = 0; k < 32; ++k) x[k] = k < vis_end ? x[k] : kNegInf;
     }
     float mx = fmaxf(x[0], x[1]);
 #pragma unroll
     for (int k = 2; k < 32; k += 2) mx = fmaxf(mx, fmaxf(x[k], x[k + 1]));
-    // a lane whose keys are all hidden here keeps mx = -3e38 and adds no
-    // maximum (a visible key's x = acc * sK is far above that)
-    float mt = mx > -3.0e38f ? mx * f : kNegInf;
-    mt = group4_max(mt);
+    const float mt = group4_max(mx * f);          // -inf when every key of the row is hidden
     // lazy reference: moved only when exceeded by more than the slack
     if (__any(mt > m_run + kSlack8)) {
       const float m_new = fmaxf(m_run, mt);
@@ -372,16 +377,16 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
     for (int w = 0; w < 8; ++w) {
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(fmaf(x[4 * w + i], f, cterm));
-        if (need_mask) p[i] = 4 * w + i < vis_end ? p[i] : 0.0f;
-      }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(x[4 * w + i], f, cterm));
+      // the first conversion fills bytes 0-1 and keeps the rest of its third
+      // operand, which the second one overwrites: any live value serves
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[2]), false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
       bop[w] = word;
     }
 
     // ---- O^T += V8^T P8^T, row sums against ones -----------------------------
+    __builtin_amdgcn_sched_barrier(0);             // no V8 reads hoisted into the softmax
     // V8 fragments one channel block ahead, as the K fragments above
     const uint8_t* vt = s_v[buf] + g * (D * 32) + n * 32;
     const int sw = (n >> 3) & 1;                   // bit 3 of the channel 16c + n
@@ -399,6 +404,7 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
       __builtin_amdgcn_sched_barrier(0);
     }
     L = mfma_fp8_16x16x128(ones8, bop, L);
+    __builtin_amdgcn_sched_barrier(0);
 
     wait_vmem_all();                               // the next tile has landed
     if (tid < KT8) s_ks[buf ^ 1][tid] = ks_next;

@@ -148,3 +148,30 @@ def test_lds_dma_never_directly_follows_an_m0_write(disassembly):
             writes_m0 = re.match(r"\s*s_\w+\s+m0\b", prev[2]) is not None
             assert not writes_m0, f"{name} @{cur[0]:#x}: {cur[1]} right after '{prev[2].strip()}'"
     assert n_dma > 0, "no LDS-DMA loads found: the dense and 12-wave prefill kernels use them"
+
+
+def test_fp8_prefill_tile_loops_wait_once_for_memory(disassembly):
+    """As for the dense kernels: the FP8 P.V prefill copies the next K and V8
+    tiles global -> LDS during the current one, so its tile loop must hold a
+    single vector-memory wait and touch no scratch (a spill reload would wait
+    for the copies in flight)."""
+    ks = {n: ins for n, ins in disassembly[1].items() if "k_prefill8" in n}
+    assert len(ks) == 3, sorted(ks)
+    for n, ins in ks.items():
+        body = _main_loop(ins)
+        assert body, f"{n}: no loop found"
+        waits = [x[2].strip() for x in body if x[1] == "s_waitcnt" and "vmcnt" in x[2]]
+        assert len(waits) == 1, (n, waits)
+        assert not [x for x in body if x[1].startswith("scratch_")], f"{n} touches scratch in its tile loop"
+
+
+def test_lds_dma_bases_are_not_sign_extended(disassembly):
+    """The LDS-DMA copies take a 64-bit scalar base assembled from two 32-bit
+    halves; a sign-extended low half (s_bfe_i64 ..., 0x200000 before the OR)
+    turns every base whose bit 31 is set into an illegal address. No kernel
+    that issues LDS-DMA loads may sign-extend a 32-bit value to 64 bits."""
+    for name, ins in disassembly[1].items():
+        if not any(x[1].startswith("global_load_lds") for x in ins):
+            continue
+        bad = [x[2].strip() for x in ins if x[1] == "s_bfe_i64"]
+        assert not bad, (name, bad[:3])
