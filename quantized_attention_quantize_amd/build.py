@@ -39,7 +39,8 @@ EXTRA = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          # the softmax maxima: IEEE mode off lets v_max_f32 take its inputs as
          # they are, instead of quieting possible signaling NaNs first (one
          # extra instruction per score); the kernels never see a NaN score
-         "prefill_fp8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+         "prefill_fp8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+         "flash.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -178,6 +178,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     if (z < 0 || z >= a.num_seqs) return;
     qtile = j - (int)a.q_rows.block0(z, QT);
   }
+  // uniform values: readfirstlane keeps the divisions' results, and all the
+  // addresses derived from them, in scalar registers
+  qtile = __builtin_amdgcn_readfirstlane(qtile);
+  hu_ = __builtin_amdgcn_readfirstlane(hu_);
+  z = __builtin_amdgcn_readfirstlane(z);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
