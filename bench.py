@@ -486,7 +486,7 @@ def _step_call(torch, qa, spec, inp, pools_n, splits):
     return step, p, out
 
 
-def run_decode_batched(torch, qa, reps=30, pools=2):
+def run_decode_batched(torch, qa, reps=30, pools=2, splits=None):
     """Batched split-K decode: 32 sequences with contexts uniform on [1024,
     32768] (seeded), 24/4 heads, d 256, INT8 K and INT8 V with per-token
     scales, 8 splits per sequence. One step = qa_paged_decode_step (query
@@ -497,12 +497,15 @@ def run_decode_batched(torch, qa, reps=30, pools=2):
     from workloads import batched_splitk_decode, paged_inputs
     spec = batched_splitk_decode()
     inp = paged_inputs(spec)
-    step, p, _ = _step_call(torch, qa, spec, inp, pools, spec.num_splits)
+    S = splits if splits is not None else spec.num_splits
+    step, p, _ = _step_call(torch, qa, spec, inp, pools, S)
+    S_run = qa.lib.qa_paged_decode_num_splits(ctypes.byref(p))
     ms = _timed_ms(torch, step, reps)
     part = _timed_ms(torch, lambda i: step(i, qa.lib.qa_paged_decode_step_partials), reps)
     by = decode_bytes(spec)["step"]
+    how = f"{S_run} splits" + (" (library choice)" if S == 0 else "")
     return {"workload": f"batched split-K decode: 32 sequences, contexts U[1024, 32768] (sum {sum(spec.context_lens)}), "
-                        "24/4 heads, d256, INT8 K + INT8 V, 8 splits; step = fused quantize/write/split kernel + combine",
+                        f"24/4 heads, d256, INT8 K + INT8 V, {how}; step = fused quantize/write/split kernel + combine",
             "ms": ms, "GBps": by / (ms * 1e-3) / 1e9, "frac_hbm_peak": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bytes": by, "split_kernel_ms": part, "split_kernel_frac_hbm_peak": by / (part * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kv_pools": pools}
@@ -735,7 +738,7 @@ def main():
         return
 
     if args.only:
-        fns = {"decode-batched": lambda: run_decode_batched(torch, qa, args.reps),
+        fns = {"decode-batched": lambda: run_decode_batched(torch, qa, args.reps, splits=args.splits or None),
                "decode-tiny": lambda: run_decode_tiny(torch, qa, args.reps),
                "producers": lambda: run_producers(torch, qa, args.reps),
                "prefill": lambda: run_prefill(torch, qa, args.reps),
@@ -799,6 +802,7 @@ def main():
                         "dense_sage_causal_fp8pv": run_dense(torch, qa, 10, True, pv_fp8=True),
                         "dense_sage_varlen_mix": run_varlen(torch, qa, 10),
                         "decode_batched_splitk": run_decode_batched(torch, qa, 20),
+                        "decode_batched_library_splits": run_decode_batched(torch, qa, 20, splits=0),
                         "decode_tiny": run_decode_tiny(torch, qa, 100),
                         **run_producers(torch, qa, 30)}
         for e in res["extra"].values():

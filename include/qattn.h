@@ -218,7 +218,12 @@ size_t qa_paged_decode_workspace_size(const qa_decode_params_t* p);
  * the context length). Each
  * split stores (max, sum, unnormalized output) in the workspace and a second
  * kernel merges them. S = 1 writes the output directly. Results are
- * bit-identical from run to run.
+ * bit-identical from run to run. With 2 to 64 sequences the sequences are
+ * run longest first (an order of execution only: it changes no result).
+ * num_splits = 0 chooses S so that num_seqs * num_kv_heads * S reaches 256
+ * workgroups for one sequence and 512 for several (segments of unequal
+ * length balance better two to a compute unit), keeping at least 16 blocks
+ * per segment and at most 256 segments.
  *
  *   q_i8          [num_seqs, num_q_heads, head_dim] int8 (from qa_quantize_q)
  *   q_scale       [num_seqs, num_q_heads] fp32

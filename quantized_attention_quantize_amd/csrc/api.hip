@@ -489,6 +489,7 @@ qa_status_t decode_call(const qa_decode_params_t* p, const int8_t* q_i8, const f
   a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.out_bf16 = p->out_dtype == QA_DT_BF16;
   a.tq = T;
   a.seq_split = p->num_seqs > 1;
+  a.lpt = p->num_seqs > 1 && p->num_seqs <= 64;
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }
 
@@ -546,6 +547,7 @@ qa_status_t decode_step(const qa_decode_params_t* p, const void* q, int64_t q_st
   a.in_bf16 = dtype == QA_DT_BF16;
   a.tq = 1;
   a.seq_split = p->num_seqs > 1;
+  a.lpt = p->num_seqs > 1 && p->num_seqs <= 64;
   if (rope != nullptr) a.rope = qa::Rope{rope->positions, rope->cos_sin, rope->rot_dim, rope->neox != 0};
   return hip_status(qa::launch_decode(a, phase, (hipStream_t)stream), what);
 }

@@ -250,8 +250,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int CG = D / 16;   // 16-channel groups of the output
   extern __shared__ float smem[];
 
-  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const int split = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Sequences longest first (a.lpt, 2..64 sequences): slot blockIdx.z takes
+  // the sequence of that rank by context length, so that the longest
+  // segments start first and the short ones fill in at the end (workgroups
+  // are dispatched in index order). Every wave ranks its lane's sequence
+  // against all the others with lane reads (ties by index, so slots and
+  // sequences correspond one to one); no barrier, no extra launch.
+  int seq = blockIdx.z;
+  int ctx;
+  if (a.lpt) {
+    const int ns = a.num_seqs;
+    const int mine = lane < ns ? a.ctx_lens[lane] : 0;
+    int rank = 0;
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const int c = __builtin_amdgcn_readlane(mine, s2);
+      rank += (c > mine || (c == mine && s2 < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(lane < ns && rank == (int)blockIdx.z);
+    seq = __builtin_amdgcn_readfirstlane(hit != 0 ? (int)__builtin_ctzll(hit) : (int)blockIdx.z);
+    ctx = __builtin_amdgcn_readlane(mine, seq);
+  } else {
+    ctx = a.ctx_lens[seq];
+  }
   const int n = lane & 15, g = lane >> 4;
   const int G = a.G, Hq = a.Hq, Hkv = a.Hkv, S = a.num_splits;
 
@@ -262,7 +284,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
   // lengths), so the table fetch waits for the context length; otherwise
   // per = ceil(max_blocks/S) depends only on host-known sizes and the
   // block-table entries are fetched together with the context length.
-  const int ctx = a.ctx_lens[seq];
   const int per = a.seq_split ? max(((ctx + 15) / 16 + S - 1) / S, 1) : (a.max_blocks + S - 1) / S;
   const int blk0 = split * per;
   const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
@@ -708,10 +729,13 @@ hipError_t dispatch(const DecodeArgs& a, DecodePhase phase, hipStream_t st) {
 }  // namespace
 
 int32_t choose_decode_splits(int32_t num_seqs, int32_t Hkv, int32_t max_blocks) {
-  // Aim for one workgroup per compute unit (256 CUs), but keep at least
-  // 16 blocks (256 tokens) per segment.
+  // Aim for one workgroup per compute unit (256 CUs) for one sequence (its
+  // segments are equal) and two for several (segments of unequal length,
+  // run longest first, balance better two to a unit), but keep at least 16
+  // blocks (256 tokens) per segment.
   const int64_t units = (int64_t)num_seqs * Hkv;
-  int64_t s = (256 + units - 1) / units;
+  const int64_t target = num_seqs > 1 ? 512 : 256;
+  int64_t s = (target + units - 1) / units;
   const int64_t cap = max_blocks / 16 > 0 ? max_blocks / 16 : 1;
   if (s > cap) s = cap;
   if (s > 256) s = 256;

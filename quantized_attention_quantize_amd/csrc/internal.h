@@ -134,6 +134,7 @@ struct DecodeArgs {
   int32_t num_seqs, Hq, Hkv, G, D, max_blocks, num_splits;
   int32_t tq;             // query tokens per sequence (G*tq <= 16 columns); 1 for plain decode
   bool seq_split;         // split each sequence's own blocks into S segments (else max_blocks / S)
+  bool lpt;               // workgroup slot z runs the sequence ranked z by context length (2..64 sequences)
   float scale_log2;       // softmax_scale * log2(e)
   bool v_int8, out_bf16;
   // fused step (q_in != nullptr): the split kernel quantizes the query rows

@@ -149,10 +149,11 @@ def test_decode_phase_validation(qa):
 def test_decode_split_heuristic(qa):
     f = lambda S, Hkv, mb: qa.lib.qa_paged_decode_num_splits(ctypes.byref(qa.decode_params(S, 6 * Hkv, Hkv, 256, mb, 10)))
     assert f(1, 4, 2048) == 64           # one long sequence: one workgroup per CU
-    assert f(32, 4, 2048) == 2
+    assert f(32, 4, 2048) == 4           # several sequences: two workgroups per CU
     assert f(1, 1, 64) == 4              # short context: at least 16 blocks per split
     assert f(1, 1, 4) == 1
     assert f(200, 4, 2048) == 1
+    assert f(64, 4, 2048) == 2
 
 
 def test_prefill_and_dense_validation(qa):
