@@ -549,72 +549,64 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
 
 // Merge the S partials of each (query head, sequence):
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
-// A workgroup of 256 threads covers 16 float4 columns of one head; thread t
-// owns column t % 16 of share t / 16 of the splits and loads its (m, l, O)
-// values in batches of 16 independent loads with a running maximum; the
-// shares are merged through LDS.
+// Many splits: one wave per (query row, head, 4 channels). Lane s reads
+// split s (and s + 64, ... when S > 64); the wave reduces the maximum, then
+// the weighted sums, with butterfly exchanges (a fixed order, so results do
+// not vary from run to run): one round of loads, no LDS, no barrier.
 template <int D>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
-                                                 const float* __restrict__ ws_ml, int32_t Hq, int32_t S,
-                                                 bool out_bf16, void* out) {
-  constexpr int CW = 16;                 // float4 columns per workgroup
-  constexpr int SH = 256 / CW;           // split shares
-  __shared__ float4 part[SH][CW];
-  __shared__ float2 mlpart[SH];
-  const int h = blockIdx.x, seq = blockIdx.y, t = threadIdx.x;
-  const int cw = t % CW, sh = t / CW;
-  const int c4 = blockIdx.z * CW + cw;
-  const int64_t base = ((int64_t)seq * Hq + h) * S;
-  float m = kNegInf, lsum = 0.0f;
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+                                                 int32_t Hq, int32_t S, int32_t rows, bool out_bf16, void* out) {
+  constexpr int C4 = D / 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (row * Hq + head) * C4 + c4
+  if (wv >= (int64_t)rows * Hq * C4) return;                        // the whole wave
+  const int c4 = (int)(wv % C4);
+  const int64_t rh = wv / C4;
+  const int64_t base = rh * S;
+  // the first split of this lane stays in registers between the two passes
+  const bool has = lane < S;
+  const float2 ml0 = has ? *reinterpret_cast<const float2*>(ws_ml + (base + lane) * 2) : make_float2(kNegInf, 0.f);
+  const float4 o0 = has ? *reinterpret_cast<const float4*>(ws_o + (base + lane) * D + 4 * c4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  float m = ml0.x;
+  for (int s = lane + 64; s < S; s += 64) m = fmaxf(m, ws_ml[(base + s) * 2]);
+  const float M = wave_max(m);
+  float l = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = sh; s0 < S; s0 += 16 * SH) {
-    float2 ml[16];
-    float4 o[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s = min(s0 + i * SH, S - 1);
-      ml[i] = *reinterpret_cast<const float2*>(ws_ml + (base + s) * 2);
-      o[i] = *reinterpret_cast<const float4*>(ws_o + (base + s) * D + 4 * c4);
+  if (M != kNegInf) {
+    if (ml0.x != kNegInf) {
+      const float w = fast_exp2(ml0.x - M);
+      l = w * ml0.y;
+      acc = make_float4(w * o0.x, w * o0.y, w * o0.z, w * o0.w);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (s0 + i * SH >= S || ml[i].x == kNegInf) continue;
-      const float mn = fmaxf(m, ml[i].x);
-      const float a0 = fast_exp2(m - mn), a1 = fast_exp2(ml[i].x - mn);
-      acc.x = acc.x * a0 + a1 * o[i].x; acc.y = acc.y * a0 + a1 * o[i].y;
-      acc.z = acc.z * a0 + a1 * o[i].z; acc.w = acc.w * a0 + a1 * o[i].w;
-      lsum = lsum * a0 + a1 * ml[i].y;
-      m = mn;
+    for (int s = lane + 64; s < S; s += 64) {
+      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + s) * 2);
+      if (ml.x == kNegInf) continue;
+      const float4 o = *reinterpret_cast<const float4*>(ws_o + (base + s) * D + 4 * c4);
+      const float w = fast_exp2(ml.x - M);
+      l += w * ml.y;
+      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
     }
   }
-  part[sh][cw] = acc;
-  if (cw == 0) mlpart[sh] = make_float2(m, lsum);
-  __syncthreads();
-  if (sh == 0) {
-    float M = kNegInf;
 #pragma unroll
-    for (int k = 0; k < SH; ++k) M = fmaxf(M, mlpart[k].x);
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    float l = 0.0f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int k = 0; k < SH; ++k) {
-        const float wt = fast_exp2(mlpart[k].x - M);
-        const float4 q = part[k][cw];
-        r.x += wt * q.x; r.y += wt * q.y; r.z += wt * q.z; r.w += wt * q.w;
-        l += wt * mlpart[k].y;
-      }
-    }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const int64_t oi = ((int64_t)seq * Hq + h) * D + 4 * c4;
-    if (out_bf16) {
-      uint2 w;
-      w.x = f32_to_bf16_bits(r.x * inv) | (f32_to_bf16_bits(r.y * inv) << 16);
-      w.y = f32_to_bf16_bits(r.z * inv) | (f32_to_bf16_bits(r.w * inv) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) = w;
-    } else {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
-    }
+  for (int k = 32; k > 0; k >>= 1) {
+    l += __shfl_xor(l, k, 64);
+    acc.x += __shfl_xor(acc.x, k, 64);
+    acc.y += __shfl_xor(acc.y, k, 64);
+    acc.z += __shfl_xor(acc.z, k, 64);
+    acc.w += __shfl_xor(acc.w, k, 64);
+  }
+  if (lane != 0) return;
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const int64_t oi = rh * D + 4 * c4;
+  if (out_bf16) {
+    uint2 w;
+    w.x = f32_to_bf16_bits(acc.x * inv) | (f32_to_bf16_bits(acc.y * inv) << 16);
+    w.y = f32_to_bf16_bits(acc.z * inv) | (f32_to_bf16_bits(acc.w * inv) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + oi) = w;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oi) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
@@ -676,7 +668,9 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
     k_combine_few<D><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits,
                                                                              rows, a.out_bf16, a.out);
   } else {
-    k_combine<D><<<dim3(a.Hq, rows, D / 64), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits, a.out_bf16, a.out);
+    const int64_t waves = (int64_t)rows * a.Hq * (D / 4);
+    k_combine<D><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, st>>>(a.ws_o, a.ws_ml, a.Hq, a.num_splits, rows,
+                                                                    a.out_bf16, a.out);
   }
   return hipGetLastError();
 }
