@@ -354,9 +354,10 @@ def run_decode_mt(torch, qa, context, T, pools, reps=50):
             "bytes": nbytes, "note": "one call: split kernel + combine (query already quantized)"}
 
 
-def run_prefill(torch, qa, reps, pv_fp8=False):
+def run_prefill(torch, qa, reps, pv_fp8=False, v_ws=False):
     """The chunked prefill workload; with pv_fp8 the FP8 P.V call (its two
-    V passes included in the time)."""
+    V passes included in the time); with v_ws the call that converts V once
+    into a workspace (that pass included)."""
     from workloads import chunked_prefill, paged_inputs
     spec = chunked_prefill()
     inp = paged_inputs(spec)
@@ -370,6 +371,10 @@ def run_prefill(torch, qa, reps, pv_fp8=False):
         ws = qa.chunked_prefill_fp8pv_workspace(qa.prefill_params(q8, lens, kc, vc, tables, spec.query_lens[0]))
         f = lambda: qa.chunked_prefill_attention_fp8pv(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0],
                                                        workspace=ws, out=out)
+    elif v_ws:
+        ws = qa.chunked_prefill_ws_workspace(qa.prefill_params(q8, lens, kc, vc, tables, spec.query_lens[0]))
+        f = lambda: qa.chunked_prefill_attention_ws(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0],
+                                                    workspace=ws, out=out)
     else:
         f = lambda: qa.chunked_prefill_attention(q8, qs, cu, lens, kc, ks, vc, vs, tables, spec.query_lens[0],
                                                  out=out)
@@ -384,7 +389,8 @@ def run_prefill(torch, qa, reps, pv_fp8=False):
     tops = (qk + pv) / (ms * 1e-3) / 1e12
     mixed = (qk / (INT8_PEAK_TOPS * 1e12) + pv / ((FP8_PEAK_TFLOPS if pv_fp8 else FP16_PEAK_TFLOPS) * 1e12)) / (ms * 1e-3)
     return {"workload": "chunked_prefill 2048 new tokens on 16384 history, 24/4 heads, d256"
-                        + (", FP8 E4M3 P.V (V scale and E4M3 passes included)" if pv_fp8 else ""),
+                        + (", FP8 E4M3 P.V (V scale and E4M3 passes included)" if pv_fp8 else "")
+                        + (", V converted once into a workspace (that pass included)" if v_ws else ""),
             "ms": ms, "TOPS": tops, "frac_int8_peak": tops / INT8_PEAK_TOPS, "frac_mixed_roofline": mixed,
             "_ops": (qk, pv, "fp8" if pv_fp8 else "f16")}
 
@@ -709,7 +715,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the prefill/dense lines")
-    ap.add_argument("--only", choices=["decode-batched", "decode-tiny", "producers", "prefill", "prefill-fp8", "dense",
+    ap.add_argument("--only", choices=["decode-batched", "decode-tiny", "producers", "prefill", "prefill-fp8", "prefill-ws", "dense",
                                        "dense-causal", "dense-fp8", "mfma-sweep"],
                     help="run one workload alone and print its line (profiling runs)")
     ap.add_argument("--reps", type=int, default=20, help="launches timed by --only")
@@ -743,6 +749,7 @@ def main():
                "producers": lambda: run_producers(torch, qa, args.reps),
                "prefill": lambda: run_prefill(torch, qa, args.reps),
                "prefill-fp8": lambda: run_prefill(torch, qa, args.reps, pv_fp8=True),
+               "prefill-ws": lambda: run_prefill(torch, qa, args.reps, v_ws=True),
                "dense": lambda: run_dense(torch, qa, args.reps, False),
                "dense-causal": lambda: run_dense(torch, qa, args.reps, True),
                "dense-fp8": lambda: run_dense(torch, qa, args.reps, False, pv_fp8=True),
@@ -795,6 +802,7 @@ def main():
                         "decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
                         "chunked_prefill": run_prefill(torch, qa, 20),
                         "chunked_prefill_fp8pv": run_prefill(torch, qa, 20, pv_fp8=True),
+                        "chunked_prefill_v_workspace": run_prefill(torch, qa, 20, v_ws=True),
                         "dense_sage_noncausal": run_dense(torch, qa, 10, False),
                         "dense_sage_causal": run_dense(torch, qa, 10, True),
                         "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True),

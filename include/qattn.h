@@ -432,6 +432,34 @@ qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int
                                          void* out, qa_stream_t stream);
 
 /*
+ * qa_chunked_prefill_attention with V converted once per call: every V block
+ * of each sequence's context is rounded to fp16 (INT8 codes exactly) into the
+ * workspace, in the order the attention kernel's LDS holds it, and the
+ * attention kernel copies those blocks straight into LDS instead of each
+ * workgroup converting them again. Same rows, masks and arguments as
+ * qa_chunked_prefill_attention ([QK-MMAC] §5.2), and the same arithmetic: the
+ * output equals that call's bit for bit.
+ *
+ *   workspace  >= qa_chunked_prefill_ws_workspace_bytes(p) =
+ *              num_seqs * max_blocks_per_seq * num_kv_heads * head_dim * 32
+ *              bytes of device memory, 16-byte aligned; no initialization
+ *              needed. After the call it holds V as fp16 [num_seqs,
+ *              max_blocks_per_seq, num_kv_heads, head_dim, 16] (logical block
+ *              j of sequence s; tokens past context_lens[s] zero; blocks
+ *              wholly past it left unset). Calls that share a workspace must
+ *              not overlap.
+ * Errors as qa_chunked_prefill_attention; QA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t qa_chunked_prefill_ws_workspace_bytes(const qa_prefill_params_t* p);
+qa_status_t qa_chunked_prefill_attention_ws(const qa_prefill_params_t* p, const int8_t* q_i8,
+                                            const float* q_scale, const int32_t* cu_seqlens_q,
+                                            const int32_t* context_lens, const int8_t* k_cache,
+                                            const float* k_scale, const void* v_cache,
+                                            const float* v_scale, const int32_t* block_tables,
+                                            void* workspace, size_t workspace_bytes, void* out,
+                                            qa_stream_t stream);
+
+/*
  * Chunked prefill with the P.V product in FP8 (E4M3) ([SAGE-MACA] lists the
  * FP8 P.V product of later SageAttention versions among the features its
  * hardware cannot run; the rows, masks and arguments are those of

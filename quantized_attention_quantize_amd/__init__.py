@@ -109,6 +109,9 @@ _SIGS = {
                                      [_size, _c_void_p, _c_void_p]),
     "qa_debug_paged_qk_int32": (ctypes.c_int, [_P(DecodeParams)] + [_c_void_p] * 6),
     "qa_chunked_prefill_attention": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 11),
+    "qa_chunked_prefill_ws_workspace_bytes": (_size, [_P(PrefillParams)]),
+    "qa_chunked_prefill_attention_ws": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 10 +
+                                        [_size, _c_void_p, _c_void_p]),
     "qa_chunked_prefill_fp8pv_workspace_bytes": (_size, [_P(PrefillParams)]),
     "qa_chunked_prefill_attention_fp8pv": (ctypes.c_int, [_P(PrefillParams)] + [_c_void_p] * 10 +
                                            [_size, _c_void_p, _c_void_p]),
@@ -400,6 +403,31 @@ def chunked_prefill_attention(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache
     _check(lib.qa_chunked_prefill_attention(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(cu_seqlens_q),
                                             _ptr(context_lens), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                                             _ptr(v_scale), _ptr(block_tables), _ptr(out), _stream()))
+    return out
+
+
+def chunked_prefill_ws_workspace(p: PrefillParams):
+    """A device workspace for qa_chunked_prefill_attention_ws."""
+    return torch.empty(lib.qa_chunked_prefill_ws_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8,
+                       device="cuda")
+
+
+def chunked_prefill_attention_ws(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
+                                 block_tables, max_seqlen_q, num_kv_heads=None, softmax_scale=0.0,
+                                 out_dtype=torch.float32, workspace=None, out=None):
+    """chunked_prefill_attention with V converted once into a workspace
+    (allocated when None); the output is the same bit for bit."""
+    _require_cuda(q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale, block_tables)
+    p = prefill_params(q_i8, context_lens, k_cache, v_cache, block_tables, max_seqlen_q, num_kv_heads,
+                       softmax_scale, out_dtype)
+    if workspace is None:
+        workspace = chunked_prefill_ws_workspace(p)
+    if out is None:
+        out = torch.empty(q_i8.shape, dtype=out_dtype, device=q_i8.device)
+    _check(lib.qa_chunked_prefill_attention_ws(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(cu_seqlens_q),
+                                               _ptr(context_lens), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                                               _ptr(v_scale), _ptr(block_tables), _ptr(workspace),
+                                               workspace.numel(), _ptr(out), _stream()))
     return out
 
 

@@ -756,6 +756,39 @@ qa_status_t qa_chunked_prefill_attention(const qa_prefill_params_t* p, const int
   return hip_status(qa::launch_flash(a, (hipStream_t)stream), "qa_chunked_prefill_attention launch");
 }
 
+size_t qa_chunked_prefill_ws_workspace_bytes(const qa_prefill_params_t* p) {
+  if (check_prefill(p) != QA_OK) return 0;
+  return (size_t)p->num_seqs * (size_t)p->max_blocks_per_seq * (size_t)p->num_kv_heads * (size_t)p->head_dim * 32;
+}
+
+qa_status_t qa_chunked_prefill_attention_ws(const qa_prefill_params_t* p, const int8_t* q_i8, const float* q_scale,
+                                            const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                            const int8_t* k_cache, const float* k_scale, const void* v_cache,
+                                            const float* v_scale, const int32_t* block_tables, void* workspace,
+                                            size_t workspace_bytes, void* out, qa_stream_t stream) {
+  qa_status_t st = check_prefill(p);
+  if (st != QA_OK) return st;
+  if (p->num_seqs == 0 || p->total_q == 0) return QA_OK;
+  st = check_prefill_ptrs(p, q_i8, q_scale, cu_seqlens_q, context_lens, k_cache, k_scale, v_cache, v_scale,
+                          block_tables, out);
+  if (st != QA_OK) return st;
+  const size_t need = qa_chunked_prefill_ws_workspace_bytes(p);
+  QA_REQUIRE(workspace != nullptr && aligned16(workspace), QA_ERR_INVALID_ARG,
+             "workspace must be a 16-byte aligned device pointer");
+  QA_REQUIRE(workspace_bytes >= need, QA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu",
+             workspace_bytes, need);
+  qa::FlashArgs a{};
+  a.q = q_i8; a.q_scale = q_scale; a.k_blocks = k_cache; a.k_scale = k_scale; a.v_blocks = v_cache;
+  a.v_scale = v_scale; a.tables = block_tables; a.cu_q = cu_seqlens_q; a.ctx_lens = context_lens; a.out = out;
+  a.num_seqs = p->num_seqs; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = p->num_q_heads / p->num_kv_heads;
+  a.D = p->head_dim; a.max_blocks = p->max_blocks_per_seq; a.max_seqlen_q = p->max_seqlen_q;
+  a.scale_log2 = log2_scale(p->softmax_scale, p->head_dim);
+  a.dense = false; a.causal = true; a.v_int8 = p->v_cache_dtype == QA_DT_I8; a.v_f16 = false;
+  a.out_bf16 = p->out_dtype == QA_DT_BF16; a.out_f16 = false;
+  a.v_ws = workspace;
+  return hip_status(qa::launch_flash(a, (hipStream_t)stream), "qa_chunked_prefill_attention_ws launch");
+}
+
 size_t qa_chunked_prefill_fp8pv_workspace_bytes(const qa_prefill_params_t* p) {
   if (check_prefill(p) != QA_OK) return 0;
   return prefill_fp8_layout(p).total;

@@ -98,15 +98,16 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(v8i_t a, v8i_t b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int D, int VK, int NT, bool KDMA>
+template <int D, int VK, int NT, bool KDMA, bool VWS>
 struct Staged {
   static constexpr int VB = VK == kVI8 ? 1 : 2;    // bytes per cached V element
   static constexpr int KUB = D;                    // 16-byte K units per block
   static constexpr int VUB = D * VB;               // 16-byte V units per block
   static constexpr int KU = (4 * KUB + NT - 1) / NT;   // K units per thread (the last one
   static constexpr int VU = (4 * VUB + NT - 1) / NT;   // may cover only some waves)
+  static constexpr int VUS = VWS ? 0 : VU;         // V units staged (none when V is copied from the workspace)
   v4i k[KDMA ? 1 : KU];   // (unused when K goes straight to LDS) plain vector types: a uint4 struct copy under the
-  v4i v[VU];     // partial-round guards left an array in memory
+  v4i v[VWS ? 1 : VU];    // partial-round guards left an array in memory
   float ks, vs;
 };
 
@@ -118,7 +119,10 @@ struct Staged {
 // workgroups.
 // PV8 (dense, two query groups per wave): P and V in FP8 (E4M3) for the
 // second product, a 32x32x64 matrix instruction per 32 channels and tile.
-template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL, bool PV8 = false>
+// VWS (paged): V tiles come as fp16 blocks from the per-call workspace that
+// k_v16_blocks fills (the LDS layout already), copied straight into LDS
+// instead of staged and converted by every workgroup.
+template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL, bool PV8 = false, bool VWS = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 4))) void k_flash(
     FlashArgs a) {
@@ -126,7 +130,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   // At 12 waves the register file has no room to stage K as well: paged K
   // tiles (INT8, already in the LDS layout) are copied straight into LDS.
   constexpr bool KDMA = !DENSE && NW == 12;
-  using St = Staged<D, VK, NT, KDMA>;
+  constexpr bool VWS_ = VWS && !DENSE;
+  using St = Staged<D, VK, NT, KDMA, VWS_>;
   static_assert(!PV8 || (DENSE && QG == 2 && D <= 128), "FP8 P.V: dense, 32 queries per wave");
   constexpr int KS = D / 64;
   constexpr int CG = D / 16;
@@ -274,6 +279,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same value, held in a scalar
   const uint32_t lane16 = (uint32_t)lane * 16u;                // each lane's 16 bytes of a 1 KB copy
   const uint32_t sk_lds = lds_addr(&s_k[0][0]), sv_lds = lds_addr(&s_v[0][0]);
+  // VWS: this (sequence, KV head)'s fp16 V blocks in the workspace
+  // [seq][logical block][Hkv][D][16]
+  const uint8_t* vws_seq = VWS_ ? reinterpret_cast<const uint8_t*>(a.v_ws) + ((int64_t)z * a.max_blocks * Hkv + kvh) * D * 32
+                                : nullptr;
+  const uint32_t vblk32 = (uint32_t)(Hkv * D * 32);   // bytes per logical block (< 2^32)
   // Physical blocks of a paged tile: lanes 0..3 read the four block-table
   // entries with one vector load, issued one tile ahead of the fetch that
   // uses them (a vector load, so that waiting for LDS reads - lgkmcnt - never
@@ -316,8 +326,21 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       const int8_t* base = a.k_blocks + (uint64_t)(uint32_t)phys(b) * kblk32 + k_head;
       st.k[i] = *reinterpret_cast<const v4i*>(base + (uint32_t)((tid + i * NT) % KUB) * 16u);
     }
+    if constexpr (VWS_) {
+      // fp16 V blocks of this sequence from the workspace: block b of the
+      // tile is logical block tile*4 + b, clamped like the block-table reads
+      constexpr int VC = D / 32;                   // 1 KB chunks per V block (per head)
 #pragma unroll
-    for (int i = 0; i < VU; ++i) {
+      for (int i = 0; i < (4 * VC + NW - 1) / NW; ++i) {
+        const int c = wave_s + NW * i, b = c / VC, part = c % VC;
+        if (4 * VC % NW != 0 && c >= 4 * VC) break;   // wave-uniform
+        const int lb = max(min(tile * 4 + b, blk_hi), 0);
+        copy16_to_lds(vws_seq + (uint64_t)(uint32_t)lb * vblk32 + part * 1024, lane16,
+                      sv_lds + (uint32_t)(kbuf * KT * D * 2 + b * D * 32 + part * 1024));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < St::VUS; ++i) {
       if ((4 * VUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * VUB) break;   // wave-uniform
       const int b = (i * NT + 64 * wave_s) / VUB;
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.v_blocks) + ((uint64_t)(uint32_t)phys(b) * kblk32 + k_head) * VB;
@@ -343,7 +366,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     }
     // V rows of keys past the context are cleared (the cache may hold anything there)
 #pragma unroll
-    for (int i = 0; i < VU; ++i) {
+    for (int i = 0; i < St::VUS; ++i) {
       if ((4 * VUB) % NT != 0 && i * NT + 64 * wave_s >= 4 * VUB) break;   // wave-uniform
       const int u = tid + i * NT;
       const int b = (i * NT + 64 * wave_s) / VUB, r = u % VUB;
@@ -452,7 +475,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   }
   // on every path (the tile loop is reached from both), so that no load
   // issued so far is waited for inside the loop
-  if constexpr (kDma || KDMA) wait_vmem_all();
+  if constexpr (kDma || KDMA || VWS_) wait_vmem_all();
   __syncthreads();
 
   const int nkb = DENSE ? (kv_len + KT - 1) / KT : 1;
@@ -699,7 +722,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(0);
     if constexpr (kDma) wait_vmem_all();   // the next tile has landed
     else commit(nxt, buf ^ 1, tile + 1);
-    if constexpr (KDMA) wait_vmem_all();   // K of the next tile has landed
+    if constexpr (KDMA || VWS_) wait_vmem_all();   // K (and V) of the next tile have landed
     __syncthreads();
   }
 
@@ -807,7 +830,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   }
 }
 
-template <int D, int VK, bool DENSE, bool CAUSAL, bool PV8 = false>
+template <int D, int VK, bool DENSE, bool CAUSAL, bool PV8 = false, bool VWS = false>
 hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
   // d = 256: waves of 16 rows (one workgroup per CU: its double-buffered
   // tiles take 99 KB of LDS), 8 waves for dense, 12 for the paged prefill,
@@ -830,9 +853,40 @@ hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
     if constexpr (QG == 2 && D <= 128) k_flash<D, QG, NW, VK, DENSE, CAUSAL, true><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
     else return hipErrorInvalidValue;    // FP8 P.V needs two query groups per wave
   } else {
-    k_flash<D, QG, NW, VK, DENSE, CAUSAL><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
+    k_flash<D, QG, NW, VK, DENSE, CAUSAL, false, VWS><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
   }
   return hipGetLastError();
+}
+
+// The V of each paged sequence in the attention kernel's LDS layout, once per
+// call: fp16 blocks [seq][logical block][Hkv][D][16 tokens] in the workspace
+// (bf16 rounded to fp16 and INT8 codes exactly, the tile staging's own
+// conversions), tokens past the context zero. Workgroup (logical block, KV
+// head, sequence); unit u = tokens 8*(u%2) .. +7 of channel u/2. Blocks past
+// the context are not written (the kernel never reads them).
+template <int D, bool VI8>
+__global__ __launch_bounds__(256) void k_v16_blocks(FlashArgs a) {
+  const int lb = blockIdx.x, kvh = blockIdx.y, z = blockIdx.z;
+  const int ctx = a.ctx_lens[z];
+  if (lb * 16 >= ctx) return;
+  const int64_t bh = (int64_t)a.tables[(int64_t)z * a.max_blocks + lb] * a.Hkv + kvh;
+  _Float16* dst = reinterpret_cast<_Float16*>(a.v_ws) + (((int64_t)z * a.max_blocks + lb) * a.Hkv + kvh) * D * 16;
+  for (int u = threadIdx.x; u < 2 * D; u += 256) {
+    const int ch = u >> 1, h = u & 1;
+    v8h f;
+    if constexpr (VI8) {
+      f = i8x8_to_f16x8(*reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.v_blocks) +
+                                                        (bh * D + ch) * 16 + 8 * h));
+    } else {
+      f = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v_blocks) +
+                                                          (bh * D + ch) * 16 + 8 * h));
+    }
+    const int t0 = lb * 16 + 8 * h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (t0 + e >= ctx) f[e] = (_Float16)0.0f;
+    *reinterpret_cast<v8h*>(dst + ch * 16 + 8 * h) = f;
+  }
 }
 
 template <int D>
@@ -841,6 +895,16 @@ hipError_t flash_d(const FlashArgs& a, hipStream_t st) {
   if (a.dense && a.pv_fp8)
     return a.causal ? run_flash<D, kVF16, true, true, true>(a, st) : run_flash<D, kVF16, true, false, true>(a, st);
   if (a.dense) return a.causal ? run_flash<D, kVF16, true, true>(a, st) : run_flash<D, kVF16, true, false>(a, st);
+  if (a.v_ws != nullptr) {
+    // paged prefill with V converted once into the workspace
+    const dim3 g((unsigned)a.max_blocks, (unsigned)a.Hkv, (unsigned)a.num_seqs);
+    if (a.v_int8) k_v16_blocks<D, true><<<g, 256, 0, st>>>(a);
+    else k_v16_blocks<D, false><<<g, 256, 0, st>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return a.v_int8 ? run_flash<D, kVI8, false, true, false, true>(a, st)
+                    : run_flash<D, kVBf16, false, true, false, true>(a, st);
+  }
   return a.v_int8 ? run_flash<D, kVI8, false, true>(a, st) : run_flash<D, kVBf16, false, true>(a, st);
 }
 

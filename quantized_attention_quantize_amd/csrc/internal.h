@@ -188,6 +188,7 @@ struct FlashArgs {
   float scale_log2;
   bool dense, causal, v_int8, v_f16, out_bf16, out_f16;
   bool pv_fp8;             // dense: FP8 P.V (head_dim 64 or 128)
+  void* v_ws;              // paged: workspace for the fp16 V blocks [seq][max_blocks][Hkv][D][16], or nullptr
 };
 hipError_t launch_flash(const FlashArgs& a, hipStream_t st);
 

@@ -204,6 +204,30 @@ def test_prefill_fp8pv_validation_and_workspace(qa):
     assert L.qa_chunked_prefill_attention_fp8pv(ctypes.byref(p), *([None] * 10), 0, None, None) == qa.QA_OK
 
 
+def test_prefill_ws_validation_and_workspace(qa):
+    """The prefill with V converted into a workspace: the 16-bit entry's
+    checks, a workspace of one fp16 V block (head_dim x 16) per logical block,
+    KV head and sequence, and a refusal of a smaller or missing one."""
+    L = qa.lib
+    p = qa.PrefillParams(3, 24, 4, 128, 16, 100, 1000, 10, 10, qa.QA_DT_BF16, qa.QA_DT_F32, 0.0)
+    need = L.qa_chunked_prefill_ws_workspace_bytes(ctypes.byref(p))
+    assert need == 3 * 100 * 4 * 128 * 16 * 2
+    call = lambda p, ws=FAKE, nb=need, q=FAKE: L.qa_chunked_prefill_attention_ws(
+        ctypes.byref(p), q, *([FAKE] * 6), None, FAKE, ws, nb, FAKE, None)   # v_scale NULL
+    assert call(p, nb=need - 1) == qa.QA_ERR_WORKSPACE_TOO_SMALL
+    assert call(p, ws=None) == qa.QA_ERR_INVALID_ARG
+    assert call(p, ws=ctypes.c_void_p(0x10008)) == qa.QA_ERR_INVALID_ARG   # not 16-byte aligned
+    assert call(p, q=None) == qa.QA_ERR_INVALID_ARG
+    p.head_dim = 96
+    assert L.qa_chunked_prefill_ws_workspace_bytes(ctypes.byref(p)) == 0
+    assert call(p) == qa.QA_ERR_UNSUPPORTED
+    p.head_dim = 128
+    p.v_cache_dtype = qa.QA_DT_I8
+    assert call(p) == qa.QA_ERR_INVALID_ARG                # INT8 V needs v_scale
+    p.num_seqs = 0
+    assert L.qa_chunked_prefill_attention_ws(ctypes.byref(p), *([None] * 10), 0, None, None) == qa.QA_OK
+
+
 def test_dense_options_validation(qa):
     L = qa.lib
     d = qa.DenseParams(2, 100, 90, 8, 4, 128, qa.QA_DT_BF16, 1, 0, 0.0, qa.QA_DT_F32)

@@ -369,6 +369,69 @@ def test_prefill_full_size_sampled(qa):
     assert_close(got[rows], want[rows], f"{spec.name} rows {rows}")
 
 
+# chunked prefill with V converted once into a workspace: the same output as
+# the plain entry bit for bit (a workspace full of NaN bytes beforehand, so a
+# read of any unwritten byte would show), the oracle's within tolerance, and
+# the workspace holding each context's V rounded to fp16
+
+
+def _prefill_ws_run(qa, inp, out_dtype=torch.float32):
+    spec = inp.spec
+    kc, ks, vc, vs = gpu_cache(qa, inp, spec.v_int8)
+    q8, qs = qa.quantize_q(dev_bits(inp.q, spec.dtype))
+    args = (q8, qs, torch.from_numpy(inp.cu_seqlens_q).cuda(), torch.from_numpy(inp.context_lens).cuda(), kc, ks,
+            vc, vs, torch.from_numpy(inp.block_tables).cuda(), max(spec.query_lens))
+    p = qa.prefill_params(q8, args[3], kc, vc, args[8], args[9], out_dtype=out_dtype)
+    ws = qa.chunked_prefill_ws_workspace(p)
+    assert ws.numel() == spec.num_seqs * inp.block_tables.shape[1] * spec.num_kv_heads * spec.head_dim * 32
+    ws.fill_(0xFF)
+    got = qa.chunked_prefill_attention_ws(*args, out_dtype=out_dtype, workspace=ws)
+    plain = qa.chunked_prefill_attention(*args, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return got, plain, ws, vc, vs
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: f"d{c[0]}_G{c[1]}_Hkv{c[2]}_{'i8V' if c[5] else 'bf16V'}_{'-'.join(map(str, c[3]))}")
+def test_prefill_ws_parity(qa, case):
+    d, G, Hkv, ctx, ql, v_int8 = case
+    say(f"prefill ws {case}")
+    spec = PagedSpec("pfw", 201 + d + G, len(ctx), G * Hkv, Hkv, d, ctx, ql, k_bias_std=2.0, v_int8=v_int8,
+                     pool_blocks=sum(-(-c // 16) for c in ctx) + 4)
+    inp = paged_inputs(spec)
+    if spec.total_q == 0:
+        return
+    got, plain, ws, vc, _ = _prefill_ws_run(qa, inp)
+    assert torch.equal(got, plain)
+    assert_close(got.cpu().numpy(), _prefill_oracle(inp), "prefill ws")
+    # the workspace: V of every block of the context, fp16 [seq, block, Hkv, d, 16]
+    nb = inp.block_tables.shape[1]
+    w = ws.view(torch.float16).view(spec.num_seqs, nb, Hkv, d, 16).cpu()
+    vcache = vc.cpu().float() if not v_int8 else vc.cpu().to(torch.float32)
+    for s_, c in enumerate(ctx):
+        for j in range(-(-c // 16)):
+            want = vcache[int(inp.block_tables[s_, j])].to(torch.float16).clone()
+            n_in = min(16, c - 16 * j)
+            want[..., n_in:] = 0
+            assert torch.equal(w[s_, j], want), (s_, j)
+
+
+def test_prefill_ws_bf16_output(qa):
+    spec = PagedSpec("pfwb", 77, 2, 12, 2, 128, [333, 70], [160, 70], k_bias_std=2.0, pool_blocks=40)
+    got, plain, _, _, _ = _prefill_ws_run(qa, paged_inputs(spec), out_dtype=torch.bfloat16)
+    assert torch.equal(got, plain)
+
+
+def test_prefill_ws_full_size(qa):
+    spec = chunked_prefill()
+    say(f"prefill ws full size {spec.name}")
+    inp = paged_inputs(spec)
+    got, plain, _, _, _ = _prefill_ws_run(qa, inp)
+    assert torch.equal(got, plain)
+    rows = [0, 2047]
+    want = _prefill_oracle(inp, rows=rows)
+    assert_close(got.cpu().numpy()[rows], want[rows], f"{spec.name} ws rows {rows}")
+
+
 # ---------------------------------------------------------------------------
 # chunked prefill with the P.V product in FP8 (E4M3): the tolerance model of
 # the dense FP8 path below (sigma of the difference to the plain definition),
