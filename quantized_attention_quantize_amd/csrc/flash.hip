@@ -518,8 +518,36 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     // the offset is folded into the exponent's constant term.
     v4i acc[QG][4];
     if constexpr (kPrio & 1) __builtin_amdgcn_s_setprio(1);
+    if constexpr (!DENSE) {
+      // paged: K fragments stream through a ring of 4 registers, read 3
+      // products ahead, the query fragments once per tile (a fence per
+      // product keeps the compiler from reading further ahead, or later)
+      auto kfrag = [&](int i) {                    // fragment i = KS*hu + s
+        const int hu = i / KS, s = i % KS;
+        const int tau = 32 * (hu >> 1) + 8 * (n >> 2) + 4 * (hu & 1) + (n & 3);
+        return *reinterpret_cast<const v4i*>(&s_k[buf][(tau >> 4) * KBS + (tau & 15) * 16 + g * 256 + s * 1024]);
+      };
+      v4i qv[QG][KS];
 #pragma unroll
-    for (int hu = 0; hu < 4; ++hu) {
+      for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qv[qg][s] = QLDS ? s_q[(wave * QG + qg) * KS + s][lane] : qf[qg][s];
+      constexpr int NF = 4 * KS, AHEAD = 3;
+      v4i kf[4];
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) kf[i] = kfrag(i);
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        if (i + AHEAD < NF) kf[(i + AHEAD) & 3] = kfrag(i + AHEAD);
+        const int hu = i / KS, s = i % KS;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg)
+          acc[qg][hu] = mfma_i8(kf[i & 3], qv[qg][s], s == 0 ? v4i{0, 0, 0, 0} : acc[qg][hu]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int hu = 0; hu < (DENSE ? 4 : 0); ++hu) {
       const int tau = 32 * (hu >> 1) + 8 * (n >> 2) + 4 * (hu & 1) + (n & 3);
       const int8_t* kp = &s_k[buf][(tau >> 4) * KBS + (tau & 15) * 16 + g * 256];
 #pragma unroll
@@ -704,8 +732,33 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
                            0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
       L8 = mfma_fp8_32x32x64(ones8, bop, L8);
     }
+    if constexpr (!DENSE) {
+      // paged: V fragments through a ring of 4 registers, 3 products ahead
+      __builtin_amdgcn_sched_barrier(0);
+      auto vfrag = [&](int i) {                    // fragment i = CG*half + c
+        const int half = i / CG, c = i % CG;
+        const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
+        return *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + 16 * c + n) * 16 + so]);
+      };
+      constexpr int NV = 2 * CG, AV = 3;
+      v8h vr[4];
 #pragma unroll
-    for (int half = 0; half < (PV8 ? 0 : 2); ++half) {
+      for (int i = 0; i < AV; ++i) vr[i] = vfrag(i);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (i + AV < NV) vr[(i + AV) & 3] = vfrag(i + AV);
+        const int half = i / CG, c = i % CG;
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vr[i & 3], pf[qg][half], O[qg][c]);
+        if (kRowSumMfma && c == CG - 1) {
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int half = 0; half < (PV8 || !DENSE ? 0 : 2); ++half) {
       const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
