@@ -16,6 +16,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> two fp16, nearest even, in one instruction (v_cvt_pk_f16_f32)
+__device__ __forceinline__ v2h cvt2_f16(float a, float b) { return __builtin_convertvector((v2f32){a, b}, v2h); }
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -78,7 +82,7 @@ __device__ __forceinline__ v8h bf16x8_to_f16x8(uint4 w) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const v2h h = (v2h){(_Float16)__uint_as_float(ws[i] << 16), (_Float16)__uint_as_float(ws[i] & 0xFFFF0000u)};
+    const v2h h = cvt2_f16(__uint_as_float(ws[i] << 16), __uint_as_float(ws[i] & 0xFFFF0000u));
     r[2 * i] = h[0];
     r[2 * i + 1] = h[1];
   }

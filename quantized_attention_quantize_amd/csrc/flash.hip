@@ -62,12 +62,12 @@ constexpr int kNW = 4;            // waves per workgroup, d <= 128
 constexpr int kNWD256Dense = 8;   // waves per workgroup, dense d = 256
 constexpr int kNWD256Paged = 12;  // waves per workgroup, paged prefill d = 256 (192-row workgroups)
 
-// 8 fp32 -> 8 fp16 through four packed conversions
+// 8 fp32 -> 8 fp16 through four packed conversions (nearest even)
 __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
   v8h r;
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
-    const v2h h = (v2h){(_Float16)p[j], (_Float16)p[j + 1]};
+    const v2h h = cvt2_f16(p[j], p[j + 1]);
     r[j] = h[0];
     r[j + 1] = h[1];
   }
