@@ -400,7 +400,7 @@ __device__ __forceinline__ uint32_t quant_byte_rcp(float x, float s, float rs) {
 // (query blocks, smooth_k with an LSE output) it also stores, per row,
 // corr_scale * sum_c x_c * corr_mu[b, h / corr_G, c] (fp32, the D/8 threads
 // of a row reduce their partial sums with shuffles).
-template <int D, int ROWS, bool BF16>
+template <int D, int ROWS, bool BF16, bool CORR = false>
 __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict__ x, Rows rows,
                                                      const int32_t* map, int32_t H, int64_t sb, int64_t st,
                                                      int64_t sh,
@@ -422,54 +422,79 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
   __shared__ float red[4];
 
-  float val[PER][8];
-  float amax = 0.0f;
+  // All PER row loads of the thread are issued before any is used (a row
+  // past the sequence end re-reads the last row, and counts as zeros), and
+  // the raw 16-bit values stay in registers: the fp32 values are formed again
+  // for the codes below, exactly as here.
+  uint4 wv[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int gi = threadIdx.x + 256 * k;
     const int r = gi / G8, c = (gi % G8) * 8;
-    const int t = blk * ROWS + r;
-    if (t < N) {
-      uint4 w = *reinterpret_cast<const uint4*>(x + seq0 + (int64_t)t * st + (int64_t)h * sh + c);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const int t = min(blk * ROWS + r, N - 1);
+    wv[k] = *reinterpret_cast<const uint4*>(x + seq0 + (int64_t)t * st + (int64_t)h * sh + c);
+  }
+  // the thread's 8 channels are the same in every row (256 is a multiple of G8)
+  const int c_thr = (threadIdx.x % G8) * 8;
+  float mu8[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        val[k][2 * i] = half_to_f32<BF16>(ws[i] & 0xFFFFu);
-        val[k][2 * i + 1] = half_to_f32<BF16>(ws[i] >> 16);
-      }
-      if (mean != nullptr) {
-        const float* mu = mean + ((int64_t)b * H + h) * D + c;
+  for (int i = 0; i < 8; ++i) mu8[i] = mean != nullptr ? mean[((int64_t)b * H + h) * D + c_thr + i] : 0.0f;
+  // fp32 values of unit k (minus the mean when given), zeros past the end
+  auto values = [&](int k, float (&v)[8]) {
+    const int t = blk * ROWS + (threadIdx.x + 256 * k) / G8;
+    const uint32_t ws[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) val[k][i] = val[k][i] - mu[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = half_to_f32<BF16>(ws[i] & 0xFFFFu);
+      v[2 * i + 1] = half_to_f32<BF16>(ws[i] >> 16);
+    }
+    if (mean != nullptr) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(val[k][i]));
-    } else {
+      for (int i = 0; i < 8; ++i) v[i] = v[i] - mu8[i];
+    }
+    if (t >= N) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) val[k][i] = 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+  };
+  float amax = 0.0f;
+  float cm[CORR ? 8 : 1];                    // LSE correction: the mean of this thread's channels
+  float dsum[CORR ? PER : 1];
+  if constexpr (CORR) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cm[i] = corr_mu[((int64_t)b * (H / corr_G) + h / corr_G) * D + c_thr + i];
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    float v[8];
+    values(k, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    if constexpr (CORR) {
+      dsum[k] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dsum[k] = fmaf(v[i], cm[i], dsum[k]);
     }
   }
-  if (corr != nullptr) {
-    const int Hm = H / corr_G;   // heads of the mean
+  if constexpr (CORR) {
+    // the G8 threads of a row are consecutive lanes of one wave (G8 divides 64)
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int gi = threadIdx.x + 256 * k;
-      const int r = gi / G8, c = (gi % G8) * 8;
-      const int t = blk * ROWS + r;
-      const float* mu = corr_mu + ((int64_t)b * Hm + h / corr_G) * D + c;
-      float dsum = 0.0f;
+      const int t = blk * ROWS + gi / G8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dsum = fmaf(val[k][i], mu[i], dsum);
-      // the G8 threads of row r are consecutive lanes of one wave (G8 divides 64)
-#pragma unroll
-      for (int o = 1; o < G8; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
-      if (gi % G8 == 0 && t < N) corr[rows.row_at(b, h, H, t)] = dsum * corr_scale;
+      for (int o = 1; o < G8; o <<= 1) dsum[k] += __shfl_xor(dsum[k], o, 64);
+      if (gi % G8 == 0 && t < N) corr[rows.row_at(b, h, H, t)] = dsum[k] * corr_scale;
     }
   }
   amax = wave_max(amax);
   if (lane == 0) red[wave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // the fp32 values are formed again below rather than kept (the compiler
+  // would otherwise keep all PER x 8 of them live across the reduction)
+#pragma unroll
+  for (int k = 0; k < PER; ++k) asm volatile("" : "+v"(wv[k].x), "+v"(wv[k].y), "+v"(wv[k].z), "+v"(wv[k].w));
   const float s = quant_scale(amax);
   const float rs = __fdiv_rn(1.0f, s);
   const bool fast = rs <= 3.0e38f;         // workgroup-uniform
@@ -478,13 +503,15 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     const int gi = threadIdx.x + 256 * k;
     const int r = gi / G8, c = (gi % G8) * 8;
     const int t = blk * ROWS + r;
+    float v[8];
+    values(k, v);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t c0 = 0, c1 = 0;
       if (amax > 0.0f) {
-        c0 = fast ? quant_byte_rcp(val[k][i], s, rs) : (uint32_t)quant_code(val[k][i], s) & 0xFFu;
-        c1 = fast ? quant_byte_rcp(val[k][4 + i], s, rs) : (uint32_t)quant_code(val[k][4 + i], s) & 0xFFu;
+        c0 = fast ? quant_byte_rcp(v[i], s, rs) : (uint32_t)quant_code(v[i], s) & 0xFFu;
+        c1 = fast ? quant_byte_rcp(v[4 + i], s, rs) : (uint32_t)quant_code(v[4 + i], s) & 0xFFu;
       }
       lo |= c0 << (8 * i);
       hi |= c1 << (8 * i);
@@ -607,7 +634,8 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
   k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, a.smooth_k, a.k_mean);
   if (a.Nq > 0) {
     float* corr = a.smooth_k ? a.lse_corr : nullptr;
-    k_block_quant<D, 128, BF16><<<grid(a.q_rows, 128, a.Hq), 256, 0, s>>>(
+    auto qk = corr != nullptr ? k_block_quant<D, 128, BF16, true> : k_block_quant<D, 128, BF16, false>;
+    qk<<<grid(a.q_rows, 128, a.Hq), 256, 0, s>>>(
         (const uint16_t*)a.q, a.q_rows, a.q_map, a.Hq, a.q_sb, a.q_st, a.q_sh, nullptr, a.q_i8, nullptr, a.q_scale,
         a.k_mean, a.Hq / a.Hkv, a.corr_scale, corr);
   }
