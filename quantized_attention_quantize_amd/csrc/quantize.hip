@@ -255,15 +255,35 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
   for (int i = 0; i < 8; ++i) dst[i] = acc[i];
 }
 
+// The column reductions below (the smooth_k / smooth_v mean, the FP8 V
+// scale): a workgroup covers kRedCols columns, kRedSlices threads per column
+// each take every kRedSlices-th chunk partial (loads unrolled, all in flight),
+// then the slices meet through LDS. The sums are exact (see k_colsum) and the
+// maxima exact, so the order does not matter.
+constexpr int kRedCols = 16, kRedSlices = 16;
+
+template <bool MAX>
+__device__ __forceinline__ double reduce_column(const double* __restrict__ p, int32_t HD, int used, int slice) {
+  double acc = 0.0;
+  int j = slice;
+  for (; j + 7 * kRedSlices < used; j += 8 * kRedSlices) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(j + u * kRedSlices) * HD];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = MAX ? fmax(acc, v[u]) : acc + v[u];
+  }
+  for (; j < used; j += kRedSlices) acc = MAX ? fmax(acc, p[(int64_t)j * HD]) : acc + p[(int64_t)j * HD];
+  return acc;
+}
+
 // mu[b][c] = fl32(fl64(sum / Nk_b)); zeros when smoothing is off or the
-// sequence is empty. A workgroup covers 64 columns: four threads per column
-// each add every fourth chunk partial, then the four sums are added through
-// LDS (all sums are exact, so the order does not matter).
+// sequence is empty.
 __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, Rows rows,
                                               int32_t HD, bool smooth, float* __restrict__ mean) {
-  __shared__ double red[4][64];
-  const int col = threadIdx.x & 63, slice = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * 64 + col;   // b * HD + c
+  __shared__ double red[kRedSlices][kRedCols];
+  const int col = threadIdx.x % kRedCols, slice = threadIdx.x / kRedCols;
+  const int64_t i = (int64_t)blockIdx.x * kRedCols + col;   // b * HD + c
   const bool live = i < (int64_t)rows.B * HD;
   const int b = live ? (int)(i / HD) : 0;
   const int Nk = live ? rows.len(b) : 0;
@@ -271,9 +291,7 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
   if (live && smooth && Nk > 0) {
     const int c = (int)(i % HD);
     const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
-    const double* p = partial + (int64_t)b * chunks * HD + c;
-    const int used = (Nk + kSumChunk - 1) / kSumChunk;
-    for (int j = slice; j < used; j += 4) s += p[(int64_t)j * HD];
+    s = reduce_column<false>(partial + (int64_t)b * chunks * HD + c, HD, (Nk + kSumChunk - 1) / kSumChunk, slice);
   }
   red[slice][col] = s;
   __syncthreads();
@@ -281,33 +299,37 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
     if (!smooth || Nk <= 0) {
       mean[i] = 0.0f;
     } else {
-      const double tot = ((red[0][col] + red[1][col]) + red[2][col]) + red[3][col];
+      double tot = 0.0;
+#pragma unroll
+      for (int k = 0; k < kRedSlices; ++k) tot += red[k][col];
       mean[i] = (float)(tot / (double)Nk);
     }
   }
 }
 
 // FP8 scale of V per (b, KV head, channel): fl32(max |V'| / 448) from the
-// chunk maxima of k_colsum<.., true> (0 for an empty sequence). As k_mean:
-// 64 columns per workgroup, four threads per column.
+// chunk maxima of k_colsum<.., true> (0 for an empty sequence).
 __global__ __launch_bounds__(256) void k_vscale(const double* __restrict__ partial, Rows rows, int32_t HD,
                                                 float* __restrict__ vscale) {
-  __shared__ double red[4][64];
-  const int col = threadIdx.x & 63, slice = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * 64 + col;   // b * HD + c
+  __shared__ double red[kRedSlices][kRedCols];
+  const int col = threadIdx.x % kRedCols, slice = threadIdx.x / kRedCols;
+  const int64_t i = (int64_t)blockIdx.x * kRedCols + col;   // b * HD + c
   const bool live = i < (int64_t)rows.B * HD;
   double m = 0.0;
   if (live) {
     const int b = (int)(i / HD), c = (int)(i % HD);
     const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
     const int used = (rows.len(b) + kSumChunk - 1) / kSumChunk;
-    const double* p = partial + (int64_t)b * chunks * HD + c;
-    for (int j = slice; j < used; j += 4) m = fmax(m, p[(int64_t)j * HD]);
+    m = reduce_column<true>(partial + (int64_t)b * chunks * HD + c, HD, used, slice);
   }
   red[slice][col] = m;
   __syncthreads();
-  if (slice == 0 && live)
-    vscale[i] = __fdiv_rn((float)fmax(fmax(red[0][col], red[1][col]), fmax(red[2][col], red[3][col])), 448.0f);
+  if (slice == 0 && live) {
+    double mx = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRedSlices; ++k) mx = fmax(mx, red[k][col]);
+    vscale[i] = __fdiv_rn((float)mx, 448.0f);
+  }
 }
 
 // V -> FP8 (E4M3) blocks of 64 tokens for the FP8 P.V product:
@@ -627,7 +649,7 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
     k_block_map<<<a.B, 256, 0, s>>>(a.k_rows, 16, a.k_map16);
   }
   const dim3 gsum = vl ? dim3((unsigned)a.k_rows.nblocks(kSumChunk), cgs, 1) : dim3(cgs, chunks, a.B);
-  const unsigned gmean = (unsigned)(((int64_t)a.B * HD + 63) / 64);
+  const unsigned gmean = (unsigned)(((int64_t)a.B * HD + kRedCols - 1) / kRedCols);
   if (a.smooth_k && a.Nk > 0)
     k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, a.k_map64, D, HD, a.k_sb, a.k_st, a.k_sh,
                                         a.partial);
