@@ -313,11 +313,7 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     const int kbase = tile * KT8;
-    // next tile: copies, its block entries one further ahead, its key scales
-    const Blocks pb = unpack(pb_next);
-    dma(buf ^ 1, tile + 1, pb);
-    pb_next = load_blocks(tile + 2);
-    const float ks_next = scale_of(tile + 1, pb);
+    const Blocks pb = unpack(pb_next);            // the next tile's physical blocks
 
     // ---- S^T = K Q^T: block b, row 4g + i = key 32g + 4b + i ------------------
     // K fragments stream through a ring of 4 registers, read 3 products
@@ -340,6 +336,14 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
       acc[b] = mfma_i8(kf[i & 3], qf[s], acc[b]);
       __builtin_amdgcn_sched_barrier(0);
     }
+
+    // next tile: copies, its block entries one further ahead, its key scales
+    // (issued after this tile's S^T products: issued before them, the copies
+    // of all waves sit in front of every wave's first products; measured 3%
+    // slower)
+    dma(buf ^ 1, tile + 1, pb);
+    pb_next = load_blocks(tile + 2);
+    const float ks_next = scale_of(tile + 1, pb);
 
     // ---- scores of keys 32g + k, k = 4b + i ------------------------------------
     float x[32];
