@@ -494,9 +494,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     const int kbase = tile * KT;
     // the next tile (past the last one the clamped blocks are re-read and the
     // spare buffer written but never used)
-    // (paged: issued after this tile's S^T products, see below)
+    // (issued after this tile's S^T products, see below)
     St nxt;
-    if constexpr (kDma) dma(buf ^ 1, tile + 1);
     const Blocks pb_cur = unpack(pb_next);
     if constexpr (!kDma) pb_next = load_blocks(tile + 2);
 
@@ -559,10 +558,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     }
 
     if constexpr (kPrio & 1) __builtin_amdgcn_s_setprio(0);
-    // paged: the next tile's loads and copies go out after the S^T products
-    // (issued before them, they sit in front of every wave's first products;
-    // measured 2-3% slower)
-    if constexpr (!kDma) fetch(nxt, tile + 1, pb_cur, buf ^ 1);
+    // the next tile's loads and copies go out after the S^T products (issued
+    // before them, they sit in front of every wave's first products; measured
+    // 2-3% slower for the paged prefill, 0.3-1.3% for dense)
+    if constexpr (kDma) dma(buf ^ 1, tile + 1);
+    else fetch(nxt, tile + 1, pb_cur, buf ^ 1);
     // key of x[j] below: kbase + 32*(j/8) + 8*g + j%8
     const int tl = 8 * g;
     // masks only on tiles that cross the context end or the causal diagonal
