@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
 
     // ---- O^T += V8^T P8^T, row sums against ones -----------------------------
     __builtin_amdgcn_sched_barrier(0);             // no V8 reads hoisted into the softmax
-    // V8 fragments one channel block ahead, as the K fragments above
+    // V8 fragments two channel blocks ahead (one ahead measured 5% slower)
     const uint8_t* vt = s_v[buf] + g * (D * 32) + n * 32;
     const int sw = (n >> 3) & 1;                   // bit 3 of the channel 16c + n
     auto vfrag = [&](int c) {
@@ -399,12 +399,13 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
       const v4i hi = *reinterpret_cast<const v4i*>(vt + c * 512 + 16 * (sw ^ 1));
       return v8i_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    v8i_t aop[2];
+    v8i_t aop[4];
     aop[0] = vfrag(0);
+    aop[1] = vfrag(1);
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
-      if (c + 1 < CG) aop[(c + 1) & 1] = vfrag(c + 1);
-      O[c] = mfma_fp8_16x16x128(aop[c & 1], bop, O[c]);
+      if (c + 2 < CG) aop[(c + 2) & 3] = vfrag(c + 2);
+      O[c] = mfma_fp8_16x16x128(aop[c & 3], bop, O[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
     L = mfma_fp8_16x16x128(ones8, bop, L);
