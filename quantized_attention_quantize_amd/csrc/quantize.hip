@@ -119,14 +119,39 @@ __device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, con
   }
 }
 
-// One wave per (token, head) row; 4 rows per workgroup.
+// Each wave quantizes kRowsPerWave (token, head) rows, every load issued
+// before the first row is reduced (one row per wave waited for its load
+// alone); 4 waves per workgroup. The codes are quant_row's.
+constexpr int kRowsPerWave = 4;
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
                                                        int32_t H, int64_t st, int64_t sh,
                                                        int8_t* __restrict__ q, float* __restrict__ scale) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  quant_row<D, BF16>(x, row, H, st, sh, q, scale, threadIdx.x & 63);
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+  if (row0 >= rows) return;
+  float v[kRowsPerWave][E];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t row = min(row0 + i, rows - 1);   // rows past the end re-read the last (not stored)
+    const int64_t t = row / H;
+    const int h = (int)(row - t * H);
+    load_halves<E, BF16>(x + t * st + (int64_t)h * sh + lane * E, v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t row = row0 + i;
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    amax = wave_max(amax);
+    const float s = quant_scale(amax);
+    if (row < rows) {
+      store_codes<E>(q + row * D + lane * E, quant_lane<E>(v[i], amax, s));
+      if (lane == 0) scale[row] = s;
+    }
+  }
 }
 
 template <int D, bool BF16, bool V_I8>
@@ -139,6 +164,99 @@ __global__ __launch_bounds__(256) void k_write_kv(const uint16_t* __restrict__ k
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   write_kv_row<D, BF16, V_I8>(k, v, row, H, st, sh, slots, kc, ks, vc, vs, threadIdx.x & 63);
+}
+
+// The cache write for runs of tokens: workgroup (group of 16 tokens, head).
+// When the group's 16 slots are the 16 slots of one cache block in order
+// (slot_j = 16*blk + j: a chunk written from a block boundary), each wave
+// quantizes 4 token rows, the codes and V values are gathered in LDS in the
+// block's own layout, and the workgroup then writes the K block (D*16 bytes)
+// and the V block (D*16 values) as contiguous 16-byte pieces: a token's V
+// row alone lands in D places 32 (16) bytes apart, which costs a memory
+// transaction per 2 (1) bytes. Any other group (unaligned, partly skipped,
+// the ragged end) writes its rows one by one as k_write_kv does. The codes
+// and scales are those of write_kv_row in either case.
+template <int D, bool BF16, bool V_I8>
+__global__ __launch_bounds__(256) void k_write_kv_blocks(const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int64_t T,
+                                                         int32_t H, int64_t st, int64_t sh,
+                                                         const int64_t* __restrict__ slots,
+                                                         int8_t* __restrict__ kc, float* __restrict__ ks,
+                                                         void* __restrict__ vc, float* __restrict__ vs) {
+  constexpr int E = D / 64;
+  constexpr int VB = V_I8 ? 1 : 2;                  // bytes per cached V value
+  __shared__ __attribute__((aligned(16))) int8_t s_k[D * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[D * 16 * VB];
+  __shared__ float s_ks[16], s_vs[16];
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the group is a whole block in order when every lane j < 16 finds slot t0 + j = slot t0 + j
+  int64_t slot0 = -1;
+  bool whole = t0 + 16 <= T;
+  if (whole) {
+    slot0 = slots[t0];
+    const int64_t sj = lane < 16 ? slots[t0 + lane] : slot0 + lane;
+    whole = slot0 >= 0 && (slot0 & 15) == 0 && __all(sj == slot0 + lane);
+  }
+  if (!whole) {
+    for (int j = wave; j < 16; j += 4) {
+      const int64_t t = t0 + j;
+      if (t < T) write_kv_row<D, BF16, V_I8>(k, v, t * H + h, H, st, sh, slots, kc, ks, vc, vs, lane);
+    }
+    return;
+  }
+  const int ch = lane * E;
+  // the wave's 4 rows: every K and V load issued before any is used
+  float kr[4][E], vr[4][V_I8 ? E : 1];
+  uint16_t vraw[4][V_I8 ? 1 : E];               // 16-bit V is copied as it is
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t src = (t0 + wave + 4 * i) * st + (int64_t)h * sh + ch;
+    load_halves<E, BF16>(k + src, kr[i]);
+    if constexpr (V_I8) {
+      load_halves<E, BF16>(v + src, vr[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) vraw[i][e] = v[src + e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = wave + 4 * i;
+    const float(&kv)[E] = kr[i];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(kv[e]));
+    amax = wave_max(amax);
+    const float sk = quant_scale(amax);
+    store_codes<E>(s_k + (ch / 16) * 256 + j * 16 + (ch % 16), quant_lane<E>(kv, amax, sk));
+    if (lane == 0) s_ks[j] = sk;
+    if constexpr (V_I8) {
+      const float(&vv)[E] = vr[i];
+      float vmax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) vmax = fmaxf(vmax, fabsf(vv[e]));
+      vmax = wave_max(vmax);
+      const float sv = quant_scale(vmax);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_v[(ch + e) * 16 + j] = (uint8_t)(vmax > 0.0f ? quant_code(vv[e], sv) : 0);
+      if (lane == 0) s_vs[j] = sv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) reinterpret_cast<uint16_t*>(s_v)[(ch + e) * 16 + j] = vraw[i][e];
+    }
+  }
+  __syncthreads();
+  const int64_t bh = (slot0 >> 4) * H + h;
+  uint4* kd = reinterpret_cast<uint4*>(kc + bh * (D * 16));
+  for (int u = threadIdx.x; u < D; u += 256) kd[u] = reinterpret_cast<const uint4*>(s_k)[u];
+  uint4* vd = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(vc) + bh * (D * 16 * VB));
+  for (int u = threadIdx.x; u < D * VB; u += 256) vd[u] = reinterpret_cast<const uint4*>(s_v)[u];
+  if (threadIdx.x < 16) {
+    ks[bh * 16 + threadIdx.x] = s_ks[threadIdx.x];
+    if constexpr (V_I8) vs[bh * 16 + threadIdx.x] = s_vs[threadIdx.x];
+  }
 }
 
 // Fused producer: workgroups [0, qblocks) quantize query rows, the rest write
@@ -610,7 +728,7 @@ template <int D>
 hipError_t quantize_rows_d(const void* x, bool bf16, int64_t T, int32_t H, int64_t st, int64_t sh,
                            int8_t* q, float* scale, hipStream_t s) {
   const int64_t rows = T * H;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid((unsigned)((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
   if (bf16)
     k_quantize_rows<D, true><<<grid, 256, 0, s>>>((const uint16_t*)x, rows, H, st, sh, q, scale);
   else
@@ -623,6 +741,17 @@ hipError_t write_kv_d(const void* k, const void* v, int64_t T, int32_t H, int64_
                       const int64_t* slots, int8_t* kc, float* ks, void* vc, bool v_i8, float* vs,
                       hipStream_t s) {
   const int64_t rows = T * H;
+  if (T >= 16) {
+    // groups of 16 tokens (whole blocks written at once when aligned)
+    const dim3 g((unsigned)((T + 15) / 16), (unsigned)H);
+    if (v_i8)
+      k_write_kv_blocks<D, BF16, true><<<g, 256, 0, s>>>((const uint16_t*)k, (const uint16_t*)v, T, H, st, sh,
+                                                         slots, kc, ks, vc, vs);
+    else
+      k_write_kv_blocks<D, BF16, false><<<g, 256, 0, s>>>((const uint16_t*)k, (const uint16_t*)v, T, H, st, sh,
+                                                          slots, kc, ks, vc, vs);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((rows + 3) / 4));
   if (v_i8)
     k_write_kv<D, BF16, true><<<grid, 256, 0, s>>>((const uint16_t*)k, (const uint16_t*)v, rows, H, st,
