@@ -82,6 +82,21 @@ __device__ __forceinline__ int group4_max_i32(int v) {
   return max((int)b[0], (int)b[1]);
 }
 
+// The same for two integers at once (three exchanges instead of four): a's
+// maximum lands in ma, b's in mb, in every lane. The first exchange trades
+// the odd 16-lane rows of a for the even rows of b, so one maximum leaves
+// a's row pairs in rows 0 and 2 and b's in rows 1 and 3; the second combines
+// the halves; the third hands each lane both results.
+__device__ __forceinline__ void group4_max2_i32(int a, int b, int& ma, int& mb) {
+  const auto s1 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const int z = max((int)s1[0], (int)s1[1]);
+  const auto s2 = __builtin_amdgcn_permlane32_swap(z, z, false, false);
+  const int u = max((int)s2[0], (int)s2[1]);
+  const auto s3 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  ma = (int)s3[0];
+  mb = (int)s3[1];
+}
+
 // Initial softmax reference: finite, so that no step needs a test for an
 // empty row (exp2 of anything minus it is 0, and a row's first visible key
 // always moves it).
@@ -174,8 +189,20 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   int qtile = CAUSAL ? nqt - 1 - wid % nqt : wid % nqt;
   int hu_ = DENSE ? wid / (nqt * a.num_seqs) : (wid / nqt) % nunits;
   int z = DENSE ? (wid / nqt) % a.num_seqs : wid / (nqt * nunits);
+  if (DENSE && CAUSAL && !a.q_rows.packed && (total & 7) == 0 && ((a.num_seqs * nunits) & 7) == 0) {
+    // causal, batched: each XCD keeps its eighth of the (query head,
+    // sequence) units and takes their query tiles longest first across all
+    // of them (per unit, the long tiles of its last units would start late)
+    const int per = (a.num_seqs * nunits) >> 3;
+    const int li = (int)(blockIdx.x >> 3);
+    const int u = (int)(blockIdx.x & 7) * per + li % per;
+    qtile = nqt - 1 - li / per;
+    hu_ = u / a.num_seqs;
+    z = u % a.num_seqs;
+  }
   if (DENSE && a.q_rows.packed) {
     // varlen: (packed 128-row block, query head), the block's sequence from the map
+
     const int nblk = (int)a.q_rows.nblocks(QT);
     const int j = CAUSAL ? nblk - 1 - wid % nblk : wid % nblk;
     hu_ = wid / nblk;
@@ -587,7 +614,35 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     bool exact_off = false;
     if constexpr (DENSE) {
       fw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qsc[0] * tsc)));
-      exact_off = kMagic && !(kOffset * fw <= 4096.0f);
+      // (fw >= 0: compared as integer bits, in scalar registers)
+      exact_off = kMagic && __float_as_int(fw) > __float_as_int(4096.0f / kOffset);
+    }
+    // dense: each lane's row maximum of the raw accumulators (a chain of
+    // three-input maxima; read as floats in [2^23, 2^24) they order like
+    // their bit patterns) and, on unmasked tiles, the row maximum across the
+    // four lane groups times the tile factor
+    int imq[QG];
+    float mtq[QG];
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        auto A = [&](int j) { return acc[qg][j >> 2][j & 3]; };
+        int m = max(max(A(0), A(1)), A(2));
+#pragma unroll
+        for (int j = 3; j < 15; j += 2) m = max(max(m, A(j)), A(j + 1));
+        imq[qg] = max(m, A(15));
+      }
+      if (!need_mask) {
+        int gm[QG];
+        if constexpr (QG == 2) {
+          group4_max2_i32(imq[0], imq[1], gm[0], gm[1]);
+        } else {
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) gm[qg] = group4_max_i32(imq[qg]);
+        }
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) mtq[qg] = (__int_as_float(gm[qg]) - kOffset) * fw;
+      }
     }
     v8h pf[QG][2];
     uint32_t pk[QG][4];                          // FP8 P.V: byte j of word w is p[4w + j]
@@ -601,9 +656,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       int im = 0;
       if constexpr (DENSE) {
         f = fw;
-        im = max(acc[qg][0][0], acc[qg][0][1]);
-#pragma unroll
-        for (int j = 2; j < 16; j += 2) im = max(im, max(acc[qg][j >> 2][j & 3], acc[qg][j >> 2][(j & 3) + 1]));
+        im = imq[qg];
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] = kMagic ? __int_as_float(acc[qg][j >> 2][j & 3]) : (float)acc[qg][j >> 2][j & 3];
         mx = kMagic ? __int_as_float(im) : (float)im;
@@ -640,7 +693,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       if (DENSE && kMagic && !need_mask) {
         // row maximum of the raw accumulators (floats in [2^23, 2^24) order
         // like their bit patterns), across the four lane groups, then scaled
-        mt = (__int_as_float(group4_max_i32(im)) - kOffset) * f;
+        mt = mtq[qg];
       } else {
         mt = mx == kNegInf ? kNegInf : (mx - off) * f;
         mt = group4_max(mt);
