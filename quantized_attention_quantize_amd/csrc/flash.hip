@@ -74,29 +74,6 @@ __device__ __forceinline__ v8h pack8(const float (&p)[8]) {
   return r;
 }
 
-// max across the four 16-lane groups of an integer (no float canonicalization)
-__device__ __forceinline__ int group4_max_i32(int v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = max((int)a[0], (int)a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max((int)b[0], (int)b[1]);
-}
-
-// The same for two integers at once (three exchanges instead of four): a's
-// maximum lands in ma, b's in mb, in every lane. The first exchange trades
-// the odd 16-lane rows of a for the even rows of b, so one maximum leaves
-// a's row pairs in rows 0 and 2 and b's in rows 1 and 3; the second combines
-// the halves; the third hands each lane both results.
-__device__ __forceinline__ void group4_max2_i32(int a, int b, int& ma, int& mb) {
-  const auto s1 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  const int z = max((int)s1[0], (int)s1[1]);
-  const auto s2 = __builtin_amdgcn_permlane32_swap(z, z, false, false);
-  const int u = max((int)s2[0], (int)s2[1]);
-  const auto s3 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  ma = (int)s3[0];
-  mb = (int)s3[1];
-}
-
 // Initial softmax reference: finite, so that no step needs a test for an
 // empty row (exp2 of anything minus it is 0, and a row's first visible key
 // always moves it).
@@ -617,12 +594,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       // (fw >= 0: compared as integer bits, in scalar registers)
       exact_off = kMagic && __float_as_int(fw) > __float_as_int(4096.0f / kOffset);
     }
-    // dense: each lane's row maximum of the raw accumulators (a chain of
+    // dense: each lane's maximum of its raw accumulators (a chain of
     // three-input maxima; read as floats in [2^23, 2^24) they order like
-    // their bit patterns) and, on unmasked tiles, the row maximum across the
-    // four lane groups times the tile factor
+    // their bit patterns)
     int imq[QG];
-    float mtq[QG];
     if constexpr (DENSE) {
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) {
@@ -631,17 +606,6 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
 #pragma unroll
         for (int j = 3; j < 15; j += 2) m = max(max(m, A(j)), A(j + 1));
         imq[qg] = max(m, A(15));
-      }
-      if (!need_mask) {
-        int gm[QG];
-        if constexpr (QG == 2) {
-          group4_max2_i32(imq[0], imq[1], gm[0], gm[1]);
-        } else {
-#pragma unroll
-          for (int qg = 0; qg < QG; ++qg) gm[qg] = group4_max_i32(imq[qg]);
-        }
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) mtq[qg] = (__int_as_float(gm[qg]) - kOffset) * fw;
       }
     }
     v8h pf[QG][2];
@@ -689,17 +653,16 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         mx -= kOffset;
         off = 0.0f;
       }
+      // this lane's largest (visible) score
       float mt;
-      if (DENSE && kMagic && !need_mask) {
-        // row maximum of the raw accumulators (floats in [2^23, 2^24) order
-        // like their bit patterns), across the four lane groups, then scaled
-        mt = mtq[qg];
-      } else {
-        mt = mx == kNegInf ? kNegInf : (mx - off) * f;
-        mt = group4_max(mt);
-      }
-      // lazy rescale: move the reference only when it is exceeded by > 2^8
+      if (DENSE && kMagic && !need_mask) mt = (__int_as_float(im) - kOffset) * f;
+      else mt = mx == kNegInf ? kNegInf : (mx - off) * f;
+      // lazy rescale: move the reference only when it is exceeded by > 2^8.
+      // A row's maximum exceeds it exactly when one of the row's lanes holds
+      // such a score, so the test needs no maximum across the lane groups;
+      // that maximum is formed only when the reference moves.
       if (__any(mt > m_run[qg] + (PV8 ? kFp8Slack : kRescaleSlack))) {
+        mt = group4_max(mt);
         const float m_new = fmaxf(m_run[qg], mt);
         const float alpha = fast_exp2(m_run[qg] - m_new);
         l_run[qg] *= alpha;

@@ -365,10 +365,13 @@ __global__ __launch_bounds__(kNW8 * 64) __attribute__((amdgpu_waves_per_eu(kNW8 
     float mx = fmaxf(x[0], x[1]);
 #pragma unroll
     for (int k = 2; k < 32; k += 2) mx = fmaxf(mx, fmaxf(x[k], x[k + 1]));
-    const float mt = group4_max(mx * f);          // -inf when every key of the row is hidden
-    // lazy reference: moved only when exceeded by more than the slack
-    if (__any(mt > m_run + kSlack8)) {
-      const float m_new = fmaxf(m_run, mt);
+    // lazy reference: moved only when exceeded by more than the slack. Some
+    // lane of the row then holds such a score, so the test takes each lane's
+    // own maximum; the maximum across the lane groups is formed only when the
+    // reference moves (-inf when every key of the row is hidden).
+    const float ml = mx * f;
+    if (__any(ml > m_run + kSlack8)) {
+      const float m_new = fmaxf(m_run, group4_max(ml));
       const float alpha = fast_exp2(m_run - m_new);
       L *= alpha;
 #pragma unroll
