@@ -572,221 +572,342 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     // masks only on tiles that cross the context end or the causal diagonal
     bool need_mask = kbase + KT > kv_len;
     if constexpr (CAUSAL) need_mask = need_mask || (kbase + KT - 1 > wq_first + offset);
-    float sk[16], sv[16];
-    if constexpr (!DENSE) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sk[j] = s_ks[buf][32 * (j >> 3) + tl + (j & 7)];
-    }
-    if constexpr (VK == kVI8) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sv[j] = s_vs[buf][32 * (j >> 3) + tl + (j & 7)];
-    }
-
-    // dense: one factor sQ_blk * sK_blk * scale for the whole workgroup and
-    // tile (one 128-row query block, one key block), held as a scalar; the
-    // folded accumulator offset costs half an ulp of offset*f in the
-    // exponent, so when offset*f > 2^12 (scores of large-magnitude inputs)
-    // the offset is subtracted exactly instead
-    float fw = 0.0f;
-    bool exact_off = false;
-    if constexpr (DENSE) {
-      fw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qsc[0] * tsc)));
-      // (fw >= 0: compared as integer bits, in scalar registers)
-      exact_off = kMagic && __float_as_int(fw) > __float_as_int(4096.0f / kOffset);
-    }
-    // dense: each lane's maximum of its raw accumulators (a chain of
-    // three-input maxima; read as floats in [2^23, 2^24) they order like
-    // their bit patterns)
-    int imq[QG];
-    if constexpr (DENSE) {
+    if constexpr (DENSE && !PV8) {
+      // ---- dense: the softmax by key halves --------------------------------
+      // P of keys 0..31 (both query groups) first; the P.V products of that
+      // half then go out between the exponentials of keys 32..63, so that the
+      // wave's matrix and vector work overlap. Hidden keys get x = -inf (their
+      // P is exp2(-inf) = 0 before any product), which needs a positive tile
+      // factor: a zero factor (a zero query or key block) scores every key 0,
+      // and the smallest normal float in its place moves no score by an
+      // amount a float resolves. One factor sQ_blk * sK_blk * scale for the
+      // workgroup and tile, held as a scalar; the folded accumulator offset
+      // costs half an ulp of offset*f in the exponent, so when offset*f >
+      // 2^12 (scores of large-magnitude inputs) the offset is subtracted
+      // exactly instead (bit patterns of positive floats compare like them).
+      const int fwb = max(__builtin_amdgcn_readfirstlane(__float_as_int(qsc[0] * tsc)), 0x00800000);
+      const float fw = __int_as_float(fwb);
+      const bool exact_off = fwb > __float_as_int(4096.0f / kOffset);
+      const float off = exact_off ? 0.0f : kOffset;
+      float x[QG][16], cterm[QG];
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) {
+        // this lane's maximum of its raw accumulators (a chain of three-input
+        // maxima; read as floats in [2^23, 2^24) they order like their bits)
         auto A = [&](int j) { return acc[qg][j >> 2][j & 3]; };
-        int m = max(max(A(0), A(1)), A(2));
+        int im = max(max(A(0), A(1)), A(2));
 #pragma unroll
-        for (int j = 3; j < 15; j += 2) m = max(max(m, A(j)), A(j + 1));
-        imq[qg] = max(m, A(15));
-      }
-    }
-    v8h pf[QG][2];
-    uint32_t pk[QG][4];                          // FP8 P.V: byte j of word w is p[4w + j]
-    float al8 = 1.0f;                            // FP8 P.V: rescale of this lane's query (32x32 layout)
-    bool resc8 = false;
+        for (int j = 3; j < 15; j += 2) im = max(max(im, A(j)), A(j + 1));
+        im = max(im, A(15));
 #pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-      // score_j = x[j] * f with one lane factor f >= 0 (dense: the Q and K
-      // block scales; paged: the Q scale, sK folded into x)
-      float x[16], f, mx;
-      int im = 0;
-      if constexpr (DENSE) {
-        f = fw;
-        im = imq[qg];
+        for (int j = 0; j < 16; ++j) x[qg][j] = __int_as_float(A(j));
+        // this lane's largest visible score
+        float mt;
+        if (need_mask) {
+          const int pos = qi[qg] + offset;
+          float mx = kNegInf;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = kMagic ? __int_as_float(acc[qg][j >> 2][j & 3]) : (float)acc[qg][j >> 2][j & 3];
-        mx = kMagic ? __int_as_float(im) : (float)im;
-      } else {
-        f = qsc[qg];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = (float)acc[qg][j >> 2][j & 3] * sk[j];
-        mx = fmaxf(x[0], x[1]);
-#pragma unroll
-        for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
-      }
-      uint32_t vis = 0xFFFFu;   // visible keys of this lane (bit j: the key of x[j])
-      if (need_mask) {
-        const int pos = qi[qg] + offset;
-        vis = 0;
-        mx = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int tk = kbase + 32 * (j >> 3) + tl + (j & 7);
-          bool ok = tk < kv_len;
-          if constexpr (CAUSAL) ok = ok && tk <= pos;
-          vis |= ok ? 1u << j : 0u;
-          mx = ok ? fmaxf(mx, x[j]) : mx;
-        }
-      }
-      float off = kMagic ? kOffset : 0.0f;
-      if (exact_off) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] -= kOffset;
-        mx -= kOffset;
-        off = 0.0f;
-      }
-      // this lane's largest (visible) score
-      float mt;
-      if (DENSE && kMagic && !need_mask) mt = (__int_as_float(im) - kOffset) * f;
-      else mt = mx == kNegInf ? kNegInf : (mx - off) * f;
-      // lazy rescale: move the reference only when it is exceeded by > 2^8.
-      // A row's maximum exceeds it exactly when one of the row's lanes holds
-      // such a score, so the test needs no maximum across the lane groups;
-      // that maximum is formed only when the reference moves.
-      if (__any(mt > m_run[qg] + (PV8 ? kFp8Slack : kRescaleSlack))) {
-        mt = group4_max(mt);
-        const float m_new = fmaxf(m_run[qg], mt);
-        const float alpha = fast_exp2(m_run[qg] - m_new);
-        l_run[qg] *= alpha;
-        if constexpr (PV8) {
-          // lane l holds query l % 32 of the wave in the 32x32 accumulators;
-          // both query groups are applied in one pass after this loop
-          if (((lane >> 4) & 1) == qg) al8 = alpha;
-          resc8 = true;
+          for (int j = 0; j < 16; ++j) {
+            const int tk = kbase + 32 * (j >> 3) + tl + (j & 7);
+            bool ok = tk < kv_len;
+            if constexpr (CAUSAL) ok = ok && tk <= pos;
+            x[qg][j] = ok ? x[qg][j] : kNegInf;
+            mx = fmaxf(mx, x[qg][j]);
+          }
+          mt = mx == kNegInf ? kNegInf : (mx - kOffset) * fw;
         } else {
+          mt = (__int_as_float(im) - kOffset) * fw;
+        }
+        if (exact_off) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) x[qg][j] -= kOffset;
+        }
+        // lazy rescale, tested on each lane's own maximum (see below)
+        if (__any(mt > m_run[qg] + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run[qg], group4_max(mt));
+          const float alpha = fast_exp2(m_run[qg] - m_new);
+          l_run[qg] *= alpha;
           Ls[qg] *= alpha;
 #pragma unroll
           for (int c = 0; c < CG; ++c) O[qg][c] *= alpha;
+          m_run[qg] = m_new;
         }
-        m_run[qg] = m_new;
+        // x*f + cterm = score - reference
+        cterm[qg] = -fmaf(off, fw, m_run[qg]);
       }
-      const float mref = m_run[qg];
-      // x*f + cterm = score - mref (FP8 P.V: + log2(448) - 3)
-      const float cterm = -fmaf(off, f, mref) + (PV8 ? kFp8Log2Top : 0.0f);
-      float p[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, cterm));
-      if (need_mask) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = (vis >> j) & 1u ? p[j] : 0.0f;
-      }
-      if constexpr (!kRowSumMfma) {
-        float psum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) psum += p[j];
-        l_run[qg] += psum;
-      }
-      if constexpr (VK == kVI8) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] *= sv[j];   // fold the per-token V scale into P
-      }
-      if constexpr (PV8) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
-          pk[qg][w] = (uint32_t)word;
-        }
-      } else {
-        pf[qg][0] = pack8(*reinterpret_cast<const float(*)[8]>(&p[0]));
-        pf[qg][1] = pack8(*reinterpret_cast<const float(*)[8]>(&p[8]));
-      }
-    }
-
-    // ---- O^T += V^T P^T (and the row sums against an all-ones block) ---------
-    if constexpr (PV8) {
-      if (resc8) {
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) O8[c] *= al8;
-        L8 *= al8;
-      }
-    }
-    if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(1);
-    if constexpr (PV8) {
-      // B = P^T for the wave's 32 queries: rows 0/1 of the 16-lane groups
-      // exchange with rows 2/3 so that lane l holds query l % 32 (query group
-      // (l / 16) % 2) and keys of lane groups 2*(l/32), 2*(l/32)+1 as bytes
-      // 0..15 and 16..31 (v_permlane16_swap: odd rows of the first operand
-      // trade places with even rows of the second).
-      v8i_t bop;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const auto xy = __builtin_amdgcn_permlane16_swap(pk[0][w], pk[1][w], false, false);
-        bop[w] = (int)xy[0];
-        bop[4 + w] = (int)xy[1];
-      }
-      // A = V^T: lane l reads channel 32*cb + l%32, the same key chunks (the
-      // V blocks store them swizzled by (channel / 4) % 4)
-      const uint8_t* vt = reinterpret_cast<const uint8_t*>(s_v[buf]);
-      const int hh = lane >> 5;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const int ch = 32 * cb + (lane & 31), sw = (ch >> 2) & 3;
-        const v4i lo = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh) ^ sw));
-        const v4i hi = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh + 1) ^ sw));
-        const v8i_t aop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        O8[cb] = mfma_fp8_32x32x64(aop, bop, O8[cb]);
-      }
-      const v8i_t ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                           0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-      L8 = mfma_fp8_32x32x64(ones8, bop, L8);
-    }
-    if constexpr (!DENSE) {
-      // paged: V fragments through a ring of 4 registers, 3 products ahead
-      __builtin_amdgcn_sched_barrier(0);
-      auto vfrag = [&](int i) {                    // fragment i = CG*half + c
-        const int half = i / CG, c = i % CG;
-        const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
+      // keys 0..31: O^T += V^T P^T and the row sums against an all-ones
+      // block; keys 32..63: P, scheduled in between (the two products of a
+      // channel group, then three vector instructions; measured against four
+      // and five and against no pattern). fp16 V fragments come through a
+      // ring of three registers, read two products ahead, the first two
+      // before the exponentials of keys 0..31.
+      const int so = 8 * (g & 1);
+      auto vfrag = [&](int half, int c) {
+        const int vb = 2 * half + (g >> 1);
         return *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + 16 * c + n) * 16 + so]);
       };
-      constexpr int NV = 2 * CG, AV = 3;
-      v8h vr[4];
+      v8h vr[3];
+      vr[0] = vfrag(0, 0);
+      vr[1] = vfrag(0, 1);
+      v8h pf[QG][2];
 #pragma unroll
-      for (int i = 0; i < AV; ++i) vr[i] = vfrag(i);
+      for (int qg = 0; qg < QG; ++qg) {
+        float p[8];
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (i + AV < NV) vr[(i + AV) & 3] = vfrag(i + AV);
-        const int half = i / CG, c = i % CG;
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vr[i & 3], pf[qg][half], O[qg][c]);
-        if (kRowSumMfma && c == CG - 1) {
-#pragma unroll
-          for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(x[qg][j], fw, cterm[qg]));
+        pf[qg][0] = pack8(p);
       }
-    }
-#pragma unroll
-    for (int half = 0; half < (PV8 || !DENSE ? 0 : 2); ++half) {
-      const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
+      if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
-        const int chn = 16 * c + n;
-        const v8h vf = *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + chn) * 16 + so]);
+        if (c + 2 < CG) vr[(c + 2) % 3] = vfrag(0, c + 2);
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vf, pf[qg][half], O[qg][c]);
+        for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vr[c % 3], pf[qg][0], O[qg][c]);
       }
-      if constexpr (kRowSumMfma) {
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
+      for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][0], Ls[qg]);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(x[qg][8 + j], fw, cterm[qg]));
+        pf[qg][1] = pack8(p);
+      }
+#pragma unroll
+      for (int c = 0; c <= CG; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QG, 0);  // matrix products
+        if (c < CG) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // vector instructions
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // keys 32..63
+      vr[0] = vfrag(1, 0);
+      vr[1] = vfrag(1, 1);
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        if (c + 2 < CG) vr[(c + 2) % 3] = vfrag(1, c + 2);
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vr[c % 3], pf[qg][1], O[qg][c]);
+      }
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][1], Ls[qg]);
+    } else {
+      float sk[16], sv[16];
+      if constexpr (!DENSE) {
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) sk[j] = s_ks[buf][32 * (j >> 3) + tl + (j & 7)];
+      }
+      if constexpr (VK == kVI8) {
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) sv[j] = s_vs[buf][32 * (j >> 3) + tl + (j & 7)];
+      }
+
+      // dense: one factor sQ_blk * sK_blk * scale for the whole workgroup and
+      // tile (one 128-row query block, one key block), held as a scalar; the
+      // folded accumulator offset costs half an ulp of offset*f in the
+      // exponent, so when offset*f > 2^12 (scores of large-magnitude inputs)
+      // the offset is subtracted exactly instead
+      float fw = 0.0f;
+      bool exact_off = false;
+      if constexpr (DENSE) {
+        fw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(qsc[0] * tsc)));
+        // (fw >= 0: compared as integer bits, in scalar registers)
+        exact_off = kMagic && __float_as_int(fw) > __float_as_int(4096.0f / kOffset);
+      }
+      // dense: each lane's maximum of its raw accumulators (a chain of
+      // three-input maxima; read as floats in [2^23, 2^24) they order like
+      // their bit patterns)
+      int imq[QG];
+      if constexpr (DENSE) {
+  #pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+          auto A = [&](int j) { return acc[qg][j >> 2][j & 3]; };
+          int m = max(max(A(0), A(1)), A(2));
+  #pragma unroll
+          for (int j = 3; j < 15; j += 2) m = max(max(m, A(j)), A(j + 1));
+          imq[qg] = max(m, A(15));
+        }
+      }
+      v8h pf[QG][2];
+      uint32_t pk[QG][4];                          // FP8 P.V: byte j of word w is p[4w + j]
+      float al8 = 1.0f;                            // FP8 P.V: rescale of this lane's query (32x32 layout)
+      bool resc8 = false;
+  #pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        // score_j = x[j] * f with one lane factor f >= 0 (dense: the Q and K
+        // block scales; paged: the Q scale, sK folded into x)
+        float x[16], f, mx;
+        int im = 0;
+        if constexpr (DENSE) {
+          f = fw;
+          im = imq[qg];
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) x[j] = kMagic ? __int_as_float(acc[qg][j >> 2][j & 3]) : (float)acc[qg][j >> 2][j & 3];
+          mx = kMagic ? __int_as_float(im) : (float)im;
+        } else {
+          f = qsc[qg];
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) x[j] = (float)acc[qg][j >> 2][j & 3] * sk[j];
+          mx = fmaxf(x[0], x[1]);
+  #pragma unroll
+          for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
+        }
+        uint32_t vis = 0xFFFFu;   // visible keys of this lane (bit j: the key of x[j])
+        if (need_mask) {
+          const int pos = qi[qg] + offset;
+          vis = 0;
+          mx = kNegInf;
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int tk = kbase + 32 * (j >> 3) + tl + (j & 7);
+            bool ok = tk < kv_len;
+            if constexpr (CAUSAL) ok = ok && tk <= pos;
+            vis |= ok ? 1u << j : 0u;
+            mx = ok ? fmaxf(mx, x[j]) : mx;
+          }
+        }
+        float off = kMagic ? kOffset : 0.0f;
+        if (exact_off) {
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) x[j] -= kOffset;
+          mx -= kOffset;
+          off = 0.0f;
+        }
+        // this lane's largest (visible) score
+        float mt;
+        if (DENSE && kMagic && !need_mask) mt = (__int_as_float(im) - kOffset) * f;
+        else mt = mx == kNegInf ? kNegInf : (mx - off) * f;
+        // lazy rescale: move the reference only when it is exceeded by > 2^8.
+        // A row's maximum exceeds it exactly when one of the row's lanes holds
+        // such a score, so the test needs no maximum across the lane groups;
+        // that maximum is formed only when the reference moves.
+        if (__any(mt > m_run[qg] + (PV8 ? kFp8Slack : kRescaleSlack))) {
+          mt = group4_max(mt);
+          const float m_new = fmaxf(m_run[qg], mt);
+          const float alpha = fast_exp2(m_run[qg] - m_new);
+          l_run[qg] *= alpha;
+          if constexpr (PV8) {
+            // lane l holds query l % 32 of the wave in the 32x32 accumulators;
+            // both query groups are applied in one pass after this loop
+            if (((lane >> 4) & 1) == qg) al8 = alpha;
+            resc8 = true;
+          } else {
+            Ls[qg] *= alpha;
+  #pragma unroll
+            for (int c = 0; c < CG; ++c) O[qg][c] *= alpha;
+          }
+          m_run[qg] = m_new;
+        }
+        const float mref = m_run[qg];
+        // x*f + cterm = score - mref (FP8 P.V: + log2(448) - 3)
+        const float cterm = -fmaf(off, f, mref) + (PV8 ? kFp8Log2Top : 0.0f);
+        float p[16];
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, cterm));
+        if (need_mask) {
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) p[j] = (vis >> j) & 1u ? p[j] : 0.0f;
+        }
+        if constexpr (!kRowSumMfma) {
+          float psum = 0.0f;
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) psum += p[j];
+          l_run[qg] += psum;
+        }
+        if constexpr (VK == kVI8) {
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) p[j] *= sv[j];   // fold the per-token V scale into P
+        }
+        if constexpr (PV8) {
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
+            pk[qg][w] = (uint32_t)word;
+          }
+        } else {
+          pf[qg][0] = pack8(*reinterpret_cast<const float(*)[8]>(&p[0]));
+          pf[qg][1] = pack8(*reinterpret_cast<const float(*)[8]>(&p[8]));
+        }
+      }
+
+      // ---- O^T += V^T P^T (and the row sums against an all-ones block) ---------
+      if constexpr (PV8) {
+        if (resc8) {
+  #pragma unroll
+          for (int c = 0; c < D / 32; ++c) O8[c] *= al8;
+          L8 *= al8;
+        }
+      }
+      if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(1);
+      if constexpr (PV8) {
+        // B = P^T for the wave's 32 queries: rows 0/1 of the 16-lane groups
+        // exchange with rows 2/3 so that lane l holds query l % 32 (query group
+        // (l / 16) % 2) and keys of lane groups 2*(l/32), 2*(l/32)+1 as bytes
+        // 0..15 and 16..31 (v_permlane16_swap: odd rows of the first operand
+        // trade places with even rows of the second).
+        v8i_t bop;
+  #pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const auto xy = __builtin_amdgcn_permlane16_swap(pk[0][w], pk[1][w], false, false);
+          bop[w] = (int)xy[0];
+          bop[4 + w] = (int)xy[1];
+        }
+        // A = V^T: lane l reads channel 32*cb + l%32, the same key chunks (the
+        // V blocks store them swizzled by (channel / 4) % 4)
+        const uint8_t* vt = reinterpret_cast<const uint8_t*>(s_v[buf]);
+        const int hh = lane >> 5;
+  #pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+          const int ch = 32 * cb + (lane & 31), sw = (ch >> 2) & 3;
+          const v4i lo = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh) ^ sw));
+          const v4i hi = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh + 1) ^ sw));
+          const v8i_t aop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          O8[cb] = mfma_fp8_32x32x64(aop, bop, O8[cb]);
+        }
+        const v8i_t ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                             0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+        L8 = mfma_fp8_32x32x64(ones8, bop, L8);
+      }
+      if constexpr (!DENSE) {
+        // paged: V fragments through a ring of 4 registers, 3 products ahead
+        __builtin_amdgcn_sched_barrier(0);
+        auto vfrag = [&](int i) {                    // fragment i = CG*half + c
+          const int half = i / CG, c = i % CG;
+          const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
+          return *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + 16 * c + n) * 16 + so]);
+        };
+        constexpr int NV = 2 * CG, AV = 3;
+        v8h vr[4];
+  #pragma unroll
+        for (int i = 0; i < AV; ++i) vr[i] = vfrag(i);
+  #pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          if (i + AV < NV) vr[(i + AV) & 3] = vfrag(i + AV);
+          const int half = i / CG, c = i % CG;
+  #pragma unroll
+          for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vr[i & 3], pf[qg][half], O[qg][c]);
+          if (kRowSumMfma && c == CG - 1) {
+  #pragma unroll
+            for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  #pragma unroll
+      for (int half = 0; half < (PV8 || !DENSE ? 0 : 2); ++half) {
+        const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
+  #pragma unroll
+        for (int c = 0; c < CG; ++c) {
+          const int chn = 16 * c + n;
+          const v8h vf = *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + chn) * 16 + so]);
+  #pragma unroll
+          for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vf, pf[qg][half], O[qg][c]);
+        }
+        if constexpr (kRowSumMfma) {
+  #pragma unroll
+          for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
+        }
       }
     }
     if constexpr (kPrio & 2) __builtin_amdgcn_s_setprio(0);
