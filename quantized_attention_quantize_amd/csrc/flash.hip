@@ -692,13 +692,15 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][1], Ls[qg]);
     } else {
+      // ---- paged tiles, and dense tiles with the FP8 P.V product: P of all
+      // 64 keys, then the products ----------------------------------------
       float sk[16], sv[16];
       if constexpr (!DENSE) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 16; ++j) sk[j] = s_ks[buf][32 * (j >> 3) + tl + (j & 7)];
       }
       if constexpr (VK == kVI8) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 16; ++j) sv[j] = s_vs[buf][32 * (j >> 3) + tl + (j & 7)];
       }
 
@@ -719,11 +721,11 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       // their bit patterns)
       int imq[QG];
       if constexpr (DENSE) {
-  #pragma unroll
+#pragma unroll
         for (int qg = 0; qg < QG; ++qg) {
           auto A = [&](int j) { return acc[qg][j >> 2][j & 3]; };
           int m = max(max(A(0), A(1)), A(2));
-  #pragma unroll
+#pragma unroll
           for (int j = 3; j < 15; j += 2) m = max(max(m, A(j)), A(j + 1));
           imq[qg] = max(m, A(15));
         }
@@ -732,7 +734,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       uint32_t pk[QG][4];                          // FP8 P.V: byte j of word w is p[4w + j]
       float al8 = 1.0f;                            // FP8 P.V: rescale of this lane's query (32x32 layout)
       bool resc8 = false;
-  #pragma unroll
+#pragma unroll
       for (int qg = 0; qg < QG; ++qg) {
         // score_j = x[j] * f with one lane factor f >= 0 (dense: the Q and K
         // block scales; paged: the Q scale, sK folded into x)
@@ -741,15 +743,15 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         if constexpr (DENSE) {
           f = fw;
           im = imq[qg];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) x[j] = kMagic ? __int_as_float(acc[qg][j >> 2][j & 3]) : (float)acc[qg][j >> 2][j & 3];
           mx = kMagic ? __int_as_float(im) : (float)im;
         } else {
           f = qsc[qg];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) x[j] = (float)acc[qg][j >> 2][j & 3] * sk[j];
           mx = fmaxf(x[0], x[1]);
-  #pragma unroll
+#pragma unroll
           for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(x[j], x[j + 1]));
         }
         uint32_t vis = 0xFFFFu;   // visible keys of this lane (bit j: the key of x[j])
@@ -757,7 +759,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
           const int pos = qi[qg] + offset;
           vis = 0;
           mx = kNegInf;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int tk = kbase + 32 * (j >> 3) + tl + (j & 7);
             bool ok = tk < kv_len;
@@ -768,7 +770,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         }
         float off = kMagic ? kOffset : 0.0f;
         if (exact_off) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) x[j] -= kOffset;
           mx -= kOffset;
           off = 0.0f;
@@ -793,7 +795,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
             resc8 = true;
           } else {
             Ls[qg] *= alpha;
-  #pragma unroll
+#pragma unroll
             for (int c = 0; c < CG; ++c) O[qg][c] *= alpha;
           }
           m_run[qg] = m_new;
@@ -802,24 +804,24 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         // x*f + cterm = score - mref (FP8 P.V: + log2(448) - 3)
         const float cterm = -fmaf(off, f, mref) + (PV8 ? kFp8Log2Top : 0.0f);
         float p[16];
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], f, cterm));
         if (need_mask) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) p[j] = (vis >> j) & 1u ? p[j] : 0.0f;
         }
         if constexpr (!kRowSumMfma) {
           float psum = 0.0f;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) psum += p[j];
           l_run[qg] += psum;
         }
         if constexpr (VK == kVI8) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) p[j] *= sv[j];   // fold the per-token V scale into P
         }
         if constexpr (PV8) {
-  #pragma unroll
+#pragma unroll
           for (int w = 0; w < 4; ++w) {
             int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
             word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
@@ -834,7 +836,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       // ---- O^T += V^T P^T (and the row sums against an all-ones block) ---------
       if constexpr (PV8) {
         if (resc8) {
-  #pragma unroll
+#pragma unroll
           for (int c = 0; c < D / 32; ++c) O8[c] *= al8;
           L8 *= al8;
         }
@@ -847,7 +849,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         // 0..15 and 16..31 (v_permlane16_swap: odd rows of the first operand
         // trade places with even rows of the second).
         v8i_t bop;
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < 4; ++w) {
           const auto xy = __builtin_amdgcn_permlane16_swap(pk[0][w], pk[1][w], false, false);
           bop[w] = (int)xy[0];
@@ -857,7 +859,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         // V blocks store them swizzled by (channel / 4) % 4)
         const uint8_t* vt = reinterpret_cast<const uint8_t*>(s_v[buf]);
         const int hh = lane >> 5;
-  #pragma unroll
+#pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
           const int ch = 32 * cb + (lane & 31), sw = (ch >> 2) & 3;
           const v4i lo = *reinterpret_cast<const v4i*>(vt + ch * 64 + 16 * ((2 * hh) ^ sw));
@@ -879,34 +881,19 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
         };
         constexpr int NV = 2 * CG, AV = 3;
         v8h vr[4];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < AV; ++i) vr[i] = vfrag(i);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < NV; ++i) {
           if (i + AV < NV) vr[(i + AV) & 3] = vfrag(i + AV);
           const int half = i / CG, c = i % CG;
-  #pragma unroll
+#pragma unroll
           for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vr[i & 3], pf[qg][half], O[qg][c]);
           if (kRowSumMfma && c == CG - 1) {
-  #pragma unroll
+#pragma unroll
             for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
           }
           __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-  #pragma unroll
-      for (int half = 0; half < (PV8 || !DENSE ? 0 : 2); ++half) {
-        const int vb = 2 * half + (g >> 1), so = 8 * (g & 1);
-  #pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          const int chn = 16 * c + n;
-          const v8h vf = *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + chn) * 16 + so]);
-  #pragma unroll
-          for (int qg = 0; qg < QG; ++qg) O[qg][c] = mfma_f16(vf, pf[qg][half], O[qg][c]);
-        }
-        if constexpr (kRowSumMfma) {
-  #pragma unroll
-          for (int qg = 0; qg < QG; ++qg) Ls[qg] = mfma_f16(ones, pf[qg][half], Ls[qg]);
         }
       }
     }
