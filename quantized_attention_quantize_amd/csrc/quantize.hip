@@ -34,16 +34,13 @@ __device__ __forceinline__ void store_codes(int8_t* p, uint32_t packed) {
   else *reinterpret_cast<uint8_t*>(p) = (uint8_t)packed;
 }
 
-// Quantize E values held by one lane against the wave-wide scale of its row.
+// Quantize E values held by one lane against the wave-wide scale of its row
+// (amax the row's largest |x|, s = quant_scale(amax)).
 template <int E>
 __device__ __forceinline__ uint32_t quant_lane(const float (&v)[E], float amax, float s) {
-  uint32_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    int c = amax > 0.0f ? quant_code(v[e], s) : 0;
-    packed |= ((uint32_t)c & 0xFFu) << (8 * e);
-  }
-  return packed;
+  uint32_t w[1];
+  quant_bytes<E>(v, amax, s, __fdiv_rn(1.0f, s), w);
+  return w[0];
 }
 
 // Quantize one (token, head) row of head_dim values with one wave.
@@ -108,9 +105,9 @@ __device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, con
     vmax = wave_max(vmax);
     const float sv = quant_scale(vmax);
     int8_t* vd = reinterpret_cast<int8_t*>(vc);
+    const uint32_t codes = quant_lane<E>(vv, vmax, sv);
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      vd[(bh * D + ch + e) * 16 + off] = (int8_t)(vmax > 0.0f ? quant_code(vv[e], sv) : 0);
+    for (int e = 0; e < E; ++e) vd[(bh * D + ch + e) * 16 + off] = (int8_t)(codes >> (8 * e));
     if (lane == 0) vs[bh * 16 + off] = sv;
   } else {
     uint16_t* vd = reinterpret_cast<uint16_t*>(vc);
@@ -239,8 +236,9 @@ __global__ __launch_bounds__(256) void k_write_kv_blocks(const uint16_t* __restr
       for (int e = 0; e < E; ++e) vmax = fmaxf(vmax, fabsf(vv[e]));
       vmax = wave_max(vmax);
       const float sv = quant_scale(vmax);
+      const uint32_t codes = quant_lane<E>(vv, vmax, sv);
 #pragma unroll
-      for (int e = 0; e < E; ++e) s_v[(ch + e) * 16 + j] = (uint8_t)(vmax > 0.0f ? quant_code(vv[e], sv) : 0);
+      for (int e = 0; e < E; ++e) s_v[(ch + e) * 16 + j] = (uint8_t)(codes >> (8 * e));
       if (lane == 0) s_vs[j] = sv;
     } else {
 #pragma unroll
@@ -319,10 +317,18 @@ __global__ __launch_bounds__(256) void k_block_map(Rows rows, int32_t R, int32_t
 // start of each sequence; chunks past its end hold zeros.
 // ABSMAX: the chunk's largest |fl32(x - mu[b, c])| instead of the sum (mu
 // optional), for the per-channel FP8 scale of V.
+// A workgroup covers 64 groups of 8 columns and one chunk; its four waves
+// take the chunk's rows in four interleaved slices, every row load of a thread
+// in flight at once, and meet through LDS.
+constexpr int kSumSlices = 4;
+constexpr int kSumCols = 64 * 8;   // columns per workgroup
+
 template <bool BF16, bool ABSMAX = false>
 __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, Rows rows, const int32_t* map,
                                                 int32_t D, int32_t HD, int64_t sb, int64_t st, int64_t sh,
                                                 double* __restrict__ partial, const float* __restrict__ mu = nullptr) {
+  constexpr int RPS = kSumChunk / kSumSlices;   // rows per slice
+  __shared__ double red[kSumSlices - 1][8][64];
   const int chunks = (rows.N + kSumChunk - 1) / kSumChunk;
   // batched grid (column groups, chunks, B); varlen (packed chunks, column groups)
   int b = blockIdx.z, chunk = blockIdx.y, cg = blockIdx.x;
@@ -333,14 +339,15 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
     chunk = (int)(j - rows.block0(b, kSumChunk));
     cg = blockIdx.y;
   }
-  const int c8 = (cg * 256 + threadIdx.x) * 8;
-  if (c8 >= HD) return;
+  const int sl = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c8 = (cg * 64 + lane) * 8;
+  const bool live = c8 < HD;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int t0 = chunk * kSumChunk, t1 = min(t0 + kSumChunk, rows.len(b));
   const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
-  const uint16_t* base = k + seq0 + (int64_t)(c8 / D) * sh + c8 % D;
+  const uint16_t* base = k + seq0 + (int64_t)(live ? c8 / D : 0) * sh + (live ? c8 % D : 0);
   float m8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (ABSMAX && mu != nullptr) {
+  if (ABSMAX && mu != nullptr && live) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) m8[i] = mu[(int64_t)b * HD + c8 + i];
   }
@@ -358,16 +365,27 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ k, 
       }
     }
   };
-  int t = t0;
-  // eight independent loads in flight per thread
-  for (; t + 8 <= t1; t += 8) {
-    uint4 w[8];
+  // rows t0 + sl + 4i of the slice (past the chunk: the last row, not added)
+  if (live && t1 > t0) {
+    uint4 w[RPS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(t + j) * st);
+    for (int i = 0; i < RPS; ++i)
+      w[i] = *reinterpret_cast<const uint4*>(base + (int64_t)min(t0 + sl + kSumSlices * i, t1 - 1) * st);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) add(w[j]);
+    for (int i = 0; i < RPS; ++i)
+      if (t0 + sl + kSumSlices * i < t1) add(w[i]);
   }
-  for (; t < t1; ++t) add(*reinterpret_cast<const uint4*>(base + (int64_t)t * st));
+  if (sl > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[sl - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (sl > 0 || !live) return;
+#pragma unroll
+  for (int s2 = 0; s2 < kSumSlices - 1; ++s2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = ABSMAX ? fmax(acc[i], red[s2][i][lane]) : acc[i] + red[s2][i][lane];
+  }
   double* dst = partial + ((int64_t)b * chunks + chunk) * HD + c8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dst[i] = acc[i];
@@ -516,23 +534,6 @@ __global__ __launch_bounds__(256) void k_v8_blocks(const uint16_t* __restrict__ 
   }
 }
 
-// quant_code (clamp(rne(fl32(x / s)), -127, 127)) without a division per
-// value, for |x| <= the block's max (so |x / s| <= 127 and no clamp is
-// needed): with rs = fl32(1/s), y = fl32(x * rs) lies within
-// 1.5 * 2^-23 * |x/s| <= 2.3e-5 of fl32(x / s), so the nearest integer to y
-// is the code unless y is within 6.1e-5 of a half-integer; those rare values
-// take the exact quotient. Adding 1.5 * 2^23 rounds to the nearest integer
-// (ties to even) and leaves the code in the low byte of the float's bits.
-// Callers use it only while rs is finite and below 3e38.
-__device__ __forceinline__ uint32_t quant_byte_rcp(float x, float s, float rs) {
-#pragma clang fp contract(off)
-  constexpr float kM = 12582912.0f;   // 1.5 * 2^23
-  const float y = x * rs;
-  float t = y + kM;
-  if (fabsf(y - (t - kM)) > 0.49993896484375f) t = rintf(__fdiv_rn(x, s)) + kM;
-  return __float_as_uint(t) & 0xFFu;
-}
-
 // Per-block quantization of one (b, head, block) of ROWS tokens x D channels:
 // one scale over all ROWS*D values (after subtracting mu when given).
 // Writes NHD codes (codes_nhd) and/or the blocked K layout (codes_blk).
@@ -637,7 +638,6 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
   for (int k = 0; k < PER; ++k) asm volatile("" : "+v"(wv[k].x), "+v"(wv[k].y), "+v"(wv[k].z), "+v"(wv[k].w));
   const float s = quant_scale(amax);
   const float rs = __fdiv_rn(1.0f, s);
-  const bool fast = rs <= 3.0e38f;         // workgroup-uniform
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int gi = threadIdx.x + 256 * k;
@@ -645,17 +645,9 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
     const int t = blk * ROWS + r;
     float v[8];
     values(k, v);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t c0 = 0, c1 = 0;
-      if (amax > 0.0f) {
-        c0 = fast ? quant_byte_rcp(v[i], s, rs) : (uint32_t)quant_code(v[i], s) & 0xFFu;
-        c1 = fast ? quant_byte_rcp(v[4 + i], s, rs) : (uint32_t)quant_code(v[4 + i], s) & 0xFFu;
-      }
-      lo |= c0 << (8 * i);
-      hi |= c1 << (8 * i);
-    }
+    uint32_t w[2];
+    quant_bytes<8>(v, amax, s, rs, w);
+    uint32_t lo = w[0], hi = w[1];
     if (t >= N) lo = hi = 0;
     if (codes_nhd != nullptr && t < N)
       *reinterpret_cast<uint2*>(codes_nhd + ((rows.start(b) + t) * H + h) * D + c) = make_uint2(lo, hi);
@@ -666,6 +658,95 @@ __global__ __launch_bounds__(256) void k_block_quant(const uint16_t* __restrict_
         *reinterpret_cast<uint2*>(codes_blk + ((pb * H + h) * (D / 16) + c / 16) * 256 + (t % 16) * 16 + (c % 16)) =
             make_uint2(lo, hi);
     }
+  }
+  if (threadIdx.x == 0) scale[rows.scale_at(b, h, H, blk, ROWS)] = s;
+}
+
+// K blocks of 64 tokens straight into the blocked layout
+// [block16][head][D/16][16 tokens][16 channels]: the codes, scale and mean
+// handling of k_block_quant<D, 64> (codes_blk only), with each thread unit 16
+// channels of one token (two 16-byte loads, one 16-byte store) placed so that
+// the 64 lanes of a wave write 16 token slots of four neighbouring 16-channel
+// chunks, 1 KB of contiguous codes (eight-byte units 256 bytes apart wrote
+// 16-byte pieces).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_kblock_quant(const uint16_t* __restrict__ x, Rows rows,
+                                                      const int32_t* map, int32_t H, int64_t sb, int64_t st,
+                                                      int64_t sh, const float* __restrict__ mean,
+                                                      int8_t* __restrict__ codes_blk, float* __restrict__ scale) {
+  constexpr int ROWS = 64, CH = D / 16;          // 16-channel chunks per row
+  constexpr int PER = ROWS * CH / 256;           // units per thread
+  static_assert(ROWS * CH % 256 == 0 && 256 % (16 * CH) == 0, "units must tile the workgroup");
+  const BlockRef br = block_of(rows, map, ROWS, blockIdx.z);
+  if (br.b < 0) return;
+  const int blk = br.blk, h = head_of(rows), b = br.b;
+  const int N = rows.len(b);
+  if (blk * ROWS >= N) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seq0 = rows.packed ? rows.start(b) * st : (int64_t)b * sb;
+  __shared__ float red[4];
+  // unit u = threadIdx.x + 256 k: token slot u % 16 of 16-row group u / (16 CH),
+  // chunk (u / 16) % CH (the same chunk for every k of a thread)
+  const int slot = threadIdx.x % 16, cc = (threadIdx.x / 16) % CH;
+  uint4 wv[PER][2];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int r = ((threadIdx.x + 256 * k) / (16 * CH)) * 16 + slot;
+    const int t = min(blk * ROWS + r, N - 1);
+    const uint16_t* src = x + seq0 + (int64_t)t * st + (int64_t)h * sh + cc * 16;
+    wv[k][0] = *reinterpret_cast<const uint4*>(src);
+    wv[k][1] = *reinterpret_cast<const uint4*>(src + 8);
+  }
+  float mu[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mu[i] = mean != nullptr ? mean[((int64_t)b * H + h) * D + cc * 16 + i] : 0.0f;
+  auto values = [&](int k, float (&v)[16]) {
+    const int t = blk * ROWS + ((threadIdx.x + 256 * k) / (16 * CH)) * 16 + slot;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t ws[4] = {wv[k][q].x, wv[k][q].y, wv[k][q].z, wv[k][q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * q + 2 * i] = half_to_f32<BF16>(ws[i] & 0xFFFFu) - mu[8 * q + 2 * i];
+        v[8 * q + 2 * i + 1] = half_to_f32<BF16>(ws[i] >> 16) - mu[8 * q + 2 * i + 1];
+      }
+    }
+    if (t >= N) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+  };
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    float v[16];
+    values(k, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // the fp32 values are formed again below rather than kept
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) asm volatile("" : "+v"(wv[k][q].x), "+v"(wv[k][q].y), "+v"(wv[k][q].z), "+v"(wv[k][q].w));
+  const float s = quant_scale(amax);
+  const float rs = __fdiv_rn(1.0f, s);
+  const int nb16 = (N + 15) / 16;                // 16-token blocks of the sequence
+  const int64_t pb0 = rows.block0(b, 16) + blk * (ROWS / 16);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int g16 = (threadIdx.x + 256 * k) / (16 * CH);
+    float v[16];
+    values(k, v);
+    uint32_t w[4];
+    quant_bytes<16>(v, amax, s, rs, w);
+    if (blk * (ROWS / 16) + g16 < nb16)
+      *reinterpret_cast<uint4*>(codes_blk + (((pb0 + g16) * H + h) * CH + cc) * 256 + slot * 16) =
+          make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (threadIdx.x == 0) scale[rows.scale_at(b, h, H, blk, ROWS)] = s;
 }
@@ -766,7 +847,7 @@ template <int D, bool BF16>
 hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
   const int HD = a.Hkv * D;
   const int chunks = (a.Nk + kSumChunk - 1) / kSumChunk;
-  const int cgs = (HD / 8 + 255) / 256;   // column groups of the sums
+  const int cgs = (HD + kSumCols - 1) / kSumCols;   // column groups of the sums
   const bool vl = a.k_rows.packed;
   // varlen grids run over the packed blocks of all sequences (block maps first)
   auto grid = [&](const Rows& r, int R, int heads) {
@@ -791,9 +872,14 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
         a.k_mean, a.Hq / a.Hkv, a.corr_scale, corr);
   }
   if (a.Nk > 0) {
-    k_block_quant<D, 64, BF16><<<grid(a.k_rows, 64, a.Hkv), 256, 0, s>>>(
-        (const uint16_t*)a.k, a.k_rows, a.k_map64, a.Hkv, a.k_sb, a.k_st, a.k_sh, a.k_mean, a.k_i8, a.k_paged,
-        a.k_scale, nullptr, 1, 0.0f, nullptr);
+    if (a.k_i8 == nullptr && a.k_paged != nullptr)
+      k_kblock_quant<D, BF16><<<grid(a.k_rows, 64, a.Hkv), 256, 0, s>>>(
+          (const uint16_t*)a.k, a.k_rows, a.k_map64, a.Hkv, a.k_sb, a.k_st, a.k_sh, a.k_mean, a.k_paged,
+          a.k_scale);
+    else
+      k_block_quant<D, 64, BF16><<<grid(a.k_rows, 64, a.Hkv), 256, 0, s>>>(
+          (const uint16_t*)a.k, a.k_rows, a.k_map64, a.Hkv, a.k_sb, a.k_st, a.k_sh, a.k_mean, a.k_i8, a.k_paged,
+          a.k_scale, nullptr, 1, 0.0f, nullptr);
     if (a.v_paged != nullptr || a.v8 != nullptr) {
       if (a.smooth_v) {
         // the column sums of K are consumed: the buffer takes those of V
