@@ -232,10 +232,16 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
     pa.q_map = (int32_t*)(ws + w.q_map); pa.k_map64 = (int32_t*)(ws + w.k_map64);
     pa.k_map16 = (int32_t*)(ws + w.k_map16);
   }
+  // the attention kernel quantizes its own query block (one workgroup, one
+  // 128-row block of one head) unless the LSE correction needs the separate pass
+  pa.skip_q = pa.lse_corr == nullptr;
   qa_status_t st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
   if (st != QA_OK) return st;
   qa::FlashArgs a{};
   a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
+  if (pa.skip_q) {
+    a.q_in = (const uint16_t*)q; a.q_sb = c.sq.b; a.q_st = c.sq.t; a.q_sh = c.sq.h; a.q_in_bf16 = c.bf16;
+  }
   if (c.pv_fp8) { a.v_blocks = pa.v8; a.v8_scale = pa.v8_scale; a.pv_fp8 = true; }
   a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;
   a.o_sb = c.so.b; a.o_st = c.so.t; a.o_sh = c.so.h;

@@ -11,7 +11,10 @@
 // come from this library's own preprocessing, already in the LDS layout with
 // fp16 V, and are copied global -> LDS directly (global_load_lds_dwordx4),
 // which frees the staging registers for a third wave per SIMD. One barrier
-// per tile.
+// per tile. A dense workgroup's 128 query rows are one query block of the
+// per-block quantization ([SAGE-MACA]): the kernel quantizes it from the
+// 16-bit queries in its prologue (the preprocessing then skips the query
+// pass), with the block quantizer's arithmetic.
 //
 // Matrix products are computed transposed, as in the decode kernel:
 //   S^T = K Q^T   (v_mfma_i32_16x16x64_i8; A = 16 keys from LDS, B = 16 queries
@@ -40,6 +43,7 @@
 // same K/V) are assigned to the same XCD and share its L2.
 #include "common.h"
 #include "internal.h"
+#include "quant.h"
 
 namespace qa {
 namespace {
@@ -102,6 +106,71 @@ struct Staged {
   v4i v[VWS ? 1 : VU];    // partial-round guards left an array in memory
   float ks, vs;
 };
+
+// A dense workgroup's query block (128 rows of head h from row r0 of its
+// sequence; rows past the sequence count as zeros), quantized in the kernel
+// as the block quantizer does it: one scale over the block, quant_scale of
+// its largest |x|, and the codes of quant_bytes. Lane (n, g) of a wave
+// loads the 16-bit values of its fragments (row qi[qg], channels 64s + 16g
+// .. +15) and receives their codes; the block maximum meets in s_red (one
+// float per wave). Returns the block's scale.
+template <int D, int QG, int NW, bool BF16>
+__device__ __forceinline__ float quant_q_block(const FlashArgs& a, int64_t qseq, int h, int Tq,
+                                               const int (&qi)[QG], v4i (&qf)[QG][D / 64], float* s_red) {
+  constexpr int KS = D / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
+  uint4 raw[QG][KS][2];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const bool ok = qi[qg] < Tq;
+    const uint16_t* src = a.q_in + qseq + (int64_t)min(qi[qg], Tq - 1) * a.q_st + (int64_t)h * a.q_sh + 16 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      raw[qg][s][0] = ok ? *reinterpret_cast<const uint4*>(src + 64 * s) : make_uint4(0, 0, 0, 0);
+      raw[qg][s][1] = ok ? *reinterpret_cast<const uint4*>(src + 64 * s + 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  auto vals = [&](int qg, int s, float (&v)[16]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t ws[4] = {raw[qg][s][q].x, raw[qg][s][q].y, raw[qg][s][q].z, raw[qg][s][q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * q + 2 * i] = half_to_f32<BF16>(ws[i] & 0xFFFFu);
+        v[8 * q + 2 * i + 1] = half_to_f32<BF16>(ws[i] >> 16);
+      }
+    }
+  };
+  float am = 0.0f;
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float v[16];
+      vals(qg, s, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+    }
+  am = wave_max(am);
+  if (lane == 0) s_red[wave] = am;
+  __syncthreads();
+  am = s_red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) am = fmaxf(am, s_red[w]);
+  const float sc = quant_scale(am);
+  const float rs = __fdiv_rn(1.0f, sc);
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float v[16];
+      vals(qg, s, v);
+      uint32_t w[4];
+      quant_bytes<16>(v, am, sc, rs, w);
+      qf[qg][s] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  return sc;
+}
 
 // NW waves per workgroup, each with QG groups of 16 query rows. Paged
 // prefill packs the G query heads of one KV head into the rows ([QK-MMAC]
@@ -230,6 +299,7 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
     qi[qg] = DENSE ? r : r / G;
     qh[qg] = DENSE ? hu_ : kvh * G + (r - qi[qg] * G);
     const bool ok = qi[qg] < Tq;
+    if (DENSE && a.q_in != nullptr) continue;   // quantized below
     const int8_t* qp = a.q + ((q_row0 + qi[qg]) * Hq + qh[qg]) * D + 16 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -239,6 +309,18 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       qsc[qg] = a.q_scale[a.q_rows.scale_at(z, qh[qg], Hq, min(qi[qg] / 128, nqb - 1), 128)] * a.scale_log2;
     } else {
       qsc[qg] = ok ? a.q_scale[(q_row0 + qi[qg]) * Hq + qh[qg]] * a.scale_log2 : 0.0f;
+    }
+  }
+  if constexpr (DENSE) {
+    if (a.q_in != nullptr) {
+      // the workgroup's rows are one 128-row query block of head hu_
+      static_assert(QT == 128, "a dense workgroup holds one query block");
+      __shared__ float s_qred[NW];
+      const int64_t qseq = a.q_rows.packed ? (int64_t)a.q_rows.start(z) * a.q_st : (int64_t)z * a.q_sb;
+      const float sq = a.q_in_bf16 ? quant_q_block<D, QG, NW, true>(a, qseq, hu_, Tq, qi, qf, s_qred)
+                                   : quant_q_block<D, QG, NW, false>(a, qseq, hu_, Tq, qi, qf, s_qred);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) qsc[qg] = sq * a.scale_log2;
     }
   }
   const int wq_first = (r0 + wave * 16 * QG) / G;   // first query token of this wave

@@ -100,6 +100,7 @@ struct SagePrepArgs {
   bool smooth_v;          // subtract the per-channel V mean (v_mean) in the V blocks
   float* v_mean;          // [B, Hkv, D] (smooth_v)
   float* lse_corr;        // q_rows.row_at layout: smooth_k correction of the LSE, or nullptr
+  bool skip_q;            // the attention kernel quantizes the query blocks itself
   float corr_scale;       // softmax scale (natural-log units) for lse_corr
   int8_t* q_i8;           // NHD codes
   float* q_scale;         // q_rows.scale_at(.., 128) layout
@@ -189,6 +190,12 @@ struct FlashArgs {
   bool dense, causal, v_int8, v_f16, out_bf16, out_f16;
   bool pv_fp8;             // dense: FP8 P.V (head_dim 64 or 128)
   void* v_ws;              // paged: workspace for the fp16 V blocks [seq][max_blocks][Hkv][D][16], or nullptr
+  // dense: the 16-bit queries themselves, quantized per 128-row block by the
+  // attention kernel (q and q_scale unused), element (b, t, h, c) at
+  // b*q_sb + t*q_st + h*q_sh + c (varlen: (start(b) + t)*q_st + h*q_sh + c); or nullptr
+  const uint16_t* q_in;
+  int64_t q_sb, q_st, q_sh;
+  bool q_in_bf16;
 };
 hipError_t launch_flash(const FlashArgs& a, hipStream_t st);
 

@@ -4,6 +4,7 @@
 // clamp(rne(fl32(x / s)), -127, 127), with correctly rounded fp32 divisions.
 // A zero row gets s = 0 and zero codes.
 #include "common.h"
+#include "quant.h"
 #include "internal.h"
 
 namespace qa {
@@ -24,48 +25,6 @@ __device__ __forceinline__ void load_halves(const uint16_t* p, float (&v)[E]) {
     v[1] = half_to_f32<BF16>(w >> 16);
   } else {
     v[0] = half_to_f32<BF16>(*p);
-  }
-}
-
-// The codes of N values of one block or row against its scale s (amax = the
-// largest |x| of the block, s = quant_scale(amax)), packed as bytes into
-// ceil(N/4) words, the same codes as quant_code. For amax > 0 and rs =
-// fl32(1/s) finite and below 3e38 there is no division per value: |x/s| <=
-// 127 needs no clamp, and y = fl32(x * rs) lies within 1.5 * 2^-23 * |x/s|
-// <= 2.3e-5 of fl32(x / s), so the nearest integer to y is the code unless y
-// is within 6.1e-5 of a half-integer; when one of the N values is, all N
-// take the exact quotient (one branch per N values, rarely taken). Adding
-// 1.5 * 2^23 rounds to the nearest integer (ties to even) and leaves the
-// code in the low byte of the float's bits. amax = 0 gives zero codes.
-template <int N>
-__device__ __forceinline__ void quant_bytes(const float (&x)[N], float amax, float s, float rs,
-                                            uint32_t (&w)[(N + 3) / 4]) {
-#pragma clang fp contract(off)
-  constexpr float kM = 12582912.0f;   // 1.5 * 2^23
-  float t[N];
-  if (amax > 0.0f && rs <= 3.0e38f) {
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const float y = x[i] * rs;
-      t[i] = y + kM;
-      bad |= fabsf(y - (t[i] - kM)) > 0.49993896484375f;
-    }
-    if (bad) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) t[i] = rintf(__fdiv_rn(x[i], s)) + kM;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) t[i] = (float)(amax > 0.0f ? quant_code(x[i], s) : 0) + kM;
-  }
-#pragma unroll
-  for (int q = 0; q < (N + 3) / 4; ++q) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * q + i < N) v |= (__float_as_uint(t[4 * q + i]) & 0xFFu) << (8 * i);
-    w[q] = v;
   }
 }
 
@@ -906,7 +865,7 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
     k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.k, a.k_rows, a.k_map64, D, HD, a.k_sb, a.k_st, a.k_sh,
                                         a.partial);
   k_mean<<<gmean, 256, 0, s>>>(a.partial, a.k_rows, HD, a.smooth_k, a.k_mean);
-  if (a.Nq > 0) {
+  if (a.Nq > 0 && !a.skip_q) {
     float* corr = a.smooth_k ? a.lse_corr : nullptr;
     auto qk = corr != nullptr ? k_block_quant<D, 128, BF16, true> : k_block_quant<D, 128, BF16, false>;
     qk<<<grid(a.q_rows, 128, a.Hq), 256, 0, s>>>(
