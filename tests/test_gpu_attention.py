@@ -660,6 +660,30 @@ def test_dense_options_parity(qa, case, smooth_v, smooth_k):
         assert torch.equal(plain, out_n)
 
 
+@pytest.mark.parametrize("pv_fp8", [False, True])
+@pytest.mark.parametrize("case", [(2, 300, 257, 4, 2, 128, "bf16", True), (1, 200, 333, 2, 2, 64, "f16", False),
+                                  (1, 129, 400, 6, 1, 256, "f16", True), (2, 1, 70, 2, 1, 128, "bf16", False)],
+                         ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{c[6]}_{'causal' if c[7] else 'full'}")
+def test_dense_query_blocks_in_kernel(qa, case, pv_fp8):
+    """The attention kernel quantizes its 128-row query blocks itself, except
+    when the smooth_k LSE correction asks for the separate query pass (whose
+    codes the preprocessing tests pin to the oracle's bit for bit); the LSE
+    output changes nothing else, so both calls give the same output bit for
+    bit."""
+    B, Nq, Nk, Hq, Hkv, d, dt, causal = case
+    if pv_fp8 and d > 128:
+        pytest.skip("FP8 P.V: head_dim 64 or 128")
+    say(f"dense query blocks in the kernel {case} pv_fp8={pv_fp8}")
+    spec = DenseSpec("dn_qk", 733 + d, B, Hq, Hkv, Nq, Nk, d, k_bias_std=3.0, dtype=dt)
+    inp = dense_inputs(spec)
+    q, k, v = dev_bits(inp.q, dt), dev_bits(inp.k, dt), dev_bits(inp.v, dt)
+    fused = qa.dense_sage_attention_ex(q, k, v, is_causal=causal, smooth_k=True, pv_fp8=pv_fp8)
+    separate, _ = qa.dense_sage_attention_ex(q, k, v, is_causal=causal, smooth_k=True, pv_fp8=pv_fp8,
+                                             return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, separate)
+
+
 def test_dense_options_full_size_sampled(qa):
     """The dense workload (2 x 8192 x 32 heads, d 128) through the options
     call in HND with smooth_v and the LSE, sampled rows and heads against the
