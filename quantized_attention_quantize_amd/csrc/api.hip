@@ -235,12 +235,18 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
   // the attention kernel quantizes its own query block (one workgroup, one
   // 128-row block of one head) unless the LSE correction needs the separate pass
   pa.skip_q = pa.lse_corr == nullptr;
+  // fp16 V without smooth_v, batched, whole 64-key tiles: the attention
+  // kernel copies V tiles in token order (no V block pass)
+  pa.skip_v = !c.bf16 && !pa.smooth_v && !c.pv_fp8 && !c.q.packed && c.k.N > 0 && c.k.N % 64 == 0;
   qa_status_t st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
   if (st != QA_OK) return st;
   qa::FlashArgs a{};
   a.q = pa.q_i8; a.q_scale = pa.q_scale; a.k_blocks = pa.k_paged; a.k_scale = pa.k_scale; a.v_blocks = pa.v_paged;
   if (pa.skip_q) {
     a.q_in = (const uint16_t*)q; a.q_sb = c.sq.b; a.q_st = c.sq.t; a.q_sh = c.sq.h; a.q_in_bf16 = c.bf16;
+  }
+  if (pa.skip_v) {
+    a.v_tok = (const uint16_t*)v; a.v_sb = c.sk.b; a.v_st = c.sk.t; a.v_sh = c.sk.h;
   }
   if (c.pv_fp8) { a.v_blocks = pa.v8; a.v8_scale = pa.v8_scale; a.pv_fp8 = true; }
   a.v_scale = nullptr; a.tables = nullptr; a.cu_q = nullptr; a.ctx_lens = nullptr; a.out = out;

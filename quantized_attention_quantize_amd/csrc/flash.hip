@@ -14,7 +14,10 @@
 // per tile. A dense workgroup's 128 query rows are one query block of the
 // per-block quantization ([SAGE-MACA]): the kernel quantizes it from the
 // 16-bit queries in its prologue (the preprocessing then skips the query
-// pass), with the block quantizer's arithmetic.
+// pass), with the block quantizer's arithmetic. With fp16 V (no smooth_v,
+// whole 64-key tiles) the dense kernel copies V tiles in token order from
+// the input itself and forms its P.V operands with transposing LDS reads,
+// so the preprocessing has no V pass either.
 //
 // Matrix products are computed transposed, as in the decode kernel:
 //   S^T = K Q^T   (v_mfma_i32_16x16x64_i8; A = 16 keys from LDS, B = 16 queries
@@ -107,6 +110,40 @@ struct Staged {
   float ks, vs;
 };
 
+// V tiles in token order (dense, 16-bit V input without a transpose pass):
+// a 64-key tile of D channels is D/8 copies of 1 KB (chunks), each of 512/D
+// token rows of D*2 bytes. A P.V operand comes from transposing reads
+// (ds_read_b64_tr_b16: lane i of a 16-lane group receives element i%4 of the
+// 8-byte reads of lanes 4j + i/4, j = 0..3), four token rows x 16 channels
+// per group; the two groups of a half-wave read rows R + j and R + 8 + j
+// (j = 0..3, R = 32h + 16p + t0). Row r = 32h + 16p + 8b + 4c + j has the
+// level L = 4b + j, and chunk q = L*D/64 + k starts at q*1024 + 32*L bytes:
+// the eight rows of a read pass sit on eight levels (disjoint 32-byte bank
+// spans) and the chunks, whose offsets never decrease, do not overlap.
+template <int D>
+constexpr int kVtokChunks = D / 8;
+template <int D>
+__device__ __forceinline__ uint32_t vtok_chunk(int q) {
+  return (uint32_t)q * 1024u + 32u * (uint32_t)(q / (D / 64));
+}
+// byte offset of token row r in a tile buffer
+template <int D>
+__device__ __forceinline__ uint32_t vtok_row_off(int r) {
+  constexpr int CPL = D / 64, RPC = 512 / D;   // chunks per level, rows per chunk
+  const int L = 4 * ((r >> 3) & 1) + (r & 3);
+  const int idx = 4 * (r >> 5) + 2 * ((r >> 4) & 1) + ((r >> 2) & 1);
+  return vtok_chunk<D>(L * CPL + idx / RPC) + (uint32_t)((idx % RPC) * D * 2);
+}
+// the token row that lane lam of chunk q's copy takes (D/8 lanes per row)
+template <int D>
+__device__ __forceinline__ int vtok_dma_row(int q, int lam) {
+  constexpr int CPL = D / 64, RPC = 512 / D, LPR = D / 8;
+  const int L = q / CPL, idx = (q % CPL) * RPC + lam / LPR;
+  return 32 * (idx >> 2) + 16 * ((idx >> 1) & 1) + 8 * (L >> 2) + 4 * (idx & 1) + (L & 3);
+}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+
 // A dense workgroup's query block (128 rows of head h from row r0 of its
 // sequence; rows past the sequence count as zeros), quantized in the kernel
 // as the block quantizer does it: one scale over the block, quant_scale of
@@ -183,7 +220,8 @@ __device__ __forceinline__ float quant_q_block(const FlashArgs& a, int64_t qseq,
 // VWS (paged): V tiles come as fp16 blocks from the per-call workspace that
 // k_v16_blocks fills (the LDS layout already), copied straight into LDS
 // instead of staged and converted by every workgroup.
-template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL, bool PV8 = false, bool VWS = false>
+template <int D, int QG, int NW, int VK, bool DENSE, bool CAUSAL, bool PV8 = false, bool VWS = false,
+          bool VTOK = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 4))) void k_flash(
     FlashArgs a) {
@@ -211,7 +249,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   constexpr int kAcc0 = kMagic ? 0x4B400000 : 0;                            // bit pattern of 1.5 * 2^23
   constexpr float kOffset = 12582912.0f;                                     // 1.5 * 2^23
   __shared__ __attribute__((aligned(16))) int8_t s_k[2][4 * KBS];
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][KT * D];
+  // VTOK: V tiles in token order (see vtok_chunk), 256 bytes of bank offsets more
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][KT * D + (VTOK ? 128 : 0)];
   __shared__ float s_ks[DENSE ? 1 : 2][KT];
   __shared__ float s_vs[DENSE ? 1 : 2][KT];
   // With 12 waves the query fragments are parked in LDS (each lane re-reads
@@ -508,6 +547,21 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   // (scalar arithmetic, no 64 x 64-bit products per copy).
   const int8_t* kseq = a.k_blocks + blk_base * k_blk + k_head;
   const uint8_t* vseq = reinterpret_cast<const uint8_t*>(a.v_blocks) + (blk_base * k_blk + k_head) * 2;
+  // VTOK: this (sequence, KV head)'s 16-bit V rows; lane l of chunk q's copy
+  // takes 16 bytes of token row vtok_dma_row(q, l) of the tile
+  const uint8_t* vtok_seq = nullptr;
+  uint32_t vtok_row = 0;
+  uint32_t vtok_off[VTOK ? (kVtokChunks<D> + NW - 1) / NW : 1];
+  if constexpr (VTOK) {
+    vtok_seq = reinterpret_cast<const uint8_t*>(a.v_tok) + ((int64_t)z * a.v_sb + (int64_t)kvh * a.v_sh) * 2;
+    vtok_row = (uint32_t)(a.v_st * 2);
+    constexpr int LPR = D / 8;                     // lanes per token row
+#pragma unroll
+    for (int i = 0; i < (kVtokChunks<D> + NW - 1) / NW; ++i) {
+      const int q = wave_s + NW * i;
+      vtok_off[i] = (uint32_t)vtok_dma_row<D>(min(q, kVtokChunks<D> - 1), lane) * vtok_row + (uint32_t)(lane % LPR) * 16u;
+    }
+  }
   auto dma = [&](int buf, int tile) {
     constexpr int KC = D / 64;                     // 1 KB chunks per K block (per head)
     constexpr int VC = D / 32;                     // 1 KB chunks per V block (per head)
@@ -538,10 +592,22 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       }
     }
 #pragma unroll
-    for (int i = 0; i < (PV8 ? 0 : (4 * VC + NW - 1) / NW); ++i) {
+    for (int i = 0; i < (PV8 || VTOK ? 0 : (4 * VC + NW - 1) / NW); ++i) {
       const int c = wave_s + NW * i, b = c / VC, part = c % VC;
       if (4 * VC % NW != 0 && c >= 4 * VC) break;   // wave-uniform
       copy16_to_lds(vseq + 2 * blk(b) + part * 1024, lane16, sv_lds + (uint32_t)(buf * KT * D * 2 + b * D * 32 + part * 1024));
+    }
+    if constexpr (VTOK) {
+      // chunk q of the tile's 16-bit V rows (the tile is clamped to the last
+      // one, as the K blocks are)
+      const int t = min(tile, (kv_len + KT - 1) / KT - 1);
+      const uint8_t* src = vtok_seq + (uint64_t)(uint32_t)(t * KT) * vtok_row;
+#pragma unroll
+      for (int i = 0; i < (kVtokChunks<D> + NW - 1) / NW; ++i) {
+        const int q = wave_s + NW * i;
+        if (kVtokChunks<D> % NW != 0 && q >= kVtokChunks<D>) break;   // wave-uniform
+        copy16_to_lds(src, vtok_off[i], sv_lds + (uint32_t)(buf * (KT * D * 2 + 256)) + vtok_chunk<D>(q));
+      }
     }
   };
   constexpr bool kDma = DENSE;
@@ -724,9 +790,24 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       // ring of three registers, read two products ahead, the first two
       // before the exponentials of keys 0..31.
       const int so = 8 * (g & 1);
-      auto vfrag = [&](int half, int c) {
-        const int vb = 2 * half + (g >> 1);
-        return *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + 16 * c + n) * 16 + so]);
+      auto vfrag = [&](int half, int c) -> v8h {
+        if constexpr (VTOK) {
+          // channel 16c + n, keys 32 half + 8g + 0..7: two transposing reads,
+          // each of four token rows x 16 channels of the lane's 16-lane group
+          const int row = 32 * half + 8 * g + (n >> 2), col = 16 * c + 4 * (n & 3);
+          const char* b0 = reinterpret_cast<const char*>(&s_v[buf][0]);
+          // (the results are taken as whole 32-bit words: built element by
+          // element from the 16-bit results, the operand came out wrong)
+          auto rd = [&](int r) {
+            return __builtin_bit_cast(v2i32, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(b0 + vtok_row_off<D>(r) + col * 2)));
+          };
+          const v2i32 lo = rd(row), hi = rd(row + 4);
+          return __builtin_bit_cast(v8h, v4i{lo[0], lo[1], hi[0], hi[1]});
+        } else {
+          const int vb = 2 * half + (g >> 1);
+          return *reinterpret_cast<const v8h*>(&s_v[buf][(vb * D + 16 * c + n) * 16 + so]);
+        }
       };
       v8h vr[3];
       vr[0] = vfrag(0, 0);
@@ -1112,6 +1193,8 @@ hipError_t run_flash(const FlashArgs& a, hipStream_t st) {
   if constexpr (PV8) {
     if constexpr (QG == 2 && D <= 128) k_flash<D, QG, NW, VK, DENSE, CAUSAL, true><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
     else return hipErrorInvalidValue;    // FP8 P.V needs two query groups per wave
+  } else if (DENSE && a.v_tok != nullptr) {
+    k_flash<D, QG, NW, VK, DENSE, CAUSAL, false, false, DENSE><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
   } else {
     k_flash<D, QG, NW, VK, DENSE, CAUSAL, false, VWS><<<dim3((unsigned)total), NW * 64, 0, st>>>(a);
   }

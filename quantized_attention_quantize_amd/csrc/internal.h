@@ -101,6 +101,7 @@ struct SagePrepArgs {
   float* v_mean;          // [B, Hkv, D] (smooth_v)
   float* lse_corr;        // q_rows.row_at layout: smooth_k correction of the LSE, or nullptr
   bool skip_q;            // the attention kernel quantizes the query blocks itself
+  bool skip_v;            // the attention kernel reads V in token order itself
   float corr_scale;       // softmax scale (natural-log units) for lse_corr
   int8_t* q_i8;           // NHD codes
   float* q_scale;         // q_rows.scale_at(.., 128) layout
@@ -196,6 +197,11 @@ struct FlashArgs {
   const uint16_t* q_in;
   int64_t q_sb, q_st, q_sh;
   bool q_in_bf16;
+  // dense: the fp16 V input read by the attention kernel in token order (no
+  // V block pass; batched, Nk a multiple of 64, no smooth_v), element
+  // (b, t, h, c) at b*v_sb + t*v_st + h*v_sh + c; or nullptr
+  const uint16_t* v_tok;
+  int64_t v_sb, v_st, v_sh;
 };
 hipError_t launch_flash(const FlashArgs& a, hipStream_t st);
 

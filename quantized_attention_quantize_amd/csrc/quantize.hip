@@ -881,7 +881,7 @@ hipError_t sage_prep_d(const SagePrepArgs& a, hipStream_t s) {
       k_block_quant<D, 64, BF16><<<grid(a.k_rows, 64, a.Hkv), 256, 0, s>>>(
           (const uint16_t*)a.k, a.k_rows, a.k_map64, a.Hkv, a.k_sb, a.k_st, a.k_sh, a.k_mean, a.k_i8, a.k_paged,
           a.k_scale, nullptr, 1, 0.0f, nullptr);
-    if (a.v_paged != nullptr || a.v8 != nullptr) {
+    if ((a.v_paged != nullptr || a.v8 != nullptr) && !a.skip_v) {
       if (a.smooth_v) {
         // the column sums of K are consumed: the buffer takes those of V
         k_colsum<BF16><<<gsum, 256, 0, s>>>((const uint16_t*)a.v, a.k_rows, a.k_map64, D, HD, a.v_sb, a.v_st,

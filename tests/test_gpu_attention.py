@@ -684,6 +684,32 @@ def test_dense_query_blocks_in_kernel(qa, case, pv_fp8):
     assert torch.equal(fused, separate)
 
 
+@pytest.mark.parametrize("case", [(2, 200, 256, 4, 2, 128, True), (1, 130, 512, 2, 2, 64, False),
+                                  (1, 129, 192, 6, 1, 256, True), (2, 64, 64, 2, 1, 128, False)],
+                         ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{'causal' if c[6] else 'full'}")
+def test_dense_token_order_v(qa, case):
+    """fp16 V, no smooth_v, whole 64-key tiles: the attention kernel copies V
+    tiles in token order and forms its P.V operands with transposing LDS
+    reads (no V block pass). Each sequence's output must equal, bit for bit,
+    that of a one-sequence varlen call (which takes the V block pass: the
+    same fp16 values in the other layout), and match the oracle."""
+    B, Nq, Nk, Hq, Hkv, d, causal = case
+    say(f"dense token-order V {case}")
+    spec = DenseSpec("dn_vt", 877 + d, B, Hq, Hkv, Nq, Nk, d, k_bias_std=3.0, dtype="f16")
+    inp = dense_inputs(spec)
+    q, k, v = dev_bits(inp.q, "f16"), dev_bits(inp.k, "f16"), dev_bits(inp.v, "f16")
+    out = qa.dense_sage_attention(q, k, v, is_causal=causal)
+    for b in range(B):
+        cq = torch.tensor([0, Nq], dtype=torch.int32, device="cuda")
+        ck = torch.tensor([0, Nk], dtype=torch.int32, device="cuda")
+        one = qa.dense_sage_attention_varlen(q[b].contiguous(), k[b].contiguous(), v[b].contiguous(), cq, ck, Nq, Nk,
+                                             is_causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(one, out[b]), f"sequence {b}"
+    want = oracle.sage_forward(inp.q, inp.k, inp.v, "f16", causal=causal)
+    assert_close(out.cpu().numpy(), want, "dense token-order V")
+
+
 def test_dense_options_full_size_sampled(qa):
     """The dense workload (2 x 8192 x 32 heads, d 128) through the options
     call in HND with smooth_v and the LSE, sampled rows and heads against the
