@@ -235,9 +235,9 @@ qa_status_t run_dense(const DenseCall& c, const void* q, const void* k, const vo
   // the attention kernel quantizes its own query block (one workgroup, one
   // 128-row block of one head) unless the LSE correction needs the separate pass
   pa.skip_q = pa.lse_corr == nullptr;
-  // fp16 V without smooth_v, batched, whole 64-key tiles: the attention
-  // kernel copies V tiles in token order (no V block pass)
-  pa.skip_v = !c.bf16 && !pa.smooth_v && !c.pv_fp8 && !c.q.packed && c.k.N > 0 && c.k.N % 64 == 0;
+  // fp16 V without smooth_v: the attention kernel copies V tiles in token
+  // order (no V block pass)
+  pa.skip_v = !c.bf16 && !pa.smooth_v && !c.pv_fp8 && c.k.N > 0;
   qa_status_t st = hip_status(qa::launch_sage_prep(pa, (hipStream_t)stream), "dense preprocessing launch");
   if (st != QA_OK) return st;
   qa::FlashArgs a{};

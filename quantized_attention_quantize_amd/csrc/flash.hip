@@ -553,7 +553,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
   uint32_t vtok_row = 0;
   uint32_t vtok_off[VTOK ? (kVtokChunks<D> + NW - 1) / NW : 1];
   if constexpr (VTOK) {
-    vtok_seq = reinterpret_cast<const uint8_t*>(a.v_tok) + ((int64_t)z * a.v_sb + (int64_t)kvh * a.v_sh) * 2;
+    const int64_t vrow0 = a.k_rows.packed ? (int64_t)a.k_rows.start(z) * a.v_st : (int64_t)z * a.v_sb;
+    vtok_seq = reinterpret_cast<const uint8_t*>(a.v_tok) + (vrow0 + (int64_t)kvh * a.v_sh) * 2;
     vtok_row = (uint32_t)(a.v_st * 2);
     constexpr int LPR = D / 8;                     // lanes per token row
 #pragma unroll
@@ -602,11 +603,26 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? (DENSE ? kWpeDense : kWpe) : NW / 
       // one, as the K blocks are)
       const int t = min(tile, (kv_len + KT - 1) / KT - 1);
       const uint8_t* src = vtok_seq + (uint64_t)(uint32_t)(t * KT) * vtok_row;
+      const int vis = kv_len - t * KT;   // rows of the tile inside the sequence (>= 1)
+      if (vis >= KT) {   // wave-uniform
+#pragma unroll
+        for (int i = 0; i < (kVtokChunks<D> + NW - 1) / NW; ++i) {
+          const int q = wave_s + NW * i;
+          if (kVtokChunks<D> % NW != 0 && q >= kVtokChunks<D>) break;   // wave-uniform
+          copy16_to_lds(src, vtok_off[i], sv_lds + (uint32_t)(buf * (KT * D * 2 + 256)) + vtok_chunk<D>(q));
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < (kVtokChunks<D> + NW - 1) / NW; ++i) {
         const int q = wave_s + NW * i;
         if (kVtokChunks<D> % NW != 0 && q >= kVtokChunks<D>) break;   // wave-uniform
-        copy16_to_lds(src, vtok_off[i], sv_lds + (uint32_t)(buf * (KT * D * 2 + 256)) + vtok_chunk<D>(q));
+        // a partial last tile re-reads the sequence's last row for the rows
+        // past the sequence: P is exactly 0 at those keys, so with finite V
+        // they add 0 (a zero fill of LDS would make the compiler wait for
+        // the copies in flight)
+        const uint32_t off = (uint32_t)min(vtok_dma_row<D>(q, lane), vis - 1) * vtok_row + (uint32_t)(lane % (D / 8)) * 16u;
+        copy16_to_lds(src, off, sv_lds + (uint32_t)(buf * (KT * D * 2 + 256)) + vtok_chunk<D>(q));
       }
     }
   };

@@ -198,8 +198,8 @@ struct FlashArgs {
   int64_t q_sb, q_st, q_sh;
   bool q_in_bf16;
   // dense: the fp16 V input read by the attention kernel in token order (no
-  // V block pass; batched, Nk a multiple of 64, no smooth_v), element
-  // (b, t, h, c) at b*v_sb + t*v_st + h*v_sh + c; or nullptr
+  // V block pass; no smooth_v), element (b, t, h, c) at b*v_sb + t*v_st +
+  // h*v_sh + c (varlen: (start(b) + t)*v_st + h*v_sh + c); or nullptr
   const uint16_t* v_tok;
   int64_t v_sb, v_st, v_sh;
 };

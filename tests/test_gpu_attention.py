@@ -684,21 +684,41 @@ def test_dense_query_blocks_in_kernel(qa, case, pv_fp8):
     assert torch.equal(fused, separate)
 
 
-@pytest.mark.parametrize("case", [(2, 200, 256, 4, 2, 128, True), (1, 130, 512, 2, 2, 64, False),
-                                  (1, 129, 192, 6, 1, 256, True), (2, 64, 64, 2, 1, 128, False)],
+def _zero_mean_v_bits(seq_lens, H, d, seed):
+    """fp16 V rows k/64 (|k| <= 256) whose every sequence has channel sums of
+    exactly 0 (the second half of its rows negates the first, a last odd row
+    is 0): the smooth_v mean is exactly 0 in any summation order, so smooth_v
+    leaves the output unchanged bit for bit."""
+    rng = np.random.default_rng(seed)
+    parts = []
+    for L in seq_lens:
+        half = rng.integers(-256, 257, size=(L // 2, H, d)) / 64.0
+        rows = np.concatenate([half, -half[rng.permutation(L // 2)], np.zeros((L % 2, H, d))])
+        parts.append(rows[rng.permutation(L)] if L else rows)
+    return np.concatenate(parts).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("case", [(2, 200, 256, 4, 2, 128, True), (1, 130, 500, 2, 2, 64, False),
+                                  (1, 129, 193, 6, 1, 256, True), (2, 64, 64, 2, 1, 128, False),
+                                  (2, 70, 1, 2, 1, 64, False)],
                          ids=lambda c: f"B{c[0]}_{c[1]}x{c[2]}_H{c[3]}/{c[4]}_d{c[5]}_{'causal' if c[6] else 'full'}")
 def test_dense_token_order_v(qa, case):
-    """fp16 V, no smooth_v, whole 64-key tiles: the attention kernel copies V
-    tiles in token order and forms its P.V operands with transposing LDS
-    reads (no V block pass). Each sequence's output must equal, bit for bit,
-    that of a one-sequence varlen call (which takes the V block pass: the
-    same fp16 values in the other layout), and match the oracle."""
+    """fp16 V without smooth_v: the attention kernel copies V tiles in token
+    order (a partial last tile re-reads the last row, where P is 0) and forms its P.V operands with transposing LDS reads. With channel
+    sums of exactly 0, the smooth_v call (which takes the V block pass: the
+    same fp16 values in the other layout, mean 0) must give the same output
+    bit for bit; each sequence must equal its one-sequence varlen call; and
+    the output must match the oracle."""
     B, Nq, Nk, Hq, Hkv, d, causal = case
     say(f"dense token-order V {case}")
     spec = DenseSpec("dn_vt", 877 + d, B, Hq, Hkv, Nq, Nk, d, k_bias_std=3.0, dtype="f16")
     inp = dense_inputs(spec)
-    q, k, v = dev_bits(inp.q, "f16"), dev_bits(inp.k, "f16"), dev_bits(inp.v, "f16")
+    vbits = _zero_mean_v_bits([Nk] * B, Hkv, d, 5 + d).reshape(B, Nk, Hkv, d)
+    q, k, v = dev_bits(inp.q, "f16"), dev_bits(inp.k, "f16"), dev_bits(vbits, "f16")
     out = qa.dense_sage_attention(q, k, v, is_causal=causal)
+    blocks = qa.dense_sage_attention_ex(q, k, v, is_causal=causal, smooth_v=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, blocks), "token-order V against the V block pass"
     for b in range(B):
         cq = torch.tensor([0, Nq], dtype=torch.int32, device="cuda")
         ck = torch.tensor([0, Nk], dtype=torch.int32, device="cuda")
@@ -706,8 +726,33 @@ def test_dense_token_order_v(qa, case):
                                              is_causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(one, out[b]), f"sequence {b}"
-    want = oracle.sage_forward(inp.q, inp.k, inp.v, "f16", causal=causal)
+    want = oracle.sage_forward(inp.q, inp.k, vbits, "f16", causal=causal)
     assert_close(out.cpu().numpy(), want, "dense token-order V")
+
+
+@pytest.mark.parametrize("case", [([200, 7, 0, 129], [256, 64, 30, 1], 4, 2, 128, True),
+                                  ([65, 300], [63, 191], 2, 1, 64, False),
+                                  ([33, 1, 97], [130, 5, 97], 2, 2, 256, True)],
+                         ids=lambda c: f"{'-'.join(map(str, c[0]))}_on_{'-'.join(map(str, c[1]))}_H{c[2]}/{c[3]}_d{c[4]}")
+def test_dense_varlen_token_order_v(qa, case):
+    """Packed fp16 sequences of ragged lengths (partial last tiles, a
+    sequence without queries): token-order V (each sequence's rows from its
+    own offset) against the smooth_v call's V block pass on channel sums of
+    exactly 0, bit for bit, and against the oracle."""
+    seq_q, seq_k, Hq, Hkv, d, causal = case
+    say(f"dense varlen token-order V {case}")
+    spec = VarlenSpec("vl_vt", 91 + d, seq_q, seq_k, Hq, Hkv, d, dtype="f16")
+    inp = varlen_inputs(spec)
+    vbits = _zero_mean_v_bits(seq_k, Hkv, d, 9 + d)
+    cu_q, cu_k = torch.from_numpy(inp.cu_q).cuda(), torch.from_numpy(inp.cu_k).cuda()
+    q, k, v = dev_bits(inp.q, "f16"), dev_bits(inp.k, "f16"), dev_bits(vbits, "f16")
+    run = lambda sv: qa.dense_sage_attention_varlen(q, k, v, cu_q, cu_k, max(seq_q), max(seq_k), is_causal=causal,
+                                                    smooth_v=sv)
+    out, blocks = run(False), run(True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, blocks), "token-order V against the V block pass"
+    want = oracle.sage_varlen_forward(inp.q, inp.k, vbits, inp.cu_q, inp.cu_k, "f16", causal=causal)
+    assert_close(out.cpu().numpy(), want, "dense varlen token-order V")
 
 
 def test_dense_options_full_size_sampled(qa):
