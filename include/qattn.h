@@ -73,10 +73,13 @@ const char* qa_last_error(void);
  *
  *   q        [num_tokens, num_heads, head_dim] bf16 or f16 (dtype), element
  *            (t, h, i) at q + t*stride_token + h*stride_head + i (strides in
- *            elements; the innermost stride is 1)
- *   q_i8     out [num_tokens, num_heads, head_dim] int8, contiguous
+ *            elements, multiples of 8; the innermost stride is 1); 16-byte
+ *            aligned
+ *   q_i8     out [num_tokens, num_heads, head_dim] int8, contiguous, 8-byte
+ *            aligned
  *   q_scale  out [num_tokens, num_heads] fp32, contiguous
- * num_tokens == 0 is a no-op.
+ * num_tokens == 0 is a no-op; a misaligned pointer or stride is
+ * QA_ERR_INVALID_ARG.
  */
 qa_status_t qa_quantize_q(const void* q, qa_dtype_t dtype, int64_t num_tokens,
                           int32_t num_heads, int32_t head_dim, int64_t stride_token,

@@ -336,6 +336,7 @@ qa_status_t qa_quantize_q(const void* q, qa_dtype_t dtype, int64_t num_tokens, i
   QA_REQUIRE(aligned16(q) && stride_token % 8 == 0 && stride_head % 8 == 0 && stride_token >= 0 &&
                  stride_head >= 0,
              QA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  QA_REQUIRE(((uintptr_t)q_i8 & 7u) == 0, QA_ERR_INVALID_ARG, "q_i8 must be 8-byte aligned");
   QA_REQUIRE(num_tokens * num_heads / 4 < (int64_t)INT32_MAX, QA_ERR_UNSUPPORTED, "too many rows");
   return hip_status(qa::launch_quantize_rows(q, dtype == QA_DT_BF16, num_tokens, num_heads, head_dim,
                                              stride_token, stride_head, q_i8, q_scale, (hipStream_t)stream),

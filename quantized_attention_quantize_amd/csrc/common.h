@@ -114,11 +114,36 @@ __device__ __forceinline__ v8h i8x8_to_f16x8(uint2 w) {
 
 // ---- wave reductions (wave64) ----------------------------------------------
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// A lane's view of another lane of its 16-lane row through a DPP operand
+// (no LDS traffic): 0xB1 / 0x4E are the quad permutations [1,0,3,2] and
+// [2,3,0,1] (lanes l^1 and l^2), 0x124 / 0x128 rotate the row by 4 and 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+
+// max / sum over the 16 lanes of each row (lanes 16r .. 16r+15): quad
+// exchanges, then the row rotated by 4 and by 8. Every lane ends with the
+// row's result (a sum in an order that depends on the lane, fixed per lane).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  return fmaxf(v, dpp_f<0x128>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x124>(v);
+  return v + dpp_f<0x128>(v);
+}
+
+__device__ __forceinline__ float group4_max(float v);
+__device__ __forceinline__ float group4_sum(float v);
+
+// max / sum over the whole wave: rows of 16, then the four rows
+__device__ __forceinline__ float wave_max(float v) { return group4_max(row16_max(v)); }
+__device__ __forceinline__ float wave_sum(float v) { return group4_sum(row16_sum(v)); }
 
 // max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48).
 // v_permlane16_swap / v_permlane32_swap with both operands equal to v leave

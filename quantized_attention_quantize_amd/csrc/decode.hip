@@ -551,8 +551,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 // Many splits: one wave per (query row, head, 4 channels). Lane s reads
 // split s (and s + 64, ... when S > 64); the wave reduces the maximum, then
-// the weighted sums, with butterfly exchanges (a fixed order, so results do
-// not vary from run to run): one round of loads, no LDS, no barrier.
+// the weighted sums, with lane exchanges inside the registers (DPP and
+// permlane: a fixed order, so results do not vary from run to run): one
+// round of loads, no LDS, no barrier.
 template <int D>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                  int32_t Hq, int32_t S, int32_t rows, bool out_bf16, void* out) {
@@ -588,14 +589,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ws_o,
       acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
     }
   }
-#pragma unroll
-  for (int k = 32; k > 0; k >>= 1) {
-    l += __shfl_xor(l, k, 64);
-    acc.x += __shfl_xor(acc.x, k, 64);
-    acc.y += __shfl_xor(acc.y, k, 64);
-    acc.z += __shfl_xor(acc.z, k, 64);
-    acc.w += __shfl_xor(acc.w, k, 64);
-  }
+  l = wave_sum(l);
+  acc.x = wave_sum(acc.x);
+  acc.y = wave_sum(acc.y);
+  acc.z = wave_sum(acc.z);
+  acc.w = wave_sum(acc.w);
   if (lane != 0) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   const int64_t oi = rh * D + 4 * c4;

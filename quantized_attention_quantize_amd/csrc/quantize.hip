@@ -117,37 +117,108 @@ __device__ __forceinline__ void write_kv_row(const uint16_t* __restrict__ k, con
   }
 }
 
-// Each wave quantizes kRowsPerWave (token, head) rows, every load issued
-// before the first row is reduced (one row per wave waited for its load
-// alone); 4 waves per workgroup. The codes are quant_row's.
-constexpr int kRowsPerWave = 4;
+// Rows held by 16 lanes: lane li of a 16-lane row holds D/16 channels of
+// one (token, head) row, in pieces of kPieceLen consecutive channels
+// (16-byte loads for D >= 128); piece p starts at channel (16p + li) *
+// kPieceLen, so each load instruction of the row reads one contiguous span.
+template <int D>
+constexpr int kPieceLen = D >= 128 ? 8 : D / 16;
+template <int D>
+constexpr int kPieces = D / 16 / kPieceLen<D>;
+template <int D>
+__device__ __forceinline__ int piece_ch(int li, int p) { return (16 * p + li) * kPieceLen<D>; }
+
+// The lane's D/16 16-bit values of `row`, two per word, in channel order.
+template <int D>
+__device__ __forceinline__ void load_row16(const uint16_t* row, int li, uint32_t (&w)[D / 32]) {
+  constexpr int PL = kPieceLen<D>;
+#pragma unroll
+  for (int p = 0; p < kPieces<D>; ++p) {
+    if constexpr (PL == 8) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + piece_ch<D>(li, p));
+      w[4 * p] = u.x; w[4 * p + 1] = u.y; w[4 * p + 2] = u.z; w[4 * p + 3] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(row + piece_ch<D>(li, p));
+      w[2 * p] = u.x; w[2 * p + 1] = u.y;
+    }
+  }
+}
+
+template <int N, bool BF16>
+__device__ __forceinline__ float unpack_absmax(const uint32_t (&w)[N / 2], float (&v)[N]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    v[i] = half_to_f32<BF16>(i & 1 ? w[i / 2] >> 16 : w[i / 2] & 0xFFFFu);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  return amax;
+}
+
+// The lane's codes (quant_bytes words, channel order) to row / block memory:
+// piece p goes to dst(p), 8 (or 4) bytes.
+template <int D, typename F>
+__device__ __forceinline__ void store_pieces(const uint32_t (&c)[D / 64], F dst) {
+  constexpr int PL = kPieceLen<D>;
+#pragma unroll
+  for (int p = 0; p < kPieces<D>; ++p) {
+    if constexpr (PL == 8) *reinterpret_cast<uint2*>(dst(p)) = make_uint2(c[2 * p], c[2 * p + 1]);
+    else *reinterpret_cast<uint32_t*>(dst(p)) = c[p];
+  }
+}
+
+// Each wave quantizes groups of 4 (token, head) rows, 16 lanes per row:
+// group g holds rows 4g .. 4g+3, and the waves of the grid take the groups
+// round-robin (wave w: groups w, w + nw, ...), loading the next group while
+// they quantize the current one, so that the loads of one group overlap the
+// arithmetic of the previous (in a single pass every wave would load, then
+// every wave compute, with memory idle meanwhile). The row maximum is
+// reduced inside its 16 lanes through DPP (no LDS); the codes are
+// quant_bytes', i.e. those of quant_code.
+// Row 4*grp + sub (clamped to the last row: rows past the end re-read it and
+// are not stored). The division by H is done once per wave on the scalar
+// unit for the group's first row; each lane then steps over at most
+// sub / H + 1 token boundaries.
+template <int D, bool BF16>
+__device__ __forceinline__ void load_row_group(const uint16_t* __restrict__ x, int64_t rows, int32_t H, int64_t st,
+                                               int64_t sh, int64_t grp, int sub, int li, uint32_t (&w)[D / 32]) {
+  const int64_t r0 = __builtin_amdgcn_readfirstlane((uint32_t)(4 * grp)) |
+                     ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((4 * grp) >> 32)) << 32);
+  const int64_t t0 = r0 / H;                        // wave-uniform
+  const int h0 = (int)(r0 - t0 * H);
+  int64_t t = t0;
+  int h = h0 + (int)(min(r0 + sub, rows - 1) - r0);
+  while (h >= H) {                                  // at most 3 steps (sub < 4)
+    h -= H;
+    ++t;
+  }
+  load_row16<D>(x + t * st + (int64_t)h * sh, li, w);
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x, int64_t rows,
                                                        int32_t H, int64_t st, int64_t sh,
                                                        int8_t* __restrict__ q, float* __restrict__ scale) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
-  if (row0 >= rows) return;
-  float v[kRowsPerWave][E];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int64_t row = min(row0 + i, rows - 1);   // rows past the end re-read the last (not stored)
-    const int64_t t = row / H;
-    const int h = (int)(row - t * H);
-    load_halves<E, BF16>(x + t * st + (int64_t)h * sh + lane * E, v[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int64_t row = row0 + i;
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
-    amax = wave_max(amax);
+  constexpr int E = D / 16;
+  const int lane = threadIdx.x & 63, li = lane & 15, sub = lane >> 4;
+  const int64_t ngroups = (rows + 3) / 4;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (grp >= ngroups) return;                      // the whole wave
+  uint32_t w[D / 32];
+  load_row_group<D, BF16>(x, rows, H, st, sh, grp, sub, li, w);
+  for (; grp < ngroups; grp += nw) {
+    float v[E];
+    const float amax_l = unpack_absmax<E, BF16>(w, v);
+    if (grp + nw < ngroups) load_row_group<D, BF16>(x, rows, H, st, sh, grp + nw, sub, li, w);
+    const int64_t row = 4 * grp + sub;
+    const float amax = row16_max(amax_l);
     const float s = quant_scale(amax);
+    uint32_t c[E / 4];
+    quant_bytes<E>(v, amax, s, __fdiv_rn(1.0f, s), c);
     if (row < rows) {
-      store_codes<E>(q + row * D + lane * E, quant_lane<E>(v[i], amax, s));
-      if (lane == 0) scale[row] = s;
+      store_pieces<D>(c, [&](int p) { return q + row * D + piece_ch<D>(li, p); });
+      if (li == 0) scale[row] = s;
     }
   }
 }
@@ -167,7 +238,7 @@ __global__ __launch_bounds__(256) void k_write_kv(const uint16_t* __restrict__ k
 // The cache write for runs of tokens: workgroup (group of 16 tokens, head).
 // When the group's 16 slots are the 16 slots of one cache block in order
 // (slot_j = 16*blk + j: a chunk written from a block boundary), each wave
-// quantizes 4 token rows, the codes and V values are gathered in LDS in the
+// quantizes 4 token rows (16 lanes each), the codes and V values are gathered in LDS in the
 // block's own layout, and the workgroup then writes the K block (D*16 bytes)
 // and the V block (D*16 values) as contiguous 16-byte pieces: a token's V
 // row alone lands in D places 32 (16) bytes apart, which costs a memory
@@ -181,7 +252,6 @@ __global__ __launch_bounds__(256) void k_write_kv_blocks(const uint16_t* __restr
                                                          const int64_t* __restrict__ slots,
                                                          int8_t* __restrict__ kc, float* __restrict__ ks,
                                                          void* __restrict__ vc, float* __restrict__ vs) {
-  constexpr int E = D / 64;
   constexpr int VB = V_I8 ? 1 : 2;                  // bytes per cached V value
   __shared__ __attribute__((aligned(16))) int8_t s_k[D * 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[D * 16 * VB];
@@ -204,47 +274,43 @@ __global__ __launch_bounds__(256) void k_write_kv_blocks(const uint16_t* __restr
     }
     return;
   }
-  const int ch = lane * E;
-  // the wave's 4 rows: every K and V load issued before any is used
-  float kr[4][E], vr[4][V_I8 ? E : 1];
-  uint16_t vraw[4][V_I8 ? 1 : E];               // 16-bit V is copied as it is
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t src = (t0 + wave + 4 * i) * st + (int64_t)h * sh + ch;
-    load_halves<E, BF16>(k + src, kr[i]);
-    if constexpr (V_I8) {
-      load_halves<E, BF16>(v + src, vr[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) vraw[i][e] = v[src + e];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = wave + 4 * i;
-    const float(&kv)[E] = kr[i];
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(kv[e]));
-    amax = wave_max(amax);
+  // 16 lanes per token: wave w holds tokens 4w .. 4w+3 of the group, every
+  // K and V load issued before any is used; row maxima through DPP
+  constexpr int N = D / 16;
+  const int li = lane & 15, j = 4 * wave + (lane >> 4);
+  const int64_t src = (t0 + j) * st + (int64_t)h * sh;
+  uint32_t kw[D / 32], vw[D / 32];
+  load_row16<D>(k + src, li, kw);
+  load_row16<D>(v + src, li, vw);
+  {
+    float kv[N];
+    const float amax = row16_max(unpack_absmax<N, BF16>(kw, kv));
     const float sk = quant_scale(amax);
-    store_codes<E>(s_k + (ch / 16) * 256 + j * 16 + (ch % 16), quant_lane<E>(kv, amax, sk));
-    if (lane == 0) s_ks[j] = sk;
-    if constexpr (V_I8) {
-      const float(&vv)[E] = vr[i];
-      float vmax = 0.0f;
+    uint32_t c[N / 4];
+    quant_bytes<N>(kv, amax, sk, __fdiv_rn(1.0f, sk), c);
+    // channel ch of token j sits at (ch / 16) * 256 + j * 16 + ch % 16 of the K block
+    store_pieces<D>(c, [&](int p) {
+      const int ch = piece_ch<D>(li, p);
+      return s_k + (ch / 16) * 256 + j * 16 + (ch % 16);
+    });
+    if (li == 0) s_ks[j] = sk;
+  }
+  // V: channel ch of token j at ch * 16 + j of the V block
+  if constexpr (V_I8) {
+    float vv[N];
+    const float vmax = row16_max(unpack_absmax<N, BF16>(vw, vv));
+    const float sv = quant_scale(vmax);
+    uint32_t c[N / 4];
+    quant_bytes<N>(vv, vmax, sv, __fdiv_rn(1.0f, sv), c);
 #pragma unroll
-      for (int e = 0; e < E; ++e) vmax = fmaxf(vmax, fabsf(vv[e]));
-      vmax = wave_max(vmax);
-      const float sv = quant_scale(vmax);
-      const uint32_t codes = quant_lane<E>(vv, vmax, sv);
+    for (int i = 0; i < N; ++i)
+      s_v[(piece_ch<D>(li, i / kPieceLen<D>) + i % kPieceLen<D>) * 16 + j] = (uint8_t)(c[i / 4] >> (8 * (i % 4)));
+    if (li == 0) s_vs[j] = sv;
+  } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s_v[(ch + e) * 16 + j] = (uint8_t)(codes >> (8 * e));
-      if (lane == 0) s_vs[j] = sv;
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) reinterpret_cast<uint16_t*>(s_v)[(ch + e) * 16 + j] = vraw[i][e];
-    }
+    for (int i = 0; i < N; ++i)
+      reinterpret_cast<uint16_t*>(s_v)[(piece_ch<D>(li, i / kPieceLen<D>) + i % kPieceLen<D>) * 16 + j] =
+          (uint16_t)(i & 1 ? vw[i / 2] >> 16 : vw[i / 2] & 0xFFFFu);
   }
   __syncthreads();
   const int64_t bh = (slot0 >> 4) * H + h;
@@ -806,11 +872,17 @@ __global__ __launch_bounds__(256) void k_v_blocks(const uint16_t* __restrict__ v
   }
 }
 
+// workgroups of the row quantizer: four per CU (16 waves)
+constexpr int64_t kQuantGrid = 1024;
+
 template <int D>
 hipError_t quantize_rows_d(const void* x, bool bf16, int64_t T, int32_t H, int64_t st, int64_t sh,
                            int8_t* q, float* scale, hipStream_t s) {
   const int64_t rows = T * H;
-  const dim3 grid((unsigned)((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
+  // four waves of 4-row groups per workgroup; at most kQuantGrid workgroups,
+  // each wave then walks several groups
+  const int64_t wgs = ((rows + 3) / 4 + 3) / 4;
+  const dim3 grid((unsigned)(wgs < kQuantGrid ? wgs : kQuantGrid));
   if (bf16)
     k_quantize_rows<D, true><<<grid, 256, 0, s>>>((const uint16_t*)x, rows, H, st, sh, q, scale);
   else
