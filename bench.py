@@ -826,26 +826,36 @@ def main():
         res["practical_peak"] = pk
         res["roofline"]["frac_of_practical_stream"] = round(achieved / pk["stream_read_1GiB_GBps"], 4)
         rms = r["rope_ms_per_step"]
-        res["extra"] = {"decode_step_rope": {
-                            "workload": "qwen27b decode step with rotary embedding in the split kernel (64 of 256 "
-                                        "channels rotated): rotate + quantize the query, rotate + write the new token, "
-                                        "split-K attention, combine",
-                            "ms": rms, "GBps": r["step_bytes"] / (rms * 1e-3) / 1e9,
-                            "frac_hbm_peak": r["step_bytes"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-                        "decode_2_tokens": run_decode_mt(torch, qa, args.context, 2, args.pools),
-                        "chunked_prefill": run_prefill(torch, qa, 20),
-                        "chunked_prefill_fp8pv": run_prefill(torch, qa, 20, pv_fp8=True),
-                        "chunked_prefill_v_workspace": run_prefill(torch, qa, 20, v_ws=True),
-                        "dense_sage_noncausal": run_dense(torch, qa, 10, False),
-                        "dense_sage_causal": run_dense(torch, qa, 10, True),
-                        "dense_sage_hnd_smooth_v_lse": run_dense(torch, qa, 10, False, options=True),
-                        "dense_sage_noncausal_fp8pv": run_dense(torch, qa, 10, False, pv_fp8=True),
-                        "dense_sage_causal_fp8pv": run_dense(torch, qa, 10, True, pv_fp8=True),
-                        "dense_sage_varlen_mix": run_varlen(torch, qa, 10),
-                        "decode_batched_splitk": run_decode_batched(torch, qa, 20),
-                        "decode_batched_library_splits": run_decode_batched(torch, qa, 20, splits=0),
-                        "decode_tiny": run_decode_tiny(torch, qa, 100),
-                        **run_producers(torch, qa, 30)}
+        extra = {"decode_step_rope": {
+            "workload": "qwen27b decode step with rotary embedding in the split kernel (64 of 256 "
+                        "channels rotated): rotate + quantize the query, rotate + write the new token, "
+                        "split-K attention, combine",
+            "ms": rms, "GBps": r["step_bytes"] / (rms * 1e-3) / 1e9,
+            "frac_hbm_peak": r["step_bytes"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        runs = [("decode_2_tokens", lambda: run_decode_mt(torch, qa, args.context, 2, args.pools)),
+                ("chunked_prefill", lambda: run_prefill(torch, qa, 20)),
+                ("chunked_prefill_fp8pv", lambda: run_prefill(torch, qa, 20, pv_fp8=True)),
+                ("chunked_prefill_v_workspace", lambda: run_prefill(torch, qa, 20, v_ws=True)),
+                ("dense_sage_noncausal", lambda: run_dense(torch, qa, 10, False)),
+                ("dense_sage_causal", lambda: run_dense(torch, qa, 10, True)),
+                ("dense_sage_hnd_smooth_v_lse", lambda: run_dense(torch, qa, 10, False, options=True)),
+                ("dense_sage_noncausal_fp8pv", lambda: run_dense(torch, qa, 10, False, pv_fp8=True)),
+                ("dense_sage_causal_fp8pv", lambda: run_dense(torch, qa, 10, True, pv_fp8=True)),
+                ("dense_sage_varlen_mix", lambda: run_varlen(torch, qa, 10)),
+                ("decode_batched_splitk", lambda: run_decode_batched(torch, qa, 20)),
+                ("decode_batched_library_splits", lambda: run_decode_batched(torch, qa, 20, splits=0)),
+                ("decode_tiny", lambda: run_decode_tiny(torch, qa, 100)),
+                (None, lambda: run_producers(torch, qa, 30))]
+        for name, fn in runs:
+            t_run = time.time()
+            out = fn()
+            if name is None:
+                extra.update(out)
+            else:
+                extra[name] = out
+            # one progress line per workload (stderr; stdout keeps the one JSON line)
+            print(f"bench: {name or ', '.join(out)} done in {time.time() - t_run:.1f} s", file=sys.stderr, flush=True)
+        res["extra"] = extra
         for e in res["extra"].values():
             if "_ops" not in e:
                 continue
