@@ -153,29 +153,40 @@ __global__ __launch_bounds__(256) void k_v8_tiles(PrefillFp8Args a) {
   const int nblk = min((ctx + 15) / 16, a.max_blocks);
   const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
   uint8_t* dst = a.v8 + (((int64_t)seq * a.v8_seq_tiles + tile) * a.Hkv + kvh) * (int64_t)(KT8 * D);
-  for (int u = threadIdx.x; u < kBlk8 * D * 2; u += 256) {
-    const int h8 = u & 1, ch = (u >> 1) % D, j = (u >> 1) / D;
-    const int b = tile * kBlk8 + j;
-    const float sc = s_sv[ch];
-    float x[8];
+  // units u = threadIdx.x + 256 i; each thread loads a batch of units before
+  // converting any (blocks past the sequence read its last block, masked)
+  constexpr int PER = kBlk8 * D * 2 / 256;          // units per thread
+  constexpr int BATCH = PER < 4 ? PER : 4;
+  static_assert(PER % BATCH == 0, "whole batches");
+  for (int i0 = 0; i0 < PER; i0 += BATCH) {
+    float v[BATCH][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-    if (b < nblk && sc > 0.0f) {
-      const int64_t bh = (int64_t)trow[b] * a.Hkv + kvh;
-      float v[8];
-      v_row8<D, VI8>(a, bh, ch, h8, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = b * 16 + 8 * h8 + e < ctx ? __fdiv_rn(v[e], sc) : 0.0f;
+    for (int k = 0; k < BATCH; ++k) {
+      const int u = (int)threadIdx.x + 256 * (i0 + k);
+      const int h8 = u & 1, ch = (u >> 1) % D, j = (u >> 1) / D;
+      const int b = min(tile * kBlk8 + j, nblk - 1);
+      v_row8<D, VI8>(a, (int64_t)trow[b] * a.Hkv + kvh, ch, h8, v[k]);
     }
-    uint32_t w[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k], x[4 * k + 1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * k + 2], x[4 * k + 3], word, true);
-      w[k] = (uint32_t)word;
+    for (int k = 0; k < BATCH; ++k) {
+      const int u = (int)threadIdx.x + 256 * (i0 + k);
+      const int h8 = u & 1, ch = (u >> 1) % D, j = (u >> 1) / D;
+      const int b = tile * kBlk8 + j;
+      const float sc = s_sv[ch];
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = b < nblk && sc > 0.0f && b * 16 + 8 * h8 + e < ctx ? __fdiv_rn(v[k][e], sc) : 0.0f;
+      uint32_t w[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q], x[4 * q + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2], x[4 * q + 3], word, true);
+        w[q] = (uint32_t)word;
+      }
+      const int off = (j >> 1) * D * 32 + ch * 32 + 16 * ((j & 1) ^ ((ch >> 3) & 1)) + 8 * h8;
+      *reinterpret_cast<uint2*>(dst + off) = make_uint2(w[0], w[1]);
     }
-    const int off = (j >> 1) * D * 32 + ch * 32 + 16 * ((j & 1) ^ ((ch >> 3) & 1)) + 8 * h8;
-    *reinterpret_cast<uint2*>(dst + off) = make_uint2(w[0], w[1]);
   }
 }
 
