@@ -34,7 +34,7 @@ def _q_bits(T, H, d, dtype, seed):
     return to_bf16_bits(x) if dtype == "bf16" else to_f16_bits(x)
 
 
-QSHAPES = [(1, 6, 64), (1, 24, 256), (32, 24, 256), (2048, 24, 256), (7, 3, 128), (5, 16, 64)]
+QSHAPES = [(1, 6, 64), (1, 24, 256), (32, 24, 256), (2048, 24, 256), (7, 3, 128), (5, 16, 64), (4099, 6, 128)]
 
 
 @pytest.mark.parametrize("shape", QSHAPES, ids=[f"{t}x{h}x{d}" for t, h, d in QSHAPES])
